@@ -1,0 +1,137 @@
+"""CPU oracle for the stable merge of two sorted arrays.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The product
+library (``ordered_merge_sorted_amd``) never imports, links or calls it, and
+this package imports nothing from the product: the two share no code.
+
+The arithmetic lives in ``oracle.c`` (plain C, built with gcc into
+``liboracle.so`` next to it); this module only marshals numpy arrays.  See the
+header of ``oracle.c`` for what each routine computes and which passage of the
+pages it follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+GCC_FLAGS = ["-O2", "-std=c99", "-Wall", "-Werror", "-shared", "-fPIC"]
+
+
+def compile_c(src: str, out: str) -> str:
+    """Compile one C source into a shared library with gcc."""
+    tmp = out + ".tmp%d" % os.getpid()
+    subprocess.check_call(["gcc", *GCC_FLAGS, src, "-o", tmp])
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` (no GPU needed)."""
+    if force or not os.path.exists(LIB):
+        compile_c(SRC, LIB)
+    return LIB
+
+
+def _i32(x) -> np.ndarray:
+    x = np.ascontiguousarray(x)
+    if x.dtype != np.int32:
+        raise TypeError("oracle keys must be int32, got %s" % x.dtype)
+    return x
+
+
+def _u32(x) -> np.ndarray:
+    x = np.ascontiguousarray(x)
+    if x.dtype != np.uint32:
+        raise TypeError("oracle payloads must be uint32, got %s" % x.dtype)
+    return x
+
+
+def _ptr(x: np.ndarray):
+    return ctypes.c_void_p(x.ctypes.data)
+
+
+class Oracle:
+    """The oracle routines of one compiled copy of ``oracle.c``."""
+
+    def __init__(self, lib_path: str = LIB):
+        lib = ctypes.CDLL(lib_path)
+        p, i64 = ctypes.c_void_p, ctypes.c_int64
+        lib.oracle_merge_i32.argtypes = [p, i64, p, i64, p]
+        lib.oracle_merge_i32.restype = None
+        lib.oracle_merge_kv.argtypes = [p, p, i64, p, p, i64, p, p]
+        lib.oracle_merge_kv.restype = None
+        lib.oracle_co_rank_all.argtypes = [p, i64, p, i64, p]
+        lib.oracle_co_rank_all.restype = None
+        self._lib = lib
+        self.path = lib_path
+
+    def merge_i32(self, A, B) -> np.ndarray:
+        """Stable merge of sorted int32 ``A`` and ``B``; equal keys: A first."""
+        A, B = _i32(A), _i32(B)
+        C = np.empty(A.size + B.size, dtype=np.int32)
+        self._lib.oracle_merge_i32(_ptr(A), A.size, _ptr(B), B.size, _ptr(C))
+        return C
+
+    def merge_kv(self, A_keys, A_vals, B_keys, B_vals):
+        """Stable merge of (int32 key, uint32 payload) pairs by key; A first on ties."""
+        Ak, Bk = _i32(A_keys), _i32(B_keys)
+        Av, Bv = _u32(A_vals), _u32(B_vals)
+        if Ak.size != Av.size or Bk.size != Bv.size:
+            raise ValueError("key and payload lengths differ")
+        Ck = np.empty(Ak.size + Bk.size, dtype=np.int32)
+        Cv = np.empty(Ak.size + Bk.size, dtype=np.uint32)
+        self._lib.oracle_merge_kv(_ptr(Ak), _ptr(Av), Ak.size, _ptr(Bk),
+                                  _ptr(Bv), Bk.size, _ptr(Ck), _ptr(Cv))
+        return Ck, Cv
+
+    def co_rank_all(self, A, B) -> np.ndarray:
+        """int64 array I of length m+n+1: I[k] = number of A elements among the
+        first k merged outputs (the co-rank of k); the B count is k - I[k]."""
+        A, B = _i32(A), _i32(B)
+        I = np.empty(A.size + B.size + 1, dtype=np.int64)
+        self._lib.oracle_co_rank_all(_ptr(A), A.size, _ptr(B), B.size, _ptr(I))
+        return I
+
+    def co_rank(self, k: int, A, B) -> int:
+        """Co-rank of one output rank k (0 <= k <= m+n)."""
+        A, B = _i32(A), _i32(B)
+        if not 0 <= k <= A.size + B.size:
+            raise ValueError("k out of range")
+        return int(self.co_rank_all(A, B)[k])
+
+
+_default = None
+
+
+def default() -> Oracle:
+    """The oracle built from ``oracle.c`` (built on first use if missing)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(LIB):
+            build(force=False)
+        _default = Oracle(LIB)
+    return _default
+
+
+def merge_i32(A, B):
+    return default().merge_i32(A, B)
+
+
+def merge_kv(A_keys, A_vals, B_keys, B_vals):
+    return default().merge_kv(A_keys, A_vals, B_keys, B_vals)
+
+
+def co_rank_all(A, B):
+    return default().co_rank_all(A, B)
+
+
+def co_rank(k, A, B):
+    return default().co_rank(k, A, B)

@@ -1,0 +1,290 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises AssertionError
+when the oracle disagrees with the fact.  ``tests/test_oracle_pins.py`` runs
+them against the real oracle; ``tests/test_oracle_mutants.py`` runs them
+against copies of the oracle with planted mistakes and expects a failure.
+
+Sources of truth used here:
+  * values printed on the pages (golden fixtures under tests/golden/);
+  * hand derivation from the definition on tiny inputs;
+  * brute force: a stable sort of the tagged concatenation A||B;
+  * a library routine that is specified to be this merge (heapq.merge is
+    stable and takes the first iterable first on equal keys);
+  * a structurally different formula: the rank scatter
+    A[i] -> C[i + #{b in B : b < A[i]}],  B[j] -> C[j + #{a in A : a <= B[j]}];
+  * closed forms of the even/odd workload;
+  * invariants: i+j=k, the co-rank bounds, unit steps, order, permutation.
+"""
+from __future__ import annotations
+
+import heapq
+import itertools
+import json
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+U31 = np.uint32(1 << 31)
+
+
+def load_golden(name: str) -> dict:
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def tags(m: int, n: int):
+    """Distinct payload tags: A element i -> i, B element j -> 2^31 + j."""
+    return (np.arange(m, dtype=np.uint32),
+            (U31 + np.arange(n, dtype=np.uint32)).astype(np.uint32))
+
+
+def as_i32(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.int32)
+
+
+# ---------------------------------------------------------------- golden pins
+
+def pin_worked_example(orc) -> None:
+    """Page-printed co-ranks, thread calls and thread-1 output (12-merge/02)."""
+    g = load_golden("worked_example_corank.json")
+    A, B = as_i32(g["A"]), as_i32(g["B"])
+    I = orc.co_rank_all(A, B)
+    for k, i, j in zip(g["boundary_k"], g["boundary_i"], g["boundary_j"]):
+        assert I[k] == i, ("co_rank(%d)" % k, int(I[k]), i)
+        assert k - I[k] == j
+    C = orc.merge_i32(A, B)
+    out = g["thread1_output"]
+    c0 = out["c_start"]
+    assert list(C[c0:c0 + len(out["values"])]) == out["values"]
+    ks = g["boundary_k"]
+    for call in g["thread_calls"]:
+        t = call["thread"]
+        k0, k1 = ks[t], ks[t + 1]
+        assert call["a_start"] == I[k0] and call["a_len"] == I[k1] - I[k0]
+        assert call["b_start"] == k0 - I[k0]
+        assert call["b_len"] == (k1 - I[k1]) - (k0 - I[k0])
+        assert call["c_start"] == k0
+        # Merging the thread's two sub-arrays alone gives its slice of C.
+        part = orc.merge_i32(A[call["a_start"]:call["a_start"] + call["a_len"]],
+                             B[call["b_start"]:call["b_start"] + call["b_len"]])
+        assert np.array_equal(part, C[k0:k1])
+
+
+def pin_equal_element_case(orc) -> None:
+    """merge_path.cu's tie case.  Expected values derived by hand from the
+    definition: the walk takes A0 (1<=1), A1 (1<=1), B0 (2>1), A2 (2<=2),
+    B1 (3>2), B2 (3>2), A3 (3<=4), then B3 because A is exhausted."""
+    g = load_golden("equal_element_case.json")
+    A, B = as_i32(g["A"]), as_i32(g["B"])
+    assert list(orc.merge_i32(A, B)) == [1, 1, 1, 2, 2, 2, 3, 4]
+    Av, Bv = tags(A.size, B.size)
+    Ck, Cv = orc.merge_kv(A, Av, B, Bv)
+    src = ["A%d" % v if v < U31 else "B%d" % (v - U31) for v in Cv]
+    assert src == ["A0", "A1", "B0", "A2", "B1", "B2", "A3", "B3"], src
+    assert list(Ck) == [1, 1, 1, 2, 2, 2, 3, 4]
+    assert list(orc.co_rank_all(A, B)) == [0, 1, 2, 2, 3, 3, 3, 4, 4]
+
+
+# ------------------------------------------------------ brute force / library
+
+def _stable_sort_reference(A, B):
+    """Brute force: stable sort by key of the tagged concatenation A||B."""
+    keys = np.concatenate([A, B]).astype(np.int64)
+    Av, Bv = tags(A.size, B.size)
+    vals = np.concatenate([Av, Bv])
+    order = np.argsort(keys, kind="stable")
+    return keys[order].astype(np.int32), vals[order]
+
+
+def _check_against_brute(orc, A, B) -> None:
+    Av, Bv = tags(A.size, B.size)
+    Ck, Cv = orc.merge_kv(A, Av, B, Bv)
+    Rk, Rv = _stable_sort_reference(A, B)
+    assert np.array_equal(Ck, Rk) and np.array_equal(Cv, Rv), (A, B)
+    assert np.array_equal(orc.merge_i32(A, B), Rk), (A, B)
+    # co-rank = number of A tags among the first k outputs
+    I = orc.co_rank_all(A, B)
+    from_a = np.concatenate([[0], np.cumsum(Rv < U31)])
+    assert np.array_equal(I, from_a), (A, B)
+
+
+def sorted_arrays(max_len: int, alphabet: int):
+    for L in range(max_len + 1):
+        for combo in itertools.combinations_with_replacement(range(alphabet), L):
+            yield np.array(combo, dtype=np.int32)
+
+
+def pin_exhaustive_tiny(orc, max_len: int = 5, alphabet: int = 3) -> None:
+    """Every pair of sorted arrays of length <= max_len over {0..alphabet-1}."""
+    arrs = list(sorted_arrays(max_len, alphabet))
+    for A in arrs:
+        for B in arrs:
+            _check_against_brute(orc, A, B)
+
+
+def _random_sorted(g, size, lo, hi):
+    return np.sort(g.integers(lo, hi, size=size, dtype=np.int64)).astype(np.int32)
+
+
+def pin_random_brute(orc, seed: int = 7, cases: int = 200) -> None:
+    """Random sizes and value ranges, including the int32 extremes."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    imin, imax = -(1 << 31), (1 << 31) - 1
+    for c in range(cases):
+        m, n = (int(x) for x in g.integers(0, 300, size=2))
+        span = int(g.choice([2, 5, 50, 1 << 32]))
+        if span == 1 << 32:
+            A = _random_sorted(g, m, imin, imax + 1)
+            B = _random_sorted(g, n, imin, imax + 1)
+            # plant the extremes so the sign and the ends are exercised
+            if m:
+                A[0], A[-1] = imin, imax
+            if n:
+                B[0], B[-1] = imin, imax
+            A.sort(); B.sort()
+        else:
+            base = int(g.integers(imin, imax - span))
+            A = _random_sorted(g, m, base, base + span)
+            B = _random_sorted(g, n, base, base + span)
+        _check_against_brute(orc, A, B)
+
+
+def pin_heapq_merge(orc, seed: int = 11, cases: int = 30) -> None:
+    """heapq.merge is stable and takes the earlier iterable first on ties."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    for c in range(cases):
+        m, n = (int(x) for x in g.integers(0, 2000, size=2))
+        A = _random_sorted(g, m, -20, 20)
+        B = _random_sorted(g, n, -20, 20)
+        Av, Bv = tags(m, n)
+        ref = list(heapq.merge(zip(A.tolist(), Av.tolist()),
+                               zip(B.tolist(), Bv.tolist()),
+                               key=lambda p: p[0]))
+        Ck, Cv = orc.merge_kv(A, Av, B, Bv)
+        assert Ck.tolist() == [p[0] for p in ref]
+        assert Cv.tolist() == [p[1] for p in ref]
+
+
+def pin_rank_scatter(orc, seed: int = 13, cases: int = 20) -> None:
+    """Each element's output position from its rank in the other array."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    for c in range(cases):
+        m, n = (int(x) for x in g.integers(0, 50000, size=2))
+        span = int(g.choice([16, 1000, 1 << 31]))
+        A = _random_sorted(g, m, -span, span)
+        B = _random_sorted(g, n, -span, span)
+        pos_a = np.arange(m) + np.searchsorted(B, A, side="left")
+        pos_b = np.arange(n) + np.searchsorted(A, B, side="right")
+        Rk = np.empty(m + n, dtype=np.int32)
+        Rv = np.empty(m + n, dtype=np.uint32)
+        Av, Bv = tags(m, n)
+        Rk[pos_a], Rv[pos_a] = A, Av
+        Rk[pos_b], Rv[pos_b] = B, Bv
+        Ck, Cv = orc.merge_kv(A, Av, B, Bv)
+        assert np.array_equal(Ck, Rk) and np.array_equal(Cv, Rv)
+        # co-rank from the scatter: #A among the first k outputs
+        I = orc.co_rank_all(A, B)
+        marks = np.zeros(m + n, dtype=np.int64)
+        marks[pos_a] = 1
+        assert np.array_equal(I, np.concatenate([[0], np.cumsum(marks)]))
+
+
+# ------------------------------------------------------------- closed forms
+
+def pin_even_odd_closed_form(orc) -> None:
+    """merge_path.cu's workload: A = 0,2,4,.. (m = 2^21+611), B = 1,3,5,..
+    (n = 2^21).  Then C[k] = k for k < 2^22 and C[2^22 + r] = 2^22 + 2r for
+    r < 611; co_rank(k) = ceil(k/2) for k <= 2^22 and k - 2^21 beyond."""
+    m, n = (1 << 21) + 611, 1 << 21
+    A = (2 * np.arange(m, dtype=np.int64)).astype(np.int32)
+    B = (2 * np.arange(n, dtype=np.int64) + 1).astype(np.int32)
+    C = orc.merge_i32(A, B)
+    h = 1 << 22
+    assert np.array_equal(C[:h], np.arange(h, dtype=np.int32))
+    assert np.array_equal(C[h:], (h + 2 * np.arange(611)).astype(np.int32))
+    I = orc.co_rank_all(A, B)
+    k = np.arange(m + n + 1, dtype=np.int64)
+    want = np.where(k <= h, (k + 1) // 2, k - (1 << 21))
+    assert np.array_equal(I, want)
+
+
+# --------------------------------------------------------------- invariants
+
+def check_invariants(A, B, C, I) -> None:
+    """i+j=k bounds, unit steps, acceptance test, order and permutation."""
+    m, n = A.size, B.size
+    k = np.arange(m + n + 1, dtype=np.int64)
+    assert I.shape == (m + n + 1,)
+    assert np.all(I >= np.maximum(0, k - n)) and np.all(I <= np.minimum(k, m))
+    d = np.diff(I)
+    assert np.all((d == 0) | (d == 1))
+    J = k - I
+    # acceptance test of the pages at every k: A[i-1] <= B[j] and B[j-1] < A[i]
+    A64, B64 = A.astype(np.int64), B.astype(np.int64)
+    lo_ok = (I == 0) | (J == n)
+    ia, jb = np.clip(I - 1, 0, max(m - 1, 0)), np.clip(J, 0, max(n - 1, 0))
+    if m and n:
+        lo_ok |= A64[ia] <= B64[jb]
+    hi_ok = (J == 0) | (I == m)
+    ia2, jb2 = np.clip(I, 0, max(m - 1, 0)), np.clip(J - 1, 0, max(n - 1, 0))
+    if m and n:
+        hi_ok |= B64[jb2] < A64[ia2]
+    assert np.all(lo_ok) and np.all(hi_ok)
+    assert np.all(np.diff(C.astype(np.int64)) >= 0)
+    # permutation: the same multiset of keys
+    assert np.array_equal(np.sort(C), np.sort(np.concatenate([A, B])))
+    # the step of I says where each output came from
+    from_a = d == 1
+    assert np.array_equal(C[from_a], A) and np.array_equal(C[~from_a], B)
+
+
+def pin_invariants(orc, seed: int = 17, cases: int = 40) -> None:
+    g = np.random.Generator(np.random.PCG64(seed))
+    for c in range(cases):
+        m, n = (int(x) for x in g.integers(0, 3000, size=2))
+        span = int(g.choice([3, 100, 1 << 31]))
+        A = _random_sorted(g, m, -span, span)
+        B = _random_sorted(g, n, -span, span)
+        check_invariants(A, B, orc.merge_i32(A, B), orc.co_rank_all(A, B))
+
+
+def pin_kv_lexicographic(orc, m: int = 1 << 16, n: int = 1 << 16,
+                         seed: int = 19) -> None:
+    """With A payloads 0..m-1 and B payloads 2^31+0..n-1 ascending within each
+    sorted array, the stable merge is strictly increasing in (key, payload),
+    i.e. it equals a lexicographic sort of the concatenated pairs."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    A = _random_sorted(g, m, 0, 256)
+    B = _random_sorted(g, n, 0, 256)
+    Av, Bv = tags(m, n)
+    Ck, Cv = orc.merge_kv(A, Av, B, Bv)
+    order = np.lexsort((np.concatenate([Av, Bv]), np.concatenate([A, B])))
+    assert np.array_equal(Ck, np.concatenate([A, B])[order])
+    assert np.array_equal(Cv, np.concatenate([Av, Bv])[order])
+
+
+ALL_PINS = [
+    pin_worked_example,
+    pin_equal_element_case,
+    pin_exhaustive_tiny,
+    pin_random_brute,
+    pin_heapq_merge,
+    pin_rank_scatter,
+    pin_even_odd_closed_form,
+    pin_invariants,
+    pin_kv_lexicographic,
+]
+
+
+def run_all(orc) -> list:
+    """Run every pin; return the names of the pins that failed."""
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            failed.append(pin.__name__)
+    return failed

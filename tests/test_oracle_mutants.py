@@ -1,0 +1,67 @@
+"""Planted mistakes in copies of the oracle must each fail at least one pin.
+
+Each mutant is a textual change to a copy of oracle/oracle.c (a flipped tie
+rule, a transposed compare, a dropped bound, a wrong index), compiled with gcc
+into a temporary library.  The pins then run against it in a child process, so
+a mutant that reads out of bounds and crashes also counts as caught.  The real
+oracle is never modified.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+MUTANTS = {
+    "ties_b_first": ("A[i] <= B[j]", "A[i] < B[j]"),
+    "compare_transposed": ("A[i] <= B[j]", "B[j] <= A[i]"),
+    "b_exhaustion_dropped": ("    if (j >= n)\n        return 1;\n", ""),
+    "a_exhaustion_dropped": ("if (i < m && A[i] <= B[j])", "if (A[i] <= B[j])"),
+    "key_index_off_by_one": ("C[k] = A[i];", "C[k] = A[i > 0 ? i - 1 : 0];"),
+    "payload_index_off_by_one": ("Cv[k] = Av[i];", "Cv[k] = Av[i > 0 ? i - 1 : 0];"),
+    "payload_from_key": ("Cv[k] = Av[i];", "Cv[k] = (uint32_t)Ak[i];"),
+    "co_rank_shifted": ("I[k + 1] = i;", "I[k] = i;"),
+    "co_rank_counts_b": ("            ++i;\n        else\n            ++j;\n        I[k + 1] = i;",
+                         "            ++j;\n        else\n            ++i;\n        I[k + 1] = i;"),
+    "co_rank_start_one": ("I[0] = 0;", "I[0] = 1;"),
+}
+
+RUNNER = r"""
+import sys
+sys.path[:0] = [{root!r}, {tests!r}]
+import oracle, oracle_pins
+failed = oracle_pins.run_all(oracle.Oracle({lib!r}))
+print("FAILED_PINS", failed)
+sys.exit(1 if failed else 0)
+"""
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(oracle.SRC).read()
+    assert src.count(old) >= 1, "mutation site missing: %r" % old
+    mutated = src.replace(old, new)
+    assert mutated != src
+    c = tmp_path / "mutant.c"
+    c.write_text(mutated)
+    lib = str(tmp_path / "libmutant.so")
+    oracle.compile_c(str(c), lib)
+    code = RUNNER.format(root=os.path.dirname(HERE), tests=HERE, lib=lib)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True,
+                       text=True, timeout=600)
+    assert r.returncode != 0, "mutant %s passed every pin:\n%s" % (name, r.stdout)
+
+
+def test_unmutated_copy_passes(tmp_path):
+    """Control: the same harness on an unchanged copy passes every pin."""
+    lib = str(tmp_path / "libcopy.so")
+    oracle.compile_c(oracle.SRC, lib)
+    code = RUNNER.format(root=os.path.dirname(HERE), tests=HERE, lib=lib)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True,
+                       text=True, timeout=600)
+    assert r.returncode == 0, r.stdout + r.stderr
