@@ -1,0 +1,145 @@
+/*
+ * omerge.h -- C ABI of libomerge.so: stable merge of two sorted int32 arrays
+ * on an AMD Instinct MI355X (gfx950), by the co-rank method.
+ *
+ * The operation (page "Co-rank Function ... and Basic Parallel Merge Kernel",
+ * pmpp.huatsai.dev/12-merge/02, overview and "Co-rank function definition";
+ * page "merge_path.cu", gpu-preview.ayushworks.com/code/day36-merge): given A
+ * (m keys) and B (n keys), each sorted ascending by signed 32-bit compare,
+ * write C (m+n keys), the sorted sequence of all of them, where equal keys
+ * keep A's elements before B's and each array's own order.  The output rank
+ * space 0..m+n is cut into equal slices; the co-rank of a slice boundary k is
+ * the i such that A[0..i) and B[0..k-i) are exactly the first k outputs.
+ *
+ * Conventions shared by every entry point below
+ *   - Pointers to arrays are DEVICE pointers (HIP device memory, or memory the
+ *     device can address).  The caller allocates and owns every buffer,
+ *     including outputs; the library never frees a caller's buffer.
+ *   - Arrays are 4-byte aligned and contiguous.  Any 4-byte alignment works;
+ *     16-byte-aligned arrays take the vector path on every full 16 bytes.
+ *   - Lengths are int64 and must be >= 0.  A pointer may be NULL only when its
+ *     length is 0.  m + n == 0 is a no-op that returns OMERGE_OK.
+ *   - Outputs must not overlap any input (checked by address range).
+ *   - A and B must be sorted ascending.  This is NOT checked.  Unsorted input
+ *     gives an unspecified output, but the call still returns, every kernel
+ *     still terminates and no access leaves the given arrays.
+ *   - Work is enqueued on `stream` (NULL = the null stream) of the CURRENT HIP
+ *     device and the call returns before it completes, like a kernel launch.
+ *     Nothing synchronises the device.  Faults during execution surface at the
+ *     caller's next synchronisation.  Calls on different streams are
+ *     independent; the library keeps no mutable global state except a
+ *     per-thread copy of the last HIP error code and a per-device cache of the
+ *     device's compute-unit count.
+ *   - Every entry point returns an omerge_status.  The library never prints
+ *     and never exits the process.
+ *
+ * `struct ihipStream_t *` is the type HIP calls hipStream_t; it is spelled
+ * out here so that this header needs no HIP header.
+ */
+#ifndef OMERGE_H
+#define OMERGE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+
+enum omerge_status {
+    OMERGE_OK = 0,
+    OMERGE_INVALID_ARG = 1, /* bad pointer, length, alignment or overlap   */
+    OMERGE_OVERFLOW = 2,    /* sizes beyond what int64 / the grid can index */
+    OMERGE_HIP_ERROR = 3    /* a HIP call failed: see omerge_last_hip_error */
+};
+
+/*
+ * merge_i32 -- stable merge of int32 keys (the pages' operation).
+ *   A[m], B[n]  in:  sorted int32 keys (device).
+ *   C[m+n]      out: merged keys (device).
+ * Enqueues a partition kernel (one co-rank per segment boundary) and the
+ * segment merge kernel on `stream`; the partition array is stream-ordered
+ * scratch (hipMallocAsync/hipFreeAsync on `stream`).
+ */
+int merge_i32(const int32_t *A, int64_t m, const int32_t *B, int64_t n,
+              int32_t *C, struct ihipStream_t *stream);
+
+/*
+ * merge_kv -- stable merge of (int32 key, uint32 payload) pairs by key.
+ * Only keys are compared; each payload moves with its key, so on equal keys
+ * the payloads come out A's first, then B's, each in its array's order.
+ * The pages merge keys only; carrying a payload is the plain extension.
+ *   A_keys[m], A_vals[m], B_keys[n], B_vals[n]  in  (device).
+ *   C_keys[m+n], C_vals[m+n]                    out (device; must not
+ *                                                overlap each other).
+ */
+int merge_kv(const int32_t *A_keys, const uint32_t *A_vals, int64_t m,
+             const int32_t *B_keys, const uint32_t *B_vals, int64_t n,
+             int32_t *C_keys, uint32_t *C_vals, struct ihipStream_t *stream);
+
+/*
+ * omerge_co_rank -- device co-rank at arbitrary output ranks (page
+ * "Co-rank Function ...", section "Binary-Search Implementation": bounds
+ * i = min(k,m), i_low = max(0,k-n), j_low = max(0,k-m), half-step rounded up,
+ * A wins ties).
+ *   k[count]     in:  output ranks, each in [0, m+n] (device).  A rank out of
+ *                     range is clamped into it.
+ *   i_out[count] out: co-rank i of each rank; the B count is k - i (device).
+ */
+int omerge_co_rank(const int32_t *A, int64_t m, const int32_t *B, int64_t n,
+                   const int64_t *k, int64_t count, int64_t *i_out,
+                   struct ihipStream_t *stream);
+
+/*
+ * The two stages of merge_i32 / merge_kv, exposed so that a caller can hold
+ * the partition (for example to split one merge across devices by output
+ * rank, or to time the stages apart).
+ *
+ * omerge_segment_length -- the segment length (outputs per workgroup) that
+ *   merge_i32 (kv = 0) or merge_kv (kv != 0) uses on the current device for
+ *   these sizes.  Always a positive multiple of 4.  Returns -1 on bad sizes.
+ * omerge_partition_count -- number of int64 entries the partition array needs
+ *   for `total` = m+n outputs cut into segments of `seg_len`:
+ *   ceil(total/seg_len) + 1.  Returns -1 on bad sizes.
+ * omerge_partition -- part[s] = co-rank of k_s = min(s*seg_len, m+n) for
+ *   s = 0 .. ceil((m+n)/seg_len)  (pages: block-level co-rank of the tiled
+ *   kernel, page "Tiled and Circular Buffer Merge Kernel", section
+ *   "Block-Level Co-Rank").  seg_len must be a positive multiple of 4 no
+ *   larger than 2^30.  part is device memory of omerge_partition_count
+ *   entries.
+ * omerge_merge_segments_i32 / _kv -- the segment merge kernel alone, given a
+ *   partition made by omerge_partition with the same seg_len.  The partition
+ *   entries are clamped into their valid ranges before use, so a wrong
+ *   partition gives a wrong output but never an access outside the arrays.
+ */
+int64_t omerge_segment_length(int64_t m, int64_t n, int kv);
+int64_t omerge_partition_count(int64_t total, int64_t seg_len);
+int omerge_partition(const int32_t *A, int64_t m, const int32_t *B, int64_t n,
+                     int64_t seg_len, int64_t *part,
+                     struct ihipStream_t *stream);
+int omerge_merge_segments_i32(const int32_t *A, int64_t m, const int32_t *B,
+                              int64_t n, const int64_t *part, int64_t seg_len,
+                              int32_t *C, struct ihipStream_t *stream);
+int omerge_merge_segments_kv(const int32_t *A_keys, const uint32_t *A_vals,
+                             int64_t m, const int32_t *B_keys,
+                             const uint32_t *B_vals, int64_t n,
+                             const int64_t *part, int64_t seg_len,
+                             int32_t *C_keys, uint32_t *C_vals,
+                             struct ihipStream_t *stream);
+
+/* Text for an omerge_status value (static storage; never NULL). */
+const char *omerge_status_string(int status);
+
+/* The hipError_t of the last HIP call that failed on this host thread
+ * (0 if none has failed). */
+int omerge_last_hip_error(void);
+
+/* Library version as an integer: major*10000 + minor*100 + patch. */
+int omerge_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OMERGE_H */

@@ -1,0 +1,321 @@
+// omerge.hip -- host launcher and C ABI of libomerge.so (declared in
+// include/omerge.h).  Validates arguments, picks the launch geometry for the
+// current device, and enqueues the partition kernel and the segment merge
+// kernel on the caller's stream.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <mutex>
+
+#include "../../include/omerge.h"
+#include "merge_kernel.hpp"
+
+namespace omerge {
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+// Kernel shapes.  256 lanes = 4 wavefronts per workgroup.  Key-only tiles
+// hold 4096 outputs; key+payload tiles hold 2048 so both fit three
+// workgroups per CU in the 160 KB of LDS.
+constexpr int kThreads = 256;
+constexpr int kItemsI32 = 16;
+constexpr int kItemsKV = 8;
+using CfgI32 = MergeCfg<kThreads, kItemsI32, false>;
+using CfgKV = MergeCfg<kThreads, kItemsKV, true>;
+
+constexpr int64_t kMaxSegLen = int64_t(1) << 30;
+constexpr int64_t kMaxTotal = int64_t(1) << 62;
+constexpr int64_t kMaxGridBlocks = int64_t(1) << 31;  // keeps blocks*256 < 2^39
+
+thread_local hipError_t g_last_error = hipSuccess;
+
+int hip_fail(hipError_t e) {
+    g_last_error = e;
+    return OMERGE_HIP_ERROR;
+}
+
+// Per-device launch facts, filled once per device.
+struct DeviceInfo {
+    bool ready = false;
+    int cus = 0;
+    int wg_per_cu_i32 = 0;
+    int wg_per_cu_kv = 0;
+};
+constexpr int kMaxDevices = 64;
+DeviceInfo g_dev[kMaxDevices];
+std::mutex g_dev_mutex;
+
+int device_info(DeviceInfo* out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= kMaxDevices) return OMERGE_INVALID_ARG;
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    DeviceInfo& d = g_dev[dev];
+    if (!d.ready) {
+        int cus = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return hip_fail(e);
+        int a = 0, b = 0;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &a, merge_segments_kernel<kThreads, kItemsI32, false>, kThreads, 0);
+        if (e != hipSuccess) return hip_fail(e);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &b, merge_segments_kernel<kThreads, kItemsKV, true>, kThreads, 0);
+        if (e != hipSuccess) return hip_fail(e);
+        d.cus = cus > 0 ? cus : 1;
+        d.wg_per_cu_i32 = a > 0 ? a : 1;
+        d.wg_per_cu_kv = b > 0 ? b : 1;
+        d.ready = true;
+    }
+    *out = d;
+    return OMERGE_OK;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Segment length: a whole number R of tiles per workgroup.  Every segment
+// costs the same, so the kernel runs in ceil(P / slots) rounds of R tiles,
+// where P = segments and slots = workgroups resident on the chip.  Pick the
+// R in [1, 32] that wastes the least of the last round, preferring longer
+// segments (fewer co-rank searches, fewer ring prologues) on a tie.
+int64_t choose_seg_len(int64_t total, int tile, int slots) {
+    const int64_t tiles = ceil_div(total, tile);
+    int64_t best_r = 1;
+    double best_eff = -1.0;
+    for (int64_t r = 1; r <= 32; ++r) {
+        const int64_t segs = ceil_div(tiles, r);
+        const int64_t rounds = ceil_div(segs, slots);
+        const double eff = double(tiles) / double(rounds * r * slots);
+        if (eff >= best_eff * 0.999) {
+            best_eff = eff > best_eff ? eff : best_eff;
+            best_r = r;
+        }
+        if (segs == 1) break;
+    }
+    return best_r * tile;
+}
+
+bool overlaps(const void* p, int64_t pn, const void* q, int64_t qn) {
+    if (!p || !q || pn <= 0 || qn <= 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), a1 = a0 + uintptr_t(pn) * 4;
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(q), b1 = b0 + uintptr_t(qn) * 4;
+    return a0 < b1 && b0 < a1;
+}
+
+bool bad_array(const void* p, int64_t len) {
+    if (len < 0) return true;
+    if (len == 0) return false;
+    return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 3) != 0;
+}
+
+int check_sizes(int64_t m, int64_t n) {
+    if (m < 0 || n < 0) return OMERGE_INVALID_ARG;
+    if (m > kMaxTotal || n > kMaxTotal || m > kMaxTotal - n) return OMERGE_OVERFLOW;
+    return OMERGE_OK;
+}
+
+int check_seg_len(int64_t seg_len) {
+    if (seg_len <= 0 || seg_len > kMaxSegLen || (seg_len & 3) != 0) return OMERGE_INVALID_ARG;
+    return OMERGE_OK;
+}
+
+int launch_partition(const int32_t* A, int64_t m, const int32_t* B, int64_t n,
+                     int64_t seg_len, int64_t* part, hipStream_t stream) {
+    const int64_t count = ceil_div(m + n, seg_len) + 1;
+    const int64_t blocks = ceil_div(count, kThreads);
+    if (blocks > kMaxGridBlocks) return OMERGE_OVERFLOW;
+    hipLaunchKernelGGL(partition_kernel, dim3(static_cast<unsigned>(blocks)),
+                       dim3(kThreads), 0, stream, A, m, B, n, seg_len, count, part);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? OMERGE_OK : hip_fail(e);
+}
+
+template <bool KV>
+int launch_merge(const int32_t* A, const uint32_t* Av, int64_t m,
+                 const int32_t* B, const uint32_t* Bv, int64_t n,
+                 const int64_t* part, int64_t seg_len, int32_t* C,
+                 uint32_t* Cv, hipStream_t stream) {
+    const int64_t segs = ceil_div(m + n, seg_len);
+    if (segs > kMaxGridBlocks) return OMERGE_OVERFLOW;
+    constexpr int items = KV ? kItemsKV : kItemsI32;
+    hipLaunchKernelGGL((merge_segments_kernel<kThreads, items, KV>),
+                       dim3(static_cast<unsigned>(segs)), dim3(kThreads), 0, stream,
+                       A, Av, m, B, Bv, n, part, seg_len, C, Cv);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? OMERGE_OK : hip_fail(e);
+}
+
+int seg_len_for(int64_t m, int64_t n, bool kv, int64_t* seg_len) {
+    DeviceInfo d;
+    int rc = device_info(&d);
+    if (rc != OMERGE_OK) return rc;
+    const int tile = kv ? CfgKV::kTile : CfgI32::kTile;
+    const int slots = d.cus * (kv ? d.wg_per_cu_kv : d.wg_per_cu_i32);
+    *seg_len = choose_seg_len(m + n, tile, slots);
+    return OMERGE_OK;
+}
+
+// Whole merge: partition into stream-ordered scratch, then merge.
+template <bool KV>
+int merge_full(const int32_t* A, const uint32_t* Av, int64_t m,
+               const int32_t* B, const uint32_t* Bv, int64_t n, int32_t* C,
+               uint32_t* Cv, hipStream_t stream) {
+    const int64_t total = m + n;
+    if (total == 0) return OMERGE_OK;
+    int64_t seg_len = 0;
+    int rc = seg_len_for(m, n, KV, &seg_len);
+    if (rc != OMERGE_OK) return rc;
+    const int64_t count = ceil_div(total, seg_len) + 1;
+    int64_t* part = nullptr;
+    hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&part),
+                                  static_cast<size_t>(count) * sizeof(int64_t), stream);
+    if (e != hipSuccess) return hip_fail(e);
+    rc = launch_partition(A, m, B, n, seg_len, part, stream);
+    if (rc == OMERGE_OK) rc = launch_merge<KV>(A, Av, m, B, Bv, n, part, seg_len, C, Cv, stream);
+    e = hipFreeAsync(part, stream);
+    if (rc == OMERGE_OK && e != hipSuccess) rc = hip_fail(e);
+    return rc;
+}
+
+int check_i32_args(const int32_t* A, int64_t m, const int32_t* B, int64_t n,
+                   const int32_t* C) {
+    int rc = check_sizes(m, n);
+    if (rc != OMERGE_OK) return rc;
+    if (bad_array(A, m) || bad_array(B, n) || bad_array(C, m + n)) return OMERGE_INVALID_ARG;
+    if (overlaps(C, m + n, A, m) || overlaps(C, m + n, B, n)) return OMERGE_INVALID_ARG;
+    return OMERGE_OK;
+}
+
+int check_kv_args(const int32_t* Ak, const uint32_t* Av, int64_t m,
+                  const int32_t* Bk, const uint32_t* Bv, int64_t n,
+                  const int32_t* Ck, const uint32_t* Cv) {
+    int rc = check_sizes(m, n);
+    if (rc != OMERGE_OK) return rc;
+    const int64_t t = m + n;
+    if (bad_array(Ak, m) || bad_array(Av, m) || bad_array(Bk, n) || bad_array(Bv, n) ||
+        bad_array(Ck, t) || bad_array(Cv, t))
+        return OMERGE_INVALID_ARG;
+    const void* ins[4] = {Ak, Av, Bk, Bv};
+    const int64_t lens[4] = {m, m, n, n};
+    for (int i = 0; i < 4; ++i) {
+        if (overlaps(Ck, t, ins[i], lens[i]) || overlaps(Cv, t, ins[i], lens[i]))
+            return OMERGE_INVALID_ARG;
+    }
+    if (overlaps(Ck, t, Cv, t)) return OMERGE_INVALID_ARG;
+    return OMERGE_OK;
+}
+
+int check_part(const int64_t* part, int64_t total, int64_t seg_len) {
+    int rc = check_seg_len(seg_len);
+    if (rc != OMERGE_OK) return rc;
+    if (total > 0 && (part == nullptr || (reinterpret_cast<uintptr_t>(part) & 7) != 0))
+        return OMERGE_INVALID_ARG;
+    return OMERGE_OK;
+}
+
+}  // namespace
+}  // namespace omerge
+
+using namespace omerge;
+
+extern "C" {
+
+int merge_i32(const int32_t* A, int64_t m, const int32_t* B, int64_t n,
+              int32_t* C, hipStream_t stream) {
+    int rc = check_i32_args(A, m, B, n, C);
+    if (rc != OMERGE_OK) return rc;
+    return merge_full<false>(A, nullptr, m, B, nullptr, n, C, nullptr, stream);
+}
+
+int merge_kv(const int32_t* A_keys, const uint32_t* A_vals, int64_t m,
+             const int32_t* B_keys, const uint32_t* B_vals, int64_t n,
+             int32_t* C_keys, uint32_t* C_vals, hipStream_t stream) {
+    int rc = check_kv_args(A_keys, A_vals, m, B_keys, B_vals, n, C_keys, C_vals);
+    if (rc != OMERGE_OK) return rc;
+    return merge_full<true>(A_keys, A_vals, m, B_keys, B_vals, n, C_keys, C_vals, stream);
+}
+
+int omerge_co_rank(const int32_t* A, int64_t m, const int32_t* B, int64_t n,
+                   const int64_t* k, int64_t count, int64_t* i_out,
+                   hipStream_t stream) {
+    int rc = check_sizes(m, n);
+    if (rc != OMERGE_OK) return rc;
+    if (count < 0 || bad_array(A, m) || bad_array(B, n)) return OMERGE_INVALID_ARG;
+    if (count == 0) return OMERGE_OK;
+    if (k == nullptr || i_out == nullptr || (reinterpret_cast<uintptr_t>(k) & 7) ||
+        (reinterpret_cast<uintptr_t>(i_out) & 7))
+        return OMERGE_INVALID_ARG;
+    const int64_t blocks = ceil_div(count, kThreads);
+    if (blocks > kMaxGridBlocks) return OMERGE_OVERFLOW;
+    hipLaunchKernelGGL(co_rank_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
+                       0, stream, A, m, B, n, k, count, i_out);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? OMERGE_OK : hip_fail(e);
+}
+
+int64_t omerge_segment_length(int64_t m, int64_t n, int kv) {
+    if (check_sizes(m, n) != OMERGE_OK) return -1;
+    int64_t seg_len = 0;
+    if (seg_len_for(m, n, kv != 0, &seg_len) != OMERGE_OK) return -1;
+    return seg_len;
+}
+
+int64_t omerge_partition_count(int64_t total, int64_t seg_len) {
+    if (total < 0 || total > kMaxTotal || check_seg_len(seg_len) != OMERGE_OK) return -1;
+    return ceil_div(total, seg_len) + 1;
+}
+
+int omerge_partition(const int32_t* A, int64_t m, const int32_t* B, int64_t n,
+                     int64_t seg_len, int64_t* part, hipStream_t stream) {
+    int rc = check_sizes(m, n);
+    if (rc != OMERGE_OK) return rc;
+    if (bad_array(A, m) || bad_array(B, n)) return OMERGE_INVALID_ARG;
+    rc = check_seg_len(seg_len);
+    if (rc != OMERGE_OK) return rc;
+    if (part == nullptr || (reinterpret_cast<uintptr_t>(part) & 7)) return OMERGE_INVALID_ARG;
+    return launch_partition(A, m, B, n, seg_len, part, stream);
+}
+
+int omerge_merge_segments_i32(const int32_t* A, int64_t m, const int32_t* B,
+                              int64_t n, const int64_t* part, int64_t seg_len,
+                              int32_t* C, hipStream_t stream) {
+    int rc = check_i32_args(A, m, B, n, C);
+    if (rc != OMERGE_OK) return rc;
+    rc = check_part(part, m + n, seg_len);
+    if (rc != OMERGE_OK) return rc;
+    if (m + n == 0) return OMERGE_OK;
+    return launch_merge<false>(A, nullptr, m, B, nullptr, n, part, seg_len, C, nullptr, stream);
+}
+
+int omerge_merge_segments_kv(const int32_t* A_keys, const uint32_t* A_vals,
+                             int64_t m, const int32_t* B_keys,
+                             const uint32_t* B_vals, int64_t n,
+                             const int64_t* part, int64_t seg_len,
+                             int32_t* C_keys, uint32_t* C_vals,
+                             hipStream_t stream) {
+    int rc = check_kv_args(A_keys, A_vals, m, B_keys, B_vals, n, C_keys, C_vals);
+    if (rc != OMERGE_OK) return rc;
+    rc = check_part(part, m + n, seg_len);
+    if (rc != OMERGE_OK) return rc;
+    if (m + n == 0) return OMERGE_OK;
+    return launch_merge<true>(A_keys, A_vals, m, B_keys, B_vals, n, part, seg_len, C_keys,
+                              C_vals, stream);
+}
+
+const char* omerge_status_string(int status) {
+    switch (status) {
+        case OMERGE_OK: return "ok";
+        case OMERGE_INVALID_ARG: return "invalid argument";
+        case OMERGE_OVERFLOW: return "size overflow";
+        case OMERGE_HIP_ERROR: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+int omerge_last_hip_error(void) { return static_cast<int>(g_last_error); }
+
+int omerge_version(void) { return kVersion; }
+
+}  // extern "C"

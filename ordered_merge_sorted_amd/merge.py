@@ -1,0 +1,245 @@
+"""Python binding of libomerge.so: argument marshalling only.
+
+Every function checks its tensors (dtype, device, layout), allocates outputs
+with torch when none are given, and calls the C ABI declared in
+include/omerge.h on the tensors' device and the current torch stream (or the
+stream given).  All work runs in the library's HIP kernels; nothing here
+computes.  If the library is missing or fails to load, every call raises
+OmergeError: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+from .build import LIB
+
+OK, INVALID_ARG, OVERFLOW, HIP_ERROR = 0, 1, 2, 3
+
+
+class OmergeError(RuntimeError):
+    """A libomerge call failed, or the library could not be loaded."""
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return LIB
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libomerge.so (once).  Raises OmergeError if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB):
+        raise OmergeError(
+            "libomerge.so is not built at %s; build it with "
+            "`python -m ordered_merge_sorted_amd.build`" % LIB)
+    try:
+        lib = ctypes.CDLL(LIB)
+    except OSError as e:
+        raise OmergeError("cannot load %s: %s" % (LIB, e)) from e
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    sig = {
+        "merge_i32": (i32, [p, i64, p, i64, p, p]),
+        "merge_kv": (i32, [p, p, i64, p, p, i64, p, p, p]),
+        "omerge_co_rank": (i32, [p, i64, p, i64, p, i64, p, p]),
+        "omerge_segment_length": (i64, [i64, i64, i32]),
+        "omerge_partition_count": (i64, [i64, i64]),
+        "omerge_partition": (i32, [p, i64, p, i64, i64, p, p]),
+        "omerge_merge_segments_i32": (i32, [p, i64, p, i64, p, i64, p, p]),
+        "omerge_merge_segments_kv": (i32, [p, p, i64, p, p, i64, p, i64, p, p, p]),
+        "omerge_status_string": (ctypes.c_char_p, [i32]),
+        "omerge_last_hip_error": (i32, []),
+        "omerge_version": (i32, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _raise_on(rc: int, what: str) -> None:
+    if rc == OK:
+        return
+    lib = load_library()
+    msg = lib.omerge_status_string(rc).decode()
+    if rc == HIP_ERROR:
+        msg += " (hipError_t %d)" % lib.omerge_last_hip_error()
+    raise OmergeError("%s failed: %s" % (what, msg))
+
+
+_PAYLOAD_DTYPES = (torch.int32, getattr(torch, "uint32", torch.int32))
+
+
+def _vec(t: torch.Tensor, name: str, dtypes, device=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype not in dtypes:
+        raise TypeError("%s must have dtype %s, got %s" % (name, " or ".join(map(str, dtypes)), t.dtype))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU, got %s" % (name, t.device))
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if t.dim() != 1:
+        raise ValueError("%s must be 1-D" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _ptr(t: torch.Tensor):
+    return ctypes.c_void_p(t.data_ptr() if t.numel() else 0)
+
+
+def _stream(device: torch.device, stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _out(out, n: int, dtype, device, name: str) -> torch.Tensor:
+    if out is None:
+        return torch.empty(n, dtype=dtype, device=device)
+    _vec(out, name, (dtype,), device)
+    if out.numel() != n:
+        raise ValueError("%s must have %d elements, got %d" % (name, n, out.numel()))
+    return out
+
+
+def merge_i32(a: torch.Tensor, b: torch.Tensor, out: Optional[torch.Tensor] = None,
+              stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Stable merge of sorted int32 tensors a and b (equal keys: a first)."""
+    _vec(a, "a", (torch.int32,))
+    _vec(b, "b", (torch.int32,), a.device)
+    out = _out(out, a.numel() + b.numel(), torch.int32, a.device, "out")
+    lib = load_library()
+    with torch.cuda.device(a.device):
+        rc = lib.merge_i32(_ptr(a), a.numel(), _ptr(b), b.numel(), _ptr(out),
+                           _stream(a.device, stream))
+    _raise_on(rc, "merge_i32")
+    return out
+
+
+def merge_kv(a_keys: torch.Tensor, a_vals: torch.Tensor, b_keys: torch.Tensor,
+             b_vals: torch.Tensor, out_keys: Optional[torch.Tensor] = None,
+             out_vals: Optional[torch.Tensor] = None,
+             stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Stable merge of (int32 key, 32-bit payload) pairs by key; payloads are
+    never compared and move with their keys (a's first on equal keys)."""
+    dev = a_keys.device if isinstance(a_keys, torch.Tensor) else None
+    _vec(a_keys, "a_keys", (torch.int32,))
+    _vec(b_keys, "b_keys", (torch.int32,), dev)
+    _vec(a_vals, "a_vals", _PAYLOAD_DTYPES, dev)
+    _vec(b_vals, "b_vals", (a_vals.dtype,), dev)
+    if a_vals.numel() != a_keys.numel() or b_vals.numel() != b_keys.numel():
+        raise ValueError("key and payload lengths differ")
+    t = a_keys.numel() + b_keys.numel()
+    out_keys = _out(out_keys, t, torch.int32, dev, "out_keys")
+    out_vals = _out(out_vals, t, a_vals.dtype, dev, "out_vals")
+    lib = load_library()
+    with torch.cuda.device(dev):
+        rc = lib.merge_kv(_ptr(a_keys), _ptr(a_vals), a_keys.numel(), _ptr(b_keys),
+                          _ptr(b_vals), b_keys.numel(), _ptr(out_keys), _ptr(out_vals),
+                          _stream(dev, stream))
+    _raise_on(rc, "merge_kv")
+    return out_keys, out_vals
+
+
+def co_rank(a: torch.Tensor, b: torch.Tensor, k: torch.Tensor,
+            out: Optional[torch.Tensor] = None,
+            stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Device co-rank i(k) for each int64 output rank in k (clamped to [0, m+n])."""
+    _vec(a, "a", (torch.int32,))
+    _vec(b, "b", (torch.int32,), a.device)
+    _vec(k, "k", (torch.int64,), a.device)
+    out = _out(out, k.numel(), torch.int64, a.device, "out")
+    lib = load_library()
+    with torch.cuda.device(a.device):
+        rc = lib.omerge_co_rank(_ptr(a), a.numel(), _ptr(b), b.numel(), _ptr(k), k.numel(),
+                                _ptr(out), _stream(a.device, stream))
+    _raise_on(rc, "omerge_co_rank")
+    return out
+
+
+def segment_length(m: int, n: int, kv: bool = False, device=None) -> int:
+    """Outputs per workgroup that merge_i32 / merge_kv use for these sizes."""
+    lib = load_library()
+    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+        s = lib.omerge_segment_length(int(m), int(n), int(bool(kv)))
+    if s <= 0:
+        raise OmergeError("omerge_segment_length failed for m=%d n=%d" % (m, n))
+    return int(s)
+
+
+def partition_count(total: int, seg_len: int) -> int:
+    c = load_library().omerge_partition_count(int(total), int(seg_len))
+    if c < 0:
+        raise OmergeError("bad sizes for a partition: total=%d seg_len=%d" % (total, seg_len))
+    return int(c)
+
+
+def partition(a: torch.Tensor, b: torch.Tensor, seg_len: int,
+              out: Optional[torch.Tensor] = None,
+              stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """int64 co-ranks of the segment boundaries k_s = min(s*seg_len, m+n)."""
+    _vec(a, "a", (torch.int32,))
+    _vec(b, "b", (torch.int32,), a.device)
+    count = partition_count(a.numel() + b.numel(), seg_len)
+    out = _out(out, count, torch.int64, a.device, "out")
+    lib = load_library()
+    with torch.cuda.device(a.device):
+        rc = lib.omerge_partition(_ptr(a), a.numel(), _ptr(b), b.numel(), int(seg_len),
+                                  _ptr(out), _stream(a.device, stream))
+    _raise_on(rc, "omerge_partition")
+    return out
+
+
+def merge_segments_i32(a: torch.Tensor, b: torch.Tensor, part: torch.Tensor, seg_len: int,
+                       out: Optional[torch.Tensor] = None,
+                       stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """The segment merge kernel alone, given partition(a, b, seg_len)."""
+    _vec(a, "a", (torch.int32,))
+    _vec(b, "b", (torch.int32,), a.device)
+    _vec(part, "part", (torch.int64,), a.device)
+    if part.numel() != partition_count(a.numel() + b.numel(), seg_len):
+        raise ValueError("part has the wrong length for seg_len")
+    out = _out(out, a.numel() + b.numel(), torch.int32, a.device, "out")
+    lib = load_library()
+    with torch.cuda.device(a.device):
+        rc = lib.omerge_merge_segments_i32(_ptr(a), a.numel(), _ptr(b), b.numel(), _ptr(part),
+                                           int(seg_len), _ptr(out), _stream(a.device, stream))
+    _raise_on(rc, "omerge_merge_segments_i32")
+    return out
+
+
+def merge_segments_kv(a_keys, a_vals, b_keys, b_vals, part, seg_len, out_keys=None,
+                      out_vals=None, stream=None):
+    """The key+payload segment merge kernel alone, given a partition."""
+    dev = a_keys.device if isinstance(a_keys, torch.Tensor) else None
+    _vec(a_keys, "a_keys", (torch.int32,))
+    _vec(b_keys, "b_keys", (torch.int32,), dev)
+    _vec(a_vals, "a_vals", _PAYLOAD_DTYPES, dev)
+    _vec(b_vals, "b_vals", (a_vals.dtype,), dev)
+    _vec(part, "part", (torch.int64,), dev)
+    if a_vals.numel() != a_keys.numel() or b_vals.numel() != b_keys.numel():
+        raise ValueError("key and payload lengths differ")
+    t = a_keys.numel() + b_keys.numel()
+    if part.numel() != partition_count(t, seg_len):
+        raise ValueError("part has the wrong length for seg_len")
+    out_keys = _out(out_keys, t, torch.int32, dev, "out_keys")
+    out_vals = _out(out_vals, t, a_vals.dtype, dev, "out_vals")
+    lib = load_library()
+    with torch.cuda.device(dev):
+        rc = lib.omerge_merge_segments_kv(
+            _ptr(a_keys), _ptr(a_vals), a_keys.numel(), _ptr(b_keys), _ptr(b_vals),
+            b_keys.numel(), _ptr(part), int(seg_len), _ptr(out_keys), _ptr(out_vals),
+            _stream(dev, stream))
+    _raise_on(rc, "omerge_merge_segments_kv")
+    return out_keys, out_vals

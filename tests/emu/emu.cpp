@@ -1,0 +1,93 @@
+// CPU emulation of the HIP kernels, for tests only.  It compiles the product
+// kernel headers unchanged against the stand-in HIP header next to it and
+// runs each workgroup as THREADS host threads that meet at a std::barrier.
+// Workgroups run one after another.  Exposes extern "C" entry points that the
+// tests call through ctypes.
+#include <barrier>
+#include <functional>
+#include <thread>
+#include <vector>
+
+#include "hip/hip_runtime.h"
+#include "merge_kernel.hpp"
+
+thread_local EmuDim3 threadIdx;
+thread_local EmuDim3 blockIdx;
+EmuDim3 blockDim;
+EmuDim3 gridDim;
+
+static std::barrier<>* g_barrier = nullptr;
+void __syncthreads() { g_barrier->arrive_and_wait(); }
+
+// Runs `body` for every workgroup 0..blocks-1 with `threads` lanes each.
+static void run_grid(int64_t blocks, int threads, const std::function<void()>& body) {
+    std::barrier<> bar(threads);
+    g_barrier = &bar;
+    blockDim = {static_cast<unsigned>(threads), 1, 1};
+    gridDim = {static_cast<unsigned>(blocks), 1, 1};
+    std::vector<std::thread> pool;
+    for (int t = 0; t < threads; ++t) {
+        pool.emplace_back([&, t] {
+            threadIdx = {static_cast<unsigned>(t), 0, 0};
+            for (int64_t b = 0; b < blocks; ++b) {
+                blockIdx = {static_cast<unsigned>(b), 0, 0};
+                body();
+                bar.arrive_and_wait();  // the workgroup is done before the next starts
+            }
+        });
+    }
+    for (auto& th : pool) th.join();
+    g_barrier = nullptr;
+}
+
+template <int T, int I, bool KV>
+static void merge_cfg(const int32_t* A, const uint32_t* Av, int64_t m, const int32_t* B,
+                      const uint32_t* Bv, int64_t n, const int64_t* part, int64_t seg_len,
+                      int32_t* C, uint32_t* Cv) {
+    const int64_t segs = (m + n + seg_len - 1) / seg_len;
+    run_grid(segs, T, [&] {
+        omerge::merge_segments_kernel<T, I, KV>(A, Av, m, B, Bv, n, part, seg_len, C, Cv);
+    });
+}
+
+extern "C" {
+
+// variant 0 = the shapes the library launches; 1 = small shapes (64 lanes,
+// 4 items) that wrap the rings many times on small inputs.
+int emu_tile(int variant, int kv) {
+    if (variant == 0) return kv ? omerge::MergeCfg<256, 8, true>::kTile
+                                : omerge::MergeCfg<256, 16, false>::kTile;
+    return omerge::MergeCfg<64, 4, false>::kTile;
+}
+
+void emu_partition(const int32_t* A, int64_t m, const int32_t* B, int64_t n, int64_t seg_len,
+                   int64_t* part) {
+    const int64_t count = (m + n + seg_len - 1) / seg_len + 1;
+    const int64_t blocks = (count + 255) / 256;
+    run_grid(blocks, 256, [&] { omerge::partition_kernel(A, m, B, n, seg_len, count, part); });
+}
+
+void emu_co_rank(const int32_t* A, int64_t m, const int32_t* B, int64_t n, const int64_t* ks,
+                 int64_t count, int64_t* out) {
+    const int64_t blocks = (count + 255) / 256;
+    run_grid(blocks, 256, [&] { omerge::co_rank_kernel(A, m, B, n, ks, count, out); });
+}
+
+void emu_merge_i32(int variant, const int32_t* A, int64_t m, const int32_t* B, int64_t n,
+                   const int64_t* part, int64_t seg_len, int32_t* C) {
+    if (variant == 0)
+        merge_cfg<256, 16, false>(A, nullptr, m, B, nullptr, n, part, seg_len, C, nullptr);
+    else
+        merge_cfg<64, 4, false>(A, nullptr, m, B, nullptr, n, part, seg_len, C, nullptr);
+}
+
+void emu_merge_kv(int variant, const int32_t* A, const uint32_t* Av, int64_t m, const int32_t* B,
+                  const uint32_t* Bv, int64_t n, const int64_t* part, int64_t seg_len, int32_t* C,
+                  uint32_t* Cv) {
+    if (variant == 0)
+        merge_cfg<256, 8, true>(A, Av, m, B, Bv, n, part, seg_len, C, Cv);
+    else
+        merge_cfg<64, 4, true>(A, Av, m, B, Bv, n, part, seg_len, C, Cv);
+}
+
+}  // extern "C"

@@ -1,0 +1,26 @@
+// Stand-in for <hip/hip_runtime.h> used ONLY by the CPU emulation of the
+// kernels (tests/emu/emu.cpp).  It lets the unmodified kernel headers compile
+// as host C++: every lane becomes a std::thread, __shared__ memory becomes a
+// static array shared by the workgroup's threads, and __syncthreads() is a
+// real barrier.  Built with AddressSanitizer and UBSan, an out-of-bounds or
+// misaligned access in the kernel logic becomes a CPU error report.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#define __global__
+#define __device__
+#define __host__
+#define __forceinline__ inline
+#define __launch_bounds__(...)
+#define __shared__ static
+#define __builtin_amdgcn_readfirstlane(x) (x)
+
+struct EmuDim3 {
+    unsigned x, y, z;
+};
+extern thread_local EmuDim3 threadIdx;
+extern thread_local EmuDim3 blockIdx;
+extern EmuDim3 blockDim;
+extern EmuDim3 gridDim;
+void __syncthreads();

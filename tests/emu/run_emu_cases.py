@@ -1,0 +1,200 @@
+"""Runs the CPU emulation of the HIP kernels (libemu.so, built with ASan and
+UBSan) on seeded cases and compares every output with the oracle.
+
+Started by tests/test_kernel_emulation.py in a child process whose
+LD_PRELOAD holds the sanitizer runtime; any out-of-bounds or misaligned
+access aborts the child.  Exit status 0 = every case matched.
+
+usage: run_emu_cases.py LIBEMU GROUP
+"""
+import ctypes
+import os
+import sys
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path[:0] = [os.path.dirname(os.path.dirname(HERE))]
+import oracle  # noqa: E402
+
+U31 = np.uint32(1 << 31)
+
+
+def load(path):
+    lib = ctypes.CDLL(path)
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.emu_tile.argtypes = [i32, i32]
+    lib.emu_tile.restype = i32
+    lib.emu_partition.argtypes = [p, i64, p, i64, i64, p]
+    lib.emu_co_rank.argtypes = [p, i64, p, i64, p, i64, p]
+    lib.emu_merge_i32.argtypes = [i32, p, i64, p, i64, p, i64, p]
+    lib.emu_merge_kv.argtypes = [i32, p, p, i64, p, p, i64, p, i64, p, p]
+    return lib
+
+
+def placed(x, off):
+    """Copy of x whose data pointer is `off` 4-byte words past a 64-byte
+    boundary, so every address phase is exercised."""
+    buf = np.empty(x.size + 32, dtype=x.dtype)
+    base = (-(buf.ctypes.data // 4)) % 16
+    v = buf[base + off: base + off + x.size]
+    v[...] = x
+    return v
+
+
+def ptr(x):
+    return ctypes.c_void_p(x.ctypes.data) if x.size else ctypes.c_void_p(0)
+
+
+def sorted_pair(g, m, n, span):
+    """Sorted A (m) and B (n) drawn from one shared value window of `span`
+    values, so small spans give many ties across the two arrays."""
+    if span >= 1 << 32:
+        lo, hi = -(1 << 31), 1 << 31
+    else:
+        lo = int(g.integers(-(1 << 31), (1 << 31) - span))
+        hi = lo + span
+    A = np.sort(g.integers(lo, hi, size=m, dtype=np.int64)).astype(np.int32)
+    B = np.sort(g.integers(lo, hi, size=n, dtype=np.int64)).astype(np.int32)
+    return A, B
+
+
+class Runner:
+    def __init__(self, lib):
+        self.lib = lib
+        self.fail = 0
+        self.cases = 0
+
+    def check(self, ok, what):
+        self.cases += 1
+        if not ok:
+            self.fail += 1
+            print("MISMATCH", what, flush=True)
+
+    def partition(self, A, B, seg_len):
+        count = (A.size + B.size + seg_len - 1) // seg_len + 1
+        part = np.full(count, -7, dtype=np.int64)
+        self.lib.emu_partition(ptr(A), A.size, ptr(B), B.size, seg_len, ptr(part))
+        return part
+
+    def case_i32(self, variant, A, B, seg_len, offs=(0, 0, 0), label=""):
+        m, n = A.size, B.size
+        Ap, Bp = placed(A, offs[0]), placed(B, offs[1])
+        part = self.partition(Ap, Bp, seg_len)
+        I = oracle.co_rank_all(A, B)
+        ks = np.minimum(np.arange(part.size, dtype=np.int64) * seg_len, m + n)
+        self.check(np.array_equal(part, I[ks]), ("partition", label, m, n, seg_len))
+        C = placed(np.full(m + n, 12345, dtype=np.int32), offs[2])
+        if m + n:
+            self.lib.emu_merge_i32(variant, ptr(Ap), m, ptr(Bp), n, ptr(part), seg_len, ptr(C))
+        want = oracle.merge_i32(A, B)
+        ok = np.array_equal(C, want)
+        if not ok:
+            bad = int(np.argmax(C != want))
+            label = (label, "first diff", bad, int(C[bad]), int(want[bad]))
+        self.check(ok, ("merge_i32", variant, label, m, n, seg_len, offs))
+
+    def case_kv(self, variant, A, B, seg_len, offs=(0, 0, 0, 0, 0, 0), label=""):
+        m, n = A.size, B.size
+        Av = np.arange(m, dtype=np.uint32)
+        Bv = (U31 + np.arange(n, dtype=np.uint32)).astype(np.uint32)
+        Ap, Avp, Bp, Bvp = placed(A, offs[0]), placed(Av, offs[1]), placed(B, offs[2]), placed(Bv, offs[3])
+        part = self.partition(Ap, Bp, seg_len)
+        Ck = placed(np.zeros(m + n, dtype=np.int32), offs[4])
+        Cv = placed(np.zeros(m + n, dtype=np.uint32), offs[5])
+        if m + n:
+            self.lib.emu_merge_kv(variant, ptr(Ap), ptr(Avp), m, ptr(Bp), ptr(Bvp), n,
+                                  ptr(part), seg_len, ptr(Ck), ptr(Cv))
+        wk, wv = oracle.merge_kv(A, Av, B, Bv)
+        self.check(np.array_equal(Ck, wk) and np.array_equal(Cv, wv),
+                   ("merge_kv", variant, label, m, n, seg_len, offs))
+
+    def case_co_rank(self, A, B):
+        ks = np.arange(A.size + B.size + 1, dtype=np.int64)
+        out = np.zeros_like(ks)
+        self.lib.emu_co_rank(ptr(A), A.size, ptr(B), B.size, ptr(ks), ks.size, ptr(out))
+        self.check(np.array_equal(out, oracle.co_rank_all(A, B)), ("co_rank", A.size, B.size))
+
+
+def group_small(r, g):
+    """64-lane, 4-item shapes (tile 256): many ring wraps on small inputs."""
+    tile = r.lib.emu_tile(1, 0)
+    for c in range(60):
+        m, n = (int(x) for x in g.integers(0, 2500, size=2))
+        if c % 10 == 0:
+            m = 0
+        if c % 10 == 1:
+            n = 0
+        span = int(g.choice([2, 16, 1000, 1 << 32]))
+        A, B = sorted_pair(g, m, n, span)
+        seg_len = int(g.choice([tile, 2 * tile, 3 * tile, 4 * int(g.integers(1, 300))]))
+        offs = tuple(int(x) for x in g.integers(0, 4, size=6))
+        r.case_i32(1, A, B, seg_len, offs[:3], "small")
+        r.case_kv(1, A, B, seg_len, offs, "small")
+        if m + n <= 400:
+            r.case_co_rank(A, B)
+
+
+def group_skew(r, g):
+    """One side dense, the other packed in a narrow interval: tiles swing
+    between all-A and mostly-B, and one ring drains while the other fills."""
+    tile = r.lib.emu_tile(1, 0)
+    for c in range(12):
+        m = int(g.integers(2000, 6000))
+        n = int(g.integers(0, 600))
+        A = np.sort(g.integers(0, 1 << 20, size=m)).astype(np.int32)
+        lo = int(g.integers(0, 1 << 20))
+        B = np.sort(g.integers(lo, lo + 64, size=n)).astype(np.int32)
+        if c % 2:
+            A, B = B, A
+        seg_len = int(g.choice([tile, 5 * tile, 4 * int(g.integers(1, 700))]))
+        r.case_i32(1, A, B, seg_len, tuple(int(x) for x in g.integers(0, 4, size=3)), "skew")
+        r.case_kv(1, A, B, seg_len, tuple(int(x) for x in g.integers(0, 4, size=6)), "skew")
+
+
+def group_production(r, g):
+    """The shapes the library launches (256 lanes; 4096-output tiles for
+    keys, 2048 for key+payload), over several tiles and segments."""
+    for kv in (False, True):
+        tile = r.lib.emu_tile(0, int(kv))
+        for c in range(4):
+            m = int(g.integers(0, 7 * tile))
+            n = int(g.integers(0, 7 * tile))
+            span = int(g.choice([4, 300, 1 << 32]))
+            A, B = sorted_pair(g, m, n, span)
+            seg_len = [tile, 3 * tile, 2 * tile + 1364, 4 * tile][c]
+            if kv:
+                r.case_kv(0, A, B, seg_len, tuple(int(x) for x in g.integers(0, 4, size=6)), "prod")
+            else:
+                r.case_i32(0, A, B, seg_len, tuple(int(x) for x in g.integers(0, 4, size=3)), "prod")
+
+
+def group_unsorted(r, g):
+    """Unsorted input breaks the precondition: the kernels must still stop
+    and stay inside the arrays (the sanitizers watch every access)."""
+    tile = r.lib.emu_tile(1, 0)
+    for c in range(15):
+        m, n = (int(x) for x in g.integers(0, 1500, size=2))
+        A = g.integers(-50, 50, size=m).astype(np.int32)
+        B = g.integers(-50, 50, size=n).astype(np.int32)
+        seg_len = int(g.choice([tile, 3 * tile, 4 * int(g.integers(1, 200))]))
+        part = r.partition(A, B, seg_len)
+        C = np.zeros(m + n, dtype=np.int32)
+        if m + n:
+            r.lib.emu_merge_i32(1, ptr(A), m, ptr(B), n, ptr(part), seg_len, ptr(C))
+        # a nonsense partition must not take the kernel out of bounds either
+        junk = g.integers(-(1 << 40), 1 << 40, size=part.size).astype(np.int64)
+        if m + n:
+            r.lib.emu_merge_i32(1, ptr(A), m, ptr(B), n, ptr(junk), seg_len, ptr(C))
+        r.cases += 1
+
+
+GROUPS = {"small": group_small, "skew": group_skew,
+          "production": group_production, "unsorted": group_unsorted}
+
+if __name__ == "__main__":
+    lib = load(sys.argv[1])
+    r = Runner(lib)
+    GROUPS[sys.argv[2]](r, np.random.Generator(np.random.PCG64(4242)))
+    print("cases", r.cases, "failures", r.fail, flush=True)
+    sys.exit(1 if r.fail else 0)

@@ -1,0 +1,140 @@
+"""The C ABI library on the CPU: it loads, exports every function that
+include/omerge.h declares, and rejects bad arguments before touching a
+device.  No call here launches work."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import ordered_merge_sorted_amd as om
+from ordered_merge_sorted_amd import merge as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "omerge.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \t\*]*?\b([A-Za-z_]\w*)\s*\(", text, flags=re.M)
+    return sorted(set(names) - {"defined"})
+
+
+def test_header_declares_the_api():
+    names = declared_functions()
+    for want in ("merge_i32", "merge_kv", "omerge_co_rank", "omerge_partition",
+                 "omerge_merge_segments_i32", "omerge_merge_segments_kv",
+                 "omerge_status_string"):
+        assert want in names, names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = om.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", om.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = set(declared_functions()) - exported
+    assert not missing, missing
+
+
+def test_header_compiles_as_c():
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", HEADER],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_status_strings_and_version():
+    lib = om.load_library()
+    assert lib.omerge_status_string(0) == b"ok"
+    assert lib.omerge_status_string(1) == b"invalid argument"
+    assert lib.omerge_status_string(2) == b"size overflow"
+    assert lib.omerge_status_string(3) == b"HIP error"
+    assert lib.omerge_status_string(99) == b"unknown status"
+    assert lib.omerge_version() >= 100
+    assert lib.omerge_last_hip_error() == 0
+
+
+def test_partition_count():
+    assert om.partition_count(0, 4096) == 1
+    assert om.partition_count(1, 4096) == 2
+    assert om.partition_count(4096, 4096) == 2
+    assert om.partition_count(4097, 4096) == 3
+    assert om.partition_count(1 << 29, 87384) == 6145
+    lib = om.load_library()
+    assert lib.omerge_partition_count(100, 6) == -1       # not a multiple of 4
+    assert lib.omerge_partition_count(100, 0) == -1
+    assert lib.omerge_partition_count(-1, 4096) == -1
+    assert lib.omerge_partition_count(100, (1 << 30) + 4) == -1
+
+
+FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation
+
+
+def P(x):
+    return ctypes.c_void_p(x)
+
+
+@pytest.mark.parametrize("args,want", [
+    ((P(0), 5, P(FAKE), 5, P(FAKE + 4096)), M.INVALID_ARG),          # A NULL, m > 0
+    ((P(FAKE), 5, P(0), 5, P(FAKE + 4096)), M.INVALID_ARG),          # B NULL, n > 0
+    ((P(FAKE), 5, P(FAKE + 64), 5, P(0)), M.INVALID_ARG),            # C NULL
+    ((P(FAKE), -1, P(FAKE), 5, P(FAKE + 4096)), M.INVALID_ARG),      # negative m
+    ((P(FAKE), 5, P(FAKE), -3, P(FAKE + 4096)), M.INVALID_ARG),      # negative n
+    ((P(FAKE + 2), 5, P(FAKE + 64), 5, P(FAKE + 4096)), M.INVALID_ARG),  # misaligned A
+    ((P(FAKE), 5, P(FAKE + 64), 5, P(FAKE + 4097)), M.INVALID_ARG),  # misaligned C
+    ((P(FAKE), 5, P(FAKE + 64), 5, P(FAKE + 8)), M.INVALID_ARG),     # C overlaps A
+    ((P(FAKE), 5, P(FAKE + 64), 5, P(FAKE + 40)), M.INVALID_ARG),    # C overlaps B
+    ((P(FAKE), 1 << 62, P(FAKE), 1 << 62, P(FAKE)), M.OVERFLOW),     # m+n > 2^62
+    ((P(0), 0, P(0), 0, P(0)), M.OK),                                # empty: no-op
+])
+def test_merge_i32_validation(args, want):
+    lib = om.load_library()
+    assert lib.merge_i32(*args, P(0)) == want
+
+
+def test_merge_kv_validation():
+    lib = om.load_library()
+    f = lib.merge_kv
+    a, av, b, bv = FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000
+    ck, cv = FAKE + 0x4000, FAKE + 0x5000
+    assert f(P(a), P(0), 4, P(b), P(bv), 4, P(ck), P(cv), P(0)) == M.INVALID_ARG
+    assert f(P(a), P(av), 4, P(b), P(bv), 4, P(ck), P(ck + 8), P(0)) == M.INVALID_ARG  # outputs overlap
+    assert f(P(a), P(av), 4, P(b), P(bv), 4, P(av), P(cv), P(0)) == M.INVALID_ARG      # C_keys over A_vals
+    assert f(P(a), P(av), 4, P(b), P(bv), 4, P(ck), P(bv + 4), P(0)) == M.INVALID_ARG  # C_vals over B_vals
+    assert f(P(0), P(0), 0, P(0), P(0), 0, P(0), P(0), P(0)) == M.OK
+
+
+def test_stage_validation():
+    lib = om.load_library()
+    a, b, part, c = FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000
+    assert lib.omerge_partition(P(a), 8, P(b), 8, 6, P(part), P(0)) == M.INVALID_ARG  # seg_len % 4
+    assert lib.omerge_partition(P(a), 8, P(b), 8, 0, P(part), P(0)) == M.INVALID_ARG
+    assert lib.omerge_partition(P(a), 8, P(b), 8, 8, P(0), P(0)) == M.INVALID_ARG
+    assert lib.omerge_partition(P(a), 8, P(b), 8, 8, P(part + 4), P(0)) == M.INVALID_ARG
+    assert lib.omerge_merge_segments_i32(P(a), 8, P(b), 8, P(0), 8, P(c), P(0)) == M.INVALID_ARG
+    assert lib.omerge_merge_segments_i32(P(a), 8, P(b), 8, P(part), 10, P(c), P(0)) == M.INVALID_ARG
+    assert lib.omerge_co_rank(P(a), 8, P(b), 8, P(0), 4, P(c), P(0)) == M.INVALID_ARG
+    assert lib.omerge_co_rank(P(a), 8, P(b), 8, P(part), -1, P(c), P(0)) == M.INVALID_ARG
+    assert lib.omerge_co_rank(P(a), 8, P(b), 8, P(0), 0, P(0), P(0)) == M.OK
+
+
+def test_binding_rejects_bad_tensors():
+    import torch
+    cpu = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        om.merge_i32(cpu, cpu)
+    with pytest.raises(TypeError):
+        om.merge_i32(cpu.float(), cpu)
+    with pytest.raises(TypeError):
+        om.merge_i32([1, 2], cpu)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(M, "_lib", None)
+    monkeypatch.setattr(M, "LIB", str(tmp_path / "absent.so"))
+    with pytest.raises(M.OmergeError, match="not built"):
+        M.load_library()

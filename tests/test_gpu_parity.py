@@ -1,0 +1,281 @@
+"""HIP path against the CPU oracle, element by element (needs an MI355X).
+
+Every output is compared exactly: a merge only permutes its input, so there
+is no tolerance (page 'merge_path.cu' compares the same way).  Key-only
+output cannot show the tie rule, so the co-ranks and the key+payload merge
+are checked directly as well.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ordered_merge_sorted_amd as om
+from ordered_merge_sorted_amd.workloads import WORKLOADS, ORDER
+
+pytestmark = pytest.mark.gpu
+
+U31 = np.uint32(1 << 31)
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print("[gpu-case]", *a, flush=True)
+
+
+def dev(x, off=0):
+    """numpy -> device tensor; with off > 0 the data starts `off` words into
+    a larger allocation, so the pointer has a different 16-byte phase."""
+    if x.dtype == np.uint32:
+        x = x.view(np.int32)
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if off == 0:
+        return t.to(DEV)
+    big = torch.empty(x.size + off, dtype=t.dtype, device=DEV)
+    big[off:] = t.to(DEV)
+    return big[off:]
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+def first_diff(got, want):
+    bad = np.flatnonzero(got != want)
+    return None if bad.size == 0 else (int(bad[0]), got[bad[0]], want[bad[0]], int(bad.size))
+
+
+def assert_same(got, want, what):
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    d = first_diff(got, want)
+    assert d is None, "%s: first difference at %d (got %r, want %r), %d differ" % ((what,) + d)
+
+
+def pair(g, m, n, span):
+    if span >= 1 << 32:
+        lo, hi = -(1 << 31), 1 << 31
+    else:
+        lo = int(g.integers(-(1 << 31), (1 << 31) - span))
+        hi = lo + span
+    A = np.sort(g.integers(lo, hi, size=m, dtype=np.int64)).astype(np.int32)
+    B = np.sort(g.integers(lo, hi, size=n, dtype=np.int64)).astype(np.int32)
+    return A, B
+
+
+def tags(m, n):
+    return np.arange(m, dtype=np.uint32), (U31 + np.arange(n, dtype=np.uint32)).astype(np.uint32)
+
+
+# --------------------------------------------------------------- small cases
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_i32_and_kv(seed):
+    g = np.random.Generator(np.random.PCG64(1000 + seed))
+    m, n = (int(x) for x in g.integers(0, 40000, size=2))
+    span = int(g.choice([2, 16, 4096, 1 << 32]))
+    A, B = pair(g, m, n, span)
+    Av, Bv = tags(m, n)
+    offs = [int(x) for x in g.integers(0, 4, size=6)] if seed % 2 else [0] * 6
+    say("random", seed, m, n, span, offs)
+    got = om.merge_i32(dev(A, offs[0]), dev(B, offs[1]))
+    assert_same(host(got), oracle.merge_i32(A, B), "merge_i32")
+    gk, gv = om.merge_kv(dev(A, offs[0]), dev(Av, offs[1]), dev(B, offs[2]), dev(Bv, offs[3]))
+    wk, wv = oracle.merge_kv(A, Av, B, Bv)
+    assert_same(host(gk), wk, "merge_kv keys")
+    assert_same(host(gv).view(np.uint32), wv, "merge_kv payloads")
+
+
+@pytest.mark.parametrize("seg_tiles", [1, 2, 3, 0])
+def test_explicit_segments(seg_tiles):
+    """Stage API with several segment lengths, including one that is not a
+    whole number of tiles (short last tile in every segment)."""
+    g = np.random.Generator(np.random.PCG64(77 + seg_tiles))
+    m, n = 70001, 53333
+    A, B = pair(g, m, n, 64)
+    Av, Bv = tags(m, n)
+    for kv, tile in ((False, 4096), (True, 2048)):
+        seg_len = tile * seg_tiles if seg_tiles else 4 * 1777
+        say("segments", kv, seg_len)
+        a, b = dev(A), dev(B)
+        part = om.partition(a, b, seg_len)
+        I = oracle.co_rank_all(A, B)
+        ks = np.minimum(np.arange(part.numel()) * seg_len, m + n)
+        assert_same(host(part), I[ks], "partition")
+        if kv:
+            gk, gv = om.merge_segments_kv(a, dev(Av), b, dev(Bv), part, seg_len)
+            wk, wv = oracle.merge_kv(A, Av, B, Bv)
+            assert_same(host(gk), wk, "keys")
+            assert_same(host(gv).view(np.uint32), wv, "payloads")
+        else:
+            got = om.merge_segments_i32(a, b, part, seg_len)
+            assert_same(host(got), oracle.merge_i32(A, B), "merge_segments_i32")
+
+
+def test_co_rank_every_k_with_ties():
+    """Device co-rank at every output rank: here the A-first tie rule is
+    visible even though the merged keys alone would not show it."""
+    g = np.random.Generator(np.random.PCG64(5))
+    for m, n, span in ((3000, 2000, 3), (1, 5000, 2), (4096, 4096, 1 << 32), (0, 77, 5), (77, 0, 5)):
+        A, B = pair(g, m, n, span)
+        say("co_rank", m, n, span)
+        ks = torch.arange(m + n + 1, dtype=torch.int64, device=DEV)
+        got = om.co_rank(dev(A), dev(B), ks)
+        assert_same(host(got), oracle.co_rank_all(A, B), "co_rank")
+    # out-of-range ranks are clamped into [0, m+n]
+    A, B = pair(g, 10, 10, 4)
+    got = om.co_rank(dev(A), dev(B), torch.tensor([-5, 0, 20, 99], dtype=torch.int64, device=DEV))
+    assert list(host(got)) == [0, 0, 10, 10]
+
+
+def test_worked_examples():
+    import json, os
+    gold = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    g1 = json.load(open(os.path.join(gold, "worked_example_corank.json")))
+    A, B = np.array(g1["A"], np.int32), np.array(g1["B"], np.int32)
+    ks = torch.tensor(g1["boundary_k"], dtype=torch.int64, device=DEV)
+    assert list(host(om.co_rank(dev(A), dev(B), ks))) == g1["boundary_i"]
+    C = host(om.merge_i32(dev(A), dev(B)))
+    assert list(C[3:6]) == g1["thread1_output"]["values"]
+    g2 = json.load(open(os.path.join(gold, "equal_element_case.json")))
+    A, B = np.array(g2["A"], np.int32), np.array(g2["B"], np.int32)
+    Av, Bv = tags(4, 4)
+    gk, gv = om.merge_kv(dev(A), dev(Av), dev(B), dev(Bv))
+    src = ["A%d" % v if v < U31 else "B%d" % (v - U31) for v in host(gv).view(np.uint32)]
+    assert src == ["A0", "A1", "B0", "A2", "B1", "B2", "A3", "B3"]
+    assert list(host(gk)) == [1, 1, 1, 2, 2, 2, 3, 4]
+
+
+EDGE = [
+    (0, 0), (1, 0), (0, 1), (1, 1), (3, 0), (0, 4095), (4095, 1), (4096, 0), (4097, 0),
+    (2048, 2048), (2049, 2048), (1, 100000), (100000, 1), (12289, 4093),
+]
+
+
+@pytest.mark.parametrize("m,n", EDGE)
+def test_edge_sizes(m, n):
+    g = np.random.Generator(np.random.PCG64(m * 7919 + n))
+    A, B = pair(g, m, n, 8)
+    Av, Bv = tags(m, n)
+    say("edge", m, n)
+    assert_same(host(om.merge_i32(dev(A), dev(B))), oracle.merge_i32(A, B), "i32")
+    gk, gv = om.merge_kv(dev(A), dev(Av), dev(B), dev(Bv))
+    wk, wv = oracle.merge_kv(A, Av, B, Bv)
+    assert_same(host(gk), wk, "kv keys")
+    assert_same(host(gv).view(np.uint32), wv, "kv payloads")
+
+
+def test_int32_extremes_and_all_equal():
+    imin, imax = -(1 << 31), (1 << 31) - 1
+    cases = [
+        (np.array([imin, imin, -1, 0, imax, imax], np.int32), np.array([imin, 0, 0, imax], np.int32)),
+        (np.full(10000, 7, np.int32), np.full(9000, 7, np.int32)),
+        (np.full(5000, imax, np.int32), np.full(5000, imin, np.int32)),
+        (np.full(5000, imin, np.int32), np.full(5000, imax, np.int32)),
+    ]
+    for A, B in cases:
+        Av, Bv = tags(A.size, B.size)
+        say("extremes", A.size, B.size)
+        assert_same(host(om.merge_i32(dev(A), dev(B))), oracle.merge_i32(A, B), "i32")
+        gk, gv = om.merge_kv(dev(A), dev(Av), dev(B), dev(Bv))
+        wk, wv = oracle.merge_kv(A, Av, B, Bv)
+        assert_same(host(gv).view(np.uint32), wv, "kv payloads")
+
+
+def test_uint32_payload_dtype():
+    if not hasattr(torch, "uint32"):
+        pytest.skip("torch has no uint32")
+    A, B = pair(np.random.Generator(np.random.PCG64(3)), 3000, 2000, 10)
+    Av, Bv = tags(3000, 2000)
+    av = torch.from_numpy(Av).to(DEV)
+    bv = torch.from_numpy(Bv).to(DEV)
+    gk, gv = om.merge_kv(dev(A), av, dev(B), bv)
+    assert gv.dtype == torch.uint32
+    assert_same(gv.cpu().numpy(), oracle.merge_kv(A, Av, B, Bv)[1], "uint32 payloads")
+
+
+def test_non_default_stream():
+    g = np.random.Generator(np.random.PCG64(9))
+    A, B = pair(g, 300000, 200000, 1000)
+    a, b = dev(A), dev(B)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream(DEV)
+    with torch.cuda.stream(s):
+        out = torch.empty(A.size + B.size, dtype=torch.int32, device=DEV)
+        om.merge_i32(a, b, out=out)
+        ev = torch.cuda.Event()
+        ev.record(s)
+    ev.synchronize()
+    assert_same(host(out), oracle.merge_i32(A, B), "stream")
+
+
+def test_repeatable_and_preallocated_out():
+    g = np.random.Generator(np.random.PCG64(10))
+    A, B = pair(g, 123457, 98765, 50)
+    a, b = dev(A), dev(B)
+    out = torch.full((A.size + B.size,), -1, dtype=torch.int32, device=DEV)
+    first = host(om.merge_i32(a, b, out=out)).copy()
+    for _ in range(3):
+        assert_same(host(om.merge_i32(a, b, out=out)), first, "repeat")
+    assert_same(first, oracle.merge_i32(A, B), "oracle")
+
+
+def test_unsorted_input_returns():
+    """Sortedness is not checked; unsorted input must still return (the
+    kernels' loops are bounded) with an output of the right size."""
+    g = np.random.Generator(np.random.PCG64(11))
+    A = g.integers(-100, 100, size=50000).astype(np.int32)
+    B = g.integers(-100, 100, size=30000).astype(np.int32)
+    out = om.merge_i32(dev(A), dev(B))
+    torch.cuda.synchronize()
+    assert out.numel() == 80000
+
+
+# ------------------------------------------------------- full-size workloads
+
+@pytest.mark.parametrize("name", ORDER)
+def test_workload_bit_exact(name):
+    w = WORKLOADS[name]
+    say("workload", name, w.m, w.n)
+    arrs = w.make()
+    if w.kv:
+        Ak, Av, Bk, Bv = arrs
+        gk, gv = om.merge_kv(dev(Ak), dev(Av), dev(Bk), dev(Bv))
+        gk, gv = host(gk), host(gv).view(np.uint32)
+        wk, wv = oracle.merge_kv(Ak, Av, Bk, Bv)
+        assert_same(gk, wk, name + " keys")
+        assert_same(gv, wv, name + " payloads")
+        # merged (key, payload) strictly increasing: the lexicographic sort
+        assert np.all((gk[1:] > gk[:-1]) | ((gk[1:] == gk[:-1]) & (gv[1:] > gv[:-1])))
+    else:
+        A, B = arrs
+        got = host(om.merge_i32(dev(A), dev(B)))
+        assert_same(got, oracle.merge_i32(A, B), name)
+        if name.startswith("even_odd"):
+            h = 1 << 22
+            assert np.array_equal(got[:h], np.arange(h, dtype=np.int32))
+
+
+def test_headline_stage_path_matches():
+    """The launch sequence the benchmark times (partition, then segment
+    merge, with the library's own segment length) on the headline workload,
+    checked on every output."""
+    w = WORKLOADS["uniform_i32_2p28x2p28"]
+    A, B = w.make()
+    a, b = dev(A), dev(B)
+    seg_len = om.segment_length(w.m, w.n)
+    say("headline stages", seg_len)
+    part = om.partition(a, b, seg_len)
+    got = host(om.merge_segments_i32(a, b, part, seg_len))
+    # Each boundary's co-rank is the unique split that passes the acceptance
+    # test A[i-1] <= B[j] and B[j-1] < A[i] (j = k - i), with the usual
+    # exemptions at the array ends.
+    ks = np.minimum(np.arange(part.numel(), dtype=np.int64) * seg_len, w.total)
+    I = host(part)
+    J = ks - I
+    m, n = w.m, w.n
+    assert np.all((I >= np.maximum(0, ks - n)) & (I <= np.minimum(ks, m)))
+    A64, B64 = A.astype(np.int64), B.astype(np.int64)
+    ok_lo = (I == 0) | (J == n) | (A64[np.clip(I - 1, 0, m - 1)] <= B64[np.clip(J, 0, n - 1)])
+    ok_hi = (J == 0) | (I == m) | (B64[np.clip(J - 1, 0, n - 1)] < A64[np.clip(I, 0, m - 1)])
+    assert np.all(ok_lo & ok_hi)
+    assert_same(got, oracle.merge_i32(A, B), "headline")
