@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Benchmark of the stable co-rank merge on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one pass of the whole hot path over resident inputs: the
+partition kernel (one co-rank per segment boundary) and the segment merge
+kernel, launched through the C ABI on the current torch stream.  The default
+workload is 2^28 + 2^28 int32 keys iid uniform over the int32 range, sorted.
+
+Before timing, the merged output of one untimed launch is compared with the
+CPU oracle on every element (a wrong answer never produces a number), and the
+oracle run is timed as the reported CPU baseline.  Then W untimed steps, then
+exactly K timed steps between device synchronisations.  HIP events around
+each segment-merge launch give that kernel's mean duration for the roofline
+figure.  A streaming copy of the same byte count is timed beside it as the
+bandwidth this device actually delivers.
+
+Prints ONE JSON line on stdout; the device banner and extra figures go to
+stderr.  Only one GPU is used: --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+METRIC = "merged elements/sec and achieved HBM GB/s (% of MI355X peak), int32 m=n=2^28"
+COUNTER_FILE = os.path.join(ROOT, "profiles", "merge_segments_uniform_i32_2p28x2p28_traffic.md")
+KERNEL_SOURCES = ["corank.hpp", "merge_kernel.hpp", "omerge.hip"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "ordered_merge_sorted_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per segment-merge launch from the committed counter summary,
+    if it was taken on the kernel source as it is now; else None."""
+    if not os.path.exists(COUNTER_FILE):
+        return None
+    text = open(COUNTER_FILE).read()
+    src = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not src or not val or src.group(1) != kernel_source_hash():
+        return None
+    return float(val.group(1))
+
+
+def device_banner(torch):
+    p = torch.cuda.get_device_properties(0)
+    arch = getattr(p, "gcnArchName", "?")
+    log("GPU: %s (%s), %d CUs, %.1f GiB, L2 %s MiB" % (
+        p.name, arch, p.multi_processor_count, p.total_memory / 2**30,
+        getattr(p, "L2_cache_size", 0) / 2**20 if hasattr(p, "L2_cache_size") else "?"))
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    log("host: %d cores available to this process (nproc %s)" % (cores, os.cpu_count()))
+    return arch
+
+
+def time_oracle(w, arrs, want_runs_s=10.0, max_runs=5):
+    """Single-threaded CPU oracle on the full workload; repeated until about
+    want_runs_s seconds have passed (at most max_runs).  Returns (out, rates)."""
+    import oracle
+    rates, out = [], None
+    t_all = time.perf_counter()
+    for r in range(max_runs):
+        t0 = time.perf_counter()
+        out = oracle.merge_kv(*arrs) if w.kv else oracle.merge_i32(*arrs)
+        dt = time.perf_counter() - t0
+        rates.append(w.total / dt)
+        log("oracle run %d: %.2f s, %.3g elements/s" % (r, dt, w.total / dt))
+        if time.perf_counter() - t_all >= want_runs_s:
+            break
+    return out, rates
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None, help="workload name (default: the int32 2^28+2^28 merge)")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip timing the oracle (the output check still runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("--steps must be >= 1 and --warmup >= 0")
+
+    import torch
+
+    import ordered_merge_sorted_amd as om
+    from ordered_merge_sorted_amd.workloads import HEADLINE, WORKLOADS
+
+    name = args.workload or HEADLINE
+    w = WORKLOADS[name]
+    arch = device_banner(torch)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    t0 = time.perf_counter()
+    arrs = w.make()
+    log("workload %s: m=%d n=%d (%s); generated in %.1f s" % (name, w.m, w.n, w.description,
+                                                             time.perf_counter() - t0))
+
+    # Inputs resident in HBM before anything is timed.
+    def to_dev(x):
+        return torch.from_numpy(x.view(np.int32) if x.dtype == np.uint32 else x).to(dev)
+
+    d_arrs = [to_dev(x) for x in arrs]
+    total = w.total
+    seg_len = om.segment_length(w.m, w.n, kv=w.kv)
+    count = om.partition_count(total, seg_len)
+    part = torch.empty(count, dtype=torch.int64, device=dev)
+    if w.kv:
+        out_k = torch.empty(total, dtype=torch.int32, device=dev)
+        out_v = torch.empty(total, dtype=torch.int32, device=dev)
+    else:
+        out = torch.empty(total, dtype=torch.int32, device=dev)
+
+    def launch_partition():
+        om.partition(d_arrs[0], d_arrs[2] if w.kv else d_arrs[1], seg_len, out=part, stream=stream)
+
+    def launch_merge():
+        if w.kv:
+            om.merge_segments_kv(d_arrs[0], d_arrs[1], d_arrs[2], d_arrs[3], part, seg_len,
+                                 out_keys=out_k, out_vals=out_v, stream=stream)
+        else:
+            om.merge_segments_i32(d_arrs[0], d_arrs[1], part, seg_len, out=out, stream=stream)
+
+    # One untimed, checked step (every element against the oracle).
+    launch_partition()
+    launch_merge()
+    torch.cuda.synchronize()
+    if args.no_cpu_baseline:
+        import oracle
+        want = oracle.merge_kv(*arrs) if w.kv else oracle.merge_i32(*arrs)
+        rates = []
+    else:
+        want, rates = time_oracle(w, arrs)
+    if w.kv:
+        ok = np.array_equal(out_k.cpu().numpy(), want[0]) and \
+            np.array_equal(out_v.cpu().numpy().view(np.uint32), want[1])
+    else:
+        ok = np.array_equal(out.cpu().numpy(), want)
+    if not ok:
+        log("FAILED: the merged output differs from the oracle; no number is reported")
+        sys.exit(1)
+    log("checked: output bit-exact against the oracle (%d elements)" % total)
+    del want
+
+    # Warmup, then exactly K timed steps.
+    for _ in range(args.warmup):
+        launch_partition()
+        launch_merge()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    start_all = torch.cuda.Event(enable_timing=True)
+    stop_all = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter()
+    start_all.record(stream)
+    for k in range(args.steps):
+        launch_partition()
+        ev[k][0].record(stream)
+        launch_merge()
+        ev[k][1].record(stream)
+    stop_all.record(stream)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter() - t_host
+    ms_total = start_all.elapsed_time(stop_all)
+    ms_step = ms_total / args.steps
+    merge_ms = [a.elapsed_time(b) for a, b in ev]
+    merge_ms_mean = float(np.mean(merge_ms))
+
+    bpe = w.bytes_per_element
+    alg_bytes = 2 * total * bpe  # each element read once and written once
+    value = total / (ms_step * 1e-3)
+    step_gbs = alg_bytes / (ms_step * 1e-3) / 1e9
+    kern_gbs = alg_bytes / (merge_ms_mean * 1e-3) / 1e9
+
+    # Streaming copy of the same byte count: the bandwidth this device gives.
+    src = torch.empty(total * bpe // 4, dtype=torch.int32, device=dev)
+    src.random_(0, 1 << 30)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        om.stream_copy(src, out=dst, stream=stream)
+    cs, ce = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    cs.record(stream)
+    for _ in range(reps):
+        om.stream_copy(src, out=dst, stream=stream)
+    ce.record(stream)
+    torch.cuda.synchronize()
+    copy_ms = cs.elapsed_time(ce) / reps
+    copy_gbs = alg_bytes / (copy_ms * 1e-3) / 1e9
+    del src, dst
+
+    # One-call API (includes its stream-ordered scratch allocation).
+    if not w.kv:
+        for _ in range(3):
+            om.merge_i32(d_arrs[0], d_arrs[1], out=out, stream=stream)
+        s1, s2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s1.record(stream)
+        for _ in range(10):
+            om.merge_i32(d_arrs[0], d_arrs[1], out=out, stream=stream)
+        s2.record(stream)
+        torch.cuda.synchronize()
+        onecall_ms = s1.elapsed_time(s2) / 10
+    else:
+        onecall_ms = None
+
+    log("step: %.4f ms (host clock %.4f ms/step) -> %.4g elements/s, %.1f GB/s (%.1f%% of %.0f)" % (
+        ms_step, t_host * 1e3 / args.steps, value, step_gbs, 100 * step_gbs / HBM_PEAK_GBS, HBM_PEAK_GBS))
+    log("segment merge kernel: %.4f ms mean (min %.4f, max %.4f) -> %.1f GB/s" % (
+        merge_ms_mean, min(merge_ms), max(merge_ms), kern_gbs))
+    log("partition kernel + gaps: %.4f ms per step" % (ms_step - merge_ms_mean))
+    log("stream copy of the same bytes: %.4f ms -> %.1f GB/s; merge step at %.1f%% of it" % (
+        copy_ms, copy_gbs, 100 * step_gbs / copy_gbs))
+    if onecall_ms is not None:
+        log("merge_i32 one call (with its scratch allocation): %.4f ms" % onecall_ms)
+
+    cpu = None
+    if rates:
+        cpu = {"value": float(np.median(rates)), "unit": "merged elements/s", "cores": 1,
+               "kind": "oracle",
+               "sample": "full workload (%d + %d elements), %d run(s), median; single-threaded C "
+                         "two-pointer merge" % (w.m, w.n, len(rates))}
+
+    traffic = recorded_traffic() if name == HEADLINE else None
+    line = {
+        "metric": METRIC if name == HEADLINE else "merged elements/sec (%s)" % name,
+        "value": value,
+        "unit": "merged elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32+uint32" if w.kv else "int32",
+        "data": "synthetic",
+        "config": {"workload": name, "m": w.m, "n": w.n, "key_payload": w.kv,
+                   "seg_len": seg_len, "segments": count - 1, "gpu_arch": arch},
+        "gbps": step_gbs,
+        "pct_hbm_peak": 100 * step_gbs / HBM_PEAK_GBS,
+        "copy_gbps_same_bytes": copy_gbs,
+        "roofline": {"bound": "hbm", "achieved": kern_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": kern_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "merge_segments_kernel", "kernel_ms": merge_ms_mean,
+                     "algorithmic_bytes_per_launch": alg_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

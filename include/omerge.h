@@ -128,6 +128,17 @@ int omerge_merge_segments_kv(const int32_t *A_keys, const uint32_t *A_vals,
                              int32_t *C_keys, uint32_t *C_vals,
                              struct ihipStream_t *stream);
 
+/*
+ * omerge_stream_copy -- measurement reference, not part of the merge: copies
+ * n 32-bit words from src to dst (device, non-overlapping) with 16-byte
+ * loads and stores, i.e. the same bytes a merge of n outputs must move.  A
+ * benchmark times it beside the merge to measure the bandwidth this device
+ * actually delivers, and uses its known byte count to calibrate hardware
+ * traffic counters.
+ */
+int omerge_stream_copy(const int32_t *src, int64_t n, int32_t *dst,
+                       struct ihipStream_t *stream);
+
 /* Text for an omerge_status value (static storage; never NULL). */
 const char *omerge_status_string(int status);
 

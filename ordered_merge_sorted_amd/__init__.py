@@ -15,4 +15,5 @@ from .merge import (  # noqa: F401
     partition,
     partition_count,
     segment_length,
+    stream_copy,
 )

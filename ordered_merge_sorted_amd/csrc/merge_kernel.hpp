@@ -28,9 +28,29 @@
 //     tile t's stores; the HBM latency hides behind the merge.
 //   * Each lane searches the END of its slice; its start is its left
 //     neighbour's end, read from a small LDS array, and the last lane's end
-//     is the tile's split.  One search per lane per tile.
-//   * The LDS stage is padded by one word every 32 so that lanes writing
-//     their ITEMS outputs at stride ITEMS spread over the banks.
+//     is the tile's split.  One search per lane per tile.  Inside a tile the
+//     search is a fixed-trip, branchless bisection of the merge diagonal
+//     (one probe pair per step) within the same bounds as the pages' search;
+//     it returns the same unique co-rank with about a third of the
+//     instructions of the two-test loop.
+//   * Key-only merges order a lane's ITEMS outputs with a min/max bitonic
+//     network instead of the serial two-pointer loop.  The co-ranks already
+//     fix which elements belong to each lane (A first on ties); inside a lane
+//     equal keys are indistinguishable in a key-only output, so any exact
+//     ordering of the lane's keys is bit-identical to the stable merge.  The
+//     network has no LDS round trip per output and no branches.  Key+payload
+//     merges keep the serial loop, where the tie order is visible.
+//   * Each ring has a guard zone that mirrors its first ITEMS slots past its
+//     end, so a lane reads its ITEMS candidates at one base address with
+//     immediate offsets and no wrap arithmetic.
+//   * The LDS stage is padded by 4 words every 32, which makes the 16-byte
+//     stage writes (lane-contiguous) and 16-byte stage reads (for the
+//     coalesced stores) free of bank conflicts.
+//   * The partition kernel can search each boundary with a group of G lanes:
+//     G points of the diagonal are tested at once and a ballot narrows the
+//     interval G-fold per round (the pages note the search may be
+//     higher-radix).  Fewer dependent HBM round trips, more lines touched
+//     per round; G is a tuning choice of the launcher.
 //   * All arithmetic is int32 compares and index arithmetic; no MFMA.
 #pragma once
 
@@ -49,6 +69,16 @@ __host__ __device__ constexpr int next_pow2(int x) {
     return p;
 }
 
+// Number of bits of x: the steps a bisection of x+1 candidates needs.
+__host__ __device__ constexpr int bit_length(int x) {
+    int b = 0;
+    while (x > 0) {
+        x >>= 1;
+        ++b;
+    }
+    return b;
+}
+
 template <typename T>
 __device__ __forceinline__ T clamp_to(T x, T lo, T hi) {
     return x < lo ? lo : (x > hi ? hi : x);
@@ -62,39 +92,129 @@ __device__ __forceinline__ int word_phase(const void* p) {
 template <int THREADS, int ITEMS, bool KV>
 struct MergeCfg {
     static_assert(THREADS % 64 == 0, "whole 64-lane wavefronts");
-    static_assert(ITEMS % 4 == 0, "refills and stores move 4 elements per lane");
+    static_assert(ITEMS >= 4 && (ITEMS & (ITEMS - 1)) == 0,
+                  "ITEMS: a power of two, at least one 16-byte vector");
+    static_assert(ITEMS <= 32 || ITEMS % 32 == 0, "lane-contiguous stage rows");
     static constexpr int kTile = THREADS * ITEMS;  // outputs per tile
     static constexpr int kCap = next_pow2(kTile);  // ring capacity per side
     static constexpr int kMask = kCap - 1;
-    static constexpr int kVec = ITEMS / 4;  // 16-byte vectors per lane per refill
-    static constexpr int kStageWords = kTile + kTile / 32 + 1;
+    static constexpr int kGuard = ITEMS;           // mirrored slots past the end
+    static constexpr int kSide = kCap + kGuard;    // words per side ring
+    static constexpr int kVec = ITEMS / 4;         // 16-byte vectors per lane
+    static constexpr int kSearchSteps = bit_length(kTile);
+    static constexpr int kStageWords = kTile + kTile / 8;
     // LDS layout in 32-bit words.
-    static constexpr int kRing = 0;  // keys: A ring [0,kCap), B ring [kCap,2kCap)
-    static constexpr int kValRing = kRing + 2 * kCap;  // payload rings (KV)
-    static constexpr int kStage = kValRing + (KV ? 2 * kCap : 0);
+    static constexpr int kRing = 0;  // keys: A ring [0,kSide), B ring [kSide,2kSide)
+    static constexpr int kValRing = kRing + 2 * kSide;  // payload rings (KV)
+    static constexpr int kStage = kValRing + (KV ? 2 * kSide : 0);
     static constexpr int kValStage = kStage + kStageWords;
     static constexpr int kSplit = kValStage + (KV ? kStageWords : 0);
     static constexpr int kWords = kSplit + THREADS;
     static constexpr int kLdsBytes = kWords * 4;
 };
 
-// Padded stage index: one spare word every 32.
-__device__ __forceinline__ int stage_at(int p) { return p + (p >> 5); }
+// Global 16-byte accesses for streaming data.  By default they carry the
+// nontemporal hint: every input is read once and every output written once,
+// and on MI355X the hint raises a plain 16-byte copy from ~5.7 to ~6.2 TB/s
+// and the merge by ~4%.  Building with OMERGE_NT_LOADS=0 / OMERGE_NT_STORES=0
+// gives plain accesses.
+#ifndef OMERGE_NT_LOADS
+#define OMERGE_NT_LOADS 1
+#endif
+#ifndef OMERGE_NT_STORES
+#define OMERGE_NT_STORES 1
+#endif
+__device__ __forceinline__ int4v load_stream4(const int32_t* p) {
+    const int4v* q = reinterpret_cast<const int4v*>(p);
+    return OMERGE_NT_LOADS ? __builtin_nontemporal_load(q) : *q;
+}
+__device__ __forceinline__ void store_stream4(int32_t* p, int4v x) {
+    int4v* q = reinterpret_cast<int4v*>(p);
+    if (OMERGE_NT_STORES)
+        __builtin_nontemporal_store(x, q);
+    else
+        *q = x;
+}
+
+// Stage word of tile output p: 4 spare words after every 32.
+__device__ __forceinline__ int stage_word(int p) { return p + ((p >> 5) << 2); }
 
 // ---------------------------------------------------------------------------
 // Partition and co-rank query kernels.
 
-__global__ void partition_kernel(const int32_t* __restrict__ A, int64_t m,
-                                 const int32_t* __restrict__ B, int64_t n,
-                                 int64_t seg_len, int64_t count,
-                                 int64_t* __restrict__ part) {
-    const int64_t s = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
-    if (s >= count) return;
-    const int64_t total = m + n;
-    const int64_t k = s < count - 1 ? s * seg_len : total;
-    part[s] = co_rank_global(k, A, m, B, n);
+// Co-rank of k over global memory by a group of G lanes (G divides 64;
+// `g_lane` = 0..G-1 within the group, `g_shift` = the group's first lane in
+// the wavefront).  Each round tests G points of [lo, hi) on the diagonal.  A
+// point i passes when A[i] <= B[k-1-i], i.e. A[i] is among the first k
+// outputs; the passing points form a prefix, so the answer lies just after
+// the last passing point and at or before the first failing one.  Every
+// round keeps max(0,k-n) <= lo <= hi <= min(k,m) and shrinks the interval,
+// whatever the data, so the loop ends even on unsorted input.  All lanes of
+// the wavefront must call this together (the vote is wavefront-wide).
+template <int G>
+__device__ __forceinline__ int64_t co_rank_group(int64_t k, const int32_t* __restrict__ A,
+                                                 int64_t m, const int32_t* __restrict__ B,
+                                                 int64_t n, int g_lane, int g_shift) {
+    static_assert(G >= 2 && G <= 64 && (64 % G) == 0, "group size");
+    constexpr int kLog = bit_length(G) - 1;
+    int64_t lo = k > n ? k - n : 0;
+    int64_t hi = k < m ? k : m;
+    for (int round = 0; round < 64; ++round) {
+        if (__ballot(lo < hi) == 0) break;  // every group of the wavefront is done
+        const int64_t span = hi - lo;
+        const int64_t q = span >> kLog, r = span & (G - 1);
+        const int live = span < G ? static_cast<int>(span) : G;
+        // l-th point: lo + floor(span*l/G) for long intervals, lo + l for short.
+        auto point = [=](int l) -> int64_t {
+            return span < G ? lo + l : lo + q * l + ((r * l) >> kLog);
+        };
+        const int64_t p = point(g_lane);
+        bool pass = false;
+        if (g_lane < live) pass = A[p] <= B[k - 1 - p];
+        const unsigned long long votes = __ballot(pass);
+        const unsigned long long mine =
+            G == 64 ? votes : (votes >> g_shift) & ((1ull << (G == 64 ? 0 : G)) - 1);
+        const int c = __popcll(mine);
+        if (lo < hi) {
+            const int64_t new_lo = c > 0 ? point(c - 1) + 1 : lo;
+            const int64_t new_hi = c < live ? point(c) : hi;
+            lo = new_lo;
+            hi = new_hi;
+        }
+    }
+    return lo;
 }
 
+// part[s] = co-rank of k_s = min(s*seg_len, m+n).  G = 1: one lane per
+// boundary running the pages' two-test search; G > 1: G lanes per boundary
+// testing G points per round.
+template <int G>
+__global__ __launch_bounds__(256) void partition_kernel(const int32_t* __restrict__ A, int64_t m,
+                                                        const int32_t* __restrict__ B, int64_t n,
+                                                        int64_t seg_len, int64_t count,
+                                                        int64_t* __restrict__ part) {
+    const int64_t gid = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+    if constexpr (G == 1) {
+        if (gid >= count) return;
+        const int64_t k = gid < count - 1 ? gid * seg_len : m + n;
+        part[gid] = co_rank_global(k, A, m, B, n);
+    } else {
+        const int64_t s = gid / G;
+        // A wavefront whose groups are all past the end leaves together;
+        // groups past the end inside a live wavefront vote with empty ranges.
+        if ((gid & ~int64_t(63)) / G >= count) return;
+        const int64_t sc = s < count ? s : count - 1;
+        const int64_t k = sc < count - 1 ? sc * seg_len : m + n;
+        const int g_lane = static_cast<int>(gid % G);
+        const int g_shift = static_cast<int>(threadIdx.x & 63) - g_lane;
+        const int64_t i = co_rank_group<G>(s < count ? k : 0, A, s < count ? m : 0, B,
+                                           s < count ? n : 0, g_lane, g_shift);
+        if (g_lane == 0 && s < count) part[s] = i;
+    }
+}
+
+// Co-rank at arbitrary ranks, one lane per query, with the pages' two-test
+// search (corank.hpp).
 __global__ void co_rank_kernel(const int32_t* __restrict__ A, int64_t m,
                                const int32_t* __restrict__ B, int64_t n,
                                const int64_t* __restrict__ ks, int64_t count,
@@ -105,13 +225,48 @@ __global__ void co_rank_kernel(const int32_t* __restrict__ A, int64_t m,
     out[s] = co_rank_global(k, A, m, B, n);
 }
 
+// Bandwidth reference: each lane copies UNROLL 16-byte vectors, all loads
+// issued before the stores; single words at the two ends.
+template <int UNROLL>
+__global__ __launch_bounds__(256) void stream_copy_kernel(const int32_t* __restrict__ src,
+                                                          int64_t n, int32_t* __restrict__ dst) {
+    const int64_t lane = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+    const int head0 = (4 - (word_phase(dst) & 3)) & 3;
+    const int64_t head = head0 < n ? head0 : n;
+    const bool same_phase = ((word_phase(src) - word_phase(dst)) & 3) == 0;
+    if (same_phase) {
+        const int64_t nvec = (n - head) >> 2;
+        const int64_t first = blockIdx.x * static_cast<int64_t>(blockDim.x) * UNROLL + threadIdx.x;
+        int4v v[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int64_t q = first + u * static_cast<int64_t>(blockDim.x);
+            if (q < nvec) v[u] = load_stream4(src + head + 4 * q);
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int64_t q = first + u * static_cast<int64_t>(blockDim.x);
+            if (q < nvec) store_stream4(dst + head + 4 * q, v[u]);
+        }
+        if (lane < head) dst[lane] = src[lane];
+        const int64_t done = head + 4 * nvec;
+        if (lane < n - done) dst[done + lane] = src[done + lane];
+    } else {
+        for (int u = 0; u < 4 * UNROLL; ++u) {
+            const int64_t p = (lane / 64) * 64 * 4 * UNROLL + u * 64 + (lane & 63);
+            if (p < n) dst[p] = src[p];
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Ring refill: copies a segment-relative range [r0, r1) of one side into its
 // ring.  Issue and commit are split so the loads can be in flight while the
 // current tile is merged.  Body vectors of side A and side B share one lane
 // assignment, so a refill of at most TILE elements needs kVec vectors per
 // lane.  Up to 3 head and 3 tail elements per side are loaded one by one by
-// lanes 0..11.
+// lanes 0..11.  Slots below the guard size are also written to their mirror
+// past the ring's end.
 
 struct SideRange {
     const int32_t* src;  // segment base of this array in global memory
@@ -133,26 +288,28 @@ struct SideRange {
     }
 };
 
-template <int THREADS, int ITEMS, int MASK>
+template <int THREADS, int ITEMS, int CAP, int SIDE>
 struct Refill {
     static constexpr int kVec = ITEMS / 4;
+    static constexpr int kMask = CAP - 1;
+    static constexpr int kGuard = SIDE - CAP;
     int4v body[kVec];
     int loose;        // one head/tail element (lanes 0..11)
     int loose_slot;   // its ring word index, or -1
+    int loose_side;   // 0 = A ring, 1 = B ring
     SideRange sa, sb;
 
-    __device__ __forceinline__ void issue(const SideRange& a, const SideRange& b,
-                                          int tid) {
+    __device__ __forceinline__ void issue(const SideRange& a, const SideRange& b, int tid) {
         sa = a;
         sb = b;
 #pragma unroll
         for (int v = 0; v < kVec; ++v) {
             const int q = tid + v * THREADS;
             if (q < sa.nvec) {
-                body[v] = *reinterpret_cast<const int4v*>(sa.src + sa.r0 + sa.head + 4 * q);
+                body[v] = load_stream4(sa.src + sa.r0 + sa.head + 4 * q);
             } else if (q - sa.nvec < sb.nvec) {
                 const int qb = q - sa.nvec;
-                body[v] = *reinterpret_cast<const int4v*>(sb.src + sb.r0 + sb.head + 4 * qb);
+                body[v] = load_stream4(sb.src + sb.r0 + sb.head + 4 * qb);
             }
         }
         loose_slot = -1;
@@ -167,28 +324,77 @@ struct Refill {
             }
             if (r >= 0) {
                 loose = s.src[r];
-                loose_slot = ((s.base + r) & MASK) + (tid < 6 ? 0 : MASK + 1);
+                loose_slot = (s.base + r) & kMask;
+                loose_side = tid < 6 ? 0 : 1;
             }
         }
     }
 
-    // ring points at the A ring; the B ring follows it at MASK+1 words.
+    __device__ __forceinline__ static void put4(int* side, int slot, int4v x) {
+        *reinterpret_cast<int4v*>(side + slot) = x;
+        if (slot < kGuard) *reinterpret_cast<int4v*>(side + CAP + slot) = x;
+    }
+
+    // ring points at the A ring; the B ring starts SIDE words later.
     __device__ __forceinline__ void commit(int* ring, int tid) const {
 #pragma unroll
         for (int v = 0; v < kVec; ++v) {
             const int q = tid + v * THREADS;
             if (q < sa.nvec) {
-                const int slot = (sa.base + sa.r0 + sa.head + 4 * q) & MASK;
-                *reinterpret_cast<int4v*>(ring + slot) = body[v];
+                put4(ring, (sa.base + sa.r0 + sa.head + 4 * q) & kMask, body[v]);
             } else if (q - sa.nvec < sb.nvec) {
                 const int qb = q - sa.nvec;
-                const int slot = (sb.base + sb.r0 + sb.head + 4 * qb) & MASK;
-                *reinterpret_cast<int4v*>(ring + MASK + 1 + slot) = body[v];
+                put4(ring + SIDE, (sb.base + sb.r0 + sb.head + 4 * qb) & kMask, body[v]);
             }
         }
-        if (loose_slot >= 0) ring[loose_slot] = loose;
+        if (loose_slot >= 0) {
+            int* side = ring + (loose_side ? SIDE : 0);
+            side[loose_slot] = loose;
+            if (loose_slot < kGuard) side[CAP + loose_slot] = loose;
+        }
     }
 };
+
+// Co-rank of diagonal k inside one tile: A window of wa elements starting at
+// ring slot sa, B window of wb elements at slot sb.  Bisects [max(0,k-wb),
+// min(k,wa)] for the first i at which A[i] is not among the first k outputs
+// (A[i] <= B[k-1-i] fails).  STEPS = bit_length(TILE) covers every interval;
+// finished lanes idle through the remaining steps, so the loop has no
+// data-dependent exit.
+template <int STEPS, int MASK>
+__device__ __forceinline__ int co_rank_tile(int k, int wa, int wb, const int* ring_a, int sa,
+                                            const int* ring_b, int sb) {
+    int lo = k > wb ? k - wb : 0;
+    int hi = k < wa ? k : wa;
+#pragma unroll
+    for (int step = 0; step < STEPS; ++step) {
+        const int mid = (lo + hi) >> 1;
+        const int av = ring_a[(sa + mid) & MASK];
+        const int bv = ring_b[(sb + k - 1 - mid) & MASK];
+        const bool live = lo < hi;
+        const bool a_first = av <= bv;
+        lo = (live && a_first) ? mid + 1 : lo;
+        hi = (live && !a_first) ? mid : hi;
+    }
+    return lo;
+}
+
+// Orders x[0..N) ascending when x is bitonic (min/max network).
+template <int N>
+__device__ __forceinline__ void bitonic_clean(int (&x)[N]) {
+#pragma unroll
+    for (int d = N / 2; d >= 1; d >>= 1) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            if ((i & d) == 0) {
+                const int lo = min(x[i], x[i + d]);
+                const int hi = max(x[i], x[i + d]);
+                x[i] = lo;
+                x[i + d] = hi;
+            }
+        }
+    }
+}
 
 // Stores tile outputs [0, len) from the padded LDS stage to dst[0, len):
 // 16-byte stores on the aligned body, single words at the ends.
@@ -199,23 +405,34 @@ __device__ __forceinline__ void store_tile(int32_t* __restrict__ dst, int len,
     const int head = head0 < len ? head0 : len;
     const int nvec = (len - head) >> 2;
     const int tail = (len - head) & 3;
+    if (head == 0) {
 #pragma unroll
-    for (int v = 0; v < ITEMS / 4; ++v) {
-        const int q = tid + v * THREADS;
-        if (q < nvec) {
-            const int p = head + 4 * q;
-            int4v x;
-            x.x = stage[stage_at(p)];
-            x.y = stage[stage_at(p + 1)];
-            x.z = stage[stage_at(p + 2)];
-            x.w = stage[stage_at(p + 3)];
-            *reinterpret_cast<int4v*>(dst + p) = x;
+        for (int v = 0; v < ITEMS / 4; ++v) {
+            const int q = tid + v * THREADS;
+            if (q < nvec) {
+                const int p = 4 * q;
+                store_stream4(dst + p, *reinterpret_cast<const int4v*>(stage + stage_word(p)));
+            }
         }
+    } else {
+#pragma unroll
+        for (int v = 0; v < ITEMS / 4; ++v) {
+            const int q = tid + v * THREADS;
+            if (q < nvec) {
+                const int p = head + 4 * q;
+                int4v x;
+                x.x = stage[stage_word(p)];
+                x.y = stage[stage_word(p + 1)];
+                x.z = stage[stage_word(p + 2)];
+                x.w = stage[stage_word(p + 3)];
+                store_stream4(dst + p, x);
+            }
+        }
+        if (tid < head) dst[tid] = stage[stage_word(tid)];
     }
-    if (tid < head) dst[tid] = stage[stage_at(tid)];
     if (tid >= 4 && tid - 4 < tail) {
         const int p = head + 4 * nvec + (tid - 4);
-        dst[p] = stage[stage_at(p)];
+        dst[p] = stage[stage_word(p)];
     }
 }
 
@@ -232,9 +449,11 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
     constexpr int kTile = Cfg::kTile;
     constexpr int kCap = Cfg::kCap;
     constexpr int kMask = Cfg::kMask;
+    constexpr int kSide = Cfg::kSide;
+    using RefillT = Refill<THREADS, ITEMS, kCap, kSide>;
     __shared__ __attribute__((aligned(16))) int lds[Cfg::kWords];
-    int* const ring = lds + Cfg::kRing;
-    int* const vring = lds + Cfg::kValRing;
+    int* const ring = lds + Cfg::kRing;      // A ring; B ring at ring + kSide
+    int* const vring = lds + Cfg::kValRing;  // payload rings, same layout
     int* const stage = lds + Cfg::kStage;
     int* const vstage = lds + Cfg::kValStage;
     int* const split = lds + Cfg::kSplit;
@@ -276,7 +495,7 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
     {
         SideRange ra, rb, none;
         none.set(As, a_base, 0, 0);
-        Refill<THREADS, ITEMS, kMask> fa, fb;
+        RefillT fa, fb;
         ra.set(As, a_base, 0, a_loaded);
         rb.set(Bs, b_base, 0, b_loaded);
         fa.issue(ra, none, tid);
@@ -302,12 +521,13 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
         const int wb = b_loaded - b_cons;
         const int sa = (a_base + a_cons) & kMask;  // slot of the window's first A
         const int sb = (b_base + b_cons) & kMask;
+        const int* const ring_a = ring;
+        const int* const ring_b = ring + kSide;
 
-        // Co-rank of the end of this lane's slice, searched in the ring.
+        // Co-rank of the end of this lane's slice, searched in the ring; the
+        // lane's start is its left neighbour's end.
         const int c_end = (tid + 1) * ITEMS < c_tile ? (tid + 1) * ITEMS : c_tile;
-        const int e = co_rank<int>(
-            c_end, wa, wb, [=](int x) { return ring[(sa + x) & kMask]; },
-            [=](int x) { return ring[kCap + ((sb + x) & kMask)]; }, kMaxStepsTile);
+        const int e = co_rank_tile<Cfg::kSearchSteps, kMask>(c_end, wa, wb, ring_a, sa, ring_b, sb);
         split[tid] = e;
         __syncthreads();
         // A elements this tile consumes; the same for every lane, so it is
@@ -317,12 +537,13 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
         const int s = tid > 0 ? split[tid - 1] : 0;
 
         // Prefetch the next refill: exactly what this tile consumes, clamped
-        // to what is left of the segment.
+        // to what is left of the segment.  It is in flight while this tile
+        // is merged and stored.
         const int a_cons2 = a_cons + x_t;
         const int b_cons2 = b_cons + (c_tile - x_t);
         const int a_loaded2 = a_cons2 + kTile < a_len ? a_cons2 + kTile : a_len;
         const int b_loaded2 = b_cons2 + kTile < b_len ? b_cons2 + kTile : b_len;
-        Refill<THREADS, ITEMS, kMask> rf, rv;
+        RefillT rf, rv;
         {
             SideRange ra, rb;
             ra.set(As, a_base, a_loaded, a_loaded2);
@@ -336,44 +557,82 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
             }
         }
 
-        // Sequential merge of this lane's slice, in registers.
-        int out[ITEMS];
-        int src[ITEMS];
-        {
+        // This lane's row of the stage: ITEMS contiguous words.
+        int* const row = stage + stage_word(tid * ITEMS);
+        if (!KV) {
+            // Candidates: the next ITEMS keys of each side from the lane's
+            // split.  The lane's outputs are the ITEMS smallest of them; any
+            // candidate past the lane's own range is >= all of its outputs
+            // (it comes later in the merge), so only candidates past the
+            // window need replacing, by INT_MAX.
+            const int bs = c_beg - s;
+            const int* const pa = ring_a + ((sa + s) & kMask);
+            const int* const pb = ring_b + ((sb + bs) & kMask);
+            int a[ITEMS], b[ITEMS], x[ITEMS];
+#pragma unroll
+            for (int t = 0; t < ITEMS; ++t) {
+                a[t] = pa[t];
+                b[t] = pb[t];
+            }
+            if (s + ITEMS > wa || bs + ITEMS > wb) {
+#pragma unroll
+                for (int t = 0; t < ITEMS; ++t) {
+                    a[t] = s + t < wa ? a[t] : INT32_MAX;
+                    b[t] = bs + t < wb ? b[t] : INT32_MAX;
+                }
+            }
+            // a ascending followed by b descending is bitonic; the pairwise
+            // minima hold its ITEMS smallest, themselves bitonic.
+#pragma unroll
+            for (int t = 0; t < ITEMS; ++t) x[t] = min(a[t], b[ITEMS - 1 - t]);
+            bitonic_clean<ITEMS>(x);
+#pragma unroll
+            for (int v = 0; v < ITEMS / 4; ++v) {
+                int4v q;
+                q.x = x[4 * v];
+                q.y = x[4 * v + 1];
+                q.z = x[4 * v + 2];
+                q.w = x[4 * v + 3];
+                *reinterpret_cast<int4v*>(row + 4 * v) = q;
+            }
+        } else {
+            // Key+payload: the serial two-pointer merge of the lane's exact
+            // ranges, so equal keys keep A's payloads first.
+            int out[ITEMS];
+            int src[ITEMS];
             int a = s;
             int b = c_beg - s;
             const int a_end = e;
             const int b_end = c_end - e;
-            int ka = ring[(sa + a) & kMask];
-            int kb = ring[kCap + ((sb + b) & kMask)];
+            int ka = ring_a[(sa + a) & kMask];
+            int kb = ring_b[(sb + b) & kMask];
 #pragma unroll
             for (int t = 0; t < ITEMS; ++t) {
                 const bool take_a = a < a_end && (b >= b_end || ka <= kb);
                 out[t] = take_a ? ka : kb;
-                if (KV) {
-                    src[t] = take_a ? Cfg::kValRing + ((sa + a + d_a) & kMask)
-                                    : Cfg::kValRing + kCap + ((sb + b + d_b) & kMask);
-                }
+                src[t] = take_a ? ((sa + a + d_a) & kMask) : kSide + ((sb + b + d_b) & kMask);
                 a += take_a ? 1 : 0;
                 b += take_a ? 0 : 1;
                 if (t + 1 < ITEMS) {
-                    const int w = take_a ? ((sa + a) & kMask) : kCap + ((sb + b) & kMask);
+                    const int w = take_a ? ((sa + a) & kMask) : kSide + ((sb + b) & kMask);
                     const int nxt = ring[w];
                     ka = take_a ? nxt : ka;
                     kb = take_a ? kb : nxt;
                 }
             }
-        }
-        const int my_len = c_end - c_beg;
+            int* const vrow = vstage + stage_word(tid * ITEMS);
 #pragma unroll
-        for (int t = 0; t < ITEMS; ++t) {
-            if (t < my_len) {
-                stage[stage_at(c_beg + t)] = out[t];
-                if (KV) vstage[stage_at(c_beg + t)] = lds[src[t]];
+            for (int t = 0; t < ITEMS; ++t) {
+                row[t] = out[t];
+                vrow[t] = vring[src[t]];
             }
         }
         __syncthreads();
 
+        // Coalesced 16-byte stores of the whole tile.  (Storing each lane's
+        // ITEMS outputs straight from registers frees the stage's LDS but
+        // measured 10% slower, and 2.3x slower with nontemporal stores: the
+        // 16-byte pieces of a line then reach HBM separately.)
         store_tile<THREADS, ITEMS>(Cs + c_done, c_tile, stage, tid);
         if (KV) {
             store_tile<THREADS, ITEMS>(reinterpret_cast<int32_t*>(Cv + k0) + c_done,

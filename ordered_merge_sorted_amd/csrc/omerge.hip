@@ -15,12 +15,34 @@ namespace {
 
 constexpr int kVersion = 100;  // 0.1.0
 
-// Kernel shapes.  256 lanes = 4 wavefronts per workgroup.  Key-only tiles
-// hold 4096 outputs; key+payload tiles hold 2048 so both fit three
-// workgroups per CU in the 160 KB of LDS.
-constexpr int kThreads = 256;
-constexpr int kItemsI32 = 16;
-constexpr int kItemsKV = 8;
+// Kernel shapes (compile-time tunables; the defaults are the measured best
+// on MI355X).  256 lanes = 4 wavefronts per workgroup.  Key-only tiles hold
+// 4096 outputs; key+payload tiles hold 2048 so both fit three workgroups per
+// CU in the 160 KB of LDS.
+#ifndef OMERGE_THREADS
+#define OMERGE_THREADS 256
+#endif
+#ifndef OMERGE_ITEMS_I32
+#define OMERGE_ITEMS_I32 16
+#endif
+#ifndef OMERGE_ITEMS_KV
+#define OMERGE_ITEMS_KV 8
+#endif
+#ifndef OMERGE_PART_LANES  // lanes per boundary in the partition search (1 = pages' loop)
+#define OMERGE_PART_LANES 4
+#endif
+#ifndef OMERGE_MAX_TILES_PER_SEG
+#define OMERGE_MAX_TILES_PER_SEG 32
+#endif
+#ifndef OMERGE_COPY_UNROLL
+#define OMERGE_COPY_UNROLL 4
+#endif
+constexpr int kThreads = OMERGE_THREADS;
+constexpr int kItemsI32 = OMERGE_ITEMS_I32;
+constexpr int kItemsKV = OMERGE_ITEMS_KV;
+constexpr int kPartLanes = OMERGE_PART_LANES;
+constexpr int kMaxTilesPerSeg = OMERGE_MAX_TILES_PER_SEG;
+constexpr int kCopyUnroll = OMERGE_COPY_UNROLL;  // 16-byte vectors per lane in the copy
 using CfgI32 = MergeCfg<kThreads, kItemsI32, false>;
 using CfgKV = MergeCfg<kThreads, kItemsKV, true>;
 
@@ -78,13 +100,13 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Segment length: a whole number R of tiles per workgroup.  Every segment
 // costs the same, so the kernel runs in ceil(P / slots) rounds of R tiles,
 // where P = segments and slots = workgroups resident on the chip.  Pick the
-// R in [1, 32] that wastes the least of the last round, preferring longer
+// R in [1, kMaxTilesPerSeg] that wastes the least of the last round, preferring longer
 // segments (fewer co-rank searches, fewer ring prologues) on a tie.
 int64_t choose_seg_len(int64_t total, int tile, int slots) {
     const int64_t tiles = ceil_div(total, tile);
     int64_t best_r = 1;
     double best_eff = -1.0;
-    for (int64_t r = 1; r <= 32; ++r) {
+    for (int64_t r = 1; r <= kMaxTilesPerSeg; ++r) {
         const int64_t segs = ceil_div(tiles, r);
         const int64_t rounds = ceil_div(segs, slots);
         const double eff = double(tiles) / double(rounds * r * slots);
@@ -124,10 +146,10 @@ int check_seg_len(int64_t seg_len) {
 int launch_partition(const int32_t* A, int64_t m, const int32_t* B, int64_t n,
                      int64_t seg_len, int64_t* part, hipStream_t stream) {
     const int64_t count = ceil_div(m + n, seg_len) + 1;
-    const int64_t blocks = ceil_div(count, kThreads);
+    const int64_t blocks = ceil_div(count * kPartLanes, 256);
     if (blocks > kMaxGridBlocks) return OMERGE_OVERFLOW;
-    hipLaunchKernelGGL(partition_kernel, dim3(static_cast<unsigned>(blocks)),
-                       dim3(kThreads), 0, stream, A, m, B, n, seg_len, count, part);
+    hipLaunchKernelGGL(partition_kernel<kPartLanes>, dim3(static_cast<unsigned>(blocks)),
+                       dim3(256), 0, stream, A, m, B, n, seg_len, count, part);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? OMERGE_OK : hip_fail(e);
 }
@@ -302,6 +324,18 @@ int omerge_merge_segments_kv(const int32_t* A_keys, const uint32_t* A_vals,
     if (m + n == 0) return OMERGE_OK;
     return launch_merge<true>(A_keys, A_vals, m, B_keys, B_vals, n, part, seg_len, C_keys,
                               C_vals, stream);
+}
+
+int omerge_stream_copy(const int32_t* src, int64_t n, int32_t* dst, hipStream_t stream) {
+    if (bad_array(src, n) || bad_array(dst, n) || overlaps(src, n, dst, n)) return OMERGE_INVALID_ARG;
+    if (n == 0) return OMERGE_OK;
+    if (n > kMaxTotal) return OMERGE_OVERFLOW;
+    const int64_t blocks = ceil_div(ceil_div(n, 4), int64_t(256) * kCopyUnroll);
+    if (blocks > kMaxGridBlocks) return OMERGE_OVERFLOW;
+    hipLaunchKernelGGL(stream_copy_kernel<kCopyUnroll>, dim3(static_cast<unsigned>(blocks)),
+                       dim3(256), 0, stream, src, n, dst);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? OMERGE_OK : hip_fail(e);
 }
 
 const char* omerge_status_string(int status) {

@@ -54,6 +54,7 @@ def load_library() -> ctypes.CDLL:
         "omerge_partition": (i32, [p, i64, p, i64, i64, p, p]),
         "omerge_merge_segments_i32": (i32, [p, i64, p, i64, p, i64, p, p]),
         "omerge_merge_segments_kv": (i32, [p, p, i64, p, p, i64, p, i64, p, p, p]),
+        "omerge_stream_copy": (i32, [p, i64, p, p]),
         "omerge_status_string": (ctypes.c_char_p, [i32]),
         "omerge_last_hip_error": (i32, []),
         "omerge_version": (i32, []),
@@ -243,3 +244,16 @@ def merge_segments_kv(a_keys, a_vals, b_keys, b_vals, part, seg_len, out_keys=No
             _stream(dev, stream))
     _raise_on(rc, "omerge_merge_segments_kv")
     return out_keys, out_vals
+
+
+def stream_copy(src: torch.Tensor, out: Optional[torch.Tensor] = None,
+                stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Measurement reference: copy an int32 tensor with the library's
+    16-byte streaming copy kernel (the bytes a merge of as many outputs moves)."""
+    _vec(src, "src", (torch.int32,))
+    out = _out(out, src.numel(), torch.int32, src.device, "out")
+    lib = load_library()
+    with torch.cuda.device(src.device):
+        rc = lib.omerge_stream_copy(_ptr(src), src.numel(), _ptr(out), _stream(src.device, stream))
+    _raise_on(rc, "omerge_stream_copy")
+    return out

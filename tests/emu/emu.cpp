@@ -19,10 +19,29 @@ EmuDim3 gridDim;
 static std::barrier<>* g_barrier = nullptr;
 void __syncthreads() { g_barrier->arrive_and_wait(); }
 
+// Per-wavefront vote: lanes post their predicate, meet, read all 64, meet again.
+struct WaveVote {
+    std::barrier<> bar{64};
+    int pred[64] = {};
+};
+static std::vector<WaveVote>* g_waves = nullptr;
+unsigned long long __ballot(int pred) {
+    WaveVote& w = (*g_waves)[threadIdx.x / 64];
+    const int lane = threadIdx.x % 64;
+    w.pred[lane] = pred != 0;
+    w.bar.arrive_and_wait();
+    unsigned long long mask = 0;
+    for (int l = 0; l < 64; ++l) mask |= static_cast<unsigned long long>(w.pred[l]) << l;
+    w.bar.arrive_and_wait();
+    return mask;
+}
+
 // Runs `body` for every workgroup 0..blocks-1 with `threads` lanes each.
 static void run_grid(int64_t blocks, int threads, const std::function<void()>& body) {
     std::barrier<> bar(threads);
     g_barrier = &bar;
+    std::vector<WaveVote> waves(threads / 64);
+    g_waves = &waves;
     blockDim = {static_cast<unsigned>(threads), 1, 1};
     gridDim = {static_cast<unsigned>(blocks), 1, 1};
     std::vector<std::thread> pool;
@@ -60,11 +79,21 @@ int emu_tile(int variant, int kv) {
     return omerge::MergeCfg<64, 4, false>::kTile;
 }
 
-void emu_partition(const int32_t* A, int64_t m, const int32_t* B, int64_t n, int64_t seg_len,
-                   int64_t* part) {
+// lanes = lanes per boundary in the partition search (1, 4, 8, 16, 64).
+void emu_partition(int lanes, const int32_t* A, int64_t m, const int32_t* B, int64_t n,
+                   int64_t seg_len, int64_t* part) {
     const int64_t count = (m + n + seg_len - 1) / seg_len + 1;
-    const int64_t blocks = (count + 255) / 256;
-    run_grid(blocks, 256, [&] { omerge::partition_kernel(A, m, B, n, seg_len, count, part); });
+    const int64_t blocks = (count * lanes + 255) / 256;
+    auto go = [&](auto kernel) {
+        run_grid(blocks, 256, [&] { kernel(A, m, B, n, seg_len, count, part); });
+    };
+    switch (lanes) {
+        case 1: go(omerge::partition_kernel<1>); break;
+        case 4: go(omerge::partition_kernel<4>); break;
+        case 8: go(omerge::partition_kernel<8>); break;
+        case 16: go(omerge::partition_kernel<16>); break;
+        default: go(omerge::partition_kernel<64>); break;
+    }
 }
 
 void emu_co_rank(const int32_t* A, int64_t m, const int32_t* B, int64_t n, const int64_t* ks,

@@ -24,3 +24,11 @@ extern thread_local EmuDim3 blockIdx;
 extern EmuDim3 blockDim;
 extern EmuDim3 gridDim;
 void __syncthreads();
+// Wavefront vote: every lane of the 64-lane wavefront must call it together
+// (the emulator meets them at a per-wavefront barrier).
+unsigned long long __ballot(int pred);
+inline int __popcll(unsigned long long x) { return __builtin_popcountll(x); }
+template <typename T>
+inline T min(T a, T b) { return b < a ? b : a; }
+template <typename T>
+inline T max(T a, T b) { return a < b ? b : a; }

@@ -24,16 +24,25 @@ def _asan_runtime():
     return hits[0] if hits else None
 
 
-@pytest.fixture(scope="module")
-def libemu(tmp_path_factory):
+# Compile-time variants of the kernels: the default build (nontemporal
+# streaming accesses) and plain accesses.
+FLAG_SETS = {
+    "default": [],
+    "plain_access": ["-DOMERGE_NT_LOADS=0", "-DOMERGE_NT_STORES=0"],
+}
+
+
+@pytest.fixture(scope="module", params=sorted(FLAG_SETS))
+def libemu(request, tmp_path_factory):
     clang = os.path.join(LLVM, "bin/clang++")
     rt = _asan_runtime()
     if not os.path.exists(clang) or rt is None:
         pytest.skip("host clang++ with the ASan runtime is not installed")
-    out = str(tmp_path_factory.mktemp("emu") / "libemu.so")
+    out = str(tmp_path_factory.mktemp("emu") / ("libemu_%s.so" % request.param))
     san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-shared-libsan"]
     subprocess.check_call(
         [clang, "-std=c++20", "-O1", "-g", "-fPIC", "-shared", "-fno-omit-frame-pointer", *san,
+         *FLAG_SETS[request.param],
          "-I" + os.path.join(HERE, "emu"),
          "-I" + os.path.join(ROOT, "ordered_merge_sorted_amd", "csrc"),
          os.path.join(HERE, "emu", "emu.cpp"), "-o", out])
