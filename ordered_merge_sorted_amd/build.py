@@ -18,13 +18,15 @@ CSRC = os.path.join(PKG, "csrc")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIB_DIR, "libomerge.so")
 SOURCES = [os.path.join(CSRC, "omerge.hip")]
+INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 DEPENDS = SOURCES + [os.path.join(CSRC, f) for f in ("corank.hpp", "merge_kernel.hpp")] + [
-    os.path.join(os.path.dirname(PKG), "include", "omerge.h")]
+    os.path.join(INCLUDE, "omerge.h")]
 
 ARCH = "gfx950"
 HIPCC_FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I" + INCLUDE,
 ]
 
 

@@ -7,7 +7,7 @@
 
 #include <mutex>
 
-#include "../../include/omerge.h"
+#include "omerge.h"
 #include "merge_kernel.hpp"
 
 namespace omerge {
@@ -31,8 +31,8 @@ constexpr int kVersion = 100;  // 0.1.0
 #ifndef OMERGE_PART_LANES  // lanes per boundary in the partition search (1 = pages' loop)
 #define OMERGE_PART_LANES 4
 #endif
-#ifndef OMERGE_MAX_TILES_PER_SEG
-#define OMERGE_MAX_TILES_PER_SEG 32
+#ifndef OMERGE_TILES_PER_SEG  // target tiles per workgroup segment
+#define OMERGE_TILES_PER_SEG 8
 #endif
 #ifndef OMERGE_COPY_UNROLL
 #define OMERGE_COPY_UNROLL 4
@@ -41,7 +41,9 @@ constexpr int kThreads = OMERGE_THREADS;
 constexpr int kItemsI32 = OMERGE_ITEMS_I32;
 constexpr int kItemsKV = OMERGE_ITEMS_KV;
 constexpr int kPartLanes = OMERGE_PART_LANES;
-constexpr int kMaxTilesPerSeg = OMERGE_MAX_TILES_PER_SEG;
+constexpr int kTargetTilesPerSeg = OMERGE_TILES_PER_SEG;
+constexpr int kMinTilesPerSeg = kTargetTilesPerSeg > 2 ? kTargetTilesPerSeg - 2 : 1;
+constexpr int kMaxTilesPerSeg = kTargetTilesPerSeg + 2;
 constexpr int kCopyUnroll = OMERGE_COPY_UNROLL;  // 16-byte vectors per lane in the copy
 using CfgI32 = MergeCfg<kThreads, kItemsI32, false>;
 using CfgKV = MergeCfg<kThreads, kItemsKV, true>;
@@ -97,24 +99,35 @@ int device_info(DeviceInfo* out) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Segment length: a whole number R of tiles per workgroup.  Every segment
-// costs the same, so the kernel runs in ceil(P / slots) rounds of R tiles,
-// where P = segments and slots = workgroups resident on the chip.  Pick the
-// R in [1, kMaxTilesPerSeg] that wastes the least of the last round, preferring longer
-// segments (fewer co-rank searches, fewer ring prologues) on a tie.
+// Segment length: a whole number R of tiles per workgroup.  Two costs pull
+// R in opposite directions.  The partition reads a few random cache lines
+// per boundary, so short segments make it expensive (131072 one-tile
+// segments of the 2^28+2^28 merge: 0.21 ms of partition).  Long segments
+// spread the workgroups resident at one time over a wide span of A, B and C
+// (about slots*R tiles), and HBM serves such scattered streams more slowly
+// than one compact moving window (the same merge at 19 tiles per segment:
+// 0.827 ms; at 8: 0.799 ms).  Measured on MI355X, R = 8 balances the two;
+// the window [6, 10] is searched for the R whose last round of workgroups is
+// fullest.  Inputs with fewer tiles than about 6 rounds' worth get the
+// smallest R that keeps a single round.
 int64_t choose_seg_len(int64_t total, int tile, int slots) {
     const int64_t tiles = ceil_div(total, tile);
-    int64_t best_r = 1;
-    double best_eff = -1.0;
-    for (int64_t r = 1; r <= kMaxTilesPerSeg; ++r) {
+    if (tiles <= int64_t(slots) * kMinTilesPerSeg) {
+        const int64_t r = ceil_div(tiles, slots);
+        return (r < 1 ? 1 : r) * tile;
+    }
+    int64_t best_r = kTargetTilesPerSeg;
+    double best_score = -1.0;
+    for (int64_t r = kMinTilesPerSeg; r <= kMaxTilesPerSeg; ++r) {
         const int64_t segs = ceil_div(tiles, r);
         const int64_t rounds = ceil_div(segs, slots);
         const double eff = double(tiles) / double(rounds * r * slots);
-        if (eff >= best_eff * 0.999) {
-            best_eff = eff > best_eff ? eff : best_eff;
+        const int64_t off = r > kTargetTilesPerSeg ? r - kTargetTilesPerSeg : kTargetTilesPerSeg - r;
+        const double score = eff - 0.004 * double(off);  // prefer R near the target
+        if (score > best_score) {
+            best_score = score;
             best_r = r;
         }
-        if (segs == 1) break;
     }
     return best_r * tile;
 }

@@ -71,12 +71,12 @@ static void merge_cfg(const int32_t* A, const uint32_t* Av, int64_t m, const int
 
 extern "C" {
 
-// variant 0 = the shapes the library launches; 1 = small shapes (64 lanes,
+// variant 0 = the shapes the library launches; 1 = small shapes (128 lanes,
 // 4 items) that wrap the rings many times on small inputs.
 int emu_tile(int variant, int kv) {
     if (variant == 0) return kv ? omerge::MergeCfg<256, 8, true>::kTile
                                 : omerge::MergeCfg<256, 16, false>::kTile;
-    return omerge::MergeCfg<64, 4, false>::kTile;
+    return omerge::MergeCfg<128, 4, false>::kTile;
 }
 
 // lanes = lanes per boundary in the partition search (1, 4, 8, 16, 64).
@@ -107,7 +107,7 @@ void emu_merge_i32(int variant, const int32_t* A, int64_t m, const int32_t* B, i
     if (variant == 0)
         merge_cfg<256, 16, false>(A, nullptr, m, B, nullptr, n, part, seg_len, C, nullptr);
     else
-        merge_cfg<64, 4, false>(A, nullptr, m, B, nullptr, n, part, seg_len, C, nullptr);
+        merge_cfg<128, 4, false>(A, nullptr, m, B, nullptr, n, part, seg_len, C, nullptr);
 }
 
 void emu_merge_kv(int variant, const int32_t* A, const uint32_t* Av, int64_t m, const int32_t* B,
@@ -116,7 +116,7 @@ void emu_merge_kv(int variant, const int32_t* A, const uint32_t* Av, int64_t m, 
     if (variant == 0)
         merge_cfg<256, 8, true>(A, Av, m, B, Bv, n, part, seg_len, C, Cv);
     else
-        merge_cfg<64, 4, true>(A, Av, m, B, Bv, n, part, seg_len, C, Cv);
+        merge_cfg<128, 4, true>(A, Av, m, B, Bv, n, part, seg_len, C, Cv);
 }
 
 }  // extern "C"
