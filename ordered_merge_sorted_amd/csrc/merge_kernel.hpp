@@ -437,6 +437,42 @@ __device__ __forceinline__ void store_tile(int32_t* __restrict__ dst, int len,
     }
 }
 
+// Stores a one-sided tile straight from a ring window: output p is the
+// window's element p, at ring slot (start + p) & MASK.  Consecutive lanes read
+// consecutive slots (no bank conflicts); 16-byte reads when the ring quads
+// line up with the output's 16-byte vectors, single words otherwise.
+template <int THREADS, int V, int MASK>
+__device__ __forceinline__ void store_from_ring(int32_t* __restrict__ dst, int len,
+                                                const int* side, int start, int tid) {
+    const int head0 = (4 - (word_phase(dst) & 3)) & 3;
+    const int head = head0 < len ? head0 : len;
+    const int nvec = (len - head) >> 2;
+    const int tail = (len - head) & 3;
+    const bool quads = ((start + head) & 3) == 0;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        const int q = tid + v * THREADS;
+        if (q < nvec) {
+            const int p = head + 4 * q;
+            int4v x;
+            if (quads) {
+                x = *reinterpret_cast<const int4v*>(side + ((start + p) & MASK));
+            } else {
+                x.x = side[(start + p) & MASK];
+                x.y = side[(start + p + 1) & MASK];
+                x.z = side[(start + p + 2) & MASK];
+                x.w = side[(start + p + 3) & MASK];
+            }
+            store_stream4(dst + p, x);
+        }
+    }
+    if (tid < head) dst[tid] = side[(start + tid) & MASK];
+    if (tid >= 4 && tid - 4 < tail) {
+        const int p = head + 4 * nvec + (tid - 4);
+        dst[p] = side[(start + p) & MASK];
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Segment merge kernel: one workgroup per segment of the output.
 
@@ -522,6 +558,7 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
     }
     __syncthreads();
 
+    bool probe_one_sided = true;  // test the first tile up front
     for (int c_done = 0; c_done < c_len;) {
         const int c_tile = c_len - c_done < kTile ? c_len - c_done : kTile;
         const int wa = a_loaded - a_cons;  // A window in the ring: min(TILE, left)
@@ -531,17 +568,39 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
         const int* const ring_a = ring;
         const int* const ring_b = ring + kSide;
 
+        // One-sided tile: every output comes from one side when the tile's
+        // last A precedes the first B (A wins ties), or the tile's last B
+        // precedes the first A.  Then the tile is a copy of that side's window:
+        // no sort and no stage.  Such tiles come in runs (skewed inputs, long
+        // runs of equal keys), so the check is made up front -- skipping the
+        // searches too -- only after a one-sided tile; otherwise the searches'
+        // own result (x_t = 0 or c_tile) detects it at no extra cost.
+        int side = 0;  // 0: general tile, 1: all from A, 2: all from B
+        if (probe_one_sided) {
+            const bool all_a =
+                wa >= c_tile && (wb == 0 || ring_a[(sa + c_tile - 1) & kMask] <= ring_b[sb]);
+            const bool all_b = !all_a && wb >= c_tile &&
+                               (wa == 0 || ring_b[(sb + c_tile - 1) & kMask] < ring_a[sa]);
+            side = __builtin_amdgcn_readfirstlane(all_a ? 1 : (all_b ? 2 : 0));
+        }
+
         // Co-rank of the end of this lane's slice, searched in the ring; the
         // lane's start is its left neighbour's end.
         const int c_end = (tid + 1) * ITEMS < c_tile ? (tid + 1) * ITEMS : c_tile;
-        const int e = co_rank_tile<Cfg::kSearchSteps, kMask>(c_end, wa, wb, ring_a, sa, ring_b, sb);
-        split[tid] = e;
-        __syncthreads();
-        // A elements this tile consumes; the same for every lane, so it is
-        // moved to a scalar register and the refill bookkeeping stays scalar.
-        const int x_t = __builtin_amdgcn_readfirstlane(split[THREADS - 1]);
-        const int c_beg = tid * ITEMS < c_tile ? tid * ITEMS : c_tile;
-        const int s = tid > 0 ? split[tid - 1] : 0;
+        int e = 0;
+        int x_t;  // A elements this tile consumes
+        if (side == 0) {
+            e = co_rank_tile<Cfg::kSearchSteps, kMask>(c_end, wa, wb, ring_a, sa, ring_b, sb);
+            split[tid] = e;
+            __syncthreads();
+            // The same for every lane, so it is moved to a scalar register and
+            // the refill bookkeeping stays scalar.
+            x_t = __builtin_amdgcn_readfirstlane(split[THREADS - 1]);
+            side = x_t == c_tile ? 1 : (x_t == 0 ? 2 : 0);
+        } else {
+            x_t = side == 1 ? c_tile : 0;
+        }
+        probe_one_sided = side != 0;
 
         // Prefetch the next refill: exactly what this tile consumes, clamped
         // to what is left of the segment.  It is in flight while this tile
@@ -564,94 +623,112 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
             }
         }
 
-        // This lane's row of the stage: ITEMS contiguous words.
-        int* const row = stage + stage_word(tid * ITEMS);
-        if (!KV) {
-            // Candidates: the next ITEMS keys of each side from the lane's
-            // split.  The lane's outputs are the ITEMS smallest of them; any
-            // candidate past the lane's own range is >= all of its outputs
-            // (it comes later in the merge), so only candidates past the
-            // window need replacing, by INT_MAX.
-            const int bs = c_beg - s;
-            const int* const pa = ring_a + ((sa + s) & kMask);
-            const int* const pb = ring_b + ((sb + bs) & kMask);
-            int a[ITEMS], b[ITEMS], x[ITEMS];
-#pragma unroll
-            for (int t = 0; t < ITEMS; ++t) {
-                a[t] = pa[t];
-                b[t] = pb[t];
+        if (side != 0) {
+            const int* const win = side == 1 ? ring_a : ring_b;
+            const int start = side == 1 ? sa : sb;
+            store_from_ring<THREADS, kStoreVec, kMask>(Cs + c_done, c_tile, win, start, tid);
+            if (KV) {
+                const int* const vwin = side == 1 ? vring : vring + kSide;
+                const int vstart = side == 1 ? (sa + d_a) & kMask : (sb + d_b) & kMask;
+                store_from_ring<THREADS, kStoreVec, kMask>(
+                    reinterpret_cast<int32_t*>(Cv + k0) + c_done, c_tile, vwin, vstart, tid);
             }
-            if (s + ITEMS > wa || bs + ITEMS > wb) {
-#pragma unroll
-                for (int t = 0; t < ITEMS; ++t) {
-                    a[t] = s + t < wa ? a[t] : INT32_MAX;
-                    b[t] = bs + t < wb ? b[t] : INT32_MAX;
-                }
-            }
-            // a ascending followed by b descending is bitonic; the pairwise
-            // minima hold its ITEMS smallest, themselves bitonic.
-#pragma unroll
-            for (int t = 0; t < ITEMS; ++t) x[t] = min(a[t], b[ITEMS - 1 - t]);
-            bitonic_clean<ITEMS>(x);
-#pragma unroll
-            for (int v = 0; v < ITEMS / 4; ++v) {
-                int4v q;
-                q.x = x[4 * v];
-                q.y = x[4 * v + 1];
-                q.z = x[4 * v + 2];
-                q.w = x[4 * v + 3];
-                *reinterpret_cast<int4v*>(row + 4 * v) = q;
-            }
+            __syncthreads();  // every read of the consumed slots is done
+            rf.commit(ring, tid);
+            if (KV) rv.commit(vring, tid);
         } else {
-            // Key+payload: the serial two-pointer merge of the lane's exact
-            // ranges, so equal keys keep A's payloads first.
-            int out[ITEMS];
-            int src[ITEMS];
-            int a = s;
-            int b = c_beg - s;
-            const int a_end = e;
-            const int b_end = c_end - e;
-            int ka = ring_a[(sa + a) & kMask];
-            int kb = ring_b[(sb + b) & kMask];
-#pragma unroll
-            for (int t = 0; t < ITEMS; ++t) {
-                const bool take_a = a < a_end && (b >= b_end || ka <= kb);
-                out[t] = take_a ? ka : kb;
-                src[t] = take_a ? ((sa + a + d_a) & kMask) : kSide + ((sb + b + d_b) & kMask);
-                a += take_a ? 1 : 0;
-                b += take_a ? 0 : 1;
-                if (t + 1 < ITEMS) {
-                    const int w = take_a ? ((sa + a) & kMask) : kSide + ((sb + b) & kMask);
-                    const int nxt = ring[w];
-                    ka = take_a ? nxt : ka;
-                    kb = take_a ? kb : nxt;
+            const int c_beg = tid * ITEMS < c_tile ? tid * ITEMS : c_tile;
+            const int s = tid > 0 ? split[tid - 1] : 0;
+
+            // This lane's row of the stage: ITEMS contiguous words.
+            int* const row = stage + stage_word(tid * ITEMS);
+            if (!KV) {
+                // Candidates: the next ITEMS keys of each side from the lane's
+                // split.  The lane's outputs are the ITEMS smallest of them; any
+                // candidate past the lane's own range is >= all of its outputs
+                // (it comes later in the merge), so only candidates past the
+                // window need replacing, by INT_MAX.
+                const int bs = c_beg - s;
+                const int* const pa = ring_a + ((sa + s) & kMask);
+                const int* const pb = ring_b + ((sb + bs) & kMask);
+                int a[ITEMS], b[ITEMS], x[ITEMS];
+    #pragma unroll
+                for (int t = 0; t < ITEMS; ++t) {
+                    a[t] = pa[t];
+                    b[t] = pb[t];
+                }
+                if (s + ITEMS > wa || bs + ITEMS > wb) {
+    #pragma unroll
+                    for (int t = 0; t < ITEMS; ++t) {
+                        a[t] = s + t < wa ? a[t] : INT32_MAX;
+                        b[t] = bs + t < wb ? b[t] : INT32_MAX;
+                    }
+                }
+                // a ascending followed by b descending is bitonic; the pairwise
+                // minima hold its ITEMS smallest, themselves bitonic.
+    #pragma unroll
+                for (int t = 0; t < ITEMS; ++t) x[t] = min(a[t], b[ITEMS - 1 - t]);
+                bitonic_clean<ITEMS>(x);
+    #pragma unroll
+                for (int v = 0; v < ITEMS / 4; ++v) {
+                    int4v q;
+                    q.x = x[4 * v];
+                    q.y = x[4 * v + 1];
+                    q.z = x[4 * v + 2];
+                    q.w = x[4 * v + 3];
+                    *reinterpret_cast<int4v*>(row + 4 * v) = q;
+                }
+            } else {
+                // Key+payload: the serial two-pointer merge of the lane's exact
+                // ranges, so equal keys keep A's payloads first.
+                int out[ITEMS];
+                int src[ITEMS];
+                int a = s;
+                int b = c_beg - s;
+                const int a_end = e;
+                const int b_end = c_end - e;
+                int ka = ring_a[(sa + a) & kMask];
+                int kb = ring_b[(sb + b) & kMask];
+    #pragma unroll
+                for (int t = 0; t < ITEMS; ++t) {
+                    const bool take_a = a < a_end && (b >= b_end || ka <= kb);
+                    out[t] = take_a ? ka : kb;
+                    src[t] = take_a ? ((sa + a + d_a) & kMask) : kSide + ((sb + b + d_b) & kMask);
+                    a += take_a ? 1 : 0;
+                    b += take_a ? 0 : 1;
+                    if (t + 1 < ITEMS) {
+                        const int w = take_a ? ((sa + a) & kMask) : kSide + ((sb + b) & kMask);
+                        const int nxt = ring[w];
+                        ka = take_a ? nxt : ka;
+                        kb = take_a ? kb : nxt;
+                    }
+                }
+                int* const vrow = vstage + stage_word(tid * ITEMS);
+    #pragma unroll
+                for (int t = 0; t < ITEMS; ++t) {
+                    row[t] = out[t];
+                    vrow[t] = vring[src[t]];
                 }
             }
-            int* const vrow = vstage + stage_word(tid * ITEMS);
-#pragma unroll
-            for (int t = 0; t < ITEMS; ++t) {
-                row[t] = out[t];
-                vrow[t] = vring[src[t]];
+            __syncthreads();
+
+            // Commit the refill before this tile's stores go out: the wait on
+            // the vector-memory counter (which counts loads and stores alike)
+            // then covers the refill loads and only stores issued a whole tile
+            // earlier.  The refill lands in the slots this tile consumed.
+            rf.commit(ring, tid);
+            if (KV) rv.commit(vring, tid);
+
+            // Coalesced 16-byte stores of the whole tile.  (Storing each lane's
+            // ITEMS outputs straight from registers frees the stage's LDS but
+            // measured 10% slower, and 2.3x slower with nontemporal stores: the
+            // 16-byte pieces of a line then reach HBM apart.)
+            store_tile<THREADS, kStoreVec>(Cs + c_done, c_tile, stage, tid);
+            if (KV) {
+                store_tile<THREADS, kStoreVec>(reinterpret_cast<int32_t*>(Cv + k0) + c_done,
+                                               c_tile, vstage, tid);
             }
-        }
-        __syncthreads();
-
-        // Commit the refill before this tile's stores go out: the wait on
-        // the vector-memory counter (which counts loads and stores alike)
-        // then covers the refill loads and only stores issued a whole tile
-        // earlier.  The refill lands in the slots this tile consumed.
-        rf.commit(ring, tid);
-        if (KV) rv.commit(vring, tid);
-
-        // Coalesced 16-byte stores of the whole tile.  (Storing each lane's
-        // ITEMS outputs straight from registers frees the stage's LDS but
-        // measured 10% slower, and 2.3x slower with nontemporal stores: the
-        // 16-byte pieces of a line then reach HBM apart.)
-        store_tile<THREADS, kStoreVec>(Cs + c_done, c_tile, stage, tid);
-        if (KV) {
-            store_tile<THREADS, kStoreVec>(reinterpret_cast<int32_t*>(Cv + k0) + c_done,
-                                           c_tile, vstage, tid);
-        }
+        }  // general tile
 
         a_cons = a_cons2;
         b_cons = b_cons2;

@@ -160,6 +160,34 @@ def group_skew(r, g):
         r.case_kv(1, A, B, seg_len, tuple(int(x) for x in g.integers(0, 4, size=6)), "skew")
 
 
+def group_blocks(r, g):
+    """Runs of one side longer than a tile: whole tiles come from A alone or
+    B alone (the one-sided fast path), with mixed tiles at the seams."""
+    tile = r.lib.emu_tile(1, 0)
+    cases = []
+    for c in range(10):
+        L = [int(x) for x in g.integers(1, 6 * tile, size=int(g.integers(2, 7)))]
+        A, B, v = [], [], 0
+        for i, ln in enumerate(L):
+            tgt = A if (i + c) % 2 == 0 else B
+            tgt.extend(range(v, v + ln))
+            v += ln - (2 if c % 3 == 0 else 0)  # seams with equal keys across sides
+        A = np.array(A, dtype=np.int32); B = np.array(B, dtype=np.int32)
+        A.sort(); B.sort()
+        cases.append((A, B))
+    cases.append((np.arange(0, 3000, dtype=np.int32), np.arange(3000, 5000, dtype=np.int32)))
+    cases.append((np.arange(3000, 5000, dtype=np.int32), np.arange(0, 3000, dtype=np.int32)))
+    cases.append((np.full(2000, 7, np.int32), np.full(3000, 7, np.int32)))
+    for A, B in cases:
+        seg_len = int(g.choice([tile, 3 * tile, 4 * int(g.integers(1, 700))]))
+        r.case_i32(1, A, B, seg_len, tuple(int(x) for x in g.integers(0, 4, size=3)), "blocks")
+        r.case_kv(1, A, B, seg_len, tuple(int(x) for x in g.integers(0, 4, size=6)), "blocks")
+    tile0 = r.lib.emu_tile(0, 0)
+    A = np.arange(0, 9000, dtype=np.int32); B = np.arange(9000, 20000, dtype=np.int32)
+    r.case_i32(0, A, B, 3 * tile0, (1, 2, 3), "blocks-prod")
+    r.case_kv(0, B, A, 3 * r.lib.emu_tile(0, 1), (0, 1, 2, 3, 1, 2), "blocks-prod")
+
+
 def group_production(r, g):
     """The shapes the library launches (256 lanes; 4096-output tiles for
     keys, 2048 for key+payload), over several tiles and segments."""
@@ -197,7 +225,7 @@ def group_unsorted(r, g):
         r.cases += 1
 
 
-GROUPS = {"small": group_small, "skew": group_skew,
+GROUPS = {"small": group_small, "skew": group_skew, "blocks": group_blocks,
           "production": group_production, "unsorted": group_unsorted}
 
 if __name__ == "__main__":

@@ -145,6 +145,31 @@ def test_worked_examples():
     assert list(host(gk)) == [1, 1, 1, 2, 2, 2, 3, 4]
 
 
+@pytest.mark.parametrize("layout", ["a_then_b", "b_then_a", "alternating", "equal_seams"])
+def test_one_sided_tiles(layout):
+    """Runs of one side longer than a tile (whole tiles from A alone or B
+    alone), with mixed tiles at the seams."""
+    if layout == "a_then_b":
+        A, B = np.arange(0, 300000, dtype=np.int32), np.arange(300000, 500000, dtype=np.int32)
+    elif layout == "b_then_a":
+        A, B = np.arange(200000, 500000, dtype=np.int32), np.arange(0, 200000, dtype=np.int32)
+    else:
+        g = np.random.Generator(np.random.PCG64(99))
+        runs = g.integers(1, 40000, size=24)
+        A, B, v = [], [], 0
+        for i, ln in enumerate(runs):
+            (A if i % 2 == 0 else B).extend(range(v, v + int(ln)))
+            v += int(ln) - (3 if layout == "equal_seams" else 0)
+        A, B = np.sort(np.array(A, np.int32)), np.sort(np.array(B, np.int32))
+    Av, Bv = tags(A.size, B.size)
+    say("one-sided", layout, A.size, B.size)
+    assert_same(host(om.merge_i32(dev(A), dev(B))), oracle.merge_i32(A, B), "i32")
+    gk, gv = om.merge_kv(dev(A), dev(Av), dev(B), dev(Bv))
+    wk, wv = oracle.merge_kv(A, Av, B, Bv)
+    assert_same(host(gk), wk, "kv keys")
+    assert_same(host(gv).view(np.uint32), wv, "kv payloads")
+
+
 EDGE = [
     (0, 0), (1, 0), (0, 1), (1, 1), (3, 0), (0, 4095), (4095, 1), (4096, 0), (4097, 0),
     (2048, 2048), (2049, 2048), (1, 100000), (100000, 1), (12289, 4093),
