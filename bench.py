@@ -11,10 +11,11 @@ workload is 2^28 + 2^28 int32 keys iid uniform over the int32 range, sorted.
 Before timing, the merged output of one untimed launch is compared with the
 CPU oracle on every element (a wrong answer never produces a number), and the
 oracle run is timed as the reported CPU baseline.  Then W untimed steps, then
-exactly K timed steps between device synchronisations.  HIP events around
-each segment-merge launch give that kernel's mean duration for the roofline
-figure.  A streaming copy of the same byte count is timed beside it as the
-bandwidth this device actually delivers.
+exactly K timed steps back to back between device synchronisations (the step
+rate).  The same K steps are then run again with a HIP event pair around
+every segment-merge launch, which gives that kernel's mean duration for the
+roofline figure.  A streaming copy of the same byte count is timed beside it
+as the bandwidth this device actually delivers.
 
 Prints ONE JSON line on stdout; the device banner and extra figures go to
 stderr.  Only one GPU is used: --gpus above 1 exits with a message.
@@ -96,6 +97,39 @@ def time_oracle(w, arrs, want_runs_s=10.0, max_runs=5):
     return out, rates
 
 
+def ablation(om, d_arrs, want, w, stream):
+    """Global-memory kernels of the pages (no LDS) on the same inputs: one
+    co-rank search then a walk, or two searches per slice, at 1..256 outputs
+    per lane.  Each is checked against the oracle before it is timed."""
+    import torch
+    out = torch.empty(w.total, dtype=torch.int32, device=d_arrs[0].device)
+    log("ablation: global-memory merge kernels vs the LDS-tiled segment merge")
+    log("%-28s %10s %10s %8s" % ("kernel", "ms", "GB/s", "% peak"))
+    for two in (False, True):
+        for per in (1, 4, 16, 64, 256):
+            def go():
+                om.merge_i32_direct(d_arrs[0], d_arrs[1], per_thread=per, two_searches=two,
+                                    out=out, stream=stream)
+            out.fill_(-1)
+            go()
+            torch.cuda.synchronize()
+            if not np.array_equal(out.cpu().numpy(), want):
+                log("FAILED: direct kernel per=%d two_searches=%s differs from the oracle" % (per, two))
+                sys.exit(1)
+            for _ in range(2):
+                go()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(5):
+                go()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / 5
+            gbs = w.roofline_bytes / (ms * 1e-3) / 1e9
+            log("%-28s %10.3f %10.1f %8.1f" % ("%s, %d per lane" % ("two searches" if two else "search+walk", per),
+                                                ms, gbs, 100 * gbs / HBM_PEAK_GBS))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,6 +138,9 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name (default: the int32 2^28+2^28 merge)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the oracle (the output check still runs)")
+    ap.add_argument("--ablation", action="store_true",
+                    help="also time the global-memory (no LDS) merge kernels at 1..256 outputs "
+                         "per lane, each checked against the oracle; table on stderr")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -165,6 +202,8 @@ def main():
         rates = []
     else:
         want, rates = time_oracle(w, arrs)
+    if args.ablation and not w.kv:
+        ablation(om, d_arrs, want, w, stream)
     if w.kv:
         ok = np.array_equal(out_k.cpu().numpy(), want[0]) and \
             np.array_equal(out_v.cpu().numpy().view(np.uint32), want[1])
@@ -182,8 +221,8 @@ def main():
         launch_merge()
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    # Timed region 1 (the step rate): exactly K steps back to back, bracketed
+    # by device synchronisation, one event pair and the host clock.
     start_all = torch.cuda.Event(enable_timing=True)
     stop_all = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -191,14 +230,25 @@ def main():
     start_all.record(stream)
     for k in range(args.steps):
         launch_partition()
-        ev[k][0].record(stream)
         launch_merge()
-        ev[k][1].record(stream)
     stop_all.record(stream)
     torch.cuda.synchronize()
     t_host = time.perf_counter() - t_host
     ms_total = start_all.elapsed_time(stop_all)
     ms_step = ms_total / args.steps
+
+    # Timed region 2 (the roofline figure): the same K steps with a HIP event
+    # pair around every segment-merge launch on its stream.  (The extra event
+    # packets cost ~1.5% of a step, so region 1 alone gives the step rate.)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        launch_partition()
+        ev[k][0].record(stream)
+        launch_merge()
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
     merge_ms = [a.elapsed_time(b) for a, b in ev]
     merge_ms_mean = float(np.mean(merge_ms))
 

@@ -129,6 +129,24 @@ int omerge_merge_segments_kv(const int32_t *A_keys, const uint32_t *A_vals,
                              struct ihipStream_t *stream);
 
 /*
+ * omerge_merge_i32_direct -- the same stable merge computed the way the
+ * pages' global-memory kernels do it, kept as a measured ablation of the
+ * LDS-tiled path: one lane per slice of `per_thread` outputs, reading A and B
+ * and writing C in HBM directly, with no LDS.
+ *   two_searches != 0: each lane finds the co-ranks of both ends of its slice
+ *     and merges its two sub-arrays (page "Co-rank Function ... and Basic
+ *     Parallel Merge Kernel", section "Basic Parallel Merge Kernel");
+ *   two_searches == 0: each lane finds the co-rank of its slice start only and
+ *     walks per_thread steps of the two-pointer merge (page "merge_path.cu",
+ *     its co-rank kernel).
+ * Arguments as merge_i32; per_thread in [1, 2^30].  The output is identical
+ * to merge_i32's.
+ */
+int omerge_merge_i32_direct(const int32_t *A, int64_t m, const int32_t *B,
+                            int64_t n, int32_t *C, int64_t per_thread,
+                            int two_searches, struct ihipStream_t *stream);
+
+/*
  * omerge_stream_copy -- measurement reference, not part of the merge: copies
  * n 32-bit words from src to dst (device, non-overlapping) with 16-byte
  * loads and stores, i.e. the same bytes a merge of n outputs must move.  A

@@ -9,6 +9,7 @@ from .merge import (  # noqa: F401
     library_path,
     load_library,
     merge_i32,
+    merge_i32_direct,
     merge_kv,
     merge_segments_i32,
     merge_segments_kv,

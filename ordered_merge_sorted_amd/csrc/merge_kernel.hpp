@@ -225,6 +225,42 @@ __global__ void co_rank_kernel(const int32_t* __restrict__ A, int64_t m,
     out[s] = co_rank_global(k, A, m, B, n);
 }
 
+// Global-memory merge, no LDS: one lane per slice of `per` outputs
+// [k0, k1).  With two_searches the lane finds the co-ranks of both ends and
+// merges exactly its two sub-arrays (the basic kernel of page "Co-rank
+// Function ... and Basic Parallel Merge Kernel"); otherwise it finds the
+// co-rank of k0 only and walks k1-k0 steps of the two-pointer merge with the
+// whole arrays' bounds (the co-rank kernel of page "merge_path.cu").  Every
+// read and write goes to HBM directly, lane-strided: this is the pattern the
+// pages' coalescing critique describes, kept as a measured ablation.
+__global__ __launch_bounds__(256) void direct_merge_kernel(const int32_t* __restrict__ A, int64_t m,
+                                                           const int32_t* __restrict__ B, int64_t n,
+                                                           int32_t* __restrict__ C, int64_t per,
+                                                           int two_searches) {
+    const int64_t t = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+    const int64_t total = m + n;
+    const int64_t k0 = t * per;
+    if (k0 >= total) return;
+    const int64_t k1 = k0 + per < total ? k0 + per : total;
+    int64_t a = co_rank_global(k0, A, m, B, n);
+    int64_t b = k0 - a;
+    int64_t a_end = m, b_end = n;
+    if (two_searches) {
+        a_end = co_rank_global(k1, A, m, B, n);
+        b_end = k1 - a_end;
+    }
+    for (int64_t k = k0; k < k1; ++k) {
+        const bool take_a = a < a_end && (b >= b_end || A[a] <= B[b]);
+        if (take_a) {
+            C[k] = A[a];
+            ++a;
+        } else {
+            C[k] = B[b];
+            ++b;
+        }
+    }
+}
+
 // Bandwidth reference: each lane copies UNROLL 16-byte vectors, all loads
 // issued before the stores; single words at the two ends.
 template <int UNROLL>

@@ -339,6 +339,22 @@ int omerge_merge_segments_kv(const int32_t* A_keys, const uint32_t* A_vals,
                               C_vals, stream);
 }
 
+int omerge_merge_i32_direct(const int32_t* A, int64_t m, const int32_t* B, int64_t n,
+                            int32_t* C, int64_t per_thread, int two_searches,
+                            hipStream_t stream) {
+    int rc = check_i32_args(A, m, B, n, C);
+    if (rc != OMERGE_OK) return rc;
+    if (per_thread < 1 || per_thread > (int64_t(1) << 30)) return OMERGE_INVALID_ARG;
+    const int64_t total = m + n;
+    if (total == 0) return OMERGE_OK;
+    const int64_t blocks = ceil_div(ceil_div(total, per_thread), 256);
+    if (blocks > kMaxGridBlocks) return OMERGE_OVERFLOW;
+    hipLaunchKernelGGL(direct_merge_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                       stream, A, m, B, n, C, per_thread, two_searches);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? OMERGE_OK : hip_fail(e);
+}
+
 int omerge_stream_copy(const int32_t* src, int64_t n, int32_t* dst, hipStream_t stream) {
     if (bad_array(src, n) || bad_array(dst, n) || overlaps(src, n, dst, n)) return OMERGE_INVALID_ARG;
     if (n == 0) return OMERGE_OK;

@@ -55,6 +55,7 @@ def load_library() -> ctypes.CDLL:
         "omerge_merge_segments_i32": (i32, [p, i64, p, i64, p, i64, p, p]),
         "omerge_merge_segments_kv": (i32, [p, p, i64, p, p, i64, p, i64, p, p, p]),
         "omerge_stream_copy": (i32, [p, i64, p, p]),
+        "omerge_merge_i32_direct": (i32, [p, i64, p, i64, p, i64, i32, p]),
         "omerge_status_string": (ctypes.c_char_p, [i32]),
         "omerge_last_hip_error": (i32, []),
         "omerge_version": (i32, []),
@@ -256,4 +257,22 @@ def stream_copy(src: torch.Tensor, out: Optional[torch.Tensor] = None,
     with torch.cuda.device(src.device):
         rc = lib.omerge_stream_copy(_ptr(src), src.numel(), _ptr(out), _stream(src.device, stream))
     _raise_on(rc, "omerge_stream_copy")
+    return out
+
+
+def merge_i32_direct(a: torch.Tensor, b: torch.Tensor, per_thread: int = 16,
+                     two_searches: bool = False, out: Optional[torch.Tensor] = None,
+                     stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """The global-memory merge kernels (no LDS), for ablation against
+    merge_i32: one lane per slice of per_thread outputs; two co-rank searches
+    per slice (basic kernel) or one search then a walk (co-rank kernel)."""
+    _vec(a, "a", (torch.int32,))
+    _vec(b, "b", (torch.int32,), a.device)
+    out = _out(out, a.numel() + b.numel(), torch.int32, a.device, "out")
+    lib = load_library()
+    with torch.cuda.device(a.device):
+        rc = lib.omerge_merge_i32_direct(_ptr(a), a.numel(), _ptr(b), b.numel(), _ptr(out),
+                                         int(per_thread), int(bool(two_searches)),
+                                         _stream(a.device, stream))
+    _raise_on(rc, "omerge_merge_i32_direct")
     return out

@@ -102,6 +102,12 @@ void emu_co_rank(const int32_t* A, int64_t m, const int32_t* B, int64_t n, const
     run_grid(blocks, 256, [&] { omerge::co_rank_kernel(A, m, B, n, ks, count, out); });
 }
 
+void emu_direct(const int32_t* A, int64_t m, const int32_t* B, int64_t n, int32_t* C,
+                int64_t per, int two) {
+    const int64_t blocks = ((m + n + per - 1) / per + 255) / 256;
+    run_grid(blocks, 256, [&] { omerge::direct_merge_kernel(A, m, B, n, C, per, two); });
+}
+
 void emu_merge_i32(int variant, const int32_t* A, int64_t m, const int32_t* B, int64_t n,
                    const int64_t* part, int64_t seg_len, int32_t* C) {
     if (variant == 0)

@@ -29,6 +29,7 @@ def load(path):
     lib.emu_co_rank.argtypes = [p, i64, p, i64, p, i64, p]
     lib.emu_merge_i32.argtypes = [i32, p, i64, p, i64, p, i64, p]
     lib.emu_merge_kv.argtypes = [i32, p, p, i64, p, p, i64, p, i64, p, p]
+    lib.emu_direct.argtypes = [p, i64, p, i64, p, i64, i32]
     return lib
 
 
@@ -225,7 +226,21 @@ def group_unsorted(r, g):
         r.cases += 1
 
 
-GROUPS = {"small": group_small, "skew": group_skew, "blocks": group_blocks,
+def group_direct(r, g):
+    """The global-memory kernels (basic: two searches; walk: one search)."""
+    for c in range(16):
+        m, n = (int(x) for x in g.integers(0, 3000, size=2))
+        A, B = sorted_pair(g, m, n, int(g.choice([2, 50, 1 << 32])))
+        want = oracle.merge_i32(A, B)
+        for per in (1, 4, 16, 64, 256):
+            for two in (0, 1):
+                C = np.full(m + n, 777, dtype=np.int32)
+                if m + n:
+                    r.lib.emu_direct(ptr(A), m, ptr(B), n, ptr(C), per, two)
+                r.check(np.array_equal(C, want), ("direct", m, n, per, two))
+
+
+GROUPS = {"small": group_small, "direct": group_direct, "skew": group_skew, "blocks": group_blocks,
           "production": group_production, "unsorted": group_unsorted}
 
 if __name__ == "__main__":

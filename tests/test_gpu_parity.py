@@ -170,6 +170,19 @@ def test_one_sided_tiles(layout):
     assert_same(host(gv).view(np.uint32), wv, "kv payloads")
 
 
+@pytest.mark.parametrize("two_searches", [False, True])
+def test_direct_global_memory_kernels(two_searches):
+    """The no-LDS ablation kernels give the same output at every slice size."""
+    g = np.random.Generator(np.random.PCG64(321))
+    for m, n, span in ((40000, 30001, 64), (0, 5000, 8), (7777, 1, 1 << 32)):
+        A, B = pair(g, m, n, span)
+        want = oracle.merge_i32(A, B)
+        for per in (1, 4, 16, 64, 256):
+            say("direct", two_searches, m, n, per)
+            got = om.merge_i32_direct(dev(A), dev(B), per_thread=per, two_searches=two_searches)
+            assert_same(host(got), want, "direct per=%d" % per)
+
+
 EDGE = [
     (0, 0), (1, 0), (0, 1), (1, 1), (3, 0), (0, 4095), (4095, 1), (4096, 0), (4097, 0),
     (2048, 2048), (2049, 2048), (1, 100000), (100000, 1), (12289, 4093),
