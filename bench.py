@@ -130,6 +130,57 @@ def ablation(om, d_arrs, want, w, stream):
                                                 ms, gbs, 100 * gbs / HBM_PEAK_GBS))
 
 
+def typed_orders(om, d_arrs, c_ref, w, stream):
+    """The key orders of omerge_merge_keys on inputs derived from the int32
+    workload on the device: uint32 keys x ^ 2^31 and float32 keys with bits
+    (x ^ 2^31) >> 1 (non-negative patterns, so bit order is totalOrder; some
+    are infinities and NaNs), each ascending and reversed for descending.
+    Each output is checked against the same map of the int32 merge output
+    (keys only: the sorted multiset is unique) before it is timed."""
+    import torch
+    log("key orders (omerge_merge_keys, %s)" % w.name)
+    log("%-28s %10s %10s %8s" % ("order", "ms", "GB/s", "% peak"))
+    sign = torch.tensor(-(1 << 31), dtype=torch.int32, device=c_ref.device)
+    maps = {
+        "int32": (lambda x: x, torch.int32),
+        "uint32": (lambda x: x ^ sign, getattr(torch, "uint32", torch.int32)),
+        "float32": (lambda x: torch.bitwise_right_shift((x ^ sign).view(torch.int32), 1) &
+                    0x7FFFFFFF, torch.float32),
+    }
+    for name, (f, tdt) in maps.items():
+        if name == "uint32" and tdt is torch.int32:
+            continue
+        for desc in (False, True):
+            a, b = (f(x) for x in d_arrs[:2])
+            want = f(c_ref)
+            if desc:
+                a, b, want = a.flip(0), b.flip(0), want.flip(0)
+            a, b = a.contiguous().view(tdt), b.contiguous().view(tdt)
+            out = torch.empty(w.total, dtype=tdt, device=c_ref.device)
+
+            def go():
+                om.merge(a, b, descending=desc, out=out, stream=stream)
+            go()
+            torch.cuda.synchronize()
+            if not torch.equal(out.view(torch.int32), want.contiguous()):
+                log("FAILED: key order %s%s differs from the mapped int32 merge" %
+                    (name, " desc" if desc else ""))
+                sys.exit(1)
+            for _ in range(5):
+                go()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(20):
+                go()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 20
+            gbs = w.roofline_bytes / (ms * 1e-3) / 1e9
+            log("%-28s %10.3f %10.1f %8.1f" % (name + (" descending" if desc else " ascending"),
+                                                ms, gbs, 100 * gbs / HBM_PEAK_GBS))
+            del a, b, out, want
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,7 +191,8 @@ def main():
                     help="skip timing the oracle (the output check still runs)")
     ap.add_argument("--ablation", action="store_true",
                     help="also time the global-memory (no LDS) merge kernels at 1..256 outputs "
-                         "per lane, each checked against the oracle; table on stderr")
+                         "per lane, each checked against the oracle, and every key order of "
+                         "omerge_merge_keys; tables on stderr")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -214,6 +266,8 @@ def main():
         sys.exit(1)
     log("checked: output bit-exact against the oracle (%d elements)" % total)
     del want
+    if args.ablation and not w.kv:
+        typed_orders(om, d_arrs, out, w, stream)
 
     # Warmup, then exactly K timed steps.
     for _ in range(args.warmup):

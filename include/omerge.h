@@ -79,6 +79,51 @@ int merge_kv(const int32_t *A_keys, const uint32_t *A_vals, int64_t m,
              int32_t *C_keys, uint32_t *C_vals, struct ihipStream_t *stream);
 
 /*
+ * Key types and orders of omerge_merge_keys / omerge_merge_pairs.
+ *
+ * The pages compare int keys (page "Co-rank Function ...") and float keys
+ * (page "merge_path.cu", its kernels and CPU reference).  Every 32-bit key
+ * type below merges with the same kernels: each key is mapped to a signed
+ * int32 by an order-preserving bijection of its bits on the way into the
+ * kernel and mapped back on the way out, so the output keys are the input
+ * keys' exact bit patterns.
+ *   OMERGE_KEY_I32  signed 32-bit integers (merge_i32's order).
+ *   OMERGE_KEY_U32  unsigned 32-bit integers.
+ *   OMERGE_KEY_F32  IEEE 754 binary32 in the standard's totalOrder:
+ *                   -NaN < -inf < negative finite < -0.0 < +0.0 < positive
+ *                   finite < +inf < +NaN; NaNs of one sign order by payload
+ *                   bits (larger payload = farther from zero).  -0.0 and +0.0
+ *                   are therefore NOT equal keys here.
+ * OR-ing OMERGE_DESCENDING reverses the order: A and B must then be sorted
+ * descending, and C is descending.  In every order, equal keys keep A's
+ * elements first, then each array's own order.
+ */
+enum omerge_key_kind {
+    OMERGE_KEY_I32 = 0,
+    OMERGE_KEY_U32 = 1,
+    OMERGE_KEY_F32 = 2
+};
+#define OMERGE_DESCENDING 4
+
+/*
+ * omerge_merge_keys -- stable merge of 32-bit keys of the type and order
+ * `order` (an omerge_key_kind, optionally | OMERGE_DESCENDING).
+ *   A[m], B[n]  in:  4-byte keys sorted in that order (device).
+ *   C[m+n]      out: merged keys (device).
+ * Same conventions, costs and scratch as merge_i32, which it equals for
+ * order == OMERGE_KEY_I32.  An unknown order code is OMERGE_INVALID_ARG.
+ *
+ * omerge_merge_pairs -- the same for (key, uint32 payload) pairs, as
+ * merge_kv; payloads are never compared or changed.
+ */
+int omerge_merge_keys(const void *A, int64_t m, const void *B, int64_t n,
+                      void *C, int order, struct ihipStream_t *stream);
+int omerge_merge_pairs(const void *A_keys, const uint32_t *A_vals, int64_t m,
+                       const void *B_keys, const uint32_t *B_vals, int64_t n,
+                       void *C_keys, uint32_t *C_vals, int order,
+                       struct ihipStream_t *stream);
+
+/*
  * omerge_co_rank -- device co-rank at arbitrary output ranks (page
  * "Co-rank Function ...", section "Binary-Search Implementation": bounds
  * i = min(k,m), i_low = max(0,k-n), j_low = max(0,k-m), half-step rounded up,

@@ -54,6 +54,21 @@ def _u32(x) -> np.ndarray:
     return x
 
 
+KIND_I32, KIND_U32, KIND_F32, ORDER_DESCENDING = 0, 1, 2, 4
+_KIND = {np.dtype(np.int32): KIND_I32, np.dtype(np.uint32): KIND_U32,
+         np.dtype(np.float32): KIND_F32}
+_KIND_DTYPE = {v: k for k, v in _KIND.items()}
+
+
+def _typed_pair(A, B):
+    """Key kind of A and B (same dtype), and both as uint32 bit views."""
+    A, B = np.ascontiguousarray(A), np.ascontiguousarray(B)
+    if A.dtype != B.dtype or A.dtype not in _KIND:
+        raise TypeError("keys must both be int32, uint32 or float32, got %s and %s"
+                        % (A.dtype, B.dtype))
+    return _KIND[A.dtype], A.view(np.uint32), B.view(np.uint32)
+
+
 def _ptr(x: np.ndarray):
     return ctypes.c_void_p(x.ctypes.data)
 
@@ -70,6 +85,12 @@ class Oracle:
         lib.oracle_merge_kv.restype = None
         lib.oracle_co_rank_all.argtypes = [p, i64, p, i64, p]
         lib.oracle_co_rank_all.restype = None
+        lib.oracle_merge_keys.argtypes = [ctypes.c_int, p, i64, p, i64, p]
+        lib.oracle_merge_keys.restype = None
+        lib.oracle_merge_pairs.argtypes = [ctypes.c_int, p, p, i64, p, p, i64, p, p]
+        lib.oracle_merge_pairs.restype = None
+        lib.oracle_key_le.argtypes = [ctypes.c_int, ctypes.c_uint32, ctypes.c_uint32]
+        lib.oracle_key_le.restype = ctypes.c_int
         self._lib = lib
         self.path = lib_path
 
@@ -91,6 +112,37 @@ class Oracle:
         self._lib.oracle_merge_kv(_ptr(Ak), _ptr(Av), Ak.size, _ptr(Bk),
                                   _ptr(Bv), Bk.size, _ptr(Ck), _ptr(Cv))
         return Ck, Cv
+
+    def merge_keys(self, A, B, descending: bool = False) -> np.ndarray:
+        """Stable merge of sorted int32, uint32 or float32 keys in that type's
+        order (float32: IEEE 754 totalOrder), descending if asked; A first on
+        ties.  Returns an array of the keys' dtype holding the input bits."""
+        kind, A, B = _typed_pair(A, B)
+        order = kind | (ORDER_DESCENDING if descending else 0)
+        C = np.empty(A.size + B.size, dtype=np.uint32)
+        self._lib.oracle_merge_keys(order, _ptr(A), A.size, _ptr(B), B.size, _ptr(C))
+        return C.view(_KIND_DTYPE[kind])
+
+    def merge_pairs(self, A_keys, A_vals, B_keys, B_vals, descending: bool = False):
+        """merge_keys for (key, uint32 payload) pairs; payloads move with keys."""
+        kind, Ak, Bk = _typed_pair(A_keys, B_keys)
+        Av, Bv = _u32(A_vals), _u32(B_vals)
+        if Ak.size != Av.size or Bk.size != Bv.size:
+            raise ValueError("key and payload lengths differ")
+        order = kind | (ORDER_DESCENDING if descending else 0)
+        Ck = np.empty(Ak.size + Bk.size, dtype=np.uint32)
+        Cv = np.empty(Ak.size + Bk.size, dtype=np.uint32)
+        self._lib.oracle_merge_pairs(order, _ptr(Ak), _ptr(Av), Ak.size, _ptr(Bk),
+                                     _ptr(Bv), Bk.size, _ptr(Ck), _ptr(Cv))
+        return Ck.view(_KIND_DTYPE[kind]), Cv
+
+    def key_le(self, dtype, x, y, descending: bool = False) -> bool:
+        """The order relation itself: does key x come before key y, or tie?"""
+        kind = _KIND[np.dtype(dtype)]
+        xb = int(np.array([x], dtype=dtype).view(np.uint32)[0])
+        yb = int(np.array([y], dtype=dtype).view(np.uint32)[0])
+        order = kind | (ORDER_DESCENDING if descending else 0)
+        return bool(self._lib.oracle_key_le(order, xb, yb))
 
     def co_rank_all(self, A, B) -> np.ndarray:
         """int64 array I of length m+n+1: I[k] = number of A elements among the
@@ -127,6 +179,18 @@ def merge_i32(A, B):
 
 def merge_kv(A_keys, A_vals, B_keys, B_vals):
     return default().merge_kv(A_keys, A_vals, B_keys, B_vals)
+
+
+def merge_keys(A, B, descending=False):
+    return default().merge_keys(A, B, descending)
+
+
+def merge_pairs(A_keys, A_vals, B_keys, B_vals, descending=False):
+    return default().merge_pairs(A_keys, A_vals, B_keys, B_vals, descending)
+
+
+def key_le(dtype, x, y, descending=False):
+    return default().key_le(dtype, x, y, descending)
 
 
 def co_rank_all(A, B):

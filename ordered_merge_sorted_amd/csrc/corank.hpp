@@ -35,6 +35,38 @@
 
 namespace omerge {
 
+// Key orders.  Every supported 32-bit key type and direction is merged as
+// signed int32 after an order-preserving bijection of the key's bits, applied
+// when a key is read from HBM and undone when it is written back, so the
+// output keeps the input's exact bits:
+//   int32 ascending      identity
+//   uint32 ascending     flip the sign bit
+//   float32 ascending    IEEE 754 totalOrder (-NaN < -inf < ... < -0 < +0 <
+//                        ... < +inf < +NaN): flip the low 31 bits of negative
+//                        values, so larger magnitudes sort lower
+//   descending           bitwise NOT of the ascending image (~y = -y-1
+//                        reverses signed order)
+// Ties (equal images) still take A first.  Each map is its own inverse up to
+// the final NOT, which from_ord undoes first.
+enum KeyKind : int { kKeyI32 = 0, kKeyU32 = 1, kKeyF32 = 2 };
+
+template <int ORDER>  // ORDER = KeyKind | (descending << 2)
+struct KeyOrder {
+    static constexpr int kKind = ORDER & 3;
+    static constexpr bool kDescending = (ORDER >> 2) != 0;
+    __host__ __device__ static __forceinline__ int asc(int x) {
+        if (kKind == kKeyU32) return x ^ INT32_MIN;
+        if (kKind == kKeyF32) return x ^ ((x >> 31) & INT32_MAX);
+        return x;
+    }
+    __host__ __device__ static __forceinline__ int to_ord(int x) {
+        return kDescending ? ~asc(x) : asc(x);
+    }
+    __host__ __device__ static __forceinline__ int from_ord(int y) {
+        return asc(kDescending ? ~y : y);
+    }
+};
+
 // Adjustment cap for 64-bit searches over global memory and for 32-bit
 // searches inside one LDS tile (windows of at most 2^16 elements).
 constexpr int kMaxStepsGlobal = 2 * 64 + 2;
@@ -72,15 +104,18 @@ __device__ __forceinline__ Idx co_rank(Idx k, Idx m, Idx n, LoadA load_a,
     return i;
 }
 
-// Co-rank over two arrays in global memory, 64-bit indices.
+// Co-rank over two arrays in global memory, 64-bit indices, keys compared
+// in the order ORDER (KeyOrder).
+template <int ORDER = 0>
 __device__ __forceinline__ int64_t co_rank_global(int64_t k,
                                                   const int32_t* __restrict__ A,
                                                   int64_t m,
                                                   const int32_t* __restrict__ B,
                                                   int64_t n) {
+    using K = KeyOrder<ORDER>;
     return co_rank<int64_t>(
-        k, m, n, [=](int64_t x) { return A[x]; },
-        [=](int64_t x) { return B[x]; }, kMaxStepsGlobal);
+        k, m, n, [=](int64_t x) { return K::to_ord(A[x]); },
+        [=](int64_t x) { return K::to_ord(B[x]); }, kMaxStepsGlobal);
 }
 
 }  // namespace omerge

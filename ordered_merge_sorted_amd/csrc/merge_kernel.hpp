@@ -151,7 +151,7 @@ __device__ __forceinline__ int stage_word(int p) { return p + ((p >> 5) << 2); }
 // round keeps max(0,k-n) <= lo <= hi <= min(k,m) and shrinks the interval,
 // whatever the data, so the loop ends even on unsorted input.  All lanes of
 // the wavefront must call this together (the vote is wavefront-wide).
-template <int G>
+template <int G, int ORDER>
 __device__ __forceinline__ int64_t co_rank_group(int64_t k, const int32_t* __restrict__ A,
                                                  int64_t m, const int32_t* __restrict__ B,
                                                  int64_t n, int g_lane, int g_shift) {
@@ -170,7 +170,8 @@ __device__ __forceinline__ int64_t co_rank_group(int64_t k, const int32_t* __res
         };
         const int64_t p = point(g_lane);
         bool pass = false;
-        if (g_lane < live) pass = A[p] <= B[k - 1 - p];
+        if (g_lane < live)
+            pass = KeyOrder<ORDER>::to_ord(A[p]) <= KeyOrder<ORDER>::to_ord(B[k - 1 - p]);
         const unsigned long long votes = __ballot(pass);
         const unsigned long long mine =
             G == 64 ? votes : (votes >> g_shift) & ((1ull << (G == 64 ? 0 : G)) - 1);
@@ -188,7 +189,7 @@ __device__ __forceinline__ int64_t co_rank_group(int64_t k, const int32_t* __res
 // part[s] = co-rank of k_s = min(s*seg_len, m+n).  G = 1: one lane per
 // boundary running the pages' two-test search; G > 1: G lanes per boundary
 // testing G points per round.
-template <int G>
+template <int G, int ORDER>
 __global__ __launch_bounds__(256) void partition_kernel(const int32_t* __restrict__ A, int64_t m,
                                                         const int32_t* __restrict__ B, int64_t n,
                                                         int64_t seg_len, int64_t count,
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(256) void partition_kernel(const int32_t* __restric
     if constexpr (G == 1) {
         if (gid >= count) return;
         const int64_t k = gid < count - 1 ? gid * seg_len : m + n;
-        part[gid] = co_rank_global(k, A, m, B, n);
+        part[gid] = co_rank_global<ORDER>(k, A, m, B, n);
     } else {
         const int64_t s = gid / G;
         // A wavefront whose groups are all past the end leaves together;
@@ -207,7 +208,7 @@ __global__ __launch_bounds__(256) void partition_kernel(const int32_t* __restric
         const int64_t k = sc < count - 1 ? sc * seg_len : m + n;
         const int g_lane = static_cast<int>(gid % G);
         const int g_shift = static_cast<int>(threadIdx.x & 63) - g_lane;
-        const int64_t i = co_rank_group<G>(s < count ? k : 0, A, s < count ? m : 0, B,
+        const int64_t i = co_rank_group<G, ORDER>(s < count ? k : 0, A, s < count ? m : 0, B,
                                            s < count ? n : 0, g_lane, g_shift);
         if (g_lane == 0 && s < count) part[s] = i;
     }
@@ -215,6 +216,7 @@ __global__ __launch_bounds__(256) void partition_kernel(const int32_t* __restric
 
 // Co-rank at arbitrary ranks, one lane per query, with the pages' two-test
 // search (corank.hpp).
+template <int ORDER>
 __global__ void co_rank_kernel(const int32_t* __restrict__ A, int64_t m,
                                const int32_t* __restrict__ B, int64_t n,
                                const int64_t* __restrict__ ks, int64_t count,
@@ -222,7 +224,7 @@ __global__ void co_rank_kernel(const int32_t* __restrict__ A, int64_t m,
     const int64_t s = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
     if (s >= count) return;
     const int64_t k = clamp_to<int64_t>(ks[s], 0, m + n);
-    out[s] = co_rank_global(k, A, m, B, n);
+    out[s] = co_rank_global<ORDER>(k, A, m, B, n);
 }
 
 // Global-memory merge, no LDS: one lane per slice of `per` outputs
@@ -371,22 +373,32 @@ struct Refill {
         if (slot < kGuard) *reinterpret_cast<int4v*>(side + CAP + slot) = x;
     }
 
-    // ring points at the A ring; the B ring starts SIDE words later.
+    // ring points at the A ring; the B ring starts SIDE words later.  Keys
+    // enter the ring as their order images (KeyOrder<ORDER>::to_ord); payload
+    // rings use the identity order 0.
+    template <int ORDER>
     __device__ __forceinline__ void commit(int* ring, int tid) const {
+        using K = KeyOrder<ORDER>;
 #pragma unroll
         for (int v = 0; v < kVec; ++v) {
             const int q = tid + v * NL;
+            int4v x = body[v];
+            x.x = K::to_ord(x.x);
+            x.y = K::to_ord(x.y);
+            x.z = K::to_ord(x.z);
+            x.w = K::to_ord(x.w);
             if (q < sa.nvec) {
-                put4(ring, (sa.base + sa.r0 + sa.head + 4 * q) & kMask, body[v]);
+                put4(ring, (sa.base + sa.r0 + sa.head + 4 * q) & kMask, x);
             } else if (q - sa.nvec < sb.nvec) {
                 const int qb = q - sa.nvec;
-                put4(ring + SIDE, (sb.base + sb.r0 + sb.head + 4 * qb) & kMask, body[v]);
+                put4(ring + SIDE, (sb.base + sb.r0 + sb.head + 4 * qb) & kMask, x);
             }
         }
         if (loose_slot >= 0) {
             int* side = ring + (loose_side ? SIDE : 0);
-            side[loose_slot] = loose;
-            if (loose_slot < kGuard) side[CAP + loose_slot] = loose;
+            const int y = K::to_ord(loose);
+            side[loose_slot] = y;
+            if (loose_slot < kGuard) side[CAP + loose_slot] = y;
         }
     }
 };
@@ -435,9 +447,10 @@ __device__ __forceinline__ void bitonic_clean(int (&x)[N]) {
 // Stores tile outputs [0, len) from the padded LDS stage to dst[0, len) with
 // NS storing lanes (`tid` = 0..NS-1), V 16-byte vectors per lane at most:
 // 16-byte stores on the aligned body, single words at the ends.
-template <int NS, int V>
+template <int NS, int V, int ORDER>
 __device__ __forceinline__ void store_tile(int32_t* __restrict__ dst, int len,
                                            const int* stage, int tid) {
+    using K = KeyOrder<ORDER>;
     const int head0 = (4 - (word_phase(dst) & 3)) & 3;
     const int head = head0 < len ? head0 : len;
     const int nvec = (len - head) >> 2;
@@ -448,7 +461,12 @@ __device__ __forceinline__ void store_tile(int32_t* __restrict__ dst, int len,
             const int q = tid + v * NS;
             if (q < nvec) {
                 const int p = 4 * q;
-                store_stream4(dst + p, *reinterpret_cast<const int4v*>(stage + stage_word(p)));
+                int4v x = *reinterpret_cast<const int4v*>(stage + stage_word(p));
+                x.x = K::from_ord(x.x);
+                x.y = K::from_ord(x.y);
+                x.z = K::from_ord(x.z);
+                x.w = K::from_ord(x.w);
+                store_stream4(dst + p, x);
             }
         }
     } else {
@@ -458,18 +476,18 @@ __device__ __forceinline__ void store_tile(int32_t* __restrict__ dst, int len,
             if (q < nvec) {
                 const int p = head + 4 * q;
                 int4v x;
-                x.x = stage[stage_word(p)];
-                x.y = stage[stage_word(p + 1)];
-                x.z = stage[stage_word(p + 2)];
-                x.w = stage[stage_word(p + 3)];
+                x.x = K::from_ord(stage[stage_word(p)]);
+                x.y = K::from_ord(stage[stage_word(p + 1)]);
+                x.z = K::from_ord(stage[stage_word(p + 2)]);
+                x.w = K::from_ord(stage[stage_word(p + 3)]);
                 store_stream4(dst + p, x);
             }
         }
-        if (tid < head) dst[tid] = stage[stage_word(tid)];
+        if (tid < head) dst[tid] = K::from_ord(stage[stage_word(tid)]);
     }
     if (tid >= 4 && tid - 4 < tail) {
         const int p = head + 4 * nvec + (tid - 4);
-        dst[p] = stage[stage_word(p)];
+        dst[p] = K::from_ord(stage[stage_word(p)]);
     }
 }
 
@@ -477,9 +495,10 @@ __device__ __forceinline__ void store_tile(int32_t* __restrict__ dst, int len,
 // window's element p, at ring slot (start + p) & MASK.  Consecutive lanes read
 // consecutive slots (no bank conflicts); 16-byte reads when the ring quads
 // line up with the output's 16-byte vectors, single words otherwise.
-template <int THREADS, int V, int MASK>
+template <int THREADS, int V, int MASK, int ORDER>
 __device__ __forceinline__ void store_from_ring(int32_t* __restrict__ dst, int len,
                                                 const int* side, int start, int tid) {
+    using K = KeyOrder<ORDER>;
     const int head0 = (4 - (word_phase(dst) & 3)) & 3;
     const int head = head0 < len ? head0 : len;
     const int nvec = (len - head) >> 2;
@@ -499,20 +518,24 @@ __device__ __forceinline__ void store_from_ring(int32_t* __restrict__ dst, int l
                 x.z = side[(start + p + 2) & MASK];
                 x.w = side[(start + p + 3) & MASK];
             }
+            x.x = K::from_ord(x.x);
+            x.y = K::from_ord(x.y);
+            x.z = K::from_ord(x.z);
+            x.w = K::from_ord(x.w);
             store_stream4(dst + p, x);
         }
     }
-    if (tid < head) dst[tid] = side[(start + tid) & MASK];
+    if (tid < head) dst[tid] = K::from_ord(side[(start + tid) & MASK]);
     if (tid >= 4 && tid - 4 < tail) {
         const int p = head + 4 * nvec + (tid - 4);
-        dst[p] = side[(start + p) & MASK];
+        dst[p] = K::from_ord(side[(start + p) & MASK]);
     }
 }
 
 // ---------------------------------------------------------------------------
 // Segment merge kernel: one workgroup per segment of the output.
 
-template <int THREADS, int ITEMS, bool KV>
+template <int THREADS, int ITEMS, bool KV, int ORDER = 0>
 __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
     const int32_t* __restrict__ A, const uint32_t* __restrict__ Av, int64_t m,
     const int32_t* __restrict__ B, const uint32_t* __restrict__ Bv, int64_t n,
@@ -579,8 +602,8 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
         rb.set(Bs, b_base, 0, b_loaded);
         fa.issue(ra, none, tid);
         fb.issue(none, rb, tid);
-        fa.commit(ring, tid);
-        fb.commit(ring, tid);
+        fa.template commit<ORDER>(ring, tid);
+        fb.template commit<ORDER>(ring, tid);
         if (KV) {
             SideRange va, vb, vnone;
             vnone.set(Avs, va_base, 0, 0);
@@ -588,8 +611,8 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
             vb.set(Bvs, vb_base, 0, b_loaded);
             fa.issue(va, vnone, tid);
             fb.issue(vnone, vb, tid);
-            fa.commit(vring, tid);
-            fb.commit(vring, tid);
+            fa.template commit<0>(vring, tid);
+            fb.template commit<0>(vring, tid);
         }
     }
     __syncthreads();
@@ -662,16 +685,16 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
         if (side != 0) {
             const int* const win = side == 1 ? ring_a : ring_b;
             const int start = side == 1 ? sa : sb;
-            store_from_ring<THREADS, kStoreVec, kMask>(Cs + c_done, c_tile, win, start, tid);
+            store_from_ring<THREADS, kStoreVec, kMask, ORDER>(Cs + c_done, c_tile, win, start, tid);
             if (KV) {
                 const int* const vwin = side == 1 ? vring : vring + kSide;
                 const int vstart = side == 1 ? (sa + d_a) & kMask : (sb + d_b) & kMask;
-                store_from_ring<THREADS, kStoreVec, kMask>(
+                store_from_ring<THREADS, kStoreVec, kMask, 0>(
                     reinterpret_cast<int32_t*>(Cv + k0) + c_done, c_tile, vwin, vstart, tid);
             }
             __syncthreads();  // every read of the consumed slots is done
-            rf.commit(ring, tid);
-            if (KV) rv.commit(vring, tid);
+            rf.template commit<ORDER>(ring, tid);
+            if (KV) rv.template commit<0>(vring, tid);
         } else {
             const int c_beg = tid * ITEMS < c_tile ? tid * ITEMS : c_tile;
             const int s = tid > 0 ? split[tid - 1] : 0;
@@ -752,16 +775,16 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
             // the vector-memory counter (which counts loads and stores alike)
             // then covers the refill loads and only stores issued a whole tile
             // earlier.  The refill lands in the slots this tile consumed.
-            rf.commit(ring, tid);
-            if (KV) rv.commit(vring, tid);
+            rf.template commit<ORDER>(ring, tid);
+            if (KV) rv.template commit<0>(vring, tid);
 
             // Coalesced 16-byte stores of the whole tile.  (Storing each lane's
             // ITEMS outputs straight from registers frees the stage's LDS but
             // measured 10% slower, and 2.3x slower with nontemporal stores: the
             // 16-byte pieces of a line then reach HBM apart.)
-            store_tile<THREADS, kStoreVec>(Cs + c_done, c_tile, stage, tid);
+            store_tile<THREADS, kStoreVec, ORDER>(Cs + c_done, c_tile, stage, tid);
             if (KV) {
-                store_tile<THREADS, kStoreVec>(reinterpret_cast<int32_t*>(Cv + k0) + c_done,
+                store_tile<THREADS, kStoreVec, 0>(reinterpret_cast<int32_t*>(Cv + k0) + c_done,
                                                c_tile, vstage, tid);
             }
         }  // general tile

@@ -156,18 +156,19 @@ int check_seg_len(int64_t seg_len) {
     return OMERGE_OK;
 }
 
+template <int ORDER>
 int launch_partition(const int32_t* A, int64_t m, const int32_t* B, int64_t n,
                      int64_t seg_len, int64_t* part, hipStream_t stream) {
     const int64_t count = ceil_div(m + n, seg_len) + 1;
     const int64_t blocks = ceil_div(count * kPartLanes, 256);
     if (blocks > kMaxGridBlocks) return OMERGE_OVERFLOW;
-    hipLaunchKernelGGL(partition_kernel<kPartLanes>, dim3(static_cast<unsigned>(blocks)),
+    hipLaunchKernelGGL((partition_kernel<kPartLanes, ORDER>), dim3(static_cast<unsigned>(blocks)),
                        dim3(256), 0, stream, A, m, B, n, seg_len, count, part);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? OMERGE_OK : hip_fail(e);
 }
 
-template <bool KV>
+template <bool KV, int ORDER>
 int launch_merge(const int32_t* A, const uint32_t* Av, int64_t m,
                  const int32_t* B, const uint32_t* Bv, int64_t n,
                  const int64_t* part, int64_t seg_len, int32_t* C,
@@ -175,7 +176,7 @@ int launch_merge(const int32_t* A, const uint32_t* Av, int64_t m,
     const int64_t segs = ceil_div(m + n, seg_len);
     if (segs > kMaxGridBlocks) return OMERGE_OVERFLOW;
     constexpr int items = KV ? kItemsKV : kItemsI32;
-    hipLaunchKernelGGL((merge_segments_kernel<kThreads, items, KV>),
+    hipLaunchKernelGGL((merge_segments_kernel<kThreads, items, KV, ORDER>),
                        dim3(static_cast<unsigned>(segs)), dim3(kThreads), 0, stream,
                        A, Av, m, B, Bv, n, part, seg_len, C, Cv);
     hipError_t e = hipGetLastError();
@@ -193,7 +194,7 @@ int seg_len_for(int64_t m, int64_t n, bool kv, int64_t* seg_len) {
 }
 
 // Whole merge: partition into stream-ordered scratch, then merge.
-template <bool KV>
+template <bool KV, int ORDER>
 int merge_full(const int32_t* A, const uint32_t* Av, int64_t m,
                const int32_t* B, const uint32_t* Bv, int64_t n, int32_t* C,
                uint32_t* Cv, hipStream_t stream) {
@@ -207,8 +208,9 @@ int merge_full(const int32_t* A, const uint32_t* Av, int64_t m,
     hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&part),
                                   static_cast<size_t>(count) * sizeof(int64_t), stream);
     if (e != hipSuccess) return hip_fail(e);
-    rc = launch_partition(A, m, B, n, seg_len, part, stream);
-    if (rc == OMERGE_OK) rc = launch_merge<KV>(A, Av, m, B, Bv, n, part, seg_len, C, Cv, stream);
+    rc = launch_partition<ORDER>(A, m, B, n, seg_len, part, stream);
+    if (rc == OMERGE_OK)
+        rc = launch_merge<KV, ORDER>(A, Av, m, B, Bv, n, part, seg_len, C, Cv, stream);
     e = hipFreeAsync(part, stream);
     if (rc == OMERGE_OK && e != hipSuccess) rc = hip_fail(e);
     return rc;
@@ -242,6 +244,31 @@ int check_kv_args(const int32_t* Ak, const uint32_t* Av, int64_t m,
     return OMERGE_OK;
 }
 
+// Key order codes of the C ABI (omerge_key_kind | OMERGE_DESCENDING) map onto
+// KeyOrder's template argument one to one; anything else is rejected.
+bool valid_order(int order) {
+    const int kind = order & ~OMERGE_DESCENDING;
+    return kind == OMERGE_KEY_I32 || kind == OMERGE_KEY_U32 || kind == OMERGE_KEY_F32;
+}
+static_assert(OMERGE_KEY_I32 == kKeyI32 && OMERGE_KEY_U32 == kKeyU32 &&
+                  OMERGE_KEY_F32 == kKeyF32 && OMERGE_DESCENDING == 4,
+              "ABI order codes must match KeyOrder");
+
+template <bool KV>
+int merge_ordered(const int32_t* A, const uint32_t* Av, int64_t m, const int32_t* B,
+                  const uint32_t* Bv, int64_t n, int32_t* C, uint32_t* Cv, int order,
+                  hipStream_t stream) {
+    switch (order) {
+        case kKeyI32: return merge_full<KV, kKeyI32>(A, Av, m, B, Bv, n, C, Cv, stream);
+        case kKeyU32: return merge_full<KV, kKeyU32>(A, Av, m, B, Bv, n, C, Cv, stream);
+        case kKeyF32: return merge_full<KV, kKeyF32>(A, Av, m, B, Bv, n, C, Cv, stream);
+        case kKeyI32 | 4: return merge_full<KV, kKeyI32 | 4>(A, Av, m, B, Bv, n, C, Cv, stream);
+        case kKeyU32 | 4: return merge_full<KV, kKeyU32 | 4>(A, Av, m, B, Bv, n, C, Cv, stream);
+        case kKeyF32 | 4: return merge_full<KV, kKeyF32 | 4>(A, Av, m, B, Bv, n, C, Cv, stream);
+        default: return OMERGE_INVALID_ARG;
+    }
+}
+
 int check_part(const int64_t* part, int64_t total, int64_t seg_len) {
     int rc = check_seg_len(seg_len);
     if (rc != OMERGE_OK) return rc;
@@ -261,7 +288,7 @@ int merge_i32(const int32_t* A, int64_t m, const int32_t* B, int64_t n,
               int32_t* C, hipStream_t stream) {
     int rc = check_i32_args(A, m, B, n, C);
     if (rc != OMERGE_OK) return rc;
-    return merge_full<false>(A, nullptr, m, B, nullptr, n, C, nullptr, stream);
+    return merge_full<false, kKeyI32>(A, nullptr, m, B, nullptr, n, C, nullptr, stream);
 }
 
 int merge_kv(const int32_t* A_keys, const uint32_t* A_vals, int64_t m,
@@ -269,7 +296,31 @@ int merge_kv(const int32_t* A_keys, const uint32_t* A_vals, int64_t m,
              int32_t* C_keys, uint32_t* C_vals, hipStream_t stream) {
     int rc = check_kv_args(A_keys, A_vals, m, B_keys, B_vals, n, C_keys, C_vals);
     if (rc != OMERGE_OK) return rc;
-    return merge_full<true>(A_keys, A_vals, m, B_keys, B_vals, n, C_keys, C_vals, stream);
+    return merge_full<true, kKeyI32>(A_keys, A_vals, m, B_keys, B_vals, n, C_keys, C_vals,
+                                     stream);
+}
+
+int omerge_merge_keys(const void* A, int64_t m, const void* B, int64_t n, void* C,
+                      int order, hipStream_t stream) {
+    if (!valid_order(order)) return OMERGE_INVALID_ARG;
+    const int32_t* a = static_cast<const int32_t*>(A);
+    const int32_t* b = static_cast<const int32_t*>(B);
+    int32_t* c = static_cast<int32_t*>(C);
+    int rc = check_i32_args(a, m, b, n, c);
+    if (rc != OMERGE_OK) return rc;
+    return merge_ordered<false>(a, nullptr, m, b, nullptr, n, c, nullptr, order, stream);
+}
+
+int omerge_merge_pairs(const void* A_keys, const uint32_t* A_vals, int64_t m,
+                       const void* B_keys, const uint32_t* B_vals, int64_t n, void* C_keys,
+                       uint32_t* C_vals, int order, hipStream_t stream) {
+    if (!valid_order(order)) return OMERGE_INVALID_ARG;
+    const int32_t* ak = static_cast<const int32_t*>(A_keys);
+    const int32_t* bk = static_cast<const int32_t*>(B_keys);
+    int32_t* ck = static_cast<int32_t*>(C_keys);
+    int rc = check_kv_args(ak, A_vals, m, bk, B_vals, n, ck, C_vals);
+    if (rc != OMERGE_OK) return rc;
+    return merge_ordered<true>(ak, A_vals, m, bk, B_vals, n, ck, C_vals, order, stream);
 }
 
 int omerge_co_rank(const int32_t* A, int64_t m, const int32_t* B, int64_t n,
@@ -284,7 +335,7 @@ int omerge_co_rank(const int32_t* A, int64_t m, const int32_t* B, int64_t n,
         return OMERGE_INVALID_ARG;
     const int64_t blocks = ceil_div(count, kThreads);
     if (blocks > kMaxGridBlocks) return OMERGE_OVERFLOW;
-    hipLaunchKernelGGL(co_rank_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
+    hipLaunchKernelGGL(co_rank_kernel<kKeyI32>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
                        0, stream, A, m, B, n, k, count, i_out);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? OMERGE_OK : hip_fail(e);
@@ -310,7 +361,7 @@ int omerge_partition(const int32_t* A, int64_t m, const int32_t* B, int64_t n,
     rc = check_seg_len(seg_len);
     if (rc != OMERGE_OK) return rc;
     if (part == nullptr || (reinterpret_cast<uintptr_t>(part) & 7)) return OMERGE_INVALID_ARG;
-    return launch_partition(A, m, B, n, seg_len, part, stream);
+    return launch_partition<kKeyI32>(A, m, B, n, seg_len, part, stream);
 }
 
 int omerge_merge_segments_i32(const int32_t* A, int64_t m, const int32_t* B,
@@ -321,7 +372,7 @@ int omerge_merge_segments_i32(const int32_t* A, int64_t m, const int32_t* B,
     rc = check_part(part, m + n, seg_len);
     if (rc != OMERGE_OK) return rc;
     if (m + n == 0) return OMERGE_OK;
-    return launch_merge<false>(A, nullptr, m, B, nullptr, n, part, seg_len, C, nullptr, stream);
+    return launch_merge<false, kKeyI32>(A, nullptr, m, B, nullptr, n, part, seg_len, C, nullptr, stream);
 }
 
 int omerge_merge_segments_kv(const int32_t* A_keys, const uint32_t* A_vals,
@@ -335,7 +386,7 @@ int omerge_merge_segments_kv(const int32_t* A_keys, const uint32_t* A_vals,
     rc = check_part(part, m + n, seg_len);
     if (rc != OMERGE_OK) return rc;
     if (m + n == 0) return OMERGE_OK;
-    return launch_merge<true>(A_keys, A_vals, m, B_keys, B_vals, n, part, seg_len, C_keys,
+    return launch_merge<true, kKeyI32>(A_keys, A_vals, m, B_keys, B_vals, n, part, seg_len, C_keys,
                               C_vals, stream);
 }
 

@@ -59,6 +59,39 @@ static void run_grid(int64_t blocks, int threads, const std::function<void()>& b
     g_barrier = nullptr;
 }
 
+template <int T, int I, bool KV, int ORDER>
+static void typed_cfg(const int32_t* A, const uint32_t* Av, int64_t m, const int32_t* B,
+                      const uint32_t* Bv, int64_t n, int64_t seg_len, int64_t* part, int32_t* C,
+                      uint32_t* Cv) {
+    const int64_t count = (m + n + seg_len - 1) / seg_len + 1;
+    run_grid((count * 4 + 255) / 256, 256, [&] {
+        omerge::partition_kernel<4, ORDER>(A, m, B, n, seg_len, count, part);
+    });
+    if (m + n == 0) return;
+    run_grid(count - 1, T, [&] {
+        omerge::merge_segments_kernel<T, I, KV, ORDER>(A, Av, m, B, Bv, n, part, seg_len, C, Cv);
+    });
+}
+
+template <int ORDER>
+static void typed_order(int variant, int kv, const int32_t* A, const uint32_t* Av, int64_t m,
+                        const int32_t* B, const uint32_t* Bv, int64_t n, int64_t seg_len,
+                        int64_t* part, int32_t* C, uint32_t* Cv) {
+    if (variant == 0) {
+        if constexpr (ORDER == 6) {  // production shapes: float32 descending only
+            if (kv)
+                typed_cfg<256, 8, true, ORDER>(A, Av, m, B, Bv, n, seg_len, part, C, Cv);
+            else
+                typed_cfg<256, 16, false, ORDER>(A, Av, m, B, Bv, n, seg_len, part, C, Cv);
+        }
+        return;
+    }
+    if (kv)
+        typed_cfg<128, 4, true, ORDER>(A, Av, m, B, Bv, n, seg_len, part, C, Cv);
+    else
+        typed_cfg<128, 4, false, ORDER>(A, Av, m, B, Bv, n, seg_len, part, C, Cv);
+}
+
 template <int T, int I, bool KV>
 static void merge_cfg(const int32_t* A, const uint32_t* Av, int64_t m, const int32_t* B,
                       const uint32_t* Bv, int64_t n, const int64_t* part, int64_t seg_len,
@@ -88,18 +121,18 @@ void emu_partition(int lanes, const int32_t* A, int64_t m, const int32_t* B, int
         run_grid(blocks, 256, [&] { kernel(A, m, B, n, seg_len, count, part); });
     };
     switch (lanes) {
-        case 1: go(omerge::partition_kernel<1>); break;
-        case 4: go(omerge::partition_kernel<4>); break;
-        case 8: go(omerge::partition_kernel<8>); break;
-        case 16: go(omerge::partition_kernel<16>); break;
-        default: go(omerge::partition_kernel<64>); break;
+        case 1: go(omerge::partition_kernel<1, 0>); break;
+        case 4: go(omerge::partition_kernel<4, 0>); break;
+        case 8: go(omerge::partition_kernel<8, 0>); break;
+        case 16: go(omerge::partition_kernel<16, 0>); break;
+        default: go(omerge::partition_kernel<64, 0>); break;
     }
 }
 
 void emu_co_rank(const int32_t* A, int64_t m, const int32_t* B, int64_t n, const int64_t* ks,
                  int64_t count, int64_t* out) {
     const int64_t blocks = (count + 255) / 256;
-    run_grid(blocks, 256, [&] { omerge::co_rank_kernel(A, m, B, n, ks, count, out); });
+    run_grid(blocks, 256, [&] { omerge::co_rank_kernel<0>(A, m, B, n, ks, count, out); });
 }
 
 void emu_direct(const int32_t* A, int64_t m, const int32_t* B, int64_t n, int32_t* C,
@@ -123,6 +156,22 @@ void emu_merge_kv(int variant, const int32_t* A, const uint32_t* Av, int64_t m, 
         merge_cfg<256, 8, true>(A, Av, m, B, Bv, n, part, seg_len, C, Cv);
     else
         merge_cfg<128, 4, true>(A, Av, m, B, Bv, n, part, seg_len, C, Cv);
+}
+
+// Partition and merge for a key order (kind | 4 if descending); variant 1 =
+// small shapes for every order, variant 0 = production shapes for order 6.
+void emu_merge_typed(int variant, int order, int kv, const int32_t* A, const uint32_t* Av,
+                     int64_t m, const int32_t* B, const uint32_t* Bv, int64_t n, int64_t seg_len,
+                     int64_t* part, int32_t* C, uint32_t* Cv) {
+    switch (order) {
+        case 0: typed_order<0>(variant, kv, A, Av, m, B, Bv, n, seg_len, part, C, Cv); break;
+        case 1: typed_order<1>(variant, kv, A, Av, m, B, Bv, n, seg_len, part, C, Cv); break;
+        case 2: typed_order<2>(variant, kv, A, Av, m, B, Bv, n, seg_len, part, C, Cv); break;
+        case 4: typed_order<4>(variant, kv, A, Av, m, B, Bv, n, seg_len, part, C, Cv); break;
+        case 5: typed_order<5>(variant, kv, A, Av, m, B, Bv, n, seg_len, part, C, Cv); break;
+        case 6: typed_order<6>(variant, kv, A, Av, m, B, Bv, n, seg_len, part, C, Cv); break;
+        default: break;
+    }
 }
 
 }  // extern "C"

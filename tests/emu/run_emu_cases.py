@@ -30,6 +30,7 @@ def load(path):
     lib.emu_merge_i32.argtypes = [i32, p, i64, p, i64, p, i64, p]
     lib.emu_merge_kv.argtypes = [i32, p, p, i64, p, p, i64, p, i64, p, p]
     lib.emu_direct.argtypes = [p, i64, p, i64, p, i64, i32]
+    lib.emu_merge_typed.argtypes = [i32, i32, i32, p, p, i64, p, p, i64, i64, p, p, p]
     return lib
 
 
@@ -240,7 +241,76 @@ def group_direct(r, g):
                 r.check(np.array_equal(C, want), ("direct", m, n, per, two))
 
 
-GROUPS = {"small": group_small, "direct": group_direct, "skew": group_skew, "blocks": group_blocks,
+def typed_sorted_pair(g, dtype, desc, m, n, pool_f32):
+    """Sorted A, B of one key type in the given direction.  Float keys are
+    drawn from pool_f32, a list already in IEEE totalOrder."""
+    if dtype == np.float32:
+        ia = np.sort(g.integers(0, len(pool_f32), size=m))
+        ib = np.sort(g.integers(0, len(pool_f32), size=n))
+        A, B = pool_f32[ia], pool_f32[ib]
+    else:
+        info = np.iinfo(dtype)
+        span = int(g.choice([3, 1000, 1 << 32]))
+        lo = int(info.min) if span == 1 << 32 else int(g.integers(info.min, int(info.max) - span))
+        A = np.sort(g.integers(lo, lo + span, size=m)).astype(dtype)
+        B = np.sort(g.integers(lo, lo + span, size=n)).astype(dtype)
+    if desc:
+        A, B = A[::-1], B[::-1]
+    return np.ascontiguousarray(A), np.ascontiguousarray(B)
+
+
+def f32_pool(g):
+    """Special binary32 values and random ones, sorted by the oracle's
+    totalOrder relation."""
+    import functools
+    special = np.array([0xFFC00000, 0xFFFFFFFF, 0xFF800001, 0xFF800000, 0xFF7FFFFF, 0xBF800000,
+                        0x80000001, 0x80000000, 0x00000000, 0x00000001, 0x3F800000, 0x7F7FFFFF,
+                        0x7F800000, 0x7F800001, 0x7FC00000, 0x7FFFFFFF], dtype=np.uint32)
+    rnd = g.integers(0, 1 << 32, size=80, dtype=np.uint64).astype(np.uint32)
+    vals = np.unique(np.concatenate([special, rnd])).view(np.float32)
+    cmp = lambda x, y: -1 if not oracle.key_le(np.float32, y, x) else (
+        1 if not oracle.key_le(np.float32, x, y) else 0)
+    return np.array(sorted(vals.tolist(), key=functools.cmp_to_key(
+        lambda a, b: cmp(np.float32(a), np.float32(b)))), dtype=np.float32)
+
+
+def group_orders(r, g):
+    """Every key order (int32/uint32/float32, ascending/descending) through
+    the ordered partition and merge kernels, keys and pairs, against the
+    oracle; the partition against co-ranks read off the oracle's pair tags."""
+    pool = f32_pool(g)
+    tile = r.lib.emu_tile(1, 0)
+    plan = [(o, 1) for o in (0, 1, 2, 4, 5, 6) for _ in range(5)] + [(6, 0)] * 3
+    for c, (order, variant) in enumerate(plan):
+        dtype = {0: np.int32, 1: np.uint32, 2: np.float32}[order & 3]
+        desc = bool(order & 4)
+        big = r.lib.emu_tile(0, 0) if variant == 0 else tile
+        m, n = (int(x) for x in g.integers(0, 5 * big, size=2))
+        if c % 7 == 0:
+            m = 0
+        A, B = typed_sorted_pair(g, dtype, desc, m, n, pool)
+        Av = np.arange(m, dtype=np.uint32)
+        Bv = (U31 + np.arange(n, dtype=np.uint32)).astype(np.uint32)
+        wk, wv = oracle.merge_pairs(A, Av, B, Bv, desc)
+        from_a = np.concatenate([[0], np.cumsum(wv < U31)]).astype(np.int64)
+        for kv in (0, 1):
+            t = r.lib.emu_tile(variant, kv)
+            seg_len = int(g.choice([t, 3 * t, 4 * int(g.integers(1, 300))]))
+            count = (m + n + seg_len - 1) // seg_len + 1
+            part = np.full(count, -3, dtype=np.int64)
+            Ck = np.zeros(m + n, dtype=np.uint32)
+            Cv = np.zeros(m + n, dtype=np.uint32)
+            r.lib.emu_merge_typed(variant, order, kv, ptr(A), ptr(Av), m, ptr(B), ptr(Bv), n,
+                                  seg_len, ptr(part), ptr(Ck), ptr(Cv))
+            ks = np.minimum(np.arange(count, dtype=np.int64) * seg_len, m + n)
+            r.check(np.array_equal(part, from_a[ks]), ("typed partition", order, kv, m, n, seg_len))
+            ok = np.array_equal(Ck, wk.view(np.uint32))
+            if kv:
+                ok = ok and np.array_equal(Cv, wv)
+            r.check(ok, ("typed merge", order, variant, kv, m, n, seg_len))
+
+
+GROUPS = {"orders": group_orders, "small": group_small, "direct": group_direct, "skew": group_skew, "blocks": group_blocks,
           "production": group_production, "unsorted": group_unsorted}
 
 if __name__ == "__main__":

@@ -266,6 +266,176 @@ def pin_kv_lexicographic(orc, m: int = 1 << 16, n: int = 1 << 16,
     assert np.array_equal(Cv, np.concatenate([Av, Bv])[order])
 
 
+# --------------------------------------------- key types and descending order
+#
+# Float keys follow IEEE 754-2008 clause 5.10 (totalOrder).  The table below
+# is written out by hand from that clause and the binary32 encoding (sign bit,
+# 8 exponent bits, 23 fraction bits whose top bit marks a quiet NaN): every
+# entry is a different datum, listed in increasing totalOrder.  The clause's
+# rules used, in order: negative-sign NaNs lie below everything else and
+# positive-sign NaNs above; -0 lies below +0; numbers otherwise by value; among
+# NaNs of one sign, signaling lies nearer zero than quiet, and a larger payload
+# lies farther from zero.
+
+F32_TOTAL_ORDER = [
+    (0xFFFFFFFF, "-qNaN, largest payload"),
+    (0xFFC00001, "-qNaN, payload 1"),
+    (0xFFC00000, "-qNaN, payload 0"),
+    (0xFFBFFFFF, "-sNaN, largest payload"),
+    (0xFF800001, "-sNaN, payload 1"),
+    (0xFF800000, "-infinity"),
+    (0xFF7FFFFF, "-largest finite (-3.4028235e38)"),
+    (0xC0000000, "-2.0"),
+    (0xBF800001, "-(1.0 + 2^-23)"),
+    (0xBF800000, "-1.0"),
+    (0x80800000, "-smallest normal (-2^-126)"),
+    (0x807FFFFF, "-largest subnormal"),
+    (0x80000001, "-smallest subnormal (-2^-149)"),
+    (0x80000000, "-0.0"),
+    (0x00000000, "+0.0"),
+    (0x00000001, "+smallest subnormal (2^-149)"),
+    (0x007FFFFF, "+largest subnormal"),
+    (0x00800000, "+smallest normal (2^-126)"),
+    (0x3F800000, "1.0"),
+    (0x3F800001, "1.0 + 2^-23"),
+    (0x40000000, "2.0"),
+    (0x7F7FFFFF, "largest finite (3.4028235e38)"),
+    (0x7F800000, "+infinity"),
+    (0x7F800001, "+sNaN, payload 1"),
+    (0x7FBFFFFF, "+sNaN, largest payload"),
+    (0x7FC00000, "+qNaN, payload 0"),
+    (0x7FC00001, "+qNaN, payload 1"),
+    (0x7FFFFFFF, "+qNaN, largest payload"),
+]
+
+
+def f32_bits(bits) -> np.ndarray:
+    return np.asarray(bits, dtype=np.uint32).view(np.float32)
+
+
+def pin_f32_total_order_table(orc) -> None:
+    """The order relation on every pair of the hand-written table, both ways."""
+    bits = [b for b, _ in F32_TOTAL_ORDER]
+    vals = f32_bits(bits)
+    for a in range(len(bits)):
+        for b in range(len(bits)):
+            assert orc.key_le(np.float32, vals[a], vals[b]) == (a <= b), \
+                (F32_TOTAL_ORDER[a][1], F32_TOTAL_ORDER[b][1])
+            assert orc.key_le(np.float32, vals[a], vals[b], descending=True) == (a >= b)
+
+
+def _stable_by(rank, A, B):
+    """Brute force: stable sort of the tagged concatenation A||B by rank(x)."""
+    items = [(x, 0, i) for i, x in enumerate(A)] + [(x, 1, j) for j, x in enumerate(B)]
+    order = sorted(range(len(items)), key=lambda t: rank(items[t][0]))
+    return [items[t] for t in order]
+
+
+def _check_typed(orc, A, B, rank, descending) -> None:
+    want = _stable_by(rank, A, B)
+    C = orc.merge_keys(A, B, descending)
+    assert C.dtype == A.dtype
+    assert np.array_equal(C.view(np.uint32),
+                          np.array([w[0] for w in want], dtype=A.dtype).view(np.uint32))
+    Av, Bv = tags(A.size, B.size)
+    Ck, Cv = orc.merge_pairs(A, Av, B, Bv, descending)
+    assert np.array_equal(Ck.view(np.uint32), C.view(np.uint32))
+    want_tags = [(i if side == 0 else (1 << 31) + i) for _, side, i in want]
+    assert np.array_equal(Cv, np.array(want_tags, dtype=np.uint32))
+
+
+def pin_f32_special_brute(orc, seed: int = 37, cases: int = 300) -> None:
+    """Random multisets over the table, sorted by table position (ascending)
+    or its reverse (descending), against the brute-force stable sort."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    bits = np.array([b for b, _ in F32_TOTAL_ORDER], dtype=np.uint32)
+    for c in range(cases):
+        m, n = (int(x) for x in g.integers(0, 12, size=2))
+        desc = bool(c & 1)
+        ia = np.sort(g.integers(0, len(bits), size=m))
+        ib = np.sort(g.integers(0, len(bits), size=n))
+        if desc:
+            ia, ib = ia[::-1], ib[::-1]
+        A, B = f32_bits(bits[ia]), f32_bits(bits[ib])
+        pos = {int(b): r for r, b in enumerate(bits)}
+        rank = (lambda x: -pos[int(np.float32(x).view(np.uint32))]) if desc else \
+            (lambda x: pos[int(np.float32(x).view(np.uint32))])
+        _check_typed(orc, A, B, rank, desc)
+
+
+def pin_f32_numpy_finite(orc, seed: int = 41, cases: int = 40) -> None:
+    """Finite keys, zeros of one sign only: the order is the ordinary numeric
+    one, so numpy's stable sort of the concatenation is the merge (for
+    descending, the stable sort of the negated keys)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    for c in range(cases):
+        m, n = (int(x) for x in g.integers(0, 2000, size=2))
+        desc = bool(c & 1)
+        scale = float(g.choice([1.0, 1e-40, 1e30]))
+        pool = (g.standard_normal(64) * scale).astype(np.float32)
+        pool[pool == 0] = np.float32(0.0)
+        A = np.sort(g.choice(pool, size=m)).astype(np.float32)
+        B = np.sort(g.choice(pool, size=n)).astype(np.float32)
+        if desc:
+            A, B = A[::-1].copy(), B[::-1].copy()
+        cat = np.concatenate([A, B])
+        order = np.argsort(-cat if desc else cat, kind="stable")
+        assert np.array_equal(orc.merge_keys(A, B, desc), cat[order])
+
+
+def pin_integer_kinds_brute(orc, seed: int = 43, cases: int = 200) -> None:
+    """int32 and uint32 keys, both orders, including the type extremes, against
+    the brute-force stable sort by Python integer value."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    for c in range(cases):
+        dtype = np.uint32 if c % 4 < 2 else np.int32
+        desc = bool(c & 1)
+        info = np.iinfo(dtype)
+        pool = np.array([info.min, info.min + 1, -1 if dtype == np.int32 else 1 << 31,
+                         0, 1, (1 << 31) - 1, info.max - 1, info.max], dtype=np.int64)
+        pool = np.concatenate([pool, g.integers(info.min, int(info.max) + 1, size=4)])
+        m, n = (int(x) for x in g.integers(0, 14, size=2))
+        A = np.sort(g.choice(pool, size=m)).astype(dtype)
+        B = np.sort(g.choice(pool, size=n)).astype(dtype)
+        if desc:
+            A, B = A[::-1].copy(), B[::-1].copy()
+        rank = (lambda x: -int(x)) if desc else (lambda x: int(x))
+        _check_typed(orc, A, B, rank, desc)
+
+
+def pin_integer_kinds_numpy(orc, seed: int = 47, cases: int = 24) -> None:
+    """Larger int32 / uint32 cases against numpy's stable argsort (descending:
+    of the reversed keys, max - x, computed in int64)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    for c in range(cases):
+        dtype = np.uint32 if c % 4 < 2 else np.int32
+        desc = bool(c & 1)
+        info = np.iinfo(dtype)
+        span = int(g.choice([4, 1 << 32]))
+        lo = int(info.min) if span > 4 else 0
+        m, n = (int(x) for x in g.integers(0, 5000, size=2))
+        A = np.sort(g.integers(lo, lo + span, size=m)).astype(dtype)
+        B = np.sort(g.integers(lo, lo + span, size=n)).astype(dtype)
+        if desc:
+            A, B = A[::-1].copy(), B[::-1].copy()
+        cat = np.concatenate([A, B])
+        key = int(info.max) - cat.astype(np.int64) if desc else cat.astype(np.int64)
+        order = np.argsort(key, kind="stable")
+        assert np.array_equal(orc.merge_keys(A, B, desc), cat[order])
+
+
+def pin_typed_i32_worked_example(orc) -> None:
+    """The typed routine on int32 ascending reproduces the page's worked
+    example output (12-merge/02), and reversing both inputs and the order
+    gives the reversed output up to the tie rule (checked through tags)."""
+    g = load_golden("worked_example_corank.json")
+    A, B = as_i32(g["A"]), as_i32(g["B"])
+    assert np.array_equal(orc.merge_keys(A, B), orc.merge_i32(A, B))
+    assert orc.merge_keys(A, B).tolist() == [1, 7, 7, 8, 9, 10, 10, 10, 12]
+    Ck = orc.merge_keys(A[::-1].copy(), B[::-1].copy(), descending=True)
+    assert Ck.tolist() == [12, 10, 10, 10, 9, 8, 7, 7, 1]
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_equal_element_case,
@@ -276,6 +446,12 @@ ALL_PINS = [
     pin_even_odd_closed_form,
     pin_invariants,
     pin_kv_lexicographic,
+    pin_f32_total_order_table,
+    pin_f32_special_brute,
+    pin_f32_numpy_finite,
+    pin_integer_kinds_brute,
+    pin_integer_kinds_numpy,
+    pin_typed_i32_worked_example,
 ]
 
 

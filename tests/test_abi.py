@@ -9,7 +9,7 @@ import subprocess
 import pytest
 
 import ordered_merge_sorted_amd as om
-from ordered_merge_sorted_amd import merge as M
+from ordered_merge_sorted_amd import binding as M
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "omerge.h")
@@ -106,6 +106,40 @@ def test_merge_kv_validation():
     assert f(P(a), P(av), 4, P(b), P(bv), 4, P(av), P(cv), P(0)) == M.INVALID_ARG      # C_keys over A_vals
     assert f(P(a), P(av), 4, P(b), P(bv), 4, P(ck), P(bv + 4), P(0)) == M.INVALID_ARG  # C_vals over B_vals
     assert f(P(0), P(0), 0, P(0), P(0), 0, P(0), P(0), P(0)) == M.OK
+
+
+def test_typed_entry_validation():
+    """Order codes outside {0,1,2,4,5,6} are rejected; the typed entries apply
+    the same pointer checks as merge_i32 / merge_kv."""
+    lib = om.load_library()
+    a, av, b, bv = FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000
+    ck, cv = FAKE + 0x4000, FAKE + 0x5000
+    for bad in (3, 7, 8, -1, 1 << 20):
+        assert lib.omerge_merge_keys(P(a), 4, P(b), 4, P(ck), bad, P(0)) == M.INVALID_ARG
+        assert lib.omerge_merge_pairs(P(a), P(av), 4, P(b), P(bv), 4, P(ck), P(cv), bad,
+                                      P(0)) == M.INVALID_ARG
+    for order in (0, 1, 2, 4, 5, 6):
+        assert lib.omerge_merge_keys(P(a), 4, P(b), 4, P(a + 8), order, P(0)) == M.INVALID_ARG
+        assert lib.omerge_merge_keys(P(0), 0, P(0), 0, P(0), order, P(0)) == M.OK
+        assert lib.omerge_merge_pairs(P(a), P(av), 4, P(b), P(bv), 4, P(ck), P(ck + 4), order,
+                                      P(0)) == M.INVALID_ARG
+        assert lib.omerge_merge_pairs(P(0), P(0), 0, P(0), P(0), 0, P(0), P(0), order,
+                                      P(0)) == M.OK
+    assert (M.KEY_I32, M.KEY_U32, M.KEY_F32, M.DESCENDING) == (0, 1, 2, 4)
+    text = open(HEADER).read()
+    for name, v in (("OMERGE_KEY_I32", 0), ("OMERGE_KEY_U32", 1), ("OMERGE_KEY_F32", 2)):
+        assert re.search(r"\b%s = %d\b" % (name, v), text), name
+    assert re.search(r"#define OMERGE_DESCENDING 4\b", text)
+
+
+def test_order_code_of_dtypes():
+    import torch
+    assert om.order_code(torch.int32) == 0
+    assert om.order_code(torch.float32, descending=True) == 6
+    if hasattr(torch, "uint32"):
+        assert om.order_code(torch.uint32) == 1
+    with pytest.raises(TypeError):
+        om.order_code(torch.int64)
 
 
 def test_stage_validation():

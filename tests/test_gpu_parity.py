@@ -268,6 +268,116 @@ def test_unsorted_input_returns():
     assert out.numel() == 80000
 
 
+# ------------------------------------------------------ key types and orders
+
+TYPED = [(np.int32, False), (np.int32, True), (np.uint32, False), (np.uint32, True),
+         (np.float32, False), (np.float32, True)]
+TYPED_IDS = ["%s-%s" % (np.dtype(d).name, "desc" if r else "asc") for d, r in TYPED]
+
+
+def dev_typed(x, off=0):
+    """Keys of any 32-bit dtype to a device tensor of the matching torch dtype
+    (moved as int32 bits)."""
+    tdt = {np.dtype(np.int32): torch.int32, np.dtype(np.uint32): torch.uint32,
+           np.dtype(np.float32): torch.float32}[x.dtype]
+    return dev(np.ascontiguousarray(x).view(np.int32), off).view(tdt)
+
+
+def host_bits(t):
+    return t.view(torch.int32).cpu().numpy().view(np.uint32)
+
+
+_F32_POOL = None
+
+
+def f32_pool():
+    """About 2000 distinct binary32 values, signed zeros, infinities,
+    subnormals and NaNs of both signs among them, sorted with the oracle's
+    totalOrder relation."""
+    global _F32_POOL
+    if _F32_POOL is None:
+        import functools
+        g = np.random.Generator(np.random.PCG64(77))
+        special = np.array([0xFFC00000, 0xFFFFFFFF, 0xFF800001, 0xFF800000, 0xFF7FFFFF,
+                            0x80800000, 0x80000001, 0x80000000, 0x00000000, 0x00000001,
+                            0x00800000, 0x7F7FFFFF, 0x7F800000, 0x7F800001, 0x7FC00000,
+                            0x7FFFFFFF], dtype=np.uint32)
+        finite = (g.standard_normal(1500) * 1e3).astype(np.float32).view(np.uint32)
+        anybits = g.integers(0, 1 << 32, size=500, dtype=np.uint64).astype(np.uint32)
+        vals = np.unique(np.concatenate([special, finite, anybits])).view(np.float32)
+
+        def cmp(x, y):
+            if not oracle.key_le(np.float32, x, y):
+                return 1
+            return 0 if oracle.key_le(np.float32, y, x) else -1
+        _F32_POOL = np.array(sorted(vals.tolist(), key=functools.cmp_to_key(
+            lambda a, b: cmp(np.float32(a), np.float32(b)))), dtype=np.float32)
+    return _F32_POOL
+
+
+def typed_pair(g, dtype, desc, m, n):
+    if dtype == np.float32:
+        pool = f32_pool()
+        A = pool[np.sort(g.integers(0, pool.size, size=m))]
+        B = pool[np.sort(g.integers(0, pool.size, size=n))]
+    else:
+        info = np.iinfo(dtype)
+        span = int(g.choice([3, 5000, 1 << 32]))
+        lo = int(info.min) if span == 1 << 32 else int(g.integers(info.min, int(info.max) - span))
+        A = np.sort(g.integers(lo, lo + span, size=m)).astype(dtype)
+        B = np.sort(g.integers(lo, lo + span, size=n)).astype(dtype)
+    if desc:
+        A, B = A[::-1], B[::-1]
+    return np.ascontiguousarray(A), np.ascontiguousarray(B)
+
+
+@pytest.mark.parametrize("dtype,desc", TYPED, ids=TYPED_IDS)
+def test_typed_keys_and_pairs(dtype, desc):
+    """Every key type and direction, keys and pairs, several tiles plus a
+    ragged tail, every pointer phase; output bits against the oracle."""
+    g = np.random.Generator(np.random.PCG64(500 + TYPED.index((dtype, desc))))
+    for c in range(4):
+        m, n = (int(x) for x in g.integers(0, 60000, size=2))
+        if c == 3:
+            m = 0
+        A, B = typed_pair(g, dtype, desc, m, n)
+        offs = [int(x) for x in g.integers(0, 4, size=6)]
+        say("typed", np.dtype(dtype).name, desc, m, n, offs)
+        got = om.merge(dev_typed(A, offs[0]), dev_typed(B, offs[1]), descending=desc)
+        assert got.dtype == dev_typed(A[:0]).dtype
+        want = oracle.merge_keys(A, B, desc)
+        assert_same(host_bits(got), want.view(np.uint32), "typed keys")
+        Av, Bv = tags(m, n)
+        gk, gv = om.merge_pairs(dev_typed(A, offs[2]), dev(Av, offs[3]), dev_typed(B, offs[4]),
+                                dev(Bv, offs[5]), descending=desc)
+        wk, wv = oracle.merge_pairs(A, Av, B, Bv, desc)
+        assert_same(host_bits(gk), wk.view(np.uint32), "typed pair keys")
+        assert_same(host(gv).view(np.uint32), wv, "typed pair payloads")
+
+
+def test_i32_order_code_is_merge_i32():
+    g = np.random.Generator(np.random.PCG64(611))
+    A, B = pair(g, 30000, 20000, 64)
+    assert_same(host(om.merge(dev(A), dev(B))), host(om.merge_i32(dev(A), dev(B))), "i32 order 0")
+
+
+@pytest.mark.parametrize("dtype,desc", [(np.float32, True), (np.uint32, False)],
+                         ids=["float32-desc", "uint32-asc"])
+def test_typed_large(dtype, desc):
+    """2^24 + 2^24 keys and pairs (8192 tiles) of a non-int32 order."""
+    g = np.random.Generator(np.random.PCG64(613))
+    m = n = 1 << 24
+    A, B = typed_pair(g, dtype, desc, m, n)
+    say("typed large", np.dtype(dtype).name, desc)
+    got = om.merge(dev_typed(A), dev_typed(B), descending=desc)
+    assert_same(host_bits(got), oracle.merge_keys(A, B, desc).view(np.uint32), "typed large")
+    Av, Bv = tags(m, n)
+    gk, gv = om.merge_pairs(dev_typed(A), dev(Av), dev_typed(B), dev(Bv), descending=desc)
+    wk, wv = oracle.merge_pairs(A, Av, B, Bv, desc)
+    assert_same(host_bits(gk), wk.view(np.uint32), "typed large pair keys")
+    assert_same(host(gv).view(np.uint32), wv, "typed large pair payloads")
+
+
 # ------------------------------------------------------- full-size workloads
 
 @pytest.mark.parametrize("name", ORDER)

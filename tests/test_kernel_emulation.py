@@ -49,7 +49,8 @@ def libemu(request, tmp_path_factory):
     return out, rt
 
 
-@pytest.mark.parametrize("group", ["small", "skew", "blocks", "direct", "production", "unsorted"])
+@pytest.mark.parametrize("group", ["small", "skew", "blocks", "direct", "production", "unsorted",
+                                   "orders"])
 def test_emulated_kernels_match_oracle(libemu, group):
     lib, rt = libemu
     env = dict(os.environ, LD_PRELOAD=rt, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1",

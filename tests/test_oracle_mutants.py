@@ -28,6 +28,26 @@ MUTANTS = {
     "co_rank_counts_b": ("            ++i;\n        else\n            ++j;\n        I[k + 1] = i;",
                          "            ++j;\n        else\n            ++i;\n        I[k + 1] = i;"),
     "co_rank_start_one": ("I[0] = 0;", "I[0] = 1;"),
+    "zeros_equal": ("return x_neg >= y_neg;", "return 1;"),
+    "zeros_reversed": ("return x_neg >= y_neg;", "return x_neg <= y_neg;"),
+    "nan_sign_ignored": ("        return x_neg;             /* -NaN before anything",
+                         "        return 0;             /* -NaN before anything"),
+    "nan_pair_sign_ignored": ("            return x_neg;         /* -NaN before +NaN */",
+                              "            return y_neg;         /* -NaN before +NaN */"),
+    "neg_nan_payload_ascending": ("x_neg ? x_frac >= y_frac", "x_neg ? x_frac <= y_frac"),
+    "nan_payload_ignored": ("return x_neg ? x_frac >= y_frac : x_frac <= y_frac;",
+                            "return x_frac + y_frac + 1u > 0u;"),
+    "float_as_signed_int": ("        return total_order_f32(x, y);",
+                            "        return total_order_f32(x, x) && (int32_t)x <= (int32_t)y;"),
+    "u32_as_signed": ("        return x <= y;", "        return (int32_t)x <= (int32_t)y;"),
+    "descending_ties_b_first": ("return le_ascending(kind, y, x);",
+                                "return !le_ascending(kind, x, y);"),
+    "descending_not_reversed": ("return le_ascending(kind, y, x);",
+                                "return le_ascending(kind, x, y);"),
+    "typed_b_exhaustion_dropped": ("    if (j >= n)\n        return 1;\n    if (i < m && oracle_key_le",
+                                   "    if (i < m && oracle_key_le"),
+    "typed_payload_from_b": ("            Cv[k] = Av[i];\n            ++i;\n        } else {\n            Ck[k] = Bk[j];",
+                             "            Cv[k] = Bv[j < n ? j : 0];\n            ++i;\n        } else {\n            Ck[k] = Bk[j];"),
 }
 
 RUNNER = r"""
