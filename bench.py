@@ -132,9 +132,10 @@ def ablation(om, d_arrs, want, w, stream):
 
 def typed_orders(om, d_arrs, c_ref, w, stream):
     """The key orders of omerge_merge_keys on inputs derived from the int32
-    workload on the device: uint32 keys x ^ 2^31 and float32 keys with bits
+    workload on the device: uint32 keys x ^ 2^31, float32 keys with bits
     (x ^ 2^31) >> 1 (non-negative patterns, so bit order is totalOrder; some
-    are infinities and NaNs), each ascending and reversed for descending.
+    are infinities and NaNs), int64 keys x * 2^32 and float64 keys with bits
+    (x ^ 2^31 as uint32) << 31, each ascending and reversed for descending.
     Each output is checked against the same map of the int32 merge output
     (keys only: the sorted multiset is unique) before it is timed."""
     import torch
@@ -146,6 +147,10 @@ def typed_orders(om, d_arrs, c_ref, w, stream):
         "uint32": (lambda x: x ^ sign, getattr(torch, "uint32", torch.int32)),
         "float32": (lambda x: torch.bitwise_right_shift((x ^ sign).view(torch.int32), 1) &
                     0x7FFFFFFF, torch.float32),
+        # 64-bit keys: x * 2^32 (int64), and the 32-bit unsigned image shifted
+        # into a non-negative binary64 pattern (float64)
+        "int64": (lambda x: x.to(torch.int64) << 32, torch.int64),
+        "float64": (lambda x: ((x ^ sign).to(torch.int64) & 0xFFFFFFFF) << 31, torch.float64),
     }
     for name, (f, tdt) in maps.items():
         if name == "uint32" and tdt is torch.int32:
@@ -162,7 +167,8 @@ def typed_orders(om, d_arrs, c_ref, w, stream):
                 om.merge(a, b, descending=desc, out=out, stream=stream)
             go()
             torch.cuda.synchronize()
-            if not torch.equal(out.view(torch.int32), want.contiguous()):
+            bits = torch.int32 if out.element_size() == 4 else torch.int64
+            if not torch.equal(out.view(bits), want.contiguous()):
                 log("FAILED: key order %s%s differs from the mapped int32 merge" %
                     (name, " desc" if desc else ""))
                 sys.exit(1)
@@ -175,7 +181,7 @@ def typed_orders(om, d_arrs, c_ref, w, stream):
             e1.record(stream)
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / 20
-            gbs = w.roofline_bytes / (ms * 1e-3) / 1e9
+            gbs = 2 * w.total * out.element_size() / (ms * 1e-3) / 1e9
             log("%-28s %10.3f %10.1f %8.1f" % (name + (" descending" if desc else " ascending"),
                                                 ms, gbs, 100 * gbs / HBM_PEAK_GBS))
             del a, b, out, want

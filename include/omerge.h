@@ -15,8 +15,9 @@
  *   - Pointers to arrays are DEVICE pointers (HIP device memory, or memory the
  *     device can address).  The caller allocates and owns every buffer,
  *     including outputs; the library never frees a caller's buffer.
- *   - Arrays are 4-byte aligned and contiguous.  Any 4-byte alignment works;
- *     16-byte-aligned arrays take the vector path on every full 16 bytes.
+ *   - Arrays are contiguous and aligned to their element size (4 bytes; 8
+ *     for 64-bit keys or payloads).  Any such alignment works; 16-byte-aligned
+ *     arrays take the vector path on every full 16 bytes.
  *   - Lengths are int64 and must be >= 0.  A pointer may be NULL only when its
  *     length is 0.  m + n == 0 is a no-op that returns OMERGE_OK.
  *   - Outputs must not overlap any input (checked by address range).
@@ -82,46 +83,54 @@ int merge_kv(const int32_t *A_keys, const uint32_t *A_vals, int64_t m,
  * Key types and orders of omerge_merge_keys / omerge_merge_pairs.
  *
  * The pages compare int keys (page "Co-rank Function ...") and float keys
- * (page "merge_path.cu", its kernels and CPU reference).  Every 32-bit key
- * type below merges with the same kernels: each key is mapped to a signed
- * int32 by an order-preserving bijection of its bits on the way into the
- * kernel and mapped back on the way out, so the output keys are the input
- * keys' exact bit patterns.
- *   OMERGE_KEY_I32  signed 32-bit integers (merge_i32's order).
- *   OMERGE_KEY_U32  unsigned 32-bit integers.
- *   OMERGE_KEY_F32  IEEE 754 binary32 in the standard's totalOrder:
- *                   -NaN < -inf < negative finite < -0.0 < +0.0 < positive
- *                   finite < +inf < +NaN; NaNs of one sign order by payload
- *                   bits (larger payload = farther from zero).  -0.0 and +0.0
- *                   are therefore NOT equal keys here.
+ * (page "merge_path.cu", its kernels and CPU reference).  Every key type
+ * below merges with the same kernels: each key is mapped to a signed integer
+ * of its width by an order-preserving bijection of its bits on the way into
+ * the kernel and mapped back on the way out, so the output keys are the
+ * input keys' exact bit patterns.
+ *   OMERGE_KEY_I32 / _I64  signed 32- / 64-bit integers (merge_i32's order).
+ *   OMERGE_KEY_U32 / _U64  unsigned 32- / 64-bit integers.
+ *   OMERGE_KEY_F32 / _F64  IEEE 754 binary32 / binary64 in the standard's
+ *                          totalOrder: -NaN < -inf < negative finite < -0.0 <
+ *                          +0.0 < positive finite < +inf < +NaN; NaNs of one
+ *                          sign order by their fraction bits (larger = farther
+ *                          from zero).  -0.0 and +0.0 are therefore NOT equal
+ *                          keys here.
  * OR-ing OMERGE_DESCENDING reverses the order: A and B must then be sorted
  * descending, and C is descending.  In every order, equal keys keep A's
- * elements first, then each array's own order.
+ * elements first, then each array's own order.  64-bit keys and payloads
+ * must be 8-byte aligned.
  */
 enum omerge_key_kind {
     OMERGE_KEY_I32 = 0,
     OMERGE_KEY_U32 = 1,
-    OMERGE_KEY_F32 = 2
+    OMERGE_KEY_F32 = 2,
+    OMERGE_KEY_I64 = 3,
+    OMERGE_KEY_U64 = 4,
+    OMERGE_KEY_F64 = 5
 };
-#define OMERGE_DESCENDING 4
+#define OMERGE_DESCENDING 8
 
 /*
- * omerge_merge_keys -- stable merge of 32-bit keys of the type and order
- * `order` (an omerge_key_kind, optionally | OMERGE_DESCENDING).
- *   A[m], B[n]  in:  4-byte keys sorted in that order (device).
+ * omerge_merge_keys -- stable merge of keys of the type and order `order`
+ * (an omerge_key_kind, optionally | OMERGE_DESCENDING).
+ *   A[m], B[n]  in:  keys (4 or 8 bytes each, per the kind) sorted in that
+ *                    order (device).
  *   C[m+n]      out: merged keys (device).
  * Same conventions, costs and scratch as merge_i32, which it equals for
  * order == OMERGE_KEY_I32.  An unknown order code is OMERGE_INVALID_ARG.
  *
- * omerge_merge_pairs -- the same for (key, uint32 payload) pairs, as
- * merge_kv; payloads are never compared or changed.
+ * omerge_merge_pairs -- the same for (key, payload) pairs, as merge_kv.
+ * Payloads are payload_bytes (4 or 8) wide; they are never compared or
+ * changed, and move with their keys.  Any other payload_bytes is
+ * OMERGE_INVALID_ARG.
  */
 int omerge_merge_keys(const void *A, int64_t m, const void *B, int64_t n,
                       void *C, int order, struct ihipStream_t *stream);
-int omerge_merge_pairs(const void *A_keys, const uint32_t *A_vals, int64_t m,
-                       const void *B_keys, const uint32_t *B_vals, int64_t n,
-                       void *C_keys, uint32_t *C_vals, int order,
-                       struct ihipStream_t *stream);
+int omerge_merge_pairs(const void *A_keys, const void *A_vals, int64_t m,
+                       const void *B_keys, const void *B_vals, int64_t n,
+                       void *C_keys, void *C_vals, int order,
+                       int payload_bytes, struct ihipStream_t *stream);
 
 /*
  * omerge_co_rank -- device co-rank at arbitrary output ranks (page

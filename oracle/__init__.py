@@ -54,19 +54,32 @@ def _u32(x) -> np.ndarray:
     return x
 
 
-KIND_I32, KIND_U32, KIND_F32, ORDER_DESCENDING = 0, 1, 2, 4
+KIND_I32, KIND_U32, KIND_F32, KIND_I64, KIND_U64, KIND_F64 = 0, 1, 2, 3, 4, 5
+ORDER_DESCENDING = 8
 _KIND = {np.dtype(np.int32): KIND_I32, np.dtype(np.uint32): KIND_U32,
-         np.dtype(np.float32): KIND_F32}
+         np.dtype(np.float32): KIND_F32, np.dtype(np.int64): KIND_I64,
+         np.dtype(np.uint64): KIND_U64, np.dtype(np.float64): KIND_F64}
 _KIND_DTYPE = {v: k for k, v in _KIND.items()}
+_BITS = {4: np.uint32, 8: np.uint64}
 
 
 def _typed_pair(A, B):
-    """Key kind of A and B (same dtype), and both as uint32 bit views."""
+    """Key kind of A and B (same dtype), and both as unsigned bit views."""
     A, B = np.ascontiguousarray(A), np.ascontiguousarray(B)
     if A.dtype != B.dtype or A.dtype not in _KIND:
-        raise TypeError("keys must both be int32, uint32 or float32, got %s and %s"
-                        % (A.dtype, B.dtype))
-    return _KIND[A.dtype], A.view(np.uint32), B.view(np.uint32)
+        raise TypeError("keys must both be one of %s, got %s and %s"
+                        % (sorted(str(d) for d in _KIND), A.dtype, B.dtype))
+    bits = _BITS[A.dtype.itemsize]
+    return _KIND[A.dtype], A.view(bits), B.view(bits)
+
+
+def _payloads(Av, Bv):
+    """Payload arrays of one 4- or 8-byte dtype, as unsigned bit views."""
+    Av, Bv = np.ascontiguousarray(Av), np.ascontiguousarray(Bv)
+    if Av.dtype != Bv.dtype or Av.dtype.itemsize not in _BITS:
+        raise TypeError("payloads must share one 4- or 8-byte dtype")
+    bits = _BITS[Av.dtype.itemsize]
+    return Av.dtype, Av.view(bits), Bv.view(bits)
 
 
 def _ptr(x: np.ndarray):
@@ -87,9 +100,10 @@ class Oracle:
         lib.oracle_co_rank_all.restype = None
         lib.oracle_merge_keys.argtypes = [ctypes.c_int, p, i64, p, i64, p]
         lib.oracle_merge_keys.restype = None
-        lib.oracle_merge_pairs.argtypes = [ctypes.c_int, p, p, i64, p, p, i64, p, p]
+        lib.oracle_merge_pairs.argtypes = [ctypes.c_int, ctypes.c_int, p, p, i64, p, p, i64,
+                                           p, p]
         lib.oracle_merge_pairs.restype = None
-        lib.oracle_key_le.argtypes = [ctypes.c_int, ctypes.c_uint32, ctypes.c_uint32]
+        lib.oracle_key_le.argtypes = [ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64]
         lib.oracle_key_le.restype = ctypes.c_int
         self._lib = lib
         self.path = lib_path
@@ -114,33 +128,37 @@ class Oracle:
         return Ck, Cv
 
     def merge_keys(self, A, B, descending: bool = False) -> np.ndarray:
-        """Stable merge of sorted int32, uint32 or float32 keys in that type's
-        order (float32: IEEE 754 totalOrder), descending if asked; A first on
-        ties.  Returns an array of the keys' dtype holding the input bits."""
+        """Stable merge of sorted keys (int32, uint32, float32, int64, uint64
+        or float64) in that type's order (floats: IEEE 754 totalOrder),
+        descending if asked; A first on ties.  Returns an array of the keys'
+        dtype holding the input bits."""
         kind, A, B = _typed_pair(A, B)
         order = kind | (ORDER_DESCENDING if descending else 0)
-        C = np.empty(A.size + B.size, dtype=np.uint32)
+        C = np.empty(A.size + B.size, dtype=A.dtype)
         self._lib.oracle_merge_keys(order, _ptr(A), A.size, _ptr(B), B.size, _ptr(C))
         return C.view(_KIND_DTYPE[kind])
 
     def merge_pairs(self, A_keys, A_vals, B_keys, B_vals, descending: bool = False):
-        """merge_keys for (key, uint32 payload) pairs; payloads move with keys."""
+        """merge_keys for (key, payload) pairs; payloads of any one 4- or
+        8-byte dtype move with their keys and are returned in that dtype."""
         kind, Ak, Bk = _typed_pair(A_keys, B_keys)
-        Av, Bv = _u32(A_vals), _u32(B_vals)
+        vdt, Av, Bv = _payloads(A_vals, B_vals)
         if Ak.size != Av.size or Bk.size != Bv.size:
             raise ValueError("key and payload lengths differ")
         order = kind | (ORDER_DESCENDING if descending else 0)
-        Ck = np.empty(Ak.size + Bk.size, dtype=np.uint32)
-        Cv = np.empty(Ak.size + Bk.size, dtype=np.uint32)
-        self._lib.oracle_merge_pairs(order, _ptr(Ak), _ptr(Av), Ak.size, _ptr(Bk),
-                                     _ptr(Bv), Bk.size, _ptr(Ck), _ptr(Cv))
-        return Ck.view(_KIND_DTYPE[kind]), Cv
+        Ck = np.empty(Ak.size + Bk.size, dtype=Ak.dtype)
+        Cv = np.empty(Ak.size + Bk.size, dtype=Av.dtype)
+        self._lib.oracle_merge_pairs(order, Av.dtype.itemsize, _ptr(Ak), _ptr(Av), Ak.size,
+                                     _ptr(Bk), _ptr(Bv), Bk.size, _ptr(Ck), _ptr(Cv))
+        return Ck.view(_KIND_DTYPE[kind]), Cv.view(vdt)
 
     def key_le(self, dtype, x, y, descending: bool = False) -> bool:
         """The order relation itself: does key x come before key y, or tie?"""
-        kind = _KIND[np.dtype(dtype)]
-        xb = int(np.array([x], dtype=dtype).view(np.uint32)[0])
-        yb = int(np.array([y], dtype=dtype).view(np.uint32)[0])
+        dt = np.dtype(dtype)
+        kind = _KIND[dt]
+        bits = _BITS[dt.itemsize]
+        xb = int(np.array([x], dtype=dt).view(bits)[0])
+        yb = int(np.array([y], dtype=dt).view(bits)[0])
         order = kind | (ORDER_DESCENDING if descending else 0)
         return bool(self._lib.oracle_key_le(order, xb, yb))
 

@@ -6,8 +6,11 @@ libomerge.so); this package is the thin Python binding over torch tensors.
 from .binding import (  # noqa: F401
     DESCENDING,
     KEY_F32,
+    KEY_F64,
     KEY_I32,
+    KEY_I64,
     KEY_U32,
+    KEY_U64,
     OmergeError,
     co_rank,
     library_path,

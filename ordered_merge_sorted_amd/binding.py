@@ -49,7 +49,7 @@ def load_library() -> ctypes.CDLL:
         "merge_i32": (i32, [p, i64, p, i64, p, p]),
         "merge_kv": (i32, [p, p, i64, p, p, i64, p, p, p]),
         "omerge_merge_keys": (i32, [p, i64, p, i64, p, i32, p]),
-        "omerge_merge_pairs": (i32, [p, p, i64, p, p, i64, p, p, i32, p]),
+        "omerge_merge_pairs": (i32, [p, p, i64, p, p, i64, p, p, i32, i32, p]),
         "omerge_co_rank": (i32, [p, i64, p, i64, p, i64, p, p]),
         "omerge_segment_length": (i64, [i64, i64, i32]),
         "omerge_partition_count": (i64, [i64, i64]),
@@ -157,26 +157,36 @@ def merge_kv(a_keys: torch.Tensor, a_vals: torch.Tensor, b_keys: torch.Tensor,
 
 
 # Key order codes of include/omerge.h (omerge_key_kind | OMERGE_DESCENDING).
-KEY_I32, KEY_U32, KEY_F32, DESCENDING = 0, 1, 2, 4
-_KEY_KIND = {torch.int32: KEY_I32, torch.float32: KEY_F32}
-if hasattr(torch, "uint32"):
-    _KEY_KIND[torch.uint32] = KEY_U32
+KEY_I32, KEY_U32, KEY_F32, KEY_I64, KEY_U64, KEY_F64 = 0, 1, 2, 3, 4, 5
+DESCENDING = 8
+_KEY_KIND = {torch.int32: KEY_I32, torch.float32: KEY_F32,
+             torch.int64: KEY_I64, torch.float64: KEY_F64}
+for _name, _kind in (("uint32", KEY_U32), ("uint64", KEY_U64)):
+    if hasattr(torch, _name):
+        _KEY_KIND[getattr(torch, _name)] = _kind
+# Payloads: any 4- or 8-byte dtype; they are moved as bits, never compared.
+_ANY_PAYLOAD = tuple(d for d in (torch.int32, torch.float32, torch.int64, torch.float64,
+                                 getattr(torch, "uint32", None), getattr(torch, "uint64", None))
+                     if d is not None)
 
 
 def order_code(dtype: torch.dtype, descending: bool = False) -> int:
-    """The C ABI order code for keys of `dtype` (int32, uint32 or float32)."""
+    """The C ABI order code for keys of `dtype` (int32, uint32, float32,
+    int64, uint64 or float64)."""
     if dtype not in _KEY_KIND:
-        raise TypeError("keys must have dtype int32, uint32 or float32, got %s" % dtype)
+        raise TypeError("keys must have dtype int32, uint32, float32, int64, uint64 or "
+                        "float64, got %s" % dtype)
     return _KEY_KIND[dtype] | (DESCENDING if descending else 0)
 
 
 def merge(a: torch.Tensor, b: torch.Tensor, descending: bool = False,
           out: Optional[torch.Tensor] = None,
           stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
-    """Stable merge of sorted 32-bit key tensors (equal keys: a first).
+    """Stable merge of sorted key tensors (equal keys: a first).
 
-    int32 and uint32 compare as integers; float32 compares in IEEE 754
-    totalOrder (-NaN < -inf < ... < -0.0 < +0.0 < ... < +inf < +NaN).  With
+    Integer keys compare as integers of their type; float32 and float64 keys
+    compare in IEEE 754 totalOrder (-NaN < -inf < ... < -0.0 < +0.0 < ... <
+    +inf < +NaN).  With
     descending=True, a and b are sorted descending and so is the result.
     Output keys are the input keys' exact bit patterns."""
     _vec(a, "a", tuple(_KEY_KIND))
@@ -196,12 +206,13 @@ def merge_pairs(a_keys: torch.Tensor, a_vals: torch.Tensor, b_keys: torch.Tensor
                 out_keys: Optional[torch.Tensor] = None,
                 out_vals: Optional[torch.Tensor] = None,
                 stream: Optional[torch.cuda.Stream] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """merge() for (key, 32-bit payload) pairs: payloads move with their keys
-    and are never compared (a's first on equal keys)."""
+    """merge() for (key, payload) pairs, payloads of any 4- or 8-byte dtype:
+    they move with their keys and are never compared (a's first on equal
+    keys)."""
     dev = a_keys.device if isinstance(a_keys, torch.Tensor) else None
     _vec(a_keys, "a_keys", tuple(_KEY_KIND))
     _vec(b_keys, "b_keys", (a_keys.dtype,), dev)
-    _vec(a_vals, "a_vals", _PAYLOAD_DTYPES, dev)
+    _vec(a_vals, "a_vals", _ANY_PAYLOAD, dev)
     _vec(b_vals, "b_vals", (a_vals.dtype,), dev)
     if a_vals.numel() != a_keys.numel() or b_vals.numel() != b_keys.numel():
         raise ValueError("key and payload lengths differ")
@@ -213,7 +224,8 @@ def merge_pairs(a_keys: torch.Tensor, a_vals: torch.Tensor, b_keys: torch.Tensor
     with torch.cuda.device(dev):
         rc = lib.omerge_merge_pairs(_ptr(a_keys), _ptr(a_vals), a_keys.numel(), _ptr(b_keys),
                                     _ptr(b_vals), b_keys.numel(), _ptr(out_keys),
-                                    _ptr(out_vals), order, _stream(dev, stream))
+                                    _ptr(out_vals), order, a_vals.element_size(),
+                                    _stream(dev, stream))
     _raise_on(rc, "omerge_merge_pairs")
     return out_keys, out_vals
 

@@ -33,36 +33,55 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <limits>
+#include <type_traits>
+
 namespace omerge {
 
-// Key orders.  Every supported 32-bit key type and direction is merged as
-// signed int32 after an order-preserving bijection of the key's bits, applied
-// when a key is read from HBM and undone when it is written back, so the
-// output keeps the input's exact bits:
-//   int32 ascending      identity
-//   uint32 ascending     flip the sign bit
-//   float32 ascending    IEEE 754 totalOrder (-NaN < -inf < ... < -0 < +0 <
-//                        ... < +inf < +NaN): flip the low 31 bits of negative
-//                        values, so larger magnitudes sort lower
-//   descending           bitwise NOT of the ascending image (~y = -y-1
-//                        reverses signed order)
-// Ties (equal images) still take A first.  Each map is its own inverse up to
-// the final NOT, which from_ord undoes first.
-enum KeyKind : int { kKeyI32 = 0, kKeyU32 = 1, kKeyF32 = 2 };
+// Key orders.  Every supported key type and direction is merged as a signed
+// integer of the key's width after an order-preserving bijection of its bits,
+// applied when a key is read from HBM and undone when it is written back, so
+// the output keeps the input's exact bits:
+//   int32 / int64 ascending      identity
+//   uint32 / uint64 ascending    flip the sign bit
+//   float32 / float64 ascending  IEEE 754 totalOrder (-NaN < -inf < ... < -0 <
+//                                +0 < ... < +inf < +NaN): flip every bit but
+//                                the sign of negative values, so larger
+//                                magnitudes sort lower
+//   descending                   bitwise NOT of the ascending image
+//                                (~y = -y-1 reverses signed order)
+// Ties (equal images) still take A first.  Each ascending map is its own
+// inverse; from_ord undoes the final NOT first.
+enum KeyKind : int {
+    kKeyI32 = 0,
+    kKeyU32 = 1,
+    kKeyF32 = 2,
+    kKeyI64 = 3,
+    kKeyU64 = 4,
+    kKeyF64 = 5
+};
+constexpr int kKeyDescending = 8;  // OR-ed into a kind: descending order
 
-template <int ORDER>  // ORDER = KeyKind | (descending << 2)
+template <int ORDER>  // ORDER = KeyKind | kKeyDescending (optional)
 struct KeyOrder {
-    static constexpr int kKind = ORDER & 3;
-    static constexpr bool kDescending = (ORDER >> 2) != 0;
-    __host__ __device__ static __forceinline__ int asc(int x) {
-        if (kKind == kKeyU32) return x ^ INT32_MIN;
-        if (kKind == kKeyF32) return x ^ ((x >> 31) & INT32_MAX);
+    static constexpr int kKind = ORDER & 7;
+    static constexpr bool kDescending = (ORDER & kKeyDescending) != 0;
+    static constexpr bool kWide = kKind >= kKeyI64;
+    // The key's bits as a signed integer of its width.
+    using T = typename std::conditional<kWide, long long, int>::type;
+    static constexpr int kWords = kWide ? 2 : 1;  // 32-bit words per key
+    static constexpr T kMax = kWide ? T(INT64_MAX) : T(INT32_MAX);
+    __host__ __device__ static __forceinline__ T asc(T x) {
+        constexpr int kTop = 8 * sizeof(T) - 1;
+        constexpr T kSign = std::numeric_limits<T>::min();  // the sign bit alone
+        if (kKind == kKeyU32 || kKind == kKeyU64) return x ^ kSign;
+        if (kKind == kKeyF32 || kKind == kKeyF64) return x ^ ((x >> kTop) & ~kSign);
         return x;
     }
-    __host__ __device__ static __forceinline__ int to_ord(int x) {
+    __host__ __device__ static __forceinline__ T to_ord(T x) {
         return kDescending ? ~asc(x) : asc(x);
     }
-    __host__ __device__ static __forceinline__ int from_ord(int y) {
+    __host__ __device__ static __forceinline__ T from_ord(T y) {
         return asc(kDescending ? ~y : y);
     }
 };
@@ -81,10 +100,10 @@ __device__ __forceinline__ Idx co_rank(Idx k, Idx m, Idx n, LoadA load_a,
     Idx i_low = k > n ? k - n : Idx(0);
     Idx j_low = k > m ? k - m : Idx(0);
     for (int step = 0; step < max_steps; ++step) {
-        const int a_prev = load_a(i > 0 ? i - 1 : Idx(0));
-        const int a_here = load_a(i < m ? i : m - 1);
-        const int b_prev = load_b(j > 0 ? j - 1 : Idx(0));
-        const int b_here = load_b(j < n ? j : n - 1);
+        const auto a_prev = load_a(i > 0 ? i - 1 : Idx(0));
+        const auto a_here = load_a(i < m ? i : m - 1);
+        const auto b_prev = load_b(j > 0 ? j - 1 : Idx(0));
+        const auto b_here = load_b(j < n ? j : n - 1);
         const bool too_many_a = i > 0 && j < n && a_prev > b_here;
         const bool too_many_b = j > 0 && i < m && b_prev >= a_here;
         if (too_many_a) {
@@ -107,11 +126,9 @@ __device__ __forceinline__ Idx co_rank(Idx k, Idx m, Idx n, LoadA load_a,
 // Co-rank over two arrays in global memory, 64-bit indices, keys compared
 // in the order ORDER (KeyOrder).
 template <int ORDER = 0>
-__device__ __forceinline__ int64_t co_rank_global(int64_t k,
-                                                  const int32_t* __restrict__ A,
-                                                  int64_t m,
-                                                  const int32_t* __restrict__ B,
-                                                  int64_t n) {
+__device__ __forceinline__ int64_t co_rank_global(
+    int64_t k, const typename KeyOrder<ORDER>::T* __restrict__ A, int64_t m,
+    const typename KeyOrder<ORDER>::T* __restrict__ B, int64_t n) {
     using K = KeyOrder<ORDER>;
     return co_rank<int64_t>(
         k, m, n, [=](int64_t x) { return K::to_ord(A[x]); },

@@ -89,26 +89,37 @@ __device__ __forceinline__ int word_phase(const void* p) {
     return static_cast<int>(reinterpret_cast<uintptr_t>(p) >> 2);
 }
 
-template <int THREADS, int ITEMS, bool KV>
+// Tile geometry and LDS layout.  Elements are KW 32-bit words of key (1 or
+// 2) and VW words of payload (0 = keys only, 1 or 2); rings, stages and
+// refills work in 32-bit words, searches and merges in elements.
+template <int THREADS, int ITEMS, int KW, int VW>
 struct MergeCfg {
     static_assert(THREADS % 64 == 0, "whole 64-lane wavefronts");
     static_assert(ITEMS >= 4 && (ITEMS & (ITEMS - 1)) == 0,
                   "ITEMS: a power of two, at least one 16-byte vector");
-    static_assert(ITEMS <= 32 || ITEMS % 32 == 0, "lane-contiguous stage rows");
-    static constexpr int kTile = THREADS * ITEMS;  // outputs per tile
-    static constexpr int kCap = next_pow2(kTile);  // ring capacity per side
+    static_assert(KW == 1 || KW == 2, "32- or 64-bit keys");
+    static_assert(VW >= 0 && VW <= 2, "no payload, or a 32- or 64-bit one");
+    static_assert(ITEMS * KW <= 32 || (ITEMS * KW) % 32 == 0, "lane-contiguous stage rows");
+    static_assert(VW == 0 || ITEMS * VW <= 32 || (ITEMS * VW) % 32 == 0,
+                  "lane-contiguous stage rows");
+    static constexpr bool kKV = VW > 0;
+    static constexpr int kTile = THREADS * ITEMS;       // outputs per tile
+    static constexpr int kCap = next_pow2(kTile * KW);  // key ring words per side
     static constexpr int kMask = kCap - 1;
-    static constexpr int kGuard = ITEMS;           // mirrored slots past the end
-    static constexpr int kSide = kCap + kGuard;    // words per side ring
-    static constexpr int kVec = ITEMS / 4;         // 16-byte vectors per lane
+    static constexpr int kGuard = ITEMS * KW;           // mirrored words past the end
+    static constexpr int kSide = kCap + kGuard;         // words per key side ring
+    static constexpr int kVCap = VW ? next_pow2(kTile * VW) : 1;  // payload ring words
+    static constexpr int kVMask = kVCap - 1;
+    static constexpr int kVSide = VW ? kVCap : 0;       // payload rings need no guard
     static constexpr int kSearchSteps = bit_length(kTile);
-    static constexpr int kStageWords = kTile + kTile / 8;
+    static constexpr int kStageWords = kTile * KW + kTile * KW / 8;
+    static constexpr int kVStageWords = kTile * VW + kTile * VW / 8;
     // LDS layout in 32-bit words.
     static constexpr int kRing = 0;  // keys: A ring [0,kSide), B ring [kSide,2kSide)
-    static constexpr int kValRing = kRing + 2 * kSide;  // payload rings (KV)
-    static constexpr int kStage = kValRing + (KV ? 2 * kSide : 0);
+    static constexpr int kValRing = kRing + 2 * kSide;  // payload rings
+    static constexpr int kStage = kValRing + 2 * kVSide;
     static constexpr int kValStage = kStage + kStageWords;
-    static constexpr int kSplit = kValStage + (KV ? kStageWords : 0);
+    static constexpr int kSplit = kValStage + kVStageWords;
     static constexpr int kWords = kSplit + THREADS;
     static constexpr int kLdsBytes = kWords * 4;
 };
@@ -152,8 +163,10 @@ __device__ __forceinline__ int stage_word(int p) { return p + ((p >> 5) << 2); }
 // whatever the data, so the loop ends even on unsorted input.  All lanes of
 // the wavefront must call this together (the vote is wavefront-wide).
 template <int G, int ORDER>
-__device__ __forceinline__ int64_t co_rank_group(int64_t k, const int32_t* __restrict__ A,
-                                                 int64_t m, const int32_t* __restrict__ B,
+__device__ __forceinline__ int64_t co_rank_group(int64_t k,
+                                                 const typename KeyOrder<ORDER>::T* __restrict__ A,
+                                                 int64_t m,
+                                                 const typename KeyOrder<ORDER>::T* __restrict__ B,
                                                  int64_t n, int g_lane, int g_shift) {
     static_assert(G >= 2 && G <= 64 && (64 % G) == 0, "group size");
     constexpr int kLog = bit_length(G) - 1;
@@ -190,10 +203,10 @@ __device__ __forceinline__ int64_t co_rank_group(int64_t k, const int32_t* __res
 // boundary running the pages' two-test search; G > 1: G lanes per boundary
 // testing G points per round.
 template <int G, int ORDER>
-__global__ __launch_bounds__(256) void partition_kernel(const int32_t* __restrict__ A, int64_t m,
-                                                        const int32_t* __restrict__ B, int64_t n,
-                                                        int64_t seg_len, int64_t count,
-                                                        int64_t* __restrict__ part) {
+__global__ __launch_bounds__(256) void partition_kernel(
+    const typename KeyOrder<ORDER>::T* __restrict__ A, int64_t m,
+    const typename KeyOrder<ORDER>::T* __restrict__ B, int64_t n, int64_t seg_len, int64_t count,
+    int64_t* __restrict__ part) {
     const int64_t gid = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
     if constexpr (G == 1) {
         if (gid >= count) return;
@@ -217,8 +230,8 @@ __global__ __launch_bounds__(256) void partition_kernel(const int32_t* __restric
 // Co-rank at arbitrary ranks, one lane per query, with the pages' two-test
 // search (corank.hpp).
 template <int ORDER>
-__global__ void co_rank_kernel(const int32_t* __restrict__ A, int64_t m,
-                               const int32_t* __restrict__ B, int64_t n,
+__global__ void co_rank_kernel(const typename KeyOrder<ORDER>::T* __restrict__ A, int64_t m,
+                               const typename KeyOrder<ORDER>::T* __restrict__ B, int64_t n,
                                const int64_t* __restrict__ ks, int64_t count,
                                int64_t* __restrict__ out) {
     const int64_t s = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
@@ -298,21 +311,70 @@ __global__ __launch_bounds__(256) void stream_copy_kernel(const int32_t* __restr
 }
 
 // ---------------------------------------------------------------------------
-// Ring refill: copies a segment-relative range [r0, r1) of one side into its
-// ring.  Issue and commit are split so the loads can be in flight while the
-// current tile is merged.  The NL loading lanes share one assignment of the
-// body vectors of side A then side B, so a refill of at most TILE elements
-// needs V = TILE/(4*NL) vectors per lane.  Up to 3 head and 3 tail elements
-// per side are loaded one by one by loading lanes 0..11.  Slots below the
-// guard size are also written to their mirror past the ring's end.
+// Element maps.  Keys enter the rings as their order images
+// (KeyOrder<ORDER>::to_ord) and leave through from_ord; payloads use an
+// identity order of their width.  A 16-byte vector holds 4/W elements of W
+// words: arrays of 64-bit elements are 8-byte aligned, so a 16-byte-aligned
+// vector (and every ring or stage quad) starts on an element.
+
+__device__ __forceinline__ long long join_words(int lo, int hi) {
+    return static_cast<long long>((static_cast<unsigned long long>(static_cast<unsigned>(hi)) << 32) |
+                                  static_cast<unsigned>(lo));
+}
+__device__ __forceinline__ int low_word(long long x) { return static_cast<int>(x); }
+__device__ __forceinline__ int high_word(long long x) { return static_cast<int>(x >> 32); }
+
+template <int ORDER, bool TO>
+__device__ __forceinline__ typename KeyOrder<ORDER>::T map_elem(typename KeyOrder<ORDER>::T x) {
+    return TO ? KeyOrder<ORDER>::to_ord(x) : KeyOrder<ORDER>::from_ord(x);
+}
+
+template <int ORDER, bool TO>
+__device__ __forceinline__ int4v map_vec(int4v x) {
+    if constexpr (KeyOrder<ORDER>::kWords == 1) {
+        x.x = map_elem<ORDER, TO>(x.x);
+        x.y = map_elem<ORDER, TO>(x.y);
+        x.z = map_elem<ORDER, TO>(x.z);
+        x.w = map_elem<ORDER, TO>(x.w);
+    } else {
+        const long long e0 = map_elem<ORDER, TO>(join_words(x.x, x.y));
+        const long long e1 = map_elem<ORDER, TO>(join_words(x.z, x.w));
+        x.x = low_word(e0);
+        x.y = high_word(e0);
+        x.z = low_word(e1);
+        x.w = high_word(e1);
+    }
+    return x;
+}
+
+// One element of type T at word `w` of an LDS or global word array.
+template <typename T>
+__device__ __forceinline__ T ld_elem(const int* base, int w) {
+    return *reinterpret_cast<const T*>(base + w);
+}
+template <typename T>
+__device__ __forceinline__ void st_elem(int* base, int w, T x) {
+    *reinterpret_cast<T*>(base + w) = x;
+}
+
+// ---------------------------------------------------------------------------
+// Ring refill: copies a segment-relative word range [r0, r1) of one side
+// into its ring.  Issue and commit are split so the loads can be in flight
+// while the current tile is merged.  The NL loading lanes share one
+// assignment of the body vectors of side A then side B, so a refill of at
+// most TILE elements needs V = TILE*W/(4*NL) vectors per lane.  The partial
+// vectors at the two ends of a side (up to 3 words each: 3 elements of one
+// word, or 1 element of two) are loaded one element at a time by loading
+// lanes 0..11.  Slots below the guard size are also written to their mirror
+// past the ring's end.
 
 struct SideRange {
-    const int32_t* src;  // segment base of this array in global memory
-    int base;            // ring slot of segment-relative index 0
-    int r0;              // first segment-relative index to load
-    int head;            // elements before the first 16-byte boundary
+    const int32_t* src;  // segment base of this array in global memory (words)
+    int base;            // ring slot of segment-relative word 0
+    int r0;              // first segment-relative word to load
+    int head;            // words before the first 16-byte boundary
     int nvec;            // whole 16-byte vectors
-    int tail;            // elements after the last whole vector
+    int tail;            // words after the last whole vector
 
     __device__ __forceinline__ void set(const int32_t* s, int b, int lo, int hi) {
         src = s;
@@ -326,14 +388,16 @@ struct SideRange {
     }
 };
 
-template <int NL, int V, int CAP, int SIDE>
+template <int NL, int V, int CAP, int SIDE, int ORDER>
 struct Refill {
+    using T = typename KeyOrder<ORDER>::T;  // one element (W words)
+    static constexpr int W = KeyOrder<ORDER>::kWords;
     static constexpr int kVec = V;
     static constexpr int kMask = CAP - 1;
     static constexpr int kGuard = SIDE - CAP;
     int4v body[kVec];
-    int loose;        // one head/tail element (lanes 0..11)
-    int loose_slot;   // its ring word index, or -1
+    T loose;          // one head/tail element (lanes 0..11)
+    int loose_slot;   // its first ring word, or -1
     int loose_side;   // 0 = A ring, 1 = B ring
     SideRange sa, sb;
 
@@ -354,14 +418,14 @@ struct Refill {
         if (tid < 12) {
             const SideRange& s = tid < 6 ? sa : sb;
             const int w = tid < 6 ? tid : tid - 6;
-            int r = -1;
+            int r = -1;  // first word of this lane's element
             if (w < 3) {
-                if (w < s.head) r = s.r0 + w;
-            } else if (w - 3 < s.tail) {
-                r = s.r0 + s.head + 4 * s.nvec + (w - 3);
+                if (W * (w + 1) <= s.head) r = s.r0 + W * w;
+            } else if (W * (w - 2) <= s.tail) {
+                r = s.r0 + s.head + 4 * s.nvec + W * (w - 3);
             }
             if (r >= 0) {
-                loose = s.src[r];
+                loose = ld_elem<T>(s.src, r);
                 loose_slot = (s.base + r) & kMask;
                 loose_side = tid < 6 ? 0 : 1;
             }
@@ -373,20 +437,12 @@ struct Refill {
         if (slot < kGuard) *reinterpret_cast<int4v*>(side + CAP + slot) = x;
     }
 
-    // ring points at the A ring; the B ring starts SIDE words later.  Keys
-    // enter the ring as their order images (KeyOrder<ORDER>::to_ord); payload
-    // rings use the identity order 0.
-    template <int ORDER>
+    // ring points at the A ring; the B ring starts SIDE words later.
     __device__ __forceinline__ void commit(int* ring, int tid) const {
-        using K = KeyOrder<ORDER>;
 #pragma unroll
         for (int v = 0; v < kVec; ++v) {
             const int q = tid + v * NL;
-            int4v x = body[v];
-            x.x = K::to_ord(x.x);
-            x.y = K::to_ord(x.y);
-            x.z = K::to_ord(x.z);
-            x.w = K::to_ord(x.w);
+            const int4v x = map_vec<ORDER, true>(body[v]);
             if (q < sa.nvec) {
                 put4(ring, (sa.base + sa.r0 + sa.head + 4 * q) & kMask, x);
             } else if (q - sa.nvec < sb.nvec) {
@@ -396,29 +452,30 @@ struct Refill {
         }
         if (loose_slot >= 0) {
             int* side = ring + (loose_side ? SIDE : 0);
-            const int y = K::to_ord(loose);
-            side[loose_slot] = y;
-            if (loose_slot < kGuard) side[CAP + loose_slot] = y;
+            const T y = map_elem<ORDER, true>(loose);
+            st_elem<T>(side, loose_slot, y);
+            if (loose_slot < kGuard) st_elem<T>(side, CAP + loose_slot, y);
         }
     }
 };
 
 // Co-rank of diagonal k inside one tile: A window of wa elements starting at
-// ring slot sa, B window of wb elements at slot sb.  Bisects [max(0,k-wb),
-// min(k,wa)] for the first i at which A[i] is not among the first k outputs
-// (A[i] <= B[k-1-i] fails).  STEPS = bit_length(TILE) covers every interval;
-// finished lanes idle through the remaining steps, so the loop has no
-// data-dependent exit.
-template <int STEPS, int MASK>
+// ring word sa, B window of wb elements at word sb, W words per key.  Bisects
+// [max(0,k-wb), min(k,wa)] for the first i at which A[i] is not among the
+// first k outputs (A[i] <= B[k-1-i] fails).  STEPS = bit_length(TILE) covers
+// every interval; finished lanes idle through the remaining steps, so the
+// loop has no data-dependent exit.
+template <int STEPS, int MASK, typename T>
 __device__ __forceinline__ int co_rank_tile(int k, int wa, int wb, const int* ring_a, int sa,
                                             const int* ring_b, int sb) {
+    constexpr int W = sizeof(T) / 4;
     int lo = k > wb ? k - wb : 0;
     int hi = k < wa ? k : wa;
 #pragma unroll
     for (int step = 0; step < STEPS; ++step) {
         const int mid = (lo + hi) >> 1;
-        const int av = ring_a[(sa + mid) & MASK];
-        const int bv = ring_b[(sb + k - 1 - mid) & MASK];
+        const T av = ld_elem<T>(ring_a, (sa + W * mid) & MASK);
+        const T bv = ld_elem<T>(ring_b, (sb + W * (k - 1 - mid)) & MASK);
         const bool live = lo < hi;
         const bool a_first = av <= bv;
         lo = (live && a_first) ? mid + 1 : lo;
@@ -428,15 +485,15 @@ __device__ __forceinline__ int co_rank_tile(int k, int wa, int wb, const int* ri
 }
 
 // Orders x[0..N) ascending when x is bitonic (min/max network).
-template <int N>
-__device__ __forceinline__ void bitonic_clean(int (&x)[N]) {
+template <int N, typename T>
+__device__ __forceinline__ void bitonic_clean(T (&x)[N]) {
 #pragma unroll
     for (int d = N / 2; d >= 1; d >>= 1) {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             if ((i & d) == 0) {
-                const int lo = min(x[i], x[i + d]);
-                const int hi = max(x[i], x[i + d]);
+                const T lo = min(x[i], x[i + d]);
+                const T hi = max(x[i], x[i + d]);
                 x[i] = lo;
                 x[i + d] = hi;
             }
@@ -444,13 +501,15 @@ __device__ __forceinline__ void bitonic_clean(int (&x)[N]) {
     }
 }
 
-// Stores tile outputs [0, len) from the padded LDS stage to dst[0, len) with
-// NS storing lanes (`tid` = 0..NS-1), V 16-byte vectors per lane at most:
-// 16-byte stores on the aligned body, single words at the ends.
+// Stores tile output words [0, len) from the padded LDS stage to dst[0, len)
+// with NS storing lanes (`tid` = 0..NS-1), V 16-byte vectors per lane at
+// most: 16-byte stores on the aligned body, single elements at the ends.
+// Elements leave through KeyOrder<ORDER>::from_ord.
 template <int NS, int V, int ORDER>
 __device__ __forceinline__ void store_tile(int32_t* __restrict__ dst, int len,
                                            const int* stage, int tid) {
-    using K = KeyOrder<ORDER>;
+    using T = typename KeyOrder<ORDER>::T;
+    constexpr int W = KeyOrder<ORDER>::kWords;
     const int head0 = (4 - (word_phase(dst) & 3)) & 3;
     const int head = head0 < len ? head0 : len;
     const int nvec = (len - head) >> 2;
@@ -461,12 +520,8 @@ __device__ __forceinline__ void store_tile(int32_t* __restrict__ dst, int len,
             const int q = tid + v * NS;
             if (q < nvec) {
                 const int p = 4 * q;
-                int4v x = *reinterpret_cast<const int4v*>(stage + stage_word(p));
-                x.x = K::from_ord(x.x);
-                x.y = K::from_ord(x.y);
-                x.z = K::from_ord(x.z);
-                x.w = K::from_ord(x.w);
-                store_stream4(dst + p, x);
+                const int4v x = *reinterpret_cast<const int4v*>(stage + stage_word(p));
+                store_stream4(dst + p, map_vec<ORDER, false>(x));
             }
         }
     } else {
@@ -476,29 +531,34 @@ __device__ __forceinline__ void store_tile(int32_t* __restrict__ dst, int len,
             if (q < nvec) {
                 const int p = head + 4 * q;
                 int4v x;
-                x.x = K::from_ord(stage[stage_word(p)]);
-                x.y = K::from_ord(stage[stage_word(p + 1)]);
-                x.z = K::from_ord(stage[stage_word(p + 2)]);
-                x.w = K::from_ord(stage[stage_word(p + 3)]);
-                store_stream4(dst + p, x);
+                x.x = stage[stage_word(p)];
+                x.y = stage[stage_word(p + 1)];
+                x.z = stage[stage_word(p + 2)];
+                x.w = stage[stage_word(p + 3)];
+                store_stream4(dst + p, map_vec<ORDER, false>(x));
             }
         }
-        if (tid < head) dst[tid] = K::from_ord(stage[stage_word(tid)]);
+        if (W * tid < head) {
+            int* const d = reinterpret_cast<int*>(dst);
+            st_elem<T>(d, W * tid, map_elem<ORDER, false>(ld_elem<T>(stage, stage_word(W * tid))));
+        }
     }
-    if (tid >= 4 && tid - 4 < tail) {
-        const int p = head + 4 * nvec + (tid - 4);
-        dst[p] = K::from_ord(stage[stage_word(p)]);
+    if (tid >= 4 && W * (tid - 3) <= tail) {
+        const int p = head + 4 * nvec + W * (tid - 4);
+        int* const d = reinterpret_cast<int*>(dst);
+        st_elem<T>(d, p, map_elem<ORDER, false>(ld_elem<T>(stage, stage_word(p))));
     }
 }
 
-// Stores a one-sided tile straight from a ring window: output p is the
-// window's element p, at ring slot (start + p) & MASK.  Consecutive lanes read
+// Stores a one-sided tile straight from a ring window: output word p is the
+// window's word p, at ring slot (start + p) & MASK.  Consecutive lanes read
 // consecutive slots (no bank conflicts); 16-byte reads when the ring quads
 // line up with the output's 16-byte vectors, single words otherwise.
 template <int THREADS, int V, int MASK, int ORDER>
 __device__ __forceinline__ void store_from_ring(int32_t* __restrict__ dst, int len,
                                                 const int* side, int start, int tid) {
-    using K = KeyOrder<ORDER>;
+    using T = typename KeyOrder<ORDER>::T;
+    constexpr int W = KeyOrder<ORDER>::kWords;
     const int head0 = (4 - (word_phase(dst) & 3)) & 3;
     const int head = head0 < len ? head0 : len;
     const int nvec = (len - head) >> 2;
@@ -518,44 +578,56 @@ __device__ __forceinline__ void store_from_ring(int32_t* __restrict__ dst, int l
                 x.z = side[(start + p + 2) & MASK];
                 x.w = side[(start + p + 3) & MASK];
             }
-            x.x = K::from_ord(x.x);
-            x.y = K::from_ord(x.y);
-            x.z = K::from_ord(x.z);
-            x.w = K::from_ord(x.w);
-            store_stream4(dst + p, x);
+            store_stream4(dst + p, map_vec<ORDER, false>(x));
         }
     }
-    if (tid < head) dst[tid] = K::from_ord(side[(start + tid) & MASK]);
-    if (tid >= 4 && tid - 4 < tail) {
-        const int p = head + 4 * nvec + (tid - 4);
-        dst[p] = K::from_ord(side[(start + p) & MASK]);
+    int* const d = reinterpret_cast<int*>(dst);
+    if (W * tid < head)
+        st_elem<T>(d, W * tid, map_elem<ORDER, false>(ld_elem<T>(side, (start + W * tid) & MASK)));
+    if (tid >= 4 && W * (tid - 3) <= tail) {
+        const int p = head + 4 * nvec + W * (tid - 4);
+        st_elem<T>(d, p, map_elem<ORDER, false>(ld_elem<T>(side, (start + p) & MASK)));
     }
 }
 
 // ---------------------------------------------------------------------------
 // Segment merge kernel: one workgroup per segment of the output.
+//
+// Keys are typed by ORDER (KeyOrder<ORDER>::T, 1 or 2 words); payloads are
+// VW words per element (0 = keys only), passed as word arrays.
 
-template <int THREADS, int ITEMS, bool KV, int ORDER = 0>
+template <int THREADS, int ITEMS, int VW, int ORDER>
 __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
-    const int32_t* __restrict__ A, const uint32_t* __restrict__ Av, int64_t m,
-    const int32_t* __restrict__ B, const uint32_t* __restrict__ Bv, int64_t n,
+    const typename KeyOrder<ORDER>::T* __restrict__ A, const uint32_t* __restrict__ Av, int64_t m,
+    const typename KeyOrder<ORDER>::T* __restrict__ B, const uint32_t* __restrict__ Bv, int64_t n,
     const int64_t* __restrict__ part, int64_t seg_len,
-    int32_t* __restrict__ C, uint32_t* __restrict__ Cv) {
-    using Cfg = MergeCfg<THREADS, ITEMS, KV>;
+    typename KeyOrder<ORDER>::T* __restrict__ C, uint32_t* __restrict__ Cv) {
+    using Key = typename KeyOrder<ORDER>::T;
+    constexpr int KW = KeyOrder<ORDER>::kWords;
+    constexpr bool KV = VW > 0;
+    // Payloads move through rings and stage as opaque words: an identity
+    // order of the payload's width.
+    constexpr int VORDER = VW == 2 ? kKeyI64 : kKeyI32;
+    using Cfg = MergeCfg<THREADS, ITEMS, KW, VW>;
     constexpr int kTile = Cfg::kTile;
     constexpr int kCap = Cfg::kCap;
     constexpr int kMask = Cfg::kMask;
     constexpr int kSide = Cfg::kSide;
+    constexpr int kVCap = Cfg::kVCap;
+    constexpr int kVMask = Cfg::kVMask;
+    constexpr int kVSide = Cfg::kVSide;
     // Every lane takes part in the refill loads (kLoadVec 16-byte vectors
     // each) and in the tile stores.  (Giving the loads and the stores to
     // separate wavefronts, so that no wavefront's wait on the vector-memory
     // counter ever covers a store, measured 1% slower.)
-    constexpr int kLoadVec = kTile / 4 / THREADS;
-    constexpr int kStoreVec = kTile / 4 / THREADS;
-    using RefillT = Refill<THREADS, kLoadVec, kCap, kSide>;
+    constexpr int kLoadVec = kTile * KW / 4 / THREADS;
+    constexpr int kStoreVec = kLoadVec;
+    constexpr int kVLoadVec = KV ? kTile * VW / 4 / THREADS : 1;
+    using RefillT = Refill<THREADS, kLoadVec, kCap, kSide, ORDER>;
+    using VRefillT = Refill<THREADS, kVLoadVec, kVCap, kVSide, VORDER>;
     __shared__ __attribute__((aligned(16))) int lds[Cfg::kWords];
     int* const ring = lds + Cfg::kRing;      // A ring; B ring at ring + kSide
-    int* const vring = lds + Cfg::kValRing;  // payload rings, same layout
+    int* const vring = lds + Cfg::kValRing;  // payload rings: A, then B at + kVSide
     int* const stage = lds + Cfg::kStage;
     int* const vstage = lds + Cfg::kValStage;
     int* const split = lds + Cfg::kSplit;
@@ -575,21 +647,20 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
     const int b_len = c_len - a_len;
     const int64_t j0 = k0 - i0;
 
-    const int32_t* const As = A + i0;
-    const int32_t* const Bs = B + j0;
-    int32_t* const Cs = C + k0;
+    // Word pointers to the segment's first element of each array.
+    const int32_t* const As = reinterpret_cast<const int32_t*>(A + i0);
+    const int32_t* const Bs = reinterpret_cast<const int32_t*>(B + j0);
+    int32_t* const Cs = reinterpret_cast<int32_t*>(C + k0);
     const int a_base = word_phase(As) & kMask;
     const int b_base = word_phase(Bs) & kMask;
-    // Payload rings use their own arrays' phases; d_a/d_b map a key slot to
-    // the payload slot of the same element.
-    const int32_t* const Avs = KV ? reinterpret_cast<const int32_t*>(Av + i0) : nullptr;
-    const int32_t* const Bvs = KV ? reinterpret_cast<const int32_t*>(Bv + j0) : nullptr;
-    const int va_base = KV ? (word_phase(Avs) & kMask) : 0;
-    const int vb_base = KV ? (word_phase(Bvs) & kMask) : 0;
-    const int d_a = (va_base - a_base) & kMask;
-    const int d_b = (vb_base - b_base) & kMask;
+    // Payload rings use their own arrays' phases.
+    const int32_t* const Avs = KV ? reinterpret_cast<const int32_t*>(Av) + VW * i0 : nullptr;
+    const int32_t* const Bvs = KV ? reinterpret_cast<const int32_t*>(Bv) + VW * j0 : nullptr;
+    int32_t* const Cvs = KV ? reinterpret_cast<int32_t*>(Cv) + VW * k0 : nullptr;
+    const int va_base = KV ? (word_phase(Avs) & kVMask) : 0;
+    const int vb_base = KV ? (word_phase(Bvs) & kVMask) : 0;
 
-    int a_cons = 0, b_cons = 0;  // consumed so far (segment-relative)
+    int a_cons = 0, b_cons = 0;  // elements consumed so far (segment-relative)
     int a_loaded = a_len < kTile ? a_len : kTile;
     int b_loaded = b_len < kTile ? b_len : kTile;
 
@@ -598,21 +669,22 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
         SideRange ra, rb, none;
         none.set(As, a_base, 0, 0);
         RefillT fa, fb;
-        ra.set(As, a_base, 0, a_loaded);
-        rb.set(Bs, b_base, 0, b_loaded);
+        ra.set(As, a_base, 0, KW * a_loaded);
+        rb.set(Bs, b_base, 0, KW * b_loaded);
         fa.issue(ra, none, tid);
         fb.issue(none, rb, tid);
-        fa.template commit<ORDER>(ring, tid);
-        fb.template commit<ORDER>(ring, tid);
-        if (KV) {
+        fa.commit(ring, tid);
+        fb.commit(ring, tid);
+        if constexpr (KV) {
             SideRange va, vb, vnone;
             vnone.set(Avs, va_base, 0, 0);
-            va.set(Avs, va_base, 0, a_loaded);
-            vb.set(Bvs, vb_base, 0, b_loaded);
-            fa.issue(va, vnone, tid);
-            fb.issue(vnone, vb, tid);
-            fa.template commit<0>(vring, tid);
-            fb.template commit<0>(vring, tid);
+            va.set(Avs, va_base, 0, VW * a_loaded);
+            vb.set(Bvs, vb_base, 0, VW * b_loaded);
+            VRefillT ga, gb;
+            ga.issue(va, vnone, tid);
+            gb.issue(vnone, vb, tid);
+            ga.commit(vring, tid);
+            gb.commit(vring, tid);
         }
     }
     __syncthreads();
@@ -622,8 +694,10 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
         const int c_tile = c_len - c_done < kTile ? c_len - c_done : kTile;
         const int wa = a_loaded - a_cons;  // A window in the ring: min(TILE, left)
         const int wb = b_loaded - b_cons;
-        const int sa = (a_base + a_cons) & kMask;  // slot of the window's first A
-        const int sb = (b_base + b_cons) & kMask;
+        const int sa = (a_base + KW * a_cons) & kMask;  // word of the window's first A
+        const int sb = (b_base + KW * b_cons) & kMask;
+        const int vsa = (va_base + VW * a_cons) & kVMask;  // same for the payloads
+        const int vsb = (vb_base + VW * b_cons) & kVMask;
         const int* const ring_a = ring;
         const int* const ring_b = ring + kSide;
 
@@ -637,9 +711,12 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
         int side = 0;  // 0: general tile, 1: all from A, 2: all from B
         if (probe_one_sided) {
             const bool all_a =
-                wa >= c_tile && (wb == 0 || ring_a[(sa + c_tile - 1) & kMask] <= ring_b[sb]);
-            const bool all_b = !all_a && wb >= c_tile &&
-                               (wa == 0 || ring_b[(sb + c_tile - 1) & kMask] < ring_a[sa]);
+                wa >= c_tile && (wb == 0 || ld_elem<Key>(ring_a, (sa + KW * (c_tile - 1)) & kMask) <=
+                                                ld_elem<Key>(ring_b, sb));
+            const bool all_b =
+                !all_a && wb >= c_tile &&
+                (wa == 0 ||
+                 ld_elem<Key>(ring_b, (sb + KW * (c_tile - 1)) & kMask) < ld_elem<Key>(ring_a, sa));
             side = __builtin_amdgcn_readfirstlane(all_a ? 1 : (all_b ? 2 : 0));
         }
 
@@ -649,7 +726,7 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
         int e = 0;
         int x_t;  // A elements this tile consumes
         if (side == 0) {
-            e = co_rank_tile<Cfg::kSearchSteps, kMask>(c_end, wa, wb, ring_a, sa, ring_b, sb);
+            e = co_rank_tile<Cfg::kSearchSteps, kMask, Key>(c_end, wa, wb, ring_a, sa, ring_b, sb);
             split[tid] = e;
             __syncthreads();
             // The same for every lane, so it is moved to a scalar register and
@@ -668,16 +745,17 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
         const int b_cons2 = b_cons + (c_tile - x_t);
         const int a_loaded2 = a_cons2 + kTile < a_len ? a_cons2 + kTile : a_len;
         const int b_loaded2 = b_cons2 + kTile < b_len ? b_cons2 + kTile : b_len;
-        RefillT rf, rv;
+        RefillT rf;
+        VRefillT rv;
         {
             SideRange ra, rb;
-            ra.set(As, a_base, a_loaded, a_loaded2);
-            rb.set(Bs, b_base, b_loaded, b_loaded2);
+            ra.set(As, a_base, KW * a_loaded, KW * a_loaded2);
+            rb.set(Bs, b_base, KW * b_loaded, KW * b_loaded2);
             rf.issue(ra, rb, tid);
-            if (KV) {
+            if constexpr (KV) {
                 SideRange va, vb;
-                va.set(Avs, va_base, a_loaded, a_loaded2);
-                vb.set(Bvs, vb_base, b_loaded, b_loaded2);
+                va.set(Avs, va_base, VW * a_loaded, VW * a_loaded2);
+                vb.set(Bvs, vb_base, VW * b_loaded, VW * b_loaded2);
                 rv.issue(va, vb, tid);
             }
         }
@@ -685,88 +763,100 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
         if (side != 0) {
             const int* const win = side == 1 ? ring_a : ring_b;
             const int start = side == 1 ? sa : sb;
-            store_from_ring<THREADS, kStoreVec, kMask, ORDER>(Cs + c_done, c_tile, win, start, tid);
-            if (KV) {
-                const int* const vwin = side == 1 ? vring : vring + kSide;
-                const int vstart = side == 1 ? (sa + d_a) & kMask : (sb + d_b) & kMask;
-                store_from_ring<THREADS, kStoreVec, kMask, 0>(
-                    reinterpret_cast<int32_t*>(Cv + k0) + c_done, c_tile, vwin, vstart, tid);
+            store_from_ring<THREADS, kStoreVec, kMask, ORDER>(Cs + KW * c_done, KW * c_tile, win,
+                                                              start, tid);
+            if constexpr (KV) {
+                const int* const vwin = side == 1 ? vring : vring + kVSide;
+                const int vstart = side == 1 ? vsa : vsb;
+                store_from_ring<THREADS, kVLoadVec, kVMask, VORDER>(Cvs + VW * c_done,
+                                                                    VW * c_tile, vwin, vstart, tid);
             }
             __syncthreads();  // every read of the consumed slots is done
-            rf.template commit<ORDER>(ring, tid);
-            if (KV) rv.template commit<0>(vring, tid);
+            rf.commit(ring, tid);
+            if constexpr (KV) rv.commit(vring, tid);
         } else {
             const int c_beg = tid * ITEMS < c_tile ? tid * ITEMS : c_tile;
             const int s = tid > 0 ? split[tid - 1] : 0;
 
-            // This lane's row of the stage: ITEMS contiguous words.
-            int* const row = stage + stage_word(tid * ITEMS);
-            if (!KV) {
+            // This lane's row of the stage: ITEMS contiguous elements.
+            int* const row = stage + stage_word(tid * ITEMS * KW);
+            if constexpr (!KV) {
                 // Candidates: the next ITEMS keys of each side from the lane's
                 // split.  The lane's outputs are the ITEMS smallest of them; any
                 // candidate past the lane's own range is >= all of its outputs
                 // (it comes later in the merge), so only candidates past the
-                // window need replacing, by INT_MAX.
+                // window need replacing, by the largest key image.
                 const int bs = c_beg - s;
-                const int* const pa = ring_a + ((sa + s) & kMask);
-                const int* const pb = ring_b + ((sb + bs) & kMask);
-                int a[ITEMS], b[ITEMS], x[ITEMS];
-    #pragma unroll
+                const int* const pa = ring_a + ((sa + KW * s) & kMask);
+                const int* const pb = ring_b + ((sb + KW * bs) & kMask);
+                Key a[ITEMS], b[ITEMS], x[ITEMS];
+#pragma unroll
                 for (int t = 0; t < ITEMS; ++t) {
-                    a[t] = pa[t];
-                    b[t] = pb[t];
+                    a[t] = ld_elem<Key>(pa, KW * t);
+                    b[t] = ld_elem<Key>(pb, KW * t);
                 }
                 if (s + ITEMS > wa || bs + ITEMS > wb) {
-    #pragma unroll
+#pragma unroll
                     for (int t = 0; t < ITEMS; ++t) {
-                        a[t] = s + t < wa ? a[t] : INT32_MAX;
-                        b[t] = bs + t < wb ? b[t] : INT32_MAX;
+                        a[t] = s + t < wa ? a[t] : KeyOrder<ORDER>::kMax;
+                        b[t] = bs + t < wb ? b[t] : KeyOrder<ORDER>::kMax;
                     }
                 }
                 // a ascending followed by b descending is bitonic; the pairwise
                 // minima hold its ITEMS smallest, themselves bitonic.
-    #pragma unroll
+#pragma unroll
                 for (int t = 0; t < ITEMS; ++t) x[t] = min(a[t], b[ITEMS - 1 - t]);
                 bitonic_clean<ITEMS>(x);
-    #pragma unroll
-                for (int v = 0; v < ITEMS / 4; ++v) {
+#pragma unroll
+                for (int v = 0; v < ITEMS * KW / 4; ++v) {
                     int4v q;
-                    q.x = x[4 * v];
-                    q.y = x[4 * v + 1];
-                    q.z = x[4 * v + 2];
-                    q.w = x[4 * v + 3];
+                    if constexpr (KW == 1) {
+                        q.x = x[4 * v];
+                        q.y = x[4 * v + 1];
+                        q.z = x[4 * v + 2];
+                        q.w = x[4 * v + 3];
+                    } else {
+                        q.x = low_word(x[2 * v]);
+                        q.y = high_word(x[2 * v]);
+                        q.z = low_word(x[2 * v + 1]);
+                        q.w = high_word(x[2 * v + 1]);
+                    }
                     *reinterpret_cast<int4v*>(row + 4 * v) = q;
                 }
             } else {
                 // Key+payload: the serial two-pointer merge of the lane's exact
                 // ranges, so equal keys keep A's payloads first.
-                int out[ITEMS];
-                int src[ITEMS];
+                Key out[ITEMS];
+                int src[ITEMS];  // payload ring word of each output
                 int a = s;
                 int b = c_beg - s;
                 const int a_end = e;
                 const int b_end = c_end - e;
-                int ka = ring_a[(sa + a) & kMask];
-                int kb = ring_b[(sb + b) & kMask];
-    #pragma unroll
+                Key ka = ld_elem<Key>(ring_a, (sa + KW * a) & kMask);
+                Key kb = ld_elem<Key>(ring_b, (sb + KW * b) & kMask);
+#pragma unroll
                 for (int t = 0; t < ITEMS; ++t) {
                     const bool take_a = a < a_end && (b >= b_end || ka <= kb);
                     out[t] = take_a ? ka : kb;
-                    src[t] = take_a ? ((sa + a + d_a) & kMask) : kSide + ((sb + b + d_b) & kMask);
+                    src[t] = take_a ? ((vsa + VW * a) & kVMask) : kVSide + ((vsb + VW * b) & kVMask);
                     a += take_a ? 1 : 0;
                     b += take_a ? 0 : 1;
                     if (t + 1 < ITEMS) {
-                        const int w = take_a ? ((sa + a) & kMask) : kSide + ((sb + b) & kMask);
-                        const int nxt = ring[w];
+                        const int w = take_a ? ((sa + KW * a) & kMask) : kSide + ((sb + KW * b) & kMask);
+                        const Key nxt = ld_elem<Key>(ring, w);
                         ka = take_a ? nxt : ka;
                         kb = take_a ? kb : nxt;
                     }
                 }
-                int* const vrow = vstage + stage_word(tid * ITEMS);
-    #pragma unroll
+                int* const vrow = vstage + stage_word(tid * ITEMS * VW);
+#pragma unroll
                 for (int t = 0; t < ITEMS; ++t) {
-                    row[t] = out[t];
-                    vrow[t] = vring[src[t]];
+                    st_elem<Key>(row, KW * t, out[t]);
+                    if constexpr (VW == 1) {
+                        vrow[t] = vring[src[t]];
+                    } else {
+                        st_elem<long long>(vrow, 2 * t, ld_elem<long long>(vring, src[t]));
+                    }
                 }
             }
             __syncthreads();
@@ -775,17 +865,17 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
             // the vector-memory counter (which counts loads and stores alike)
             // then covers the refill loads and only stores issued a whole tile
             // earlier.  The refill lands in the slots this tile consumed.
-            rf.template commit<ORDER>(ring, tid);
-            if (KV) rv.template commit<0>(vring, tid);
+            rf.commit(ring, tid);
+            if constexpr (KV) rv.commit(vring, tid);
 
             // Coalesced 16-byte stores of the whole tile.  (Storing each lane's
             // ITEMS outputs straight from registers frees the stage's LDS but
             // measured 10% slower, and 2.3x slower with nontemporal stores: the
             // 16-byte pieces of a line then reach HBM apart.)
-            store_tile<THREADS, kStoreVec, ORDER>(Cs + c_done, c_tile, stage, tid);
-            if (KV) {
-                store_tile<THREADS, kStoreVec, 0>(reinterpret_cast<int32_t*>(Cv + k0) + c_done,
-                                               c_tile, vstage, tid);
+            store_tile<THREADS, kStoreVec, ORDER>(Cs + KW * c_done, KW * c_tile, stage, tid);
+            if constexpr (KV) {
+                store_tile<THREADS, kVLoadVec, VORDER>(Cvs + VW * c_done, VW * c_tile, vstage,
+                                                       tid);
             }
         }  // general tile
 

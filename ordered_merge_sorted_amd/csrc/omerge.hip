@@ -34,19 +34,33 @@ constexpr int kVersion = 100;  // 0.1.0
 #ifndef OMERGE_TILES_PER_SEG  // target tiles per workgroup segment
 #define OMERGE_TILES_PER_SEG 8
 #endif
+#ifndef OMERGE_ITEMS_WIDE  // 64-bit keys, keys only
+#define OMERGE_ITEMS_WIDE 8
+#endif
+#ifndef OMERGE_ITEMS_MIXED  // 12- and 16-byte elements (a 64-bit key or payload)
+#define OMERGE_ITEMS_MIXED 4
+#endif
 #ifndef OMERGE_COPY_UNROLL
 #define OMERGE_COPY_UNROLL 4
 #endif
 constexpr int kThreads = OMERGE_THREADS;
-constexpr int kItemsI32 = OMERGE_ITEMS_I32;
-constexpr int kItemsKV = OMERGE_ITEMS_KV;
 constexpr int kPartLanes = OMERGE_PART_LANES;
 constexpr int kTargetTilesPerSeg = OMERGE_TILES_PER_SEG;
 constexpr int kMinTilesPerSeg = kTargetTilesPerSeg > 2 ? kTargetTilesPerSeg - 2 : 1;
 constexpr int kMaxTilesPerSeg = kTargetTilesPerSeg + 2;
 constexpr int kCopyUnroll = OMERGE_COPY_UNROLL;  // 16-byte vectors per lane in the copy
-using CfgI32 = MergeCfg<kThreads, kItemsI32, false>;
-using CfgKV = MergeCfg<kThreads, kItemsKV, true>;
+
+// Outputs per lane for KW key words and VW payload words per element: about
+// 64 bytes of element per lane, so every shape's tile moves ~16 KB and its
+// LDS (two rings and a stage per array) fits three workgroups per CU.
+constexpr int items_for(int kw, int vw) {
+    return kw == 1 && vw == 0   ? OMERGE_ITEMS_I32
+           : kw == 1 && vw == 1 ? OMERGE_ITEMS_KV
+           : kw == 2 && vw == 0 ? OMERGE_ITEMS_WIDE
+                                : OMERGE_ITEMS_MIXED;
+}
+constexpr int shape_index(int kw, int vw) { return (kw - 1) * 3 + vw; }
+constexpr int kShapes = 6;
 
 constexpr int64_t kMaxSegLen = int64_t(1) << 30;
 constexpr int64_t kMaxTotal = int64_t(1) << 62;
@@ -59,41 +73,38 @@ int hip_fail(hipError_t e) {
     return OMERGE_HIP_ERROR;
 }
 
-// Per-device launch facts, filled once per device.
+// Per-device launch facts, filled once per device and element shape.
 struct DeviceInfo {
-    bool ready = false;
     int cus = 0;
-    int wg_per_cu_i32 = 0;
-    int wg_per_cu_kv = 0;
+    int wg_per_cu[kShapes] = {};  // 0 = not yet queried
 };
 constexpr int kMaxDevices = 64;
 DeviceInfo g_dev[kMaxDevices];
 std::mutex g_dev_mutex;
 
-int device_info(DeviceInfo* out) {
+// Resident workgroups per CU of `kernel` on the current device (cached per
+// shape), and the device's CU count.
+int device_slots(int shape, const void* kernel, int* cus, int* wg_per_cu) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e);
     if (dev < 0 || dev >= kMaxDevices) return OMERGE_INVALID_ARG;
     std::lock_guard<std::mutex> lock(g_dev_mutex);
     DeviceInfo& d = g_dev[dev];
-    if (!d.ready) {
-        int cus = 0;
-        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (d.cus == 0) {
+        int c = 0;
+        e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return hip_fail(e);
-        int a = 0, b = 0;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &a, merge_segments_kernel<kThreads, kItemsI32, false>, kThreads, 0);
-        if (e != hipSuccess) return hip_fail(e);
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &b, merge_segments_kernel<kThreads, kItemsKV, true>, kThreads, 0);
-        if (e != hipSuccess) return hip_fail(e);
-        d.cus = cus > 0 ? cus : 1;
-        d.wg_per_cu_i32 = a > 0 ? a : 1;
-        d.wg_per_cu_kv = b > 0 ? b : 1;
-        d.ready = true;
+        d.cus = c > 0 ? c : 1;
     }
-    *out = d;
+    if (d.wg_per_cu[shape] == 0) {
+        int a = 0;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, kernel, kThreads, 0);
+        if (e != hipSuccess) return hip_fail(e);
+        d.wg_per_cu[shape] = a > 0 ? a : 1;
+    }
+    *cus = d.cus;
+    *wg_per_cu = d.wg_per_cu[shape];
     return OMERGE_OK;
 }
 
@@ -132,17 +143,20 @@ int64_t choose_seg_len(int64_t total, int tile, int slots) {
     return best_r * tile;
 }
 
-bool overlaps(const void* p, int64_t pn, const void* q, int64_t qn) {
-    if (!p || !q || pn <= 0 || qn <= 0) return false;
-    const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), a1 = a0 + uintptr_t(pn) * 4;
-    const uintptr_t b0 = reinterpret_cast<uintptr_t>(q), b1 = b0 + uintptr_t(qn) * 4;
+// Byte ranges [p, p+pb) and [q, q+qb) intersect.
+bool overlaps(const void* p, int64_t pb, const void* q, int64_t qb) {
+    if (!p || !q || pb <= 0 || qb <= 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), a1 = a0 + uintptr_t(pb);
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(q), b1 = b0 + uintptr_t(qb);
     return a0 < b1 && b0 < a1;
 }
 
-bool bad_array(const void* p, int64_t len) {
+// An array of `len` elements of `size` bytes: NULL only when empty, aligned
+// to its element size.
+bool bad_array(const void* p, int64_t len, int size = 4) {
     if (len < 0) return true;
     if (len == 0) return false;
-    return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 3) != 0;
+    return p == nullptr || (reinterpret_cast<uintptr_t>(p) & uintptr_t(size - 1)) != 0;
 }
 
 int check_sizes(int64_t m, int64_t n) {
@@ -156,117 +170,94 @@ int check_seg_len(int64_t seg_len) {
     return OMERGE_OK;
 }
 
-template <int ORDER>
-int launch_partition(const int32_t* A, int64_t m, const int32_t* B, int64_t n,
-                     int64_t seg_len, int64_t* part, hipStream_t stream) {
-    const int64_t count = ceil_div(m + n, seg_len) + 1;
-    const int64_t blocks = ceil_div(count * kPartLanes, 256);
-    if (blocks > kMaxGridBlocks) return OMERGE_OVERFLOW;
-    hipLaunchKernelGGL((partition_kernel<kPartLanes, ORDER>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(256), 0, stream, A, m, B, n, seg_len, count, part);
-    hipError_t e = hipGetLastError();
-    return e == hipSuccess ? OMERGE_OK : hip_fail(e);
-}
+// Launch helpers for one key order and payload width.  Keys are typed by
+// the order (KeyOrder<ORDER>::T); payloads travel as VW 32-bit words.
+template <int VW, int ORDER>
+struct Path {
+    using Key = typename KeyOrder<ORDER>::T;
+    static constexpr int KW = KeyOrder<ORDER>::kWords;
+    static constexpr int kItems = items_for(KW, VW);
+    static constexpr int kTile = kThreads * kItems;
+    static constexpr int kShape = shape_index(KW, VW);
 
-template <bool KV, int ORDER>
-int launch_merge(const int32_t* A, const uint32_t* Av, int64_t m,
-                 const int32_t* B, const uint32_t* Bv, int64_t n,
-                 const int64_t* part, int64_t seg_len, int32_t* C,
-                 uint32_t* Cv, hipStream_t stream) {
-    const int64_t segs = ceil_div(m + n, seg_len);
-    if (segs > kMaxGridBlocks) return OMERGE_OVERFLOW;
-    constexpr int items = KV ? kItemsKV : kItemsI32;
-    hipLaunchKernelGGL((merge_segments_kernel<kThreads, items, KV, ORDER>),
-                       dim3(static_cast<unsigned>(segs)), dim3(kThreads), 0, stream,
-                       A, Av, m, B, Bv, n, part, seg_len, C, Cv);
-    hipError_t e = hipGetLastError();
-    return e == hipSuccess ? OMERGE_OK : hip_fail(e);
-}
+    static int seg_len(int64_t m, int64_t n, int64_t* out) {
+        int cus = 0, per_cu = 0;
+        int rc = device_slots(kShape,
+                              reinterpret_cast<const void*>(
+                                  merge_segments_kernel<kThreads, kItems, VW, ORDER>),
+                              &cus, &per_cu);
+        if (rc != OMERGE_OK) return rc;
+        *out = choose_seg_len(m + n, kTile, cus * per_cu);
+        return OMERGE_OK;
+    }
 
-int seg_len_for(int64_t m, int64_t n, bool kv, int64_t* seg_len) {
-    DeviceInfo d;
-    int rc = device_info(&d);
-    if (rc != OMERGE_OK) return rc;
-    const int tile = kv ? CfgKV::kTile : CfgI32::kTile;
-    const int slots = d.cus * (kv ? d.wg_per_cu_kv : d.wg_per_cu_i32);
-    *seg_len = choose_seg_len(m + n, tile, slots);
-    return OMERGE_OK;
-}
+    static int partition(const Key* A, int64_t m, const Key* B, int64_t n, int64_t seg_len,
+                         int64_t* part, hipStream_t stream) {
+        const int64_t count = ceil_div(m + n, seg_len) + 1;
+        const int64_t blocks = ceil_div(count * kPartLanes, 256);
+        if (blocks > kMaxGridBlocks) return OMERGE_OVERFLOW;
+        hipLaunchKernelGGL((partition_kernel<kPartLanes, ORDER>),
+                           dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, A, m, B, n,
+                           seg_len, count, part);
+        hipError_t e = hipGetLastError();
+        return e == hipSuccess ? OMERGE_OK : hip_fail(e);
+    }
 
-// Whole merge: partition into stream-ordered scratch, then merge.
-template <bool KV, int ORDER>
-int merge_full(const int32_t* A, const uint32_t* Av, int64_t m,
-               const int32_t* B, const uint32_t* Bv, int64_t n, int32_t* C,
-               uint32_t* Cv, hipStream_t stream) {
-    const int64_t total = m + n;
-    if (total == 0) return OMERGE_OK;
-    int64_t seg_len = 0;
-    int rc = seg_len_for(m, n, KV, &seg_len);
-    if (rc != OMERGE_OK) return rc;
-    const int64_t count = ceil_div(total, seg_len) + 1;
-    int64_t* part = nullptr;
-    hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&part),
-                                  static_cast<size_t>(count) * sizeof(int64_t), stream);
-    if (e != hipSuccess) return hip_fail(e);
-    rc = launch_partition<ORDER>(A, m, B, n, seg_len, part, stream);
-    if (rc == OMERGE_OK)
-        rc = launch_merge<KV, ORDER>(A, Av, m, B, Bv, n, part, seg_len, C, Cv, stream);
-    e = hipFreeAsync(part, stream);
-    if (rc == OMERGE_OK && e != hipSuccess) rc = hip_fail(e);
-    return rc;
-}
+    static int merge(const Key* A, const uint32_t* Av, int64_t m, const Key* B,
+                     const uint32_t* Bv, int64_t n, const int64_t* part, int64_t seg_len, Key* C,
+                     uint32_t* Cv, hipStream_t stream) {
+        const int64_t segs = ceil_div(m + n, seg_len);
+        if (segs > kMaxGridBlocks) return OMERGE_OVERFLOW;
+        hipLaunchKernelGGL((merge_segments_kernel<kThreads, kItems, VW, ORDER>),
+                           dim3(static_cast<unsigned>(segs)), dim3(kThreads), 0, stream, A, Av, m,
+                           B, Bv, n, part, seg_len, C, Cv);
+        hipError_t e = hipGetLastError();
+        return e == hipSuccess ? OMERGE_OK : hip_fail(e);
+    }
 
-int check_i32_args(const int32_t* A, int64_t m, const int32_t* B, int64_t n,
-                   const int32_t* C) {
-    int rc = check_sizes(m, n);
-    if (rc != OMERGE_OK) return rc;
-    if (bad_array(A, m) || bad_array(B, n) || bad_array(C, m + n)) return OMERGE_INVALID_ARG;
-    if (overlaps(C, m + n, A, m) || overlaps(C, m + n, B, n)) return OMERGE_INVALID_ARG;
-    return OMERGE_OK;
-}
+    // Whole merge: partition into stream-ordered scratch, then merge.
+    static int full(const void* A, const void* Av, int64_t m, const void* B, const void* Bv,
+                    int64_t n, void* C, void* Cv, hipStream_t stream) {
+        const int64_t total = m + n;
+        if (total == 0) return OMERGE_OK;
+        int64_t sl = 0;
+        int rc = seg_len(m, n, &sl);
+        if (rc != OMERGE_OK) return rc;
+        const int64_t count = ceil_div(total, sl) + 1;
+        int64_t* part = nullptr;
+        hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&part),
+                                      static_cast<size_t>(count) * sizeof(int64_t), stream);
+        if (e != hipSuccess) return hip_fail(e);
+        const Key* a = static_cast<const Key*>(A);
+        const Key* b = static_cast<const Key*>(B);
+        rc = partition(a, m, b, n, sl, part, stream);
+        if (rc == OMERGE_OK)
+            rc = merge(a, static_cast<const uint32_t*>(Av), m, b, static_cast<const uint32_t*>(Bv),
+                       n, part, sl, static_cast<Key*>(C), static_cast<uint32_t*>(Cv), stream);
+        e = hipFreeAsync(part, stream);
+        if (rc == OMERGE_OK && e != hipSuccess) rc = hip_fail(e);
+        return rc;
+    }
+};
 
-int check_kv_args(const int32_t* Ak, const uint32_t* Av, int64_t m,
-                  const int32_t* Bk, const uint32_t* Bv, int64_t n,
-                  const int32_t* Ck, const uint32_t* Cv) {
+// Argument checks shared by every merge entry point: kb / vb = key / payload
+// bytes per element (vb = 0: keys only).
+int check_merge_args(const void* A, const void* Av, int64_t m, const void* B, const void* Bv,
+                     int64_t n, const void* C, const void* Cv, int kb, int vb) {
     int rc = check_sizes(m, n);
     if (rc != OMERGE_OK) return rc;
     const int64_t t = m + n;
-    if (bad_array(Ak, m) || bad_array(Av, m) || bad_array(Bk, n) || bad_array(Bv, n) ||
-        bad_array(Ck, t) || bad_array(Cv, t))
+    if (bad_array(A, m, kb) || bad_array(B, n, kb) || bad_array(C, t, kb)) return OMERGE_INVALID_ARG;
+    if (vb && (bad_array(Av, m, vb) || bad_array(Bv, n, vb) || bad_array(Cv, t, vb)))
         return OMERGE_INVALID_ARG;
-    const void* ins[4] = {Ak, Av, Bk, Bv};
-    const int64_t lens[4] = {m, m, n, n};
+    const void* ins[4] = {A, B, Av, Bv};
+    const int64_t lens[4] = {m * kb, n * kb, m * vb, n * vb};
     for (int i = 0; i < 4; ++i) {
-        if (overlaps(Ck, t, ins[i], lens[i]) || overlaps(Cv, t, ins[i], lens[i]))
+        if (overlaps(C, t * kb, ins[i], lens[i]) || overlaps(Cv, t * vb, ins[i], lens[i]))
             return OMERGE_INVALID_ARG;
     }
-    if (overlaps(Ck, t, Cv, t)) return OMERGE_INVALID_ARG;
+    if (overlaps(C, t * kb, Cv, t * vb)) return OMERGE_INVALID_ARG;
     return OMERGE_OK;
-}
-
-// Key order codes of the C ABI (omerge_key_kind | OMERGE_DESCENDING) map onto
-// KeyOrder's template argument one to one; anything else is rejected.
-bool valid_order(int order) {
-    const int kind = order & ~OMERGE_DESCENDING;
-    return kind == OMERGE_KEY_I32 || kind == OMERGE_KEY_U32 || kind == OMERGE_KEY_F32;
-}
-static_assert(OMERGE_KEY_I32 == kKeyI32 && OMERGE_KEY_U32 == kKeyU32 &&
-                  OMERGE_KEY_F32 == kKeyF32 && OMERGE_DESCENDING == 4,
-              "ABI order codes must match KeyOrder");
-
-template <bool KV>
-int merge_ordered(const int32_t* A, const uint32_t* Av, int64_t m, const int32_t* B,
-                  const uint32_t* Bv, int64_t n, int32_t* C, uint32_t* Cv, int order,
-                  hipStream_t stream) {
-    switch (order) {
-        case kKeyI32: return merge_full<KV, kKeyI32>(A, Av, m, B, Bv, n, C, Cv, stream);
-        case kKeyU32: return merge_full<KV, kKeyU32>(A, Av, m, B, Bv, n, C, Cv, stream);
-        case kKeyF32: return merge_full<KV, kKeyF32>(A, Av, m, B, Bv, n, C, Cv, stream);
-        case kKeyI32 | 4: return merge_full<KV, kKeyI32 | 4>(A, Av, m, B, Bv, n, C, Cv, stream);
-        case kKeyU32 | 4: return merge_full<KV, kKeyU32 | 4>(A, Av, m, B, Bv, n, C, Cv, stream);
-        case kKeyF32 | 4: return merge_full<KV, kKeyF32 | 4>(A, Av, m, B, Bv, n, C, Cv, stream);
-        default: return OMERGE_INVALID_ARG;
-    }
 }
 
 int check_part(const int64_t* part, int64_t total, int64_t seg_len) {
@@ -277,6 +268,53 @@ int check_part(const int64_t* part, int64_t total, int64_t seg_len) {
     return OMERGE_OK;
 }
 
+// Key order codes of the C ABI (omerge_key_kind | OMERGE_DESCENDING) map onto
+// KeyOrder's template argument one to one.
+static_assert(OMERGE_KEY_I32 == kKeyI32 && OMERGE_KEY_U32 == kKeyU32 &&
+                  OMERGE_KEY_F32 == kKeyF32 && OMERGE_KEY_I64 == kKeyI64 &&
+                  OMERGE_KEY_U64 == kKeyU64 && OMERGE_KEY_F64 == kKeyF64 &&
+                  OMERGE_DESCENDING == kKeyDescending,
+              "ABI order codes must match KeyOrder");
+
+bool valid_order(int order) {
+    const int kind = order & ~kKeyDescending;
+    return kind >= kKeyI32 && kind <= kKeyF64;
+}
+int key_bytes(int order) { return (order & 7) >= kKeyI64 ? 8 : 4; }
+
+template <int VW, int ORDER>
+int full_for(const void* A, const void* Av, int64_t m, const void* B, const void* Bv, int64_t n,
+             void* C, void* Cv, hipStream_t stream) {
+    return Path<VW, ORDER>::full(A, Av, m, B, Bv, n, C, Cv, stream);
+}
+
+// Dispatch on the order code (after valid_order) for payload width VW.
+template <int VW>
+int merge_ordered(int order, const void* A, const void* Av, int64_t m, const void* B,
+                  const void* Bv, int64_t n, void* C, void* Cv, hipStream_t stream) {
+#define OMERGE_CASE(o) \
+    case o: return full_for<VW, o>(A, Av, m, B, Bv, n, C, Cv, stream);
+    switch (order) {
+        OMERGE_CASE(kKeyI32)
+        OMERGE_CASE(kKeyU32)
+        OMERGE_CASE(kKeyF32)
+        OMERGE_CASE(kKeyI64)
+        OMERGE_CASE(kKeyU64)
+        OMERGE_CASE(kKeyF64)
+        OMERGE_CASE(kKeyI32 | kKeyDescending)
+        OMERGE_CASE(kKeyU32 | kKeyDescending)
+        OMERGE_CASE(kKeyF32 | kKeyDescending)
+        OMERGE_CASE(kKeyI64 | kKeyDescending)
+        OMERGE_CASE(kKeyU64 | kKeyDescending)
+        OMERGE_CASE(kKeyF64 | kKeyDescending)
+        default: return OMERGE_INVALID_ARG;
+    }
+#undef OMERGE_CASE
+}
+
+using PathI32 = Path<0, kKeyI32>;
+using PathKV = Path<1, kKeyI32>;
+
 }  // namespace
 }  // namespace omerge
 
@@ -286,41 +324,39 @@ extern "C" {
 
 int merge_i32(const int32_t* A, int64_t m, const int32_t* B, int64_t n,
               int32_t* C, hipStream_t stream) {
-    int rc = check_i32_args(A, m, B, n, C);
+    int rc = check_merge_args(A, nullptr, m, B, nullptr, n, C, nullptr, 4, 0);
     if (rc != OMERGE_OK) return rc;
-    return merge_full<false, kKeyI32>(A, nullptr, m, B, nullptr, n, C, nullptr, stream);
+    return PathI32::full(A, nullptr, m, B, nullptr, n, C, nullptr, stream);
 }
 
 int merge_kv(const int32_t* A_keys, const uint32_t* A_vals, int64_t m,
              const int32_t* B_keys, const uint32_t* B_vals, int64_t n,
              int32_t* C_keys, uint32_t* C_vals, hipStream_t stream) {
-    int rc = check_kv_args(A_keys, A_vals, m, B_keys, B_vals, n, C_keys, C_vals);
+    int rc = check_merge_args(A_keys, A_vals, m, B_keys, B_vals, n, C_keys, C_vals, 4, 4);
     if (rc != OMERGE_OK) return rc;
-    return merge_full<true, kKeyI32>(A_keys, A_vals, m, B_keys, B_vals, n, C_keys, C_vals,
-                                     stream);
+    return PathKV::full(A_keys, A_vals, m, B_keys, B_vals, n, C_keys, C_vals, stream);
 }
 
 int omerge_merge_keys(const void* A, int64_t m, const void* B, int64_t n, void* C,
                       int order, hipStream_t stream) {
     if (!valid_order(order)) return OMERGE_INVALID_ARG;
-    const int32_t* a = static_cast<const int32_t*>(A);
-    const int32_t* b = static_cast<const int32_t*>(B);
-    int32_t* c = static_cast<int32_t*>(C);
-    int rc = check_i32_args(a, m, b, n, c);
+    int rc = check_merge_args(A, nullptr, m, B, nullptr, n, C, nullptr, key_bytes(order), 0);
     if (rc != OMERGE_OK) return rc;
-    return merge_ordered<false>(a, nullptr, m, b, nullptr, n, c, nullptr, order, stream);
+    return merge_ordered<0>(order, A, nullptr, m, B, nullptr, n, C, nullptr, stream);
 }
 
-int omerge_merge_pairs(const void* A_keys, const uint32_t* A_vals, int64_t m,
-                       const void* B_keys, const uint32_t* B_vals, int64_t n, void* C_keys,
-                       uint32_t* C_vals, int order, hipStream_t stream) {
-    if (!valid_order(order)) return OMERGE_INVALID_ARG;
-    const int32_t* ak = static_cast<const int32_t*>(A_keys);
-    const int32_t* bk = static_cast<const int32_t*>(B_keys);
-    int32_t* ck = static_cast<int32_t*>(C_keys);
-    int rc = check_kv_args(ak, A_vals, m, bk, B_vals, n, ck, C_vals);
+int omerge_merge_pairs(const void* A_keys, const void* A_vals, int64_t m,
+                       const void* B_keys, const void* B_vals, int64_t n, void* C_keys,
+                       void* C_vals, int order, int payload_bytes, hipStream_t stream) {
+    if (!valid_order(order) || (payload_bytes != 4 && payload_bytes != 8))
+        return OMERGE_INVALID_ARG;
+    int rc = check_merge_args(A_keys, A_vals, m, B_keys, B_vals, n, C_keys, C_vals,
+                              key_bytes(order), payload_bytes);
     if (rc != OMERGE_OK) return rc;
-    return merge_ordered<true>(ak, A_vals, m, bk, B_vals, n, ck, C_vals, order, stream);
+    if (payload_bytes == 4)
+        return merge_ordered<1>(order, A_keys, A_vals, m, B_keys, B_vals, n, C_keys, C_vals,
+                                stream);
+    return merge_ordered<2>(order, A_keys, A_vals, m, B_keys, B_vals, n, C_keys, C_vals, stream);
 }
 
 int omerge_co_rank(const int32_t* A, int64_t m, const int32_t* B, int64_t n,
@@ -335,8 +371,8 @@ int omerge_co_rank(const int32_t* A, int64_t m, const int32_t* B, int64_t n,
         return OMERGE_INVALID_ARG;
     const int64_t blocks = ceil_div(count, kThreads);
     if (blocks > kMaxGridBlocks) return OMERGE_OVERFLOW;
-    hipLaunchKernelGGL(co_rank_kernel<kKeyI32>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
-                       0, stream, A, m, B, n, k, count, i_out);
+    hipLaunchKernelGGL(co_rank_kernel<kKeyI32>, dim3(static_cast<unsigned>(blocks)),
+                       dim3(kThreads), 0, stream, A, m, B, n, k, count, i_out);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? OMERGE_OK : hip_fail(e);
 }
@@ -344,8 +380,8 @@ int omerge_co_rank(const int32_t* A, int64_t m, const int32_t* B, int64_t n,
 int64_t omerge_segment_length(int64_t m, int64_t n, int kv) {
     if (check_sizes(m, n) != OMERGE_OK) return -1;
     int64_t seg_len = 0;
-    if (seg_len_for(m, n, kv != 0, &seg_len) != OMERGE_OK) return -1;
-    return seg_len;
+    const int rc = kv ? PathKV::seg_len(m, n, &seg_len) : PathI32::seg_len(m, n, &seg_len);
+    return rc == OMERGE_OK ? seg_len : -1;
 }
 
 int64_t omerge_partition_count(int64_t total, int64_t seg_len) {
@@ -361,18 +397,18 @@ int omerge_partition(const int32_t* A, int64_t m, const int32_t* B, int64_t n,
     rc = check_seg_len(seg_len);
     if (rc != OMERGE_OK) return rc;
     if (part == nullptr || (reinterpret_cast<uintptr_t>(part) & 7)) return OMERGE_INVALID_ARG;
-    return launch_partition<kKeyI32>(A, m, B, n, seg_len, part, stream);
+    return PathI32::partition(A, m, B, n, seg_len, part, stream);
 }
 
 int omerge_merge_segments_i32(const int32_t* A, int64_t m, const int32_t* B,
                               int64_t n, const int64_t* part, int64_t seg_len,
                               int32_t* C, hipStream_t stream) {
-    int rc = check_i32_args(A, m, B, n, C);
+    int rc = check_merge_args(A, nullptr, m, B, nullptr, n, C, nullptr, 4, 0);
     if (rc != OMERGE_OK) return rc;
     rc = check_part(part, m + n, seg_len);
     if (rc != OMERGE_OK) return rc;
     if (m + n == 0) return OMERGE_OK;
-    return launch_merge<false, kKeyI32>(A, nullptr, m, B, nullptr, n, part, seg_len, C, nullptr, stream);
+    return PathI32::merge(A, nullptr, m, B, nullptr, n, part, seg_len, C, nullptr, stream);
 }
 
 int omerge_merge_segments_kv(const int32_t* A_keys, const uint32_t* A_vals,
@@ -381,19 +417,19 @@ int omerge_merge_segments_kv(const int32_t* A_keys, const uint32_t* A_vals,
                              const int64_t* part, int64_t seg_len,
                              int32_t* C_keys, uint32_t* C_vals,
                              hipStream_t stream) {
-    int rc = check_kv_args(A_keys, A_vals, m, B_keys, B_vals, n, C_keys, C_vals);
+    int rc = check_merge_args(A_keys, A_vals, m, B_keys, B_vals, n, C_keys, C_vals, 4, 4);
     if (rc != OMERGE_OK) return rc;
     rc = check_part(part, m + n, seg_len);
     if (rc != OMERGE_OK) return rc;
     if (m + n == 0) return OMERGE_OK;
-    return launch_merge<true, kKeyI32>(A_keys, A_vals, m, B_keys, B_vals, n, part, seg_len, C_keys,
-                              C_vals, stream);
+    return PathKV::merge(A_keys, A_vals, m, B_keys, B_vals, n, part, seg_len, C_keys, C_vals,
+                         stream);
 }
 
 int omerge_merge_i32_direct(const int32_t* A, int64_t m, const int32_t* B, int64_t n,
                             int32_t* C, int64_t per_thread, int two_searches,
                             hipStream_t stream) {
-    int rc = check_i32_args(A, m, B, n, C);
+    int rc = check_merge_args(A, nullptr, m, B, nullptr, n, C, nullptr, 4, 0);
     if (rc != OMERGE_OK) return rc;
     if (per_thread < 1 || per_thread > (int64_t(1) << 30)) return OMERGE_INVALID_ARG;
     const int64_t total = m + n;

@@ -59,46 +59,81 @@ static void run_grid(int64_t blocks, int threads, const std::function<void()>& b
     g_barrier = nullptr;
 }
 
-template <int T, int I, bool KV, int ORDER>
-static void typed_cfg(const int32_t* A, const uint32_t* Av, int64_t m, const int32_t* B,
-                      const uint32_t* Bv, int64_t n, int64_t seg_len, int64_t* part, int32_t* C,
-                      uint32_t* Cv) {
+// Partition + merge for one key order, payload width VW (words) and shape.
+template <int T, int I, int VW, int ORDER>
+static void typed_cfg(const void* A, const void* Av, int64_t m, const void* B, const void* Bv,
+                      int64_t n, int64_t seg_len, int64_t* part, void* C, void* Cv) {
+    using Key = typename omerge::KeyOrder<ORDER>::T;
+    const Key* a = static_cast<const Key*>(A);
+    const Key* b = static_cast<const Key*>(B);
     const int64_t count = (m + n + seg_len - 1) / seg_len + 1;
     run_grid((count * 4 + 255) / 256, 256, [&] {
-        omerge::partition_kernel<4, ORDER>(A, m, B, n, seg_len, count, part);
+        omerge::partition_kernel<4, ORDER>(a, m, b, n, seg_len, count, part);
     });
     if (m + n == 0) return;
     run_grid(count - 1, T, [&] {
-        omerge::merge_segments_kernel<T, I, KV, ORDER>(A, Av, m, B, Bv, n, part, seg_len, C, Cv);
+        omerge::merge_segments_kernel<T, I, VW, ORDER>(
+            a, static_cast<const uint32_t*>(Av), m, b, static_cast<const uint32_t*>(Bv), n, part,
+            seg_len, static_cast<Key*>(C), static_cast<uint32_t*>(Cv));
     });
 }
 
-template <int ORDER>
-static void typed_order(int variant, int kv, const int32_t* A, const uint32_t* Av, int64_t m,
-                        const int32_t* B, const uint32_t* Bv, int64_t n, int64_t seg_len,
-                        int64_t* part, int32_t* C, uint32_t* Cv) {
-    if (variant == 0) {
-        if constexpr (ORDER == 6) {  // production shapes: float32 descending only
-            if (kv)
-                typed_cfg<256, 8, true, ORDER>(A, Av, m, B, Bv, n, seg_len, part, C, Cv);
-            else
-                typed_cfg<256, 16, false, ORDER>(A, Av, m, B, Bv, n, seg_len, part, C, Cv);
-        }
-        return;
-    }
-    if (kv)
-        typed_cfg<128, 4, true, ORDER>(A, Av, m, B, Bv, n, seg_len, part, C, Cv);
-    else
-        typed_cfg<128, 4, false, ORDER>(A, Av, m, B, Bv, n, seg_len, part, C, Cv);
+// Outputs per lane of the library's shapes (its items_for).
+constexpr int production_items(int kw, int vw) {
+    return kw == 1 && vw == 0 ? 16 : (kw + vw == 2 ? 8 : 4);
 }
 
-template <int T, int I, bool KV>
+// Which (order, payload words, shape) combinations this library holds:
+// small shapes (128 lanes, 4 items) for every order keys-only and for a
+// spread of orders with payloads; the library's shapes for float32 and
+// float64 descending with every payload width.
+constexpr bool emu_has(int variant, int order, int vw) {
+    if (variant == 0) return order == (2 | 8) || order == (5 | 8);
+    if (vw == 0) return true;
+    if (vw == 1) return order == 0 || order == (2 | 8) || order == 3 || order == (5 | 8);
+    return order == 1 || order == (3 | 8) || order == 5;
+}
+
+template <int ORDER, int VW>
+static bool typed_go(int variant, const void* A, const void* Av, int64_t m, const void* B,
+                     const void* Bv, int64_t n, int64_t seg_len, int64_t* part, void* C,
+                     void* Cv) {
+    if constexpr (emu_has(1, ORDER, VW)) {
+        if (variant == 1) {
+            typed_cfg<128, 4, VW, ORDER>(A, Av, m, B, Bv, n, seg_len, part, C, Cv);
+            return true;
+        }
+    }
+    if constexpr (emu_has(0, ORDER, VW)) {
+        if (variant == 0) {
+            constexpr int kw = omerge::KeyOrder<ORDER>::kWords;
+            typed_cfg<256, production_items(kw, VW), VW, ORDER>(A, Av, m, B, Bv, n, seg_len,
+                                                                 part, C, Cv);
+            return true;
+        }
+    }
+    return false;
+}
+
+template <int ORDER>
+static bool typed_order(int variant, int vw, const void* A, const void* Av, int64_t m,
+                        const void* B, const void* Bv, int64_t n, int64_t seg_len, int64_t* part,
+                        void* C, void* Cv) {
+    switch (vw) {
+        case 0: return typed_go<ORDER, 0>(variant, A, Av, m, B, Bv, n, seg_len, part, C, Cv);
+        case 1: return typed_go<ORDER, 1>(variant, A, Av, m, B, Bv, n, seg_len, part, C, Cv);
+        case 2: return typed_go<ORDER, 2>(variant, A, Av, m, B, Bv, n, seg_len, part, C, Cv);
+        default: return false;
+    }
+}
+
+template <int T, int I, int VW>
 static void merge_cfg(const int32_t* A, const uint32_t* Av, int64_t m, const int32_t* B,
                       const uint32_t* Bv, int64_t n, const int64_t* part, int64_t seg_len,
                       int32_t* C, uint32_t* Cv) {
     const int64_t segs = (m + n + seg_len - 1) / seg_len;
     run_grid(segs, T, [&] {
-        omerge::merge_segments_kernel<T, I, KV>(A, Av, m, B, Bv, n, part, seg_len, C, Cv);
+        omerge::merge_segments_kernel<T, I, VW, 0>(A, Av, m, B, Bv, n, part, seg_len, C, Cv);
     });
 }
 
@@ -107,9 +142,9 @@ extern "C" {
 // variant 0 = the shapes the library launches; 1 = small shapes (128 lanes,
 // 4 items) that wrap the rings many times on small inputs.
 int emu_tile(int variant, int kv) {
-    if (variant == 0) return kv ? omerge::MergeCfg<256, 8, true>::kTile
-                                : omerge::MergeCfg<256, 16, false>::kTile;
-    return omerge::MergeCfg<128, 4, false>::kTile;
+    if (variant == 0) return kv ? omerge::MergeCfg<256, 8, 1, 1>::kTile
+                                : omerge::MergeCfg<256, 16, 1, 0>::kTile;
+    return omerge::MergeCfg<128, 4, 1, 0>::kTile;
 }
 
 // lanes = lanes per boundary in the partition search (1, 4, 8, 16, 64).
@@ -144,34 +179,50 @@ void emu_direct(const int32_t* A, int64_t m, const int32_t* B, int64_t n, int32_
 void emu_merge_i32(int variant, const int32_t* A, int64_t m, const int32_t* B, int64_t n,
                    const int64_t* part, int64_t seg_len, int32_t* C) {
     if (variant == 0)
-        merge_cfg<256, 16, false>(A, nullptr, m, B, nullptr, n, part, seg_len, C, nullptr);
+        merge_cfg<256, 16, 0>(A, nullptr, m, B, nullptr, n, part, seg_len, C, nullptr);
     else
-        merge_cfg<128, 4, false>(A, nullptr, m, B, nullptr, n, part, seg_len, C, nullptr);
+        merge_cfg<128, 4, 0>(A, nullptr, m, B, nullptr, n, part, seg_len, C, nullptr);
 }
 
 void emu_merge_kv(int variant, const int32_t* A, const uint32_t* Av, int64_t m, const int32_t* B,
                   const uint32_t* Bv, int64_t n, const int64_t* part, int64_t seg_len, int32_t* C,
                   uint32_t* Cv) {
     if (variant == 0)
-        merge_cfg<256, 8, true>(A, Av, m, B, Bv, n, part, seg_len, C, Cv);
+        merge_cfg<256, 8, 1>(A, Av, m, B, Bv, n, part, seg_len, C, Cv);
     else
-        merge_cfg<128, 4, true>(A, Av, m, B, Bv, n, part, seg_len, C, Cv);
+        merge_cfg<128, 4, 1>(A, Av, m, B, Bv, n, part, seg_len, C, Cv);
 }
 
-// Partition and merge for a key order (kind | 4 if descending); variant 1 =
-// small shapes for every order, variant 0 = production shapes for order 6.
-void emu_merge_typed(int variant, int order, int kv, const int32_t* A, const uint32_t* Av,
-                     int64_t m, const int32_t* B, const uint32_t* Bv, int64_t n, int64_t seg_len,
-                     int64_t* part, int32_t* C, uint32_t* Cv) {
+// Partition and merge for a key order (kind | 8 if descending) and payload
+// width vw (32-bit words: 0, 1 or 2).  Returns 0 if this library does not
+// hold that combination (see emu_has).
+int emu_merge_typed(int variant, int order, int vw, const void* A, const void* Av, int64_t m,
+                    const void* B, const void* Bv, int64_t n, int64_t seg_len, int64_t* part,
+                    void* C, void* Cv) {
+#define EMU_ORDER(o) \
+    case o: return typed_order<o>(variant, vw, A, Av, m, B, Bv, n, seg_len, part, C, Cv);
     switch (order) {
-        case 0: typed_order<0>(variant, kv, A, Av, m, B, Bv, n, seg_len, part, C, Cv); break;
-        case 1: typed_order<1>(variant, kv, A, Av, m, B, Bv, n, seg_len, part, C, Cv); break;
-        case 2: typed_order<2>(variant, kv, A, Av, m, B, Bv, n, seg_len, part, C, Cv); break;
-        case 4: typed_order<4>(variant, kv, A, Av, m, B, Bv, n, seg_len, part, C, Cv); break;
-        case 5: typed_order<5>(variant, kv, A, Av, m, B, Bv, n, seg_len, part, C, Cv); break;
-        case 6: typed_order<6>(variant, kv, A, Av, m, B, Bv, n, seg_len, part, C, Cv); break;
-        default: break;
+        EMU_ORDER(0)
+        EMU_ORDER(1)
+        EMU_ORDER(2)
+        EMU_ORDER(3)
+        EMU_ORDER(4)
+        EMU_ORDER(5)
+        EMU_ORDER(8)
+        EMU_ORDER(9)
+        EMU_ORDER(10)
+        EMU_ORDER(11)
+        EMU_ORDER(12)
+        EMU_ORDER(13)
+        default: return 0;
     }
+#undef EMU_ORDER
+}
+
+// Tile size (outputs) of a typed shape.
+int emu_typed_tile(int variant, int order, int vw) {
+    const int kw = (order & 7) >= 3 ? 2 : 1;
+    return variant == 0 ? 256 * production_items(kw, vw) : 128 * 4;
 }
 
 }  // extern "C"

@@ -31,6 +31,9 @@ def load(path):
     lib.emu_merge_kv.argtypes = [i32, p, p, i64, p, p, i64, p, i64, p, p]
     lib.emu_direct.argtypes = [p, i64, p, i64, p, i64, i32]
     lib.emu_merge_typed.argtypes = [i32, i32, i32, p, p, i64, p, p, i64, i64, p, p, p]
+    lib.emu_merge_typed.restype = i32
+    lib.emu_typed_tile.argtypes = [i32, i32, i32]
+    lib.emu_typed_tile.restype = i32
     return lib
 
 
@@ -241,73 +244,107 @@ def group_direct(r, g):
                 r.check(np.array_equal(C, want), ("direct", m, n, per, two))
 
 
-def typed_sorted_pair(g, dtype, desc, m, n, pool_f32):
-    """Sorted A, B of one key type in the given direction.  Float keys are
-    drawn from pool_f32, a list already in IEEE totalOrder."""
+KIND_DTYPE = {0: np.int32, 1: np.uint32, 2: np.float32, 3: np.int64, 4: np.uint64,
+              5: np.float64}
+
+
+def float_pool(g, dtype):
+    """Special values (signed zeros, infinities, subnormals, NaNs of both
+    signs) and random bit patterns of a float dtype, sorted with the oracle's
+    totalOrder relation."""
+    import functools
     if dtype == np.float32:
-        ia = np.sort(g.integers(0, len(pool_f32), size=m))
-        ib = np.sort(g.integers(0, len(pool_f32), size=n))
-        A, B = pool_f32[ia], pool_f32[ib]
+        special = np.array([0xFFC00000, 0xFFFFFFFF, 0xFF800001, 0xFF800000, 0xFF7FFFFF,
+                            0xBF800000, 0x80000001, 0x80000000, 0x00000000, 0x00000001,
+                            0x3F800000, 0x7F7FFFFF, 0x7F800000, 0x7F800001, 0x7FC00000,
+                            0x7FFFFFFF], dtype=np.uint32)
+        rnd = g.integers(0, 1 << 32, size=80, dtype=np.uint64).astype(np.uint32)
+    else:
+        special = np.array([0xFFF8000000000000, 0xFFFFFFFFFFFFFFFF, 0xFFF0000000000001,
+                            0xFFF0000000000000, 0xFFEFFFFFFFFFFFFF, 0xBFF0000000000000,
+                            0x8000000000000001, 0x8000000000000000, 0x0000000000000000,
+                            0x0000000000000001, 0x3FF0000000000000, 0x3FF0000000000001,
+                            0x7FEFFFFFFFFFFFFF, 0x7FF0000000000000, 0x7FF0000000000001,
+                            0x7FF8000000000000, 0x7FFFFFFFFFFFFFFF], dtype=np.uint64)
+        rnd = g.integers(0, 1 << 64, size=80, dtype=np.uint64, endpoint=False)
+    vals = np.unique(np.concatenate([special, rnd])).view(dtype)
+
+    def cmp(x, y):
+        if not oracle.key_le(dtype, x, y):
+            return 1
+        return 0 if oracle.key_le(dtype, y, x) else -1
+    return np.array(sorted(vals.tolist(), key=functools.cmp_to_key(
+        lambda a, b: cmp(dtype(a), dtype(b)))), dtype=dtype)
+
+
+def typed_sorted_pair(g, dtype, desc, m, n, pools):
+    """Sorted A, B of one key type in the given direction.  Float keys are
+    drawn from pools[dtype], already in IEEE totalOrder."""
+    if dtype in (np.float32, np.float64):
+        pool = pools[dtype]
+        A = pool[np.sort(g.integers(0, len(pool), size=m))]
+        B = pool[np.sort(g.integers(0, len(pool), size=n))]
     else:
         info = np.iinfo(dtype)
-        span = int(g.choice([3, 1000, 1 << 32]))
-        lo = int(info.min) if span == 1 << 32 else int(g.integers(info.min, int(info.max) - span))
-        A = np.sort(g.integers(lo, lo + span, size=m)).astype(dtype)
-        B = np.sort(g.integers(lo, lo + span, size=n)).astype(dtype)
+        wide = np.dtype(dtype).itemsize == 8
+        span = int(g.choice([3, 1000, 1 << 40 if wide else 1 << 32]))
+        if span > 1000:
+            A = np.sort(g.integers(info.min, info.max, size=m, dtype=dtype, endpoint=True))
+            B = np.sort(g.integers(info.min, info.max, size=n, dtype=dtype, endpoint=True))
+        else:
+            lo = int(g.integers(info.min, int(info.max) - span, dtype=dtype))
+            A = np.sort(g.integers(lo, lo + span, size=m, dtype=dtype))
+            B = np.sort(g.integers(lo, lo + span, size=n, dtype=dtype))
     if desc:
         A, B = A[::-1], B[::-1]
     return np.ascontiguousarray(A), np.ascontiguousarray(B)
 
 
-def f32_pool(g):
-    """Special binary32 values and random ones, sorted by the oracle's
-    totalOrder relation."""
-    import functools
-    special = np.array([0xFFC00000, 0xFFFFFFFF, 0xFF800001, 0xFF800000, 0xFF7FFFFF, 0xBF800000,
-                        0x80000001, 0x80000000, 0x00000000, 0x00000001, 0x3F800000, 0x7F7FFFFF,
-                        0x7F800000, 0x7F800001, 0x7FC00000, 0x7FFFFFFF], dtype=np.uint32)
-    rnd = g.integers(0, 1 << 32, size=80, dtype=np.uint64).astype(np.uint32)
-    vals = np.unique(np.concatenate([special, rnd])).view(np.float32)
-    cmp = lambda x, y: -1 if not oracle.key_le(np.float32, y, x) else (
-        1 if not oracle.key_le(np.float32, x, y) else 0)
-    return np.array(sorted(vals.tolist(), key=functools.cmp_to_key(
-        lambda a, b: cmp(np.float32(a), np.float32(b)))), dtype=np.float32)
-
-
 def group_orders(r, g):
-    """Every key order (int32/uint32/float32, ascending/descending) through
-    the ordered partition and merge kernels, keys and pairs, against the
-    oracle; the partition against co-ranks read off the oracle's pair tags."""
-    pool = f32_pool(g)
-    tile = r.lib.emu_tile(1, 0)
-    plan = [(o, 1) for o in (0, 1, 2, 4, 5, 6) for _ in range(5)] + [(6, 0)] * 3
-    for c, (order, variant) in enumerate(plan):
-        dtype = {0: np.int32, 1: np.uint32, 2: np.float32}[order & 3]
-        desc = bool(order & 4)
-        big = r.lib.emu_tile(0, 0) if variant == 0 else tile
-        m, n = (int(x) for x in g.integers(0, 5 * big, size=2))
-        if c % 7 == 0:
-            m = 0
-        A, B = typed_sorted_pair(g, dtype, desc, m, n, pool)
-        Av = np.arange(m, dtype=np.uint32)
-        Bv = (U31 + np.arange(n, dtype=np.uint32)).astype(np.uint32)
-        wk, wv = oracle.merge_pairs(A, Av, B, Bv, desc)
-        from_a = np.concatenate([[0], np.cumsum(wv < U31)]).astype(np.int64)
-        for kv in (0, 1):
-            t = r.lib.emu_tile(variant, kv)
-            seg_len = int(g.choice([t, 3 * t, 4 * int(g.integers(1, 300))]))
+    """Every key order (int32/uint32/float32/int64/uint64/float64, ascending
+    and descending) and payload width the emulation library holds, through
+    the ordered partition and merge kernels, against the oracle; the
+    partition against co-ranks read off the oracle's payload tags."""
+    pools = {np.float32: float_pool(g, np.float32), np.float64: float_pool(g, np.float64)}
+    plan = []
+    for order in (0, 1, 2, 3, 4, 5, 8, 9, 10, 11, 12, 13):
+        for vw in (0, 1, 2):
+            for variant in (1, 0):
+                plan.append((order, vw, variant))
+    ran = 0
+    for c, (order, vw, variant) in enumerate(plan):
+        dtype = KIND_DTYPE[order & 7]
+        desc = bool(order & 8)
+        tile = r.lib.emu_typed_tile(variant, order, vw)
+        for rep in range(3 if variant == 1 else 1):
+            m, n = (int(x) for x in g.integers(0, 5 * tile, size=2))
+            if rep == 2:
+                m = 0
+            A, B = typed_sorted_pair(g, dtype, desc, m, n, pools)
+            vdt = np.uint64 if vw == 2 else np.uint32
+            top = vdt(1 << (63 if vw == 2 else 31))
+            Av = np.arange(m, dtype=vdt)
+            Bv = (top + np.arange(n, dtype=vdt)).astype(vdt)
+            wk, wv = oracle.merge_pairs(A, Av, B, Bv, desc)
+            from_a = np.concatenate([[0], np.cumsum(wv < top)]).astype(np.int64)
+            seg_len = int(g.choice([tile, 3 * tile, 4 * int(g.integers(1, 300))]))
             count = (m + n + seg_len - 1) // seg_len + 1
             part = np.full(count, -3, dtype=np.int64)
-            Ck = np.zeros(m + n, dtype=np.uint32)
-            Cv = np.zeros(m + n, dtype=np.uint32)
-            r.lib.emu_merge_typed(variant, order, kv, ptr(A), ptr(Av), m, ptr(B), ptr(Bv), n,
-                                  seg_len, ptr(part), ptr(Ck), ptr(Cv))
+            Ck = np.zeros(m + n, dtype=A.dtype)
+            Cv = np.zeros(m + n, dtype=vdt)
+            held = r.lib.emu_merge_typed(variant, order, vw, ptr(A), ptr(Av) if vw else None, m,
+                                         ptr(B), ptr(Bv) if vw else None, n, seg_len, ptr(part),
+                                         ptr(Ck), ptr(Cv) if vw else None)
+            if not held:
+                break
+            ran += 1
             ks = np.minimum(np.arange(count, dtype=np.int64) * seg_len, m + n)
-            r.check(np.array_equal(part, from_a[ks]), ("typed partition", order, kv, m, n, seg_len))
-            ok = np.array_equal(Ck, wk.view(np.uint32))
-            if kv:
+            r.check(np.array_equal(part, from_a[ks]), ("typed partition", order, vw, m, n, seg_len))
+            ok = np.array_equal(Ck.view(np.uint8), wk.view(np.uint8))
+            if vw:
                 ok = ok and np.array_equal(Cv, wv)
-            r.check(ok, ("typed merge", order, variant, kv, m, n, seg_len))
+            r.check(ok, ("typed merge", order, vw, variant, m, n, seg_len))
+    r.check(ran >= 40, ("typed combinations run", ran))
 
 
 GROUPS = {"orders": group_orders, "small": group_small, "direct": group_direct, "skew": group_skew, "blocks": group_blocks,

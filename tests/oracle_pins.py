@@ -436,6 +436,163 @@ def pin_typed_i32_worked_example(orc) -> None:
     assert Ck.tolist() == [12, 10, 10, 10, 9, 8, 7, 7, 1]
 
 
+# binary64 (sign bit, 11 exponent bits, 52 fraction bits whose top bit marks
+# a quiet NaN), in increasing totalOrder by the same rules, written out by
+# hand.
+F64_TOTAL_ORDER = [
+    (0xFFFFFFFFFFFFFFFF, "-qNaN, largest payload"),
+    (0xFFF8000000000001, "-qNaN, payload 1"),
+    (0xFFF8000000000000, "-qNaN, payload 0"),
+    (0xFFF7FFFFFFFFFFFF, "-sNaN, largest payload"),
+    (0xFFF0000000000001, "-sNaN, payload 1"),
+    (0xFFF0000000000000, "-infinity"),
+    (0xFFEFFFFFFFFFFFFF, "-largest finite"),
+    (0xC000000000000000, "-2.0"),
+    (0xBFF0000000000001, "-(1.0 + 2^-52)"),
+    (0xBFF0000000000000, "-1.0"),
+    (0xBFEFFFFFFFFFFFFF, "-(1.0 - 2^-53)"),
+    (0x8010000000000000, "-smallest normal (-2^-1022)"),
+    (0x800FFFFFFFFFFFFF, "-largest subnormal"),
+    (0x8000000000000001, "-smallest subnormal (-2^-1074)"),
+    (0x8000000000000000, "-0.0"),
+    (0x0000000000000000, "+0.0"),
+    (0x0000000000000001, "+smallest subnormal (2^-1074)"),
+    (0x000FFFFFFFFFFFFF, "+largest subnormal"),
+    (0x0010000000000000, "+smallest normal (2^-1022)"),
+    (0x3FEFFFFFFFFFFFFF, "1.0 - 2^-53"),
+    (0x3FF0000000000000, "1.0"),
+    (0x3FF0000000000001, "1.0 + 2^-52"),
+    (0x4000000000000000, "2.0"),
+    (0x7FEFFFFFFFFFFFFF, "largest finite"),
+    (0x7FF0000000000000, "+infinity"),
+    (0x7FF0000000000001, "+sNaN, payload 1"),
+    (0x7FF7FFFFFFFFFFFF, "+sNaN, largest payload"),
+    (0x7FF8000000000000, "+qNaN, payload 0"),
+    (0x7FF8000000000001, "+qNaN, payload 1"),
+    (0x7FFFFFFFFFFFFFFF, "+qNaN, largest payload"),
+]
+
+
+def f64_bits(bits) -> np.ndarray:
+    return np.asarray(bits, dtype=np.uint64).view(np.float64)
+
+
+def tags64(m: int, n: int):
+    """64-bit payload tags: A element i -> i, B element j -> 2^63 + j."""
+    return (np.arange(m, dtype=np.uint64),
+            (np.uint64(1 << 63) + np.arange(n, dtype=np.uint64)).astype(np.uint64))
+
+
+def pin_f64_total_order_table(orc) -> None:
+    bits = [b for b, _ in F64_TOTAL_ORDER]
+    vals = f64_bits(bits)
+    for a in range(len(bits)):
+        for b in range(len(bits)):
+            assert orc.key_le(np.float64, vals[a], vals[b]) == (a <= b), \
+                (F64_TOTAL_ORDER[a][1], F64_TOTAL_ORDER[b][1])
+            assert orc.key_le(np.float64, vals[a], vals[b], descending=True) == (a >= b)
+
+
+def _check_typed64(orc, A, B, rank, descending) -> None:
+    """As _check_typed, with 64-bit payload tags as well as 32-bit ones."""
+    _check_typed(orc, A, B, rank, descending)
+    want = _stable_by(rank, A, B)
+    Av, Bv = tags64(A.size, B.size)
+    Ck, Cv = orc.merge_pairs(A, Av, B, Bv, descending)
+    assert Cv.dtype == np.uint64
+    want_tags = [(i if side == 0 else (1 << 63) + i) for _, side, i in want]
+    assert np.array_equal(Cv, np.array(want_tags, dtype=np.uint64))
+    assert np.array_equal(Ck.view(np.uint8), orc.merge_keys(A, B, descending).view(np.uint8))
+
+
+def pin_f64_special_brute(orc, seed: int = 53, cases: int = 200) -> None:
+    g = np.random.Generator(np.random.PCG64(seed))
+    bits = np.array([b for b, _ in F64_TOTAL_ORDER], dtype=np.uint64)
+    pos = {int(b): r for r, b in enumerate(bits)}
+    for c in range(cases):
+        m, n = (int(x) for x in g.integers(0, 12, size=2))
+        desc = bool(c & 1)
+        ia = np.sort(g.integers(0, len(bits), size=m))
+        ib = np.sort(g.integers(0, len(bits), size=n))
+        if desc:
+            ia, ib = ia[::-1], ib[::-1]
+        A, B = f64_bits(bits[ia]), f64_bits(bits[ib])
+        key = lambda x: pos[int(np.float64(x).view(np.uint64))]
+        rank = (lambda x: -key(x)) if desc else key
+        _check_typed64(orc, A, B, rank, desc)
+
+
+def pin_f64_numpy_finite(orc, seed: int = 59, cases: int = 30) -> None:
+    """Finite binary64 keys, zeros of one sign only, against numpy's stable
+    sort (descending: of the negated keys)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    for c in range(cases):
+        m, n = (int(x) for x in g.integers(0, 2000, size=2))
+        desc = bool(c & 1)
+        scale = float(g.choice([1.0, 1e-300, 1e300]))
+        pool = g.standard_normal(64) * scale
+        pool[pool == 0] = 0.0
+        A = np.sort(g.choice(pool, size=m))
+        B = np.sort(g.choice(pool, size=n))
+        if desc:
+            A, B = A[::-1].copy(), B[::-1].copy()
+        cat = np.concatenate([A, B])
+        order = np.argsort(-cat if desc else cat, kind="stable")
+        assert np.array_equal(orc.merge_keys(A, B, desc), cat[order])
+
+
+def pin_integer64_kinds_brute(orc, seed: int = 61, cases: int = 200) -> None:
+    """int64 and uint64 keys, both orders, including the type extremes and
+    keys that differ only in their high or only in their low 32 bits."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    for c in range(cases):
+        dtype = np.uint64 if c % 4 < 2 else np.int64
+        desc = bool(c & 1)
+        info = np.iinfo(dtype)
+        lo, hi = int(info.min), int(info.max)
+        pool = [lo, lo + 1, 0, 1, (1 << 32) - 1, 1 << 32, (1 << 32) + 1, hi - 1, hi,
+                (1 << 31) - 1, 1 << 31]
+        if dtype == np.int64:
+            pool += [-1, -(1 << 32), -(1 << 32) + 1, -(1 << 31)]
+        else:
+            pool += [1 << 63, (1 << 63) + 1, (1 << 63) - 1]
+        pool += [int(x) for x in g.integers(lo, hi, size=4, dtype=dtype, endpoint=True)]
+        pool = sorted(set(pool))
+        m, n = (int(x) for x in g.integers(0, 14, size=2))
+        A = np.array(sorted(int(pool[i]) for i in g.integers(0, len(pool), size=m)),
+                     dtype=dtype)
+        B = np.array(sorted(int(pool[i]) for i in g.integers(0, len(pool), size=n)),
+                     dtype=dtype)
+        if desc:
+            A, B = A[::-1].copy(), B[::-1].copy()
+        rank = (lambda x: -int(x)) if desc else (lambda x: int(x))
+        _check_typed64(orc, A, B, rank, desc)
+
+
+def pin_integer64_kinds_sorted(orc, seed: int = 67, cases: int = 16) -> None:
+    """Larger int64 / uint64 cases against Python's stable sort of the
+    concatenation by integer value (descending: by its negation)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    for c in range(cases):
+        dtype = np.uint64 if c % 4 < 2 else np.int64
+        desc = bool(c & 1)
+        info = np.iinfo(dtype)
+        m, n = (int(x) for x in g.integers(0, 3000, size=2))
+        if c % 8 < 4:
+            draw = lambda k: g.integers(info.min, info.max, size=k, dtype=dtype, endpoint=True)
+        else:
+            base = int(g.integers(0, 1 << 20)) << 32
+            draw = lambda k: (np.uint64(base) + g.integers(0, 8, size=k).astype(np.uint64)
+                              ).astype(dtype)
+        A, B = np.sort(draw(m)), np.sort(draw(n))
+        if desc:
+            A, B = A[::-1].copy(), B[::-1].copy()
+        cat = [int(x) for x in np.concatenate([A, B])]
+        order = sorted(range(len(cat)), key=(lambda t: -cat[t]) if desc else (lambda t: cat[t]))
+        want = np.array([cat[t] for t in order], dtype=dtype)
+        assert np.array_equal(orc.merge_keys(A, B, desc), want)
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_equal_element_case,
@@ -452,6 +609,11 @@ ALL_PINS = [
     pin_integer_kinds_brute,
     pin_integer_kinds_numpy,
     pin_typed_i32_worked_example,
+    pin_f64_total_order_table,
+    pin_f64_special_brute,
+    pin_f64_numpy_finite,
+    pin_integer64_kinds_brute,
+    pin_integer64_kinds_sorted,
 ]
 
 

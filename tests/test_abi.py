@@ -109,37 +109,61 @@ def test_merge_kv_validation():
 
 
 def test_typed_entry_validation():
-    """Order codes outside {0,1,2,4,5,6} are rejected; the typed entries apply
-    the same pointer checks as merge_i32 / merge_kv."""
+    """Order codes outside the six kinds (optionally | 8) and payload widths
+    other than 4 and 8 are rejected; the typed entries apply the same pointer,
+    alignment and overlap checks as merge_i32 / merge_kv."""
     lib = om.load_library()
     a, av, b, bv = FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000
     ck, cv = FAKE + 0x4000, FAKE + 0x5000
-    for bad in (3, 7, 8, -1, 1 << 20):
+    good = (0, 1, 2, 3, 4, 5, 8, 9, 10, 11, 12, 13)
+    for bad in (6, 7, 14, 15, 16, -1, 1 << 20):
         assert lib.omerge_merge_keys(P(a), 4, P(b), 4, P(ck), bad, P(0)) == M.INVALID_ARG
-        assert lib.omerge_merge_pairs(P(a), P(av), 4, P(b), P(bv), 4, P(ck), P(cv), bad,
+        assert lib.omerge_merge_pairs(P(a), P(av), 4, P(b), P(bv), 4, P(ck), P(cv), bad, 4,
                                       P(0)) == M.INVALID_ARG
-    for order in (0, 1, 2, 4, 5, 6):
+    for vb in (0, 2, 16, -4):
+        assert lib.omerge_merge_pairs(P(a), P(av), 4, P(b), P(bv), 4, P(ck), P(cv), 0, vb,
+                                      P(0)) == M.INVALID_ARG
+    for order in good:
+        wide = (order & 7) >= 3
         assert lib.omerge_merge_keys(P(a), 4, P(b), 4, P(a + 8), order, P(0)) == M.INVALID_ARG
         assert lib.omerge_merge_keys(P(0), 0, P(0), 0, P(0), order, P(0)) == M.OK
-        assert lib.omerge_merge_pairs(P(a), P(av), 4, P(b), P(bv), 4, P(ck), P(ck + 4), order,
-                                      P(0)) == M.INVALID_ARG
-        assert lib.omerge_merge_pairs(P(0), P(0), 0, P(0), P(0), 0, P(0), P(0), order,
-                                      P(0)) == M.OK
-    assert (M.KEY_I32, M.KEY_U32, M.KEY_F32, M.DESCENDING) == (0, 1, 2, 4)
+        # 64-bit keys must be 8-byte aligned; 32-bit keys need 4 bytes only
+        rc = lib.omerge_merge_keys(P(a + 4), 0, P(b), 0, P(ck + 4), order, P(0))
+        assert rc == M.OK  # empty: no pointer is used
+        for vb in (4, 8):
+            assert lib.omerge_merge_pairs(P(a), P(av), 4, P(b), P(bv), 4, P(ck), P(ck + 4),
+                                          order, vb, P(0)) == M.INVALID_ARG
+            assert lib.omerge_merge_pairs(P(0), P(0), 0, P(0), P(0), 0, P(0), P(0), order, vb,
+                                          P(0)) == M.OK
+            if vb == 8:  # misaligned 64-bit payload
+                assert lib.omerge_merge_pairs(P(a), P(av + 4), 4, P(b), P(bv), 4, P(ck), P(cv),
+                                              order, vb, P(0)) == M.INVALID_ARG
+        if wide:  # misaligned 64-bit key
+            assert lib.omerge_merge_keys(P(a + 4), 4, P(b), 4, P(ck), order, P(0)) == \
+                M.INVALID_ARG
+            # C of 8-byte keys reaching into A's bytes
+            assert lib.omerge_merge_keys(P(a), 4, P(b), 4, P(a + 24), order, P(0)) == \
+                M.INVALID_ARG
+    assert (M.KEY_I32, M.KEY_U32, M.KEY_F32, M.KEY_I64, M.KEY_U64, M.KEY_F64,
+            M.DESCENDING) == (0, 1, 2, 3, 4, 5, 8)
     text = open(HEADER).read()
-    for name, v in (("OMERGE_KEY_I32", 0), ("OMERGE_KEY_U32", 1), ("OMERGE_KEY_F32", 2)):
-        assert re.search(r"\b%s = %d\b" % (name, v), text), name
-    assert re.search(r"#define OMERGE_DESCENDING 4\b", text)
+    for i, name in enumerate(("I32", "U32", "F32", "I64", "U64", "F64")):
+        assert re.search(r"\bOMERGE_KEY_%s = %d\b" % (name, i), text), name
+    assert re.search(r"#define OMERGE_DESCENDING 8\b", text)
 
 
 def test_order_code_of_dtypes():
     import torch
     assert om.order_code(torch.int32) == 0
-    assert om.order_code(torch.float32, descending=True) == 6
+    assert om.order_code(torch.float32, descending=True) == 10
+    assert om.order_code(torch.int64) == 3
+    assert om.order_code(torch.float64, descending=True) == 13
     if hasattr(torch, "uint32"):
         assert om.order_code(torch.uint32) == 1
+    if hasattr(torch, "uint64"):
+        assert om.order_code(torch.uint64, descending=True) == 12
     with pytest.raises(TypeError):
-        om.order_code(torch.int64)
+        om.order_code(torch.int16)
 
 
 def test_stage_validation():

@@ -270,89 +270,149 @@ def test_unsorted_input_returns():
 
 # ------------------------------------------------------ key types and orders
 
-TYPED = [(np.int32, False), (np.int32, True), (np.uint32, False), (np.uint32, True),
-         (np.float32, False), (np.float32, True)]
+KEY_DTYPES = [np.int32, np.uint32, np.float32, np.int64, np.uint64, np.float64]
+TYPED = [(d, r) for d in KEY_DTYPES for r in (False, True)]
 TYPED_IDS = ["%s-%s" % (np.dtype(d).name, "desc" if r else "asc") for d, r in TYPED]
+_TORCH = {np.dtype(np.int32): torch.int32, np.dtype(np.uint32): getattr(torch, "uint32", None),
+          np.dtype(np.float32): torch.float32, np.dtype(np.int64): torch.int64,
+          np.dtype(np.uint64): getattr(torch, "uint64", None),
+          np.dtype(np.float64): torch.float64}
 
 
 def dev_typed(x, off=0):
-    """Keys of any 32-bit dtype to a device tensor of the matching torch dtype
-    (moved as int32 bits)."""
-    tdt = {np.dtype(np.int32): torch.int32, np.dtype(np.uint32): torch.uint32,
-           np.dtype(np.float32): torch.float32}[x.dtype]
-    return dev(np.ascontiguousarray(x).view(np.int32), off).view(tdt)
+    """Keys or payloads of any 4- or 8-byte dtype to a device tensor of the
+    matching torch dtype (moved as signed-integer bits of the same width)."""
+    x = np.ascontiguousarray(x)
+    tdt = _TORCH[x.dtype]
+    bits = np.int32 if x.dtype.itemsize == 4 else np.int64
+    t = torch.from_numpy(x.view(bits))
+    if off:
+        big = torch.empty(x.size + off, dtype=t.dtype, device=DEV)
+        big[off:] = t.to(DEV)
+        t = big[off:]
+    else:
+        t = t.to(DEV)
+    return t.view(tdt)
 
 
 def host_bits(t):
-    return t.view(torch.int32).cpu().numpy().view(np.uint32)
+    bits = torch.int32 if t.element_size() == 4 else torch.int64
+    ubits = np.uint32 if t.element_size() == 4 else np.uint64
+    return t.view(bits).cpu().numpy().view(ubits)
 
 
-_F32_POOL = None
+def as_bits(x):
+    return np.ascontiguousarray(x).view(np.uint32 if x.dtype.itemsize == 4 else np.uint64)
 
 
-def f32_pool():
-    """About 2000 distinct binary32 values, signed zeros, infinities,
+_FLOAT_POOLS = {}
+
+
+def float_pool(dtype):
+    """About 2000 distinct values of a float dtype, signed zeros, infinities,
     subnormals and NaNs of both signs among them, sorted with the oracle's
     totalOrder relation."""
-    global _F32_POOL
-    if _F32_POOL is None:
+    if dtype not in _FLOAT_POOLS:
         import functools
         g = np.random.Generator(np.random.PCG64(77))
-        special = np.array([0xFFC00000, 0xFFFFFFFF, 0xFF800001, 0xFF800000, 0xFF7FFFFF,
-                            0x80800000, 0x80000001, 0x80000000, 0x00000000, 0x00000001,
-                            0x00800000, 0x7F7FFFFF, 0x7F800000, 0x7F800001, 0x7FC00000,
-                            0x7FFFFFFF], dtype=np.uint32)
-        finite = (g.standard_normal(1500) * 1e3).astype(np.float32).view(np.uint32)
-        anybits = g.integers(0, 1 << 32, size=500, dtype=np.uint64).astype(np.uint32)
-        vals = np.unique(np.concatenate([special, finite, anybits])).view(np.float32)
+        if dtype == np.float32:
+            special = np.array([0xFFC00000, 0xFFFFFFFF, 0xFF800001, 0xFF800000, 0xFF7FFFFF,
+                                0x80800000, 0x80000001, 0x80000000, 0x00000000, 0x00000001,
+                                0x00800000, 0x7F7FFFFF, 0x7F800000, 0x7F800001, 0x7FC00000,
+                                0x7FFFFFFF], dtype=np.uint32)
+            anybits = g.integers(0, 1 << 32, size=500, dtype=np.uint64).astype(np.uint32)
+        else:
+            special = np.array([0xFFF8000000000000, 0xFFFFFFFFFFFFFFFF, 0xFFF0000000000001,
+                                0xFFF0000000000000, 0xFFEFFFFFFFFFFFFF, 0x8010000000000000,
+                                0x8000000000000001, 0x8000000000000000, 0x0000000000000000,
+                                0x0000000000000001, 0x0010000000000000, 0x7FEFFFFFFFFFFFFF,
+                                0x7FF0000000000000, 0x7FF0000000000001, 0x7FF8000000000000,
+                                0x7FFFFFFFFFFFFFFF], dtype=np.uint64)
+            anybits = g.integers(0, 1 << 64, size=500, dtype=np.uint64)
+        ubits = special.dtype.type
+        finite = (g.standard_normal(1500) * 1e3).astype(dtype).view(ubits)
+        vals = np.unique(np.concatenate([special, finite, anybits.astype(ubits)])).view(dtype)
 
         def cmp(x, y):
-            if not oracle.key_le(np.float32, x, y):
+            if not oracle.key_le(dtype, x, y):
                 return 1
-            return 0 if oracle.key_le(np.float32, y, x) else -1
-        _F32_POOL = np.array(sorted(vals.tolist(), key=functools.cmp_to_key(
-            lambda a, b: cmp(np.float32(a), np.float32(b)))), dtype=np.float32)
-    return _F32_POOL
+            return 0 if oracle.key_le(dtype, y, x) else -1
+        _FLOAT_POOLS[dtype] = np.array(sorted(vals.tolist(), key=functools.cmp_to_key(
+            lambda a, b: cmp(dtype(a), dtype(b)))), dtype=dtype)
+    return _FLOAT_POOLS[dtype]
 
 
 def typed_pair(g, dtype, desc, m, n):
-    if dtype == np.float32:
-        pool = f32_pool()
+    if dtype in (np.float32, np.float64):
+        pool = float_pool(dtype)
         A = pool[np.sort(g.integers(0, pool.size, size=m))]
         B = pool[np.sort(g.integers(0, pool.size, size=n))]
     else:
         info = np.iinfo(dtype)
-        span = int(g.choice([3, 5000, 1 << 32]))
-        lo = int(info.min) if span == 1 << 32 else int(g.integers(info.min, int(info.max) - span))
-        A = np.sort(g.integers(lo, lo + span, size=m)).astype(dtype)
-        B = np.sort(g.integers(lo, lo + span, size=n)).astype(dtype)
+        span = int(g.choice([3, 5000, 0]))
+        if span == 0:  # the whole range of the type
+            A = np.sort(g.integers(info.min, info.max, size=m, dtype=dtype, endpoint=True))
+            B = np.sort(g.integers(info.min, info.max, size=n, dtype=dtype, endpoint=True))
+        else:
+            lo = int(g.integers(info.min, int(info.max) - span, dtype=dtype))
+            A = np.sort(g.integers(lo, lo + span, size=m, dtype=dtype))
+            B = np.sort(g.integers(lo, lo + span, size=n, dtype=dtype))
     if desc:
         A, B = A[::-1], B[::-1]
     return np.ascontiguousarray(A), np.ascontiguousarray(B)
 
 
+def tags64(m, n):
+    return (np.arange(m, dtype=np.uint64),
+            (np.uint64(1 << 63) + np.arange(n, dtype=np.uint64)).astype(np.uint64))
+
+
+def needs_torch_dtype(dtype):
+    if _TORCH[np.dtype(dtype)] is None:
+        pytest.skip("this torch has no %s dtype" % np.dtype(dtype).name)
+
+
 @pytest.mark.parametrize("dtype,desc", TYPED, ids=TYPED_IDS)
 def test_typed_keys_and_pairs(dtype, desc):
-    """Every key type and direction, keys and pairs, several tiles plus a
-    ragged tail, every pointer phase; output bits against the oracle."""
+    """Every key type and direction, keys only and with 4- and 8-byte
+    payloads, several tiles plus a ragged tail, several pointer phases;
+    output bits against the oracle."""
+    needs_torch_dtype(dtype)
     g = np.random.Generator(np.random.PCG64(500 + TYPED.index((dtype, desc))))
+    wide = np.dtype(dtype).itemsize == 8
     for c in range(4):
         m, n = (int(x) for x in g.integers(0, 60000, size=2))
         if c == 3:
             m = 0
         A, B = typed_pair(g, dtype, desc, m, n)
+        # offsets in elements: 64-bit arrays keep their 8-byte alignment
         offs = [int(x) for x in g.integers(0, 4, size=6)]
         say("typed", np.dtype(dtype).name, desc, m, n, offs)
         got = om.merge(dev_typed(A, offs[0]), dev_typed(B, offs[1]), descending=desc)
-        assert got.dtype == dev_typed(A[:0]).dtype
+        assert got.dtype == _TORCH[np.dtype(dtype)]
         want = oracle.merge_keys(A, B, desc)
-        assert_same(host_bits(got), want.view(np.uint32), "typed keys")
-        Av, Bv = tags(m, n)
-        gk, gv = om.merge_pairs(dev_typed(A, offs[2]), dev(Av, offs[3]), dev_typed(B, offs[4]),
-                                dev(Bv, offs[5]), descending=desc)
-        wk, wv = oracle.merge_pairs(A, Av, B, Bv, desc)
-        assert_same(host_bits(gk), wk.view(np.uint32), "typed pair keys")
-        assert_same(host(gv).view(np.uint32), wv, "typed pair payloads")
+        assert_same(host_bits(got), as_bits(want), "typed keys")
+        for tagger in (tags, tags64):
+            Av, Bv = tagger(m, n)
+            if tagger is tags64 and _TORCH[np.dtype(np.uint64)] is None:
+                Av, Bv = Av.view(np.int64), Bv.view(np.int64)
+            gk, gv = om.merge_pairs(dev_typed(A, offs[2]), dev_typed(Av, offs[3]),
+                                    dev_typed(B, offs[4]), dev_typed(Bv, offs[5]),
+                                    descending=desc)
+            wk, wv = oracle.merge_pairs(A, Av, B, Bv, desc)
+            what = "typed pair (%d-byte payloads)" % Av.dtype.itemsize
+            assert_same(host_bits(gk), as_bits(wk), what + " keys")
+            assert_same(host_bits(gv), as_bits(wv), what + " payloads")
+        if wide and dtype != np.float64:
+            # one shared high word: keys differ in the low 32 bits only
+            hi = -(5 << 32) if (dtype == np.int64 and c % 2) else (3 << 32)
+            vals = (np.int64(hi) + g.integers(0, 1 << 32, size=4000)).astype(dtype)
+            A2, B2 = np.sort(g.choice(vals, 2500)), np.sort(g.choice(vals, 1500))
+            if desc:
+                A2, B2 = A2[::-1].copy(), B2[::-1].copy()
+            got = om.merge(dev_typed(A2), dev_typed(B2), descending=desc)
+            assert_same(host_bits(got), as_bits(oracle.merge_keys(A2, B2, desc)),
+                        "low-word keys")
 
 
 def test_i32_order_code_is_merge_i32():
@@ -361,21 +421,30 @@ def test_i32_order_code_is_merge_i32():
     assert_same(host(om.merge(dev(A), dev(B))), host(om.merge_i32(dev(A), dev(B))), "i32 order 0")
 
 
-@pytest.mark.parametrize("dtype,desc", [(np.float32, True), (np.uint32, False)],
-                         ids=["float32-desc", "uint32-asc"])
+@pytest.mark.parametrize("dtype,desc", [(np.float32, True), (np.uint32, False),
+                                        (np.int64, False), (np.float64, True)],
+                         ids=["float32-desc", "uint32-asc", "int64-asc", "float64-desc"])
 def test_typed_large(dtype, desc):
-    """2^24 + 2^24 keys and pairs (8192 tiles) of a non-int32 order."""
+    """2^24 + 2^24 keys, and pairs with 4- and 8-byte payloads, of orders
+    other than int32 ascending (thousands of tiles)."""
+    needs_torch_dtype(dtype)
     g = np.random.Generator(np.random.PCG64(613))
     m = n = 1 << 24
     A, B = typed_pair(g, dtype, desc, m, n)
     say("typed large", np.dtype(dtype).name, desc)
     got = om.merge(dev_typed(A), dev_typed(B), descending=desc)
-    assert_same(host_bits(got), oracle.merge_keys(A, B, desc).view(np.uint32), "typed large")
-    Av, Bv = tags(m, n)
-    gk, gv = om.merge_pairs(dev_typed(A), dev(Av), dev_typed(B), dev(Bv), descending=desc)
-    wk, wv = oracle.merge_pairs(A, Av, B, Bv, desc)
-    assert_same(host_bits(gk), wk.view(np.uint32), "typed large pair keys")
-    assert_same(host(gv).view(np.uint32), wv, "typed large pair payloads")
+    assert_same(host_bits(got), as_bits(oracle.merge_keys(A, B, desc)), "typed large")
+    del got
+    for tagger in (tags, tags64):
+        Av, Bv = tagger(m, n)
+        if tagger is tags64 and _TORCH[np.dtype(np.uint64)] is None:
+            Av, Bv = Av.view(np.int64), Bv.view(np.int64)
+        gk, gv = om.merge_pairs(dev_typed(A), dev_typed(Av), dev_typed(B), dev_typed(Bv),
+                                descending=desc)
+        wk, wv = oracle.merge_pairs(A, Av, B, Bv, desc)
+        assert_same(host_bits(gk), as_bits(wk), "typed large pair keys")
+        assert_same(host_bits(gv), as_bits(wv), "typed large pair payloads")
+        del gk, gv
 
 
 # ------------------------------------------------------- full-size workloads

@@ -37,17 +37,29 @@ MUTANTS = {
     "neg_nan_payload_ascending": ("x_neg ? x_frac >= y_frac", "x_neg ? x_frac <= y_frac"),
     "nan_payload_ignored": ("return x_neg ? x_frac >= y_frac : x_frac <= y_frac;",
                             "return x_frac + y_frac + 1u > 0u;"),
-    "float_as_signed_int": ("        return total_order_f32(x, y);",
-                            "        return total_order_f32(x, x) && (int32_t)x <= (int32_t)y;"),
+    "float_as_signed_int": ("        return total_order_f32((uint32_t)x, (uint32_t)y);",
+                            "        return total_order_f32((uint32_t)x, (uint32_t)x) && "
+                            "(int32_t)(uint32_t)x <= (int32_t)(uint32_t)y;"),
     "u32_as_signed": ("        return x <= y;", "        return (int32_t)x <= (int32_t)y;"),
     "descending_ties_b_first": ("return le_ascending(kind, y, x);",
                                 "return !le_ascending(kind, x, y);"),
     "descending_not_reversed": ("return le_ascending(kind, y, x);",
                                 "return le_ascending(kind, x, y);"),
+    "i64_as_unsigned": ("        return (int64_t)x <= (int64_t)y;", "        return x <= y;"),
+    "u64_low_word_only": ("    case KIND_U64:\n        return x <= y;",
+                          "    case KIND_U64:\n        return (uint32_t)x <= (uint32_t)y;"),
+    "f64_zeros_equal": ("        if (x == 0.0)\n            return x_neg >= y_neg;",
+                        "        if (x == 0.0)\n            return x_neg >= 0;"),
+    "f64_nan_payload_reversed": ("        return x_neg ? x_frac >= y_frac : x_frac <= y_frac;\n    }\n    if (x_nan)\n        return x_neg;\n    return !y_neg;\n}\n\n/* Ascending",
+                                 "        return x_neg ? x_frac <= y_frac : x_frac <= y_frac;\n    }\n    if (x_nan)\n        return x_neg;\n    return !y_neg;\n}\n\n/* Ascending"),
+    "f64_as_f32": ("        return total_order_f64(x, y);",
+                   "        return total_order_f64(x, x) && total_order_f32((uint32_t)(x >> 32), (uint32_t)(y >> 32));"),
+    "key_size_64_for_f64_only": ("return kind >= KIND_I64 ? 8 : 4;", "return kind >= KIND_F64 ? 8 : 4;"),
+    "payload_half_copied": ("memcpy(cv + vs * k, av + vs * i, vs);", "memcpy(cv + vs * k, av + vs * i, 4);"),
     "typed_b_exhaustion_dropped": ("    if (j >= n)\n        return 1;\n    if (i < m && oracle_key_le",
                                    "    if (i < m && oracle_key_le"),
-    "typed_payload_from_b": ("            Cv[k] = Av[i];\n            ++i;\n        } else {\n            Ck[k] = Bk[j];",
-                             "            Cv[k] = Bv[j < n ? j : 0];\n            ++i;\n        } else {\n            Ck[k] = Bk[j];"),
+    "typed_payload_from_b": ("memcpy(cv + vs * k, av + vs * i, vs);",
+                             "memcpy(cv + vs * k, (n ? bv : av) + vs * (j < n ? j : 0), vs);"),
 }
 
 RUNNER = r"""
