@@ -36,6 +36,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+SORT_SEED = 20261207  # inputs of the sort and batched-merge timings
 METRIC = "merged elements/sec and achieved HBM GB/s (% of MI355X peak), int32 m=n=2^28"
 COUNTER_FILE = os.path.join(ROOT, "profiles", "merge_segments_uniform_i32_2p28x2p28_traffic.md")
 KERNEL_SOURCES = ["corank.hpp", "merge_kernel.hpp", "omerge.hip"]
@@ -187,6 +188,76 @@ def typed_orders(om, d_arrs, c_ref, w, stream):
             del a, b, out, want
 
 
+def _time(fn, stream, reps=5, warm=2):
+    import torch
+    for _ in range(warm):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def sort_and_batch(om, stream):
+    """The merge sort and the batched merge on 2^28 int32 keys (and 2^27
+    key+payload pairs), each checked against torch's stable sort before it
+    is timed; torch.sort is timed beside it for context."""
+    import torch
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(SORT_SEED)
+    log("merge sort and batched merge (int32)")
+    log("%-44s %10s %14s" % ("case", "ms", "elements/s"))
+    n = 1 << 28
+    keys = torch.randint(-(1 << 31), (1 << 31) - 1, (n,), dtype=torch.int32, device=dev,
+                         generator=g)
+    out = torch.empty_like(keys)
+    om.sort(keys, out=out, stream=stream)
+    ref = torch.sort(keys, stable=True).values
+    torch.cuda.synchronize()
+    if not torch.equal(out, ref):
+        log("FAILED: omerge sort differs from torch's stable sort")
+        sys.exit(1)
+    ms = _time(lambda: om.sort(keys, out=out, stream=stream), stream)
+    log("%-44s %10.3f %14.4g" % ("omerge sort, 2^28 int32 keys", ms, n / (ms * 1e-3)))
+    ms_t = _time(lambda: torch.sort(keys, stable=True), stream)
+    log("%-44s %10.3f %14.4g" % ("torch.sort(stable=True), same keys", ms_t, n / (ms_t * 1e-3)))
+    del out, ref
+    n2 = 1 << 27
+    k2 = keys[:n2].clone()
+    v2 = torch.arange(n2, dtype=torch.int32, device=dev)
+    ok_, ov_ = torch.empty_like(k2), torch.empty_like(v2)
+    om.sort(k2, v2, out=ok_, out_vals=ov_, stream=stream)
+    rk, ri = torch.sort(k2, stable=True)
+    torch.cuda.synchronize()
+    if not (torch.equal(ok_, rk) and torch.equal(ov_, ri.to(torch.int32))):
+        log("FAILED: omerge pair sort differs from torch's stable sort")
+        sys.exit(1)
+    ms = _time(lambda: om.sort(k2, v2, out=ok_, out_vals=ov_, stream=stream), stream)
+    log("%-44s %10.3f %14.4g" % ("omerge sort, 2^27 int32 keys + payloads", ms, n2 / (ms * 1e-3)))
+    del k2, v2, ok_, ov_, rk, ri
+    # 2^15 merges of 4096 + 4096 sorted keys each (2^28 outputs)
+    pairs, L = 1 << 15, 4096
+    a = torch.sort(keys[:pairs * L].view(pairs, L), dim=1).values.reshape(-1)
+    b = torch.sort(keys[pairs * L:2 * pairs * L].view(pairs, L), dim=1).values.reshape(-1)
+    offs = torch.arange(0, pairs * L + 1, L, dtype=torch.int64, device=dev)
+    c = torch.empty(2 * pairs * L, dtype=torch.int32, device=dev)
+    om.merge_batched(a, offs, b, offs, out=c, stream=stream)
+    ref = torch.sort(torch.cat([a.view(pairs, L), b.view(pairs, L)], dim=1), dim=1).values
+    torch.cuda.synchronize()
+    if not torch.equal(c.view(pairs, 2 * L), ref):
+        log("FAILED: omerge batched merge differs from torch's per-merge sort")
+        sys.exit(1)
+    ms = _time(lambda: om.merge_batched(a, offs, b, offs, out=c, stream=stream), stream)
+    gbs = 2 * c.numel() * 4 / (ms * 1e-3) / 1e9
+    log("%-44s %10.3f %14.4g  (%.0f GB/s, %.1f%% of peak)" % (
+        "batched: 2^15 merges of 4096+4096", ms, c.numel() / (ms * 1e-3), gbs,
+        100 * gbs / HBM_PEAK_GBS))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -197,8 +268,9 @@ def main():
                     help="skip timing the oracle (the output check still runs)")
     ap.add_argument("--ablation", action="store_true",
                     help="also time the global-memory (no LDS) merge kernels at 1..256 outputs "
-                         "per lane, each checked against the oracle, and every key order of "
-                         "omerge_merge_keys; tables on stderr")
+                         "per lane, each checked against the oracle, every key order of "
+                         "omerge_merge_keys, the merge sort and the batched merge; tables on "
+                         "stderr")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -274,6 +346,7 @@ def main():
     del want
     if args.ablation and not w.kv:
         typed_orders(om, d_arrs, out, w, stream)
+        sort_and_batch(om, stream)
 
     # Warmup, then exactly K timed steps.
     for _ in range(args.warmup):

@@ -133,6 +133,51 @@ int omerge_merge_pairs(const void *A_keys, const void *A_vals, int64_t m,
                        int payload_bytes, struct ihipStream_t *stream);
 
 /*
+ * omerge_merge_batched -- many independent stable merges in one call (page
+ * "Practice - Sorting Foundations and Parallel Radix Sort",
+ * pmpp.huatsai.dev/13-sorting/practice-sorting, its merge-sort stages: many
+ * small merges are spread across workgroups, and a large one is cut into
+ * pieces by co-rank).  Merge p (p = 0 .. num_merges-1) takes
+ * A[a_offsets[p] .. a_offsets[p+1]) and B[b_offsets[p] .. b_offsets[p+1])
+ * and writes C[a_offsets[p]+b_offsets[p] .. a_offsets[p+1]+b_offsets[p+1]),
+ * i.e. C is the merges' outputs one after another.
+ *   A_keys[m], B_keys[n]          in:  keys of `order` (as omerge_merge_keys),
+ *                                      each merge's run sorted in that order.
+ *   A_vals, B_vals                in:  payloads of payload_bytes (4 or 8)
+ *                                      each, or NULL when payload_bytes == 0.
+ *   a_offsets, b_offsets          in:  device int64 arrays of num_merges+1
+ *                                      nondecreasing entries with
+ *                                      a_offsets[0] = 0, a_offsets[num_merges]
+ *                                      = m (likewise b with n).  NOT checked
+ *                                      (device memory): other offsets give an
+ *                                      unspecified output, but every access
+ *                                      stays inside the arrays.
+ *   C_keys[m+n], C_vals[m+n]      out.
+ * num_merges >= 1 when m+n > 0.  Stream-ordered scratch of one 40-byte
+ * descriptor per segment; otherwise as merge_kv.
+ *
+ * omerge_sort -- stable merge sort of n keys (and their payloads): a block
+ * sort of each tile, then passes that merge adjacent sorted runs, doubling
+ * their length (the same page's merge-sort stages).  Equal keys keep their
+ * input order.
+ *   keys_in[n], vals_in[n]        in:  keys of `order`; payloads of
+ *                                      payload_bytes (0 = none, vals NULL).
+ *   keys_out[n], vals_out[n]      out: may be the inputs themselves (in
+ *                                      place); otherwise disjoint from them.
+ * Stream-ordered scratch of n keys and payloads plus the pass descriptors.
+ */
+int omerge_merge_batched(const void *A_keys, const void *A_vals,
+                         const int64_t *a_offsets, int64_t m,
+                         const void *B_keys, const void *B_vals,
+                         const int64_t *b_offsets, int64_t n,
+                         int64_t num_merges, void *C_keys, void *C_vals,
+                         int order, int payload_bytes,
+                         struct ihipStream_t *stream);
+int omerge_sort(const void *keys_in, const void *vals_in, void *keys_out,
+                void *vals_out, int64_t n, int order, int payload_bytes,
+                struct ihipStream_t *stream);
+
+/*
  * omerge_co_rank -- device co-rank at arbitrary output ranks (page
  * "Co-rank Function ...", section "Binary-Search Implementation": bounds
  * i = min(k,m), i_low = max(0,k-n), j_low = max(0,k-m), half-step rounded up,

@@ -105,6 +105,11 @@ class Oracle:
         lib.oracle_merge_pairs.restype = None
         lib.oracle_key_le.argtypes = [ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64]
         lib.oracle_key_le.restype = ctypes.c_int
+        lib.oracle_merge_batched.argtypes = [ctypes.c_int, ctypes.c_int, p, p, p, p, p, p, i64,
+                                             p, p]
+        lib.oracle_merge_batched.restype = None
+        lib.oracle_sort.argtypes = [ctypes.c_int, ctypes.c_int, p, p, i64, p, p, p, p]
+        lib.oracle_sort.restype = None
         self._lib = lib
         self.path = lib_path
 
@@ -151,6 +156,53 @@ class Oracle:
         self._lib.oracle_merge_pairs(order, Av.dtype.itemsize, _ptr(Ak), _ptr(Av), Ak.size,
                                      _ptr(Bk), _ptr(Bv), Bk.size, _ptr(Ck), _ptr(Cv))
         return Ck.view(_KIND_DTYPE[kind]), Cv.view(vdt)
+
+    def merge_batched(self, A, a_off, B, b_off, A_vals=None, B_vals=None,
+                      descending: bool = False):
+        """Independent stable merges: merge p of A[a_off[p]:a_off[p+1]] and
+        B[b_off[p]:b_off[p+1]] lands at C[a_off[p]+b_off[p] ...].  Returns C
+        (and the payloads when A_vals / B_vals are given)."""
+        kind, A, B = _typed_pair(A, B)
+        a_off = np.ascontiguousarray(a_off, dtype=np.int64)
+        b_off = np.ascontiguousarray(b_off, dtype=np.int64)
+        if a_off.size != b_off.size or a_off.size < 1:
+            raise ValueError("offset arrays differ in length or are empty")
+        if a_off[0] != 0 or b_off[0] != 0 or a_off[-1] != A.size or b_off[-1] != B.size \
+                or np.any(np.diff(a_off) < 0) or np.any(np.diff(b_off) < 0):
+            raise ValueError("offsets must run nondecreasing from 0 to the array sizes")
+        order = kind | (ORDER_DESCENDING if descending else 0)
+        C = np.empty(A.size + B.size, dtype=A.dtype)
+        if A_vals is None:
+            self._lib.oracle_merge_batched(order, 0, _ptr(A), None, _ptr(a_off), _ptr(B), None,
+                                           _ptr(b_off), a_off.size - 1, _ptr(C), None)
+            return C.view(_KIND_DTYPE[kind])
+        vdt, Av, Bv = _payloads(A_vals, B_vals)
+        if Av.size != A.size or Bv.size != B.size:
+            raise ValueError("key and payload lengths differ")
+        Cv = np.empty(A.size + B.size, dtype=Av.dtype)
+        self._lib.oracle_merge_batched(order, Av.dtype.itemsize, _ptr(A), _ptr(Av), _ptr(a_off),
+                                       _ptr(B), _ptr(Bv), _ptr(b_off), a_off.size - 1, _ptr(C),
+                                       _ptr(Cv))
+        return C.view(_KIND_DTYPE[kind]), Cv.view(vdt)
+
+    def sort(self, keys, vals=None, descending: bool = False):
+        """Stable sort by key in the key type's order (descending if asked);
+        returns the sorted keys, and the payloads moved with them."""
+        kind, K, _ = _typed_pair(keys, keys)
+        order = kind | (ORDER_DESCENDING if descending else 0)
+        out = np.empty_like(K)
+        tmp = np.empty_like(K)
+        if vals is None:
+            self._lib.oracle_sort(order, 0, _ptr(K), None, K.size, _ptr(out), None, _ptr(tmp),
+                                  None)
+            return out.view(_KIND_DTYPE[kind])
+        vdt, V, _ = _payloads(vals, vals)
+        if V.size != K.size:
+            raise ValueError("key and payload lengths differ")
+        out_v, tmp_v = np.empty_like(V), np.empty_like(V)
+        self._lib.oracle_sort(order, V.dtype.itemsize, _ptr(K), _ptr(V), K.size, _ptr(out),
+                              _ptr(out_v), _ptr(tmp), _ptr(tmp_v))
+        return out.view(_KIND_DTYPE[kind]), out_v.view(vdt)
 
     def key_le(self, dtype, x, y, descending: bool = False) -> bool:
         """The order relation itself: does key x come before key y, or tie?"""
@@ -209,6 +261,14 @@ def merge_pairs(A_keys, A_vals, B_keys, B_vals, descending=False):
 
 def key_le(dtype, x, y, descending=False):
     return default().key_le(dtype, x, y, descending)
+
+
+def merge_batched(A, a_off, B, b_off, A_vals=None, B_vals=None, descending=False):
+    return default().merge_batched(A, a_off, B, b_off, A_vals, B_vals, descending)
+
+
+def sort(keys, vals=None, descending=False):
+    return default().sort(keys, vals, descending)
 
 
 def co_rank_all(A, B):

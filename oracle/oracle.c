@@ -49,6 +49,11 @@
  *                      float "<=".  binary64 keys follow the same clause.
  *                      Descending order "x before-or-equal y" is ascending
  *                      "y before-or-equal x"; ties still take A.
+ *   oracle_merge_batched  Independent merges of consecutive ranges of A and
+ *                      B, each by the walk above, outputs one after another.
+ *   oracle_sort        Stable sort by key: bottom-up merge sort with the
+ *                      walk above (left run as A).  Its result is the unique
+ *                      stable order, which is what it is pinned against.
  *
  * int32 keys are compared signed.  Lengths are int64, matching the size_t
  * lengths of merge_path.cu.
@@ -291,5 +296,82 @@ void oracle_merge_pairs(int order, int val_bytes, const void *Ak,
             memcpy(cv + vs * k, bv + vs * j, vs);
             ++j;
         }
+    }
+}
+
+/* One typed merge of keys, with payloads when val_bytes > 0. */
+static void merge_range(int order, int val_bytes, const void *Ak,
+                        const void *Av, int64_t m, const void *Bk,
+                        const void *Bv, int64_t n, void *Ck, void *Cv)
+{
+    if (val_bytes > 0)
+        oracle_merge_pairs(order, val_bytes, Ak, Av, m, Bk, Bv, n, Ck, Cv);
+    else
+        oracle_merge_keys(order, Ak, m, Bk, n, Ck);
+}
+
+/* A batch of independent merges (the merge-sort stages of page "Practice -
+ * Sorting Foundations and Parallel Radix Sort", 13-sorting): merge p takes
+ * A[a_off[p], a_off[p+1]) and B[b_off[p], b_off[p+1]) and writes its output
+ * at C[a_off[p] + b_off[p] ...).  Each is the walk above. */
+void oracle_merge_batched(int order, int val_bytes, const void *Ak,
+                          const void *Av, const int64_t *a_off,
+                          const void *Bk, const void *Bv,
+                          const int64_t *b_off, int64_t pairs, void *Ck,
+                          void *Cv)
+{
+    int ks = key_size(order & 7), vs = val_bytes;
+    int64_t p;
+    for (p = 0; p < pairs; ++p) {
+        int64_t a0 = a_off[p], b0 = b_off[p];
+        int64_t c0 = a0 + b0;
+        merge_range(order, vs, (const unsigned char *)Ak + ks * a0,
+                    vs ? (const unsigned char *)Av + vs * a0 : 0,
+                    a_off[p + 1] - a0, (const unsigned char *)Bk + ks * b0,
+                    vs ? (const unsigned char *)Bv + vs * b0 : 0,
+                    b_off[p + 1] - b0, (unsigned char *)Ck + ks * c0,
+                    vs ? (unsigned char *)Cv + vs * c0 : 0);
+    }
+}
+
+/* Stable sort by key (same page: a stable sort keeps the input order of
+ * equal keys), as the page's merge sort: sorted runs of width 1, 2, 4, ...
+ * merged pairwise with the walk above (the left run is A, so equal keys keep
+ * their input order), until one run remains.  tmp_keys / tmp_vals hold n
+ * keys / payloads of scratch; out and in may be the same arrays. */
+void oracle_sort(int order, int val_bytes, const void *in_keys,
+                 const void *in_vals, int64_t n, void *out_keys,
+                 void *out_vals, void *tmp_keys, void *tmp_vals)
+{
+    int ks = key_size(order & 7), vs = val_bytes;
+    unsigned char *src_k = out_keys, *src_v = out_vals;
+    unsigned char *dst_k = tmp_keys, *dst_v = tmp_vals;
+    int64_t width, i;
+    if (out_keys != in_keys)
+        memcpy(out_keys, in_keys, (size_t)(n * ks));
+    if (vs > 0 && out_vals != in_vals)
+        memcpy(out_vals, in_vals, (size_t)(n * vs));
+    for (width = 1; width < n; width *= 2) {
+        for (i = 0; i < n; i += 2 * width) {
+            int64_t la = width < n - i ? width : n - i;
+            int64_t lb = n - i - la < width ? n - i - la : width;
+            merge_range(order, vs, src_k + ks * i, vs ? src_v + vs * i : 0,
+                        la, src_k + ks * (i + la),
+                        vs ? src_v + vs * (i + la) : 0, lb, dst_k + ks * i,
+                        vs ? dst_v + vs * i : 0);
+        }
+        {
+            unsigned char *t = src_k;
+            src_k = dst_k;
+            dst_k = t;
+            t = src_v;
+            src_v = dst_v;
+            dst_v = t;
+        }
+    }
+    if (src_k != (unsigned char *)out_keys) {
+        memcpy(out_keys, src_k, (size_t)(n * ks));
+        if (vs > 0)
+            memcpy(out_vals, src_v, (size_t)(n * vs));
     }
 }

@@ -1,4 +1,5 @@
-"""omerge: stable merge of two sorted arrays on AMD MI355X (gfx950).
+"""omerge: stable merges of sorted arrays, batches of merges and a stable
+merge sort, on AMD MI355X (gfx950).
 
 The work runs in hand-written HIP kernels behind a C ABI (include/omerge.h,
 libomerge.so); this package is the thin Python binding over torch tensors.
@@ -16,6 +17,7 @@ from .binding import (  # noqa: F401
     library_path,
     load_library,
     merge,
+    merge_batched,
     merge_i32,
     merge_i32_direct,
     merge_kv,
@@ -26,5 +28,6 @@ from .binding import (  # noqa: F401
     partition_count,
     order_code,
     segment_length,
+    sort,
     stream_copy,
 )

@@ -50,6 +50,8 @@ def load_library() -> ctypes.CDLL:
         "merge_kv": (i32, [p, p, i64, p, p, i64, p, p, p]),
         "omerge_merge_keys": (i32, [p, i64, p, i64, p, i32, p]),
         "omerge_merge_pairs": (i32, [p, p, i64, p, p, i64, p, p, i32, i32, p]),
+        "omerge_merge_batched": (i32, [p, p, p, i64, p, p, p, i64, i64, p, p, i32, i32, p]),
+        "omerge_sort": (i32, [p, p, p, p, i64, i32, i32, p]),
         "omerge_co_rank": (i32, [p, i64, p, i64, p, i64, p, p]),
         "omerge_segment_length": (i64, [i64, i64, i32]),
         "omerge_partition_count": (i64, [i64, i64]),
@@ -228,6 +230,73 @@ def merge_pairs(a_keys: torch.Tensor, a_vals: torch.Tensor, b_keys: torch.Tensor
                                     _stream(dev, stream))
     _raise_on(rc, "omerge_merge_pairs")
     return out_keys, out_vals
+
+
+def merge_batched(a: torch.Tensor, a_offsets: torch.Tensor, b: torch.Tensor,
+                  b_offsets: torch.Tensor, a_vals: Optional[torch.Tensor] = None,
+                  b_vals: Optional[torch.Tensor] = None, descending: bool = False,
+                  out: Optional[torch.Tensor] = None, out_vals: Optional[torch.Tensor] = None,
+                  stream: Optional[torch.cuda.Stream] = None):
+    """Independent stable merges in one call: merge p takes
+    a[a_offsets[p]:a_offsets[p+1]] and b[b_offsets[p]:b_offsets[p+1]] (each
+    sorted in the keys' order) and its output lands at
+    out[a_offsets[p]+b_offsets[p] ...].  Offsets are int64 device tensors of
+    num_merges+1 entries, from 0 to the sizes of a and b, nondecreasing (not
+    checked: they live on the device).  With payloads, returns (keys,
+    payloads)."""
+    _vec(a, "a", tuple(_KEY_KIND))
+    dev = a.device
+    _vec(b, "b", (a.dtype,), dev)
+    _vec(a_offsets, "a_offsets", (torch.int64,), dev)
+    _vec(b_offsets, "b_offsets", (torch.int64,), dev)
+    if a_offsets.numel() != b_offsets.numel() or a_offsets.numel() < 1:
+        raise ValueError("a_offsets and b_offsets must have the same, nonzero length")
+    kv = a_vals is not None or b_vals is not None
+    if kv:
+        _vec(a_vals, "a_vals", _ANY_PAYLOAD, dev)
+        _vec(b_vals, "b_vals", (a_vals.dtype,), dev)
+        if a_vals.numel() != a.numel() or b_vals.numel() != b.numel():
+            raise ValueError("key and payload lengths differ")
+    order = order_code(a.dtype, descending)
+    t = a.numel() + b.numel()
+    out = _out(out, t, a.dtype, dev, "out")
+    if kv:
+        out_vals = _out(out_vals, t, a_vals.dtype, dev, "out_vals")
+    lib = load_library()
+    with torch.cuda.device(dev):
+        rc = lib.omerge_merge_batched(
+            _ptr(a), _ptr(a_vals) if kv else None, _ptr(a_offsets), a.numel(), _ptr(b),
+            _ptr(b_vals) if kv else None, _ptr(b_offsets), b.numel(), a_offsets.numel() - 1,
+            _ptr(out), _ptr(out_vals) if kv else None, order,
+            a_vals.element_size() if kv else 0, _stream(dev, stream))
+    _raise_on(rc, "omerge_merge_batched")
+    return (out, out_vals) if kv else out
+
+
+def sort(keys: torch.Tensor, vals: Optional[torch.Tensor] = None, descending: bool = False,
+         out: Optional[torch.Tensor] = None, out_vals: Optional[torch.Tensor] = None,
+         stream: Optional[torch.cuda.Stream] = None):
+    """Stable merge sort of a key tensor (and payloads moved with the keys):
+    equal keys keep their input order.  out / out_vals may be keys / vals
+    themselves (in place).  With payloads, returns (keys, payloads)."""
+    _vec(keys, "keys", tuple(_KEY_KIND))
+    dev = keys.device
+    kv = vals is not None
+    if kv:
+        _vec(vals, "vals", _ANY_PAYLOAD, dev)
+        if vals.numel() != keys.numel():
+            raise ValueError("key and payload lengths differ")
+    order = order_code(keys.dtype, descending)
+    out = _out(out, keys.numel(), keys.dtype, dev, "out")
+    if kv:
+        out_vals = _out(out_vals, keys.numel(), vals.dtype, dev, "out_vals")
+    lib = load_library()
+    with torch.cuda.device(dev):
+        rc = lib.omerge_sort(_ptr(keys), _ptr(vals) if kv else None, _ptr(out),
+                             _ptr(out_vals) if kv else None, keys.numel(), order,
+                             vals.element_size() if kv else 0, _stream(dev, stream))
+    _raise_on(rc, "omerge_sort")
+    return (out, out_vals) if kv else out
 
 
 def co_rank(a: torch.Tensor, b: torch.Tensor, k: torch.Tensor,

@@ -1,0 +1,338 @@
+// batch_kernel.hpp -- many merges in one launch, and the merge-sort stages.
+//
+// Page "Practice - Sorting Foundations and Parallel Radix Sort"
+// (pmpp.huatsai.dev/13-sorting/practice-sorting), its merge-sort item: in
+// the early stages of a merge sort there are many independent merges of few
+// keys each, and the parallelism is across merges (one merge per block);
+// in the late stages there are few, large merges, and each one is cut into
+// independent pieces with the co-rank function of the merge chapter.  The
+// same page notes that sorting networks, although asymptotically worse, are
+// often the fastest way to sort short sequences.
+//
+// Both regimes run through one segment merge kernel here (merge_kernel.hpp,
+// descriptor mode): a plan kernel cuts every merge of a batch, or of one
+// merge-sort pass, into segments of at most seg_len outputs, each lying
+// inside one merge, and writes one descriptor per segment (its A, B and C
+// ranges).  Small merges become one segment each (parallel across merges);
+// a large merge becomes many (parallel inside the merge).  The boundary
+// co-ranks are found with the group search of the partition kernel, inside
+// the one merge that holds the boundary.
+//
+// The first stage of the merge sort is block_sort_kernel: each workgroup
+// sorts one tile in registers and LDS (a bitonic network per lane, then
+// in-LDS merges of the lanes' runs by co-rank), producing sorted runs of
+// one tile for the merge passes.
+#pragma once
+
+#include "merge_kernel.hpp"
+
+namespace omerge {
+
+// ---------------------------------------------------------------------------
+// Plans.  A plan has segs segments and segs + 1 boundaries; boundary w is
+// the start of segment w and the end of segment w-1.  One group of G lanes
+// handles one boundary: it finds the co-rank there (if the boundary is inside
+// a merge) and writes the start of desc[w] and the end of desc[w-1].
+
+// Merge-sort pass: src (total elements) holds sorted runs of `run` elements;
+// runs 2p (as A) and 2p+1 (as B) merge into the same positions of the output.
+// A full pair is cut into per_pair segments of seg_len outputs; a short last
+// pair (total not a multiple of 2*run) into as many as it needs.
+template <int G, int ORDER>
+__global__ __launch_bounds__(256) void plan_runs_kernel(
+    const typename KeyOrder<ORDER>::T* __restrict__ src, int64_t total, int64_t run,
+    int64_t seg_len, int64_t per_pair, int64_t segs, SegDesc* __restrict__ desc) {
+    static_assert(G >= 2, "group search");
+    const int64_t gid = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+    if ((gid & ~int64_t(63)) / G > segs) return;  // the whole wavefront is past the end
+    const int64_t w = gid / G;
+    const bool live = w <= segs;
+    const int g_lane = static_cast<int>(gid % G);
+    const int g_shift = static_cast<int>(threadIdx.x & 63) - g_lane;
+
+    const int64_t full_pairs = total / (2 * run);
+    int64_t p, g;  // pair, and segment within the pair
+    if (w < full_pairs * per_pair) {
+        p = w / per_pair;
+        g = w % per_pair;
+    } else {
+        p = full_pairs;
+        g = w - full_pairs * per_pair;
+    }
+    const int64_t base = p * 2 * run;
+    const int64_t rem = total > base ? total - base : 0;
+    const int64_t la = rem < run ? rem : run;
+    const int64_t lb = rem - la < run ? rem - la : run;
+    const int64_t k = g * seg_len < la + lb ? g * seg_len : la + lb;
+    const int64_t i = co_rank_group<G, ORDER>(live ? k : 0, src + base, live ? la : 0,
+                                              src + base + la, live ? lb : 0, g_lane, g_shift);
+    if (!live || g_lane != 0) return;
+    if (w < segs) {
+        desc[w].a0 = base + i;
+        desc[w].b0 = base + la + (k - i);
+        desc[w].c0 = base + k;
+    }
+    if (w > 0) {
+        if (g > 0) {  // inside a pair: the previous segment ends here
+            desc[w - 1].a1 = base + i;
+            desc[w - 1].b1 = base + la + (k - i);
+        } else {      // first segment of pair p: the previous one ends pair p-1
+            desc[w - 1].a1 = base - run;
+            desc[w - 1].b1 = base;
+        }
+    }
+}
+
+// Batch of merges: merge p takes A[a_off[p], a_off[p+1]) and B[b_off[p],
+// b_off[p+1]) to C[a_off[p]+b_off[p], a_off[p+1]+b_off[p+1]), p = 0..pairs-1
+// (a_off[0] = b_off[0] = 0, a_off[pairs] = m, b_off[pairs] = n).  The
+// boundaries are every merge's start and every multiple of seg_len inside
+// (0, m+n), in order, a merge start first where the two coincide: merge
+// start p is boundary p + ceil(c_p/seg_len) - 1 (c_p its first output), and
+// the multiple g*seg_len is boundary (g-1) + #{p : c_p <= g*seg_len}.  In
+// these concatenated coordinates the end of one segment is the start of the
+// next even across merges.  Offsets are clamped into [0, m] / [0, n], so
+// even invalid offsets keep every access in range.
+template <int G, int ORDER>
+__global__ __launch_bounds__(256) void plan_batched_kernel(
+    const typename KeyOrder<ORDER>::T* __restrict__ A, const int64_t* __restrict__ a_off,
+    int64_t m, const typename KeyOrder<ORDER>::T* __restrict__ B,
+    const int64_t* __restrict__ b_off, int64_t n, int64_t pairs, int64_t seg_len,
+    int64_t segs, SegDesc* __restrict__ desc) {
+    static_assert(G >= 2, "group search");
+    const int64_t gid = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+    if ((gid & ~int64_t(63)) / G > segs) return;
+    const int64_t w = gid / G;
+    const bool live = w <= segs;
+    const int g_lane = static_cast<int>(gid % G);
+    const int g_shift = static_cast<int>(threadIdx.x & 63) - g_lane;
+    auto ao = [&](int64_t p) { return clamp_to<int64_t>(a_off[p], 0, m); };
+    auto bo = [&](int64_t p) { return clamp_to<int64_t>(b_off[p], 0, n); };
+
+    int64_t p = 0, k = 0, idx = 0, c = 0;
+    bool search = false;
+    if (live && w <= pairs) {  // start of merge w
+        p = w;
+        c = ao(p) + bo(p);
+        idx = p + (c > 0 ? (c - 1) / seg_len : 0);
+    } else if (live) {         // multiple g*seg_len inside some merge
+        const int64_t g = w - pairs;
+        c = g * seg_len;
+        // number of merge starts <= c: upper bound over the nondecreasing starts
+        int64_t lo = 0, hi = pairs + 1;
+        while (lo < hi) {
+            const int64_t mid = (lo + hi) >> 1;
+            if (ao(mid) + bo(mid) <= c) lo = mid + 1;
+            else hi = mid;
+        }
+        idx = (g - 1) + lo;
+        p = lo > 0 ? (lo - 1 < pairs ? lo - 1 : pairs - 1) : 0;
+        k = c - (ao(p) + bo(p));
+        search = true;
+    }
+    int64_t la = 0, lb = 0;
+    if (search && p < pairs) {
+        const int64_t a1 = ao(p + 1), b1 = bo(p + 1);
+        la = a1 > ao(p) ? a1 - ao(p) : 0;
+        lb = b1 > bo(p) ? b1 - bo(p) : 0;
+        k = clamp_to<int64_t>(k, 0, la + lb);
+    } else {
+        k = 0;
+    }
+    const int64_t a_base = search ? ao(p) : 0, b_base = search ? bo(p) : 0;
+    const int64_t i = co_rank_group<G, ORDER>(k, A + a_base, la, B + b_base, lb, g_lane, g_shift);
+    if (!live || g_lane != 0 || idx < 0 || idx > segs) return;
+    const int64_t a = search ? a_base + i : ao(p);
+    const int64_t b = search ? b_base + (k - i) : bo(p);
+    if (idx < segs) {
+        desc[idx].a0 = a;
+        desc[idx].b0 = b;
+        desc[idx].c0 = c;
+    }
+    if (idx > 0) {
+        desc[idx - 1].a1 = a;
+        desc[idx - 1].b1 = b;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Block sort: workgroup t sorts elements [t*TILE, min((t+1)*TILE, total)) of
+// src into the same positions of dst (dst may be src: a tile is read whole
+// before it is written).  Keys are sorted as their order images; with
+// payloads (VW words each) the sort is stable: every element carries its
+// position in the tile, and (key, position) pairs are all distinct, so
+// ordering them exactly is the stable order.  The tile's missing tail is
+// padded with the largest image and positions past the end, which sort
+// last and are never stored.
+
+// Sorts x[0..N) (with positions pos when POS) ascending by a bitonic network.
+template <int N, bool POS, typename T>
+__device__ __forceinline__ void bitonic_sort(T (&x)[N], int (&pos)[N]) {
+#pragma unroll
+    for (int kk = 2; kk <= N; kk <<= 1) {
+#pragma unroll
+        for (int j = kk >> 1; j > 0; j >>= 1) {
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const int l = i ^ j;
+                if (l > i) {
+                    const bool up = (i & kk) == 0;
+                    const bool gt = POS ? (x[i] > x[l] || (x[i] == x[l] && pos[i] > pos[l]))
+                                        : x[i] > x[l];
+                    if (gt == up) {
+                        const T t = x[i];
+                        x[i] = x[l];
+                        x[l] = t;
+                        if (POS) {
+                            const int q = pos[i];
+                            pos[i] = pos[l];
+                            pos[l] = q;
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int THREADS, int ITEMS>
+struct SortCfg {
+    static constexpr int kTile = THREADS * ITEMS;
+};
+
+template <int THREADS, int ITEMS, int VW, int ORDER>
+__global__ __launch_bounds__(THREADS) void block_sort_kernel(
+    const typename KeyOrder<ORDER>::T* __restrict__ src, const uint32_t* __restrict__ src_v,
+    int64_t total, typename KeyOrder<ORDER>::T* dst, uint32_t* dst_v) {
+    using K = KeyOrder<ORDER>;
+    using Key = typename K::T;
+    constexpr int KW = K::kWords;
+    constexpr bool KV = VW > 0;
+    constexpr int kTile = THREADS * ITEMS;
+    static_assert(ITEMS >= 4 && (ITEMS & (ITEMS - 1)) == 0, "ITEMS: a power of two");
+    // LDS: keys (padded as the merge stage), positions, payloads, splits.
+    constexpr int kKeyWords = kTile * KW + kTile * KW / 8;
+    constexpr int kPos = kKeyWords;
+    constexpr int kPay = kPos + (KV ? kTile : 0);
+    constexpr int kSplitAt = kPay + kTile * VW;
+    __shared__ __attribute__((aligned(16))) int lds[kSplitAt + THREADS];
+    int* const kbuf = lds;
+    int* const pbuf = lds + kPos;
+    int* const vbuf = lds + kPay;
+    int* const split = lds + kSplitAt;
+
+    const int tid = threadIdx.x;
+    const int64_t t0 = blockIdx.x * static_cast<int64_t>(kTile);
+    const int len = static_cast<int>(total - t0 < kTile ? total - t0 : kTile);
+
+    // Load: lane tid takes elements tid, tid+THREADS, ... (coalesced).
+#pragma unroll
+    for (int r = 0; r < ITEMS; ++r) {
+        const int e = tid + r * THREADS;
+        const Key x = e < len ? K::to_ord(src[t0 + e]) : K::kMax;
+        st_elem<Key>(kbuf, stage_word(KW * e), x);
+        if constexpr (KV) {
+            if (e < len) {
+#pragma unroll
+                for (int v = 0; v < VW; ++v) vbuf[VW * e + v] = src_v[VW * (t0 + e) + v];
+            }
+        }
+    }
+    __syncthreads();
+
+    // Each lane sorts its row of ITEMS elements.
+    Key x[ITEMS];
+    int pos[ITEMS];
+#pragma unroll
+    for (int t = 0; t < ITEMS; ++t) {
+        x[t] = ld_elem<Key>(kbuf, stage_word(KW * (tid * ITEMS + t)));
+        pos[t] = tid * ITEMS + t;
+    }
+    bitonic_sort<ITEMS, KV>(x, pos);
+
+    // Merge rounds: runs of `run` elements merge pairwise into runs of 2*run.
+    // The A run of a pair holds earlier positions than its B run, so taking
+    // A on equal keys is the stable order.
+    for (int run = ITEMS; run < kTile; run *= 2) {
+        __syncthreads();  // every read of the previous round is done
+#pragma unroll
+        for (int t = 0; t < ITEMS; ++t) {
+            st_elem<Key>(kbuf, stage_word(KW * (tid * ITEMS + t)), x[t]);
+            if constexpr (KV) pbuf[tid * ITEMS + t] = pos[t];
+        }
+        __syncthreads();
+        const int lanes = 2 * run / ITEMS;   // lanes per merged pair
+        const int u = tid % lanes;           // this lane's place in it
+        const int a0 = (tid - u) * ITEMS;    // the pair's A run; B run at a0 + run
+        const int b0 = a0 + run;
+        const int o_end = (u + 1) * ITEMS;
+        // Co-rank of o_end (bisection, as in the segment merge).
+        int lo = o_end > run ? o_end - run : 0;
+        int hi = o_end < run ? o_end : run;
+        const int steps = bit_length(run);
+        for (int step = 0; step < steps; ++step) {
+            const int mid = (lo + hi) >> 1;
+            const Key av = ld_elem<Key>(kbuf, stage_word(KW * (a0 + mid)));
+            const Key bv = ld_elem<Key>(kbuf, stage_word(KW * (b0 + o_end - 1 - mid)));
+            const bool lv = lo < hi;
+            const bool a_first = av <= bv;
+            lo = (lv && a_first) ? mid + 1 : lo;
+            hi = (lv && !a_first) ? mid : hi;
+        }
+        split[tid] = lo;
+        __syncthreads();
+        const int s = u > 0 ? split[tid - 1] : 0;  // A elements before this lane's outputs
+        const int bs = u * ITEMS - s;
+        if constexpr (!KV) {
+            Key a[ITEMS], b[ITEMS];
+#pragma unroll
+            for (int t = 0; t < ITEMS; ++t) {
+                const int ia = s + t < run ? s + t : run - 1;
+                const int ib = bs + t < run ? bs + t : run - 1;
+                a[t] = s + t < run ? ld_elem<Key>(kbuf, stage_word(KW * (a0 + ia))) : K::kMax;
+                b[t] = bs + t < run ? ld_elem<Key>(kbuf, stage_word(KW * (b0 + ib))) : K::kMax;
+            }
+#pragma unroll
+            for (int t = 0; t < ITEMS; ++t) x[t] = min(a[t], b[ITEMS - 1 - t]);
+            bitonic_clean<ITEMS>(x);
+        } else {
+            int ai = s, bi = bs;
+            const int a_end = lo, b_end = o_end - lo;
+#pragma unroll
+            for (int t = 0; t < ITEMS; ++t) {
+                const int ca = ai < run ? ai : run - 1;
+                const int cb = bi < run ? bi : run - 1;
+                const Key ka = ld_elem<Key>(kbuf, stage_word(KW * (a0 + ca)));
+                const Key kb = ld_elem<Key>(kbuf, stage_word(KW * (b0 + cb)));
+                const bool take_a = ai < a_end && (bi >= b_end || ka <= kb);
+                x[t] = take_a ? ka : kb;
+                pos[t] = pbuf[take_a ? a0 + ca : b0 + cb];
+                ai += take_a ? 1 : 0;
+                bi += take_a ? 0 : 1;
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < ITEMS; ++t) {
+        st_elem<Key>(kbuf, stage_word(KW * (tid * ITEMS + t)), x[t]);
+        if constexpr (KV) pbuf[tid * ITEMS + t] = pos[t];
+    }
+    __syncthreads();
+
+    // Store in tile order, coalesced; payloads follow their positions.
+#pragma unroll
+    for (int r = 0; r < ITEMS; ++r) {
+        const int e = tid + r * THREADS;
+        if (e < len) {
+            dst[t0 + e] = K::from_ord(ld_elem<Key>(kbuf, stage_word(KW * e)));
+            if constexpr (KV) {
+                const int q = pbuf[e];
+#pragma unroll
+                for (int v = 0; v < VW; ++v) dst_v[VW * (t0 + e) + v] = vbuf[VW * q + v];
+            }
+        }
+    }
+}
+
+}  // namespace omerge

@@ -596,12 +596,24 @@ __device__ __forceinline__ void store_from_ring(int32_t* __restrict__ dst, int l
 // Keys are typed by ORDER (KeyOrder<ORDER>::T, 1 or 2 words); payloads are
 // VW words per element (0 = keys only), passed as word arrays.
 
-template <int THREADS, int ITEMS, int VW, int ORDER>
+// DESC = false: segment s is outputs [s*seg_len, (s+1)*seg_len) of one merge
+// of A and B, its A range given by the partition (part[s], part[s+1]).
+// DESC = true: segment s is described by desc[s] (any ranges of A, B and C,
+// e.g. one piece of one merge of a batch, or of one merge-sort pass in which
+// A and B are the same array); seg_len bounds its length and C holds c_total
+// elements.
+struct SegDesc {
+    int64_t a0, b0, c0;  // first A, B and C element
+    int64_t a1, b1;      // one past the last A and B element
+};
+
+template <int THREADS, int ITEMS, int VW, int ORDER, bool DESC = false>
 __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
     const typename KeyOrder<ORDER>::T* __restrict__ A, const uint32_t* __restrict__ Av, int64_t m,
     const typename KeyOrder<ORDER>::T* __restrict__ B, const uint32_t* __restrict__ Bv, int64_t n,
     const int64_t* __restrict__ part, int64_t seg_len,
-    typename KeyOrder<ORDER>::T* __restrict__ C, uint32_t* __restrict__ Cv) {
+    typename KeyOrder<ORDER>::T* __restrict__ C, uint32_t* __restrict__ Cv,
+    const SegDesc* __restrict__ desc, int64_t c_total) {
     using Key = typename KeyOrder<ORDER>::T;
     constexpr int KW = KeyOrder<ORDER>::kWords;
     constexpr bool KV = VW > 0;
@@ -633,19 +645,40 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
     int* const split = lds + Cfg::kSplit;
 
     const int tid = threadIdx.x;
-    const int64_t total = m + n;
     const int64_t seg = blockIdx.x;
-    const int64_t k0 = seg * seg_len;
-    const int64_t k1 = k0 + seg_len < total ? k0 + seg_len : total;
-    const int c_len = static_cast<int>(k1 - k0);
-
-    // Segment windows from the partition, clamped so that any partition
-    // (even one made from unsorted input) keeps every access in range.
-    const int64_t i0 = clamp_to<int64_t>(part[seg], k0 > n ? k0 - n : 0, k0 < m ? k0 : m);
-    const int64_t i1 = clamp_to<int64_t>(part[seg + 1], k1 > n ? k1 - n : 0, k1 < m ? k1 : m);
-    const int a_len = static_cast<int>(clamp_to<int64_t>(i1 - i0, 0, c_len));
-    const int b_len = c_len - a_len;
-    const int64_t j0 = k0 - i0;
+    int64_t k0, i0, j0;  // first output, first A and first B element of the segment
+    int c_len, a_len, b_len;
+    if constexpr (!DESC) {
+        const int64_t total = m + n;
+        k0 = seg * seg_len;
+        const int64_t k1 = k0 + seg_len < total ? k0 + seg_len : total;
+        c_len = static_cast<int>(k1 - k0);
+        // Segment windows from the partition, clamped so that any partition
+        // (even one made from unsorted input) keeps every access in range.
+        i0 = clamp_to<int64_t>(part[seg], k0 > n ? k0 - n : 0, k0 < m ? k0 : m);
+        const int64_t i1 = clamp_to<int64_t>(part[seg + 1], k1 > n ? k1 - n : 0, k1 < m ? k1 : m);
+        a_len = static_cast<int>(clamp_to<int64_t>(i1 - i0, 0, c_len));
+        b_len = c_len - a_len;
+        j0 = k0 - i0;
+    } else {
+        // A segment descriptor names its ranges of A, B and C directly.  They
+        // are clamped into the arrays (m, n and c_total elements) and to
+        // seg_len outputs, and a segment whose output would leave C is
+        // skipped, so any descriptor keeps every access in range.
+        const SegDesc d = desc[seg];
+        i0 = clamp_to<int64_t>(d.a0, 0, m);
+        const int64_t i1 = clamp_to<int64_t>(d.a1, i0, m);
+        j0 = clamp_to<int64_t>(d.b0, 0, n);
+        const int64_t j1 = clamp_to<int64_t>(d.b1, j0, n);
+        a_len = static_cast<int>(i1 - i0 < seg_len ? i1 - i0 : seg_len);
+        b_len = static_cast<int>(j1 - j0 < seg_len - a_len ? j1 - j0 : seg_len - a_len);
+        c_len = a_len + b_len;
+        k0 = d.c0;
+        if (k0 < 0 || k0 > c_total - c_len) {
+            k0 = 0;
+            a_len = b_len = c_len = 0;
+        }
+    }
 
     // Word pointers to the segment's first element of each array.
     const int32_t* const As = reinterpret_cast<const int32_t*>(A + i0);

@@ -8,7 +8,7 @@
 #include <mutex>
 
 #include "omerge.h"
-#include "merge_kernel.hpp"
+#include "batch_kernel.hpp"
 
 namespace omerge {
 namespace {
@@ -210,9 +210,124 @@ struct Path {
         if (segs > kMaxGridBlocks) return OMERGE_OVERFLOW;
         hipLaunchKernelGGL((merge_segments_kernel<kThreads, kItems, VW, ORDER>),
                            dim3(static_cast<unsigned>(segs)), dim3(kThreads), 0, stream, A, Av, m,
-                           B, Bv, n, part, seg_len, C, Cv);
+                           B, Bv, n, part, seg_len, C, Cv, nullptr, m + n);
         hipError_t e = hipGetLastError();
         return e == hipSuccess ? OMERGE_OK : hip_fail(e);
+    }
+
+    // Segment merge of `segs` described segments (descriptor mode).
+    static int merge_desc(const Key* A, const uint32_t* Av, int64_t m, const Key* B,
+                          const uint32_t* Bv, int64_t n, const SegDesc* desc, int64_t segs,
+                          int64_t seg_len, Key* C, uint32_t* Cv, int64_t c_total,
+                          hipStream_t stream) {
+        if (segs == 0) return OMERGE_OK;
+        hipLaunchKernelGGL((merge_segments_kernel<kThreads, kItems, VW, ORDER, true>),
+                           dim3(static_cast<unsigned>(segs)), dim3(kThreads), 0, stream, A, Av, m,
+                           B, Bv, n, nullptr, seg_len, C, Cv, desc, c_total);
+        hipError_t e = hipGetLastError();
+        return e == hipSuccess ? OMERGE_OK : hip_fail(e);
+    }
+
+    // A batch of `pairs` merges given by prefix offsets into A and B (device
+    // arrays of pairs+1 entries): plan the segments, then merge them.
+    static int batched(const void* A, const void* Av, const int64_t* a_off, int64_t m,
+                       const void* B, const void* Bv, const int64_t* b_off, int64_t n,
+                       int64_t pairs, void* C, void* Cv, hipStream_t stream) {
+        const int64_t total = m + n;
+        if (total == 0) return OMERGE_OK;
+        int64_t sl = 0;
+        int rc = seg_len(m, n, &sl);
+        if (rc != OMERGE_OK) return rc;
+        const int64_t segs = pairs + ceil_div(total, sl) - 1;
+        const int64_t blocks = ceil_div((segs + 1) * kPartLanes, 256);
+        if (segs > kMaxGridBlocks || blocks > kMaxGridBlocks) return OMERGE_OVERFLOW;
+        SegDesc* desc = nullptr;
+        hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&desc),
+                                      static_cast<size_t>(segs) * sizeof(SegDesc), stream);
+        if (e != hipSuccess) return hip_fail(e);
+        const Key* a = static_cast<const Key*>(A);
+        const Key* b = static_cast<const Key*>(B);
+        hipLaunchKernelGGL((plan_batched_kernel<kPartLanes, ORDER>),
+                           dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, a, a_off, m,
+                           b, b_off, n, pairs, sl, segs, desc);
+        e = hipGetLastError();
+        rc = e == hipSuccess ? OMERGE_OK : hip_fail(e);
+        if (rc == OMERGE_OK)
+            rc = merge_desc(a, static_cast<const uint32_t*>(Av), m, b,
+                            static_cast<const uint32_t*>(Bv), n, desc, segs, sl,
+                            static_cast<Key*>(C), static_cast<uint32_t*>(Cv), total, stream);
+        e = hipFreeAsync(desc, stream);
+        if (rc == OMERGE_OK && e != hipSuccess) rc = hip_fail(e);
+        return rc;
+    }
+
+    // Stable merge sort of N elements: block sort into runs of one tile,
+    // then passes that merge adjacent runs, ping-ponging between the output
+    // and a scratch copy so that the last pass lands in the output.
+    static int sort(const void* in_k, const void* in_v, void* out_k, void* out_v, int64_t N,
+                    hipStream_t stream) {
+        if (N == 0) return OMERGE_OK;
+        const int64_t tiles = ceil_div(N, kTile);
+        if (tiles > kMaxGridBlocks) return OMERGE_OVERFLOW;
+        int passes = 0;
+        for (int64_t run = kTile; run < N; run *= 2) ++passes;
+        int64_t sl = 0;
+        int rc = seg_len(N, 0, &sl);
+        if (rc != OMERGE_OK) return rc;
+        int64_t max_segs = 0;
+        for (int64_t run = kTile; run < N; run *= 2) {
+            const int64_t per_pair = ceil_div(2 * run, sl);
+            const int64_t full = N / (2 * run), rem = N - full * 2 * run;
+            const int64_t segs = full * per_pair + (rem > 0 ? ceil_div(rem, sl) : 0);
+            max_segs = segs > max_segs ? segs : max_segs;
+        }
+        if (max_segs > kMaxGridBlocks) return OMERGE_OVERFLOW;
+        // Scratch: keys, payloads and descriptors in one stream-ordered block,
+        // each part 256-byte aligned (64-bit payloads after an odd number of
+        // 32-bit keys would otherwise lose their 8-byte alignment).
+        const size_t key_bytes = static_cast<size_t>(N) * sizeof(Key);
+        const size_t val_at = (key_bytes + 255) & ~size_t(255);
+        const size_t val_bytes = static_cast<size_t>(N) * 4 * VW;
+        const size_t desc_at = (val_at + val_bytes + 255) & ~size_t(255);
+        char* scratch = nullptr;
+        if (passes > 0) {
+            hipError_t e = hipMallocAsync(
+                reinterpret_cast<void**>(&scratch),
+                desc_at + static_cast<size_t>(max_segs) * sizeof(SegDesc), stream);
+            if (e != hipSuccess) return hip_fail(e);
+        }
+        Key* const sk = reinterpret_cast<Key*>(scratch);
+        uint32_t* const sv = VW ? reinterpret_cast<uint32_t*>(scratch + val_at) : nullptr;
+        SegDesc* const desc = reinterpret_cast<SegDesc*>(scratch + desc_at);
+        Key* bufk[2] = {static_cast<Key*>(out_k), sk};
+        uint32_t* bufv[2] = {static_cast<uint32_t*>(out_v), sv};
+        int cur = passes % 2;  // block sort target: the last pass then writes out
+        hipLaunchKernelGGL((block_sort_kernel<kThreads, kItems, VW, ORDER>),
+                           dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, stream,
+                           static_cast<const Key*>(in_k), static_cast<const uint32_t*>(in_v), N,
+                           bufk[cur], bufv[cur]);
+        hipError_t e = hipGetLastError();
+        rc = e == hipSuccess ? OMERGE_OK : hip_fail(e);
+        for (int64_t run = kTile; rc == OMERGE_OK && run < N; run *= 2) {
+            const int64_t per_pair = ceil_div(2 * run, sl);
+            const int64_t full = N / (2 * run), rem = N - full * 2 * run;
+            const int64_t segs = full * per_pair + (rem > 0 ? ceil_div(rem, sl) : 0);
+            const int64_t blocks = ceil_div((segs + 1) * kPartLanes, 256);
+            hipLaunchKernelGGL((plan_runs_kernel<kPartLanes, ORDER>),
+                               dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                               bufk[cur], N, run, sl, per_pair, segs, desc);
+            e = hipGetLastError();
+            rc = e == hipSuccess ? OMERGE_OK : hip_fail(e);
+            if (rc == OMERGE_OK)
+                rc = merge_desc(bufk[cur], bufv[cur], N, bufk[cur], bufv[cur], N, desc, segs, sl,
+                                bufk[1 - cur], bufv[1 - cur], N, stream);
+            cur = 1 - cur;
+        }
+        if (scratch) {
+            e = hipFreeAsync(scratch, stream);
+            if (rc == OMERGE_OK && e != hipSuccess) rc = hip_fail(e);
+        }
+        return rc;
     }
 
     // Whole merge: partition into stream-ordered scratch, then merge.
@@ -312,6 +427,66 @@ int merge_ordered(int order, const void* A, const void* Av, int64_t m, const voi
 #undef OMERGE_CASE
 }
 
+template <int VW, int ORDER>
+int batched_for(const void* A, const void* Av, const int64_t* a_off, int64_t m, const void* B,
+                const void* Bv, const int64_t* b_off, int64_t n, int64_t pairs, void* C,
+                void* Cv, hipStream_t stream) {
+    return Path<VW, ORDER>::batched(A, Av, a_off, m, B, Bv, b_off, n, pairs, C, Cv, stream);
+}
+
+template <int VW>
+int batched_ordered(int order, const void* A, const void* Av, const int64_t* a_off, int64_t m,
+                    const void* B, const void* Bv, const int64_t* b_off, int64_t n,
+                    int64_t pairs, void* C, void* Cv, hipStream_t stream) {
+#define OMERGE_CASE(o) \
+    case o: return batched_for<VW, o>(A, Av, a_off, m, B, Bv, b_off, n, pairs, C, Cv, stream);
+    switch (order) {
+        OMERGE_CASE(kKeyI32)
+        OMERGE_CASE(kKeyU32)
+        OMERGE_CASE(kKeyF32)
+        OMERGE_CASE(kKeyI64)
+        OMERGE_CASE(kKeyU64)
+        OMERGE_CASE(kKeyF64)
+        OMERGE_CASE(kKeyI32 | kKeyDescending)
+        OMERGE_CASE(kKeyU32 | kKeyDescending)
+        OMERGE_CASE(kKeyF32 | kKeyDescending)
+        OMERGE_CASE(kKeyI64 | kKeyDescending)
+        OMERGE_CASE(kKeyU64 | kKeyDescending)
+        OMERGE_CASE(kKeyF64 | kKeyDescending)
+        default: return OMERGE_INVALID_ARG;
+    }
+#undef OMERGE_CASE
+}
+
+template <int VW, int ORDER>
+int sort_for(const void* in_k, const void* in_v, void* out_k, void* out_v, int64_t n,
+             hipStream_t stream) {
+    return Path<VW, ORDER>::sort(in_k, in_v, out_k, out_v, n, stream);
+}
+
+template <int VW>
+int sort_ordered(int order, const void* in_k, const void* in_v, void* out_k, void* out_v,
+                 int64_t n, hipStream_t stream) {
+#define OMERGE_CASE(o) \
+    case o: return sort_for<VW, o>(in_k, in_v, out_k, out_v, n, stream);
+    switch (order) {
+        OMERGE_CASE(kKeyI32)
+        OMERGE_CASE(kKeyU32)
+        OMERGE_CASE(kKeyF32)
+        OMERGE_CASE(kKeyI64)
+        OMERGE_CASE(kKeyU64)
+        OMERGE_CASE(kKeyF64)
+        OMERGE_CASE(kKeyI32 | kKeyDescending)
+        OMERGE_CASE(kKeyU32 | kKeyDescending)
+        OMERGE_CASE(kKeyF32 | kKeyDescending)
+        OMERGE_CASE(kKeyI64 | kKeyDescending)
+        OMERGE_CASE(kKeyU64 | kKeyDescending)
+        OMERGE_CASE(kKeyF64 | kKeyDescending)
+        default: return OMERGE_INVALID_ARG;
+    }
+#undef OMERGE_CASE
+}
+
 using PathI32 = Path<0, kKeyI32>;
 using PathKV = Path<1, kKeyI32>;
 
@@ -357,6 +532,69 @@ int omerge_merge_pairs(const void* A_keys, const void* A_vals, int64_t m,
         return merge_ordered<1>(order, A_keys, A_vals, m, B_keys, B_vals, n, C_keys, C_vals,
                                 stream);
     return merge_ordered<2>(order, A_keys, A_vals, m, B_keys, B_vals, n, C_keys, C_vals, stream);
+}
+
+int omerge_merge_batched(const void* A_keys, const void* A_vals, const int64_t* a_offsets,
+                         int64_t m, const void* B_keys, const void* B_vals,
+                         const int64_t* b_offsets, int64_t n, int64_t num_merges, void* C_keys,
+                         void* C_vals, int order, int payload_bytes, hipStream_t stream) {
+    if (!valid_order(order) || (payload_bytes != 0 && payload_bytes != 4 && payload_bytes != 8))
+        return OMERGE_INVALID_ARG;
+    int rc = check_merge_args(A_keys, A_vals, m, B_keys, B_vals, n, C_keys, C_vals,
+                              key_bytes(order), payload_bytes);
+    if (rc != OMERGE_OK) return rc;
+    if (num_merges < 0 || (m + n > 0 && num_merges == 0)) return OMERGE_INVALID_ARG;
+    if (num_merges > kMaxGridBlocks) return OMERGE_OVERFLOW;
+    if (m + n == 0) return OMERGE_OK;
+    if (bad_array(a_offsets, num_merges + 1, 8) || bad_array(b_offsets, num_merges + 1, 8))
+        return OMERGE_INVALID_ARG;
+    const int64_t off_bytes = (num_merges + 1) * 8;
+    const void* outs[2] = {C_keys, C_vals};
+    const int64_t out_bytes[2] = {(m + n) * key_bytes(order), (m + n) * payload_bytes};
+    for (int i = 0; i < 2; ++i) {
+        if (overlaps(outs[i], out_bytes[i], a_offsets, off_bytes) ||
+            overlaps(outs[i], out_bytes[i], b_offsets, off_bytes))
+            return OMERGE_INVALID_ARG;
+    }
+    if (payload_bytes == 0)
+        return batched_ordered<0>(order, A_keys, nullptr, a_offsets, m, B_keys, nullptr,
+                                  b_offsets, n, num_merges, C_keys, nullptr, stream);
+    if (payload_bytes == 4)
+        return batched_ordered<1>(order, A_keys, A_vals, a_offsets, m, B_keys, B_vals,
+                                  b_offsets, n, num_merges, C_keys, C_vals, stream);
+    return batched_ordered<2>(order, A_keys, A_vals, a_offsets, m, B_keys, B_vals, b_offsets, n,
+                              num_merges, C_keys, C_vals, stream);
+}
+
+int omerge_sort(const void* keys_in, const void* vals_in, void* keys_out, void* vals_out,
+                int64_t n, int order, int payload_bytes, hipStream_t stream) {
+    if (!valid_order(order) || (payload_bytes != 0 && payload_bytes != 4 && payload_bytes != 8))
+        return OMERGE_INVALID_ARG;
+    if (n < 0) return OMERGE_INVALID_ARG;
+    if (n > kMaxTotal) return OMERGE_OVERFLOW;
+    const int kb = key_bytes(order), vb = payload_bytes;
+    if (bad_array(keys_in, n, kb) || bad_array(keys_out, n, kb)) return OMERGE_INVALID_ARG;
+    if (vb && (bad_array(vals_in, n, vb) || bad_array(vals_out, n, vb))) return OMERGE_INVALID_ARG;
+    // Outputs: disjoint from each other; each input is either its own output
+    // (in place) or disjoint from both outputs.
+    if (overlaps(keys_out, n * kb, vals_out, n * vb)) return OMERGE_INVALID_ARG;
+    const void* ins[2] = {keys_in, vals_in};
+    const int64_t in_bytes[2] = {n * kb, n * vb};
+    const void* same[2] = {keys_out, vals_out};
+    for (int i = 0; i < 2; ++i) {
+        if (in_bytes[i] == 0 || ins[i] == same[i]) {
+            if (overlaps(ins[i], in_bytes[i], same[1 - i], in_bytes[1 - i]))
+                return OMERGE_INVALID_ARG;
+            continue;
+        }
+        if (overlaps(ins[i], in_bytes[i], keys_out, n * kb) ||
+            overlaps(ins[i], in_bytes[i], vals_out, n * vb))
+            return OMERGE_INVALID_ARG;
+    }
+    if (n == 0) return OMERGE_OK;
+    if (vb == 0) return sort_ordered<0>(order, keys_in, nullptr, keys_out, nullptr, n, stream);
+    if (vb == 4) return sort_ordered<1>(order, keys_in, vals_in, keys_out, vals_out, n, stream);
+    return sort_ordered<2>(order, keys_in, vals_in, keys_out, vals_out, n, stream);
 }
 
 int omerge_co_rank(const int32_t* A, int64_t m, const int32_t* B, int64_t n,

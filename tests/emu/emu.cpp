@@ -9,7 +9,7 @@
 #include <vector>
 
 #include "hip/hip_runtime.h"
-#include "merge_kernel.hpp"
+#include "batch_kernel.hpp"
 
 thread_local EmuDim3 threadIdx;
 thread_local EmuDim3 blockIdx;
@@ -74,7 +74,7 @@ static void typed_cfg(const void* A, const void* Av, int64_t m, const void* B, c
     run_grid(count - 1, T, [&] {
         omerge::merge_segments_kernel<T, I, VW, ORDER>(
             a, static_cast<const uint32_t*>(Av), m, b, static_cast<const uint32_t*>(Bv), n, part,
-            seg_len, static_cast<Key*>(C), static_cast<uint32_t*>(Cv));
+            seg_len, static_cast<Key*>(C), static_cast<uint32_t*>(Cv), nullptr, m + n);
     });
 }
 
@@ -115,6 +115,129 @@ static bool typed_go(int variant, const void* A, const void* Av, int64_t m, cons
     return false;
 }
 
+// The merge-sort pipeline of the library (block sort, then plan + merge per
+// pass, ping-pong between out and a scratch copy), for one shape.
+template <int T, int I, int VW, int ORDER>
+static void sort_cfg(const void* in_k, const void* in_v, int64_t N, void* out_k, void* out_v,
+                     int64_t seg_len) {
+    using Key = typename omerge::KeyOrder<ORDER>::T;
+    constexpr int kTile = T * I;
+    if (N == 0) return;
+    int passes = 0;
+    for (int64_t run = kTile; run < N; run *= 2) ++passes;
+    // One scratch block laid out as the library lays out its own: keys, then
+    // payloads at the next 256-byte boundary.
+    const size_t key_bytes = static_cast<size_t>(N) * sizeof(Key);
+    const size_t val_at = (key_bytes + 255) & ~size_t(255);
+    std::vector<uint64_t> block((val_at + static_cast<size_t>(N) * 4 * VW) / 8 + 1);
+    char* const scratch = reinterpret_cast<char*>(block.data());
+    Key* bufk[2] = {static_cast<Key*>(out_k), reinterpret_cast<Key*>(scratch)};
+    uint32_t* bufv[2] = {static_cast<uint32_t*>(out_v),
+                         VW ? reinterpret_cast<uint32_t*>(scratch + val_at) : nullptr};
+    int cur = passes % 2;
+    const int64_t tiles = (N + kTile - 1) / kTile;
+    run_grid(tiles, T, [&] {
+        omerge::block_sort_kernel<T, I, VW, ORDER>(static_cast<const Key*>(in_k),
+                                                   static_cast<const uint32_t*>(in_v), N,
+                                                   bufk[cur], bufv[cur]);
+    });
+    for (int64_t run = kTile; run < N; run *= 2) {
+        const int64_t per_pair = (2 * run + seg_len - 1) / seg_len;
+        const int64_t full = N / (2 * run), rem = N - full * 2 * run;
+        const int64_t segs = full * per_pair + (rem > 0 ? (rem + seg_len - 1) / seg_len : 0);
+        std::vector<omerge::SegDesc> desc(segs);
+        for (auto& d : desc) d = {-1, -1, -1, -1, -1};
+        run_grid(((segs + 1) * 4 + 255) / 256, 256, [&] {
+            omerge::plan_runs_kernel<4, ORDER>(bufk[cur], N, run, seg_len, per_pair, segs,
+                                               desc.data());
+        });
+        run_grid(segs, T, [&] {
+            omerge::merge_segments_kernel<T, I, VW, ORDER, true>(
+                bufk[cur], bufv[cur], N, bufk[cur], bufv[cur], N, nullptr, seg_len,
+                bufk[1 - cur], bufv[1 - cur], desc.data(), N);
+        });
+        cur = 1 - cur;
+    }
+}
+
+// The library's batched merge for one shape.
+template <int T, int I, int VW, int ORDER>
+static void batched_cfg(const void* A, const void* Av, const int64_t* a_off, int64_t m,
+                        const void* B, const void* Bv, const int64_t* b_off, int64_t n,
+                        int64_t pairs, int64_t seg_len, void* C, void* Cv) {
+    using Key = typename omerge::KeyOrder<ORDER>::T;
+    const int64_t total = m + n;
+    if (total == 0) return;
+    const int64_t segs = pairs + (total + seg_len - 1) / seg_len - 1;
+    std::vector<omerge::SegDesc> desc(segs);
+    for (auto& d : desc) d = {-1, -1, -1, -1, -1};
+    const Key* a = static_cast<const Key*>(A);
+    const Key* b = static_cast<const Key*>(B);
+    run_grid(((segs + 1) * 4 + 255) / 256, 256, [&] {
+        omerge::plan_batched_kernel<4, ORDER>(a, a_off, m, b, b_off, n, pairs, seg_len, segs,
+                                              desc.data());
+    });
+    run_grid(segs, T, [&] {
+        omerge::merge_segments_kernel<T, I, VW, ORDER, true>(
+            a, static_cast<const uint32_t*>(Av), m, b, static_cast<const uint32_t*>(Bv), n,
+            nullptr, seg_len, static_cast<Key*>(C), static_cast<uint32_t*>(Cv), desc.data(),
+            total);
+    });
+}
+
+// Which (order, payload) combinations the sort / batch entries hold: the
+// small shapes for int32 keys-only, float32 descending with 4-byte payloads,
+// int64 with 8-byte payloads and float64 descending keys-only; the library
+// shapes for int32 keys-only and float64 descending with 4-byte payloads.
+constexpr bool emu_sort_has(int variant, int order, int vw) {
+    if (variant == 0)
+        return (order == 0 && (vw == 0 || vw == 2)) || (order == (5 | 8) && vw == 1);
+    return (order == 0 && (vw == 0 || vw == 2)) || (order == (2 | 8) && vw == 1) ||
+           (order == 3 && vw == 2) || (order == (5 | 8) && vw == 0);
+}
+
+template <int ORDER, int VW>
+static int sort_go(int variant, const void* in_k, const void* in_v, int64_t N, void* out_k,
+                   void* out_v, int64_t seg_len) {
+    if constexpr (emu_sort_has(1, ORDER, VW)) {
+        if (variant == 1) {
+            sort_cfg<128, 4, VW, ORDER>(in_k, in_v, N, out_k, out_v, seg_len);
+            return 1;
+        }
+    }
+    if constexpr (emu_sort_has(0, ORDER, VW)) {
+        if (variant == 0) {
+            constexpr int kw = omerge::KeyOrder<ORDER>::kWords;
+            sort_cfg<256, production_items(kw, VW), VW, ORDER>(in_k, in_v, N, out_k, out_v,
+                                                               seg_len);
+            return 1;
+        }
+    }
+    return 0;
+}
+
+template <int ORDER, int VW>
+static int batched_go(int variant, const void* A, const void* Av, const int64_t* a_off,
+                      int64_t m, const void* B, const void* Bv, const int64_t* b_off, int64_t n,
+                      int64_t pairs, int64_t seg_len, void* C, void* Cv) {
+    if constexpr (emu_sort_has(1, ORDER, VW)) {
+        if (variant == 1) {
+            batched_cfg<128, 4, VW, ORDER>(A, Av, a_off, m, B, Bv, b_off, n, pairs, seg_len, C,
+                                           Cv);
+            return 1;
+        }
+    }
+    if constexpr (emu_sort_has(0, ORDER, VW)) {
+        if (variant == 0) {
+            constexpr int kw = omerge::KeyOrder<ORDER>::kWords;
+            batched_cfg<256, production_items(kw, VW), VW, ORDER>(A, Av, a_off, m, B, Bv, b_off,
+                                                                  n, pairs, seg_len, C, Cv);
+            return 1;
+        }
+    }
+    return 0;
+}
+
 template <int ORDER>
 static bool typed_order(int variant, int vw, const void* A, const void* Av, int64_t m,
                         const void* B, const void* Bv, int64_t n, int64_t seg_len, int64_t* part,
@@ -133,7 +256,8 @@ static void merge_cfg(const int32_t* A, const uint32_t* Av, int64_t m, const int
                       int32_t* C, uint32_t* Cv) {
     const int64_t segs = (m + n + seg_len - 1) / seg_len;
     run_grid(segs, T, [&] {
-        omerge::merge_segments_kernel<T, I, VW, 0>(A, Av, m, B, Bv, n, part, seg_len, C, Cv);
+        omerge::merge_segments_kernel<T, I, VW, 0>(A, Av, m, B, Bv, n, part, seg_len, C, Cv,
+                                                   nullptr, m + n);
     });
 }
 
@@ -217,6 +341,41 @@ int emu_merge_typed(int variant, int order, int vw, const void* A, const void* A
         default: return 0;
     }
 #undef EMU_ORDER
+}
+
+// The merge sort (block sort + passes) for an order and payload width;
+// returns 0 if this library does not hold the combination (emu_sort_has).
+int emu_sort(int variant, int order, int vw, const void* in_k, const void* in_v, int64_t n,
+             void* out_k, void* out_v, int64_t seg_len) {
+#define EMU_SORT(o, w) \
+    if (order == o && vw == w) return sort_go<o, w>(variant, in_k, in_v, n, out_k, out_v, seg_len);
+    EMU_SORT(0, 0)
+    EMU_SORT(0, 2)
+    EMU_SORT(10, 1)
+    EMU_SORT(3, 2)
+    EMU_SORT(13, 0)
+    EMU_SORT(13, 1)
+#undef EMU_SORT
+    return 0;
+}
+
+// The batched merge for an order and payload width (same combinations).
+int emu_batched(int variant, int order, int vw, const void* A, const void* Av,
+                const int64_t* a_off, int64_t m, const void* B, const void* Bv,
+                const int64_t* b_off, int64_t n, int64_t pairs, int64_t seg_len, void* C,
+                void* Cv) {
+#define EMU_BATCH(o, w)                                                                       \
+    if (order == o && vw == w)                                                                \
+        return batched_go<o, w>(variant, A, Av, a_off, m, B, Bv, b_off, n, pairs, seg_len, C, \
+                                Cv);
+    EMU_BATCH(0, 0)
+    EMU_BATCH(0, 2)
+    EMU_BATCH(10, 1)
+    EMU_BATCH(3, 2)
+    EMU_BATCH(13, 0)
+    EMU_BATCH(13, 1)
+#undef EMU_BATCH
+    return 0;
 }
 
 // Tile size (outputs) of a typed shape.

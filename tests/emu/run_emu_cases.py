@@ -32,6 +32,10 @@ def load(path):
     lib.emu_direct.argtypes = [p, i64, p, i64, p, i64, i32]
     lib.emu_merge_typed.argtypes = [i32, i32, i32, p, p, i64, p, p, i64, i64, p, p, p]
     lib.emu_merge_typed.restype = i32
+    lib.emu_sort.argtypes = [i32, i32, i32, p, p, i64, p, p, i64]
+    lib.emu_sort.restype = i32
+    lib.emu_batched.argtypes = [i32, i32, i32, p, p, p, i64, p, p, p, i64, i64, i64, p, p]
+    lib.emu_batched.restype = i32
     lib.emu_typed_tile.argtypes = [i32, i32, i32]
     lib.emu_typed_tile.restype = i32
     return lib
@@ -347,7 +351,99 @@ def group_orders(r, g):
     r.check(ran >= 40, ("typed combinations run", ran))
 
 
-GROUPS = {"orders": group_orders, "small": group_small, "direct": group_direct, "skew": group_skew, "blocks": group_blocks,
+SORT_COMBOS = [(1, 0, 0), (1, 0, 2), (1, 10, 1), (1, 3, 2), (1, 13, 0), (0, 0, 0), (0, 0, 2),
+               (0, 13, 1)]
+
+
+def unsorted_keys(g, dtype, n, pools):
+    """Unsorted keys with many ties (integers) or specials (floats)."""
+    if dtype in (np.float32, np.float64):
+        pool = pools[dtype]
+        return pool[g.integers(0, min(len(pool), int(g.choice([5, len(pool)]))), size=n)]
+    info = np.iinfo(dtype)
+    if g.random() < 0.5:
+        return g.integers(-3 if info.min < 0 else 0, 4, size=n).astype(dtype)
+    return g.integers(info.min, info.max, size=n, dtype=dtype, endpoint=True)
+
+
+def group_sort(r, g):
+    """The merge sort (block sort, then plan + descriptor merges per pass)
+    against the oracle's stable sort: sizes around tile multiples, several
+    segment lengths (many segments per pair, or one), in place and not."""
+    pools = {np.float32: float_pool(g, np.float32), np.float64: float_pool(g, np.float64)}
+    for variant, order, vw in SORT_COMBOS:
+        dtype = KIND_DTYPE[order & 7]
+        desc = bool(order & 8)
+        tile = r.lib.emu_typed_tile(variant, order, vw)
+        sizes = [0, 1, 5, tile - 1, tile, tile + 1, 2 * tile + 3] + \
+            [int(x) for x in g.integers(3 * tile, 9 * tile, size=2 if variant else 1)]
+        for c, n in enumerate(sizes):
+            K = np.ascontiguousarray(unsorted_keys(g, dtype, n, pools))
+            vdt = np.uint64 if vw == 2 else np.uint32
+            V = (np.arange(n, dtype=vdt) * vdt(3) + vdt(1)).astype(vdt)
+            seg_len = int(g.choice([tile, 3 * tile, 9 * tile, 100, 4 * int(g.integers(1, 200))]))
+            in_place = c % 3 == 2
+            outk = K.copy() if in_place else np.zeros_like(K)
+            outv = V.copy() if in_place else np.zeros_like(V)
+            src_k = outk if in_place else K
+            src_v = outv if in_place else V
+            held = r.lib.emu_sort(variant, order, vw, ptr(src_k), ptr(src_v) if vw else None, n,
+                                  ptr(outk), ptr(outv) if vw else None, seg_len)
+            r.check(held == 1, ("sort combo held", variant, order, vw))
+            if vw:
+                wk, wv = oracle.sort(K, V, descending=desc)
+                ok = np.array_equal(outk.view(np.uint8), wk.view(np.uint8)) and \
+                    np.array_equal(outv, wv)
+            else:
+                wk = oracle.sort(K, descending=desc)
+                ok = np.array_equal(outk.view(np.uint8), wk.view(np.uint8))
+            r.check(ok, ("sort", variant, order, vw, n, seg_len, in_place))
+
+
+def group_batched(r, g):
+    """Batches of merges (empty merges and sides, tiny and multi-segment
+    merges, merges much longer than a segment) against the oracle."""
+    pools = {np.float32: float_pool(g, np.float32), np.float64: float_pool(g, np.float64)}
+    for variant, order, vw in SORT_COMBOS:
+        dtype = KIND_DTYPE[order & 7]
+        desc = bool(order & 8)
+        tile = r.lib.emu_typed_tile(variant, order, vw)
+        for c in range(4 if variant else 2):
+            pairs = int(g.choice([1, 3, 40, 300]))
+            scale = int(g.choice([3, tile // 2, 3 * tile]))
+            la = g.integers(0, scale + 1, size=pairs) * (g.random(pairs) > 0.15)
+            lb = g.integers(0, scale + 1, size=pairs) * (g.random(pairs) > 0.15)
+            a_off = np.concatenate([[0], np.cumsum(la)]).astype(np.int64)
+            b_off = np.concatenate([[0], np.cumsum(lb)]).astype(np.int64)
+            m, n = int(a_off[-1]), int(b_off[-1])
+            A = np.empty(m, dtype=dtype)
+            B = np.empty(n, dtype=dtype)
+            for p in range(pairs):
+                a, b = typed_sorted_pair(g, dtype, desc, int(la[p]), int(lb[p]), pools)
+                A[a_off[p]:a_off[p + 1]] = a
+                B[b_off[p]:b_off[p + 1]] = b
+            vdt = np.uint64 if vw == 2 else np.uint32
+            top = vdt(1 << (63 if vw == 2 else 31))
+            Av = np.arange(m, dtype=vdt)
+            Bv = (top + np.arange(n, dtype=vdt)).astype(vdt)
+            seg_len = int(g.choice([tile, 3 * tile, 100, 4 * int(g.integers(1, 300))]))
+            Ck = np.zeros(m + n, dtype=dtype)
+            Cv = np.zeros(m + n, dtype=vdt)
+            held = r.lib.emu_batched(variant, order, vw, ptr(A), ptr(Av) if vw else None,
+                                     ptr(a_off), m, ptr(B), ptr(Bv) if vw else None, ptr(b_off),
+                                     n, pairs, seg_len, ptr(Ck), ptr(Cv) if vw else None)
+            r.check(held == 1, ("batched combo held", variant, order, vw))
+            if vw:
+                wk, wv = oracle.merge_batched(A, a_off, B, b_off, Av, Bv, descending=desc)
+                ok = np.array_equal(Ck.view(np.uint8), wk.view(np.uint8)) and \
+                    np.array_equal(Cv, wv)
+            else:
+                wk = oracle.merge_batched(A, a_off, B, b_off, descending=desc)
+                ok = np.array_equal(Ck.view(np.uint8), wk.view(np.uint8))
+            r.check(ok, ("batched", variant, order, vw, pairs, m, n, seg_len))
+
+
+GROUPS = {"sort": group_sort, "batched": group_batched, "orders": group_orders, "small": group_small, "direct": group_direct, "skew": group_skew, "blocks": group_blocks,
           "production": group_production, "unsorted": group_unsorted}
 
 if __name__ == "__main__":

@@ -593,6 +593,131 @@ def pin_integer64_kinds_sorted(orc, seed: int = 67, cases: int = 16) -> None:
         assert np.array_equal(orc.merge_keys(A, B, desc), want)
 
 
+# ---------------------------------------------- batched merges and the sort
+
+
+def _rank_of(dtype, descending):
+    """Python rank key of one key value, for brute force: integers by value,
+    floats by position in the hand-written totalOrder tables (only table
+    values are drawn), reversed for descending."""
+    if np.dtype(dtype).kind == "f":
+        table = F32_TOTAL_ORDER if np.dtype(dtype) == np.float32 else F64_TOTAL_ORDER
+        bits = np.uint32 if np.dtype(dtype) == np.float32 else np.uint64
+        pos = {b: r for r, (b, _) in enumerate(table)}
+        key = lambda x: pos[int(np.asarray(x, dtype=dtype).view(bits))]
+    else:
+        key = lambda x: int(x)
+    return (lambda x: -key(x)) if descending else key
+
+
+def _draw_keys(g, dtype, size):
+    if np.dtype(dtype).kind == "f":
+        table = F32_TOTAL_ORDER if np.dtype(dtype) == np.float32 else F64_TOTAL_ORDER
+        bits = np.uint32 if np.dtype(dtype) == np.float32 else np.uint64
+        pick = np.array([b for b, _ in table], dtype=bits)
+        return pick[g.integers(0, len(pick), size=size)].view(dtype)
+    info = np.iinfo(dtype)
+    pool = np.array([info.min, info.min + 1, 0, 1, info.max - 1, info.max], dtype=dtype)
+    mixed = np.concatenate([pool, g.integers(info.min, info.max, size=4, dtype=dtype,
+                                             endpoint=True)])
+    return mixed[g.integers(0, mixed.size, size=size)]
+
+
+def pin_sort_brute(orc, seed: int = 71, cases: int = 240) -> None:
+    """Stable sort against Python's stable sorted() of (rank, input index),
+    every key type, both orders, with 4- and 8-byte payload tags."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    dtypes = [np.int32, np.uint32, np.float32, np.int64, np.uint64, np.float64]
+    for c in range(cases):
+        dtype = dtypes[c % len(dtypes)]
+        desc = bool((c // len(dtypes)) & 1)
+        n = int(g.integers(0, 40))
+        K = _draw_keys(g, dtype, n)
+        rank = _rank_of(dtype, desc)
+        order = sorted(range(n), key=lambda t: rank(K[t]))
+        got = orc.sort(K, descending=desc)
+        assert np.array_equal(got.view(np.uint8), K[order].view(np.uint8))
+        for vdt in (np.uint32, np.uint64):
+            V = np.arange(n, dtype=vdt) + vdt(7)
+            gk, gv = orc.sort(K, V, descending=desc)
+            assert np.array_equal(gv, V[order])
+            assert np.array_equal(gk.view(np.uint8), K[order].view(np.uint8))
+
+
+def pin_sort_numpy(orc, seed: int = 73, cases: int = 12) -> None:
+    """Larger sorts against numpy's stable argsort (descending: of the
+    negated keys, in int64 for integers, for finite floats as is)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    for c in range(cases):
+        dtype = [np.int32, np.float32, np.int64, np.float64][c % 4]
+        desc = bool(c & 4)
+        n = int(g.integers(1, 30000))
+        if np.dtype(dtype).kind == "f":
+            K = (g.standard_normal(n) * 100).round(1).astype(dtype)
+            K[K == 0] = 0.0
+            key = -K if desc else K
+        else:
+            K = g.integers(-50, 50, size=n).astype(dtype)
+            key = -K.astype(np.int64) if desc else K
+        idx = np.argsort(key, kind="stable")
+        V = np.arange(n, dtype=np.uint32)
+        gk, gv = orc.sort(K, V, descending=desc)
+        assert np.array_equal(gk, K[idx]) and np.array_equal(gv, V[idx])
+
+
+def pin_sort_permutation_of_tiny(orc) -> None:
+    """Every arrangement of a small multiset sorts to the same keys, and the
+    payloads of equal keys keep their input order (exhaustive, n <= 6)."""
+    import itertools
+    for keys in ([3, 1, 2, 1, 3, 1], [5, 5, 5, 5], [2, 1, 0, -1, -2, 7]):
+        want = sorted(keys)
+        for perm in set(itertools.permutations(keys)):
+            K = np.array(perm, dtype=np.int32)
+            V = np.arange(len(perm), dtype=np.uint32)
+            gk, gv = orc.sort(K, V)
+            assert gk.tolist() == want
+            for a, b in zip(range(len(perm)), range(1, len(perm))):
+                if gk[a] == gk[b]:
+                    assert gv[a] < gv[b]
+
+
+def pin_batched_against_pairs(orc, seed: int = 79, cases: int = 60) -> None:
+    """A batch of merges equals, merge by merge, numpy's stable sort of that
+    merge's A||B (ties: A first, then input order), placed one after
+    another; empty merges and empty sides included."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    for c in range(cases):
+        pairs = int(g.integers(1, 12))
+        desc = bool(c & 1)
+        la = g.integers(0, 30, size=pairs) * (g.random(pairs) > 0.2)
+        lb = g.integers(0, 30, size=pairs) * (g.random(pairs) > 0.2)
+        a_off = np.concatenate([[0], np.cumsum(la)]).astype(np.int64)
+        b_off = np.concatenate([[0], np.cumsum(lb)]).astype(np.int64)
+        A = np.empty(int(a_off[-1]), dtype=np.int32)
+        B = np.empty(int(b_off[-1]), dtype=np.int32)
+        want = []
+        want_tags = []
+        for p in range(pairs):
+            a = np.sort(g.integers(-5, 5, size=int(la[p]))).astype(np.int32)
+            b = np.sort(g.integers(-5, 5, size=int(lb[p]))).astype(np.int32)
+            if desc:
+                a, b = a[::-1].copy(), b[::-1].copy()
+            A[a_off[p]:a_off[p + 1]] = a
+            B[b_off[p]:b_off[p + 1]] = b
+            cat = np.concatenate([a, b])
+            tag = np.concatenate([a_off[p] + np.arange(a.size), (1 << 31) + b_off[p] +
+                                  np.arange(b.size)])
+            idx = np.argsort(-cat.astype(np.int64) if desc else cat, kind="stable")
+            want.append(cat[idx])
+            want_tags.append(tag[idx])
+        Av = np.arange(A.size, dtype=np.uint32)
+        Bv = (U31 + np.arange(B.size, dtype=np.uint32)).astype(np.uint32)
+        Ck, Cv = orc.merge_batched(A, a_off, B, b_off, Av, Bv, descending=desc)
+        assert np.array_equal(Ck, np.concatenate(want))
+        assert np.array_equal(Cv, np.concatenate(want_tags).astype(np.uint32))
+        assert np.array_equal(orc.merge_batched(A, a_off, B, b_off, descending=desc), Ck)
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_equal_element_case,
@@ -614,6 +739,10 @@ ALL_PINS = [
     pin_f64_numpy_finite,
     pin_integer64_kinds_brute,
     pin_integer64_kinds_sorted,
+    pin_sort_brute,
+    pin_sort_numpy,
+    pin_sort_permutation_of_tiny,
+    pin_batched_against_pairs,
 ]
 
 

@@ -152,6 +152,39 @@ def test_typed_entry_validation():
     assert re.search(r"#define OMERGE_DESCENDING 8\b", text)
 
 
+def test_batched_and_sort_validation():
+    lib = om.load_library()
+    a, av, b, bv = FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000
+    ck, cv, ao, bo = FAKE + 0x4000, FAKE + 0x5000, FAKE + 0x6000, FAKE + 0x7000
+    f = lib.omerge_merge_batched
+    assert f(P(a), P(av), P(ao), 4, P(b), P(bv), P(bo), 4, 2, P(ck), P(cv), 0, 3, P(0)) == \
+        M.INVALID_ARG                                                     # payload width
+    assert f(P(a), P(0), P(ao), 4, P(b), P(0), P(bo), 4, 0, P(ck), P(0), 0, 0, P(0)) == \
+        M.INVALID_ARG                                                     # no merges, data
+    assert f(P(a), P(0), P(ao + 4), 4, P(b), P(0), P(bo), 4, 2, P(ck), P(0), 0, 0, P(0)) == \
+        M.INVALID_ARG                                                     # offsets alignment
+    assert f(P(a), P(0), P(0), 4, P(b), P(0), P(bo), 4, 2, P(ck), P(0), 0, 0, P(0)) == \
+        M.INVALID_ARG                                                     # offsets NULL
+    assert f(P(a), P(0), P(ck + 8), 4, P(b), P(0), P(bo), 4, 2, P(ck), P(0), 0, 0, P(0)) == \
+        M.INVALID_ARG                                                     # C over offsets
+    assert f(P(a), P(0), P(ao), 4, P(b), P(0), P(bo), 4, 2, P(a + 4), P(0), 0, 0, P(0)) == \
+        M.INVALID_ARG                                                     # C over A
+    assert f(P(a), P(0), P(ao), 4, P(b), P(0), P(bo), 4, 2, P(ck), P(0), 7, 0, P(0)) == \
+        M.INVALID_ARG                                                     # order
+    assert f(P(0), P(0), P(0), 0, P(0), P(0), P(0), 0, 0, P(0), P(0), 0, 0, P(0)) == M.OK
+    assert f(P(0), P(0), P(0), 0, P(0), P(0), P(0), 0, 5, P(0), P(0), 0, 0, P(0)) == M.OK
+    s = lib.omerge_sort
+    assert s(P(a), P(0), P(ck), P(0), -1, 0, 0, P(0)) == M.INVALID_ARG  # negative n
+    assert s(P(a), P(0), P(ck), P(0), 4, 6, 0, P(0)) == M.INVALID_ARG   # order
+    assert s(P(a), P(av), P(ck), P(cv), 4, 0, 2, P(0)) == M.INVALID_ARG  # payload width
+    assert s(P(a), P(0), P(a + 4), P(0), 4, 0, 0, P(0)) == M.INVALID_ARG  # partial overlap
+    assert s(P(a), P(av), P(ck), P(ck + 8), 4, 0, 4, P(0)) == M.INVALID_ARG  # outputs overlap
+    assert s(P(a), P(av), P(ck), P(a + 8), 4, 0, 4, P(0)) == M.INVALID_ARG  # vals out over keys in
+    assert s(P(a + 4), P(0), P(ck), P(0), 4, 3, 0, P(0)) == M.INVALID_ARG  # 64-bit misaligned
+    assert s(P(a), P(0), P(ck), P(0), 0, 0, 0, P(0)) == M.OK
+    assert s(P(0), P(0), P(0), P(0), 0, 13, 8, P(0)) == M.OK
+
+
 def test_order_code_of_dtypes():
     import torch
     assert om.order_code(torch.int32) == 0

@@ -447,6 +447,107 @@ def test_typed_large(dtype, desc):
         del gk, gv
 
 
+# ------------------------------------------------- batched merges and the sort
+
+
+def unsorted_typed(g, dtype, n):
+    """Unsorted keys: floats from the totalOrder pool (specials included),
+    integers with many ties or over the whole range."""
+    if dtype in (np.float32, np.float64):
+        pool = float_pool(dtype)
+        return pool[g.integers(0, pool.size, size=n)]
+    info = np.iinfo(dtype)
+    if g.random() < 0.5:
+        return g.integers(0, 40, size=n).astype(dtype)
+    return g.integers(info.min, info.max, size=n, dtype=dtype, endpoint=True)
+
+
+@pytest.mark.parametrize("dtype,desc", TYPED, ids=TYPED_IDS)
+def test_sort_keys_and_pairs(dtype, desc):
+    """Stable merge sort of every key type and order, keys only and with
+    4- and 8-byte payloads, around tile multiples and over many passes;
+    output bits against the oracle's stable sort."""
+    needs_torch_dtype(dtype)
+    g = np.random.Generator(np.random.PCG64(700 + TYPED.index((dtype, desc))))
+    for n in (0, 1, 1023, 1024, 2049, 4095, 4097, 70001, int(g.integers(100000, 300000))):
+        K = np.ascontiguousarray(unsorted_typed(g, dtype, n))
+        say("sort", np.dtype(dtype).name, desc, n)
+        got = om.sort(dev_typed(K), descending=desc)
+        assert_same(host_bits(got), as_bits(oracle.sort(K, descending=desc)), "sorted keys")
+        for vdt in (np.uint32, np.int64):
+            V = (np.arange(n) * 7 + 3).astype(vdt)
+            gk, gv = om.sort(dev_typed(K), dev_typed(V), descending=desc)
+            wk, wv = oracle.sort(K, V, descending=desc)
+            assert_same(host_bits(gk), as_bits(wk), "sorted pair keys")
+            assert_same(host_bits(gv), as_bits(wv), "sorted pair payloads")
+
+
+def test_sort_in_place_and_large():
+    """In-place sort (out = input), and 2^24 int32 keys with payloads (16
+    merge passes after the block sort)."""
+    g = np.random.Generator(np.random.PCG64(733))
+    K = g.integers(-(1 << 31), 1 << 31, size=300000, dtype=np.int64).astype(np.int32)
+    t = dev(K)
+    om.sort(t, out=t)
+    assert_same(host(t), oracle.sort(K), "in place")
+    n = 1 << 24
+    K = g.integers(0, 1 << 20, size=n).astype(np.int32)
+    V = np.arange(n, dtype=np.uint32)
+    say("sort large", n)
+    gk, gv = om.sort(dev(K), dev(V))
+    wk, wv = oracle.sort(K, V)
+    assert_same(host(gk), wk, "large sort keys")
+    assert_same(host(gv).view(np.uint32), wv, "large sort payloads")
+
+
+def batch_case(g, dtype, desc, pairs, scale):
+    la = g.integers(0, scale + 1, size=pairs) * (g.random(pairs) > 0.15)
+    lb = g.integers(0, scale + 1, size=pairs) * (g.random(pairs) > 0.15)
+    a_off = np.concatenate([[0], np.cumsum(la)]).astype(np.int64)
+    b_off = np.concatenate([[0], np.cumsum(lb)]).astype(np.int64)
+    A = np.empty(int(a_off[-1]), dtype=dtype)
+    B = np.empty(int(b_off[-1]), dtype=dtype)
+    for p in range(pairs):
+        a, b = typed_pair(g, dtype, desc, int(la[p]), int(lb[p]))
+        A[a_off[p]:a_off[p + 1]] = a
+        B[b_off[p]:b_off[p + 1]] = b
+    return A, a_off, B, b_off
+
+
+@pytest.mark.parametrize("dtype,desc", [(np.int32, False), (np.float32, True), (np.int64, True),
+                                        (np.uint64, False), (np.float64, False)],
+                         ids=["int32-asc", "float32-desc", "int64-desc", "uint64-asc",
+                              "float64-asc"])
+def test_batched_merges(dtype, desc):
+    """Batches of 1 to 3000 merges of mixed sizes (empty merges and sides,
+    merges shorter and much longer than a segment), keys and pairs."""
+    needs_torch_dtype(dtype)
+    g = np.random.Generator(np.random.PCG64(760 + [np.int32, np.float32, np.int64, np.uint64,
+                                                   np.float64].index(dtype)))
+    for pairs, scale in ((1, 90000), (7, 20000), (300, 900), (3000, 40)):
+        A, a_off, B, b_off = batch_case(g, dtype, desc, pairs, scale)
+        say("batched", np.dtype(dtype).name, desc, pairs, A.size, B.size)
+        da, db = dev(a_off), dev(b_off)
+        got = om.merge_batched(dev_typed(A), da, dev_typed(B), db, descending=desc)
+        want = oracle.merge_batched(A, a_off, B, b_off, descending=desc)
+        assert_same(host_bits(got), as_bits(want), "batched keys")
+        Av, Bv = tags64(A.size, B.size)
+        gk, gv = om.merge_batched(dev_typed(A), da, dev_typed(B), db, dev_typed(Av),
+                                  dev_typed(Bv), descending=desc)
+        wk, wv = oracle.merge_batched(A, a_off, B, b_off, Av, Bv, descending=desc)
+        assert_same(host_bits(gk), as_bits(wk), "batched pair keys")
+        assert_same(host_bits(gv), as_bits(wv), "batched pair payloads")
+
+
+def test_batched_single_merge_is_merge():
+    """A batch of one merge is the plain merge."""
+    g = np.random.Generator(np.random.PCG64(771))
+    A, B = pair(g, 1 << 22, 3 << 20, 1 << 20)
+    got = om.merge_batched(dev(A), dev(np.array([0, A.size], dtype=np.int64)), dev(B),
+                           dev(np.array([0, B.size], dtype=np.int64)))
+    assert_same(host(got), host(om.merge_i32(dev(A), dev(B))), "batch of one")
+
+
 # ------------------------------------------------------- full-size workloads
 
 @pytest.mark.parametrize("name", ORDER)

@@ -50,7 +50,7 @@ def libemu(request, tmp_path_factory):
 
 
 @pytest.mark.parametrize("group", ["small", "skew", "blocks", "direct", "production", "unsorted",
-                                   "orders"])
+                                   "orders", "sort", "batched"])
 def test_emulated_kernels_match_oracle(libemu, group):
     lib, rt = libemu
     env = dict(os.environ, LD_PRELOAD=rt, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1",

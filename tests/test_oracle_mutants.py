@@ -56,6 +56,11 @@ MUTANTS = {
                    "        return total_order_f64(x, x) && total_order_f32((uint32_t)(x >> 32), (uint32_t)(y >> 32));"),
     "key_size_64_for_f64_only": ("return kind >= KIND_I64 ? 8 : 4;", "return kind >= KIND_F64 ? 8 : 4;"),
     "payload_half_copied": ("memcpy(cv + vs * k, av + vs * i, vs);", "memcpy(cv + vs * k, av + vs * i, 4);"),
+    "sort_right_run_first": ("            merge_range(order, vs, src_k + ks * i, vs ? src_v + vs * i : 0,\n                        la, src_k + ks * (i + la),\n                        vs ? src_v + vs * (i + la) : 0, lb, dst_k + ks * i,",
+                             "            merge_range(order, vs, src_k + ks * (i + la),\n                        vs ? src_v + vs * (i + la) : 0, lb, src_k + ks * i,\n                        vs ? src_v + vs * i : 0, la, dst_k + ks * i,"),
+    "sort_last_pass_dropped": ("for (width = 1; width < n; width *= 2)",
+                               "for (width = 1; 2 * width < n; width *= 2)"),
+    "batched_output_at_a_offset": ("int64_t c0 = a0 + b0;", "int64_t c0 = a0 + (b0 > 0 ? b0 - 1 : 0);"),
     "typed_b_exhaustion_dropped": ("    if (j >= n)\n        return 1;\n    if (i < m && oracle_key_le",
                                    "    if (i < m && oracle_key_le"),
     "typed_payload_from_b": ("memcpy(cv + vs * k, av + vs * i, vs);",
