@@ -195,10 +195,49 @@ __device__ __forceinline__ void bitonic_sort(T (&x)[N], int (&pos)[N]) {
     }
 }
 
-template <int THREADS, int ITEMS>
-struct SortCfg {
-    static constexpr int kTile = THREADS * ITEMS;
-};
+// A lane's row of ITEMS elements (keys or int positions) to / from the
+// padded LDS layout of the merge stage (4 spare words after every 32), as
+// 16-byte accesses, which that padding keeps free of bank conflicts.
+template <int ITEMS, typename T>
+__device__ __forceinline__ void put_row(int* buf, int tid, const T (&x)[ITEMS]) {
+    constexpr int W = sizeof(T) / 4;
+    int* const row = buf + stage_word(tid * ITEMS * W);
+#pragma unroll
+    for (int v = 0; v < ITEMS * W / 4; ++v) {
+        int4v q;
+        if constexpr (W == 1) {
+            q.x = x[4 * v];
+            q.y = x[4 * v + 1];
+            q.z = x[4 * v + 2];
+            q.w = x[4 * v + 3];
+        } else {
+            q.x = low_word(x[2 * v]);
+            q.y = high_word(x[2 * v]);
+            q.z = low_word(x[2 * v + 1]);
+            q.w = high_word(x[2 * v + 1]);
+        }
+        *reinterpret_cast<int4v*>(row + 4 * v) = q;
+    }
+}
+
+template <int ITEMS, typename T>
+__device__ __forceinline__ void get_row(const int* buf, int tid, T (&x)[ITEMS]) {
+    constexpr int W = sizeof(T) / 4;
+    const int* const row = buf + stage_word(tid * ITEMS * W);
+#pragma unroll
+    for (int v = 0; v < ITEMS * W / 4; ++v) {
+        const int4v q = *reinterpret_cast<const int4v*>(row + 4 * v);
+        if constexpr (W == 1) {
+            x[4 * v] = q.x;
+            x[4 * v + 1] = q.y;
+            x[4 * v + 2] = q.z;
+            x[4 * v + 3] = q.w;
+        } else {
+            x[2 * v] = join_words(q.x, q.y);
+            x[2 * v + 1] = join_words(q.z, q.w);
+        }
+    }
+}
 
 template <int THREADS, int ITEMS, int VW, int ORDER>
 __global__ __launch_bounds__(THREADS) void block_sort_kernel(
@@ -210,10 +249,13 @@ __global__ __launch_bounds__(THREADS) void block_sort_kernel(
     constexpr bool KV = VW > 0;
     constexpr int kTile = THREADS * ITEMS;
     static_assert(ITEMS >= 4 && (ITEMS & (ITEMS - 1)) == 0, "ITEMS: a power of two");
-    // LDS: keys (padded as the merge stage), positions, payloads, splits.
-    constexpr int kKeyWords = kTile * KW + kTile * KW / 8;
+    // LDS: keys and positions, padded as the merge stage (the padding also
+    // spreads the runs' starts over the banks; unpadded, the lanes' run
+    // reads conflict badly), keys with ITEMS elements of slack for candidate
+    // reads past the last run; then payloads and splits.
+    constexpr int kKeyWords = stage_word((kTile + ITEMS) * KW);
     constexpr int kPos = kKeyWords;
-    constexpr int kPay = kPos + (KV ? kTile : 0);
+    constexpr int kPay = kPos + (KV ? stage_word(kTile) : 0);
     constexpr int kSplitAt = kPay + kTile * VW;
     __shared__ __attribute__((aligned(16))) int lds[kSplitAt + THREADS];
     int* const kbuf = lds;
@@ -224,18 +266,33 @@ __global__ __launch_bounds__(THREADS) void block_sort_kernel(
     const int tid = threadIdx.x;
     const int64_t t0 = blockIdx.x * static_cast<int64_t>(kTile);
     const int len = static_cast<int>(total - t0 < kTile ? total - t0 : kTile);
+    // Whole tiles of 16-byte-aligned arrays move as 16-byte vectors.
+    const bool vec_in = len == kTile && (reinterpret_cast<uintptr_t>(src + t0) & 15) == 0;
+    const bool vec_out = len == kTile && (reinterpret_cast<uintptr_t>(dst + t0) & 15) == 0;
 
-    // Load: lane tid takes elements tid, tid+THREADS, ... (coalesced).
+    // Load keys (coalesced) as order images; the tile's missing tail is the
+    // largest image.
+    if (vec_in) {
+        const int32_t* const w = reinterpret_cast<const int32_t*>(src + t0);
 #pragma unroll
-    for (int r = 0; r < ITEMS; ++r) {
-        const int e = tid + r * THREADS;
-        const Key x = e < len ? K::to_ord(src[t0 + e]) : K::kMax;
-        st_elem<Key>(kbuf, stage_word(KW * e), x);
-        if constexpr (KV) {
-            if (e < len) {
+        for (int r = 0; r < ITEMS * KW / 4; ++r) {
+            const int q = 4 * (tid + r * THREADS);
+            *reinterpret_cast<int4v*>(kbuf + stage_word(q)) =
+                map_vec<ORDER, true>(load_stream4(w + q));
+        }
+    } else {
 #pragma unroll
-                for (int v = 0; v < VW; ++v) vbuf[VW * e + v] = src_v[VW * (t0 + e) + v];
-            }
+        for (int r = 0; r < ITEMS; ++r) {
+            const int e = tid + r * THREADS;
+            const Key x = e < len ? K::to_ord(src[t0 + e]) : K::kMax;
+            st_elem<Key>(kbuf, stage_word(KW * e), x);
+        }
+    }
+    if constexpr (KV) {
+#pragma unroll
+        for (int r = 0; r < ITEMS * VW; ++r) {
+            const int w = tid + r * THREADS;
+            if (w < len * VW) vbuf[w] = src_v[VW * t0 + w];
         }
     }
     __syncthreads();
@@ -243,11 +300,9 @@ __global__ __launch_bounds__(THREADS) void block_sort_kernel(
     // Each lane sorts its row of ITEMS elements.
     Key x[ITEMS];
     int pos[ITEMS];
+    get_row<ITEMS>(kbuf, tid, x);
 #pragma unroll
-    for (int t = 0; t < ITEMS; ++t) {
-        x[t] = ld_elem<Key>(kbuf, stage_word(KW * (tid * ITEMS + t)));
-        pos[t] = tid * ITEMS + t;
-    }
+    for (int t = 0; t < ITEMS; ++t) pos[t] = tid * ITEMS + t;
     bitonic_sort<ITEMS, KV>(x, pos);
 
     // Merge rounds: runs of `run` elements merge pairwise into runs of 2*run.
@@ -255,11 +310,8 @@ __global__ __launch_bounds__(THREADS) void block_sort_kernel(
     // A on equal keys is the stable order.
     for (int run = ITEMS; run < kTile; run *= 2) {
         __syncthreads();  // every read of the previous round is done
-#pragma unroll
-        for (int t = 0; t < ITEMS; ++t) {
-            st_elem<Key>(kbuf, stage_word(KW * (tid * ITEMS + t)), x[t]);
-            if constexpr (KV) pbuf[tid * ITEMS + t] = pos[t];
-        }
+        put_row<ITEMS>(kbuf, tid, x);
+        if constexpr (KV) put_row<ITEMS>(pbuf, tid, pos);
         __syncthreads();
         const int lanes = 2 * run / ITEMS;   // lanes per merged pair
         const int u = tid % lanes;           // this lane's place in it
@@ -284,13 +336,25 @@ __global__ __launch_bounds__(THREADS) void block_sort_kernel(
         const int s = u > 0 ? split[tid - 1] : 0;  // A elements before this lane's outputs
         const int bs = u * ITEMS - s;
         if constexpr (!KV) {
+            // Candidates past a run's end read the next run (or the slack)
+            // and are replaced by the largest image.  ITEMS consecutive
+            // elements cross at most one 32-word pad: element t of a read
+            // starting at word w sits at stage_word(w) + KW*t, plus 4 once
+            // KW*t reaches the pad at 32 - (w & 31).
             Key a[ITEMS], b[ITEMS];
+            const int wa = KW * (a0 + s), wb = KW * (b0 + bs);
+            const int* const pa = kbuf + stage_word(wa);
+            const int* const pb = kbuf + stage_word(wb);
+            const int ca = 32 - (wa & 31), cb = 32 - (wb & 31);
 #pragma unroll
             for (int t = 0; t < ITEMS; ++t) {
-                const int ia = s + t < run ? s + t : run - 1;
-                const int ib = bs + t < run ? bs + t : run - 1;
-                a[t] = s + t < run ? ld_elem<Key>(kbuf, stage_word(KW * (a0 + ia))) : K::kMax;
-                b[t] = bs + t < run ? ld_elem<Key>(kbuf, stage_word(KW * (b0 + ib))) : K::kMax;
+                a[t] = ld_elem<Key>(pa, KW * t + (KW * t >= ca ? 4 : 0));
+                b[t] = ld_elem<Key>(pb, KW * t + (KW * t >= cb ? 4 : 0));
+            }
+#pragma unroll
+            for (int t = 0; t < ITEMS; ++t) {
+                a[t] = t < run - s ? a[t] : K::kMax;
+                b[t] = t < run - bs ? b[t] : K::kMax;
             }
 #pragma unroll
             for (int t = 0; t < ITEMS; ++t) x[t] = min(a[t], b[ITEMS - 1 - t]);
@@ -306,28 +370,39 @@ __global__ __launch_bounds__(THREADS) void block_sort_kernel(
                 const Key kb = ld_elem<Key>(kbuf, stage_word(KW * (b0 + cb)));
                 const bool take_a = ai < a_end && (bi >= b_end || ka <= kb);
                 x[t] = take_a ? ka : kb;
-                pos[t] = pbuf[take_a ? a0 + ca : b0 + cb];
+                pos[t] = pbuf[stage_word(take_a ? a0 + ca : b0 + cb)];
                 ai += take_a ? 1 : 0;
                 bi += take_a ? 0 : 1;
             }
         }
     }
     __syncthreads();
-#pragma unroll
-    for (int t = 0; t < ITEMS; ++t) {
-        st_elem<Key>(kbuf, stage_word(KW * (tid * ITEMS + t)), x[t]);
-        if constexpr (KV) pbuf[tid * ITEMS + t] = pos[t];
-    }
+    put_row<ITEMS>(kbuf, tid, x);
+    if constexpr (KV) put_row<ITEMS>(pbuf, tid, pos);
     __syncthreads();
 
     // Store in tile order, coalesced; payloads follow their positions.
+    if (vec_out) {
+        int32_t* const w = reinterpret_cast<int32_t*>(dst + t0);
 #pragma unroll
-    for (int r = 0; r < ITEMS; ++r) {
-        const int e = tid + r * THREADS;
-        if (e < len) {
-            dst[t0 + e] = K::from_ord(ld_elem<Key>(kbuf, stage_word(KW * e)));
-            if constexpr (KV) {
-                const int q = pbuf[e];
+        for (int r = 0; r < ITEMS * KW / 4; ++r) {
+            const int q = 4 * (tid + r * THREADS);
+            store_stream4(w + q, map_vec<ORDER, false>(
+                                     *reinterpret_cast<const int4v*>(kbuf + stage_word(q))));
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < ITEMS; ++r) {
+            const int e = tid + r * THREADS;
+            if (e < len) dst[t0 + e] = K::from_ord(ld_elem<Key>(kbuf, stage_word(KW * e)));
+        }
+    }
+    if constexpr (KV) {
+#pragma unroll
+        for (int r = 0; r < ITEMS; ++r) {
+            const int e = tid + r * THREADS;
+            if (e < len) {
+                const int q = pbuf[stage_word(e)];
 #pragma unroll
                 for (int v = 0; v < VW; ++v) dst_v[VW * (t0 + e) + v] = vbuf[VW * q + v];
             }

@@ -148,7 +148,7 @@ __device__ __forceinline__ void store_stream4(int32_t* p, int4v x) {
 }
 
 // Stage word of tile output p: 4 spare words after every 32.
-__device__ __forceinline__ int stage_word(int p) { return p + ((p >> 5) << 2); }
+__host__ __device__ constexpr int stage_word(int p) { return p + ((p >> 5) << 2); }
 
 // ---------------------------------------------------------------------------
 // Partition and co-rank query kernels.

@@ -49,10 +49,18 @@ def libemu(request, tmp_path_factory):
     return out, rt
 
 
-@pytest.mark.parametrize("group", ["small", "skew", "blocks", "direct", "production", "unsorted",
-                                   "orders", "sort", "batched"])
+CORE_GROUPS = ["small", "skew", "blocks", "direct", "production", "unsorted"]
+# The typed, sort and batch groups exercise the same load and store helpers
+# as the core groups, so they run in the default build only (keeps the CPU
+# suite to a few minutes).
+WIDE_GROUPS = ["orders", "sort", "batched"]
+
+
+@pytest.mark.parametrize("group", CORE_GROUPS + WIDE_GROUPS)
 def test_emulated_kernels_match_oracle(libemu, group):
     lib, rt = libemu
+    if group in WIDE_GROUPS and not lib.endswith("libemu_default.so"):
+        pytest.skip("typed, sort and batch groups run in the default build")
     env = dict(os.environ, LD_PRELOAD=rt, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1",
                UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
     r = subprocess.run([sys.executable, os.path.join(HERE, "emu", "run_emu_cases.py"), lib, group],
