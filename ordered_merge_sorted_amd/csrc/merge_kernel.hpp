@@ -16,16 +16,24 @@
 //     and the tile goes back to HBM through an LDS stage with coalesced
 //     16-byte stores.
 //
+// Elements.  Keys are 32- or 64-bit (KW = 1 or 2 words) and payloads 0, 1 or
+// 2 words (VW).  Rings, refills, stages and stores move 32-bit words;
+// searches and merges read whole elements.  Keys are held in LDS as their
+// order images (KeyOrder, corank.hpp), so every key type and direction is a
+// signed-integer merge; payloads are opaque words.
+//
 // gfx950 choices (none of these is on the pages):
-//   * Ring slot of an element = its absolute element address (address/4)
-//     modulo the power-of-two ring capacity.  A 16-byte-aligned vector in HBM
-//     then lands on a 16-byte-aligned slot quad, so refills are
-//     global_load_dwordx4 + ds_write_b128 with no wrap inside a vector.
-//     Partial vectors at the two ends of a refill are loaded one element at
-//     a time (never past the range, so never past the array).
+//   * Ring slot of a word = its absolute word address (address/4) modulo the
+//     power-of-two ring capacity.  A 16-byte-aligned vector in HBM then lands
+//     on a 16-byte-aligned slot quad, so refills are global_load_dwordx4 +
+//     ds_write_b128 with no wrap inside a vector, and 8-byte-aligned 64-bit
+//     elements land on even slots.  Partial vectors at the two ends of a
+//     refill are loaded one element at a time (never past the range, so
+//     never past the array).
 //   * The refill for tile t+1 is issued into registers as soon as tile t's
 //     split is known, before tile t is merged, and written to LDS only after
-//     tile t's stores; the HBM latency hides behind the merge.
+//     the tile's rows are staged and before its stores; the HBM latency hides
+//     behind the merge.
 //   * Each lane searches the END of its slice; its start is its left
 //     neighbour's end, read from a small LDS array, and the last lane's end
 //     is the tile's split.  One search per lane per tile.  Inside a tile the
@@ -40,9 +48,11 @@
 //     ordering of the lane's keys is bit-identical to the stable merge.  The
 //     network has no LDS round trip per output and no branches.  Key+payload
 //     merges keep the serial loop, where the tie order is visible.
-//   * Each ring has a guard zone that mirrors its first ITEMS slots past its
-//     end, so a lane reads its ITEMS candidates at one base address with
-//     immediate offsets and no wrap arithmetic.
+//   * Tiles whose outputs all come from one side are stored straight from
+//     that side's ring window: no search, no network, no stage.
+//   * Each key ring has a guard zone that mirrors its first ITEMS elements
+//     past its end, so a lane reads its ITEMS candidates at one base address
+//     with immediate offsets and no wrap arithmetic.
 //   * The LDS stage is padded by 4 words every 32, which makes the 16-byte
 //     stage writes (lane-contiguous) and 16-byte stage reads (for the
 //     coalesced stores) free of bank conflicts.
@@ -51,7 +61,10 @@
 //     interval G-fold per round (the pages note the search may be
 //     higher-radix).  Fewer dependent HBM round trips, more lines touched
 //     per round; G is a tuning choice of the launcher.
-//   * All arithmetic is int32 compares and index arithmetic; no MFMA.
+//   * A descriptor mode lets the same kernel merge any list of (A, B, C)
+//     ranges: the pieces of a batch of merges or of a merge-sort pass
+//     (batch_kernel.hpp).
+//   * All arithmetic is integer compares and index arithmetic; no MFMA.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -115,13 +115,14 @@ static bool typed_go(int variant, const void* A, const void* Av, int64_t m, cons
     return false;
 }
 
-// The merge-sort pipeline of the library (block sort, then plan + merge per
-// pass, ping-pong between out and a scratch copy), for one shape.
-template <int T, int I, int VW, int ORDER>
+// The merge-sort pipeline of the library (block sort with ST lanes, then
+// plan + merge per pass, ping-pong between out and a scratch copy), for one
+// shape.
+template <int T, int I, int VW, int ORDER, int ST = T>
 static void sort_cfg(const void* in_k, const void* in_v, int64_t N, void* out_k, void* out_v,
                      int64_t seg_len) {
     using Key = typename omerge::KeyOrder<ORDER>::T;
-    constexpr int kTile = T * I;
+    constexpr int kTile = ST * I;  // the block sort's runs
     if (N == 0) return;
     int passes = 0;
     for (int64_t run = kTile; run < N; run *= 2) ++passes;
@@ -136,8 +137,8 @@ static void sort_cfg(const void* in_k, const void* in_v, int64_t N, void* out_k,
                          VW ? reinterpret_cast<uint32_t*>(scratch + val_at) : nullptr};
     int cur = passes % 2;
     const int64_t tiles = (N + kTile - 1) / kTile;
-    run_grid(tiles, T, [&] {
-        omerge::block_sort_kernel<T, I, VW, ORDER>(static_cast<const Key*>(in_k),
+    run_grid(tiles, ST, [&] {
+        omerge::block_sort_kernel<ST, I, VW, ORDER>(static_cast<const Key*>(in_k),
                                                    static_cast<const uint32_t*>(in_v), N,
                                                    bufk[cur], bufv[cur]);
     });
@@ -208,8 +209,9 @@ static int sort_go(int variant, const void* in_k, const void* in_v, int64_t N, v
     if constexpr (emu_sort_has(0, ORDER, VW)) {
         if (variant == 0) {
             constexpr int kw = omerge::KeyOrder<ORDER>::kWords;
-            sort_cfg<256, production_items(kw, VW), VW, ORDER>(in_k, in_v, N, out_k, out_v,
-                                                               seg_len);
+            constexpr int st = (kw == 1 && VW == 0) ? 1024 : 256;  // the library's block sort
+            sort_cfg<256, production_items(kw, VW), VW, ORDER, st>(in_k, in_v, N, out_k, out_v,
+                                                                   seg_len);
             return 1;
         }
     }
