@@ -446,7 +446,34 @@ def group_batched(r, g):
             r.check(ok, ("batched", variant, order, vw, pairs, m, n, seg_len))
 
 
-GROUPS = {"sort": group_sort, "batched": group_batched, "orders": group_orders, "small": group_small, "direct": group_direct, "skew": group_skew, "blocks": group_blocks,
+def group_batched_garbage(r, g):
+    """Offsets that break the contract (negative, past the ends, decreasing,
+    huge) and unsorted keys: the plan and merge kernels must still stay inside
+    every array (the sanitizers watch each access) and return."""
+    for c in range(12):
+        variant, order, vw = SORT_COMBOS[c % len(SORT_COMBOS)]
+        dtype = KIND_DTYPE[order & 7]
+        pairs = int(g.integers(1, 60))
+        m, n = (int(x) for x in g.integers(0, 3000, size=2))
+        a_off = g.integers(-(1 << 40), 1 << 40, size=pairs + 1).astype(np.int64)
+        b_off = g.integers(-5, n + 5, size=pairs + 1).astype(np.int64)
+        if c % 3 == 0:
+            a_off = np.sort(g.integers(-3, m + 3, size=pairs + 1)).astype(np.int64)
+        A = g.integers(0, 50, size=m).astype(dtype)
+        B = g.integers(0, 50, size=n).astype(dtype)
+        vdt = np.uint64 if vw == 2 else np.uint32
+        Av = np.arange(m, dtype=vdt)
+        Bv = np.arange(n, dtype=vdt)
+        Ck = np.zeros(m + n, dtype=dtype)
+        Cv = np.zeros(m + n, dtype=vdt)
+        seg_len = int(g.choice([100, 512, 4 * int(g.integers(1, 300))]))
+        r.lib.emu_batched(variant, order, vw, ptr(A), ptr(Av) if vw else None, ptr(a_off), m,
+                          ptr(B), ptr(Bv) if vw else None, ptr(b_off), n, pairs, seg_len, ptr(Ck),
+                          ptr(Cv) if vw else None)
+        r.cases += 1
+
+
+GROUPS = {"batched_garbage": group_batched_garbage, "sort": group_sort, "batched": group_batched, "orders": group_orders, "small": group_small, "direct": group_direct, "skew": group_skew, "blocks": group_blocks,
           "production": group_production, "unsorted": group_unsorted}
 
 if __name__ == "__main__":

@@ -539,6 +539,23 @@ def test_batched_merges(dtype, desc):
         assert_same(host_bits(gv), as_bits(wv), "batched pair payloads")
 
 
+def test_batched_invalid_offsets_return():
+    """Offsets are device data and are not checked; offsets that break the
+    contract (negative, past the ends, decreasing) give an unspecified output
+    but the call returns and later work is unaffected (the kernels clamp
+    every range; the CPU emulation checks each access of such cases)."""
+    g = np.random.Generator(np.random.PCG64(777))
+    A = g.integers(0, 50, size=5000).astype(np.int32)
+    B = g.integers(0, 50, size=3000).astype(np.int32)
+    a_off = g.integers(-(1 << 40), 1 << 40, size=41).astype(np.int64)
+    b_off = g.integers(-5, 3005, size=41).astype(np.int64)
+    out = om.merge_batched(dev(A), dev(a_off), dev(B), dev(b_off))
+    torch.cuda.synchronize()
+    assert out.numel() == 8000
+    A2, B2 = pair(g, 20000, 10000, 100)
+    assert_same(host(om.merge_i32(dev(A2), dev(B2))), oracle.merge_i32(A2, B2), "after")
+
+
 def test_batched_single_merge_is_merge():
     """A batch of one merge is the plain merge."""
     g = np.random.Generator(np.random.PCG64(771))

@@ -53,7 +53,7 @@ CORE_GROUPS = ["small", "skew", "blocks", "direct", "production", "unsorted"]
 # The typed, sort and batch groups exercise the same load and store helpers
 # as the core groups, so they run in the default build only (keeps the CPU
 # suite to a few minutes).
-WIDE_GROUPS = ["orders", "sort", "batched"]
+WIDE_GROUPS = ["orders", "sort", "batched", "batched_garbage"]
 
 
 @pytest.mark.parametrize("group", CORE_GROUPS + WIDE_GROUPS)
