@@ -1,6 +1,8 @@
 /*
- * omerge.h -- C ABI of libomerge.so: stable merge of two sorted int32 arrays
- * on an AMD Instinct MI355X (gfx950), by the co-rank method.
+ * omerge.h -- C ABI of libomerge.so: stable merge of two sorted arrays on an
+ * AMD Instinct MI355X (gfx950), by the co-rank method; the same kernels also
+ * serve other key types and orders, batches of merges and a stable merge sort
+ * (declared further down).
  *
  * The operation (page "Co-rank Function ... and Basic Parallel Merge Kernel",
  * pmpp.huatsai.dev/12-merge/02, overview and "Co-rank function definition";
