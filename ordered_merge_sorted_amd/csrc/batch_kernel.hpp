@@ -410,4 +410,260 @@ __global__ __launch_bounds__(THREADS) void block_sort_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Batches of short merges.  One workgroup per tile of TILE outputs of the
+// concatenated output C, whatever merges it holds: the plan finds the global
+// co-rank (a, b) of every tile boundary (and the merge holding it); the tile
+// kernel loads the tile's A and B ranges into LDS and cuts them into pieces
+// at the merge starts that fall inside the tile.  Each lane finds the piece
+// holding its first output and its co-rank inside that piece, then merges
+// ITEMS outputs, passing into the next piece when one is exhausted (the A
+// and B ranges of consecutive merges are consecutive).  Many short merges
+// then share one workgroup instead of taking one each.
+
+struct TileBound {
+    int64_t a, b;  // global co-rank of the tile boundary: first A and B element
+    int64_t p;     // merge holding the boundary
+};
+
+// Boundary w = 0..tiles of the tile grid: k = min(w*tile, m+n).
+template <int G, int ORDER>
+__global__ __launch_bounds__(256) void plan_tiles_kernel(
+    const typename KeyOrder<ORDER>::T* __restrict__ A, const int64_t* __restrict__ a_off,
+    int64_t m, const typename KeyOrder<ORDER>::T* __restrict__ B,
+    const int64_t* __restrict__ b_off, int64_t n, int64_t pairs, int64_t tile, int64_t tiles,
+    TileBound* __restrict__ tb) {
+    static_assert(G >= 2, "group search");
+    const int64_t gid = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+    if ((gid & ~int64_t(63)) / G > tiles) return;
+    const int64_t w = gid / G;
+    const bool live = w <= tiles;
+    const int g_lane = static_cast<int>(gid % G);
+    const int g_shift = static_cast<int>(threadIdx.x & 63) - g_lane;
+    auto ao = [&](int64_t p) { return clamp_to<int64_t>(a_off[p], 0, m); };
+    auto bo = [&](int64_t p) { return clamp_to<int64_t>(b_off[p], 0, n); };
+    int64_t p = 0, k = 0, la = 0, lb = 0;
+    if (live) {
+        const int64_t total = m + n;
+        const int64_t c = w * tile < total ? w * tile : total;
+        int64_t lo = 0, hi = pairs + 1;  // merge starts <= c
+        while (lo < hi) {
+            const int64_t mid = (lo + hi) >> 1;
+            if (ao(mid) + bo(mid) <= c) lo = mid + 1;
+            else hi = mid;
+        }
+        p = lo > 0 ? (lo - 1 < pairs ? lo - 1 : pairs - 1) : 0;
+        const int64_t a1 = ao(p + 1), b1 = bo(p + 1);
+        la = a1 > ao(p) ? a1 - ao(p) : 0;
+        lb = b1 > bo(p) ? b1 - bo(p) : 0;
+        k = clamp_to<int64_t>(c - (ao(p) + bo(p)), 0, la + lb);
+    }
+    const int64_t a_base = live ? ao(p) : 0, b_base = live ? bo(p) : 0;
+    const int64_t i = co_rank_group<G, ORDER>(k, A + a_base, la, B + b_base, lb, g_lane, g_shift);
+    if (!live || g_lane != 0) return;
+    tb[w].a = a_base + i;
+    tb[w].b = b_base + (k - i);
+    tb[w].p = p;
+}
+
+template <int THREADS, int ITEMS, int VW, int ORDER>
+__global__ __launch_bounds__(THREADS) void merge_tiles_kernel(
+    const typename KeyOrder<ORDER>::T* __restrict__ A, const uint32_t* __restrict__ Av,
+    const int64_t* __restrict__ a_off, int64_t m, const typename KeyOrder<ORDER>::T* __restrict__ B,
+    const uint32_t* __restrict__ Bv, const int64_t* __restrict__ b_off, int64_t n, int64_t pairs,
+    const TileBound* __restrict__ tb, typename KeyOrder<ORDER>::T* __restrict__ C,
+    uint32_t* __restrict__ Cv) {
+    using K = KeyOrder<ORDER>;
+    using Key = typename K::T;
+    constexpr int KW = K::kWords;
+    constexpr bool KV = VW > 0;
+    constexpr int VORDER = VW == 2 ? kKeyI64 : kKeyI32;
+    constexpr int kTile = THREADS * ITEMS;
+    constexpr int kCap = kTile / 4;  // merge starts a tile holds in LDS
+    static_assert(kCap % THREADS == 0, "candidates per lane");
+    // LDS: the tile's keys (A part, then B part) as images, payloads, the
+    // output stages (padded), piece bounds and one flag per candidate.
+    constexpr int kWin = 0;
+    constexpr int kVWin = kWin + kTile * KW;
+    constexpr int kStage = kVWin + kTile * VW;
+    constexpr int kVStage = kStage + stage_word(kTile * KW);
+    constexpr int kPieceA = kVStage + (KV ? stage_word(kTile * VW) : 0);
+    constexpr int kPieceB = kPieceA + kCap + 2;
+    constexpr int kFlag = kPieceB + kCap + 2;
+    __shared__ __attribute__((aligned(16))) int lds[kFlag + kCap];
+    int* const win = lds + kWin;
+    int* const vwin = lds + kVWin;
+    int* const stage = lds + kStage;
+    int* const vstage = lds + kVStage;
+    int* const pla = lds + kPieceA;
+    int* const plb = lds + kPieceB;
+    int* const flag = lds + kFlag;
+
+    const int tid = threadIdx.x;
+    const int64_t total = m + n;
+    const int64_t k0 = blockIdx.x * static_cast<int64_t>(kTile);
+    const int64_t k1 = k0 + kTile < total ? k0 + kTile : total;
+    auto ao = [&](int64_t p) { return clamp_to<int64_t>(a_off[p], 0, m); };
+    auto bo = [&](int64_t p) { return clamp_to<int64_t>(b_off[p], 0, n); };
+
+    // Tile ranges, clamped into the arrays and the tile (any plan keeps
+    // every access in range).
+    const TileBound t0 = tb[blockIdx.x], t1 = tb[blockIdx.x + 1];
+    const int64_t a0 = clamp_to<int64_t>(t0.a, 0, m);
+    const int64_t b0 = clamp_to<int64_t>(t0.b, 0, n);
+    const int c_max = static_cast<int>(k1 - k0);
+    const int a_len = static_cast<int>(clamp_to<int64_t>(clamp_to<int64_t>(t1.a, a0, m) - a0, 0, c_max));
+    const int b_len = static_cast<int>(clamp_to<int64_t>(clamp_to<int64_t>(t1.b, b0, n) - b0, 0,
+                                                         c_max - a_len));
+    const int c_len = a_len + b_len;
+    const int64_t p0 = clamp_to<int64_t>(t0.p, 0, pairs > 0 ? pairs - 1 : 0);
+
+    // Keys (as order images) and payloads of the tile.
+#pragma unroll
+    for (int r = 0; r < ITEMS; ++r) {
+        const int e = tid + r * THREADS;
+        if (e < c_len) {
+            const bool from_a = e < a_len;
+            const int64_t g = from_a ? a0 + e : b0 + (e - a_len);
+            st_elem<Key>(win, KW * e, K::to_ord(from_a ? A[g] : B[g]));
+            if constexpr (KV) {
+                const uint32_t* const src = from_a ? Av : Bv;
+#pragma unroll
+                for (int v = 0; v < VW; ++v) vwin[VW * e + v] = static_cast<int>(src[VW * g + v]);
+            }
+        }
+    }
+    // Pieces: piece 0 starts at the tile start; piece q >= 1 at the start of
+    // merge p0+q when that start lies inside the tile.  The starts inside the
+    // tile are a prefix of the candidates p0+1, p0+2, ...
+#pragma unroll
+    for (int r = 0; r < kCap / THREADS; ++r) {
+        const int q = 1 + tid + r * THREADS;
+        const int64_t p = p0 + q;
+        bool in = false;
+        if (p < pairs) {
+            const int64_t la = ao(p) - a0, lb = bo(p) - b0;
+            in = la >= 0 && lb >= 0 && la + lb < c_len && la <= a_len && lb <= b_len;
+            pla[q] = static_cast<int>(clamp_to<int64_t>(la, 0, a_len));
+            plb[q] = static_cast<int>(clamp_to<int64_t>(lb, 0, b_len));
+        }
+        flag[q - 1] = in ? 1 : 0;
+    }
+    if (tid == 0) {
+        pla[0] = 0;
+        plb[0] = 0;
+    }
+    __syncthreads();
+    // Number of pieces: 1 + the length of the prefix of candidates inside.
+    int lo = 0, hi = kCap;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (flag[mid]) lo = mid + 1;
+        else hi = mid;
+    }
+    const int npieces = 1 + lo;
+    // More merge starts than the LDS holds (only with many empty merges):
+    // piece bounds are then read from the offsets in global memory.
+    const bool overflow = lo == kCap && p0 + kCap + 1 < pairs &&
+                          ao(p0 + kCap + 1) + bo(p0 + kCap + 1) - k0 < c_len;
+    int pieces = npieces;
+    if (overflow) {
+        int64_t l = p0 + kCap + 1, h = pairs;  // merge starts inside the tile
+        while (l < h) {
+            const int64_t mid = (l + h) >> 1;
+            if (ao(mid) + bo(mid) - k0 < c_len) l = mid + 1;
+            else h = mid;
+        }
+        pieces = static_cast<int>(l - p0);
+    }
+    auto piece_a = [&](int q) -> int {
+        if (q >= pieces) return a_len;
+        if (q == 0) return 0;
+        if (!overflow) return pla[q];
+        return static_cast<int>(clamp_to<int64_t>(ao(p0 + q) - a0, 0, a_len));
+    };
+    auto piece_b = [&](int q) -> int {
+        if (q >= pieces) return b_len;
+        if (q == 0) return 0;
+        if (!overflow) return plb[q];
+        return static_cast<int>(clamp_to<int64_t>(bo(p0 + q) - b0, 0, b_len));
+    };
+
+    const int o0 = tid * ITEMS;
+    int* const row = stage + stage_word(tid * ITEMS * KW);
+    int* const vrow = vstage + stage_word(tid * ITEMS * VW);
+    if (o0 < c_len) {
+        // The piece holding output o0: the last piece starting at or before it.
+        int ql = 0, qh = pieces - 1;
+        while (ql < qh) {
+            const int mid = (ql + qh + 1) >> 1;
+            if (piece_a(mid) + piece_b(mid) <= o0) ql = mid;
+            else qh = mid - 1;
+        }
+        int q = ql;
+        // Co-rank of o0 inside piece q (bisection, as in the segment merge).
+        const int pa = piece_a(q), pb = piece_b(q);
+        const int wa = piece_a(q + 1) - pa, wb = piece_b(q + 1) - pb;
+        const int d = o0 - pa - pb;
+        int lo2 = d > wb ? d - wb : 0, hi2 = d < wa ? d : wa;
+        while (lo2 < hi2) {
+            const int mid = (lo2 + hi2) >> 1;
+            const Key av = ld_elem<Key>(win, KW * (pa + mid));
+            const Key bv = ld_elem<Key>(win, KW * (a_len + pb + d - 1 - mid));
+            if (av <= bv) lo2 = mid + 1;
+            else hi2 = mid;
+        }
+        int i = pa + lo2, j = pb + (d - lo2);
+        int ae = piece_a(q + 1), be = piece_b(q + 1);
+        // Keys only, and all of this lane's outputs inside piece q: the
+        // candidate network of the segment merge (ITEMS from each side,
+        // masked at the piece's ends), which has no dependent LDS reads.
+        const bool one_piece = !KV && o0 + ITEMS <= ae + be && o0 + ITEMS <= c_len;
+        if (one_piece) {
+            Key a[ITEMS], b[ITEMS], x[ITEMS];
+#pragma unroll
+            for (int t = 0; t < ITEMS; ++t) {
+                a[t] = i + t < ae ? ld_elem<Key>(win, KW * (i + t)) : K::kMax;
+                b[t] = j + t < be ? ld_elem<Key>(win, KW * (a_len + j + t)) : K::kMax;
+            }
+#pragma unroll
+            for (int t = 0; t < ITEMS; ++t) x[t] = min(a[t], b[ITEMS - 1 - t]);
+            bitonic_clean<ITEMS>(x);
+#pragma unroll
+            for (int t = 0; t < ITEMS; ++t) st_elem<Key>(row, KW * t, x[t]);
+        } else {
+#pragma unroll
+            for (int t = 0; t < ITEMS; ++t) {
+                if (o0 + t < c_len) {
+                    while (i == ae && j == be && q + 1 < pieces) {  // next merge
+                        ++q;
+                        ae = piece_a(q + 1);
+                        be = piece_b(q + 1);
+                    }
+                    // (a side's end reads word 0 instead; that value is not taken)
+                    const Key ka = ld_elem<Key>(win, i < a_len ? KW * i : 0);
+                    const Key kb = ld_elem<Key>(win, j < b_len ? KW * (a_len + j) : 0);
+                    const bool take_a = i < ae && (j >= be || ka <= kb);
+                    st_elem<Key>(row, KW * t, take_a ? ka : kb);
+                    if constexpr (KV) {
+                        const int src = take_a ? i : a_len + j;
+#pragma unroll
+                        for (int v = 0; v < VW; ++v) vrow[VW * t + v] = vwin[VW * src + v];
+                    }
+                    i += take_a ? 1 : 0;
+                    j += take_a ? 0 : 1;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    constexpr int kVec = kTile * KW / 4 / THREADS;
+    store_tile<THREADS, kVec, ORDER>(reinterpret_cast<int32_t*>(C + k0), KW * c_len, stage, tid);
+    if constexpr (KV) {
+        constexpr int kVVec = kTile * VW / 4 / THREADS;
+        store_tile<THREADS, kVVec, VORDER>(reinterpret_cast<int32_t*>(Cv) + VW * k0, VW * c_len,
+                                           vstage, tid);
+    }
+}
+
 }  // namespace omerge

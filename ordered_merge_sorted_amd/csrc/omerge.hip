@@ -43,6 +43,9 @@ constexpr int kVersion = 100;  // 0.1.0
 #ifndef OMERGE_SORT_THREADS  // lanes of the block sort for 4-byte keys without payloads
 #define OMERGE_SORT_THREADS 1024
 #endif
+#ifndef OMERGE_SHORT_MERGE  // batches averaging fewer outputs per merge use the tile path
+#define OMERGE_SHORT_MERGE 1536
+#endif
 #ifndef OMERGE_COPY_UNROLL
 #define OMERGE_COPY_UNROLL 4
 #endif
@@ -238,13 +241,49 @@ struct Path {
         return e == hipSuccess ? OMERGE_OK : hip_fail(e);
     }
 
+    // A batch of short merges: one workgroup per tile of the concatenated
+    // output, whatever merges it holds (plan the tile boundaries, then merge).
+    static int batched_tiles(const Key* a, const void* Av, const int64_t* a_off, int64_t m,
+                             const Key* b, const void* Bv, const int64_t* b_off, int64_t n,
+                             int64_t pairs, void* C, void* Cv, hipStream_t stream) {
+        const int64_t tiles = ceil_div(m + n, kTile);
+        const int64_t blocks = ceil_div((tiles + 1) * kPartLanes, 256);
+        if (tiles > kMaxGridBlocks || blocks > kMaxGridBlocks) return OMERGE_OVERFLOW;
+        TileBound* tb = nullptr;
+        hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&tb),
+                                      static_cast<size_t>(tiles + 1) * sizeof(TileBound), stream);
+        if (e != hipSuccess) return hip_fail(e);
+        hipLaunchKernelGGL((plan_tiles_kernel<kPartLanes, ORDER>),
+                           dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, a, a_off, m,
+                           b, b_off, n, pairs, static_cast<int64_t>(kTile), tiles, tb);
+        e = hipGetLastError();
+        int rc = e == hipSuccess ? OMERGE_OK : hip_fail(e);
+        if (rc == OMERGE_OK) {
+            hipLaunchKernelGGL((merge_tiles_kernel<kThreads, kItems, VW, ORDER>),
+                               dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, stream, a,
+                               static_cast<const uint32_t*>(Av), a_off, m, b,
+                               static_cast<const uint32_t*>(Bv), b_off, n, pairs, tb,
+                               static_cast<Key*>(C), static_cast<uint32_t*>(Cv));
+            e = hipGetLastError();
+            rc = e == hipSuccess ? OMERGE_OK : hip_fail(e);
+        }
+        e = hipFreeAsync(tb, stream);
+        if (rc == OMERGE_OK && e != hipSuccess) rc = hip_fail(e);
+        return rc;
+    }
+
     // A batch of `pairs` merges given by prefix offsets into A and B (device
-    // arrays of pairs+1 entries): plan the segments, then merge them.
+    // arrays of pairs+1 entries).  Short merges on average (fewer than
+    // OMERGE_SHORT_MERGE outputs each) take the tile path; otherwise every
+    // merge is cut into segments, planned, and merged by the segment kernel.
     static int batched(const void* A, const void* Av, const int64_t* a_off, int64_t m,
                        const void* B, const void* Bv, const int64_t* b_off, int64_t n,
                        int64_t pairs, void* C, void* Cv, hipStream_t stream) {
         const int64_t total = m + n;
         if (total == 0) return OMERGE_OK;
+        if (total < pairs * static_cast<int64_t>(OMERGE_SHORT_MERGE))
+            return batched_tiles(static_cast<const Key*>(A), Av, a_off, m,
+                                 static_cast<const Key*>(B), Bv, b_off, n, pairs, C, Cv, stream);
         int64_t sl = 0;
         int rc = seg_len(m, n, &sl);
         if (rc != OMERGE_OK) return rc;

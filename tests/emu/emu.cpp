@@ -186,6 +186,31 @@ static void batched_cfg(const void* A, const void* Av, const int64_t* a_off, int
     });
 }
 
+// The library's tile path for batches of short merges, for one shape.
+template <int T, int I, int VW, int ORDER>
+static void tiles_cfg(const void* A, const void* Av, const int64_t* a_off, int64_t m,
+                      const void* B, const void* Bv, const int64_t* b_off, int64_t n,
+                      int64_t pairs, void* C, void* Cv) {
+    using Key = typename omerge::KeyOrder<ORDER>::T;
+    constexpr int kTile = T * I;
+    const int64_t total = m + n;
+    if (total == 0) return;
+    const int64_t tiles = (total + kTile - 1) / kTile;
+    std::vector<omerge::TileBound> tb(tiles + 1);
+    for (auto& t : tb) t = {-1, -1, -1};
+    const Key* a = static_cast<const Key*>(A);
+    const Key* b = static_cast<const Key*>(B);
+    run_grid(((tiles + 1) * 4 + 255) / 256, 256, [&] {
+        omerge::plan_tiles_kernel<4, ORDER>(a, a_off, m, b, b_off, n, pairs, kTile, tiles,
+                                            tb.data());
+    });
+    run_grid(tiles, T, [&] {
+        omerge::merge_tiles_kernel<T, I, VW, ORDER>(
+            a, static_cast<const uint32_t*>(Av), a_off, m, b, static_cast<const uint32_t*>(Bv),
+            b_off, n, pairs, tb.data(), static_cast<Key*>(C), static_cast<uint32_t*>(Cv));
+    });
+}
+
 // Which (order, payload) combinations the sort / batch entries hold: the
 // small shapes for int32 keys-only, float32 descending with 4-byte payloads,
 // int64 with 8-byte payloads and float64 descending keys-only; the library
@@ -222,6 +247,23 @@ template <int ORDER, int VW>
 static int batched_go(int variant, const void* A, const void* Av, const int64_t* a_off,
                       int64_t m, const void* B, const void* Bv, const int64_t* b_off, int64_t n,
                       int64_t pairs, int64_t seg_len, void* C, void* Cv) {
+    if (seg_len == 0) {  // the tile path
+        if constexpr (emu_sort_has(1, ORDER, VW)) {
+            if (variant == 1) {
+                tiles_cfg<128, 4, VW, ORDER>(A, Av, a_off, m, B, Bv, b_off, n, pairs, C, Cv);
+                return 1;
+            }
+        }
+        if constexpr (emu_sort_has(0, ORDER, VW)) {
+            if (variant == 0) {
+                constexpr int kw = omerge::KeyOrder<ORDER>::kWords;
+                tiles_cfg<256, production_items(kw, VW), VW, ORDER>(A, Av, a_off, m, B, Bv, b_off,
+                                                                    n, pairs, C, Cv);
+                return 1;
+            }
+        }
+        return 0;
+    }
     if constexpr (emu_sort_has(1, ORDER, VW)) {
         if (variant == 1) {
             batched_cfg<128, 4, VW, ORDER>(A, Av, a_off, m, B, Bv, b_off, n, pairs, seg_len, C,
@@ -361,7 +403,8 @@ int emu_sort(int variant, int order, int vw, const void* in_k, const void* in_v,
     return 0;
 }
 
-// The batched merge for an order and payload width (same combinations).
+// The batched merge for an order and payload width (same combinations);
+// seg_len == 0 selects the tile path for short merges.
 int emu_batched(int variant, int order, int vw, const void* A, const void* Av,
                 const int64_t* a_off, int64_t m, const void* B, const void* Bv,
                 const int64_t* b_off, int64_t n, int64_t pairs, int64_t seg_len, void* C,

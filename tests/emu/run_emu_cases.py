@@ -411,11 +411,12 @@ def group_batched(r, g):
         dtype = KIND_DTYPE[order & 7]
         desc = bool(order & 8)
         tile = r.lib.emu_typed_tile(variant, order, vw)
-        for c in range(4 if variant else 2):
-            pairs = int(g.choice([1, 3, 40, 300]))
-            scale = int(g.choice([3, tile // 2, 3 * tile]))
-            la = g.integers(0, scale + 1, size=pairs) * (g.random(pairs) > 0.15)
-            lb = g.integers(0, scale + 1, size=pairs) * (g.random(pairs) > 0.15)
+        for c in range(5 if variant else 2):
+            pairs = int(g.choice([1, 3, 40, 300, 2000]))
+            scale = int(g.choice([3, tile // 2, 3 * tile])) if pairs < 2000 else 3
+            empty = 0.15 if c % 3 else 0.7  # many empty merges: tiles overflow their piece list
+            la = g.integers(0, scale + 1, size=pairs) * (g.random(pairs) > empty)
+            lb = g.integers(0, scale + 1, size=pairs) * (g.random(pairs) > empty)
             a_off = np.concatenate([[0], np.cumsum(la)]).astype(np.int64)
             b_off = np.concatenate([[0], np.cumsum(lb)]).astype(np.int64)
             m, n = int(a_off[-1]), int(b_off[-1])
@@ -429,21 +430,26 @@ def group_batched(r, g):
             top = vdt(1 << (63 if vw == 2 else 31))
             Av = np.arange(m, dtype=vdt)
             Bv = (top + np.arange(n, dtype=vdt)).astype(vdt)
-            seg_len = int(g.choice([tile, 3 * tile, 100, 4 * int(g.integers(1, 300))]))
-            Ck = np.zeros(m + n, dtype=dtype)
-            Cv = np.zeros(m + n, dtype=vdt)
-            held = r.lib.emu_batched(variant, order, vw, ptr(A), ptr(Av) if vw else None,
-                                     ptr(a_off), m, ptr(B), ptr(Bv) if vw else None, ptr(b_off),
-                                     n, pairs, seg_len, ptr(Ck), ptr(Cv) if vw else None)
-            r.check(held == 1, ("batched combo held", variant, order, vw))
             if vw:
                 wk, wv = oracle.merge_batched(A, a_off, B, b_off, Av, Bv, descending=desc)
-                ok = np.array_equal(Ck.view(np.uint8), wk.view(np.uint8)) and \
-                    np.array_equal(Cv, wv)
             else:
                 wk = oracle.merge_batched(A, a_off, B, b_off, descending=desc)
+            # seg_len 0 = the tile path for short merges
+            seg_lens = [int(g.choice([tile, 3 * tile, 100, 4 * int(g.integers(1, 300))])), 0]
+            if pairs >= 2000:
+                seg_lens = [0]  # thousands of one-workgroup merges: the tile path only
+            for seg_len in seg_lens:
+                Ck = np.zeros(m + n, dtype=dtype)
+                Cv = np.zeros(m + n, dtype=vdt)
+                held = r.lib.emu_batched(variant, order, vw, ptr(A), ptr(Av) if vw else None,
+                                         ptr(a_off), m, ptr(B), ptr(Bv) if vw else None,
+                                         ptr(b_off), n, pairs, seg_len, ptr(Ck),
+                                         ptr(Cv) if vw else None)
+                r.check(held == 1, ("batched combo held", variant, order, vw))
                 ok = np.array_equal(Ck.view(np.uint8), wk.view(np.uint8))
-            r.check(ok, ("batched", variant, order, vw, pairs, m, n, seg_len))
+                if vw:
+                    ok = ok and np.array_equal(Cv, wv)
+                r.check(ok, ("batched", variant, order, vw, pairs, m, n, seg_len))
 
 
 def group_batched_garbage(r, g):
@@ -466,11 +472,11 @@ def group_batched_garbage(r, g):
         Bv = np.arange(n, dtype=vdt)
         Ck = np.zeros(m + n, dtype=dtype)
         Cv = np.zeros(m + n, dtype=vdt)
-        seg_len = int(g.choice([100, 512, 4 * int(g.integers(1, 300))]))
-        r.lib.emu_batched(variant, order, vw, ptr(A), ptr(Av) if vw else None, ptr(a_off), m,
-                          ptr(B), ptr(Bv) if vw else None, ptr(b_off), n, pairs, seg_len, ptr(Ck),
-                          ptr(Cv) if vw else None)
-        r.cases += 1
+        for seg_len in (int(g.choice([100, 512, 4 * int(g.integers(1, 300))])), 0):
+            r.lib.emu_batched(variant, order, vw, ptr(A), ptr(Av) if vw else None, ptr(a_off), m,
+                              ptr(B), ptr(Bv) if vw else None, ptr(b_off), n, pairs, seg_len,
+                              ptr(Ck), ptr(Cv) if vw else None)
+            r.cases += 1
 
 
 GROUPS = {"batched_garbage": group_batched_garbage, "sort": group_sort, "batched": group_batched, "orders": group_orders, "small": group_small, "direct": group_direct, "skew": group_skew, "blocks": group_blocks,
