@@ -256,6 +256,22 @@ def sort_and_batch(om, stream):
     log("%-44s %10.3f %14.4g  (%.0f GB/s, %.1f%% of peak)" % (
         "batched: 2^15 merges of 4096+4096", ms, c.numel() / (ms * 1e-3), gbs,
         100 * gbs / HBM_PEAK_GBS))
+    # 2^22 merges of 16 + 16 keys each (the tile path for short merges)
+    pairs, L = 1 << 22, 16
+    a = torch.sort(keys[:pairs * L].view(pairs, L), dim=1).values.reshape(-1)
+    b = torch.sort(keys[pairs * L:2 * pairs * L].view(pairs, L), dim=1).values.reshape(-1)
+    offs = torch.arange(0, pairs * L + 1, L, dtype=torch.int64, device=dev)
+    om.merge_batched(a, offs, b, offs, out=c, stream=stream)
+    ref = torch.sort(torch.cat([a.view(pairs, L), b.view(pairs, L)], dim=1), dim=1).values
+    torch.cuda.synchronize()
+    if not torch.equal(c.view(pairs, 2 * L), ref):
+        log("FAILED: omerge batched merge (short merges) differs from torch's per-merge sort")
+        sys.exit(1)
+    ms = _time(lambda: om.merge_batched(a, offs, b, offs, out=c, stream=stream), stream)
+    gbs = 2 * c.numel() * 4 / (ms * 1e-3) / 1e9
+    log("%-44s %10.3f %14.4g  (%.0f GB/s, %.1f%% of peak)" % (
+        "batched: 2^22 merges of 16+16", ms, c.numel() / (ms * 1e-3), gbs,
+        100 * gbs / HBM_PEAK_GBS))
 
 
 def main():
