@@ -155,7 +155,7 @@ int omerge_merge_pairs(const void *A_keys, const void *A_vals, int64_t m,
  *                                      unspecified output, but every access
  *                                      stays inside the arrays.
  *   C_keys[m+n], C_vals[m+n]      out.
- * num_merges >= 1 when m+n > 0.  Batches of short merges (fewer than 1,536
+ * num_merges >= 1 when m+n > 0.  Batches of short merges (fewer than 6,144
  * outputs per merge on average) are merged a tile of C at a time, many merges
  * per workgroup; others merge by segments.  Stream-ordered scratch of one
  * 24-byte bound per tile or one 40-byte descriptor per segment; otherwise as

@@ -421,6 +421,31 @@ __global__ __launch_bounds__(THREADS) void block_sort_kernel(
 // and B ranges of consecutive merges are consecutive).  Many short merges
 // then share one workgroup instead of taking one each.
 
+// Copies len elements (W words each, W = KeyOrder<ORDER>::kWords) from the
+// global word array src to LDS words dst[0, W*len), mapping keys with
+// to_ord (payloads use an identity order).  dst must sit at the same phase
+// as src modulo 4 words, so 16-byte vectors line up on both sides; the
+// partial vectors at the two ends (whole elements) go one element at a time.
+template <int THREADS, int ORDER>
+__device__ __forceinline__ void load_range(int* dst, const int32_t* src, int len, int tid) {
+    using T = typename KeyOrder<ORDER>::T;
+    constexpr int W = KeyOrder<ORDER>::kWords;
+    const int words = W * len;
+    const int head0 = (4 - (word_phase(src) & 3)) & 3;
+    const int head = head0 < words ? head0 : words;
+    const int nvec = (words - head) >> 2;
+    const int tail = (words - head) & 3;
+    for (int q = tid; q < nvec; q += THREADS) {
+        const int w = head + 4 * q;
+        *reinterpret_cast<int4v*>(dst + w) = map_vec<ORDER, true>(load_stream4(src + w));
+    }
+    if (W * tid < head) st_elem<T>(dst, W * tid, map_elem<ORDER, true>(ld_elem<T>(src, W * tid)));
+    if (tid >= 4 && W * (tid - 3) <= tail) {
+        const int w = head + 4 * nvec + W * (tid - 4);
+        st_elem<T>(dst, w, map_elem<ORDER, true>(ld_elem<T>(src, w)));
+    }
+}
+
 struct TileBound {
     int64_t a, b;  // global co-rank of the tile boundary: first A and B element
     int64_t p;     // merge holding the boundary
@@ -479,15 +504,23 @@ __global__ __launch_bounds__(THREADS) void merge_tiles_kernel(
     constexpr bool KV = VW > 0;
     constexpr int VORDER = VW == 2 ? kKeyI64 : kKeyI32;
     constexpr int kTile = THREADS * ITEMS;
-    constexpr int kCap = kTile / 4;  // merge starts a tile holds in LDS
+    // merge starts a tile holds in LDS (at least one candidate per lane)
+    constexpr int kCap = kTile / 8 > THREADS ? kTile / 8 : THREADS;
     static_assert(kCap % THREADS == 0, "candidates per lane");
-    // LDS: the tile's keys (A part, then B part) as images, payloads, the
-    // output stages (padded), piece bounds and one flag per candidate.
+    // LDS: the tile's keys (A part, then B part) as images and its payloads;
+    // once every lane holds its outputs in registers, the same words hold
+    // the output stages (padded).  Then piece bounds, one flag per
+    // candidate.  The overlap keeps a workgroup near 25 KB (int32 keys), so
+    // several share a CU while each waits on its loads.
+    // (Each window has 8 spare words: its A and B parts each start at the
+    // phase of their source modulo 4 words.)
     constexpr int kWin = 0;
-    constexpr int kVWin = kWin + kTile * KW;
-    constexpr int kStage = kVWin + kTile * VW;
+    constexpr int kVWin = kWin + kTile * KW + 8;
+    constexpr int kStage = 0;
     constexpr int kVStage = kStage + stage_word(kTile * KW);
-    constexpr int kPieceA = kVStage + (KV ? stage_word(kTile * VW) : 0);
+    constexpr int kInWords = kVWin + (KV ? kTile * VW + 8 : 0);
+    constexpr int kOutWords = kVStage + (KV ? stage_word(kTile * VW) : 0);
+    constexpr int kPieceA = kInWords > kOutWords ? kInWords : kOutWords;
     constexpr int kPieceB = kPieceA + kCap + 2;
     constexpr int kFlag = kPieceB + kCap + 2;
     __shared__ __attribute__((aligned(16))) int lds[kFlag + kCap];
@@ -518,20 +551,22 @@ __global__ __launch_bounds__(THREADS) void merge_tiles_kernel(
     const int c_len = a_len + b_len;
     const int64_t p0 = clamp_to<int64_t>(t0.p, 0, pairs > 0 ? pairs - 1 : 0);
 
-    // Keys (as order images) and payloads of the tile.
-#pragma unroll
-    for (int r = 0; r < ITEMS; ++r) {
-        const int e = tid + r * THREADS;
-        if (e < c_len) {
-            const bool from_a = e < a_len;
-            const int64_t g = from_a ? a0 + e : b0 + (e - a_len);
-            st_elem<Key>(win, KW * e, K::to_ord(from_a ? A[g] : B[g]));
-            if constexpr (KV) {
-                const uint32_t* const src = from_a ? Av : Bv;
-#pragma unroll
-                for (int v = 0; v < VW; ++v) vwin[VW * e + v] = static_cast<int>(src[VW * g + v]);
-            }
-        }
+    // Keys (as order images) and payloads of the tile: the A part at word
+    // offA of the window, the B part at offB, each at its source's phase.
+    const int32_t* const a_src = reinterpret_cast<const int32_t*>(A + a0);
+    const int32_t* const b_src = reinterpret_cast<const int32_t*>(B + b0);
+    const int offA = word_phase(a_src) & 3;
+    const int offB = offA + KW * a_len + ((word_phase(b_src) - offA - KW * a_len) & 3);
+    load_range<THREADS, ORDER>(win + offA, a_src, a_len, tid);
+    load_range<THREADS, ORDER>(win + offB, b_src, b_len, tid);
+    int vA = 0, vB = 0;
+    if constexpr (KV) {
+        const int32_t* const va_src = reinterpret_cast<const int32_t*>(Av) + VW * a0;
+        const int32_t* const vb_src = reinterpret_cast<const int32_t*>(Bv) + VW * b0;
+        vA = word_phase(va_src) & 3;
+        vB = vA + VW * a_len + ((word_phase(vb_src) - vA - VW * a_len) & 3);
+        load_range<THREADS, VORDER>(vwin + vA, va_src, a_len, tid);
+        load_range<THREADS, VORDER>(vwin + vB, vb_src, b_len, tid);
     }
     // Pieces: piece 0 starts at the tile start; piece q >= 1 at the start of
     // merge p0+q when that start lies inside the tile.  The starts inside the
@@ -590,8 +625,8 @@ __global__ __launch_bounds__(THREADS) void merge_tiles_kernel(
     };
 
     const int o0 = tid * ITEMS;
-    int* const row = stage + stage_word(tid * ITEMS * KW);
-    int* const vrow = vstage + stage_word(tid * ITEMS * VW);
+    Key x[ITEMS];        // this lane's outputs (order images)
+    int vx[ITEMS * (KV ? VW : 1)];  // their payload words
     if (o0 < c_len) {
         // The piece holding output o0: the last piece starting at or before it.
         int ql = 0, qh = pieces - 1;
@@ -608,8 +643,8 @@ __global__ __launch_bounds__(THREADS) void merge_tiles_kernel(
         int lo2 = d > wb ? d - wb : 0, hi2 = d < wa ? d : wa;
         while (lo2 < hi2) {
             const int mid = (lo2 + hi2) >> 1;
-            const Key av = ld_elem<Key>(win, KW * (pa + mid));
-            const Key bv = ld_elem<Key>(win, KW * (a_len + pb + d - 1 - mid));
+            const Key av = ld_elem<Key>(win, offA + KW * (pa + mid));
+            const Key bv = ld_elem<Key>(win, offB + KW * (pb + d - 1 - mid));
             if (av <= bv) lo2 = mid + 1;
             else hi2 = mid;
         }
@@ -620,17 +655,15 @@ __global__ __launch_bounds__(THREADS) void merge_tiles_kernel(
         // masked at the piece's ends), which has no dependent LDS reads.
         const bool one_piece = !KV && o0 + ITEMS <= ae + be && o0 + ITEMS <= c_len;
         if (one_piece) {
-            Key a[ITEMS], b[ITEMS], x[ITEMS];
+            Key a[ITEMS], b[ITEMS];
 #pragma unroll
             for (int t = 0; t < ITEMS; ++t) {
-                a[t] = i + t < ae ? ld_elem<Key>(win, KW * (i + t)) : K::kMax;
-                b[t] = j + t < be ? ld_elem<Key>(win, KW * (a_len + j + t)) : K::kMax;
+                a[t] = i + t < ae ? ld_elem<Key>(win, offA + KW * (i + t)) : K::kMax;
+                b[t] = j + t < be ? ld_elem<Key>(win, offB + KW * (j + t)) : K::kMax;
             }
 #pragma unroll
             for (int t = 0; t < ITEMS; ++t) x[t] = min(a[t], b[ITEMS - 1 - t]);
             bitonic_clean<ITEMS>(x);
-#pragma unroll
-            for (int t = 0; t < ITEMS; ++t) st_elem<Key>(row, KW * t, x[t]);
         } else {
 #pragma unroll
             for (int t = 0; t < ITEMS; ++t) {
@@ -641,18 +674,33 @@ __global__ __launch_bounds__(THREADS) void merge_tiles_kernel(
                         be = piece_b(q + 1);
                     }
                     // (a side's end reads word 0 instead; that value is not taken)
-                    const Key ka = ld_elem<Key>(win, i < a_len ? KW * i : 0);
-                    const Key kb = ld_elem<Key>(win, j < b_len ? KW * (a_len + j) : 0);
+                    const Key ka = ld_elem<Key>(win, i < a_len ? offA + KW * i : 0);
+                    const Key kb = ld_elem<Key>(win, j < b_len ? offB + KW * j : 0);
                     const bool take_a = i < ae && (j >= be || ka <= kb);
-                    st_elem<Key>(row, KW * t, take_a ? ka : kb);
+                    x[t] = take_a ? ka : kb;
                     if constexpr (KV) {
-                        const int src = take_a ? i : a_len + j;
+                        const int src = take_a ? vA + VW * i : vB + VW * j;
 #pragma unroll
-                        for (int v = 0; v < VW; ++v) vrow[VW * t + v] = vwin[VW * src + v];
+                        for (int v = 0; v < VW; ++v) vx[VW * t + v] = vwin[src + v];
                     }
                     i += take_a ? 1 : 0;
                     j += take_a ? 0 : 1;
                 }
+            }
+        }
+    }
+    __syncthreads();  // the window is read; its words now hold the stages
+    if (o0 < c_len) {
+        int* const row = stage + stage_word(tid * ITEMS * KW);
+#pragma unroll
+        for (int t = 0; t < ITEMS; ++t) {
+            if (o0 + t < c_len) st_elem<Key>(row, KW * t, x[t]);
+        }
+        if constexpr (KV) {
+            int* const vrow = vstage + stage_word(tid * ITEMS * VW);
+#pragma unroll
+            for (int t = 0; t < ITEMS * VW; ++t) {
+                if (o0 + t / VW < c_len) vrow[t] = vx[t];
             }
         }
     }

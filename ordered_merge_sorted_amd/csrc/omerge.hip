@@ -44,7 +44,7 @@ constexpr int kVersion = 100;  // 0.1.0
 #define OMERGE_SORT_THREADS 1024
 #endif
 #ifndef OMERGE_SHORT_MERGE  // batches averaging fewer outputs per merge use the tile path
-#define OMERGE_SHORT_MERGE 1536
+#define OMERGE_SHORT_MERGE 6144
 #endif
 #ifndef OMERGE_COPY_UNROLL
 #define OMERGE_COPY_UNROLL 4
