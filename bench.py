@@ -239,6 +239,23 @@ def sort_and_batch(om, stream):
     ms = _time(lambda: om.sort(k2, v2, out=ok_, out_vals=ov_, stream=stream), stream)
     log("%-44s %10.3f %14.4g" % ("omerge sort, 2^27 int32 keys + payloads", ms, n2 / (ms * 1e-3)))
     del k2, v2, ok_, ov_, rk, ri
+    # other key types: float32 descending and int64
+    for name, tens, desc in (
+            ("float32 descending", torch.randn(1 << 27, device=dev, generator=g), True),
+            ("int64", torch.randint(-(1 << 62), 1 << 62, (1 << 27,), dtype=torch.int64, device=dev,
+                                    generator=g), False)):
+        o = torch.empty_like(tens)
+        om.sort(tens, descending=desc, out=o, stream=stream)
+        ref = torch.sort(tens, stable=True, descending=desc).values
+        torch.cuda.synchronize()
+        if not torch.equal(o, ref):
+            log("FAILED: omerge sort (%s) differs from torch's stable sort" % name)
+            sys.exit(1)
+        ms = _time(lambda: om.sort(tens, descending=desc, out=o, stream=stream), stream)
+        ms_t = _time(lambda: torch.sort(tens, stable=True, descending=desc), stream)
+        log("%-44s %10.3f %14.4g  (torch.sort %.3f ms)" % (
+            "omerge sort, 2^27 %s keys" % name, ms, tens.numel() / (ms * 1e-3), ms_t))
+        del tens, o, ref
     # 2^15 merges of 4096 + 4096 sorted keys each (2^28 outputs)
     pairs, L = 1 << 15, 4096
     a = torch.sort(keys[:pairs * L].view(pairs, L), dim=1).values.reshape(-1)
@@ -261,6 +278,7 @@ def sort_and_batch(om, stream):
     a = torch.sort(keys[:pairs * L].view(pairs, L), dim=1).values.reshape(-1)
     b = torch.sort(keys[pairs * L:2 * pairs * L].view(pairs, L), dim=1).values.reshape(-1)
     offs = torch.arange(0, pairs * L + 1, L, dtype=torch.int64, device=dev)
+    c = torch.empty(2 * pairs * L, dtype=torch.int32, device=dev)
     om.merge_batched(a, offs, b, offs, out=c, stream=stream)
     ref = torch.sort(torch.cat([a.view(pairs, L), b.view(pairs, L)], dim=1), dim=1).values
     torch.cuda.synchronize()
