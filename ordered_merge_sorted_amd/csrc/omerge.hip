@@ -446,18 +446,13 @@ bool valid_order(int order) {
 }
 int key_bytes(int order) { return (order & 7) >= kKeyI64 ? 8 : 4; }
 
-template <int VW, int ORDER>
-int full_for(const void* A, const void* Av, int64_t m, const void* B, const void* Bv, int64_t n,
-             void* C, void* Cv, hipStream_t stream) {
-    return Path<VW, ORDER>::full(A, Av, m, B, Bv, n, C, Cv, stream);
-}
-
-// Dispatch on the order code (after valid_order) for payload width VW.
-template <int VW>
-int merge_ordered(int order, const void* A, const void* Av, int64_t m, const void* B,
-                  const void* Bv, int64_t n, void* C, void* Cv, hipStream_t stream) {
+// Calls op(Path<VW, ORDER>{}) for the run-time payload width (0, 4 or 8
+// bytes) and order code, which valid_order has accepted: one instantiation
+// per (width, order) pair.
+template <int VW, typename Op>
+int with_order(int order, Op&& op) {
 #define OMERGE_CASE(o) \
-    case o: return full_for<VW, o>(A, Av, m, B, Bv, n, C, Cv, stream);
+    case o: return op(Path<VW, o>{});
     switch (order) {
         OMERGE_CASE(kKeyI32)
         OMERGE_CASE(kKeyU32)
@@ -476,64 +471,11 @@ int merge_ordered(int order, const void* A, const void* Av, int64_t m, const voi
 #undef OMERGE_CASE
 }
 
-template <int VW, int ORDER>
-int batched_for(const void* A, const void* Av, const int64_t* a_off, int64_t m, const void* B,
-                const void* Bv, const int64_t* b_off, int64_t n, int64_t pairs, void* C,
-                void* Cv, hipStream_t stream) {
-    return Path<VW, ORDER>::batched(A, Av, a_off, m, B, Bv, b_off, n, pairs, C, Cv, stream);
-}
-
-template <int VW>
-int batched_ordered(int order, const void* A, const void* Av, const int64_t* a_off, int64_t m,
-                    const void* B, const void* Bv, const int64_t* b_off, int64_t n,
-                    int64_t pairs, void* C, void* Cv, hipStream_t stream) {
-#define OMERGE_CASE(o) \
-    case o: return batched_for<VW, o>(A, Av, a_off, m, B, Bv, b_off, n, pairs, C, Cv, stream);
-    switch (order) {
-        OMERGE_CASE(kKeyI32)
-        OMERGE_CASE(kKeyU32)
-        OMERGE_CASE(kKeyF32)
-        OMERGE_CASE(kKeyI64)
-        OMERGE_CASE(kKeyU64)
-        OMERGE_CASE(kKeyF64)
-        OMERGE_CASE(kKeyI32 | kKeyDescending)
-        OMERGE_CASE(kKeyU32 | kKeyDescending)
-        OMERGE_CASE(kKeyF32 | kKeyDescending)
-        OMERGE_CASE(kKeyI64 | kKeyDescending)
-        OMERGE_CASE(kKeyU64 | kKeyDescending)
-        OMERGE_CASE(kKeyF64 | kKeyDescending)
-        default: return OMERGE_INVALID_ARG;
-    }
-#undef OMERGE_CASE
-}
-
-template <int VW, int ORDER>
-int sort_for(const void* in_k, const void* in_v, void* out_k, void* out_v, int64_t n,
-             hipStream_t stream) {
-    return Path<VW, ORDER>::sort(in_k, in_v, out_k, out_v, n, stream);
-}
-
-template <int VW>
-int sort_ordered(int order, const void* in_k, const void* in_v, void* out_k, void* out_v,
-                 int64_t n, hipStream_t stream) {
-#define OMERGE_CASE(o) \
-    case o: return sort_for<VW, o>(in_k, in_v, out_k, out_v, n, stream);
-    switch (order) {
-        OMERGE_CASE(kKeyI32)
-        OMERGE_CASE(kKeyU32)
-        OMERGE_CASE(kKeyF32)
-        OMERGE_CASE(kKeyI64)
-        OMERGE_CASE(kKeyU64)
-        OMERGE_CASE(kKeyF64)
-        OMERGE_CASE(kKeyI32 | kKeyDescending)
-        OMERGE_CASE(kKeyU32 | kKeyDescending)
-        OMERGE_CASE(kKeyF32 | kKeyDescending)
-        OMERGE_CASE(kKeyI64 | kKeyDescending)
-        OMERGE_CASE(kKeyU64 | kKeyDescending)
-        OMERGE_CASE(kKeyF64 | kKeyDescending)
-        default: return OMERGE_INVALID_ARG;
-    }
-#undef OMERGE_CASE
+template <typename Op>
+int with_shape(int order, int payload_bytes, Op&& op) {
+    if (payload_bytes == 0) return with_order<0>(order, op);
+    if (payload_bytes == 4) return with_order<1>(order, op);
+    return with_order<2>(order, op);
 }
 
 using PathI32 = Path<0, kKeyI32>;
@@ -566,7 +508,9 @@ int omerge_merge_keys(const void* A, int64_t m, const void* B, int64_t n, void* 
     if (!valid_order(order)) return OMERGE_INVALID_ARG;
     int rc = check_merge_args(A, nullptr, m, B, nullptr, n, C, nullptr, key_bytes(order), 0);
     if (rc != OMERGE_OK) return rc;
-    return merge_ordered<0>(order, A, nullptr, m, B, nullptr, n, C, nullptr, stream);
+    return with_shape(order, 0, [&](auto path) {
+        return decltype(path)::full(A, nullptr, m, B, nullptr, n, C, nullptr, stream);
+    });
 }
 
 int omerge_merge_pairs(const void* A_keys, const void* A_vals, int64_t m,
@@ -577,10 +521,9 @@ int omerge_merge_pairs(const void* A_keys, const void* A_vals, int64_t m,
     int rc = check_merge_args(A_keys, A_vals, m, B_keys, B_vals, n, C_keys, C_vals,
                               key_bytes(order), payload_bytes);
     if (rc != OMERGE_OK) return rc;
-    if (payload_bytes == 4)
-        return merge_ordered<1>(order, A_keys, A_vals, m, B_keys, B_vals, n, C_keys, C_vals,
-                                stream);
-    return merge_ordered<2>(order, A_keys, A_vals, m, B_keys, B_vals, n, C_keys, C_vals, stream);
+    return with_shape(order, payload_bytes, [&](auto path) {
+        return decltype(path)::full(A_keys, A_vals, m, B_keys, B_vals, n, C_keys, C_vals, stream);
+    });
 }
 
 int omerge_merge_batched(const void* A_keys, const void* A_vals, const int64_t* a_offsets,
@@ -605,14 +548,12 @@ int omerge_merge_batched(const void* A_keys, const void* A_vals, const int64_t* 
             overlaps(outs[i], out_bytes[i], b_offsets, off_bytes))
             return OMERGE_INVALID_ARG;
     }
-    if (payload_bytes == 0)
-        return batched_ordered<0>(order, A_keys, nullptr, a_offsets, m, B_keys, nullptr,
-                                  b_offsets, n, num_merges, C_keys, nullptr, stream);
-    if (payload_bytes == 4)
-        return batched_ordered<1>(order, A_keys, A_vals, a_offsets, m, B_keys, B_vals,
-                                  b_offsets, n, num_merges, C_keys, C_vals, stream);
-    return batched_ordered<2>(order, A_keys, A_vals, a_offsets, m, B_keys, B_vals, b_offsets, n,
-                              num_merges, C_keys, C_vals, stream);
+    return with_shape(order, payload_bytes, [&](auto path) {
+        const bool kv = payload_bytes != 0;
+        return decltype(path)::batched(A_keys, kv ? A_vals : nullptr, a_offsets, m, B_keys,
+                                       kv ? B_vals : nullptr, b_offsets, n, num_merges, C_keys,
+                                       kv ? C_vals : nullptr, stream);
+    });
 }
 
 int omerge_sort(const void* keys_in, const void* vals_in, void* keys_out, void* vals_out,
@@ -641,9 +582,10 @@ int omerge_sort(const void* keys_in, const void* vals_in, void* keys_out, void* 
             return OMERGE_INVALID_ARG;
     }
     if (n == 0) return OMERGE_OK;
-    if (vb == 0) return sort_ordered<0>(order, keys_in, nullptr, keys_out, nullptr, n, stream);
-    if (vb == 4) return sort_ordered<1>(order, keys_in, vals_in, keys_out, vals_out, n, stream);
-    return sort_ordered<2>(order, keys_in, vals_in, keys_out, vals_out, n, stream);
+    return with_shape(order, vb, [&](auto path) {
+        return decltype(path)::sort(keys_in, vb ? vals_in : nullptr, keys_out,
+                                    vb ? vals_out : nullptr, n, stream);
+    });
 }
 
 int omerge_co_rank(const int32_t* A, int64_t m, const int32_t* B, int64_t n,
