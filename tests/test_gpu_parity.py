@@ -565,6 +565,40 @@ def test_batched_single_merge_is_merge():
     assert_same(host(got), host(om.merge_i32(dev(A), dev(B))), "batch of one")
 
 
+# ------------------------------------------------------ beyond 32-bit indices
+
+
+def test_more_than_2p32_outputs():
+    """m = n = 2^31 + 1000 int32 keys (2^32 + 2000 outputs, 32 GiB in HBM),
+    built on the device with a closed form: A[i] = i >> 2 and B[j] = j >> 2,
+    so the stable merge is C[k] = k >> 3 (each value four times from A, then
+    four times from B) and co_rank(k) = 4*(k >> 3) + min(k & 7, 4).  This
+    checks every output and sampled co-ranks past 2^31 and 2^32, where 32-bit
+    index arithmetic would wrap."""
+    m = n = (1 << 31) + 1000
+    total = m + n
+    say("beyond 2^32", m, n)
+    a = (torch.arange(m, dtype=torch.int64, device=DEV) >> 2).to(torch.int32)
+    b = (torch.arange(n, dtype=torch.int64, device=DEV) >> 2).to(torch.int32)
+    c = om.merge_i32(a, b)
+    chunk = 1 << 28
+    for k0 in range(0, total, chunk):
+        k1 = min(k0 + chunk, total)
+        want = (torch.arange(k0, k1, dtype=torch.int64, device=DEV) >> 3).to(torch.int32)
+        if not torch.equal(c[k0:k1], want):
+            bad = int(torch.nonzero(c[k0:k1] != want)[0, 0]) + k0
+            raise AssertionError("beyond 2^32: first difference at %d" % bad)
+    ks = torch.tensor([0, 1, 7, 8, (1 << 31) - 3, (1 << 31) + 5, (1 << 32) - 1, 1 << 32,
+                       (1 << 32) + 3, total - 1, total], dtype=torch.int64, device=DEV)
+    got = om.co_rank(a, b, ks).cpu().numpy()
+    kk = ks.cpu().numpy()
+    want = 4 * (kk >> 3) + np.minimum(kk & 7, 4)
+    want = np.minimum(want, m)
+    assert np.array_equal(got, want), (got, want)
+    del a, b, c
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------- full-size workloads
 
 @pytest.mark.parametrize("name", ORDER)
