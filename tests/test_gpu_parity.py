@@ -599,6 +599,26 @@ def test_more_than_2p32_outputs():
     torch.cuda.empty_cache()
 
 
+def test_sort_more_than_2p31_keys():
+    """A stable sort of n = 2^31 + 1000 int32 keys with int64 payloads, built
+    on the device: key[i] = (n-1-i) >> 2 and payload[i] = i.  Sorted
+    ascending, output p holds key p >> 2, and the four equal keys keep their
+    input order, so its payload is n - 4 - 4*(p >> 2) + (p & 3)."""
+    n = (1 << 31) + 1000
+    say("sort beyond 2^31", n)
+    i = torch.arange(n, dtype=torch.int64, device=DEV)
+    keys = ((n - 1 - i) >> 2).to(torch.int32)
+    gk, gv = om.sort(keys, i)
+    del keys
+    chunk = 1 << 28
+    for p0 in range(0, n, chunk):
+        p = torch.arange(p0, min(p0 + chunk, n), dtype=torch.int64, device=DEV)
+        assert torch.equal(gk[p0:p0 + p.numel()], (p >> 2).to(torch.int32)), p0
+        assert torch.equal(gv[p0:p0 + p.numel()], n - 4 - 4 * (p >> 2) + (p & 3)), p0
+    del gk, gv, i
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------- full-size workloads
 
 @pytest.mark.parametrize("name", ORDER)
