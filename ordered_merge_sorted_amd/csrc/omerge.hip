@@ -43,6 +43,15 @@ constexpr int kVersion = 100;  // 0.1.0
 #ifndef OMERGE_SORT_THREADS  // lanes of the block sort for 4-byte keys without payloads
 #define OMERGE_SORT_THREADS 1024
 #endif
+#ifndef OMERGE_SORT_THREADS_KV  // lanes of the block sort for 4-byte keys with 4-byte payloads
+#define OMERGE_SORT_THREADS_KV 256
+#endif
+#ifndef OMERGE_SORT_THREADS_WIDE  // lanes of the block sort for 8-byte keys without payloads
+#define OMERGE_SORT_THREADS_WIDE 1024
+#endif
+#ifndef OMERGE_SORT_THREADS_MIXED  // lanes of the block sort for the other shapes
+#define OMERGE_SORT_THREADS_MIXED 512
+#endif
 #ifndef OMERGE_SHORT_MERGE  // batches averaging fewer outputs per merge use the tile path
 #define OMERGE_SHORT_MERGE 6144
 #endif
@@ -186,11 +195,17 @@ struct Path {
     static constexpr int kTile = kThreads * kItems;
     static constexpr int kShape = shape_index(KW, VW);
     // Block sort shape: the first sorted runs are kSortTile elements long.
-    // For 4-byte keys without payloads the block sort uses 1024 lanes
-    // (16,384-key runs, two merge passes fewer; measured 2% faster for 2^28
-    // keys than 256 lanes); other shapes keep the merge's lane count, which
-    // their LDS (positions and payloads) fits.
-    static constexpr int kSortThreads = (KW == 1 && VW == 0) ? OMERGE_SORT_THREADS : kThreads;
+    // Longer runs save whole merge passes (each one read and one write of
+    // the array) at the price of more rounds inside the block sort, and the
+    // lane count is capped by what LDS fits.  Measured on MI355X (2^27 keys,
+    // or 2^26 for 12- and 16-byte elements): 1024 lanes for 4-byte keys alone
+    // (2% faster than 256) and 8-byte keys alone (4%); 512 for the 12- and
+    // 16-byte shapes (3-4%); 256 for 4-byte keys with 4-byte payloads, where
+    // 512 and 1024 were slower.
+    static constexpr int kSortThreads = (KW == 1 && VW == 0)   ? OMERGE_SORT_THREADS
+                                        : (KW == 1 && VW == 1) ? OMERGE_SORT_THREADS_KV
+                                        : (KW == 2 && VW == 0) ? OMERGE_SORT_THREADS_WIDE
+                                                               : OMERGE_SORT_THREADS_MIXED;
     static constexpr int kSortTile = kSortThreads * kItems;
 
     static int seg_len(int64_t m, int64_t n, int64_t* out) {

@@ -82,6 +82,10 @@ static void typed_cfg(const void* A, const void* Av, int64_t m, const void* B, c
 constexpr int production_items(int kw, int vw) {
     return kw == 1 && vw == 0 ? 16 : (kw + vw == 2 ? 8 : 4);
 }
+// Lanes of the library's block sort for each shape.
+constexpr int production_sort_threads(int kw, int vw) {
+    return kw == 1 && vw == 0 ? 1024 : kw == 1 && vw == 1 ? 256 : kw == 2 && vw == 0 ? 1024 : 512;
+}
 
 // Which (order, payload words, shape) combinations this library holds:
 // small shapes (128 lanes, 4 items) for every order keys-only and for a
@@ -214,10 +218,12 @@ static void tiles_cfg(const void* A, const void* Av, const int64_t* a_off, int64
 // Which (order, payload) combinations the sort / batch entries hold: the
 // small shapes for int32 keys-only, float32 descending with 4-byte payloads,
 // int64 with 8-byte payloads and float64 descending keys-only; the library
-// shapes for int32 keys-only and float64 descending with 4-byte payloads.
+// shapes for int32 keys-only or with 8-byte payloads, int64 descending
+// keys-only and float64 descending with 4-byte payloads.
 constexpr bool emu_sort_has(int variant, int order, int vw) {
     if (variant == 0)
-        return (order == 0 && (vw == 0 || vw == 2)) || (order == (5 | 8) && vw == 1);
+        return (order == 0 && (vw == 0 || vw == 2)) || (order == (5 | 8) && vw == 1) ||
+               (order == (3 | 8) && vw == 0);
     return (order == 0 && (vw == 0 || vw == 2)) || (order == (2 | 8) && vw == 1) ||
            (order == 3 && vw == 2) || (order == (5 | 8) && vw == 0);
 }
@@ -234,7 +240,7 @@ static int sort_go(int variant, const void* in_k, const void* in_v, int64_t N, v
     if constexpr (emu_sort_has(0, ORDER, VW)) {
         if (variant == 0) {
             constexpr int kw = omerge::KeyOrder<ORDER>::kWords;
-            constexpr int st = (kw == 1 && VW == 0) ? 1024 : 256;  // the library's block sort
+            constexpr int st = production_sort_threads(kw, VW);
             sort_cfg<256, production_items(kw, VW), VW, ORDER, st>(in_k, in_v, N, out_k, out_v,
                                                                    seg_len);
             return 1;
@@ -399,6 +405,7 @@ int emu_sort(int variant, int order, int vw, const void* in_k, const void* in_v,
     EMU_SORT(3, 2)
     EMU_SORT(13, 0)
     EMU_SORT(13, 1)
+    EMU_SORT(11, 0)
 #undef EMU_SORT
     return 0;
 }
@@ -419,6 +426,7 @@ int emu_batched(int variant, int order, int vw, const void* A, const void* Av,
     EMU_BATCH(3, 2)
     EMU_BATCH(13, 0)
     EMU_BATCH(13, 1)
+    EMU_BATCH(11, 0)
 #undef EMU_BATCH
     return 0;
 }
@@ -427,6 +435,12 @@ int emu_batched(int variant, int order, int vw, const void* A, const void* Av,
 int emu_typed_tile(int variant, int order, int vw) {
     const int kw = (order & 7) >= 3 ? 2 : 1;
     return variant == 0 ? 256 * production_items(kw, vw) : 128 * 4;
+}
+
+// Run length (elements) of the block sort of a shape.
+int emu_sort_tile(int variant, int order, int vw) {
+    const int kw = (order & 7) >= 3 ? 2 : 1;
+    return variant == 0 ? production_sort_threads(kw, vw) * production_items(kw, vw) : 128 * 4;
 }
 
 }  // extern "C"

@@ -38,6 +38,8 @@ def load(path):
     lib.emu_batched.restype = i32
     lib.emu_typed_tile.argtypes = [i32, i32, i32]
     lib.emu_typed_tile.restype = i32
+    lib.emu_sort_tile.argtypes = [i32, i32, i32]
+    lib.emu_sort_tile.restype = i32
     return lib
 
 
@@ -352,7 +354,7 @@ def group_orders(r, g):
 
 
 SORT_COMBOS = [(1, 0, 0), (1, 0, 2), (1, 10, 1), (1, 3, 2), (1, 13, 0), (0, 0, 0), (0, 0, 2),
-               (0, 13, 1)]
+               (0, 13, 1), (0, 11, 0)]
 
 
 def unsorted_keys(g, dtype, n, pools):
@@ -374,9 +376,7 @@ def group_sort(r, g):
     for variant, order, vw in SORT_COMBOS:
         dtype = KIND_DTYPE[order & 7]
         desc = bool(order & 8)
-        tile = r.lib.emu_typed_tile(variant, order, vw)
-        if variant == 0 and order & 7 < 3 and vw == 0:
-            tile *= 4  # the library's 1024-lane block sort for 4-byte keys
+        tile = r.lib.emu_sort_tile(variant, order, vw)  # the block sort's runs
         sizes = [0, 1, 5, tile - 1, tile, tile + 1, 2 * tile + 3] + \
             [int(x) for x in g.integers(3 * tile, 9 * tile if variant else 4 * tile,
                                         size=2 if variant else 1)]

@@ -465,11 +465,13 @@ def unsorted_typed(g, dtype, n):
 @pytest.mark.parametrize("dtype,desc", TYPED, ids=TYPED_IDS)
 def test_sort_keys_and_pairs(dtype, desc):
     """Stable merge sort of every key type and order, keys only and with
-    4- and 8-byte payloads, around tile multiples and over many passes;
-    output bits against the oracle's stable sort."""
+    4- and 8-byte payloads, around the block sort's run lengths (2,048,
+    4,096, 8,192 and 16,384 elements, by shape) and over many passes; output
+    bits against the oracle's stable sort."""
     needs_torch_dtype(dtype)
     g = np.random.Generator(np.random.PCG64(700 + TYPED.index((dtype, desc))))
-    for n in (0, 1, 1023, 1024, 2049, 4095, 4097, 70001, int(g.integers(100000, 300000))):
+    for n in (0, 1, 1023, 1024, 2047, 2048, 2049, 4095, 4097, 8191, 8192, 8193, 16383, 16384,
+              16385, 32769, 70001, int(g.integers(100000, 300000))):
         K = np.ascontiguousarray(unsorted_typed(g, dtype, n))
         say("sort", np.dtype(dtype).name, desc, n)
         got = om.sort(dev_typed(K), descending=desc)
