@@ -9,10 +9,11 @@ kernel, launched through the C ABI on the current torch stream.  The default
 workload is 2^28 + 2^28 int32 keys iid uniform over the int32 range, sorted.
 
 Before timing, the merged output of one untimed launch is compared with the
-CPU oracle on every element (a wrong answer never produces a number), and the
-oracle run is timed as the reported CPU baseline.  Then W untimed steps, then
-exactly K timed steps back to back between device synchronisations (the step
-rate).  The same K steps are then run again with a HIP event pair around
+CPU oracle on every element (a wrong answer never produces a number); that
+oracle run is the first run of the reported CPU baseline, whose other runs
+come after the GPU timing.  Then W untimed steps (the default 50, ~40 ms,
+covers the device's clock ramp after the seconds of CPU work), then exactly
+K timed steps back to back between device synchronisations (the step rate).  The same K steps are then run again with a HIP event pair around
 every segment-merge launch, which gives that kernel's mean duration for the
 roofline figure.  A streaming copy of the same byte count is timed beside it
 as the bandwidth this device actually delivers.
@@ -81,21 +82,25 @@ def device_banner(torch):
     return arch
 
 
-def time_oracle(w, arrs, want_runs_s=10.0, max_runs=5):
-    """Single-threaded CPU oracle on the full workload; repeated until about
-    want_runs_s seconds have passed (at most max_runs).  Returns (out, rates)."""
+def run_oracle(w, arrs):
+    """One single-threaded run of the CPU oracle on the full workload.
+    Returns (out, seconds)."""
     import oracle
-    rates, out = [], None
-    t_all = time.perf_counter()
-    for r in range(max_runs):
-        t0 = time.perf_counter()
-        out = oracle.merge_kv(*arrs) if w.kv else oracle.merge_i32(*arrs)
-        dt = time.perf_counter() - t0
-        rates.append(w.total / dt)
+    t0 = time.perf_counter()
+    out = oracle.merge_kv(*arrs) if w.kv else oracle.merge_i32(*arrs)
+    return out, time.perf_counter() - t0
+
+
+def time_oracle(w, arrs, first_s, want_runs_s=10.0, max_runs=5):
+    """Rates of the single-threaded CPU oracle on the full workload: the run
+    already made for the check (first_s seconds), then more runs until about
+    want_runs_s seconds have passed (at most max_runs in all)."""
+    secs = [first_s]
+    while len(secs) < max_runs and sum(secs) < want_runs_s:
+        secs.append(run_oracle(w, arrs)[1])
+    for r, dt in enumerate(secs):
         log("oracle run %d: %.2f s, %.3g elements/s" % (r, dt, w.total / dt))
-        if time.perf_counter() - t_all >= want_runs_s:
-            break
-    return out, rates
+    return [w.total / dt for dt in secs]
 
 
 def ablation(om, d_arrs, want, w, stream):
@@ -173,8 +178,7 @@ def typed_orders(om, d_arrs, c_ref, w, stream):
                 log("FAILED: key order %s%s differs from the mapped int32 merge" %
                     (name, " desc" if desc else ""))
                 sys.exit(1)
-            for _ in range(5):
-                go()
+            _warm(go)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for _ in range(20):
@@ -188,10 +192,20 @@ def typed_orders(om, d_arrs, c_ref, w, stream):
             del a, b, out, want
 
 
-def _time(fn, stream, reps=5, warm=2):
+def _warm(fn, seconds=0.03):
+    """Runs fn (synchronising) until `seconds` have passed, at least twice:
+    the device leaves its idle clocks before anything is timed."""
     import torch
-    for _ in range(warm):
+    t0, n = time.perf_counter(), 0
+    while n < 2 or time.perf_counter() - t0 < seconds:
         fn()
+        torch.cuda.synchronize()
+        n += 1
+
+
+def _time(fn, stream, reps=5):
+    import torch
+    _warm(fn)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(reps):
@@ -296,7 +310,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=None, help="workload name (default: the int32 2^28+2^28 merge)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the oracle (the output check still runs)")
@@ -360,12 +374,10 @@ def main():
     launch_partition()
     launch_merge()
     torch.cuda.synchronize()
-    if args.no_cpu_baseline:
-        import oracle
-        want = oracle.merge_kv(*arrs) if w.kv else oracle.merge_i32(*arrs)
-        rates = []
-    else:
-        want, rates = time_oracle(w, arrs)
+    # The oracle's run for the check is also the first CPU-baseline run; the
+    # rest of the CPU baseline is timed after the GPU, so that the GPU
+    # timing does not start from a device left idle for seconds.
+    want, oracle_s = run_oracle(w, arrs)
     if args.ablation and not w.kv:
         ablation(om, d_arrs, want, w, stream)
     if w.kv:
@@ -467,6 +479,7 @@ def main():
         log("merge_i32 one call (with its scratch allocation): %.4f ms" % onecall_ms)
 
     cpu = None
+    rates = [] if args.no_cpu_baseline else time_oracle(w, arrs, oracle_s)
     if rates:
         cpu = {"value": float(np.median(rates)), "unit": "merged elements/s", "cores": 1,
                "kind": "oracle",

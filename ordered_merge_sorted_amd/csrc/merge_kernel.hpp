@@ -174,7 +174,25 @@ __host__ __device__ constexpr int stage_word(int p) { return p + ((p >> 5) << 2)
 // the last passing point and at or before the first failing one.  Every
 // round keeps max(0,k-n) <= lo <= hi <= min(k,m) and shrinks the interval,
 // whatever the data, so the loop ends even on unsorted input.  All lanes of
-// the wavefront must call this together (the vote is wavefront-wide).
+// the wavefront must call this together (the votes and shuffles are
+// wavefront-wide).
+//
+// Where the points go.  The first round splits [lo, hi) evenly.  After that
+// the group knows g = image(A[i]) - image(B[k-1-i]) at both ends of the
+// interval (g <= 0 at the last passing point, g >= 1 at the first failing
+// one; g rises with i), and places the points around the linear
+// interpolation of where g crosses 1/2, spread by the larger of
+// 0.7*sqrt(width) (how far the crossing of evenly spread keys strays from
+// the line) and half the width of one unit of key image.  On keys spread
+// evenly over their range this takes about 5 rounds instead of 12 for
+// 2^28+2^28 elements.  An interpolated round that narrows the interval less
+// than an even split would (G+1 times) turns interpolation off for the rest
+// of the search, so clustered or heavily tied keys cost at most about one
+// round more than even splits.  Only the points change: the interval update
+// is the same, so the result is the co-rank whatever the placement.
+#ifndef OMERGE_PART_INTERP
+#define OMERGE_PART_INTERP 1
+#endif
 template <int G, int ORDER>
 __device__ __forceinline__ int64_t co_rank_group(int64_t k,
                                                  const typename KeyOrder<ORDER>::T* __restrict__ A,
@@ -185,26 +203,65 @@ __device__ __forceinline__ int64_t co_rank_group(int64_t k,
     constexpr int kLog = bit_length(G) - 1;
     int64_t lo = k > n ? k - n : 0;
     int64_t hi = k < m ? k : m;
+    // g at the interval's ends once known: at lo - 1 (last passing point)
+    // and at hi (first failing point).
+    double g_lo = 0.0, g_hi = 0.0;
+    bool have_lo = false, have_hi = false;
+    bool even_only = !OMERGE_PART_INTERP;
     for (int round = 0; round < 64; ++round) {
         if (__ballot(lo < hi) == 0) break;  // every group of the wavefront is done
         const int64_t span = hi - lo;
+        double centre = 0.0, spread = 0.0;
+        bool interp = false;
+        if (!even_only && have_lo && have_hi && g_hi > g_lo) {
+            const double w = static_cast<double>(span + 1);  // from lo - 1 to hi
+            const double unit = w / (g_hi - g_lo);           // outputs per unit of image
+            centre = static_cast<double>(lo - 1) + (0.5 - g_lo) * unit;
+            spread = fmax(1.0, fmax(0.7 * sqrt(w), 0.5 * unit));
+            interp = (G - 1) * spread < 0.5 * static_cast<double>(span);
+        }
         const int64_t q = span >> kLog, r = span & (G - 1);
-        const int live = span < G ? static_cast<int>(span) : G;
-        // l-th point: lo + floor(span*l/G) for long intervals, lo + l for short.
+        const int live = interp || span >= G ? G : static_cast<int>(span);
+        // l-th point: lo + floor(span*l/G) for long intervals, lo + l for
+        // short; or centre + spread*(l - (G-1)/2), clamped into [lo, hi-1]
+        // (in double first, so that the conversion stays in range; then
+        // exactly, against rounding).
+        const double dlo = static_cast<double>(lo), dhi = static_cast<double>(hi - 1);
         auto point = [=](int l) -> int64_t {
+            if (interp) {
+                const double p = rint(centre + spread * (0.5 * (2 * l - (G - 1))));
+                const int64_t i = static_cast<int64_t>(fmin(fmax(p, dlo), dhi));
+                return i < lo ? lo : (i > hi - 1 ? hi - 1 : i);
+            }
             return span < G ? lo + l : lo + q * l + ((r * l) >> kLog);
         };
         const int64_t p = point(g_lane);
         bool pass = false;
-        if (g_lane < live)
-            pass = KeyOrder<ORDER>::to_ord(A[p]) <= KeyOrder<ORDER>::to_ord(B[k - 1 - p]);
+        double g = 0.0;
+        if (g_lane < live) {
+            const auto a = KeyOrder<ORDER>::to_ord(A[p]);
+            const auto b = KeyOrder<ORDER>::to_ord(B[k - 1 - p]);
+            pass = a <= b;
+            g = static_cast<double>(a) - static_cast<double>(b);
+        }
         const unsigned long long votes = __ballot(pass);
         const unsigned long long mine =
             G == 64 ? votes : (votes >> g_shift) & ((1ull << (G == 64 ? 0 : G)) - 1);
         const int c = __popcll(mine);
+        const double g_left = __shfl(g, g_shift + (c > 0 ? c - 1 : 0));
+        const double g_right = __shfl(g, g_shift + (c < live ? c : 0));
         if (lo < hi) {
             const int64_t new_lo = c > 0 ? point(c - 1) + 1 : lo;
             const int64_t new_hi = c < live ? point(c) : hi;
+            if (c > 0) {
+                g_lo = g_left;
+                have_lo = true;
+            }
+            if (c < live) {
+                g_hi = g_right;
+                have_hi = true;
+            }
+            if (interp && (new_hi - new_lo) * (G + 1) > span) even_only = true;
             lo = new_lo;
             hi = new_hi;
         }

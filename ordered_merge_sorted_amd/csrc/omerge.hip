@@ -16,14 +16,23 @@ namespace {
 constexpr int kVersion = 100;  // 0.1.0
 
 // Kernel shapes (compile-time tunables; the defaults are the measured best
-// on MI355X).  256 lanes = 4 wavefronts per workgroup.  Key-only tiles hold
-// 4096 outputs; key+payload tiles hold 2048 so both fit three workgroups per
-// CU in the 160 KB of LDS.
+// on MI355X).  256 lanes = 4 wavefronts per workgroup.  Segment-merge tiles
+// hold 2048 outputs for 4-byte keys alone and for 4+4-byte pairs, 1024 for
+// the wider elements: about 8-16 KB of elements per tile, which fits six
+// (keys alone) or three workgroups per CU in the 160 KB of LDS.  The block
+// sort and the tile path for batches of short merges keep 16 outputs per
+// lane for 4-byte keys alone (longer first runs, fewer tiles).
 #ifndef OMERGE_THREADS
 #define OMERGE_THREADS 256
 #endif
 #ifndef OMERGE_ITEMS_I32
-#define OMERGE_ITEMS_I32 16
+#define OMERGE_ITEMS_I32 8
+#endif
+#ifndef OMERGE_SORT_ITEMS_I32  // block sort, 4-byte keys alone
+#define OMERGE_SORT_ITEMS_I32 16
+#endif
+#ifndef OMERGE_TILE_ITEMS_I32  // tile path for short merges, 4-byte keys alone
+#define OMERGE_TILE_ITEMS_I32 16
 #endif
 #ifndef OMERGE_ITEMS_KV
 #define OMERGE_ITEMS_KV 8
@@ -31,8 +40,11 @@ constexpr int kVersion = 100;  // 0.1.0
 #ifndef OMERGE_PART_LANES  // lanes per boundary in the partition search (1 = pages' loop)
 #define OMERGE_PART_LANES 4
 #endif
-#ifndef OMERGE_TILES_PER_SEG  // target tiles per workgroup segment
-#define OMERGE_TILES_PER_SEG 8
+#ifndef OMERGE_TILES_PER_SEG  // target tiles per workgroup segment of one merge
+#define OMERGE_TILES_PER_SEG 6
+#endif
+#ifndef OMERGE_TILES_PER_DESC_SEG  // the same for sort passes and batches
+#define OMERGE_TILES_PER_DESC_SEG 8
 #endif
 #ifndef OMERGE_ITEMS_WIDE  // 64-bit keys, keys only
 #define OMERGE_ITEMS_WIDE 8
@@ -60,19 +72,30 @@ constexpr int kVersion = 100;  // 0.1.0
 #endif
 constexpr int kThreads = OMERGE_THREADS;
 constexpr int kPartLanes = OMERGE_PART_LANES;
-constexpr int kTargetTilesPerSeg = OMERGE_TILES_PER_SEG;
-constexpr int kMinTilesPerSeg = kTargetTilesPerSeg > 2 ? kTargetTilesPerSeg - 2 : 1;
-constexpr int kMaxTilesPerSeg = kTargetTilesPerSeg + 2;
+// Segment-length windows: target R and the half-width searched around it.
+struct SegWindow {
+    int target, slack;
+};
+constexpr SegWindow kMergeWindow{OMERGE_TILES_PER_SEG, 1};
+constexpr SegWindow kDescWindow{OMERGE_TILES_PER_DESC_SEG, 2};
 constexpr int kCopyUnroll = OMERGE_COPY_UNROLL;  // 16-byte vectors per lane in the copy
 
-// Outputs per lane for KW key words and VW payload words per element: about
-// 64 bytes of element per lane, so every shape's tile moves ~16 KB and its
-// LDS (two rings and a stage per array) fits three workgroups per CU.
+// Outputs per lane of the segment merge for KW key words and VW payload
+// words per element: 32 bytes of element per lane for 4-byte keys alone
+// (six workgroups per CU), 64 for the other shapes (three per CU; their
+// LDS holds two rings and a stage per array).  The block sort and the tile
+// path have their own counts for 4-byte keys alone.
 constexpr int items_for(int kw, int vw) {
     return kw == 1 && vw == 0   ? OMERGE_ITEMS_I32
            : kw == 1 && vw == 1 ? OMERGE_ITEMS_KV
            : kw == 2 && vw == 0 ? OMERGE_ITEMS_WIDE
                                 : OMERGE_ITEMS_MIXED;
+}
+constexpr int sort_items_for(int kw, int vw) {
+    return kw == 1 && vw == 0 ? OMERGE_SORT_ITEMS_I32 : items_for(kw, vw);
+}
+constexpr int tile_items_for(int kw, int vw) {
+    return kw == 1 && vw == 0 ? OMERGE_TILE_ITEMS_I32 : items_for(kw, vw);
 }
 constexpr int shape_index(int kw, int vw) { return (kw - 1) * 3 + vw; }
 constexpr int kShapes = 6;
@@ -127,28 +150,33 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Segment length: a whole number R of tiles per workgroup.  Two costs pull
 // R in opposite directions.  The partition reads a few random cache lines
-// per boundary, so short segments make it expensive (131072 one-tile
-// segments of the 2^28+2^28 merge: 0.21 ms of partition).  Long segments
+// per boundary, so short segments make it expensive (the 2^28+2^28 merge
+// cut into 8,192-output segments: 36 us of partition).  Long segments
 // spread the workgroups resident at one time over a wide span of A, B and C
 // (about slots*R tiles), and HBM serves such scattered streams more slowly
-// than one compact moving window (the same merge at 19 tiles per segment:
-// 0.827 ms; at 8: 0.799 ms).  Measured on MI355X, R = 8 balances the two;
-// the window [6, 10] is searched for the R whose last round of workgroups is
-// fullest.  Inputs with fewer tiles than about 6 rounds' worth get the
-// smallest R that keeps a single round.
-int64_t choose_seg_len(int64_t total, int tile, int slots) {
+// than one compact moving window (2048-output tiles at 9 or 10 per segment:
+// 0.80 ms of merge; at 5 to 8: 0.75-0.78 ms).  Measured on MI355X, R = 6
+// balances the two for one merge, searched over [5, 7] for the R whose last
+// round of workgroups is fullest.  Sort passes and batches (descriptor
+// segments, cut again at every run or merge end) measured 2-5% faster per
+// pass with R = 8 searched over [6, 10].  Inputs with fewer tiles than the
+// window's low end times the slots get the smallest R that keeps a single
+// round.
+int64_t choose_seg_len(int64_t total, int tile, int slots, SegWindow win) {
+    const int64_t lo_r = win.target > win.slack ? win.target - win.slack : 1;
+    const int64_t hi_r = win.target + win.slack;
     const int64_t tiles = ceil_div(total, tile);
-    if (tiles <= int64_t(slots) * kMinTilesPerSeg) {
+    if (tiles <= int64_t(slots) * lo_r) {
         const int64_t r = ceil_div(tiles, slots);
         return (r < 1 ? 1 : r) * tile;
     }
-    int64_t best_r = kTargetTilesPerSeg;
+    int64_t best_r = win.target;
     double best_score = -1.0;
-    for (int64_t r = kMinTilesPerSeg; r <= kMaxTilesPerSeg; ++r) {
+    for (int64_t r = lo_r; r <= hi_r; ++r) {
         const int64_t segs = ceil_div(tiles, r);
         const int64_t rounds = ceil_div(segs, slots);
         const double eff = double(tiles) / double(rounds * r * slots);
-        const int64_t off = r > kTargetTilesPerSeg ? r - kTargetTilesPerSeg : kTargetTilesPerSeg - r;
+        const int64_t off = r > win.target ? r - win.target : win.target - r;
         const double score = eff - 0.004 * double(off);  // prefer R near the target
         if (score > best_score) {
             best_score = score;
@@ -193,6 +221,9 @@ struct Path {
     static constexpr int KW = KeyOrder<ORDER>::kWords;
     static constexpr int kItems = items_for(KW, VW);
     static constexpr int kTile = kThreads * kItems;
+    static constexpr int kTileItems = tile_items_for(KW, VW);  // tile path
+    static constexpr int kBatchTile = kThreads * kTileItems;
+    static constexpr int kSortItems = sort_items_for(KW, VW);
     static constexpr int kShape = shape_index(KW, VW);
     // Block sort shape: the first sorted runs are kSortTile elements long.
     // Longer runs save whole merge passes (each one read and one write of
@@ -206,16 +237,16 @@ struct Path {
                                         : (KW == 1 && VW == 1) ? OMERGE_SORT_THREADS_KV
                                         : (KW == 2 && VW == 0) ? OMERGE_SORT_THREADS_WIDE
                                                                : OMERGE_SORT_THREADS_MIXED;
-    static constexpr int kSortTile = kSortThreads * kItems;
+    static constexpr int kSortTile = kSortThreads * kSortItems;
 
-    static int seg_len(int64_t m, int64_t n, int64_t* out) {
+    static int seg_len(int64_t m, int64_t n, int64_t* out, SegWindow win = kMergeWindow) {
         int cus = 0, per_cu = 0;
         int rc = device_slots(kShape,
                               reinterpret_cast<const void*>(
                                   merge_segments_kernel<kThreads, kItems, VW, ORDER>),
                               &cus, &per_cu);
         if (rc != OMERGE_OK) return rc;
-        *out = choose_seg_len(m + n, kTile, cus * per_cu);
+        *out = choose_seg_len(m + n, kTile, cus * per_cu, win);
         return OMERGE_OK;
     }
 
@@ -261,7 +292,7 @@ struct Path {
     static int batched_tiles(const Key* a, const void* Av, const int64_t* a_off, int64_t m,
                              const Key* b, const void* Bv, const int64_t* b_off, int64_t n,
                              int64_t pairs, void* C, void* Cv, hipStream_t stream) {
-        const int64_t tiles = ceil_div(m + n, kTile);
+        const int64_t tiles = ceil_div(m + n, kBatchTile);
         const int64_t blocks = ceil_div((tiles + 1) * kPartLanes, 256);
         if (tiles > kMaxGridBlocks || blocks > kMaxGridBlocks) return OMERGE_OVERFLOW;
         TileBound* tb = nullptr;
@@ -270,11 +301,11 @@ struct Path {
         if (e != hipSuccess) return hip_fail(e);
         hipLaunchKernelGGL((plan_tiles_kernel<kPartLanes, ORDER>),
                            dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, a, a_off, m,
-                           b, b_off, n, pairs, static_cast<int64_t>(kTile), tiles, tb);
+                           b, b_off, n, pairs, static_cast<int64_t>(kBatchTile), tiles, tb);
         e = hipGetLastError();
         int rc = e == hipSuccess ? OMERGE_OK : hip_fail(e);
         if (rc == OMERGE_OK) {
-            hipLaunchKernelGGL((merge_tiles_kernel<kThreads, kItems, VW, ORDER>),
+            hipLaunchKernelGGL((merge_tiles_kernel<kThreads, kTileItems, VW, ORDER>),
                                dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, stream, a,
                                static_cast<const uint32_t*>(Av), a_off, m, b,
                                static_cast<const uint32_t*>(Bv), b_off, n, pairs, tb,
@@ -300,7 +331,7 @@ struct Path {
             return batched_tiles(static_cast<const Key*>(A), Av, a_off, m,
                                  static_cast<const Key*>(B), Bv, b_off, n, pairs, C, Cv, stream);
         int64_t sl = 0;
-        int rc = seg_len(m, n, &sl);
+        int rc = seg_len(m, n, &sl, kDescWindow);
         if (rc != OMERGE_OK) return rc;
         const int64_t segs = pairs + ceil_div(total, sl) - 1;
         const int64_t blocks = ceil_div((segs + 1) * kPartLanes, 256);
@@ -336,7 +367,7 @@ struct Path {
         int passes = 0;
         for (int64_t run = kSortTile; run < N; run *= 2) ++passes;
         int64_t sl = 0;
-        int rc = seg_len(N, 0, &sl);
+        int rc = seg_len(N, 0, &sl, kDescWindow);
         if (rc != OMERGE_OK) return rc;
         int64_t max_segs = 0;
         for (int64_t run = kSortTile; run < N; run *= 2) {
@@ -366,7 +397,7 @@ struct Path {
         Key* bufk[2] = {static_cast<Key*>(out_k), sk};
         uint32_t* bufv[2] = {static_cast<uint32_t*>(out_v), sv};
         int cur = passes % 2;  // block sort target: the last pass then writes out
-        hipLaunchKernelGGL((block_sort_kernel<kSortThreads, kItems, VW, ORDER>),
+        hipLaunchKernelGGL((block_sort_kernel<kSortThreads, kSortItems, VW, ORDER>),
                            dim3(static_cast<unsigned>(tiles)), dim3(kSortThreads), 0, stream,
                            static_cast<const Key*>(in_k), static_cast<const uint32_t*>(in_v), N,
                            bufk[cur], bufv[cur]);

@@ -23,6 +23,7 @@ void __syncthreads() { g_barrier->arrive_and_wait(); }
 struct WaveVote {
     std::barrier<> bar{64};
     int pred[64] = {};
+    double val[64] = {};
 };
 static std::vector<WaveVote>* g_waves = nullptr;
 unsigned long long __ballot(int pred) {
@@ -34,6 +35,16 @@ unsigned long long __ballot(int pred) {
     for (int l = 0; l < 64; ++l) mask |= static_cast<unsigned long long>(w.pred[l]) << l;
     w.bar.arrive_and_wait();
     return mask;
+}
+
+double __shfl(double var, int src) {
+    WaveVote& w = (*g_waves)[threadIdx.x / 64];
+    const int lane = threadIdx.x % 64;
+    w.val[lane] = var;
+    w.bar.arrive_and_wait();
+    const double got = w.val[src & 63];
+    w.bar.arrive_and_wait();
+    return got;
 }
 
 // Runs `body` for every workgroup 0..blocks-1 with `threads` lanes each.
@@ -80,7 +91,15 @@ static void typed_cfg(const void* A, const void* Av, int64_t m, const void* B, c
 
 // Outputs per lane of the library's shapes (its items_for).
 constexpr int production_items(int kw, int vw) {
-    return kw == 1 && vw == 0 ? 16 : (kw + vw == 2 ? 8 : 4);
+    return kw == 1 && vw == 0 ? 8 : (kw + vw == 2 ? 8 : 4);
+}
+// Outputs per lane of the library's block sort and of its tile path for
+// short merges (16 for 4-byte keys alone, else the segment merge's count).
+constexpr int production_sort_items(int kw, int vw) {
+    return kw == 1 && vw == 0 ? 16 : production_items(kw, vw);
+}
+constexpr int production_tile_items(int kw, int vw) {
+    return kw == 1 && vw == 0 ? 16 : production_items(kw, vw);
 }
 // Lanes of the library's block sort for each shape.
 constexpr int production_sort_threads(int kw, int vw) {
@@ -122,11 +141,11 @@ static bool typed_go(int variant, const void* A, const void* Av, int64_t m, cons
 // The merge-sort pipeline of the library (block sort with ST lanes, then
 // plan + merge per pass, ping-pong between out and a scratch copy), for one
 // shape.
-template <int T, int I, int VW, int ORDER, int ST = T>
+template <int T, int I, int VW, int ORDER, int ST = T, int SI = I>
 static void sort_cfg(const void* in_k, const void* in_v, int64_t N, void* out_k, void* out_v,
                      int64_t seg_len) {
     using Key = typename omerge::KeyOrder<ORDER>::T;
-    constexpr int kTile = ST * I;  // the block sort's runs
+    constexpr int kTile = ST * SI;  // the block sort's runs
     if (N == 0) return;
     int passes = 0;
     for (int64_t run = kTile; run < N; run *= 2) ++passes;
@@ -142,7 +161,7 @@ static void sort_cfg(const void* in_k, const void* in_v, int64_t N, void* out_k,
     int cur = passes % 2;
     const int64_t tiles = (N + kTile - 1) / kTile;
     run_grid(tiles, ST, [&] {
-        omerge::block_sort_kernel<ST, I, VW, ORDER>(static_cast<const Key*>(in_k),
+        omerge::block_sort_kernel<ST, SI, VW, ORDER>(static_cast<const Key*>(in_k),
                                                    static_cast<const uint32_t*>(in_v), N,
                                                    bufk[cur], bufv[cur]);
     });
@@ -241,8 +260,8 @@ static int sort_go(int variant, const void* in_k, const void* in_v, int64_t N, v
         if (variant == 0) {
             constexpr int kw = omerge::KeyOrder<ORDER>::kWords;
             constexpr int st = production_sort_threads(kw, VW);
-            sort_cfg<256, production_items(kw, VW), VW, ORDER, st>(in_k, in_v, N, out_k, out_v,
-                                                                   seg_len);
+            sort_cfg<256, production_items(kw, VW), VW, ORDER, st,
+                     production_sort_items(kw, VW)>(in_k, in_v, N, out_k, out_v, seg_len);
             return 1;
         }
     }
@@ -263,8 +282,8 @@ static int batched_go(int variant, const void* A, const void* Av, const int64_t*
         if constexpr (emu_sort_has(0, ORDER, VW)) {
             if (variant == 0) {
                 constexpr int kw = omerge::KeyOrder<ORDER>::kWords;
-                tiles_cfg<256, production_items(kw, VW), VW, ORDER>(A, Av, a_off, m, B, Bv, b_off,
-                                                                    n, pairs, C, Cv);
+                tiles_cfg<256, production_tile_items(kw, VW), VW, ORDER>(A, Av, a_off, m, B, Bv,
+                                                                         b_off, n, pairs, C, Cv);
                 return 1;
             }
         }
@@ -317,7 +336,7 @@ extern "C" {
 // 4 items) that wrap the rings many times on small inputs.
 int emu_tile(int variant, int kv) {
     if (variant == 0) return kv ? omerge::MergeCfg<256, 8, 1, 1>::kTile
-                                : omerge::MergeCfg<256, 16, 1, 0>::kTile;
+                                : omerge::MergeCfg<256, 8, 1, 0>::kTile;
     return omerge::MergeCfg<128, 4, 1, 0>::kTile;
 }
 
@@ -353,7 +372,7 @@ void emu_direct(const int32_t* A, int64_t m, const int32_t* B, int64_t n, int32_
 void emu_merge_i32(int variant, const int32_t* A, int64_t m, const int32_t* B, int64_t n,
                    const int64_t* part, int64_t seg_len, int32_t* C) {
     if (variant == 0)
-        merge_cfg<256, 16, 0>(A, nullptr, m, B, nullptr, n, part, seg_len, C, nullptr);
+        merge_cfg<256, 8, 0>(A, nullptr, m, B, nullptr, n, part, seg_len, C, nullptr);
     else
         merge_cfg<128, 4, 0>(A, nullptr, m, B, nullptr, n, part, seg_len, C, nullptr);
 }
@@ -440,7 +459,8 @@ int emu_typed_tile(int variant, int order, int vw) {
 // Run length (elements) of the block sort of a shape.
 int emu_sort_tile(int variant, int order, int vw) {
     const int kw = (order & 7) >= 3 ? 2 : 1;
-    return variant == 0 ? production_sort_threads(kw, vw) * production_items(kw, vw) : 128 * 4;
+    return variant == 0 ? production_sort_threads(kw, vw) * production_sort_items(kw, vw)
+                        : 128 * 4;
 }
 
 }  // extern "C"

@@ -8,6 +8,12 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <cmath>
+using std::fmax;
+using std::fmin;
+using std::rint;
+using std::sqrt;
+
 #define __global__
 #define __device__
 #define __host__
@@ -27,6 +33,9 @@ void __syncthreads();
 // Wavefront vote: every lane of the 64-lane wavefront must call it together
 // (the emulator meets them at a per-wavefront barrier).
 unsigned long long __ballot(int pred);
+// Wavefront shuffle: lane `src` of the caller's 64-lane wavefront (same
+// meeting rule as __ballot).
+double __shfl(double var, int src);
 inline int __popcll(unsigned long long x) { return __builtin_popcountll(x); }
 template <typename T>
 inline T min(T a, T b) { return b < a ? b : a; }

@@ -200,8 +200,8 @@ def group_blocks(r, g):
 
 
 def group_production(r, g):
-    """The shapes the library launches (256 lanes; 4096-output tiles for
-    keys, 2048 for key+payload), over several tiles and segments."""
+    """The shapes the library launches (256 lanes; 2048-output tiles for
+    keys alone and for key+payload), over several tiles and segments."""
     for kv in (False, True):
         tile = r.lib.emu_tile(0, int(kv))
         for c in range(4):
@@ -214,6 +214,39 @@ def group_production(r, g):
                 r.case_kv(0, A, B, seg_len, tuple(int(x) for x in g.integers(0, 4, size=6)), "prod")
             else:
                 r.case_i32(0, A, B, seg_len, tuple(int(x) for x in g.integers(0, 4, size=3)), "prod")
+
+
+def group_search(r, g):
+    """Key distributions chosen against the partition's interpolated probe
+    placement: clustered, exponential, two-valued, all equal, nearly linear
+    with jumps, and the int32 extremes.  Partitions at every search width
+    against the oracle's co-ranks (exact whatever the placement)."""
+    n0 = 60000
+    lo32, hi32 = -(1 << 31), (1 << 31) - 1
+    cases = [
+        ("clustered", np.concatenate([g.integers(0, 1000, n0 // 2), g.integers(10**9, 2 * 10**9, n0 // 2)]),
+         g.integers(0, 2 * 10**9, n0)),
+        ("exponential", (g.exponential(1.0, n0) * 1e6).astype(np.int64),
+         (g.exponential(1.0, n0 // 3) * 1e6).astype(np.int64)),
+        ("two-valued", g.integers(0, 2, n0), g.integers(0, 2, n0 // 2)),
+        ("all equal", np.full(n0, 5), np.full(n0 // 4, 5)),
+        ("linear with jumps", 3 * np.arange(n0) + 1000 * (np.arange(n0) > n0 // 3),
+         3 * np.arange(n0) + 1 + 10**6 * (np.arange(n0) > 2 * n0 // 3)),
+        ("extremes", g.choice([lo32, lo32 + 1, -1, 0, 1, hi32 - 1, hi32], n0),
+         g.integers(lo32, hi32, n0, endpoint=True)),
+        ("one huge gap", np.concatenate([np.arange(n0 // 2), hi32 - np.arange(n0 // 2)[::-1]]),
+         g.integers(0, n0, n0)),
+    ]
+    for c, (label, A, B) in enumerate(cases):
+        A = np.sort(np.asarray(A, dtype=np.int64)).astype(np.int32)
+        B = np.sort(np.asarray(B, dtype=np.int64)).astype(np.int32)
+        if c % 2:
+            A, B = B, A
+        seg_len = int(g.choice([389, 1000, 4096]))
+        part = r.partition(A, B, seg_len, widths=(4, 1, 8, 64))
+        I = oracle.co_rank_all(A, B)
+        ks = np.minimum(np.arange(part.size, dtype=np.int64) * seg_len, A.size + B.size)
+        r.check(np.array_equal(part, I[ks]), ("search", label, A.size, B.size, seg_len))
 
 
 def group_unsorted(r, g):
@@ -479,7 +512,7 @@ def group_batched_garbage(r, g):
             r.cases += 1
 
 
-GROUPS = {"batched_garbage": group_batched_garbage, "sort": group_sort, "batched": group_batched, "orders": group_orders, "small": group_small, "direct": group_direct, "skew": group_skew, "blocks": group_blocks,
+GROUPS = {"search": group_search, "batched_garbage": group_batched_garbage, "sort": group_sort, "batched": group_batched, "orders": group_orders, "small": group_small, "direct": group_direct, "skew": group_skew, "blocks": group_blocks,
           "production": group_production, "unsorted": group_unsorted}
 
 if __name__ == "__main__":

@@ -37,7 +37,7 @@ FLAG_SETS = {
     "default": [],
     "plain_access": ["-DOMERGE_NT_LOADS=0", "-DOMERGE_NT_STORES=0"],
 }
-CORE_GROUPS = ["small", "skew", "blocks", "direct", "production", "unsorted"]
+CORE_GROUPS = ["small", "skew", "blocks", "direct", "production", "unsorted", "search"]
 # The typed, sort and batch groups exercise the same load and store helpers
 # as the core groups, so they run in the default build only.
 WIDE_GROUPS = ["orders", "sort", "batched", "batched_garbage"]
