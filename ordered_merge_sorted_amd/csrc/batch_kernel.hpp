@@ -318,18 +318,22 @@ __global__ __launch_bounds__(THREADS) void block_sort_kernel(
         const int a0 = (tid - u) * ITEMS;    // the pair's A run; B run at a0 + run
         const int b0 = a0 + run;
         const int o_end = (u + 1) * ITEMS;
-        // Co-rank of o_end (bisection, as in the segment merge).
-        int lo = o_end > run ? o_end - run : 0;
-        int hi = o_end < run ? o_end : run;
-        const int steps = bit_length(run);
-        for (int step = 0; step < steps; ++step) {
-            const int mid = (lo + hi) >> 1;
-            const Key av = ld_elem<Key>(kbuf, stage_word(KW * (a0 + mid)));
-            const Key bv = ld_elem<Key>(kbuf, stage_word(KW * (b0 + o_end - 1 - mid)));
-            const bool lv = lo < hi;
-            const bool a_first = av <= bv;
-            lo = (lv && a_first) ? mid + 1 : lo;
-            hi = (lv && !a_first) ? mid : hi;
+        // Co-rank of o_end: the largest x in [x_lo, x_hi] such that A[x-1]
+        // comes before B[o_end-x] (A[x-1] <= B[o_end-x]; true at x_lo; the
+        // passing points form a prefix), found by binary lifting: steps of
+        // run, run/2, ..., 1 (they sum past the range, which is at most run
+        // wide), each kept when its point passes.  Every tested point x in
+        // (x_lo, x_hi] reads A[x-1] and B[o_end-x], both inside the pair's
+        // runs.
+        const int x_lo = o_end > run ? o_end - run : 0;
+        const int x_hi = o_end < run ? o_end : run;
+        int lo = x_lo;
+        for (int step = run; step > 0; step >>= 1) {
+            const int p = lo + step;
+            const int pc = p < x_hi ? p : x_hi;
+            const Key av = ld_elem<Key>(kbuf, stage_word(KW * (a0 + pc - 1)));
+            const Key bv = ld_elem<Key>(kbuf, stage_word(KW * (b0 + o_end - pc)));
+            lo = (p <= x_hi && av <= bv) ? p : lo;
         }
         split[tid] = lo;
         __syncthreads();
@@ -351,10 +355,12 @@ __global__ __launch_bounds__(THREADS) void block_sort_kernel(
                 a[t] = ld_elem<Key>(pa, KW * t + (KW * t >= ca ? 4 : 0));
                 b[t] = ld_elem<Key>(pb, KW * t + (KW * t >= cb ? 4 : 0));
             }
+            if (s + ITEMS > run || bs + ITEMS > run) {  // rare past the first rounds
 #pragma unroll
-            for (int t = 0; t < ITEMS; ++t) {
-                a[t] = t < run - s ? a[t] : K::kMax;
-                b[t] = t < run - bs ? b[t] : K::kMax;
+                for (int t = 0; t < ITEMS; ++t) {
+                    a[t] = t < run - s ? a[t] : K::kMax;
+                    b[t] = t < run - bs ? b[t] : K::kMax;
+                }
             }
 #pragma unroll
             for (int t = 0; t < ITEMS; ++t) x[t] = min(a[t], b[ITEMS - 1 - t]);
