@@ -646,6 +646,51 @@ def test_workload_bit_exact(name):
             assert np.array_equal(got[:h], np.arange(h, dtype=np.int32))
 
 
+def _check_partition(A, B, part, seg_len):
+    """Each boundary's co-rank is the unique split that passes the acceptance
+    test A[i-1] <= B[j] and B[j-1] < A[i] (j = k - i), with the usual
+    exemptions at the array ends."""
+    m, n = A.size, B.size
+    ks = np.minimum(np.arange(part.size, dtype=np.int64) * seg_len, m + n)
+    I, J = part, ks - part
+    assert np.all((I >= np.maximum(0, ks - n)) & (I <= np.minimum(ks, m)))
+    A64, B64 = A.astype(np.int64), B.astype(np.int64)
+    ok_lo = (I == 0) | (J == n) | (A64[np.clip(I - 1, 0, m - 1)] <= B64[np.clip(J, 0, n - 1)])
+    ok_hi = (J == 0) | (I == m) | (B64[np.clip(J - 1, 0, n - 1)] < A64[np.clip(I, 0, m - 1)])
+    assert np.all(ok_lo & ok_hi)
+
+
+@pytest.mark.parametrize("shape", ["clustered", "four_values", "exponential"])
+def test_partition_full_size_key_shapes(shape):
+    """The partition's probe placement interpolates on the keys and falls
+    back to even splits where that fails; at 2^27 + 2^27 keys shaped against
+    it (half of A in a tiny range, four distinct values, exponential), every
+    boundary must still be the exact co-rank and the merge bit-exact."""
+    n = 1 << 27
+    g = torch.Generator(device=DEV)
+    g.manual_seed(4100 + ["clustered", "four_values", "exponential"].index(shape))
+    if shape == "clustered":
+        a = torch.cat([torch.randint(0, 1000, (n // 2,), device=DEV, generator=g),
+                       torch.randint(10**9, 2 * 10**9, (n // 2,), device=DEV, generator=g)])
+        b = torch.randint(0, 2 * 10**9, (n,), device=DEV, generator=g)
+    elif shape == "four_values":
+        a = torch.randint(0, 4, (n,), device=DEV, generator=g)
+        b = torch.randint(0, 4, (n,), device=DEV, generator=g)
+    else:
+        e = torch.empty(2 * n, dtype=torch.float64, device=DEV).exponential_(1.0, generator=g)
+        a, b = (e[:n] * 1e6).to(torch.int64), (e[n:] * 1e6).to(torch.int64)
+    a = torch.sort(a.to(torch.int32)).values
+    b = torch.sort(b.to(torch.int32)).values
+    say("partition key shape", shape, n)
+    seg_len = om.segment_length(n, n)
+    part = om.partition(a, b, seg_len)
+    got = host(om.merge_segments_i32(a, b, part, seg_len))
+    A, B = host(a), host(b)
+    _check_partition(A, B, host(part), seg_len)
+    assert_same(got, oracle.merge_i32(A, B), shape)
+    del a, b
+
+
 def test_headline_stage_path_matches():
     """The launch sequence the benchmark times (partition, then segment
     merge, with the library's own segment length) on the headline workload,
@@ -657,16 +702,5 @@ def test_headline_stage_path_matches():
     say("headline stages", seg_len)
     part = om.partition(a, b, seg_len)
     got = host(om.merge_segments_i32(a, b, part, seg_len))
-    # Each boundary's co-rank is the unique split that passes the acceptance
-    # test A[i-1] <= B[j] and B[j-1] < A[i] (j = k - i), with the usual
-    # exemptions at the array ends.
-    ks = np.minimum(np.arange(part.numel(), dtype=np.int64) * seg_len, w.total)
-    I = host(part)
-    J = ks - I
-    m, n = w.m, w.n
-    assert np.all((I >= np.maximum(0, ks - n)) & (I <= np.minimum(ks, m)))
-    A64, B64 = A.astype(np.int64), B.astype(np.int64)
-    ok_lo = (I == 0) | (J == n) | (A64[np.clip(I - 1, 0, m - 1)] <= B64[np.clip(J, 0, n - 1)])
-    ok_hi = (J == 0) | (I == m) | (B64[np.clip(J - 1, 0, n - 1)] < A64[np.clip(I, 0, m - 1)])
-    assert np.all(ok_lo & ok_hi)
+    _check_partition(A, B, host(part), seg_len)
     assert_same(got, oracle.merge_i32(A, B), "headline")
