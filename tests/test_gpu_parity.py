@@ -93,7 +93,7 @@ def test_explicit_segments(seg_tiles):
     m, n = 70001, 53333
     A, B = pair(g, m, n, 64)
     Av, Bv = tags(m, n)
-    for kv, tile in ((False, 4096), (True, 2048)):
+    for kv, tile in ((False, 2048), (True, 2048)):  # the segment merge's tiles
         seg_len = tile * seg_tiles if seg_tiles else 4 * 1777
         say("segments", kv, seg_len)
         a, b = dev(A), dev(B)
