@@ -48,10 +48,15 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the headline kernel's sources with comments and whitespace
+    removed: it changes when the code does, not when a comment does."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "ordered_merge_sorted_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "ordered_merge_sorted_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -58,9 +58,11 @@
 //     coalesced stores) free of bank conflicts.
 //   * The partition kernel can search each boundary with a group of G lanes:
 //     G points of the diagonal are tested at once and a ballot narrows the
-//     interval G-fold per round (the pages note the search may be
-//     higher-radix).  Fewer dependent HBM round trips, more lines touched
-//     per round; G is a tuning choice of the launcher.
+//     interval to one of the G+1 gaps per round (the pages note the search
+//     may be higher-radix).  After the first round the points are placed by
+//     interpolation on the keys at the interval's ends (co_rank_group), so
+//     evenly spread keys need about 5 rounds instead of 12.  G is a tuning
+//     choice of the launcher.
 //   * A descriptor mode lets the same kernel merge any list of (A, B, C)
 //     ranges: the pieces of a batch of merges or of a merge-sort pass
 //     (batch_kernel.hpp).
