@@ -239,6 +239,48 @@ __device__ __forceinline__ void get_row(const int* buf, int tid, T (&x)[ITEMS]) 
     }
 }
 
+// x as held by lane (lane ^ mask) of the wavefront; every lane takes part.
+template <typename T>
+__device__ __forceinline__ T lane_xor(T x, int mask) {
+    if constexpr (sizeof(T) == 8) {
+        const int lo = __shfl_xor(low_word(x), mask);
+        const int hi = __shfl_xor(high_word(x), mask);
+        return static_cast<T>(join_words(lo, hi));
+    } else {
+        return __shfl_xor(x, mask);
+    }
+}
+
+// Keys alone: sorts the wavefront's 64 lanes x ITEMS keys (each lane's ITEMS
+// already ascending) into one ascending run held lane-major, by bitonic
+// merges across lanes.  Round r merges pairs of runs of 2^r lanes: a flip
+// stage (element t of a lane against element ITEMS-1-t of the mirror lane in
+// the pair, the first run keeping the minima) leaves each run bitonic; then
+// half-cleaners at lane distances 2^(r-1), ..., 1, and inside the lane.
+// Data moves between lanes by shuffles, not through LDS.
+template <int ITEMS, typename T>
+__device__ __forceinline__ void wave_merge_rounds(T (&x)[ITEMS], int lane) {
+#pragma unroll
+    for (int r = 0; r < 6; ++r) {
+        const int mirror = (2 << r) - 1;
+        const bool first = (lane & (1 << r)) == 0;
+        T y[ITEMS];
+#pragma unroll
+        for (int t = 0; t < ITEMS; ++t) y[t] = lane_xor(x[ITEMS - 1 - t], mirror);
+#pragma unroll
+        for (int t = 0; t < ITEMS; ++t) x[t] = first ? min(x[t], y[t]) : max(x[t], y[t]);
+#pragma unroll
+        for (int d = (1 << r) >> 1; d >= 1; d >>= 1) {
+            const bool low = (lane & d) == 0;
+#pragma unroll
+            for (int t = 0; t < ITEMS; ++t) y[t] = lane_xor(x[t], d);
+#pragma unroll
+            for (int t = 0; t < ITEMS; ++t) x[t] = low ? min(x[t], y[t]) : max(x[t], y[t]);
+        }
+        bitonic_clean<ITEMS>(x);
+    }
+}
+
 template <int THREADS, int ITEMS, int VW, int ORDER>
 __global__ __launch_bounds__(THREADS) void block_sort_kernel(
     const typename KeyOrder<ORDER>::T* __restrict__ src, const uint32_t* __restrict__ src_v,
@@ -305,10 +347,16 @@ __global__ __launch_bounds__(THREADS) void block_sort_kernel(
     for (int t = 0; t < ITEMS; ++t) pos[t] = tid * ITEMS + t;
     bitonic_sort<ITEMS, KV>(x, pos);
 
+    // Keys alone: the first six rounds run inside each wavefront, across
+    // lanes (equal keys are indistinguishable, so any exact order of them is
+    // the stable one).  With payloads every round merges through LDS.
+    constexpr int kWaveRun = KV ? ITEMS : ITEMS * 64;
+    if constexpr (!KV) wave_merge_rounds<ITEMS>(x, tid & 63);
+
     // Merge rounds: runs of `run` elements merge pairwise into runs of 2*run.
     // The A run of a pair holds earlier positions than its B run, so taking
     // A on equal keys is the stable order.
-    for (int run = ITEMS; run < kTile; run *= 2) {
+    for (int run = kWaveRun; run < kTile; run *= 2) {
         __syncthreads();  // every read of the previous round is done
         put_row<ITEMS>(kbuf, tid, x);
         if constexpr (KV) put_row<ITEMS>(pbuf, tid, pos);

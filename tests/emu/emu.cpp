@@ -24,6 +24,7 @@ struct WaveVote {
     std::barrier<> bar{64};
     int pred[64] = {};
     double val[64] = {};
+    int ival[64] = {};
 };
 static std::vector<WaveVote>* g_waves = nullptr;
 unsigned long long __ballot(int pred) {
@@ -43,6 +44,16 @@ double __shfl(double var, int src) {
     w.val[lane] = var;
     w.bar.arrive_and_wait();
     const double got = w.val[src & 63];
+    w.bar.arrive_and_wait();
+    return got;
+}
+
+int __shfl_xor(int var, int mask) {
+    WaveVote& w = (*g_waves)[threadIdx.x / 64];
+    const int lane = threadIdx.x % 64;
+    w.ival[lane] = var;
+    w.bar.arrive_and_wait();
+    const int got = w.ival[(lane ^ mask) & 63];
     w.bar.arrive_and_wait();
     return got;
 }

@@ -36,6 +36,8 @@ unsigned long long __ballot(int pred);
 // Wavefront shuffle: lane `src` of the caller's 64-lane wavefront (same
 // meeting rule as __ballot).
 double __shfl(double var, int src);
+// Butterfly shuffle: var of lane (lane ^ mask) of the caller's wavefront.
+int __shfl_xor(int var, int mask);
 inline int __popcll(unsigned long long x) { return __builtin_popcountll(x); }
 template <typename T>
 inline T min(T a, T b) { return b < a ? b : a; }
