@@ -239,46 +239,95 @@ __device__ __forceinline__ void get_row(const int* buf, int tid, T (&x)[ITEMS]) 
     }
 }
 
-// x as held by lane (lane ^ mask) of the wavefront; every lane takes part.
-template <typename T>
-__device__ __forceinline__ T lane_xor(T x, int mask) {
-    if constexpr (sizeof(T) == 8) {
-        const int lo = __shfl_xor(low_word(x), mask);
-        const int hi = __shfl_xor(high_word(x), mask);
-        return static_cast<T>(join_words(lo, hi));
+// A 32-bit word as held by lane (lane ^ MASK) of the wavefront; every lane
+// takes part.  The route depends on the mask: DPP inside each row of 16
+// lanes where a row pattern is the xor (quad_perm for 1, 2 and 3; half-row
+// mirror for 7; rotate by 8 for 8; row mirror for 15), ds_swizzle in bit
+// mode (and 0x1f, xor MASK) inside each half of the wavefront for the other
+// masks below 32, and a full shuffle across the halves.
+template <int MASK>
+__device__ __forceinline__ int lane_xor_word(int x) {
+    static_assert(MASK > 0 && MASK < 64, "a lane mask of the wavefront");
+    if constexpr (MASK == 1) {
+        return __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+    } else if constexpr (MASK == 2) {
+        return __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+    } else if constexpr (MASK == 3) {
+        return __builtin_amdgcn_update_dpp(x, x, 0x1B, 0xF, 0xF, false);  // quad_perm 3,2,1,0
+    } else if constexpr (MASK == 7) {
+        return __builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+    } else if constexpr (MASK == 8) {
+        return __builtin_amdgcn_update_dpp(x, x, 0x128, 0xF, 0xF, false);  // row_ror:8
+    } else if constexpr (MASK == 15) {
+        return __builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false);  // row_mirror
+    } else if constexpr (MASK < 32) {
+        return __builtin_amdgcn_ds_swizzle(x, 0x1F | (MASK << 10));
     } else {
-        return __shfl_xor(x, mask);
+        return __shfl_xor(x, MASK);
     }
 }
 
+template <int MASK, typename T>
+__device__ __forceinline__ T lane_xor(T x) {
+    if constexpr (sizeof(T) == 8) {
+        return static_cast<T>(join_words(lane_xor_word<MASK>(low_word(x)),
+                                         lane_xor_word<MASK>(high_word(x))));
+    } else {
+        return lane_xor_word<MASK>(x);
+    }
+}
+
+// One compare-exchange stage between each lane and lane ^ MASK, element by
+// element: the lower lane keeps the minima.
+template <int MASK, int ITEMS, typename T>
+__device__ __forceinline__ void lane_stage(T (&x)[ITEMS], int lane) {
+    const bool low = (lane & MASK) == 0;
+#pragma unroll
+    for (int t = 0; t < ITEMS; ++t) {
+        const T y = lane_xor<MASK>(x[t]);
+        x[t] = low ? min(x[t], y) : max(x[t], y);
+    }
+}
+
+// Round R of the in-wavefront merge: pairs of runs of 2^R lanes.  A flip
+// stage (element t against element ITEMS-1-t of the mirror lane, lane ^
+// (2^(R+1)-1); the first run keeps the minima) leaves each run bitonic;
+// half-cleaners at lane distances 2^(R-1), ..., 1 and inside the lane sort
+// it.
+template <int D, int ITEMS, typename T>
+__device__ __forceinline__ void lane_half_cleaners(T (&x)[ITEMS], int lane) {
+    if constexpr (D >= 1) {
+        lane_stage<D>(x, lane);
+        lane_half_cleaners<D / 2>(x, lane);
+    }
+}
+
+template <int R, int ITEMS, typename T>
+__device__ __forceinline__ void wave_round(T (&x)[ITEMS], int lane) {
+    constexpr int kMirror = (2 << R) - 1;
+    const bool first = (lane & (1 << R)) == 0;
+    T y[ITEMS];
+#pragma unroll
+    for (int t = 0; t < ITEMS; ++t) y[t] = lane_xor<kMirror>(x[ITEMS - 1 - t]);
+#pragma unroll
+    for (int t = 0; t < ITEMS; ++t) x[t] = first ? min(x[t], y[t]) : max(x[t], y[t]);
+    lane_half_cleaners<(1 << R) / 2>(x, lane);
+    bitonic_clean<ITEMS>(x);
+}
+
 // Keys alone: sorts the wavefront's 64 lanes x ITEMS keys (each lane's ITEMS
-// already ascending) into one ascending run held lane-major, by bitonic
-// merges across lanes.  Round r merges pairs of runs of 2^r lanes: a flip
-// stage (element t of a lane against element ITEMS-1-t of the mirror lane in
-// the pair, the first run keeping the minima) leaves each run bitonic; then
-// half-cleaners at lane distances 2^(r-1), ..., 1, and inside the lane.
-// Data moves between lanes by shuffles, not through LDS.
+// already ascending) into one ascending run held lane-major, by six rounds
+// of bitonic merges across lanes.  Data moves between lanes in registers
+// (DPP) or through the LDS crossbar without touching its banks (swizzle,
+// shuffle).
 template <int ITEMS, typename T>
 __device__ __forceinline__ void wave_merge_rounds(T (&x)[ITEMS], int lane) {
-#pragma unroll
-    for (int r = 0; r < 6; ++r) {
-        const int mirror = (2 << r) - 1;
-        const bool first = (lane & (1 << r)) == 0;
-        T y[ITEMS];
-#pragma unroll
-        for (int t = 0; t < ITEMS; ++t) y[t] = lane_xor(x[ITEMS - 1 - t], mirror);
-#pragma unroll
-        for (int t = 0; t < ITEMS; ++t) x[t] = first ? min(x[t], y[t]) : max(x[t], y[t]);
-#pragma unroll
-        for (int d = (1 << r) >> 1; d >= 1; d >>= 1) {
-            const bool low = (lane & d) == 0;
-#pragma unroll
-            for (int t = 0; t < ITEMS; ++t) y[t] = lane_xor(x[t], d);
-#pragma unroll
-            for (int t = 0; t < ITEMS; ++t) x[t] = low ? min(x[t], y[t]) : max(x[t], y[t]);
-        }
-        bitonic_clean<ITEMS>(x);
-    }
+    wave_round<0>(x, lane);
+    wave_round<1>(x, lane);
+    wave_round<2>(x, lane);
+    wave_round<3>(x, lane);
+    wave_round<4>(x, lane);
+    wave_round<5>(x, lane);
 }
 
 template <int THREADS, int ITEMS, int VW, int ORDER>

@@ -4,6 +4,7 @@
 // Workgroups run one after another.  Exposes extern "C" entry points that the
 // tests call through ctypes.
 #include <barrier>
+#include <cstdlib>
 #include <functional>
 #include <thread>
 #include <vector>
@@ -56,6 +57,48 @@ int __shfl_xor(int var, int mask) {
     const int got = w.ival[(lane ^ mask) & 63];
     w.bar.arrive_and_wait();
     return got;
+}
+
+// Posts var for the caller's lane, reads lane `src` of the same wavefront.
+static int wave_read(int var, int src) {
+    WaveVote& w = (*g_waves)[threadIdx.x / 64];
+    const int lane = threadIdx.x % 64;
+    w.ival[lane] = var;
+    w.bar.arrive_and_wait();
+    const int got = w.ival[src & 63];
+    w.bar.arrive_and_wait();
+    return got;
+}
+
+int __builtin_amdgcn_update_dpp(int old, int src, int ctrl, int row_mask, int bank_mask,
+                                bool bound_ctrl) {
+    (void)old;
+    (void)bound_ctrl;
+    if (row_mask != 0xF || bank_mask != 0xF) abort();
+    const int lane = threadIdx.x % 64;
+    const int row = lane & ~15, i = lane & 15;
+    int from;
+    if (ctrl >= 0 && ctrl <= 0xFF) {  // quad_perm: lane q of a quad reads quad lane sel[q]
+        from = (lane & ~3) | ((ctrl >> (2 * (lane & 3))) & 3);
+    } else if (ctrl >= 0x121 && ctrl <= 0x12F) {  // row_ror:n, rotate right within the row
+        const int n = ctrl - 0x120;
+        from = row | ((i + n) & 15);
+    } else if (ctrl == 0x140) {  // row_mirror
+        from = row | (15 - i);
+    } else if (ctrl == 0x141) {  // row_half_mirror
+        from = row | (i & 8) | (7 - (i & 7));
+    } else {
+        abort();
+    }
+    return wave_read(src, from);
+}
+
+int __builtin_amdgcn_ds_swizzle(int src, int pattern) {
+    if (pattern & 0x8000) abort();  // only bit mode
+    const int and_mask = pattern & 31, or_mask = (pattern >> 5) & 31, xor_mask = (pattern >> 10) & 31;
+    const int lane = threadIdx.x % 64;
+    const int from = (lane & 32) | ((((lane & 31) & and_mask) | or_mask) ^ xor_mask);
+    return wave_read(src, from);
 }
 
 // Runs `body` for every workgroup 0..blocks-1 with `threads` lanes each.

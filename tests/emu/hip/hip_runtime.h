@@ -38,6 +38,12 @@ unsigned long long __ballot(int pred);
 double __shfl(double var, int src);
 // Butterfly shuffle: var of lane (lane ^ mask) of the caller's wavefront.
 int __shfl_xor(int var, int mask);
+// DPP move (row_mask and bank_mask all set; the controls the kernels use:
+// quad_perm, row_ror, row_mirror, row_half_mirror) and ds_swizzle in bit
+// mode, as the GCN/CDNA ISA defines them, over the caller's wavefront.
+int __builtin_amdgcn_update_dpp(int old, int src, int ctrl, int row_mask, int bank_mask,
+                                bool bound_ctrl);
+int __builtin_amdgcn_ds_swizzle(int src, int pattern);
 inline int __popcll(unsigned long long x) { return __builtin_popcountll(x); }
 template <typename T>
 inline T min(T a, T b) { return b < a ? b : a; }
