@@ -277,57 +277,100 @@ __device__ __forceinline__ T lane_xor(T x) {
     }
 }
 
+// (key, position) of this lane against (yk, yp): true when the other pair
+// is the smaller.  Without positions (POS = false) keys alone decide.
+template <bool POS, typename T>
+__device__ __forceinline__ bool other_first(T k, int p, T yk, int yp) {
+    return POS ? (yk < k || (yk == k && yp < p)) : yk < k;
+}
+
 // One compare-exchange stage between each lane and lane ^ MASK, element by
-// element: the lower lane keeps the minima.
-template <int MASK, int ITEMS, typename T>
-__device__ __forceinline__ void lane_stage(T (&x)[ITEMS], int lane) {
+// element: the lower lane keeps the smaller, the upper the larger.  With
+// POS, positions travel with their keys and break ties.
+template <int MASK, bool POS, int ITEMS, typename T>
+__device__ __forceinline__ void lane_stage(T (&x)[ITEMS], int (&pos)[ITEMS], int lane) {
     const bool low = (lane & MASK) == 0;
 #pragma unroll
     for (int t = 0; t < ITEMS; ++t) {
-        const T y = lane_xor<MASK>(x[t]);
-        x[t] = low ? min(x[t], y) : max(x[t], y);
+        const T yk = lane_xor<MASK>(x[t]);
+        const int yp = POS ? lane_xor<MASK>(pos[t]) : 0;
+        const bool take = low == other_first<POS>(x[t], pos[t], yk, yp);
+        x[t] = take ? yk : x[t];
+        if (POS) pos[t] = take ? yp : pos[t];
+    }
+}
+
+// Orders x[0..N) (with positions when POS) ascending when it is bitonic.
+template <bool POS, int N, typename T>
+__device__ __forceinline__ void bitonic_clean_pos(T (&x)[N], int (&pos)[N]) {
+    if constexpr (!POS) {
+        bitonic_clean<N>(x);
+    } else {
+#pragma unroll
+        for (int d = N / 2; d >= 1; d >>= 1) {
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                if ((i & d) == 0 && other_first<true>(x[i], pos[i], x[i + d], pos[i + d])) {
+                    const T tk = x[i];
+                    x[i] = x[i + d];
+                    x[i + d] = tk;
+                    const int tp = pos[i];
+                    pos[i] = pos[i + d];
+                    pos[i + d] = tp;
+                }
+            }
+        }
     }
 }
 
 // Round R of the in-wavefront merge: pairs of runs of 2^R lanes.  A flip
 // stage (element t against element ITEMS-1-t of the mirror lane, lane ^
-// (2^(R+1)-1); the first run keeps the minima) leaves each run bitonic;
+// (2^(R+1)-1); the first run keeps the smaller) leaves each run bitonic;
 // half-cleaners at lane distances 2^(R-1), ..., 1 and inside the lane sort
 // it.
-template <int D, int ITEMS, typename T>
-__device__ __forceinline__ void lane_half_cleaners(T (&x)[ITEMS], int lane) {
+template <int D, bool POS, int ITEMS, typename T>
+__device__ __forceinline__ void lane_half_cleaners(T (&x)[ITEMS], int (&pos)[ITEMS], int lane) {
     if constexpr (D >= 1) {
-        lane_stage<D>(x, lane);
-        lane_half_cleaners<D / 2>(x, lane);
+        lane_stage<D, POS>(x, pos, lane);
+        lane_half_cleaners<D / 2, POS>(x, pos, lane);
     }
 }
 
-template <int R, int ITEMS, typename T>
-__device__ __forceinline__ void wave_round(T (&x)[ITEMS], int lane) {
+template <int R, bool POS, int ITEMS, typename T>
+__device__ __forceinline__ void wave_round(T (&x)[ITEMS], int (&pos)[ITEMS], int lane) {
     constexpr int kMirror = (2 << R) - 1;
     const bool first = (lane & (1 << R)) == 0;
-    T y[ITEMS];
+    T yk[ITEMS];
+    int yp[ITEMS];
 #pragma unroll
-    for (int t = 0; t < ITEMS; ++t) y[t] = lane_xor<kMirror>(x[ITEMS - 1 - t]);
+    for (int t = 0; t < ITEMS; ++t) {
+        yk[t] = lane_xor<kMirror>(x[ITEMS - 1 - t]);
+        yp[t] = POS ? lane_xor<kMirror>(pos[ITEMS - 1 - t]) : 0;
+    }
 #pragma unroll
-    for (int t = 0; t < ITEMS; ++t) x[t] = first ? min(x[t], y[t]) : max(x[t], y[t]);
-    lane_half_cleaners<(1 << R) / 2>(x, lane);
-    bitonic_clean<ITEMS>(x);
+    for (int t = 0; t < ITEMS; ++t) {
+        const bool take = first == other_first<POS>(x[t], pos[t], yk[t], yp[t]);
+        x[t] = take ? yk[t] : x[t];
+        if (POS) pos[t] = take ? yp[t] : pos[t];
+    }
+    lane_half_cleaners<(1 << R) / 2, POS>(x, pos, lane);
+    bitonic_clean_pos<POS>(x, pos);
 }
 
-// Keys alone: sorts the wavefront's 64 lanes x ITEMS keys (each lane's ITEMS
-// already ascending) into one ascending run held lane-major, by six rounds
-// of bitonic merges across lanes.  Data moves between lanes in registers
-// (DPP) or through the LDS crossbar without touching its banks (swizzle,
-// shuffle).
-template <int ITEMS, typename T>
-__device__ __forceinline__ void wave_merge_rounds(T (&x)[ITEMS], int lane) {
-    wave_round<0>(x, lane);
-    wave_round<1>(x, lane);
-    wave_round<2>(x, lane);
-    wave_round<3>(x, lane);
-    wave_round<4>(x, lane);
-    wave_round<5>(x, lane);
+// Sorts the wavefront's 64 lanes x ITEMS elements (each lane's ITEMS already
+// ascending) into one ascending run held lane-major, by six rounds of
+// bitonic merges across lanes.  With POS the order is (key, position), all
+// distinct, so the result is the stable order.  Data moves between lanes in
+// registers (DPP) or through the LDS crossbar without touching its banks
+// (swizzle, shuffle).
+template <bool POS, int ITEMS, typename T>
+__device__ __forceinline__ void wave_merge_rounds(T (&x)[ITEMS], int (&pos)[ITEMS], int lane) {
+    wave_round<0, POS>(x, pos, lane);
+    wave_round<1, POS>(x, pos, lane);
+    wave_round<2, POS>(x, pos, lane);
+    wave_round<3, POS>(x, pos, lane);
+    wave_round<4, POS>(x, pos, lane);
+    wave_round<5, POS>(x, pos, lane);
 }
 
 template <int THREADS, int ITEMS, int VW, int ORDER>
@@ -396,11 +439,13 @@ __global__ __launch_bounds__(THREADS) void block_sort_kernel(
     for (int t = 0; t < ITEMS; ++t) pos[t] = tid * ITEMS + t;
     bitonic_sort<ITEMS, KV>(x, pos);
 
-    // Keys alone: the first six rounds run inside each wavefront, across
-    // lanes (equal keys are indistinguishable, so any exact order of them is
-    // the stable one).  With payloads every round merges through LDS.
-    constexpr int kWaveRun = KV ? ITEMS : ITEMS * 64;
-    if constexpr (!KV) wave_merge_rounds<ITEMS>(x, tid & 63);
+    // The first six rounds run inside each wavefront, across lanes: keys
+    // alone (equal keys are indistinguishable, so any exact order of them is
+    // the stable one), or (key, position) pairs with payloads.  Each
+    // wavefront's run then holds one contiguous block of tile positions, so
+    // the A-first merges of the LDS rounds below stay stable.
+    constexpr int kWaveRun = ITEMS * 64;
+    wave_merge_rounds<KV>(x, pos, tid & 63);
 
     // Merge rounds: runs of `run` elements merge pairwise into runs of 2*run.
     // The A run of a pair holds earlier positions than its B run, so taking
