@@ -480,10 +480,10 @@ int check_part(const int64_t* part, int64_t total, int64_t seg_len) {
 
 // Key order codes of the C ABI (omerge_key_kind | OMERGE_DESCENDING) map onto
 // KeyOrder's template argument one to one.
-static_assert(OMERGE_KEY_I32 == kKeyI32 && OMERGE_KEY_U32 == kKeyU32 &&
-                  OMERGE_KEY_F32 == kKeyF32 && OMERGE_KEY_I64 == kKeyI64 &&
-                  OMERGE_KEY_U64 == kKeyU64 && OMERGE_KEY_F64 == kKeyF64 &&
-                  OMERGE_DESCENDING == kKeyDescending,
+static_assert(int(OMERGE_KEY_I32) == int(kKeyI32) && int(OMERGE_KEY_U32) == int(kKeyU32) &&
+                  int(OMERGE_KEY_F32) == int(kKeyF32) && int(OMERGE_KEY_I64) == int(kKeyI64) &&
+                  int(OMERGE_KEY_U64) == int(kKeyU64) && int(OMERGE_KEY_F64) == int(kKeyF64) &&
+                  int(OMERGE_DESCENDING) == int(kKeyDescending),
               "ABI order codes must match KeyOrder");
 
 bool valid_order(int order) {
