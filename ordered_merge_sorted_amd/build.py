@@ -19,8 +19,6 @@ LIB_DIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIB_DIR, "libomerge.so")
 SOURCES = [os.path.join(CSRC, "omerge.hip")]
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
-DEPENDS = SOURCES + [os.path.join(CSRC, f) for f in ("corank.hpp", "merge_kernel.hpp")] + [
-    os.path.join(INCLUDE, "omerge.h")]
 
 ARCH = "gfx950"
 HIPCC_FLAGS = [

@@ -1,0 +1,60 @@
+"""The gfx950 code of our own build holds the instructions the design rests
+on (CPU only: hipcc compiles the library's device code to assembly).
+
+- The headline segment merge moves HBM data as 16-byte vectors
+  (global_load_dwordx4 / global_store_dwordx4), LDS data as 128-bit rows
+  (ds_write_b128 / ds_read_b128), and uses no scratch memory.
+- The block sort's in-wavefront rounds move lanes' keys with DPP row moves
+  and ds_swizzle, and use no scratch memory.
+"""
+import os
+import re
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+from ordered_merge_sorted_amd import build  # noqa: E402
+
+MERGE = "_ZN6omerge21merge_segments_kernelILi256ELi8ELi0ELi0ELb0EE"
+BLOCK_SORT = "_ZN6omerge17block_sort_kernelILi1024ELi16ELi0ELi0EE"
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    if shutil.which(build.hipcc()) is None:
+        pytest.skip("hipcc is not installed")
+    out = str(tmp_path_factory.mktemp("isa") / "omerge.s")
+    flags = [f for f in build.HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
+    subprocess.check_call([build.hipcc(), *flags, "--cuda-device-only", "-S", "-x", "hip",
+                           *build.SOURCES, "-o", out], stderr=subprocess.DEVNULL)
+    return open(out).read()
+
+
+def body(asm, prefix):
+    """The assembly of the first function whose symbol starts with prefix,
+    and the scratch size the compiler reports for it."""
+    m = re.search(r"^(%s\w*):" % re.escape(prefix), asm, re.M)
+    assert m, "no function " + prefix
+    end = asm.index("s_endpgm", m.end())
+    meta = re.search(r"; ScratchSize: (\d+)", asm[end:])
+    return asm[m.end():end], int(meta.group(1))
+
+
+def test_segment_merge_vector_accesses(asm):
+    code, scratch = body(asm, MERGE)
+    for ins in ("global_load_dwordx4", "global_store_dwordx4", "ds_write_b128", "ds_read_b128"):
+        assert ins in code, ins
+    assert scratch == 0
+
+
+def test_block_sort_lane_exchanges(asm):
+    code, scratch = body(asm, BLOCK_SORT)
+    assert "v_mov_b32_dpp" in code
+    for pattern in ("quad_perm", "row_mirror", "row_half_mirror", "row_ror:8"):
+        assert pattern in code, pattern
+    assert "ds_swizzle_b32" in code
+    assert scratch == 0
