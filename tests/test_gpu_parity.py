@@ -704,3 +704,89 @@ def test_headline_stage_path_matches():
     got = host(om.merge_segments_i32(a, b, part, seg_len))
     _check_partition(A, B, host(part), seg_len)
     assert_same(got, oracle.merge_i32(A, B), "headline")
+
+
+# ------------------------------------------------------- random mix
+
+def _mix_keys(g, dtype, n):
+    """Keys of one of several shapes: four values, the whole range, two
+    far-apart clusters, exponential, all equal, small signed."""
+    if dtype in (np.float32, np.float64):
+        pool = float_pool(dtype)
+        return np.ascontiguousarray(pool[g.integers(0, pool.size, size=n)])
+    info = np.iinfo(dtype)
+    kind = int(g.integers(0, 6))
+    if kind == 0:
+        x = g.integers(0, 4, size=n)
+    elif kind == 1:
+        return g.integers(info.min, info.max, size=n, dtype=dtype, endpoint=True)
+    elif kind == 2:
+        x = np.concatenate([g.integers(0, 50, size=n // 2), g.integers(10**6, 10**7, size=n - n // 2)])
+    elif kind == 3:
+        x = (g.exponential(1.0, size=n) * 1e5).astype(np.int64)
+    elif kind == 4:
+        x = np.full(n, 7)
+    else:
+        x = g.integers(-1000, 1000, size=n)
+    if info.min == 0:
+        x = np.abs(x)
+    return np.ascontiguousarray(x.astype(dtype))
+
+
+def test_random_mix_against_oracle():
+    """500 seeded cases drawn across every entry point (merge, pairs, sort,
+    batch), key kind, direction and payload width, with sizes around the
+    2048-output tile and up to 10^5, and key shapes that stress the
+    partition's probe placement; every output against the oracle."""
+    g = np.random.Generator(np.random.PCG64(8080))
+    done = 0
+    while done < 500:
+        dtype, desc = TYPED[int(g.integers(0, len(TYPED)))]
+        if np.dtype(dtype) == np.uint64 and not hasattr(torch, "uint64"):
+            continue
+        if np.dtype(dtype) == np.uint32 and not hasattr(torch, "uint32"):
+            continue
+        what = int(g.integers(0, 3))
+        m = int(g.choice([0, 1, 2047, 2048, 2049, int(g.integers(1, 100000))]))
+        n = int(g.choice([0, 1, 2047, 2048, 2049, int(g.integers(1, 100000))]))
+        vdt = [None, np.uint32, np.int64][int(g.integers(0, 3))]
+        say("mix", done, what, np.dtype(dtype).name, desc, m, n, vdt)
+        if what == 0:
+            A = oracle.sort(_mix_keys(g, dtype, m), descending=desc)
+            B = oracle.sort(_mix_keys(g, dtype, n), descending=desc)
+            if vdt is None:
+                got = om.merge(dev_typed(A), dev_typed(B), descending=desc)
+                assert_same(host_bits(got), as_bits(oracle.merge_keys(A, B, descending=desc)), "mix merge")
+            else:
+                Av, Bv = (np.arange(m) * 3 + 1).astype(vdt), (np.arange(n) * 5 + 2).astype(vdt)
+                gk, gv = om.merge_pairs(dev_typed(A), dev_typed(Av), dev_typed(B), dev_typed(Bv),
+                                        descending=desc)
+                wk, wv = oracle.merge_pairs(A, Av, B, Bv, descending=desc)
+                assert_same(host_bits(gk), as_bits(wk), "mix pair keys")
+                assert_same(host_bits(gv), as_bits(wv), "mix pair payloads")
+        elif what == 1:
+            K = _mix_keys(g, dtype, m)
+            if vdt is None:
+                got = om.sort(dev_typed(K), descending=desc)
+                assert_same(host_bits(got), as_bits(oracle.sort(K, descending=desc)), "mix sort")
+            else:
+                V = (np.arange(m) * 7 + 3).astype(vdt)
+                gk, gv = om.sort(dev_typed(K), dev_typed(V), descending=desc)
+                wk, wv = oracle.sort(K, V, descending=desc)
+                assert_same(host_bits(gk), as_bits(wk), "mix sort keys")
+                assert_same(host_bits(gv), as_bits(wv), "mix sort payloads")
+        else:
+            pairs = int(g.choice([1, 3, 50, 1000]))
+            scale = int(g.choice([3, 100, 5000]))
+            la = g.integers(0, scale + 1, size=pairs)
+            lb = g.integers(0, scale + 1, size=pairs)
+            ao = np.concatenate([[0], np.cumsum(la)]).astype(np.int64)
+            bo = np.concatenate([[0], np.cumsum(lb)]).astype(np.int64)
+            A = np.concatenate([oracle.sort(_mix_keys(g, dtype, int(x)), descending=desc) for x in la])
+            B = np.concatenate([oracle.sort(_mix_keys(g, dtype, int(x)), descending=desc) for x in lb])
+            A, B = np.ascontiguousarray(A.astype(dtype)), np.ascontiguousarray(B.astype(dtype))
+            got = om.merge_batched(dev_typed(A), torch.from_numpy(ao).to(DEV), dev_typed(B),
+                                   torch.from_numpy(bo).to(DEV), descending=desc)
+            want = oracle.merge_batched(A, ao, B, bo, descending=desc)
+            assert_same(host_bits(got), as_bits(want), "mix batch")
+        done += 1
