@@ -195,16 +195,26 @@ __host__ __device__ constexpr int stage_word(int p) { return p + ((p >> 5) << 2)
 #ifndef OMERGE_PART_INTERP
 #define OMERGE_PART_INTERP 1
 #endif
+//
+// A caller that knows more may pass a narrower interval [lo_in, hi_in] that
+// holds the answer (it is intersected with the bounds above) and a guess of
+// the answer inside it; the first round then places its points around the
+// guess, spread by 0.7*sqrt(width), unless that would cover more than half
+// the interval.  A first round that misses does not turn interpolation off.
 template <int G, int ORDER>
 __device__ __forceinline__ int64_t co_rank_group(int64_t k,
                                                  const typename KeyOrder<ORDER>::T* __restrict__ A,
                                                  int64_t m,
                                                  const typename KeyOrder<ORDER>::T* __restrict__ B,
-                                                 int64_t n, int g_lane, int g_shift) {
+                                                 int64_t n, int g_lane, int g_shift,
+                                                 int64_t lo_in = 0, int64_t hi_in = INT64_MAX,
+                                                 double guess = -1.0) {
     static_assert(G >= 2 && G <= 64 && (64 % G) == 0, "group size");
     constexpr int kLog = bit_length(G) - 1;
     int64_t lo = k > n ? k - n : 0;
     int64_t hi = k < m ? k : m;
+    lo = lo_in > lo ? (lo_in < hi ? lo_in : hi) : lo;
+    hi = hi_in < hi ? (hi_in > lo ? hi_in : lo) : hi;
     // g at the interval's ends once known: at lo - 1 (last passing point)
     // and at hi (first failing point).
     double g_lo = 0.0, g_hi = 0.0;
@@ -215,7 +225,11 @@ __device__ __forceinline__ int64_t co_rank_group(int64_t k,
         const int64_t span = hi - lo;
         double centre = 0.0, spread = 0.0;
         bool interp = false;
-        if (!even_only && have_lo && have_hi && g_hi > g_lo) {
+        if (round == 0 && guess >= 0.0 && OMERGE_PART_INTERP) {
+            centre = guess;
+            spread = fmax(1.0, 0.7 * sqrt(static_cast<double>(span)));
+            interp = (G - 1) * spread < 0.5 * static_cast<double>(span);
+        } else if (!even_only && have_lo && have_hi && g_hi > g_lo) {
             const double w = static_cast<double>(span + 1);  // from lo - 1 to hi
             const double unit = w / (g_hi - g_lo);           // outputs per unit of image
             centre = static_cast<double>(lo - 1) + (0.5 - g_lo) * unit;
@@ -263,7 +277,7 @@ __device__ __forceinline__ int64_t co_rank_group(int64_t k,
                 g_hi = g_right;
                 have_hi = true;
             }
-            if (interp && (new_hi - new_lo) * (G + 1) > span) even_only = true;
+            if (interp && round > 0 && (new_hi - new_lo) * (G + 1) > span) even_only = true;
             lo = new_lo;
             hi = new_hi;
         }
@@ -272,30 +286,78 @@ __device__ __forceinline__ int64_t co_rank_group(int64_t k,
 }
 
 // part[s] = co-rank of k_s = min(s*seg_len, m+n).  G = 1: one lane per
-// boundary running the pages' two-test search; G > 1: G lanes per boundary
-// testing G points per round.
+// boundary running the pages' two-test search.  G > 1: a workgroup of 256
+// lanes holds 256/G consecutive boundaries, one G-lane group each, in two
+// phases.  Phase 1 searches every kStride-th boundary (and the first of the
+// next workgroup) over the whole diagonal.  Phase 2 searches the others
+// inside the interval their two searched neighbours c0 < s < c1 allow: the
+// co-rank never falls as k grows and grows by at most one per output, so
+// max(i(c0), i(c1) - (k_c1 - k)) <= i(k) <= min(i(c1), i(c0) + (k - k_c0)),
+// with the first probes around the straight line between the neighbours.
+// Boundaries close together share their expensive first rounds this way.
 template <int G, int ORDER>
 __global__ __launch_bounds__(256) void partition_kernel(
     const typename KeyOrder<ORDER>::T* __restrict__ A, int64_t m,
     const typename KeyOrder<ORDER>::T* __restrict__ B, int64_t n, int64_t seg_len, int64_t count,
     int64_t* __restrict__ part) {
-    const int64_t gid = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
     if constexpr (G == 1) {
+        const int64_t gid = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
         if (gid >= count) return;
         const int64_t k = gid < count - 1 ? gid * seg_len : m + n;
         part[gid] = co_rank_global<ORDER>(k, A, m, B, n);
     } else {
-        const int64_t s = gid / G;
-        // A wavefront whose groups are all past the end leaves together;
-        // groups past the end inside a live wavefront vote with empty ranges.
-        if ((gid & ~int64_t(63)) / G >= count) return;
-        const int64_t sc = s < count ? s : count - 1;
-        const int64_t k = sc < count - 1 ? sc * seg_len : m + n;
-        const int g_lane = static_cast<int>(gid % G);
-        const int g_shift = static_cast<int>(threadIdx.x & 63) - g_lane;
-        const int64_t i = co_rank_group<G, ORDER>(s < count ? k : 0, A, s < count ? m : 0, B,
-                                           s < count ? n : 0, g_lane, g_shift);
-        if (g_lane == 0 && s < count) part[s] = i;
+        constexpr int kGroups = 256 / G;  // boundaries per workgroup
+        constexpr int kStride = kGroups >= 8 ? 8 : kGroups;
+        constexpr int kCoarse = kGroups / kStride + 1;
+        constexpr int kPhase1Lanes = (kCoarse * G + 63) / 64 * 64;  // whole wavefronts
+        __shared__ int64_t coarse[kCoarse];
+        const int tid = threadIdx.x;
+        const int grp = tid / G;
+        const int g_lane = tid % G;
+        const int g_shift = (tid & 63) - g_lane;
+        const int64_t s0 = blockIdx.x * static_cast<int64_t>(kGroups);
+        auto k_of = [&](int64_t s) { return s < count - 1 ? s * seg_len : m + n; };
+        auto coarse_index = [&](int j) {
+            const int64_t s = s0 + static_cast<int64_t>(kStride) * j;
+            return s < count - 1 ? s : count - 1;
+        };
+        // Phase 1.  Groups past kCoarse (or of a wavefront past the whole
+        // grid) vote with empty ranges.
+        if (tid < kPhase1Lanes) {
+            const bool act = grp < kCoarse;
+            const int64_t kc = act ? k_of(coarse_index(grp)) : 0;
+            const int64_t ic = co_rank_group<G, ORDER>(kc, A, act ? m : 0, B, act ? n : 0, g_lane,
+                                                       g_shift);
+            if (act && g_lane == 0) coarse[grp] = ic;
+        }
+        __syncthreads();
+        // Phase 2.  A wavefront whose groups are all past the end leaves
+        // together; groups past the end inside a live wavefront, and the
+        // boundaries phase 1 has found, vote with empty ranges.
+        const int64_t s = s0 + grp;
+        if (s0 + (tid & ~63) / G >= count) return;
+        const bool live = s < count;
+        const int j = grp / kStride;
+        const bool known = grp % kStride == 0;
+        int64_t i;
+        if (live && !known) {
+            const int64_t c0 = coarse_index(j), c1 = coarse_index(j + 1);
+            const int64_t k = k_of(s), k0 = k_of(c0), k1 = k_of(c1);
+            const int64_t i0 = coarse[j], i1 = coarse[j + 1];
+            const int64_t lo = i1 - (k1 - k) > i0 ? i1 - (k1 - k) : i0;
+            const int64_t hi = i0 + (k - k0) < i1 ? i0 + (k - k0) : i1;
+            const double guess =
+                k1 > k0 ? static_cast<double>(i0) + static_cast<double>(i1 - i0) *
+                                                        static_cast<double>(k - k0) /
+                                                        static_cast<double>(k1 - k0)
+                        : -1.0;
+            i = co_rank_group<G, ORDER>(k, A, m, B, n, g_lane, g_shift, lo, hi,
+                                        guess >= static_cast<double>(lo) ? guess : -1.0);
+        } else {
+            i = co_rank_group<G, ORDER>(0, A, 0, B, 0, g_lane, g_shift);
+            if (live) i = coarse[j];
+        }
+        if (live && g_lane == 0) part[s] = i;
     }
 }
 
