@@ -43,6 +43,9 @@ constexpr int kVersion = 100;  // 0.1.0
 #ifndef OMERGE_TILES_PER_SEG  // target tiles per workgroup segment of one merge
 #define OMERGE_TILES_PER_SEG 6
 #endif
+#ifndef OMERGE_TILES_PER_SEG_KV  // the same for 4-byte keys with 4-byte payloads
+#define OMERGE_TILES_PER_SEG_KV 3
+#endif
 #ifndef OMERGE_TILES_PER_DESC_SEG  // the same for sort passes and batches
 #define OMERGE_TILES_PER_DESC_SEG 8
 #endif
@@ -76,7 +79,6 @@ constexpr int kPartLanes = OMERGE_PART_LANES;
 struct SegWindow {
     int target, slack;
 };
-constexpr SegWindow kMergeWindow{OMERGE_TILES_PER_SEG, 1};
 constexpr SegWindow kDescWindow{OMERGE_TILES_PER_DESC_SEG, 2};
 constexpr int kCopyUnroll = OMERGE_COPY_UNROLL;  // 16-byte vectors per lane in the copy
 
@@ -157,7 +159,10 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // than one compact moving window (2048-output tiles at 9 or 10 per segment:
 // 0.80 ms of merge; at 5 to 8: 0.75-0.78 ms).  Measured on MI355X, R = 6
 // balances the two for one merge, searched over [5, 7] for the R whose last
-// round of workgroups is fullest.  Sort passes and batches (descriptor
+// round of workgroups is fullest.  4+4-byte pairs (2048-pair tiles) run best
+// at exactly R = 3 (2^26+2^26 pairs, per step: 0.394 ms at 3; 0.416, 0.411
+// and 0.410 at 2, 4 and 6); 8-byte keys, with the same tile bytes, were 2%
+// slower at 3 than at 6.  Sort passes and batches (descriptor
 // segments, cut again at every run or merge end) measured 2-5% faster per
 // pass with R = 8 searched over [6, 10].  Inputs with fewer tiles than the
 // window's low end times the slots get the smallest R that keeps a single
@@ -221,6 +226,11 @@ struct Path {
     static constexpr int KW = KeyOrder<ORDER>::kWords;
     static constexpr int kItems = items_for(KW, VW);
     static constexpr int kTile = kThreads * kItems;
+    // Single merges: 6 tiles per segment, searched one tile either side;
+    // 4+4-byte pairs exactly 3 (measured apart, below choose_seg_len).
+    static constexpr bool kPairs44 = KW == 1 && VW == 1;
+    static constexpr SegWindow kMergeWindow{kPairs44 ? OMERGE_TILES_PER_SEG_KV : OMERGE_TILES_PER_SEG,
+                                            kPairs44 ? 0 : 1};
     static constexpr int kTileItems = tile_items_for(KW, VW);  // tile path
     static constexpr int kBatchTile = kThreads * kTileItems;
     static constexpr int kSortItems = sort_items_for(KW, VW);
