@@ -40,11 +40,14 @@ constexpr int kVersion = 100;  // 0.1.0
 #ifndef OMERGE_PART_LANES  // lanes per boundary in the partition search (1 = pages' loop)
 #define OMERGE_PART_LANES 4
 #endif
-#ifndef OMERGE_TILES_PER_SEG  // target tiles per workgroup segment of one merge
-#define OMERGE_TILES_PER_SEG 6
+#ifndef OMERGE_TILES_PER_SEG  // tiles per workgroup segment of one merge, 4-byte keys alone
+#define OMERGE_TILES_PER_SEG 4
 #endif
 #ifndef OMERGE_TILES_PER_SEG_KV  // the same for 4-byte keys with 4-byte payloads
 #define OMERGE_TILES_PER_SEG_KV 3
+#endif
+#ifndef OMERGE_TILES_PER_SEG_WIDE  // target for the shapes with 8-byte keys or payloads
+#define OMERGE_TILES_PER_SEG_WIDE 6
 #endif
 #ifndef OMERGE_TILES_PER_DESC_SEG  // the same for sort passes and batches
 #define OMERGE_TILES_PER_DESC_SEG 8
@@ -153,16 +156,16 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Segment length: a whole number R of tiles per workgroup.  Two costs pull
 // R in opposite directions.  The partition reads a few random cache lines
 // per boundary, so short segments make it expensive (the 2^28+2^28 merge
-// cut into 8,192-output segments: 36 us of partition).  Long segments
+// cut into 8,192-output segments: 23 us of partition).  Long segments
 // spread the workgroups resident at one time over a wide span of A, B and C
 // (about slots*R tiles), and HBM serves such scattered streams more slowly
 // than one compact moving window (2048-output tiles at 9 or 10 per segment:
-// 0.80 ms of merge; at 5 to 8: 0.75-0.78 ms).  Measured on MI355X, R = 6
-// balances the two for one merge, searched over [5, 7] for the R whose last
-// round of workgroups is fullest.  4+4-byte pairs (2048-pair tiles) run best
-// at exactly R = 3 (2^26+2^26 pairs, per step: 0.394 ms at 3; 0.416, 0.411
-// and 0.410 at 2, 4 and 6); 8-byte keys, with the same tile bytes, were 2%
-// slower at 3 than at 6.  Sort passes and batches (descriptor
+// 0.80 ms of merge; at 4 to 8: 0.75-0.78 ms).  Measured on MI355X, per step:
+// 4-byte keys alone run best at exactly R = 4 (2^28+2^28: 0.760 ms at 4,
+// 0.772 at 5, 0.776 at 6; 2^27+2^27 and 2^26+2^26 likewise), 4+4-byte pairs
+// at exactly R = 3 (2^26+2^26 pairs: 0.394 ms at 3; 0.416, 0.411 and 0.410
+// at 2, 4 and 6), and 8-byte keys at 6 (2% faster than at 3), searched one
+// tile either side for the R whose last round of workgroups is fullest.  Sort passes and batches (descriptor
 // segments, cut again at every run or merge end) measured 2-5% faster per
 // pass with R = 8 searched over [6, 10].  Inputs with fewer tiles than the
 // window's low end times the slots get the smallest R that keeps a single
@@ -226,11 +229,13 @@ struct Path {
     static constexpr int KW = KeyOrder<ORDER>::kWords;
     static constexpr int kItems = items_for(KW, VW);
     static constexpr int kTile = kThreads * kItems;
-    // Single merges: 6 tiles per segment, searched one tile either side;
-    // 4+4-byte pairs exactly 3 (measured apart, below choose_seg_len).
-    static constexpr bool kPairs44 = KW == 1 && VW == 1;
-    static constexpr SegWindow kMergeWindow{kPairs44 ? OMERGE_TILES_PER_SEG_KV : OMERGE_TILES_PER_SEG,
-                                            kPairs44 ? 0 : 1};
+    // Single merges (measured per shape, above choose_seg_len): exactly 4
+    // tiles per segment for 4-byte keys alone, 3 for 4+4-byte pairs; 6,
+    // searched one tile either side, for the shapes with 8-byte parts.
+    static constexpr SegWindow kMergeWindow =
+        KW == 1 && VW == 0   ? SegWindow{OMERGE_TILES_PER_SEG, 0}
+        : KW == 1 && VW == 1 ? SegWindow{OMERGE_TILES_PER_SEG_KV, 0}
+                             : SegWindow{OMERGE_TILES_PER_SEG_WIDE, 1};
     static constexpr int kTileItems = tile_items_for(KW, VW);  // tile path
     static constexpr int kBatchTile = kThreads * kTileItems;
     static constexpr int kSortItems = sort_items_for(KW, VW);
