@@ -461,15 +461,8 @@ def main():
 
     # One-call API (includes its stream-ordered scratch allocation).
     if not w.kv:
-        for _ in range(3):
-            om.merge_i32(d_arrs[0], d_arrs[1], out=out, stream=stream)
-        s1, s2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s1.record(stream)
-        for _ in range(10):
-            om.merge_i32(d_arrs[0], d_arrs[1], out=out, stream=stream)
-        s2.record(stream)
-        torch.cuda.synchronize()
-        onecall_ms = s1.elapsed_time(s2) / 10
+        onecall_ms = _time(lambda: om.merge_i32(d_arrs[0], d_arrs[1], out=out, stream=stream),
+                           stream, reps=10)
     else:
         onecall_ms = None
 
