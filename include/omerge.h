@@ -21,8 +21,11 @@
  *     for 64-bit keys or payloads).  Any such alignment works; 16-byte-aligned
  *     arrays take the vector path on every full 16 bytes.
  *   - Lengths are int64 and must be >= 0.  A pointer may be NULL only when its
- *     length is 0.  m + n == 0 is a no-op that returns OMERGE_OK.
- *   - Outputs must not overlap any input (checked by address range).
+ *     length is 0.  m + n == 0 is a no-op that returns OMERGE_OK.  A total
+ *     above 2^59 elements returns OMERGE_OVERFLOW (byte sizes then fit int64).
+ *   - Outputs must not overlap any input (checked by address range; for the
+ *     stage calls below this includes the partition array and the co-rank
+ *     queries).
  *   - A and B must be sorted ascending.  This is NOT checked.  Unsorted input
  *     gives an unspecified output, but the call still returns, every kernel
  *     still terminates and no access leaves the given arrays.

@@ -106,7 +106,9 @@ constexpr int shape_index(int kw, int vw) { return (kw - 1) * 3 + vw; }
 constexpr int kShapes = 6;
 
 constexpr int64_t kMaxSegLen = int64_t(1) << 30;
-constexpr int64_t kMaxTotal = int64_t(1) << 62;
+// Element counts up to 2^59: byte sizes (at most 8 bytes per key or payload)
+// and doubled run lengths then stay inside int64.
+constexpr int64_t kMaxTotal = int64_t(1) << 59;
 constexpr int64_t kMaxGridBlocks = int64_t(1) << 31;  // keeps blocks*256 < 2^39
 
 thread_local hipError_t g_last_error = hipSuccess;
@@ -485,10 +487,17 @@ int check_merge_args(const void* A, const void* Av, int64_t m, const void* B, co
     return OMERGE_OK;
 }
 
-int check_part(const int64_t* part, int64_t total, int64_t seg_len) {
+// The partition of a segment merge: seg_len valid, part an aligned array of
+// ceil(total/seg_len)+1 entries that no output (kb / vb bytes per element of
+// C / Cv) overlaps.
+int check_part(const int64_t* part, int64_t total, int64_t seg_len, const void* C, int kb,
+               const void* Cv, int vb) {
     int rc = check_seg_len(seg_len);
     if (rc != OMERGE_OK) return rc;
-    if (total > 0 && (part == nullptr || (reinterpret_cast<uintptr_t>(part) & 7) != 0))
+    if (total == 0) return OMERGE_OK;
+    if (part == nullptr || (reinterpret_cast<uintptr_t>(part) & 7) != 0) return OMERGE_INVALID_ARG;
+    const int64_t part_bytes = (ceil_div(total, seg_len) + 1) * 8;
+    if (overlaps(part, part_bytes, C, total * kb) || overlaps(part, part_bytes, Cv, total * vb))
         return OMERGE_INVALID_ARG;
     return OMERGE_OK;
 }
@@ -656,8 +665,12 @@ int omerge_co_rank(const int32_t* A, int64_t m, const int32_t* B, int64_t n,
     if (rc != OMERGE_OK) return rc;
     if (count < 0 || bad_array(A, m) || bad_array(B, n)) return OMERGE_INVALID_ARG;
     if (count == 0) return OMERGE_OK;
+    if (count > kMaxTotal) return OMERGE_OVERFLOW;
     if (k == nullptr || i_out == nullptr || (reinterpret_cast<uintptr_t>(k) & 7) ||
         (reinterpret_cast<uintptr_t>(i_out) & 7))
+        return OMERGE_INVALID_ARG;
+    if (overlaps(i_out, count * 8, A, m * 4) || overlaps(i_out, count * 8, B, n * 4) ||
+        overlaps(i_out, count * 8, k, count * 8))
         return OMERGE_INVALID_ARG;
     const int64_t blocks = ceil_div(count, kThreads);
     if (blocks > kMaxGridBlocks) return OMERGE_OVERFLOW;
@@ -687,6 +700,9 @@ int omerge_partition(const int32_t* A, int64_t m, const int32_t* B, int64_t n,
     rc = check_seg_len(seg_len);
     if (rc != OMERGE_OK) return rc;
     if (part == nullptr || (reinterpret_cast<uintptr_t>(part) & 7)) return OMERGE_INVALID_ARG;
+    const int64_t part_bytes = (ceil_div(m + n, seg_len) + 1) * 8;
+    if (overlaps(part, part_bytes, A, m * 4) || overlaps(part, part_bytes, B, n * 4))
+        return OMERGE_INVALID_ARG;
     return PathI32::partition(A, m, B, n, seg_len, part, stream);
 }
 
@@ -695,7 +711,7 @@ int omerge_merge_segments_i32(const int32_t* A, int64_t m, const int32_t* B,
                               int32_t* C, hipStream_t stream) {
     int rc = check_merge_args(A, nullptr, m, B, nullptr, n, C, nullptr, 4, 0);
     if (rc != OMERGE_OK) return rc;
-    rc = check_part(part, m + n, seg_len);
+    rc = check_part(part, m + n, seg_len, C, 4, nullptr, 0);
     if (rc != OMERGE_OK) return rc;
     if (m + n == 0) return OMERGE_OK;
     return PathI32::merge(A, nullptr, m, B, nullptr, n, part, seg_len, C, nullptr, stream);
@@ -709,7 +725,7 @@ int omerge_merge_segments_kv(const int32_t* A_keys, const uint32_t* A_vals,
                              hipStream_t stream) {
     int rc = check_merge_args(A_keys, A_vals, m, B_keys, B_vals, n, C_keys, C_vals, 4, 4);
     if (rc != OMERGE_OK) return rc;
-    rc = check_part(part, m + n, seg_len);
+    rc = check_part(part, m + n, seg_len, C_keys, 4, C_vals, 4);
     if (rc != OMERGE_OK) return rc;
     if (m + n == 0) return OMERGE_OK;
     return PathKV::merge(A_keys, A_vals, m, B_keys, B_vals, n, part, seg_len, C_keys, C_vals,
@@ -733,9 +749,10 @@ int omerge_merge_i32_direct(const int32_t* A, int64_t m, const int32_t* B, int64
 }
 
 int omerge_stream_copy(const int32_t* src, int64_t n, int32_t* dst, hipStream_t stream) {
-    if (bad_array(src, n) || bad_array(dst, n) || overlaps(src, n, dst, n)) return OMERGE_INVALID_ARG;
-    if (n == 0) return OMERGE_OK;
+    if (bad_array(src, n) || bad_array(dst, n)) return OMERGE_INVALID_ARG;
     if (n > kMaxTotal) return OMERGE_OVERFLOW;
+    if (overlaps(src, n * 4, dst, n * 4)) return OMERGE_INVALID_ARG;
+    if (n == 0) return OMERGE_OK;
     const int64_t blocks = ceil_div(ceil_div(n, 4), int64_t(256) * kCopyUnroll);
     if (blocks > kMaxGridBlocks) return OMERGE_OVERFLOW;
     hipLaunchKernelGGL(stream_copy_kernel<kCopyUnroll>, dim3(static_cast<unsigned>(blocks)),

@@ -88,7 +88,7 @@ def P(x):
     ((P(FAKE), 5, P(FAKE + 64), 5, P(FAKE + 4097)), M.INVALID_ARG),  # misaligned C
     ((P(FAKE), 5, P(FAKE + 64), 5, P(FAKE + 8)), M.INVALID_ARG),     # C overlaps A
     ((P(FAKE), 5, P(FAKE + 64), 5, P(FAKE + 40)), M.INVALID_ARG),    # C overlaps B
-    ((P(FAKE), 1 << 62, P(FAKE), 1 << 62, P(FAKE)), M.OVERFLOW),     # m+n > 2^62
+    ((P(FAKE), 1 << 62, P(FAKE), 1 << 62, P(FAKE)), M.OVERFLOW),     # m+n > 2^59
     ((P(0), 0, P(0), 0, P(0)), M.OK),                                # empty: no-op
 ])
 def test_merge_i32_validation(args, want):
@@ -211,6 +211,49 @@ def test_stage_validation():
     assert lib.omerge_co_rank(P(a), 8, P(b), 8, P(0), 4, P(c), P(0)) == M.INVALID_ARG
     assert lib.omerge_co_rank(P(a), 8, P(b), 8, P(part), -1, P(c), P(0)) == M.INVALID_ARG
     assert lib.omerge_co_rank(P(a), 8, P(b), 8, P(0), 0, P(0), P(0)) == M.OK
+
+
+def test_stage_outputs_must_not_overlap_inputs():
+    """The stage calls reject an output that overlaps an input by address
+    range: the partition array over A or B, a segment merge's output over
+    its partition, and co-ranks over A, B or the queried ranks."""
+    lib = om.load_library()
+    a, b, part, c = FAKE, FAKE + 0x1000, FAKE + 0x2000, FAKE + 0x3000
+    # 16 outputs in segments of 8: 3 partition entries (24 bytes)
+    assert lib.omerge_partition(P(a), 8, P(b), 8, 8, P(a + 16), P(0)) == M.INVALID_ARG
+    assert lib.omerge_partition(P(a), 8, P(b), 8, 8, P(b - 16), P(0)) == M.INVALID_ARG
+    seg = lib.omerge_merge_segments_i32
+    assert seg(P(a), 8, P(b), 8, P(c + 32), 8, P(c), P(0)) == M.INVALID_ARG    # part inside C
+    assert seg(P(a), 8, P(b), 8, P(c - 16), 8, P(c), P(0)) == M.INVALID_ARG    # part runs into C
+    kv = lib.omerge_merge_segments_kv
+    av, bv, cv = FAKE + 0x4000, FAKE + 0x5000, FAKE + 0x6000
+    assert kv(P(a), P(av), 8, P(b), P(bv), 8, P(part), 8, P(c), P(part + 8), P(0)) == \
+        M.INVALID_ARG                                                          # C_vals over part
+    assert kv(P(a), P(av), 8, P(b), P(bv), 8, P(cv + 8), 8, P(c), P(cv), P(0)) == M.INVALID_ARG
+    cr = lib.omerge_co_rank
+    k = FAKE + 0x7000
+    assert cr(P(a), 8, P(b), 8, P(k), 4, P(a + 8), P(0)) == M.INVALID_ARG       # over A
+    assert cr(P(a), 8, P(b), 8, P(k), 4, P(b + 24), P(0)) == M.INVALID_ARG      # over B
+    assert cr(P(a), 8, P(b), 8, P(k), 4, P(k), P(0)) == M.INVALID_ARG           # in place
+    assert cr(P(a), 8, P(b), 8, P(k), 4, P(k + 24), P(0)) == M.INVALID_ARG      # over k's tail
+    cp = lib.omerge_stream_copy
+    assert cp(P(a), 64, P(a + 128), P(0)) == M.INVALID_ARG   # overlap past the first 64 bytes
+    assert cp(P(a), 64, P(a - 252), P(0)) == M.INVALID_ARG
+
+
+def test_sizes_beyond_2p59_overflow():
+    """Totals above 2^59 elements are refused before any byte size is formed
+    (8-byte elements would otherwise overflow int64)."""
+    lib = om.load_library()
+    big = (1 << 59) + 1
+    assert lib.merge_i32(P(FAKE), big, P(FAKE), 0, P(FAKE), P(0)) == M.OVERFLOW
+    assert lib.merge_i32(P(FAKE), 1 << 58, P(FAKE), (1 << 58) + 1, P(FAKE), P(0)) == M.OVERFLOW
+    assert lib.omerge_merge_keys(P(FAKE), big, P(FAKE), 0, P(FAKE), 3, P(0)) == M.OVERFLOW
+    assert lib.omerge_sort(P(FAKE), P(0), P(FAKE), P(0), big, 3, 0, P(0)) == M.OVERFLOW
+    assert lib.omerge_co_rank(P(FAKE), 4, P(FAKE), 4, P(FAKE), big, P(FAKE), P(0)) == M.OVERFLOW
+    assert lib.omerge_stream_copy(P(FAKE), big, P(FAKE), P(0)) == M.OVERFLOW
+    assert lib.omerge_partition_count(big, 4096) == -1
+    assert lib.omerge_segment_length(big, 0, 0) == -1
 
 
 def test_binding_rejects_bad_tensors():
