@@ -126,7 +126,6 @@ struct MergeCfg {
     static constexpr int kVCap = VW ? next_pow2(kTile * VW) : 1;  // payload ring words
     static constexpr int kVMask = kVCap - 1;
     static constexpr int kVSide = VW ? kVCap : 0;       // payload rings need no guard
-    static constexpr int kSearchSteps = bit_length(kTile);
     static constexpr int kStageWords = kTile * KW + kTile * KW / 8;
     static constexpr int kVStageWords = kTile * VW + kTile * VW / 8;
     // LDS layout in 32-bit words.
@@ -596,9 +595,12 @@ struct Refill {
 // Co-rank of diagonal k inside one tile: A window of wa elements starting at
 // ring word sa, B window of wb elements at word sb, W words per key.  Bisects
 // [max(0,k-wb), min(k,wa)] for the first i at which A[i] is not among the
-// first k outputs (A[i] <= B[k-1-i] fails).  STEPS = bit_length(TILE) covers
-// every interval; finished lanes idle through the remaining steps, so the
-// loop has no data-dependent exit.
+// first k outputs (A[i] <= B[k-1-i] fails).  STEPS = bit_length of a bound
+// on the interval's width covers it; finished lanes idle through the
+// remaining steps, so the loop has no data-dependent exit.  (Binary lifting,
+// with fewer instructions per step, measured slower here: its first probes
+// sit at the lanes' interval ends, eight words apart, and conflict in the
+// LDS banks.)
 template <int STEPS, int MASK, typename T>
 __device__ __forceinline__ int co_rank_tile(int k, int wa, int wb, const int* ring_a, int sa,
                                             const int* ring_b, int sb) {
@@ -893,7 +895,22 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
         int e = 0;
         int x_t;  // A elements this tile consumes
         if (side == 0) {
-            e = co_rank_tile<Cfg::kSearchSteps, kMask, Key>(c_end, wa, wb, ring_a, sa, ring_b, sb);
+            // A lane's diagonal is at most (lane + 1) * ITEMS, so the lower
+            // wavefronts' searches take fewer steps (10, 11, 11 and 12 for
+            // 256 lanes of 8).
+            const int wave_k = __builtin_amdgcn_readfirstlane(((tid >> 6) + 1) * 64 * ITEMS);
+            if (wave_k <= kTile / 4)
+                e = co_rank_tile<bit_length(kTile / 4), kMask, Key>(c_end, wa, wb, ring_a, sa,
+                                                                    ring_b, sb);
+            else if (wave_k <= kTile / 2)
+                e = co_rank_tile<bit_length(kTile / 2), kMask, Key>(c_end, wa, wb, ring_a, sa,
+                                                                    ring_b, sb);
+            else if (wave_k < kTile)
+                e = co_rank_tile<bit_length(kTile - 1), kMask, Key>(c_end, wa, wb, ring_a, sa,
+                                                                    ring_b, sb);
+            else
+                e = co_rank_tile<bit_length(kTile), kMask, Key>(c_end, wa, wb, ring_a, sa, ring_b,
+                                                                sb);
             split[tid] = e;
             __syncthreads();
             // The same for every lane, so it is moved to a scalar register and
