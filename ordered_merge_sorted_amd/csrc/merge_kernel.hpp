@@ -13,8 +13,8 @@
 //     what it loads: section "The Half-Bandwidth Deficiency").
 //   * Inside a tile each lane finds its split by a co-rank search in LDS,
 //     merges ITEMS outputs in registers (the sequential two-pointer merge),
-//     and the tile goes back to HBM through an LDS stage with coalesced
-//     16-byte stores.
+//     and the tile goes back to HBM as coalesced 16-byte stores, from
+//     registers or through an LDS stage.
 //
 // Elements.  Keys are 32- or 64-bit (KW = 1 or 2 words) and payloads 0, 1 or
 // 2 words (VW).  Rings, refills, stages and stores move 32-bit words;
@@ -53,9 +53,16 @@
 //   * Each key ring has a guard zone that mirrors its first ITEMS elements
 //     past its end, so a lane reads its ITEMS candidates at one base address
 //     with immediate offsets and no wrap arithmetic.
-//   * The LDS stage is padded by 4 words every 32, which makes the 16-byte
-//     stage writes (lane-contiguous) and 16-byte stage reads (for the
-//     coalesced stores) free of bank conflicts.
+//   * Single merges of 4-byte keys (alone or with 4-byte payloads) store
+//     from registers: the lanes of a wavefront take its 64 slices in the
+//     order 0,32,1,33,..., so one DPP swap inside each lane pair gives every
+//     lane two 16-byte pieces of two 1 KB runs of the output
+//     (store_direct8).  With no stage a workgroup needs 17 KB of LDS instead
+//     of 26 KB, and 8 workgroups share a CU instead of 6: a third more
+//     refill loads in flight.
+//   * The other shapes go through an LDS stage padded by 4 words every 32,
+//     which makes the 16-byte stage writes (lane-contiguous) and 16-byte
+//     stage reads (for the coalesced stores) free of bank conflicts.
 //   * The partition kernel can search each boundary with a group of G lanes:
 //     G points of the diagonal are tested at once and a ballot narrows the
 //     interval to one of the G+1 gaps per round (the pages note the search
@@ -107,7 +114,7 @@ __device__ __forceinline__ int word_phase(const void* p) {
 // Tile geometry and LDS layout.  Elements are KW 32-bit words of key (1 or
 // 2) and VW words of payload (0 = keys only, 1 or 2); rings, stages and
 // refills work in 32-bit words, searches and merges in elements.
-template <int THREADS, int ITEMS, int KW, int VW>
+template <int THREADS, int ITEMS, int KW, int VW, bool STAGE = true>
 struct MergeCfg {
     static_assert(THREADS % 64 == 0, "whole 64-lane wavefronts");
     static_assert(ITEMS >= 4 && (ITEMS & (ITEMS - 1)) == 0,
@@ -126,8 +133,9 @@ struct MergeCfg {
     static constexpr int kVCap = VW ? next_pow2(kTile * VW) : 1;  // payload ring words
     static constexpr int kVMask = kVCap - 1;
     static constexpr int kVSide = VW ? kVCap : 0;       // payload rings need no guard
-    static constexpr int kStageWords = kTile * KW + kTile * KW / 8;
-    static constexpr int kVStageWords = kTile * VW + kTile * VW / 8;
+    // Output stage (none when the lanes store their outputs from registers).
+    static constexpr int kStageWords = STAGE ? kTile * KW + kTile * KW / 8 : 0;
+    static constexpr int kVStageWords = STAGE ? kTile * VW + kTile * VW / 8 : 0;
     // LDS layout in 32-bit words.
     static constexpr int kRing = 0;  // keys: A ring [0,kSide), B ring [kSide,2kSide)
     static constexpr int kValRing = kRing + 2 * kSide;  // payload rings
@@ -143,6 +151,12 @@ struct MergeCfg {
 // and on MI355X the hint raises a plain 16-byte copy from ~5.7 to ~6.2 TB/s
 // and the merge by ~4%.  Building with OMERGE_NT_LOADS=0 / OMERGE_NT_STORES=0
 // gives plain accesses.
+// Single merges of 4-byte keys store tiles from registers (store_direct8);
+// 0 sends them through the LDS stage like the other shapes.
+#ifndef OMERGE_DIRECT_STORE
+#define OMERGE_DIRECT_STORE 1
+#endif
+
 #ifndef OMERGE_NT_LOADS
 #define OMERGE_NT_LOADS 1
 #endif
@@ -726,6 +740,55 @@ __device__ __forceinline__ void store_from_ring(int32_t* __restrict__ dst, int l
     }
 }
 
+// Stores a tile from registers, for one word per output and 8 outputs per
+// lane.  The lanes of a wavefront own its 64 slices of 8 outputs in the
+// order lane 2i -> slice i, lane 2i+1 -> slice 32+i (direct_slice).  One swap
+// inside each lane pair (DPP) then gives every lane the 4 outputs
+// [4l, 4l+4) and [256+4l, 256+4l+4) of the wavefront's 512: two 16-byte
+// stores per lane, each wavefront instruction writing 1 KB contiguous.  x
+// holds the lane's outputs (order images for keys, mapped back here);
+// `base` is the wavefront's first output word in dst, `len` how many of the
+// tile's words exist past dst.  16-byte stores need dst 16-byte aligned
+// (`aligned`); otherwise, and at the tile's ragged end, single words.
+__device__ __forceinline__ int direct_slice(int tid) {
+    return (tid & ~63) + ((tid & 63) >> 1) + ((tid & 1) << 5);
+}
+
+__device__ __forceinline__ int swap_pair_lanes(int x) {
+    return __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+}
+
+template <int ORDER>
+__device__ __forceinline__ void store_direct8(int32_t* __restrict__ dst, int base, int len,
+                                              bool aligned, const int (&x)[8], int tid) {
+    const bool odd = (tid & 1) != 0;
+    int z[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) z[t] = swap_pair_lanes(odd ? x[t] : x[4 + t]);
+    int4v v[2];
+    v[0].x = odd ? z[0] : x[0];
+    v[0].y = odd ? z[1] : x[1];
+    v[0].z = odd ? z[2] : x[2];
+    v[0].w = odd ? z[3] : x[3];
+    v[1].x = odd ? x[4] : z[0];
+    v[1].y = odd ? x[5] : z[1];
+    v[1].z = odd ? x[6] : z[2];
+    v[1].w = odd ? x[7] : z[3];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int p = base + 256 * h + 4 * (tid & 63);
+        const int4v y = map_vec<ORDER, false>(v[h]);
+        if (aligned && p + 4 <= len) {
+            store_stream4(dst + p, y);
+        } else {
+            const int ys[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (p + u < len) dst[p + u] = ys[u];
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Segment merge kernel: one workgroup per segment of the output.
 //
@@ -756,7 +819,13 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
     // Payloads move through rings and stage as opaque words: an identity
     // order of the payload's width.
     constexpr int VORDER = VW == 2 ? kKeyI64 : kKeyI32;
-    using Cfg = MergeCfg<THREADS, ITEMS, KW, VW>;
+    // Single merges of 4-byte keys (with or without 4-byte payloads) store
+    // each tile from registers (store_direct8), with no LDS stage: the LDS
+    // saved lets more workgroups, and so more refill loads, share a CU.
+    // The other shapes, and descriptor segments (which may start at any
+    // word of C), go through the stage.
+    constexpr bool kDirect = OMERGE_DIRECT_STORE && !DESC && KW == 1 && VW <= 1 && ITEMS == 8;
+    using Cfg = MergeCfg<THREADS, ITEMS, KW, VW, !kDirect>;
     constexpr int kTile = Cfg::kTile;
     constexpr int kCap = Cfg::kCap;
     constexpr int kMask = Cfg::kMask;
@@ -781,6 +850,8 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
     int* const split = lds + Cfg::kSplit;
 
     const int tid = threadIdx.x;
+    // The slice of the tile this lane merges: ITEMS outputs from slice*ITEMS.
+    const int slice = kDirect ? direct_slice(tid) : tid;
     const int64_t seg = blockIdx.x;
     int64_t k0, i0, j0;  // first output, first A and first B element of the segment
     int c_len, a_len, b_len;
@@ -828,6 +899,9 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
     int32_t* const Cvs = KV ? reinterpret_cast<int32_t*>(Cv) + VW * k0 : nullptr;
     const int va_base = KV ? (word_phase(Avs) & kVMask) : 0;
     const int vb_base = KV ? (word_phase(Bvs) & kVMask) : 0;
+    // 16-byte stores from registers need a 16-byte-aligned output.
+    [[maybe_unused]] const bool c_aligned = (word_phase(Cs) & 3) == 0;
+    [[maybe_unused]] const bool cv_aligned = KV && (word_phase(Cvs) & 3) == 0;
 
     int a_cons = 0, b_cons = 0;  // elements consumed so far (segment-relative)
     int a_loaded = a_len < kTile ? a_len : kTile;
@@ -891,7 +965,7 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
 
         // Co-rank of the end of this lane's slice, searched in the ring; the
         // lane's start is its left neighbour's end.
-        const int c_end = (tid + 1) * ITEMS < c_tile ? (tid + 1) * ITEMS : c_tile;
+        const int c_end = (slice + 1) * ITEMS < c_tile ? (slice + 1) * ITEMS : c_tile;
         int e = 0;
         int x_t;  // A elements this tile consumes
         if (side == 0) {
@@ -911,7 +985,7 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
             else
                 e = co_rank_tile<bit_length(kTile), kMask, Key>(c_end, wa, wb, ring_a, sa, ring_b,
                                                                 sb);
-            split[tid] = e;
+            split[slice] = e;
             __syncthreads();
             // The same for every lane, so it is moved to a scalar register and
             // the refill bookkeeping stays scalar.
@@ -959,11 +1033,14 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
             rf.commit(ring, tid);
             if constexpr (KV) rv.commit(vring, tid);
         } else {
-            const int c_beg = tid * ITEMS < c_tile ? tid * ITEMS : c_tile;
-            const int s = tid > 0 ? split[tid - 1] : 0;
+            const int c_beg = slice * ITEMS < c_tile ? slice * ITEMS : c_tile;
+            const int s = slice > 0 ? split[slice - 1] : 0;
 
             // This lane's row of the stage: ITEMS contiguous elements.
             int* const row = stage + stage_word(tid * ITEMS * KW);
+            // Outputs kept in registers for store_direct8 (keys, payloads).
+            int kout[kDirect ? ITEMS : 1];
+            int vout[kDirect && KV ? ITEMS : 1];
             if constexpr (!KV) {
                 // Candidates: the next ITEMS keys of each side from the lane's
                 // split.  The lane's outputs are the ITEMS smallest of them; any
@@ -991,6 +1068,10 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
 #pragma unroll
                 for (int t = 0; t < ITEMS; ++t) x[t] = min(a[t], b[ITEMS - 1 - t]);
                 bitonic_clean<ITEMS>(x);
+                if constexpr (kDirect) {
+#pragma unroll
+                    for (int t = 0; t < ITEMS; ++t) kout[t] = static_cast<int>(x[t]);
+                } else {
 #pragma unroll
                 for (int v = 0; v < ITEMS * KW / 4; ++v) {
                     int4v q;
@@ -1006,6 +1087,7 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
                         q.w = high_word(x[2 * v + 1]);
                     }
                     *reinterpret_cast<int4v*>(row + 4 * v) = q;
+                }
                 }
             } else {
                 // Key+payload: the serial two-pointer merge of the lane's exact
@@ -1032,6 +1114,14 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
                         kb = take_a ? kb : nxt;
                     }
                 }
+                if constexpr (kDirect) {
+                    // Payloads leave the ring before the refill lands there.
+#pragma unroll
+                    for (int t = 0; t < ITEMS; ++t) {
+                        kout[t] = static_cast<int>(out[t]);
+                        vout[t] = vring[src[t]];
+                    }
+                } else {
                 int* const vrow = vstage + stage_word(tid * ITEMS * VW);
 #pragma unroll
                 for (int t = 0; t < ITEMS; ++t) {
@@ -1041,6 +1131,7 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
                     } else {
                         st_elem<long long>(vrow, 2 * t, ld_elem<long long>(vring, src[t]));
                     }
+                }
                 }
             }
             __syncthreads();
@@ -1052,14 +1143,25 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
             rf.commit(ring, tid);
             if constexpr (KV) rv.commit(vring, tid);
 
-            // Coalesced 16-byte stores of the whole tile.  (Storing each lane's
-            // ITEMS outputs straight from registers frees the stage's LDS but
-            // measured 10% slower, and 2.3x slower with nontemporal stores: the
-            // 16-byte pieces of a line then reach HBM apart.)
-            store_tile<THREADS, kStoreVec, ORDER>(Cs + KW * c_done, KW * c_tile, stage, tid);
-            if constexpr (KV) {
-                store_tile<THREADS, kVLoadVec, VORDER>(Cvs + VW * c_done, VW * c_tile, vstage,
-                                                       tid);
+            if constexpr (kDirect) {
+                // From registers: each wavefront stores its 512 outputs as two
+                // 1 KB runs (store_direct8).
+                const int wbase = (tid >> 6) * 64 * ITEMS;
+                store_direct8<ORDER>(Cs + c_done, wbase, c_tile, c_aligned, kout, tid);
+                if constexpr (KV)
+                    store_direct8<VORDER>(Cvs + c_done, wbase, c_tile, cv_aligned, vout, tid);
+            } else {
+                // Coalesced 16-byte stores of the whole tile from the stage.
+                // (Storing each lane's ITEMS contiguous outputs straight from
+                // registers, as two 16-byte stores per lane, measured 10%
+                // slower, and 2.3x slower with nontemporal stores: each store
+                // instruction then covers every other 16 bytes, and the pieces
+                // of a line reach HBM apart.  store_direct8 avoids that.)
+                store_tile<THREADS, kStoreVec, ORDER>(Cs + KW * c_done, KW * c_tile, stage, tid);
+                if constexpr (KV) {
+                    store_tile<THREADS, kVLoadVec, VORDER>(Cvs + VW * c_done, VW * c_tile,
+                                                           vstage, tid);
+                }
             }
         }  // general tile
 

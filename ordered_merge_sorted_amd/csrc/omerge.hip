@@ -41,7 +41,7 @@ constexpr int kVersion = 100;  // 0.1.0
 #define OMERGE_PART_LANES 4
 #endif
 #ifndef OMERGE_TILES_PER_SEG  // tiles per workgroup segment of one merge, 4-byte keys alone
-#define OMERGE_TILES_PER_SEG 4
+#define OMERGE_TILES_PER_SEG 2
 #endif
 #ifndef OMERGE_TILES_PER_SEG_KV  // the same for 4-byte keys with 4-byte payloads
 #define OMERGE_TILES_PER_SEG_KV 3
@@ -156,18 +156,19 @@ int device_slots(int shape, const void* kernel, int* cus, int* wg_per_cu) {
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Segment length: a whole number R of tiles per workgroup.  Two costs pull
-// R in opposite directions.  The partition reads a few random cache lines
-// per boundary, so short segments make it expensive (the 2^28+2^28 merge
-// cut into 8,192-output segments: 23 us of partition).  Long segments
-// spread the workgroups resident at one time over a wide span of A, B and C
-// (about slots*R tiles), and HBM serves such scattered streams more slowly
-// than one compact moving window (2048-output tiles at 9 or 10 per segment:
-// 0.80 ms of merge; at 4 to 8: 0.75-0.78 ms).  Measured on MI355X, per step:
-// 4-byte keys alone run best at exactly R = 4 (2^28+2^28: 0.760 ms at 4,
-// 0.772 at 5, 0.776 at 6; 2^27+2^27 and 2^26+2^26 likewise), 4+4-byte pairs
-// at exactly R = 3 (2^26+2^26 pairs: 0.394 ms at 3; 0.416, 0.411 and 0.410
-// at 2, 4 and 6), and 8-byte keys at 6 (2% faster than at 3), searched one
-// tile either side for the R whose last round of workgroups is fullest.  Sort passes and batches (descriptor
+// R in opposite directions.  The partition reads about ten random cache
+// lines per boundary, so short segments make it expensive (the 2^28+2^28
+// merge: 23 us of partition with 8,192-output segments, 40 us with 4,096).
+// Long segments spread the workgroups resident at one time over a wide span
+// of A, B and C (about slots*R tiles), and HBM serves such scattered streams
+// more slowly than one compact moving window.  Measured on MI355X, per step,
+// with tiles stored from registers (8 workgroups per CU): 4-byte keys alone
+// run best at exactly R = 2 (2^28+2^28: 0.738 ms at 2, 0.741 at 3, 0.752 at
+// 4, 0.780 at 5, the merge kernel alone 0.697, 0.713, 0.728 and 0.757 ms;
+// 2^27+2^24 skewed: 0.213 ms at 2, 0.222-0.224 at 3 and 4), 4+4-byte pairs
+// at exactly R = 3 (2^26+2^26 pairs: 0.387 ms at 2 and 3, 0.391 at 4), and
+// 8-byte keys at 6 (2% faster than at 3), searched one tile either side for
+// the R whose last round of workgroups is fullest.  Sort passes and batches (descriptor
 // segments, cut again at every run or merge end) measured 2-5% faster per
 // pass with R = 8 searched over [6, 10].  Inputs with fewer tiles than the
 // window's low end times the slots get the smallest R that keeps a single
@@ -231,7 +232,7 @@ struct Path {
     static constexpr int KW = KeyOrder<ORDER>::kWords;
     static constexpr int kItems = items_for(KW, VW);
     static constexpr int kTile = kThreads * kItems;
-    // Single merges (measured per shape, above choose_seg_len): exactly 4
+    // Single merges (measured per shape, above choose_seg_len): exactly 2
     // tiles per segment for 4-byte keys alone, 3 for 4+4-byte pairs; 6,
     // searched one tile either side, for the shapes with 8-byte parts.
     static constexpr SegWindow kMergeWindow =
