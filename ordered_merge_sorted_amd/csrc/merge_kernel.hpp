@@ -308,7 +308,13 @@ __device__ __forceinline__ int64_t co_rank_group(int64_t k,
 // max(i(c0), i(c1) - (k_c1 - k)) <= i(k) <= min(i(c1), i(c0) + (k - k_c0)),
 // with the first probes around the straight line between the neighbours.
 // Boundaries close together share their expensive first rounds this way.
-template <int G, int ORDER>
+// STRIDE is kStride (capped at 256/G); phase 2 may use G2 <= G lanes per
+// boundary.  Fewer phase-1 searches fetch fewer random lines, while wider
+// phase-2 gaps take more rounds: on 4,096-output segments a stride of 16
+// measured marginally fastest (2^28+2^28 uniform keys: 40.0 us and 210 MB
+// of reads against 40.7 us and 215 MB at 8; no gain at 32 or 64), and
+// 2-lane phase-2 groups were slower.
+template <int G, int ORDER, int G2 = G, int STRIDE = 8>
 __global__ __launch_bounds__(256) void partition_kernel(
     const typename KeyOrder<ORDER>::T* __restrict__ A, int64_t m,
     const typename KeyOrder<ORDER>::T* __restrict__ B, int64_t n, int64_t seg_len, int64_t count,
@@ -320,7 +326,10 @@ __global__ __launch_bounds__(256) void partition_kernel(
         part[gid] = co_rank_global<ORDER>(k, A, m, B, n);
     } else {
         constexpr int kGroups = 256 / G;  // boundaries per workgroup
-        constexpr int kStride = kGroups >= 8 ? 8 : kGroups;
+        constexpr int kStride = kGroups >= STRIDE ? STRIDE : kGroups;
+        // Phase 2 searches each boundary with G2 lanes (G2 <= G), so its
+        // groups fill the first kGroups*G2 lanes: whole wavefronts.
+        static_assert(G2 >= 2 && G2 <= G && (kGroups * G2) % 64 == 0, "phase-2 group size");
         constexpr int kCoarse = kGroups / kStride + 1;
         constexpr int kPhase1Lanes = (kCoarse * G + 63) / 64 * 64;  // whole wavefronts
         __shared__ int64_t coarse[kCoarse];
@@ -344,14 +353,19 @@ __global__ __launch_bounds__(256) void partition_kernel(
             if (act && g_lane == 0) coarse[grp] = ic;
         }
         __syncthreads();
-        // Phase 2.  A wavefront whose groups are all past the end leaves
-        // together; groups past the end inside a live wavefront, and the
-        // boundaries phase 1 has found, vote with empty ranges.
-        const int64_t s = s0 + grp;
-        if (s0 + (tid & ~63) / G >= count) return;
+        // Phase 2.  Wavefronts past the phase-2 lanes, and a wavefront whose
+        // groups are all past the end, leave together; groups past the end
+        // inside a live wavefront, and the boundaries phase 1 has found,
+        // vote with empty ranges.
+        if (tid >= kGroups * G2) return;
+        const int grp2 = tid / G2;
+        const int g_lane2 = tid % G2;
+        const int g_shift2 = (tid & 63) - g_lane2;
+        const int64_t s = s0 + grp2;
+        if (s0 + (tid & ~63) / G2 >= count) return;
         const bool live = s < count;
-        const int j = grp / kStride;
-        const bool known = grp % kStride == 0;
+        const int j = grp2 / kStride;
+        const bool known = grp2 % kStride == 0;
         int64_t i;
         if (live && !known) {
             const int64_t c0 = coarse_index(j), c1 = coarse_index(j + 1);
@@ -364,13 +378,13 @@ __global__ __launch_bounds__(256) void partition_kernel(
                                                         static_cast<double>(k - k0) /
                                                         static_cast<double>(k1 - k0)
                         : -1.0;
-            i = co_rank_group<G, ORDER>(k, A, m, B, n, g_lane, g_shift, lo, hi,
-                                        guess >= static_cast<double>(lo) ? guess : -1.0);
+            i = co_rank_group<G2, ORDER>(k, A, m, B, n, g_lane2, g_shift2, lo, hi,
+                                         guess >= static_cast<double>(lo) ? guess : -1.0);
         } else {
-            i = co_rank_group<G, ORDER>(0, A, 0, B, 0, g_lane, g_shift);
+            i = co_rank_group<G2, ORDER>(0, A, 0, B, 0, g_lane2, g_shift2);
             if (live) i = coarse[j];
         }
-        if (live && g_lane == 0) part[s] = i;
+        if (live && g_lane2 == 0) part[s] = i;
     }
 }
 

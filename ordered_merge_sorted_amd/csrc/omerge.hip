@@ -40,6 +40,12 @@ constexpr int kVersion = 100;  // 0.1.0
 #ifndef OMERGE_PART_LANES  // lanes per boundary in the partition search (1 = pages' loop)
 #define OMERGE_PART_LANES 4
 #endif
+#ifndef OMERGE_PART_LANES2  // lanes per boundary in the partition's second phase
+#define OMERGE_PART_LANES2 OMERGE_PART_LANES
+#endif
+#ifndef OMERGE_PART_STRIDE  // the partition's first phase searches every STRIDE-th boundary
+#define OMERGE_PART_STRIDE 16
+#endif
 #ifndef OMERGE_TILES_PER_SEG  // tiles per workgroup segment of one merge, 4-byte keys alone
 #define OMERGE_TILES_PER_SEG 2
 #endif
@@ -78,6 +84,7 @@ constexpr int kVersion = 100;  // 0.1.0
 #endif
 constexpr int kThreads = OMERGE_THREADS;
 constexpr int kPartLanes = OMERGE_PART_LANES;
+constexpr int kPartLanes2 = OMERGE_PART_LANES2;
 // Segment-length windows: target R and the half-width searched around it.
 struct SegWindow {
     int target, slack;
@@ -273,7 +280,7 @@ struct Path {
         const int64_t count = ceil_div(m + n, seg_len) + 1;
         const int64_t blocks = ceil_div(count * kPartLanes, 256);
         if (blocks > kMaxGridBlocks) return OMERGE_OVERFLOW;
-        hipLaunchKernelGGL((partition_kernel<kPartLanes, ORDER>),
+        hipLaunchKernelGGL((partition_kernel<kPartLanes, ORDER, kPartLanes2, OMERGE_PART_STRIDE>),
                            dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, A, m, B, n,
                            seg_len, count, part);
         hipError_t e = hipGetLastError();

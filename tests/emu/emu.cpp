@@ -394,7 +394,9 @@ int emu_tile(int variant, int kv) {
     return omerge::MergeCfg<128, 4, 1, 0>::kTile;
 }
 
-// lanes = lanes per boundary in the partition search (1, 4, 8, 16, 64).
+// lanes = lanes per boundary in the partition search (1, 4, 8, 16, 64), or
+// 42, 416, 4216, 432, 464 for 4 lanes in phase 1 with 2 or 4 in phase 2 and
+// a phase-1 stride of 8, 16, 32 or 64.
 void emu_partition(int lanes, const int32_t* A, int64_t m, const int32_t* B, int64_t n,
                    int64_t seg_len, int64_t* part) {
     const int64_t count = (m + n + seg_len - 1) / seg_len + 1;
@@ -407,6 +409,12 @@ void emu_partition(int lanes, const int32_t* A, int64_t m, const int32_t* B, int
         case 4: go(omerge::partition_kernel<4, 0>); break;
         case 8: go(omerge::partition_kernel<8, 0>); break;
         case 16: go(omerge::partition_kernel<16, 0>); break;
+        // 4 lanes in phase 1; phase-2 lanes and phase-1 stride vary.
+        case 42: go(omerge::partition_kernel<4, 0, 2, 8>); break;
+        case 416: go(omerge::partition_kernel<4, 0, 4, 16>); break;
+        case 4216: go(omerge::partition_kernel<4, 0, 2, 16>); break;
+        case 432: go(omerge::partition_kernel<4, 0, 4, 32>); break;
+        case 464: go(omerge::partition_kernel<4, 0, 4, 64>); break;
         default: go(omerge::partition_kernel<64, 0>); break;
     }
 }
