@@ -151,12 +151,6 @@ struct MergeCfg {
 // and on MI355X the hint raises a plain 16-byte copy from ~5.7 to ~6.2 TB/s
 // and the merge by ~4%.  Building with OMERGE_NT_LOADS=0 / OMERGE_NT_STORES=0
 // gives plain accesses.
-// Single merges of 4-byte keys store tiles from registers (store_direct8);
-// 0 sends them through the LDS stage like the other shapes.
-#ifndef OMERGE_DIRECT_STORE
-#define OMERGE_DIRECT_STORE 1
-#endif
-
 #ifndef OMERGE_NT_LOADS
 #define OMERGE_NT_LOADS 1
 #endif
@@ -820,7 +814,11 @@ struct SegDesc {
     int64_t a1, b1;      // one past the last A and B element
 };
 
-template <int THREADS, int ITEMS, int VW, int ORDER, bool DESC = false>
+// REG = true: tiles leave from registers (store_direct8) instead of through
+// the LDS stage; 4-byte keys with no or 4-byte payloads and 8 outputs per
+// lane only.  Any output works, but only 16-byte-aligned segment outputs
+// get 16-byte stores, so the launcher picks it when they are.
+template <int THREADS, int ITEMS, int VW, int ORDER, bool DESC = false, bool REG = false>
 __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
     const typename KeyOrder<ORDER>::T* __restrict__ A, const uint32_t* __restrict__ Av, int64_t m,
     const typename KeyOrder<ORDER>::T* __restrict__ B, const uint32_t* __restrict__ Bv, int64_t n,
@@ -833,12 +831,11 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
     // Payloads move through rings and stage as opaque words: an identity
     // order of the payload's width.
     constexpr int VORDER = VW == 2 ? kKeyI64 : kKeyI32;
-    // Single merges of 4-byte keys (with or without 4-byte payloads) store
-    // each tile from registers (store_direct8), with no LDS stage: the LDS
-    // saved lets more workgroups, and so more refill loads, share a CU.
-    // The other shapes, and descriptor segments (which may start at any
-    // word of C), go through the stage.
-    constexpr bool kDirect = OMERGE_DIRECT_STORE && !DESC && KW == 1 && VW <= 1 && ITEMS == 8;
+    // With REG each tile is stored from registers (store_direct8) and there
+    // is no LDS stage: the LDS saved lets more workgroups, and so more refill
+    // loads, share a CU.
+    static_assert(!REG || (KW == 1 && VW <= 1 && ITEMS == 8), "register stores: 4-byte keys");
+    constexpr bool kDirect = REG;
     using Cfg = MergeCfg<THREADS, ITEMS, KW, VW, !kDirect>;
     constexpr int kTile = Cfg::kTile;
     constexpr int kCap = Cfg::kCap;

@@ -49,6 +49,9 @@ constexpr int kVersion = 100;  // 0.1.0
 #ifndef OMERGE_TILES_PER_SEG  // tiles per workgroup segment of one merge, 4-byte keys alone
 #define OMERGE_TILES_PER_SEG 2
 #endif
+#ifndef OMERGE_TILES_PER_SEG_STAGED  // the same, through the LDS stage (unaligned outputs)
+#define OMERGE_TILES_PER_SEG_STAGED 4
+#endif
 #ifndef OMERGE_TILES_PER_SEG_KV  // the same for 4-byte keys with 4-byte payloads
 #define OMERGE_TILES_PER_SEG_KV 3
 #endif
@@ -57,6 +60,9 @@ constexpr int kVersion = 100;  // 0.1.0
 #endif
 #ifndef OMERGE_TILES_PER_DESC_SEG  // the same for sort passes and batches
 #define OMERGE_TILES_PER_DESC_SEG 8
+#endif
+#ifndef OMERGE_TILES_PER_SORT_SEG  // sort passes whose tiles are stored from registers
+#define OMERGE_TILES_PER_SORT_SEG 4
 #endif
 #ifndef OMERGE_ITEMS_WIDE  // 64-bit keys, keys only
 #define OMERGE_ITEMS_WIDE 8
@@ -90,6 +96,7 @@ struct SegWindow {
     int target, slack;
 };
 constexpr SegWindow kDescWindow{OMERGE_TILES_PER_DESC_SEG, 2};
+constexpr SegWindow kSortRegWindow{OMERGE_TILES_PER_SORT_SEG, 2};
 constexpr int kCopyUnroll = OMERGE_COPY_UNROLL;  // 16-byte vectors per lane in the copy
 
 // Outputs per lane of the segment merge for KW key words and VW payload
@@ -128,14 +135,14 @@ int hip_fail(hipError_t e) {
 // Per-device launch facts, filled once per device and element shape.
 struct DeviceInfo {
     int cus = 0;
-    int wg_per_cu[kShapes] = {};  // 0 = not yet queried
+    int wg_per_cu[2 * kShapes] = {};  // per shape and store path; 0 = not yet queried
 };
 constexpr int kMaxDevices = 64;
 DeviceInfo g_dev[kMaxDevices];
 std::mutex g_dev_mutex;
 
 // Resident workgroups per CU of `kernel` on the current device (cached per
-// shape), and the device's CU count.
+// `shape`, an index below 2*kShapes), and the device's CU count.
 int device_slots(int shape, const void* kernel, int* cus, int* wg_per_cu) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -212,6 +219,9 @@ bool overlaps(const void* p, int64_t pb, const void* q, int64_t qb) {
     return a0 < b1 && b0 < a1;
 }
 
+// p is 16-byte aligned (or NULL).
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 // An array of `len` elements of `size` bytes: NULL only when empty, aligned
 // to its element size.
 bool bad_array(const void* p, int64_t len, int size = 4) {
@@ -242,10 +252,14 @@ struct Path {
     // Single merges (measured per shape, above choose_seg_len): exactly 2
     // tiles per segment for 4-byte keys alone, 3 for 4+4-byte pairs; 6,
     // searched one tile either side, for the shapes with 8-byte parts.
+    // Through the LDS stage (unaligned outputs) 4-byte keys alone ran best
+    // at 4.
     static constexpr SegWindow kMergeWindow =
         KW == 1 && VW == 0   ? SegWindow{OMERGE_TILES_PER_SEG, 0}
         : KW == 1 && VW == 1 ? SegWindow{OMERGE_TILES_PER_SEG_KV, 0}
                              : SegWindow{OMERGE_TILES_PER_SEG_WIDE, 1};
+    static constexpr SegWindow kStagedMergeWindow =
+        KW == 1 && VW == 0 ? SegWindow{OMERGE_TILES_PER_SEG_STAGED, 0} : kMergeWindow;
     static constexpr int kTileItems = tile_items_for(KW, VW);  // tile path
     static constexpr int kBatchTile = kThreads * kTileItems;
     static constexpr int kSortItems = sort_items_for(KW, VW);
@@ -264,14 +278,47 @@ struct Path {
                                                                : OMERGE_SORT_THREADS_MIXED;
     static constexpr int kSortTile = kSortThreads * kSortItems;
 
-    static int seg_len(int64_t m, int64_t n, int64_t* out, SegWindow win = kMergeWindow) {
+    // Tiles stored from registers (no LDS stage): 4-byte keys with no or
+    // 4-byte payloads.  Launches take it when every segment's output is
+    // 16-byte aligned; otherwise the staged kernel, which stores 16-byte
+    // vectors at any output phase.  Slots are counted for the kernel the
+    // aligned case runs.
+    static constexpr bool kReg = KW == 1 && VW <= 1 && kItems == 8;
+
+    template <bool DESC>
+    static void launch_merge(bool reg, int64_t blocks, hipStream_t stream, const Key* A,
+                             const uint32_t* Av, int64_t m, const Key* B, const uint32_t* Bv,
+                             int64_t n, const int64_t* part, int64_t seg_len, Key* C, uint32_t* Cv,
+                             const SegDesc* desc, int64_t c_total) {
+        const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
+        if constexpr (kReg) {
+            if (reg) {
+                hipLaunchKernelGGL((merge_segments_kernel<kThreads, kItems, VW, ORDER, DESC, true>),
+                                   grid, block, 0, stream, A, Av, m, B, Bv, n, part, seg_len, C,
+                                   Cv, desc, c_total);
+                return;
+            }
+        }
+        hipLaunchKernelGGL((merge_segments_kernel<kThreads, kItems, VW, ORDER, DESC, false>), grid,
+                           block, 0, stream, A, Av, m, B, Bv, n, part, seg_len, C, Cv, desc,
+                           c_total);
+    }
+
+    // Segment length for the register-store kernel (reg, where the shape has
+    // one) or the staged one; `win` overrides the single-merge window.
+    static int seg_len(int64_t m, int64_t n, int64_t* out, bool reg = kReg,
+                       const SegWindow* win = nullptr) {
+        reg = reg && kReg;
+        const void* kernel =
+            reg ? reinterpret_cast<const void*>(
+                      merge_segments_kernel<kThreads, kItems, VW, ORDER, false, kReg>)
+                : reinterpret_cast<const void*>(
+                      merge_segments_kernel<kThreads, kItems, VW, ORDER, false, false>);
         int cus = 0, per_cu = 0;
-        int rc = device_slots(kShape,
-                              reinterpret_cast<const void*>(
-                                  merge_segments_kernel<kThreads, kItems, VW, ORDER>),
-                              &cus, &per_cu);
+        int rc = device_slots(2 * kShape + (reg ? 1 : 0), kernel, &cus, &per_cu);
         if (rc != OMERGE_OK) return rc;
-        *out = choose_seg_len(m + n, kTile, cus * per_cu, win);
+        *out = choose_seg_len(m + n, kTile, cus * per_cu,
+                              win ? *win : (reg ? kMergeWindow : kStagedMergeWindow));
         return OMERGE_OK;
     }
 
@@ -292,22 +339,23 @@ struct Path {
                      uint32_t* Cv, hipStream_t stream) {
         const int64_t segs = ceil_div(m + n, seg_len);
         if (segs > kMaxGridBlocks) return OMERGE_OVERFLOW;
-        hipLaunchKernelGGL((merge_segments_kernel<kThreads, kItems, VW, ORDER>),
-                           dim3(static_cast<unsigned>(segs)), dim3(kThreads), 0, stream, A, Av, m,
-                           B, Bv, n, part, seg_len, C, Cv, nullptr, m + n);
+        // Segment outputs start at multiples of seg_len (a multiple of 4).
+        const bool reg = aligned16(C) && (VW == 0 || aligned16(Cv));
+        launch_merge<false>(reg, segs, stream, A, Av, m, B, Bv, n, part, seg_len, C, Cv, nullptr,
+                            m + n);
         hipError_t e = hipGetLastError();
         return e == hipSuccess ? OMERGE_OK : hip_fail(e);
     }
 
-    // Segment merge of `segs` described segments (descriptor mode).
+    // Segment merge of `segs` described segments (descriptor mode); `reg`:
+    // every segment's output is known to be 16-byte aligned.
     static int merge_desc(const Key* A, const uint32_t* Av, int64_t m, const Key* B,
                           const uint32_t* Bv, int64_t n, const SegDesc* desc, int64_t segs,
-                          int64_t seg_len, Key* C, uint32_t* Cv, int64_t c_total,
+                          int64_t seg_len, Key* C, uint32_t* Cv, int64_t c_total, bool reg,
                           hipStream_t stream) {
         if (segs == 0) return OMERGE_OK;
-        hipLaunchKernelGGL((merge_segments_kernel<kThreads, kItems, VW, ORDER, true>),
-                           dim3(static_cast<unsigned>(segs)), dim3(kThreads), 0, stream, A, Av, m,
-                           B, Bv, n, nullptr, seg_len, C, Cv, desc, c_total);
+        launch_merge<true>(reg, segs, stream, A, Av, m, B, Bv, n, nullptr, seg_len, C, Cv, desc,
+                           c_total);
         hipError_t e = hipGetLastError();
         return e == hipSuccess ? OMERGE_OK : hip_fail(e);
     }
@@ -356,7 +404,7 @@ struct Path {
             return batched_tiles(static_cast<const Key*>(A), Av, a_off, m,
                                  static_cast<const Key*>(B), Bv, b_off, n, pairs, C, Cv, stream);
         int64_t sl = 0;
-        int rc = seg_len(m, n, &sl, kDescWindow);
+        int rc = seg_len(m, n, &sl, false, &kDescWindow);
         if (rc != OMERGE_OK) return rc;
         const int64_t segs = pairs + ceil_div(total, sl) - 1;
         const int64_t blocks = ceil_div((segs + 1) * kPartLanes, 256);
@@ -375,7 +423,8 @@ struct Path {
         if (rc == OMERGE_OK)
             rc = merge_desc(a, static_cast<const uint32_t*>(Av), m, b,
                             static_cast<const uint32_t*>(Bv), n, desc, segs, sl,
-                            static_cast<Key*>(C), static_cast<uint32_t*>(Cv), total, stream);
+                            static_cast<Key*>(C), static_cast<uint32_t*>(Cv), total,
+                            /*reg=*/false, stream);
         e = hipFreeAsync(desc, stream);
         if (rc == OMERGE_OK && e != hipSuccess) rc = hip_fail(e);
         return rc;
@@ -391,8 +440,16 @@ struct Path {
         if (tiles > kMaxGridBlocks) return OMERGE_OVERFLOW;
         int passes = 0;
         for (int64_t run = kSortTile; run < N; run *= 2) ++passes;
+        // Pass segments start at multiples of seg_len inside pairs of runs
+        // (multiples of the block-sort tile, itself a multiple of 4), and the
+        // scratch copy is 256-byte aligned: with 16-byte-aligned outputs
+        // every segment's output is 16-byte aligned.  Those passes store from
+        // registers and measured fastest with 4-tile segments (2^28 int32
+        // keys: 6.93 ms against 7.12 ms staged at 8; 2^27 pairs: 7.44 against
+        // 7.91); the staged passes keep 8.
+        const bool reg = kReg && aligned16(out_k) && (VW == 0 || aligned16(out_v));
         int64_t sl = 0;
-        int rc = seg_len(N, 0, &sl, kDescWindow);
+        int rc = seg_len(N, 0, &sl, reg, reg ? &kSortRegWindow : &kDescWindow);
         if (rc != OMERGE_OK) return rc;
         int64_t max_segs = 0;
         for (int64_t run = kSortTile; run < N; run *= 2) {
@@ -440,7 +497,7 @@ struct Path {
             rc = e == hipSuccess ? OMERGE_OK : hip_fail(e);
             if (rc == OMERGE_OK)
                 rc = merge_desc(bufk[cur], bufv[cur], N, bufk[cur], bufv[cur], N, desc, segs, sl,
-                                bufk[1 - cur], bufv[1 - cur], N, stream);
+                                bufk[1 - cur], bufv[1 - cur], N, reg, stream);
             cur = 1 - cur;
         }
         if (scratch) {
@@ -455,8 +512,10 @@ struct Path {
                     int64_t n, void* C, void* Cv, hipStream_t stream) {
         const int64_t total = m + n;
         if (total == 0) return OMERGE_OK;
+        // The segment length suits the store path merge() will take.
+        const bool reg = aligned16(C) && (VW == 0 || aligned16(Cv));
         int64_t sl = 0;
-        int rc = seg_len(m, n, &sl);
+        int rc = seg_len(m, n, &sl, reg);
         if (rc != OMERGE_OK) return rc;
         const int64_t count = ceil_div(total, sl) + 1;
         int64_t* part = nullptr;

@@ -124,6 +124,38 @@ static void run_grid(int64_t blocks, int threads, const std::function<void()>& b
     g_barrier = nullptr;
 }
 
+// The library's choice of store path: tiles leave from registers (REG) for
+// 4-byte keys with no or 4-byte payloads and 8 outputs per lane, when every
+// segment output is 16-byte aligned; otherwise through the LDS stage.
+template <int I, int VW, int ORDER>
+constexpr bool reg_shape() {
+    return omerge::KeyOrder<ORDER>::kWords == 1 && VW <= 1 && I == 8;
+}
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Runs merge_segments_kernel<T, I, VW, ORDER, DESC, reg> over `blocks`
+// workgroups (reg only where the shape allows it).
+template <int T, int I, int VW, int ORDER, bool DESC>
+static void run_merge(bool reg, int64_t blocks, const typename omerge::KeyOrder<ORDER>::T* A,
+                      const uint32_t* Av, int64_t m, const typename omerge::KeyOrder<ORDER>::T* B,
+                      const uint32_t* Bv, int64_t n, const int64_t* part, int64_t seg_len,
+                      typename omerge::KeyOrder<ORDER>::T* C, uint32_t* Cv,
+                      const omerge::SegDesc* desc, int64_t c_total) {
+    if constexpr (reg_shape<I, VW, ORDER>()) {
+        if (reg) {
+            run_grid(blocks, T, [&] {
+                omerge::merge_segments_kernel<T, I, VW, ORDER, DESC, true>(
+                    A, Av, m, B, Bv, n, part, seg_len, C, Cv, desc, c_total);
+            });
+            return;
+        }
+    }
+    run_grid(blocks, T, [&] {
+        omerge::merge_segments_kernel<T, I, VW, ORDER, DESC, false>(A, Av, m, B, Bv, n, part,
+                                                                   seg_len, C, Cv, desc, c_total);
+    });
+}
+
 // Partition + merge for one key order, payload width VW (words) and shape.
 template <int T, int I, int VW, int ORDER>
 static void typed_cfg(const void* A, const void* Av, int64_t m, const void* B, const void* Bv,
@@ -136,11 +168,11 @@ static void typed_cfg(const void* A, const void* Av, int64_t m, const void* B, c
         omerge::partition_kernel<4, ORDER>(a, m, b, n, seg_len, count, part);
     });
     if (m + n == 0) return;
-    run_grid(count - 1, T, [&] {
-        omerge::merge_segments_kernel<T, I, VW, ORDER>(
-            a, static_cast<const uint32_t*>(Av), m, b, static_cast<const uint32_t*>(Bv), n, part,
-            seg_len, static_cast<Key*>(C), static_cast<uint32_t*>(Cv), nullptr, m + n);
-    });
+    const bool reg = aligned16(C) && (VW == 0 || aligned16(Cv));
+    run_merge<T, I, VW, ORDER, false>(reg, count - 1, a, static_cast<const uint32_t*>(Av), m, b,
+                                      static_cast<const uint32_t*>(Bv), n, part, seg_len,
+                                      static_cast<Key*>(C), static_cast<uint32_t*>(Cv), nullptr,
+                                      m + n);
 }
 
 // Outputs per lane of the library's shapes (its items_for).
@@ -229,11 +261,10 @@ static void sort_cfg(const void* in_k, const void* in_v, int64_t N, void* out_k,
             omerge::plan_runs_kernel<4, ORDER>(bufk[cur], N, run, seg_len, per_pair, segs,
                                                desc.data());
         });
-        run_grid(segs, T, [&] {
-            omerge::merge_segments_kernel<T, I, VW, ORDER, true>(
-                bufk[cur], bufv[cur], N, bufk[cur], bufv[cur], N, nullptr, seg_len,
-                bufk[1 - cur], bufv[1 - cur], desc.data(), N);
-        });
+        const bool reg = aligned16(out_k) && (VW == 0 || aligned16(out_v));
+        run_merge<T, I, VW, ORDER, true>(reg, segs, bufk[cur], bufv[cur], N, bufk[cur], bufv[cur],
+                                         N, nullptr, seg_len, bufk[1 - cur], bufv[1 - cur],
+                                         desc.data(), N);
         cur = 1 - cur;
     }
 }
@@ -378,10 +409,9 @@ static void merge_cfg(const int32_t* A, const uint32_t* Av, int64_t m, const int
                       const uint32_t* Bv, int64_t n, const int64_t* part, int64_t seg_len,
                       int32_t* C, uint32_t* Cv) {
     const int64_t segs = (m + n + seg_len - 1) / seg_len;
-    run_grid(segs, T, [&] {
-        omerge::merge_segments_kernel<T, I, VW, 0>(A, Av, m, B, Bv, n, part, seg_len, C, Cv,
-                                                   nullptr, m + n);
-    });
+    const bool reg = aligned16(C) && (VW == 0 || aligned16(Cv));
+    run_merge<T, I, VW, 0, false>(reg, segs, A, Av, m, B, Bv, n, part, seg_len, C, Cv, nullptr,
+                                  m + n);
 }
 
 extern "C" {

@@ -257,6 +257,37 @@ def test_repeatable_and_preallocated_out():
     assert_same(first, oracle.merge_i32(A, B), "oracle")
 
 
+@pytest.mark.parametrize("off", [1, 2, 3])
+def test_unaligned_outputs(off):
+    """Outputs that start `off` words past a 16-byte boundary: the 4-byte-key
+    merges then store tiles word by word instead of as 16-byte vectors.
+    Several segments and a ragged tail; every output against the oracle and
+    the words around each output untouched."""
+    g = np.random.Generator(np.random.PCG64(40 + off))
+    A, B = pair(g, 21011 + off, 17003, 300)
+    Av, Bv = tags(A.size, B.size)
+    t = A.size + B.size
+    say("unaligned outputs", off, A.size, B.size)
+    sentinel = -123456789
+
+    def window(o):
+        buf = torch.full((t + 8,), sentinel, dtype=torch.int32, device=DEV)
+        return buf, buf[o:o + t]
+
+    buf, out = window(off)
+    om.merge_i32(dev(A), dev(B), out=out)
+    bk, ok_ = window(off)
+    bv, ov = window((off + 1) % 4)
+    om.merge_kv(dev(A), dev(Av), dev(B), dev(Bv), out_keys=ok_, out_vals=ov)
+    wk, wv = oracle.merge_kv(A, Av, B, Bv)
+    assert_same(host(out), oracle.merge_i32(A, B), "merge_i32, unaligned output")
+    assert_same(host(ok_), wk, "merge_kv keys, unaligned output")
+    assert_same(host(ov).view(np.uint32), wv, "merge_kv payloads, unaligned output")
+    for b, o in ((buf, off), (bk, off), (bv, (off + 1) % 4)):
+        h = host(b)
+        assert np.all(h[:o] == sentinel) and np.all(h[o + t:] == sentinel), "write outside output"
+
+
 def test_unsorted_input_returns():
     """Sortedness is not checked; unsorted input must still return (the
     kernels' loops are bounded) with an output of the right size."""

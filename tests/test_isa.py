@@ -1,9 +1,12 @@
 """The gfx950 code of our own build holds the instructions the design rests
 on (CPU only: hipcc compiles the library's device code to assembly).
 
-- The headline segment merge moves HBM data as 16-byte vectors
-  (global_load_dwordx4 / global_store_dwordx4), LDS data as 128-bit rows
-  (ds_write_b128 / ds_read_b128), and uses no scratch memory.
+- The headline segment merge (tiles stored from registers) moves HBM data
+  as 16-byte vectors (global_load_dwordx4 / global_store_dwordx4), writes
+  refills to LDS as 128-bit rows (ds_write_b128), swaps halves of lane pairs
+  by DPP (quad_perm 1,0,3,2), and uses no scratch memory.
+- Its staged variant (unaligned outputs) also reads the LDS stage as
+  128-bit rows (ds_read_b128).
 - The block sort's in-wavefront rounds move lanes' keys with DPP row moves
   and ds_swizzle, and use no scratch memory.
 """
@@ -19,7 +22,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 from ordered_merge_sorted_amd import build  # noqa: E402
 
-MERGE = "_ZN6omerge21merge_segments_kernelILi256ELi8ELi0ELi0ELb0EE"
+MERGE = "_ZN6omerge21merge_segments_kernelILi256ELi8ELi0ELi0ELb0ELb1EE"
+MERGE_STAGED = "_ZN6omerge21merge_segments_kernelILi256ELi8ELi0ELi0ELb0ELb0EE"
 BLOCK_SORT = "_ZN6omerge17block_sort_kernelILi1024ELi16ELi0ELi0EE"
 
 
@@ -46,6 +50,11 @@ def body(asm, prefix):
 
 def test_segment_merge_vector_accesses(asm):
     code, scratch = body(asm, MERGE)
+    for ins in ("global_load_dwordx4", "global_store_dwordx4", "ds_write_b128",
+                "quad_perm:[1,0,3,2]"):
+        assert ins in code, ins
+    assert scratch == 0
+    code, scratch = body(asm, MERGE_STAGED)
     for ins in ("global_load_dwordx4", "global_store_dwordx4", "ds_write_b128", "ds_read_b128"):
         assert ins in code, ins
     assert scratch == 0
