@@ -515,6 +515,38 @@ def test_sort_keys_and_pairs(dtype, desc):
             assert_same(host_bits(gv), as_bits(wv), "sorted pair payloads")
 
 
+@pytest.mark.parametrize("off", [0, 1, 2])
+def test_sort_unaligned_outputs(off):
+    """Sorts of int32 keys (alone and with int32 payloads) into outputs `off`
+    words past a 16-byte boundary: aligned outputs take the passes that
+    store from registers, unaligned ones the staged passes.  Many passes and
+    a ragged last pair; every output against the oracle and the words
+    around each output untouched."""
+    g = np.random.Generator(np.random.PCG64(760 + off))
+    n = 300007
+    K = g.integers(-1000, 1000, size=n).astype(np.int32)
+    V = np.arange(n, dtype=np.int32)
+    say("sort unaligned outputs", off, n)
+    sentinel = -987654321
+
+    def window(o):
+        buf = torch.full((n + 8,), sentinel, dtype=torch.int32, device=DEV)
+        return buf, buf[o:o + n]
+
+    bk, ok_ = window(off)
+    om.sort(dev(K), out=ok_)
+    pk, pko = window(off)
+    pv, pvo = window((off + 2) % 4)
+    om.sort(dev(K), dev(V), out=pko, out_vals=pvo)
+    assert_same(host(ok_), oracle.sort(K), "sorted keys, offset output")
+    wk, wv = oracle.sort(K, V)
+    assert_same(host(pko), wk, "sorted pair keys, offset output")
+    assert_same(host(pvo), wv, "sorted pair payloads, offset output")
+    for b, o in ((bk, off), (pk, off), (pv, (off + 2) % 4)):
+        h = host(b)
+        assert np.all(h[:o] == sentinel) and np.all(h[o + n:] == sentinel), "write outside output"
+
+
 def test_sort_in_place_and_large():
     """In-place sort (out = input), and 2^24 int32 keys with payloads (16
     merge passes after the block sort)."""
