@@ -20,9 +20,10 @@
  *   - Arrays are contiguous and aligned to their element size (4 bytes; 8
  *     for 64-bit keys or payloads).  Any such alignment works; 16-byte-aligned
  *     arrays take the vector path on every full 16 bytes.  Merges and sorts
- *     of 4-byte keys (with or without 4-byte payloads) into 16-byte-aligned
- *     outputs also store their tiles straight from registers, which is a
- *     few percent faster than the LDS-staged stores used otherwise.
+ *     of 4-byte keys (with or without 4-byte payloads) and of 8-byte keys
+ *     alone into 16-byte-aligned outputs also store their tiles straight
+ *     from registers, which is a few percent faster than the LDS-staged
+ *     stores used otherwise.
  *   - Lengths are int64 and must be >= 0.  A pointer may be NULL only when its
  *     length is 0.  m + n == 0 is a no-op that returns OMERGE_OK.  A total
  *     above 2^59 elements returns OMERGE_OVERFLOW (byte sizes then fit int64).

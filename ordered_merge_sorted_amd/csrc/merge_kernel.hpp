@@ -797,6 +797,70 @@ __device__ __forceinline__ void store_direct8(int32_t* __restrict__ dst, int bas
     }
 }
 
+// The same for two words per output (8-byte keys): a lane's slice is 64
+// bytes and the wavefront's output four 1 KB runs.  Lane 4Q+r merges slice
+// 16r+Q (direct_slice_wide), so store u (run u) needs the four 16-byte
+// quarters of the slice lane 4Q+u holds, one per lane of quad Q: a 4x4
+// transpose of 16-byte blocks inside each quad, done as two exchange stages
+// (lane pairs 1 apart, then 2 apart) in which each lane sends by DPP the two
+// blocks it replaces.  w holds the lane's 8 outputs as 16 words.
+__device__ __forceinline__ int direct_slice_wide(int tid) {
+    return (tid & ~63) + ((tid & 3) << 4) + ((tid & 63) >> 2);
+}
+
+template <int XOR>
+__device__ __forceinline__ int swap_quad_lanes(int x) {
+    static_assert(XOR == 1 || XOR == 2, "quad exchange");
+    return __builtin_amdgcn_update_dpp(x, x, XOR == 1 ? 0xB1 : 0x4E, 0xF, 0xF, false);
+}
+
+// One exchange stage: blocks j with (j ^ r) & XOR set (r = lane in quad) go
+// to the partner r ^ XOR, which sends back its blocks j ^ XOR into them.
+template <int XOR>
+__device__ __forceinline__ void quad_exchange(int (&w)[16], int r) {
+    const bool hi = (r & XOR) != 0;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        // The two blocks of this pair of positions: lo has bit XOR clear.
+        const int lo = XOR == 1 ? 2 * k : k;
+        const int hib = lo + XOR;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int a = w[4 * lo + u];
+            const int b = w[4 * hib + u];
+            const int recv = swap_quad_lanes<XOR>(hi ? a : b);
+            w[4 * lo + u] = hi ? recv : a;
+            w[4 * hib + u] = hi ? b : recv;
+        }
+    }
+}
+
+template <int ORDER>
+__device__ __forceinline__ void store_direct16(int32_t* __restrict__ dst, int base, int len,
+                                               bool aligned, int (&w)[16], int tid) {
+    const int r = tid & 3;
+    quad_exchange<1>(w, r);
+    quad_exchange<2>(w, r);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        const int p = base + 256 * h + 4 * (tid & 63);
+        int4v v;
+        v.x = w[4 * h];
+        v.y = w[4 * h + 1];
+        v.z = w[4 * h + 2];
+        v.w = w[4 * h + 3];
+        const int4v y = map_vec<ORDER, false>(v);
+        if (aligned && p + 4 <= len) {
+            store_stream4(dst + p, y);
+        } else {
+            if (p < len) dst[p] = y.x;
+            if (p + 1 < len) dst[p + 1] = y.y;
+            if (p + 2 < len) dst[p + 2] = y.z;
+            if (p + 3 < len) dst[p + 3] = y.w;
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Segment merge kernel: one workgroup per segment of the output.
 //
@@ -814,9 +878,9 @@ struct SegDesc {
     int64_t a1, b1;      // one past the last A and B element
 };
 
-// REG = true: tiles leave from registers (store_direct8) instead of through
-// the LDS stage; 4-byte keys with no or 4-byte payloads and 8 outputs per
-// lane only.  Any output works, but only 16-byte-aligned segment outputs
+// REG = true: tiles leave from registers (store_direct8, store_direct16)
+// instead of through the LDS stage; 4-byte keys with no or 4-byte payloads,
+// or 8-byte keys alone, and 8 outputs per lane only.  Any output works, but only 16-byte-aligned segment outputs
 // get 16-byte stores, so the launcher picks it when they are.
 template <int THREADS, int ITEMS, int VW, int ORDER, bool DESC = false, bool REG = false>
 __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
@@ -834,7 +898,8 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
     // With REG each tile is stored from registers (store_direct8) and there
     // is no LDS stage: the LDS saved lets more workgroups, and so more refill
     // loads, share a CU.
-    static_assert(!REG || (KW == 1 && VW <= 1 && ITEMS == 8), "register stores: 4-byte keys");
+    static_assert(!REG || (((KW == 1 && VW <= 1) || (KW == 2 && VW == 0)) && ITEMS == 8),
+                  "register stores: 4-byte keys with no or 4-byte payloads, or 8-byte keys");
     constexpr bool kDirect = REG;
     using Cfg = MergeCfg<THREADS, ITEMS, KW, VW, !kDirect>;
     constexpr int kTile = Cfg::kTile;
@@ -862,7 +927,7 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
 
     const int tid = threadIdx.x;
     // The slice of the tile this lane merges: ITEMS outputs from slice*ITEMS.
-    const int slice = kDirect ? direct_slice(tid) : tid;
+    const int slice = !kDirect ? tid : (KW == 1 ? direct_slice(tid) : direct_slice_wide(tid));
     const int64_t seg = blockIdx.x;
     int64_t k0, i0, j0;  // first output, first A and first B element of the segment
     int c_len, a_len, b_len;
@@ -1050,7 +1115,7 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
             // This lane's row of the stage: ITEMS contiguous elements.
             int* const row = stage + stage_word(tid * ITEMS * KW);
             // Outputs kept in registers for store_direct8 (keys, payloads).
-            int kout[kDirect ? ITEMS : 1];
+            int kout[kDirect ? ITEMS * KW : 1];
             int vout[kDirect && KV ? ITEMS : 1];
             if constexpr (!KV) {
                 // Candidates: the next ITEMS keys of each side from the lane's
@@ -1081,7 +1146,14 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
                 bitonic_clean<ITEMS>(x);
                 if constexpr (kDirect) {
 #pragma unroll
-                    for (int t = 0; t < ITEMS; ++t) kout[t] = static_cast<int>(x[t]);
+                    for (int t = 0; t < ITEMS; ++t) {
+                        if constexpr (KW == 1) {
+                            kout[t] = static_cast<int>(x[t]);
+                        } else {
+                            kout[2 * t] = low_word(x[t]);
+                            kout[2 * t + 1] = high_word(x[t]);
+                        }
+                    }
                 } else {
 #pragma unroll
                 for (int v = 0; v < ITEMS * KW / 4; ++v) {
@@ -1157,8 +1229,12 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
             if constexpr (kDirect) {
                 // From registers: each wavefront stores its 512 outputs as two
                 // 1 KB runs (store_direct8).
-                const int wbase = (tid >> 6) * 64 * ITEMS;
-                store_direct8<ORDER>(Cs + c_done, wbase, c_tile, c_aligned, kout, tid);
+                const int wbase = (tid >> 6) * 64 * ITEMS * KW;
+                if constexpr (KW == 1)
+                    store_direct8<ORDER>(Cs + c_done, wbase, c_tile, c_aligned, kout, tid);
+                else
+                    store_direct16<ORDER>(Cs + KW * c_done, wbase, KW * c_tile, c_aligned, kout,
+                                          tid);
                 if constexpr (KV)
                     store_direct8<VORDER>(Cvs + c_done, wbase, c_tile, cv_aligned, vout, tid);
             } else {

@@ -55,6 +55,9 @@ constexpr int kVersion = 100;  // 0.1.0
 #ifndef OMERGE_TILES_PER_SEG_KV  // the same for 4-byte keys with 4-byte payloads
 #define OMERGE_TILES_PER_SEG_KV 3
 #endif
+#ifndef OMERGE_TILES_PER_SEG_WIDE_KEYS  // target for 8-byte keys alone, stored from registers
+#define OMERGE_TILES_PER_SEG_WIDE_KEYS 3
+#endif
 #ifndef OMERGE_TILES_PER_SEG_WIDE  // target for the shapes with 8-byte keys or payloads
 #define OMERGE_TILES_PER_SEG_WIDE 6
 #endif
@@ -181,10 +184,11 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // 4, 0.780 at 5, the merge kernel alone 0.697, 0.713, 0.728 and 0.757 ms;
 // 2^27+2^24 skewed: 0.213 ms at 2, 0.222-0.224 at 3 and 4), 4+4-byte pairs
 // at exactly R = 3 (2^26+2^26 pairs: 0.387 ms at 2 and 3, 0.391 at 4), and
-// 8-byte keys at 6 (2% faster than at 3), searched one tile either side for
-// the R whose last round of workgroups is fullest.  Sort passes and batches (descriptor
-// segments, cut again at every run or merge end) measured 2-5% faster per
-// pass with R = 8 searched over [6, 10].  Inputs with fewer tiles than the
+// 8-byte keys at 3 (through the stage at 6, 2% faster than at 3), searched
+// one tile either side for the R whose last round of workgroups is fullest.
+// Batches and staged sort passes (descriptor segments, cut again at every run
+// or merge end) measured 2-5% faster per pass with R = 8 searched over
+// [6, 10]; sort passes stored from registers take 4 over [2, 6].  Inputs with fewer tiles than the
 // window's low end times the slots get the smallest R that keeps a single
 // round.
 int64_t choose_seg_len(int64_t total, int tile, int slots, SegWindow win) {
@@ -250,16 +254,20 @@ struct Path {
     static constexpr int kItems = items_for(KW, VW);
     static constexpr int kTile = kThreads * kItems;
     // Single merges (measured per shape, above choose_seg_len): exactly 2
-    // tiles per segment for 4-byte keys alone, 3 for 4+4-byte pairs; 6,
-    // searched one tile either side, for the shapes with 8-byte parts.
-    // Through the LDS stage (unaligned outputs) 4-byte keys alone ran best
-    // at 4.
+    // tiles per segment for 4-byte keys alone, 3 for 4+4-byte pairs; 3,
+    // searched one tile either side, for 8-byte keys alone (2^28+2^28 int64:
+    // 1.54 ms at 3, 1.55 at 4, 1.57-1.59 at 6); 6 for the 12- and 16-byte
+    // shapes.  Through the LDS stage (unaligned outputs) 4-byte keys alone
+    // ran best at 4 and 8-byte keys at 6.
     static constexpr SegWindow kMergeWindow =
         KW == 1 && VW == 0   ? SegWindow{OMERGE_TILES_PER_SEG, 0}
         : KW == 1 && VW == 1 ? SegWindow{OMERGE_TILES_PER_SEG_KV, 0}
+        : KW == 2 && VW == 0 ? SegWindow{OMERGE_TILES_PER_SEG_WIDE_KEYS, 1}
                              : SegWindow{OMERGE_TILES_PER_SEG_WIDE, 1};
     static constexpr SegWindow kStagedMergeWindow =
-        KW == 1 && VW == 0 ? SegWindow{OMERGE_TILES_PER_SEG_STAGED, 0} : kMergeWindow;
+        KW == 1 && VW == 0   ? SegWindow{OMERGE_TILES_PER_SEG_STAGED, 0}
+        : KW == 2 && VW == 0 ? SegWindow{OMERGE_TILES_PER_SEG_WIDE, 1}
+                             : kMergeWindow;
     static constexpr int kTileItems = tile_items_for(KW, VW);  // tile path
     static constexpr int kBatchTile = kThreads * kTileItems;
     static constexpr int kSortItems = sort_items_for(KW, VW);
@@ -279,11 +287,11 @@ struct Path {
     static constexpr int kSortTile = kSortThreads * kSortItems;
 
     // Tiles stored from registers (no LDS stage): 4-byte keys with no or
-    // 4-byte payloads.  Launches take it when every segment's output is
+    // 4-byte payloads, and 8-byte keys alone.  Launches take it when every segment's output is
     // 16-byte aligned; otherwise the staged kernel, which stores 16-byte
     // vectors at any output phase.  Slots are counted for the kernel the
     // aligned case runs.
-    static constexpr bool kReg = KW == 1 && VW <= 1 && kItems == 8;
+    static constexpr bool kReg = ((KW == 1 && VW <= 1) || (KW == 2 && VW == 0)) && kItems == 8;
 
     template <bool DESC>
     static void launch_merge(bool reg, int64_t blocks, hipStream_t stream, const Key* A,

@@ -129,7 +129,8 @@ static void run_grid(int64_t blocks, int threads, const std::function<void()>& b
 // segment output is 16-byte aligned; otherwise through the LDS stage.
 template <int I, int VW, int ORDER>
 constexpr bool reg_shape() {
-    return omerge::KeyOrder<ORDER>::kWords == 1 && VW <= 1 && I == 8;
+    constexpr int kw = omerge::KeyOrder<ORDER>::kWords;
+    return ((kw == 1 && VW <= 1) || (kw == 2 && VW == 0)) && I == 8;
 }
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 

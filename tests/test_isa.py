@@ -7,6 +7,7 @@ on (CPU only: hipcc compiles the library's device code to assembly).
   by DPP (quad_perm 1,0,3,2), and uses no scratch memory.
 - Its staged variant (unaligned outputs) also reads the LDS stage as
   128-bit rows (ds_read_b128).
+- No instantiation of the segment merge uses scratch memory.
 - The block sort's in-wavefront rounds move lanes' keys with DPP row moves
   and ds_swizzle, and use no scratch memory.
 """
@@ -58,6 +59,16 @@ def test_segment_merge_vector_accesses(asm):
     for ins in ("global_load_dwordx4", "global_store_dwordx4", "ds_write_b128", "ds_read_b128"):
         assert ins in code, ins
     assert scratch == 0
+
+
+def test_no_merge_kernel_spills(asm):
+    """Every instantiation of the segment merge (each key order, payload
+    width, mode and store path) runs without scratch: a spill of the
+    register-stored outputs once made the 8-byte-key merge twice as slow."""
+    names = sorted(set(re.findall(r"^(_ZN6omerge21merge_segments_kernel\w*):", asm, re.M)))
+    assert len(names) >= 24, len(names)
+    spilled = [n for n in names if body(asm, n)[1] != 0]
+    assert not spilled, spilled
 
 
 def test_block_sort_lane_exchanges(asm):
