@@ -209,7 +209,9 @@ int omerge_co_rank(const int32_t *A, int64_t m, const int32_t *B, int64_t n,
  *
  * omerge_segment_length -- the segment length (outputs per workgroup) that
  *   merge_i32 (kv = 0) or merge_kv (kv != 0) uses on the current device for
- *   these sizes.  Always a positive multiple of 4.  Returns -1 on bad sizes.
+ *   these sizes and 16-byte-aligned outputs (merges into unaligned outputs
+ *   pick their own).  Always a positive multiple of 4.  Returns -1 on bad
+ *   sizes.
  * omerge_partition_count -- number of int64 entries the partition array needs
  *   for `total` = m+n outputs cut into segments of `seg_len`:
  *   ceil(total/seg_len) + 1.  Returns -1 on bad sizes.
