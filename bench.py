@@ -96,7 +96,7 @@ def run_oracle(w, arrs):
     return out, time.perf_counter() - t0
 
 
-def time_oracle(w, arrs, first_s, want_runs_s=10.0, max_runs=5):
+def time_oracle(w, arrs, first_s, want_runs_s=12.0, max_runs=8):
     """Rates of the single-threaded CPU oracle on the full workload: the run
     already made for the check (first_s seconds), then more runs until about
     want_runs_s seconds have passed (at most max_runs in all)."""
