@@ -32,11 +32,11 @@
 //     never past the array).
 //   * The refill for tile t+1 is issued into registers as soon as tile t's
 //     split is known, before tile t is merged, and written to LDS only after
-//     the tile's rows are staged and before its stores; the HBM latency hides
-//     behind the merge.
-//   * Each lane searches the END of its slice; its start is its left
-//     neighbour's end, read from a small LDS array, and the last lane's end
-//     is the tile's split.  One search per lane per tile.  Inside a tile the
+//     every lane has read its candidates and before the tile's stores; the
+//     HBM latency hides behind the merge.
+//   * Each lane searches the END of its slice; its start is the previous
+//     slice's end, read from a small LDS array, and the last slice's end is
+//     the tile's split.  One search per lane per tile.  Inside a tile the
 //     search is a fixed-trip, branchless bisection of the merge diagonal
 //     (one probe pair per step) within the same bounds as the pages' search;
 //     it returns the same unique co-rank with about a third of the
@@ -53,16 +53,19 @@
 //   * Each key ring has a guard zone that mirrors its first ITEMS elements
 //     past its end, so a lane reads its ITEMS candidates at one base address
 //     with immediate offsets and no wrap arithmetic.
-//   * Single merges of 4-byte keys (alone or with 4-byte payloads) store
-//     from registers: the lanes of a wavefront take its 64 slices in the
-//     order 0,32,1,33,..., so one DPP swap inside each lane pair gives every
-//     lane two 16-byte pieces of two 1 KB runs of the output
-//     (store_direct8).  With no stage a workgroup needs 17 KB of LDS instead
-//     of 26 KB, and 8 workgroups share a CU instead of 6: a third more
-//     refill loads in flight.
-//   * The other shapes go through an LDS stage padded by 4 words every 32,
-//     which makes the 16-byte stage writes (lane-contiguous) and 16-byte
-//     stage reads (for the coalesced stores) free of bank conflicts.
+//   * Merges and sort passes of 4-byte keys (alone or with 4-byte payloads)
+//     into 16-byte-aligned outputs store from registers: the lanes of a
+//     wavefront take its 64 slices in the order 0,32,1,33,..., so one DPP
+//     swap inside each lane pair gives every lane two 16-byte pieces of two
+//     1 KB runs of the output (store_direct8).  With no stage a 4-byte-key
+//     workgroup needs 17 KB of LDS instead of 26 KB, and 8 workgroups share
+//     a CU instead of 6: a third more refill loads in flight.  8-byte keys
+//     alone do the same with a transpose inside each lane quad
+//     (store_direct16).
+//   * The other shapes, unaligned outputs and batches go through an LDS stage
+//     padded by 4 words every 32, which makes the 16-byte stage writes
+//     (lane-contiguous) and 16-byte stage reads (for the coalesced stores)
+//     free of bank conflicts.
 //   * The partition kernel can search each boundary with a group of G lanes:
 //     G points of the diagonal are tested at once and a ballot narrows the
 //     interval to one of the G+1 gaps per round (the pages note the search
