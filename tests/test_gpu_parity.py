@@ -288,6 +288,27 @@ def test_unaligned_outputs(off):
         assert np.all(h[:o] == sentinel) and np.all(h[o + t:] == sentinel), "write outside output"
 
 
+@pytest.mark.parametrize("off", [0, 1])
+def test_unaligned_outputs_wide(off):
+    """int64 and float64 keys into outputs `off` elements (8 bytes) past a
+    16-byte boundary: aligned outputs take the register-store merge (quad
+    transpose), unaligned ones the staged one.  Several segments and a
+    ragged tail; every output against the oracle, guard words untouched."""
+    g = np.random.Generator(np.random.PCG64(50 + off))
+    for dtype in (np.int64, np.float64):
+        A, B = typed_pair(g, dtype, False, 30011 + off, 25013)
+        t = A.size + B.size
+        say("unaligned wide outputs", np.dtype(dtype).name, off, A.size, B.size)
+        buf = torch.full((t + 4,), -7, dtype=torch.int64, device=DEV)
+        out = buf[off:off + t]
+        if dtype == np.float64:
+            out = out.view(torch.float64)
+        om.merge(dev_typed(A), dev_typed(B), out=out)
+        assert_same(host_bits(out), as_bits(oracle.merge_keys(A, B, False)), "wide, offset output")
+        h = host(buf)
+        assert np.all(h[:off] == -7) and np.all(h[off + t:] == -7), "write outside output"
+
+
 def test_unsorted_input_returns():
     """Sortedness is not checked; unsorted input must still return (the
     kernels' loops are bounded) with an output of the right size."""
