@@ -188,9 +188,9 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // one tile either side for the R whose last round of workgroups is fullest.
 // Batches and staged sort passes (descriptor segments, cut again at every run
 // or merge end) measured 2-5% faster per pass with R = 8 searched over
-// [6, 10]; sort passes stored from registers take 4 over [2, 6].  Inputs with fewer tiles than the
-// window's low end times the slots get the smallest R that keeps a single
-// round.
+// [6, 10]; sort passes stored from registers take 4 over [2, 6].  Inputs
+// with fewer tiles than the window's low end times the slots get the
+// smallest R that keeps a single round.
 int64_t choose_seg_len(int64_t total, int tile, int slots, SegWindow win) {
     const int64_t lo_r = win.target > win.slack ? win.target - win.slack : 1;
     const int64_t hi_r = win.target + win.slack;
@@ -287,9 +287,9 @@ struct Path {
     static constexpr int kSortTile = kSortThreads * kSortItems;
 
     // Tiles stored from registers (no LDS stage): 4-byte keys with no or
-    // 4-byte payloads, and 8-byte keys alone.  Launches take it when every segment's output is
-    // 16-byte aligned; otherwise the staged kernel, which stores 16-byte
-    // vectors at any output phase.  Slots are counted for the kernel the
+    // 4-byte payloads, and 8-byte keys alone.  Launches take it when every
+    // segment's output is 16-byte aligned; otherwise the staged kernel,
+    // which stores 16-byte vectors at any output phase.  Slots are counted for the kernel the
     // aligned case runs.
     static constexpr bool kReg = ((KW == 1 && VW <= 1) || (KW == 2 && VW == 0)) && kItems == 8;
 
