@@ -166,7 +166,7 @@ static void typed_cfg(const void* A, const void* Av, int64_t m, const void* B, c
     const Key* b = static_cast<const Key*>(B);
     const int64_t count = (m + n + seg_len - 1) / seg_len + 1;
     run_grid((count * 4 + 255) / 256, 256, [&] {
-        omerge::partition_kernel<4, ORDER>(a, m, b, n, seg_len, count, part);
+        omerge::partition_kernel<4, ORDER, 4, 16>(a, m, b, n, seg_len, count, part);
     });
     if (m + n == 0) return;
     const bool reg = aligned16(C) && (VW == 0 || aligned16(Cv));
@@ -425,9 +425,8 @@ int emu_tile(int variant, int kv) {
     return omerge::MergeCfg<128, 4, 1, 0>::kTile;
 }
 
-// lanes = lanes per boundary in the partition search (1, 4, 8, 16, 64), or
-// 42, 416, 4216, 432, 464 for 4 lanes in phase 1 with 2 or 4 in phase 2 and
-// a phase-1 stride of 8, 16, 32 or 64.
+// lanes = lanes per boundary in the partition search (1, 4, 8, 16, 64; phase-1
+// stride 8), or 416 for the library's launch (4 lanes, stride 16).
 void emu_partition(int lanes, const int32_t* A, int64_t m, const int32_t* B, int64_t n,
                    int64_t seg_len, int64_t* part) {
     const int64_t count = (m + n + seg_len - 1) / seg_len + 1;
@@ -440,12 +439,8 @@ void emu_partition(int lanes, const int32_t* A, int64_t m, const int32_t* B, int
         case 4: go(omerge::partition_kernel<4, 0>); break;
         case 8: go(omerge::partition_kernel<8, 0>); break;
         case 16: go(omerge::partition_kernel<16, 0>); break;
-        // 4 lanes in phase 1; phase-2 lanes and phase-1 stride vary.
-        case 42: go(omerge::partition_kernel<4, 0, 2, 8>); break;
+        // The library's launch: 4 lanes, every 16th boundary in phase 1.
         case 416: go(omerge::partition_kernel<4, 0, 4, 16>); break;
-        case 4216: go(omerge::partition_kernel<4, 0, 2, 16>); break;
-        case 432: go(omerge::partition_kernel<4, 0, 4, 32>); break;
-        case 464: go(omerge::partition_kernel<4, 0, 4, 64>); break;
         default: go(omerge::partition_kernel<64, 0>); break;
     }
 }
