@@ -8,17 +8,27 @@ partition kernel (one co-rank per segment boundary) and the segment merge
 kernel, launched through the C ABI on the current torch stream.  The default
 workload is 2^28 + 2^28 int32 keys iid uniform over the int32 range, sorted.
 
-Before timing, the merged output of one untimed launch is compared with the
-CPU oracle on every element (a wrong answer never produces a number); that
-oracle run is the first run of the reported CPU baseline, whose other runs
-come after the GPU timing.  Then W untimed steps (the default 50, ~40 ms,
-covers the device's clock ramp after the seconds of CPU work), then exactly
-K timed steps back to back between device synchronisations (the step rate).  The same K steps are then run again with a HIP event pair around
-every segment-merge launch, which gives that kernel's mean duration for the
-roofline figure.  A streaming copy of the same byte count is timed beside it
-as the bandwidth this device actually delivers.
+Order of work (a wrong answer never produces a number, and the timed steps
+never follow seconds of device idle):
+  1. The inputs are generated and the CPU oracle merges them, before anything
+     runs on the device.  That oracle run is the first run of the reported
+     CPU baseline.
+  2. One untimed step is checked against the oracle on every element.
+  3. The bandwidth references run on the same byte count: the library's
+     16-byte streaming copy kernel and, independently, a device-to-device
+     hipMemcpyAsync (torch's copy_); then the one-call merge_i32.  They keep
+     the device busy right up to the warm-up.
+  4. Exactly W untimed steps, then exactly K timed steps back to back between
+     device synchronisations: the step rate.
+  5. The same K steps again with a HIP event pair around each kernel on its
+     stream: the partition's and the segment merge's mean launch durations
+     (the roofline figure is the merge kernel's).
+  6. The output of the last timed step is checked against the oracle again.
+  7. The other four workloads, each checked on every element before it is
+     timed, one row each on stderr (and in the JSON line).
+  8. More oracle runs, up to about 12 s of CPU work in all: the CPU baseline.
 
-Prints ONE JSON line on stdout; the device banner and extra figures go to
+Prints ONE JSON line on stdout; the device banner and the tables go to
 stderr.  Only one GPU is used: --gpus above 1 exits with a message.
 """
 from __future__ import annotations
@@ -37,6 +47,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+MALL_BYTES = 256 << 20  # MI355X Infinity Cache: footprints below it are cache resident
 SORT_SEED = 20261207  # inputs of the sort and batched-merge timings
 METRIC = "merged elements/sec and achieved HBM GB/s (% of MI355X peak), int32 m=n=2^28"
 COUNTER_FILE = os.path.join(ROOT, "profiles", "merge_segments_uniform_i32_2p28x2p28_traffic.md")
@@ -79,12 +90,15 @@ def device_banner(torch):
     log("GPU: %s (%s), %d CUs, %.1f GiB, L2 %s MiB" % (
         p.name, arch, p.multi_processor_count, p.total_memory / 2**30,
         getattr(p, "L2_cache_size", 0) / 2**20 if hasattr(p, "L2_cache_size") else "?"))
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count()
-    log("host: %d cores available to this process (nproc %s)" % (cores, os.cpu_count()))
+    log("host: %d cores available to this process (nproc %s)" % (host_cores(), os.cpu_count()))
     return arch
+
+
+def host_cores() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
 
 
 def run_oracle(w, arrs):
@@ -108,18 +122,183 @@ def time_oracle(w, arrs, first_s, want_runs_s=12.0, max_runs=8):
     return [w.total / dt for dt in secs]
 
 
-def ablation(om, d_arrs, want, w, stream):
+def _warm(fn, seconds=0.03, at_least=2):
+    """Runs fn (synchronising) until `seconds` have passed, at least
+    `at_least` times: the device leaves its idle clocks before anything is
+    timed."""
+    import torch
+    t0, n = time.perf_counter(), 0
+    while n < at_least or time.perf_counter() - t0 < seconds:
+        fn()
+        torch.cuda.synchronize()
+        n += 1
+
+
+def _time(fn, stream, reps=5, warm=True):
+    """Mean ms of fn over `reps` back-to-back calls between one event pair."""
+    import torch
+    if warm:
+        _warm(fn)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+class Resident:
+    """One workload's inputs resident in HBM, its partition array and its
+    outputs, with the two launches of a step."""
+
+    def __init__(self, om, torch, w, arrs, dev, stream):
+        def to_dev(x):
+            return torch.from_numpy(x.view(np.int32) if x.dtype == np.uint32 else x).to(dev)
+
+        self.om, self.w, self.stream = om, w, stream
+        self.d = [to_dev(x) for x in arrs]
+        self.seg_len = om.segment_length(w.m, w.n, kv=w.kv)
+        self.count = om.partition_count(w.total, self.seg_len)
+        self.part = torch.empty(self.count, dtype=torch.int64, device=dev)
+        self.out = torch.empty(w.total, dtype=torch.int32, device=dev)
+        self.out_v = torch.empty(w.total, dtype=torch.int32, device=dev) if w.kv else None
+
+    def partition(self):
+        d = self.d
+        self.om.partition(d[0], d[2] if self.w.kv else d[1], self.seg_len, out=self.part,
+                          stream=self.stream)
+
+    def merge(self):
+        d = self.d
+        if self.w.kv:
+            self.om.merge_segments_kv(d[0], d[1], d[2], d[3], self.part, self.seg_len,
+                                      out_keys=self.out, out_vals=self.out_v, stream=self.stream)
+        else:
+            self.om.merge_segments_i32(d[0], d[1], self.part, self.seg_len, out=self.out,
+                                       stream=self.stream)
+
+    def step(self):
+        self.partition()
+        self.merge()
+
+    def one_call(self):
+        d = self.d
+        if self.w.kv:
+            self.om.merge_kv(d[0], d[1], d[2], d[3], out_keys=self.out, out_vals=self.out_v,
+                             stream=self.stream)
+        else:
+            self.om.merge_i32(d[0], d[1], out=self.out, stream=self.stream)
+
+    def matches(self, want) -> bool:
+        import torch
+        torch.cuda.synchronize()
+        if self.w.kv:
+            return (np.array_equal(self.out.cpu().numpy(), want[0]) and
+                    np.array_equal(self.out_v.cpu().numpy().view(np.uint32), want[1]))
+        return np.array_equal(self.out.cpu().numpy(), want)
+
+    def timed_steps(self, steps):
+        """Exactly `steps` steps back to back between device synchronisations:
+        (event ms per step, host-clock ms per step)."""
+        import torch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        e0.record(self.stream)
+        for _ in range(steps):
+            self.step()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        t = time.perf_counter() - t
+        return e0.elapsed_time(e1) / steps, t * 1e3 / steps
+
+    def kernel_times(self, steps):
+        """`steps` steps with an event before the partition, between the two
+        launches and after the merge: per-launch ms of each kernel."""
+        import torch
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for k in range(steps):
+            ev[k][0].record(self.stream)
+            self.partition()
+            ev[k][1].record(self.stream)
+            self.merge()
+            ev[k][2].record(self.stream)
+        torch.cuda.synchronize()
+        part = [e[0].elapsed_time(e[1]) for e in ev]
+        merge = [e[1].elapsed_time(e[2]) for e in ev]
+        return part, merge
+
+
+def copy_references(om, torch, nbytes, dev, stream, reps=10):
+    """ms of the library's streaming copy kernel and of a device-to-device
+    hipMemcpyAsync (torch copy_ of contiguous same-dtype tensors), each over
+    `nbytes` bytes read and as many written."""
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device=dev)
+    src.random_(0, 1 << 30)
+    dst = torch.empty_like(src)
+    copy_ms = _time(lambda: om.stream_copy(src, out=dst, stream=stream), stream, reps=reps)
+    if not torch.equal(src, dst):
+        log("FAILED: the streaming copy kernel's output differs from its input")
+        sys.exit(1)
+    dst.zero_()
+    with torch.cuda.stream(stream):
+        memcpy_ms = _time(lambda: dst.copy_(src), stream, reps=reps)
+    if not torch.equal(src, dst):
+        log("FAILED: the device-to-device copy's output differs from its input")
+        sys.exit(1)
+    del src, dst
+    return copy_ms, memcpy_ms
+
+
+def workload_row(om, torch, name, dev, stream, warmup, steps):
+    """One workload: generated, merged by the oracle, checked on every
+    element, then timed (at least `warmup` untimed steps and 50 ms, then at
+    least `steps` timed steps and 20 ms).  Returns the row as a dict."""
+    from ordered_merge_sorted_amd.workloads import WORKLOADS
+    w = WORKLOADS[name]
+    arrs = w.make()
+    want, _ = run_oracle(w, arrs)
+    r = Resident(om, torch, w, arrs, dev, stream)
+    r.out.fill_(-1)
+    r.step()
+    if not r.matches(want):
+        log("FAILED: workload %s: the merged output differs from the oracle" % name)
+        sys.exit(1)
+    del want
+    _warm(r.step, seconds=0.05, at_least=max(warmup, 2))
+    one_ms = r.timed_steps(1)[0]
+    reps = max(steps, int(20.0 / max(one_ms, 1e-3)) + 1)
+    ms, _ = r.timed_steps(reps)
+    part, merge = r.kernel_times(reps)
+    alg = w.roofline_bytes
+    copy_ms, _ = copy_references(om, torch, alg // 2, dev, stream)
+    gbs = alg / (ms * 1e-3) / 1e9
+    row = {"step_ms": ms, "steps": reps,
+           "elements_per_s": w.total / (ms * 1e-3),
+           "gbps": gbs, "pct_peak": 100 * gbs / HBM_PEAK_GBS,
+           "pct_copy": 100 * copy_ms / ms,
+           "merge_kernel_ms": float(np.mean(merge)),
+           "partition_kernel_ms": float(np.mean(part)),
+           "cache_resident": alg <= MALL_BYTES,
+           "checked": "bit-exact vs oracle"}
+    del r
+    torch.cuda.empty_cache()
+    return row
+
+
+def ablation(om, torch, d_a, d_b, want, w, stream):
     """Global-memory kernels of the pages (no LDS) on the same inputs: one
     co-rank search then a walk, or two searches per slice, at 1..256 outputs
     per lane.  Each is checked against the oracle before it is timed."""
-    import torch
-    out = torch.empty(w.total, dtype=torch.int32, device=d_arrs[0].device)
-    log("ablation: global-memory merge kernels vs the LDS-tiled segment merge")
+    out = torch.empty(w.total, dtype=torch.int32, device=d_a.device)
+    log("ablation on %s: global-memory merge kernels (no LDS)" % w.name)
     log("%-28s %10s %10s %8s" % ("kernel", "ms", "GB/s", "% peak"))
     for two in (False, True):
         for per in (1, 4, 16, 64, 256):
             def go():
-                om.merge_i32_direct(d_arrs[0], d_arrs[1], per_thread=per, two_searches=two,
+                om.merge_i32_direct(d_a, d_b, per_thread=per, two_searches=two,
                                     out=out, stream=stream)
             out.fill_(-1)
             go()
@@ -127,21 +306,15 @@ def ablation(om, d_arrs, want, w, stream):
             if not np.array_equal(out.cpu().numpy(), want):
                 log("FAILED: direct kernel per=%d two_searches=%s differs from the oracle" % (per, two))
                 sys.exit(1)
-            for _ in range(2):
-                go()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(5):
-                go()
-            b.record(stream)
-            torch.cuda.synchronize()
-            ms = a.elapsed_time(b) / 5
+            ms = _time(go, stream, reps=5, warm=False) if per > 1 or w.total < (1 << 26) else \
+                _time(go, stream, reps=2, warm=False)
             gbs = w.roofline_bytes / (ms * 1e-3) / 1e9
             log("%-28s %10.3f %10.1f %8.1f" % ("%s, %d per lane" % ("two searches" if two else "search+walk", per),
                                                 ms, gbs, 100 * gbs / HBM_PEAK_GBS))
+    del out
 
 
-def typed_orders(om, d_arrs, c_ref, w, stream):
+def typed_orders(om, torch, d_arrs, c_ref, w, stream):
     """The key orders of omerge_merge_keys on inputs derived from the int32
     workload on the device: uint32 keys x ^ 2^31, float32 keys with bits
     (x ^ 2^31) >> 1 (non-negative patterns, so bit order is totalOrder; some
@@ -149,7 +322,6 @@ def typed_orders(om, d_arrs, c_ref, w, stream):
     (x ^ 2^31 as uint32) << 31, each ascending and reversed for descending.
     Each output is checked against the same map of the int32 merge output
     (keys only: the sorted multiset is unique) before it is timed."""
-    import torch
     log("key orders (omerge_merge_keys, %s)" % w.name)
     log("%-28s %10s %10s %8s" % ("order", "ms", "GB/s", "% peak"))
     sign = torch.tensor(-(1 << 31), dtype=torch.int32, device=c_ref.device)
@@ -183,48 +355,17 @@ def typed_orders(om, d_arrs, c_ref, w, stream):
                 log("FAILED: key order %s%s differs from the mapped int32 merge" %
                     (name, " desc" if desc else ""))
                 sys.exit(1)
-            _warm(go)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(20):
-                go()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / 20
+            ms = _time(go, stream, reps=20)
             gbs = 2 * w.total * out.element_size() / (ms * 1e-3) / 1e9
             log("%-28s %10.3f %10.1f %8.1f" % (name + (" descending" if desc else " ascending"),
                                                 ms, gbs, 100 * gbs / HBM_PEAK_GBS))
             del a, b, out, want
 
 
-def _warm(fn, seconds=0.03):
-    """Runs fn (synchronising) until `seconds` have passed, at least twice:
-    the device leaves its idle clocks before anything is timed."""
-    import torch
-    t0, n = time.perf_counter(), 0
-    while n < 2 or time.perf_counter() - t0 < seconds:
-        fn()
-        torch.cuda.synchronize()
-        n += 1
-
-
-def _time(fn, stream, reps=5):
-    import torch
-    _warm(fn)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
-        fn()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
-
-
-def sort_and_batch(om, stream):
+def sort_and_batch(om, torch, stream):
     """The merge sort and the batched merge on 2^28 int32 keys (and 2^27
     key+payload pairs), each checked against torch's stable sort before it
     is timed; torch.sort is timed beside it for context."""
-    import torch
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev)
     g.manual_seed(SORT_SEED)
@@ -275,40 +416,23 @@ def sort_and_batch(om, stream):
         log("%-44s %10.3f %14.4g  (torch.sort %.3f ms)" % (
             "omerge sort, 2^27 %s keys" % name, ms, tens.numel() / (ms * 1e-3), ms_t))
         del tens, o, ref
-    # 2^15 merges of 4096 + 4096 sorted keys each (2^28 outputs)
-    pairs, L = 1 << 15, 4096
-    a = torch.sort(keys[:pairs * L].view(pairs, L), dim=1).values.reshape(-1)
-    b = torch.sort(keys[pairs * L:2 * pairs * L].view(pairs, L), dim=1).values.reshape(-1)
-    offs = torch.arange(0, pairs * L + 1, L, dtype=torch.int64, device=dev)
-    c = torch.empty(2 * pairs * L, dtype=torch.int32, device=dev)
-    om.merge_batched(a, offs, b, offs, out=c, stream=stream)
-    ref = torch.sort(torch.cat([a.view(pairs, L), b.view(pairs, L)], dim=1), dim=1).values
-    torch.cuda.synchronize()
-    if not torch.equal(c.view(pairs, 2 * L), ref):
-        log("FAILED: omerge batched merge differs from torch's per-merge sort")
-        sys.exit(1)
-    ms = _time(lambda: om.merge_batched(a, offs, b, offs, out=c, stream=stream), stream)
-    gbs = 2 * c.numel() * 4 / (ms * 1e-3) / 1e9
-    log("%-44s %10.3f %14.4g  (%.0f GB/s, %.1f%% of peak)" % (
-        "batched: 2^15 merges of 4096+4096", ms, c.numel() / (ms * 1e-3), gbs,
-        100 * gbs / HBM_PEAK_GBS))
-    # 2^22 merges of 16 + 16 keys each (the tile path for short merges)
-    pairs, L = 1 << 22, 16
-    a = torch.sort(keys[:pairs * L].view(pairs, L), dim=1).values.reshape(-1)
-    b = torch.sort(keys[pairs * L:2 * pairs * L].view(pairs, L), dim=1).values.reshape(-1)
-    offs = torch.arange(0, pairs * L + 1, L, dtype=torch.int64, device=dev)
-    c = torch.empty(2 * pairs * L, dtype=torch.int32, device=dev)
-    om.merge_batched(a, offs, b, offs, out=c, stream=stream)
-    ref = torch.sort(torch.cat([a.view(pairs, L), b.view(pairs, L)], dim=1), dim=1).values
-    torch.cuda.synchronize()
-    if not torch.equal(c.view(pairs, 2 * L), ref):
-        log("FAILED: omerge batched merge (short merges) differs from torch's per-merge sort")
-        sys.exit(1)
-    ms = _time(lambda: om.merge_batched(a, offs, b, offs, out=c, stream=stream), stream)
-    gbs = 2 * c.numel() * 4 / (ms * 1e-3) / 1e9
-    log("%-44s %10.3f %14.4g  (%.0f GB/s, %.1f%% of peak)" % (
-        "batched: 2^22 merges of 16+16", ms, c.numel() / (ms * 1e-3), gbs,
-        100 * gbs / HBM_PEAK_GBS))
+    for pairs, L, label in ((1 << 15, 4096, "batched: 2^15 merges of 4096+4096"),
+                            (1 << 22, 16, "batched: 2^22 merges of 16+16")):
+        a = torch.sort(keys[:pairs * L].view(pairs, L), dim=1).values.reshape(-1)
+        b = torch.sort(keys[pairs * L:2 * pairs * L].view(pairs, L), dim=1).values.reshape(-1)
+        offs = torch.arange(0, pairs * L + 1, L, dtype=torch.int64, device=dev)
+        c = torch.empty(2 * pairs * L, dtype=torch.int32, device=dev)
+        om.merge_batched(a, offs, b, offs, out=c, stream=stream)
+        ref = torch.sort(torch.cat([a.view(pairs, L), b.view(pairs, L)], dim=1), dim=1).values
+        torch.cuda.synchronize()
+        if not torch.equal(c.view(pairs, 2 * L), ref):
+            log("FAILED: omerge batched merge (%s) differs from torch's per-merge sort" % label)
+            sys.exit(1)
+        ms = _time(lambda: om.merge_batched(a, offs, b, offs, out=c, stream=stream), stream)
+        gbs = 2 * c.numel() * 4 / (ms * 1e-3) / 1e9
+        log("%-44s %10.3f %14.4g  (%.0f GB/s, %.1f%% of peak)" % (
+            label, ms, c.numel() / (ms * 1e-3), gbs, 100 * gbs / HBM_PEAK_GBS))
+        del a, b, offs, c, ref
 
 
 def main():
@@ -318,12 +442,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=None, help="workload name (default: the int32 2^28+2^28 merge)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
-                    help="skip timing the oracle (the output check still runs)")
+                    help="skip the extra oracle runs of the CPU baseline (the output checks "
+                         "still run)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the rows of the other workloads (e.g. under a profiler)")
     ap.add_argument("--ablation", action="store_true",
                     help="also time the global-memory (no LDS) merge kernels at 1..256 outputs "
-                         "per lane, each checked against the oracle, every key order of "
-                         "omerge_merge_keys, the merge sort and the batched merge; tables on "
-                         "stderr")
+                         "per lane on the headline and even/odd workloads, each checked against "
+                         "the oracle, every key order of omerge_merge_keys, the merge sort and "
+                         "the batched merge; tables on stderr")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -336,146 +463,105 @@ def main():
     import torch
 
     import ordered_merge_sorted_amd as om
-    from ordered_merge_sorted_amd.workloads import HEADLINE, WORKLOADS
+    from ordered_merge_sorted_amd.workloads import HEADLINE, ORDER, WORKLOADS
 
     name = args.workload or HEADLINE
+    if name not in WORKLOADS:
+        ap.error("unknown workload %s (one of %s)" % (name, ", ".join(ORDER)))
     w = WORKLOADS[name]
     arch = device_banner(torch)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
 
+    # 1. Inputs and the oracle's reference, before anything runs on the device.
     t0 = time.perf_counter()
     arrs = w.make()
     log("workload %s: m=%d n=%d (%s); generated in %.1f s" % (name, w.m, w.n, w.description,
                                                              time.perf_counter() - t0))
-
-    # Inputs resident in HBM before anything is timed.
-    def to_dev(x):
-        return torch.from_numpy(x.view(np.int32) if x.dtype == np.uint32 else x).to(dev)
-
-    d_arrs = [to_dev(x) for x in arrs]
-    total = w.total
-    seg_len = om.segment_length(w.m, w.n, kv=w.kv)
-    count = om.partition_count(total, seg_len)
-    part = torch.empty(count, dtype=torch.int64, device=dev)
-    if w.kv:
-        out_k = torch.empty(total, dtype=torch.int32, device=dev)
-        out_v = torch.empty(total, dtype=torch.int32, device=dev)
-    else:
-        out = torch.empty(total, dtype=torch.int32, device=dev)
-
-    def launch_partition():
-        om.partition(d_arrs[0], d_arrs[2] if w.kv else d_arrs[1], seg_len, out=part, stream=stream)
-
-    def launch_merge():
-        if w.kv:
-            om.merge_segments_kv(d_arrs[0], d_arrs[1], d_arrs[2], d_arrs[3], part, seg_len,
-                                 out_keys=out_k, out_vals=out_v, stream=stream)
-        else:
-            om.merge_segments_i32(d_arrs[0], d_arrs[1], part, seg_len, out=out, stream=stream)
-
-    # One untimed, checked step (every element against the oracle).
-    launch_partition()
-    launch_merge()
-    torch.cuda.synchronize()
-    # The oracle's run for the check is also the first CPU-baseline run; the
-    # rest of the CPU baseline is timed after the GPU, so that the GPU
-    # timing does not start from a device left idle for seconds.
     want, oracle_s = run_oracle(w, arrs)
-    if args.ablation and not w.kv:
-        ablation(om, d_arrs, want, w, stream)
-    if w.kv:
-        ok = np.array_equal(out_k.cpu().numpy(), want[0]) and \
-            np.array_equal(out_v.cpu().numpy().view(np.uint32), want[1])
-    else:
-        ok = np.array_equal(out.cpu().numpy(), want)
-    if not ok:
+    log("oracle reference: %.2f s on one host core" % oracle_s)
+
+    # 2. Resident inputs; one untimed step checked on every element.
+    r = Resident(om, torch, w, arrs, dev, stream)
+    r.out.fill_(-1)
+    r.step()
+    if not r.matches(want):
         log("FAILED: the merged output differs from the oracle; no number is reported")
         sys.exit(1)
-    log("checked: output bit-exact against the oracle (%d elements)" % total)
-    del want
+    log("checked: output bit-exact against the oracle (%d elements)" % w.total)
     if args.ablation and not w.kv:
-        typed_orders(om, d_arrs, out, w, stream)
-        sort_and_batch(om, stream)
+        ablation(om, torch, r.d[0], r.d[1], want, w, stream)
+        typed_orders(om, torch, r.d, r.out, w, stream)
 
-    # Warmup, then exactly K timed steps.
+    # 3. Bandwidth references and the one-call API over the same bytes; they
+    # run right before the warm-up, so the device is busy from here on.
+    alg_bytes = w.roofline_bytes  # each element read once and written once
+    copy_ms, memcpy_ms = copy_references(om, torch, alg_bytes // 2, dev, stream)
+    onecall_ms = _time(r.one_call, stream, reps=10)
+
+    # 4. Exactly W untimed steps, then exactly K timed steps (the step rate).
     for _ in range(args.warmup):
-        launch_partition()
-        launch_merge()
-    torch.cuda.synchronize()
+        r.step()
+    ms_step, host_ms = r.timed_steps(args.steps)
 
-    # Timed region 1 (the step rate): exactly K steps back to back, bracketed
-    # by device synchronisation, one event pair and the host clock.
-    start_all = torch.cuda.Event(enable_timing=True)
-    stop_all = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_host = time.perf_counter()
-    start_all.record(stream)
-    for k in range(args.steps):
-        launch_partition()
-        launch_merge()
-    stop_all.record(stream)
-    torch.cuda.synchronize()
-    t_host = time.perf_counter() - t_host
-    ms_total = start_all.elapsed_time(stop_all)
-    ms_step = ms_total / args.steps
-
-    # Timed region 2 (the roofline figure): the same K steps with a HIP event
-    # pair around every segment-merge launch on its stream.  (The extra event
-    # packets cost ~1.5% of a step, so region 1 alone gives the step rate.)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for k in range(args.steps):
-        launch_partition()
-        ev[k][0].record(stream)
-        launch_merge()
-        ev[k][1].record(stream)
-    torch.cuda.synchronize()
-    merge_ms = [a.elapsed_time(b) for a, b in ev]
+    # 5. The same K steps with an event pair around each kernel.
+    part_ms, merge_ms = r.kernel_times(args.steps)
     merge_ms_mean = float(np.mean(merge_ms))
+    part_ms_mean = float(np.mean(part_ms))
 
-    bpe = w.bytes_per_element
-    alg_bytes = 2 * total * bpe  # each element read once and written once
-    value = total / (ms_step * 1e-3)
+    # 6. The last timed step's output against the oracle.
+    if not r.matches(want):
+        log("FAILED: the output of the timed steps differs from the oracle; no number is reported")
+        sys.exit(1)
+    del want
+
+    value = w.total / (ms_step * 1e-3)
     step_gbs = alg_bytes / (ms_step * 1e-3) / 1e9
     kern_gbs = alg_bytes / (merge_ms_mean * 1e-3) / 1e9
-
-    # Streaming copy of the same byte count: the bandwidth this device gives.
-    src = torch.empty(total * bpe // 4, dtype=torch.int32, device=dev)
-    src.random_(0, 1 << 30)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        om.stream_copy(src, out=dst, stream=stream)
-    cs, ce = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 10
-    cs.record(stream)
-    for _ in range(reps):
-        om.stream_copy(src, out=dst, stream=stream)
-    ce.record(stream)
-    torch.cuda.synchronize()
-    copy_ms = cs.elapsed_time(ce) / reps
     copy_gbs = alg_bytes / (copy_ms * 1e-3) / 1e9
-    del src, dst
-
-    # One-call API (includes its stream-ordered scratch allocation).
-    if not w.kv:
-        onecall_ms = _time(lambda: om.merge_i32(d_arrs[0], d_arrs[1], out=out, stream=stream),
-                           stream, reps=10)
-    else:
-        onecall_ms = None
-
+    memcpy_gbs = alg_bytes / (memcpy_ms * 1e-3) / 1e9
     log("step: %.4f ms (host clock %.4f ms/step) -> %.4g elements/s, %.1f GB/s (%.1f%% of %.0f)" % (
-        ms_step, t_host * 1e3 / args.steps, value, step_gbs, 100 * step_gbs / HBM_PEAK_GBS, HBM_PEAK_GBS))
-    log("segment merge kernel: %.4f ms mean (min %.4f, max %.4f) -> %.1f GB/s" % (
-        merge_ms_mean, min(merge_ms), max(merge_ms), kern_gbs))
-    log("partition kernel + gaps: %.4f ms per step" % (ms_step - merge_ms_mean))
-    log("stream copy of the same bytes: %.4f ms -> %.1f GB/s; merge step at %.1f%% of it" % (
-        copy_ms, copy_gbs, 100 * step_gbs / copy_gbs))
-    if onecall_ms is not None:
-        log("merge_i32 one call (with its scratch allocation): %.4f ms" % onecall_ms)
+        ms_step, host_ms, value, step_gbs, 100 * step_gbs / HBM_PEAK_GBS, HBM_PEAK_GBS))
+    log("segment merge kernel: %.4f ms mean (min %.4f, max %.4f) -> %.1f GB/s (%.1f%% of peak)" % (
+        merge_ms_mean, min(merge_ms), max(merge_ms), kern_gbs, 100 * kern_gbs / HBM_PEAK_GBS))
+    log("partition kernel: %.4f ms mean (min %.4f, max %.4f); step - merge kernel: %.4f ms" % (
+        part_ms_mean, min(part_ms), max(part_ms), ms_step - merge_ms_mean))
+    log("streaming copy kernel, same bytes: %.4f ms -> %.1f GB/s; step at %.1f%% of it" % (
+        copy_ms, copy_gbs, 100 * copy_ms / ms_step))
+    log("hipMemcpyAsync device to device, same bytes: %.4f ms -> %.1f GB/s" % (memcpy_ms, memcpy_gbs))
+    log("%s one call (with its scratch allocation): %.4f ms" % (
+        "merge_kv" if w.kv else "merge_i32", onecall_ms))
+    seg_len, count = r.seg_len, r.count
+    del r
+    torch.cuda.empty_cache()
 
+    # 7. The other workloads, one row each.
+    rows = {}
+    if not args.headline_only:
+        log("%-24s %9s %11s %9s %7s %7s %9s %9s  %s" % (
+            "workload", "step ms", "elements/s", "GB/s", "% peak", "% copy", "merge ms",
+            "part. ms", "note"))
+        for other in ORDER:
+            if other == name:
+                continue
+            row = workload_row(om, torch, other, dev, stream, args.warmup, args.steps)
+            rows[other] = row
+            log("%-24s %9.4f %11.4g %9.1f %7.1f %7.1f %9.4f %9.4f  %s" % (
+                other, row["step_ms"], row["elements_per_s"], row["gbps"], row["pct_peak"],
+                row["pct_copy"], row["merge_kernel_ms"], row["partition_kernel_ms"],
+                "cache resident (%.0f MB moved)" % (WORKLOADS[other].roofline_bytes / 1e6)
+                if row["cache_resident"] else "checked bit-exact"))
+            if args.ablation and other == "even_odd_2p21":
+                wo = WORKLOADS[other]
+                ao = wo.make()
+                ro = Resident(om, torch, wo, ao, dev, stream)
+                ablation(om, torch, ro.d[0], ro.d[1], run_oracle(wo, ao)[0], wo, stream)
+                del ro
+    if args.ablation and not w.kv:
+        sort_and_batch(om, torch, stream)
+
+    # 8. The CPU baseline: more runs of the oracle on the headline workload.
     cpu = None
     rates = [] if args.no_cpu_baseline else time_oracle(w, arrs, oracle_s)
     if rates:
@@ -503,11 +589,17 @@ def main():
         "gbps": step_gbs,
         "pct_hbm_peak": 100 * step_gbs / HBM_PEAK_GBS,
         "copy_gbps_same_bytes": copy_gbs,
+        "memcpy_d2d_gbps_same_bytes": memcpy_gbs,
+        "partition_kernel_ms": part_ms_mean,
+        "one_call_ms": onecall_ms,
         "roofline": {"bound": "hbm", "achieved": kern_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": kern_gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "merge_segments_kernel", "kernel_ms": merge_ms_mean,
+                     "scope": "segment merge kernel alone; the whole step is pct_hbm_peak",
+                     "step_frac": step_gbs / HBM_PEAK_GBS,
                      "algorithmic_bytes_per_launch": alg_bytes},
         "cpu_baseline": cpu,
+        "workloads": rows,
     }
     print(json.dumps(line), flush=True)
 
