@@ -61,7 +61,8 @@ enum omerge_status {
     OMERGE_OK = 0,
     OMERGE_INVALID_ARG = 1, /* bad pointer, length, alignment or overlap   */
     OMERGE_OVERFLOW = 2,    /* sizes beyond what int64 / the grid can index */
-    OMERGE_HIP_ERROR = 3    /* a HIP call failed: see omerge_last_hip_error */
+    OMERGE_HIP_ERROR = 3,   /* a HIP call failed: see omerge_last_hip_error */
+    OMERGE_SCRATCH_LIMIT = 4 /* larger than merge_i32_no_alloc's static scratch */
 };
 
 /*
@@ -74,6 +75,25 @@ enum omerge_status {
  */
 int merge_i32(const int32_t *A, int64_t m, const int32_t *B, int64_t n,
               int32_t *C, struct ihipStream_t *stream);
+
+/*
+ * merge_i32_no_alloc -- merge_i32 for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, kernels and result as merge_i32, but it
+ * calls no hipMalloc/hipMallocAsync/hipFree and no allocating library
+ * routine: the partition array lives in a file-scope device array of the
+ * library (2^20 + 1 co-ranks, 8 MiB on each GPU the library runs on, held
+ * until the process ends).
+ *   m + n at most 2^32; larger totals return OMERGE_SCRATCH_LIMIT before
+ *   anything is enqueued.
+ *   Every call on one GPU uses that GPU's one array, so calls that may
+ *   overlap in time on one GPU (other streams, other host threads) RACE and
+ *   must be serialised by the caller; calls in one stream are ordered.
+ *   Nothing in the array needs clearing: each call writes every entry it
+ *   reads.
+ */
+int merge_i32_no_alloc(const int32_t *A, int64_t m, const int32_t *B,
+                       int64_t n, int32_t *C, struct ihipStream_t *stream);
 
 /*
  * merge_kv -- stable merge of (int32 key, uint32 payload) pairs by key.

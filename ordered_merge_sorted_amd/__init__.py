@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     merge_batched,
     merge_i32,
     merge_i32_direct,
+    merge_i32_no_alloc,
     merge_kv,
     merge_pairs,
     merge_segments_i32,

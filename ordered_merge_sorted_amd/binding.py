@@ -17,7 +17,7 @@ import torch
 
 from .build import LIB
 
-OK, INVALID_ARG, OVERFLOW, HIP_ERROR = 0, 1, 2, 3
+OK, INVALID_ARG, OVERFLOW, HIP_ERROR, SCRATCH_LIMIT = 0, 1, 2, 3, 4
 
 
 class OmergeError(RuntimeError):
@@ -47,6 +47,7 @@ def load_library() -> ctypes.CDLL:
     p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     sig = {
         "merge_i32": (i32, [p, i64, p, i64, p, p]),
+        "merge_i32_no_alloc": (i32, [p, i64, p, i64, p, p]),
         "merge_kv": (i32, [p, p, i64, p, p, i64, p, p, p]),
         "omerge_merge_keys": (i32, [p, i64, p, i64, p, i32, p]),
         "omerge_merge_pairs": (i32, [p, p, i64, p, p, i64, p, p, i32, i32, p]),
@@ -130,6 +131,24 @@ def merge_i32(a: torch.Tensor, b: torch.Tensor, out: Optional[torch.Tensor] = No
         rc = lib.merge_i32(_ptr(a), a.numel(), _ptr(b), b.numel(), _ptr(out),
                            _stream(a.device, stream))
     _raise_on(rc, "merge_i32")
+    return out
+
+
+def merge_i32_no_alloc(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor,
+                       stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """merge_i32 through the entry point that allocates no device memory (its
+    scratch is a static array of the library; m + n <= 2^32).  `out` must be
+    given: this call allocates nothing, here either."""
+    _vec(a, "a", (torch.int32,))
+    _vec(b, "b", (torch.int32,), a.device)
+    if out is None:
+        raise ValueError("merge_i32_no_alloc needs an output tensor")
+    out = _out(out, a.numel() + b.numel(), torch.int32, a.device, "out")
+    lib = load_library()
+    with torch.cuda.device(a.device):
+        rc = lib.merge_i32_no_alloc(_ptr(a), a.numel(), _ptr(b), b.numel(), _ptr(out),
+                                    _stream(a.device, stream))
+    _raise_on(rc, "merge_i32_no_alloc")
     return out
 
 

@@ -10,6 +10,16 @@
 #include "omerge.h"
 #include "batch_kernel.hpp"
 
+// Scratch of merge_i32_no_alloc: the partition array of one merge, held in a
+// file-scope device array (each GPU the library runs on has its own copy,
+// for the life of the process).  2^20 + 1 co-ranks cover any total up to
+// 2^32 (segments of at least 4,096 outputs there; smaller totals have at most
+// one segment per resident workgroup).  Host code must not use the name
+// `scratch` as a device address: it is a host-side stand-in.  The device
+// address comes from hipGetSymbolAddress, once per device (no_alloc_scratch).
+#define OMERGE_NO_ALLOC_ENTRIES ((1 << 20) + 1)
+static __device__ __align__(256) int64_t scratch[OMERGE_NO_ALLOC_ENTRIES];
+
 namespace omerge {
 namespace {
 
@@ -171,6 +181,29 @@ int device_slots(int shape, const void* kernel, int* cus, int* wg_per_cu) {
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Device address of the file-scope `scratch` array on the current device,
+// looked up once per device (with that device current) and kept.
+constexpr int64_t kNoAllocMaxTotal = int64_t(1) << 32;
+int64_t* g_scratch_addr[kMaxDevices] = {};
+std::mutex g_scratch_mutex;
+
+int no_alloc_scratch(int64_t** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= kMaxDevices) return OMERGE_INVALID_ARG;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_addr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e);
+        if (p == nullptr) return hip_fail(hipErrorInvalidSymbol);
+        g_scratch_addr[dev] = static_cast<int64_t*>(p);
+    }
+    *out = g_scratch_addr[dev];
+    return OMERGE_OK;
+}
 
 // Segment length: a whole number R of tiles per workgroup.  Two costs pull
 // R in opposite directions.  The partition reads about ten random cache
@@ -515,9 +548,13 @@ struct Path {
         return rc;
     }
 
-    // Whole merge: partition into stream-ordered scratch, then merge.
+    // Whole merge: partition, then merge.  The partition array is
+    // stream-ordered scratch, or, when `fixed` is given, the caller's device
+    // array of `fixed_cap` entries (then nothing is allocated, and a merge
+    // needing more entries returns OMERGE_SCRATCH_LIMIT before any launch).
     static int full(const void* A, const void* Av, int64_t m, const void* B, const void* Bv,
-                    int64_t n, void* C, void* Cv, hipStream_t stream) {
+                    int64_t n, void* C, void* Cv, hipStream_t stream, int64_t* fixed = nullptr,
+                    int64_t fixed_cap = 0) {
         const int64_t total = m + n;
         if (total == 0) return OMERGE_OK;
         // The segment length suits the store path merge() will take.
@@ -526,18 +563,24 @@ struct Path {
         int rc = seg_len(m, n, &sl, reg);
         if (rc != OMERGE_OK) return rc;
         const int64_t count = ceil_div(total, sl) + 1;
-        int64_t* part = nullptr;
-        hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&part),
-                                      static_cast<size_t>(count) * sizeof(int64_t), stream);
-        if (e != hipSuccess) return hip_fail(e);
+        int64_t* part = fixed;
+        if (fixed != nullptr) {
+            if (count > fixed_cap) return OMERGE_SCRATCH_LIMIT;
+        } else {
+            hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&part),
+                                          static_cast<size_t>(count) * sizeof(int64_t), stream);
+            if (e != hipSuccess) return hip_fail(e);
+        }
         const Key* a = static_cast<const Key*>(A);
         const Key* b = static_cast<const Key*>(B);
         rc = partition(a, m, b, n, sl, part, stream);
         if (rc == OMERGE_OK)
             rc = merge(a, static_cast<const uint32_t*>(Av), m, b, static_cast<const uint32_t*>(Bv),
                        n, part, sl, static_cast<Key*>(C), static_cast<uint32_t*>(Cv), stream);
-        e = hipFreeAsync(part, stream);
-        if (rc == OMERGE_OK && e != hipSuccess) rc = hip_fail(e);
+        if (fixed == nullptr) {
+            hipError_t e = hipFreeAsync(part, stream);
+            if (rc == OMERGE_OK && e != hipSuccess) rc = hip_fail(e);
+        }
         return rc;
     }
 };
@@ -638,6 +681,19 @@ int merge_i32(const int32_t* A, int64_t m, const int32_t* B, int64_t n,
     int rc = check_merge_args(A, nullptr, m, B, nullptr, n, C, nullptr, 4, 0);
     if (rc != OMERGE_OK) return rc;
     return PathI32::full(A, nullptr, m, B, nullptr, n, C, nullptr, stream);
+}
+
+int merge_i32_no_alloc(const int32_t* A, int64_t m, const int32_t* B, int64_t n,
+                       int32_t* C, hipStream_t stream) {
+    int rc = check_merge_args(A, nullptr, m, B, nullptr, n, C, nullptr, 4, 0);
+    if (rc != OMERGE_OK) return rc;
+    if (m + n == 0) return OMERGE_OK;
+    if (m + n > kNoAllocMaxTotal) return OMERGE_SCRATCH_LIMIT;
+    int64_t* part = nullptr;
+    rc = no_alloc_scratch(&part);
+    if (rc != OMERGE_OK) return rc;
+    return PathI32::full(A, nullptr, m, B, nullptr, n, C, nullptr, stream, part,
+                         OMERGE_NO_ALLOC_ENTRIES);
 }
 
 int merge_kv(const int32_t* A_keys, const uint32_t* A_vals, int64_t m,
@@ -842,6 +898,7 @@ const char* omerge_status_string(int status) {
         case OMERGE_INVALID_ARG: return "invalid argument";
         case OMERGE_OVERFLOW: return "size overflow";
         case OMERGE_HIP_ERROR: return "HIP error";
+        case OMERGE_SCRATCH_LIMIT: return "exceeds the static scratch of merge_i32_no_alloc";
         default: return "unknown status";
     }
 }

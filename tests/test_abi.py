@@ -272,3 +272,18 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(M, "LIB", str(tmp_path / "absent.so"))
     with pytest.raises(M.OmergeError, match="not built"):
         M.load_library()
+
+
+def test_no_alloc_rejects_totals_beyond_its_scratch():
+    # Checked before anything is enqueued: the fake pointers are never used.
+    lib = om.load_library()
+    f = lib.merge_i32_no_alloc
+    a, b, c = FAKE, FAKE + (1 << 34), FAKE + (1 << 36)
+    assert f(P(a), (1 << 31), P(b), (1 << 31) + 4, P(c), P(0)) == M.SCRATCH_LIMIT
+    assert f(P(a), (1 << 32) + 1, P(0), 0, P(c), P(0)) == M.SCRATCH_LIMIT
+    assert lib.omerge_status_string(M.SCRATCH_LIMIT) == \
+        b"exceeds the static scratch of merge_i32_no_alloc"
+    # the usual argument checks come first
+    assert f(P(0), 5, P(b), 5, P(c), P(0)) == M.INVALID_ARG
+    assert f(P(a), 5, P(a + 8), 5, P(a + 16), P(0)) == M.INVALID_ARG
+    assert f(P(0), 0, P(0), 0, P(0), P(0)) == M.OK
