@@ -288,30 +288,54 @@ def workload_row(om, torch, name, dev, stream, warmup, steps):
     return row
 
 
-def ablation(om, torch, d_a, d_b, want, w, stream):
-    """Global-memory kernels of the pages (no LDS) on the same inputs: one
-    co-rank search then a walk, or two searches per slice, at 1..256 outputs
-    per lane.  Each is checked against the oracle before it is timed."""
-    out = torch.empty(w.total, dtype=torch.int32, device=d_a.device)
-    log("ablation on %s: global-memory merge kernels (no LDS)" % w.name)
-    log("%-28s %10s %10s %8s" % ("kernel", "ms", "GB/s", "% peak"))
+def ablation(om, torch, name, dev, stream, arrs=None, want=None):
+    """The pages' global-memory merge kernels (no LDS) beside the LDS-tiled
+    step, on one workload: one co-rank search then a walk, or two searches
+    per slice, at 1, 4, 16, 64 and 256 outputs per lane.  Every variant is
+    checked against the oracle on every element before it is timed.
+    Launch order (the profiles' tables rely on it): for each of the ten
+    variants one checked launch then `reps` timed ones; then the LDS-tiled
+    step (partition + segment merge) once checked, warmed for 30 ms, and
+    `reps` times timed."""
+    from ordered_merge_sorted_amd.workloads import WORKLOADS
+    w = WORKLOADS[name]
+    if arrs is None:
+        arrs = w.make()
+    if want is None:
+        want = run_oracle(w, arrs)[0]
+    r = Resident(om, torch, w, arrs, dev, stream)
+    d_a, d_b = r.d[0], r.d[1]
+    reps = 5
+    log("ablation on %s: the pages' global-memory merge kernels (no LDS), %d timed launches "
+        "each after one checked launch" % (name, reps))
+    log("%-34s %10s %10s %8s" % ("kernel", "ms", "GB/s", "% peak"))
     for two in (False, True):
         for per in (1, 4, 16, 64, 256):
             def go():
                 om.merge_i32_direct(d_a, d_b, per_thread=per, two_searches=two,
-                                    out=out, stream=stream)
-            out.fill_(-1)
+                                    out=r.out, stream=stream)
+            r.out.fill_(-1)
             go()
-            torch.cuda.synchronize()
-            if not np.array_equal(out.cpu().numpy(), want):
+            if not r.matches(want):
                 log("FAILED: direct kernel per=%d two_searches=%s differs from the oracle" % (per, two))
                 sys.exit(1)
-            ms = _time(go, stream, reps=5, warm=False) if per > 1 or w.total < (1 << 26) else \
-                _time(go, stream, reps=2, warm=False)
+            ms = _time(go, stream, reps=reps, warm=False)
             gbs = w.roofline_bytes / (ms * 1e-3) / 1e9
-            log("%-28s %10.3f %10.1f %8.1f" % ("%s, %d per lane" % ("two searches" if two else "search+walk", per),
+            log("%-34s %10.3f %10.1f %8.1f" % ("%s, %d per lane" % ("two searches" if two else "search+walk", per),
                                                 ms, gbs, 100 * gbs / HBM_PEAK_GBS))
-    del out
+    r.out.fill_(-1)
+    r.step()
+    if not r.matches(want):
+        log("FAILED: the LDS-tiled step differs from the oracle")
+        sys.exit(1)
+    # (warmed first: after the global-memory kernels' seconds of sparse
+    # traffic the device needs a few steps to reach its streaming rate)
+    ms = _time(r.step, stream, reps=reps)
+    gbs = w.roofline_bytes / (ms * 1e-3) / 1e9
+    log("%-34s %10.3f %10.1f %8.1f" % ("LDS-tiled step (partition + merge)", ms, gbs,
+                                        100 * gbs / HBM_PEAK_GBS))
+    del r
+    torch.cuda.empty_cache()
 
 
 def typed_orders(om, torch, d_arrs, c_ref, w, stream):
@@ -451,6 +475,9 @@ def main():
                          "per lane on the headline and even/odd workloads, each checked against "
                          "the oracle, every key order of omerge_merge_keys, the merge sort and "
                          "the batched merge; tables on stderr")
+    ap.add_argument("--ablation-direct", action="store_true",
+                    help="only the global-memory kernels' tables of --ablation (headline and "
+                         "even/odd workloads), e.g. under a profiler")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -490,8 +517,11 @@ def main():
         log("FAILED: the merged output differs from the oracle; no number is reported")
         sys.exit(1)
     log("checked: output bit-exact against the oracle (%d elements)" % w.total)
+    if (args.ablation or args.ablation_direct) and not w.kv:
+        ablation(om, torch, name, dev, stream, arrs, want)
+        if name != "even_odd_2p21":
+            ablation(om, torch, "even_odd_2p21", dev, stream)
     if args.ablation and not w.kv:
-        ablation(om, torch, r.d[0], r.d[1], want, w, stream)
         typed_orders(om, torch, r.d, r.out, w, stream)
 
     # 3. Bandwidth references and the one-call API over the same bytes; they
@@ -552,12 +582,6 @@ def main():
                 row["pct_copy"], row["merge_kernel_ms"], row["partition_kernel_ms"],
                 "cache resident (%.0f MB moved)" % (WORKLOADS[other].roofline_bytes / 1e6)
                 if row["cache_resident"] else "checked bit-exact"))
-            if args.ablation and other == "even_odd_2p21":
-                wo = WORKLOADS[other]
-                ao = wo.make()
-                ro = Resident(om, torch, wo, ao, dev, stream)
-                ablation(om, torch, ro.d[0], ro.d[1], run_oracle(wo, ao)[0], wo, stream)
-                del ro
     if args.ablation and not w.kv:
         sort_and_batch(om, torch, stream)
 
