@@ -639,7 +639,13 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(
     tb[w].p = p;
 }
 
-template <int THREADS, int ITEMS, int VW, int ORDER>
+// REG = true (keys alone, 16 words of output per lane: 4-byte keys x 16 or
+// 8-byte keys x 8): each lane merges the slice direct_slice_wide gives it,
+// and the tile leaves from registers (store_direct16, the quad transpose of
+// the segment merge), with no LDS stage.  The launcher picks it when C is
+// 16-byte aligned; every tile's output then is (tiles start at multiples of
+// the tile length, a multiple of 4).
+template <int THREADS, int ITEMS, int VW, int ORDER, bool REG = false>
 __global__ __launch_bounds__(THREADS) void merge_tiles_kernel(
     const typename KeyOrder<ORDER>::T* __restrict__ A, const uint32_t* __restrict__ Av,
     const int64_t* __restrict__ a_off, int64_t m, const typename KeyOrder<ORDER>::T* __restrict__ B,
@@ -652,14 +658,19 @@ __global__ __launch_bounds__(THREADS) void merge_tiles_kernel(
     constexpr bool KV = VW > 0;
     constexpr int VORDER = VW == 2 ? kKeyI64 : kKeyI32;
     constexpr int kTile = THREADS * ITEMS;
+    static_assert(!REG || (VW == 0 && KW * ITEMS == 16), "register stores: 16 key words per lane");
+    static_assert(kTile < 65536, "piece bounds are packed in 16 bits");
     // merge starts a tile holds in LDS (at least one candidate per lane)
     constexpr int kCap = kTile / 8 > THREADS ? kTile / 8 : THREADS;
     static_assert(kCap % THREADS == 0, "candidates per lane");
+    constexpr int kWaves = THREADS / 64;
     // LDS: the tile's keys (A part, then B part) as images and its payloads;
     // once every lane holds its outputs in registers, the same words hold
-    // the output stages (padded).  Then piece bounds, one flag per
-    // candidate.  The overlap keeps a workgroup near 25 KB (int32 keys), so
-    // several share a CU while each waits on its loads.
+    // the output stages (padded), unless the tile leaves from registers.
+    // Then the piece bounds, each piece's first A and B index packed in one
+    // word, and one count per wavefront.  A keys-only workgroup of 4-byte
+    // keys needs 18.5 KB with register stores (8 share a CU) and 20.5 KB
+    // with the stage (7).
     // (Each window has 8 spare words: its A and B parts each start at the
     // phase of their source modulo 4 words.)
     constexpr int kWin = 0;
@@ -667,18 +678,17 @@ __global__ __launch_bounds__(THREADS) void merge_tiles_kernel(
     constexpr int kStage = 0;
     constexpr int kVStage = kStage + stage_word(kTile * KW);
     constexpr int kInWords = kVWin + (KV ? kTile * VW + 8 : 0);
-    constexpr int kOutWords = kVStage + (KV ? stage_word(kTile * VW) : 0);
-    constexpr int kPieceA = kInWords > kOutWords ? kInWords : kOutWords;
-    constexpr int kPieceB = kPieceA + kCap + 2;
-    constexpr int kFlag = kPieceB + kCap + 2;
-    __shared__ __attribute__((aligned(16))) int lds[kFlag + kCap];
+    constexpr int kOutWords = REG ? 0 : kVStage + (KV ? stage_word(kTile * VW) : 0);
+    constexpr int kPiece = kInWords > kOutWords ? kInWords : kOutWords;
+    constexpr int kCount = kPiece + kCap + 2;
+    __shared__ __attribute__((aligned(16))) int lds[kCount + kWaves];
     int* const win = lds + kWin;
     int* const vwin = lds + kVWin;
-    int* const stage = lds + kStage;
-    int* const vstage = lds + kVStage;
-    int* const pla = lds + kPieceA;
-    int* const plb = lds + kPieceB;
-    int* const flag = lds + kFlag;
+    // (no stage with register stores: its pointers are not used then)
+    [[maybe_unused]] int* const stage = lds + (REG ? 0 : kStage);
+    [[maybe_unused]] int* const vstage = lds + (REG ? 0 : kVStage);
+    int* const pl = lds + kPiece;
+    int* const cnt = lds + kCount;
 
     const int tid = threadIdx.x;
     const int64_t total = m + n;
@@ -718,40 +728,41 @@ __global__ __launch_bounds__(THREADS) void merge_tiles_kernel(
     }
     // Pieces: piece 0 starts at the tile start; piece q >= 1 at the start of
     // merge p0+q when that start lies inside the tile.  The starts inside the
-    // tile are a prefix of the candidates p0+1, p0+2, ...
+    // tile are a prefix of the candidates p0+1, p0+2, ..., and none is past
+    // the merge that holds the tile's end (the next boundary's merge), so
+    // only those candidates' offsets are read.
+    const int64_t p_end = clamp_to<int64_t>(t1.p, p0, pairs > 0 ? pairs - 1 : 0);
+    // The starts inside form a prefix of the candidates, so counting them
+    // (ballots, then one count per wavefront) gives its length.
+    int inside = 0;
 #pragma unroll
     for (int r = 0; r < kCap / THREADS; ++r) {
         const int q = 1 + tid + r * THREADS;
         const int64_t p = p0 + q;
         bool in = false;
-        if (p < pairs) {
+        if (p <= p_end) {
             const int64_t la = ao(p) - a0, lb = bo(p) - b0;
             in = la >= 0 && lb >= 0 && la + lb < c_len && la <= a_len && lb <= b_len;
-            pla[q] = static_cast<int>(clamp_to<int64_t>(la, 0, a_len));
-            plb[q] = static_cast<int>(clamp_to<int64_t>(lb, 0, b_len));
+            pl[q] = static_cast<int>(clamp_to<int64_t>(la, 0, a_len)) |
+                    (static_cast<int>(clamp_to<int64_t>(lb, 0, b_len)) << 16);
         }
-        flag[q - 1] = in ? 1 : 0;
+        inside += __popcll(__ballot(in));
     }
-    if (tid == 0) {
-        pla[0] = 0;
-        plb[0] = 0;
-    }
+    if ((tid & 63) == 0) cnt[tid >> 6] = inside;
+    if (tid == 0) pl[0] = 0;
     __syncthreads();
-    // Number of pieces: 1 + the length of the prefix of candidates inside.
-    int lo = 0, hi = kCap;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (flag[mid]) lo = mid + 1;
-        else hi = mid;
-    }
+    int lo = 0;
+#pragma unroll
+    for (int wv = 0; wv < kWaves; ++wv) lo += cnt[wv];
+    lo = lo < kCap ? lo : kCap;
     const int npieces = 1 + lo;
     // More merge starts than the LDS holds (only with many empty merges):
     // piece bounds are then read from the offsets in global memory.
-    const bool overflow = lo == kCap && p0 + kCap + 1 < pairs &&
+    const bool overflow = lo == kCap && p0 + kCap + 1 <= p_end &&
                           ao(p0 + kCap + 1) + bo(p0 + kCap + 1) - k0 < c_len;
     int pieces = npieces;
     if (overflow) {
-        int64_t l = p0 + kCap + 1, h = pairs;  // merge starts inside the tile
+        int64_t l = p0 + kCap + 1, h = p_end + 1;  // merge starts inside the tile
         while (l < h) {
             const int64_t mid = (l + h) >> 1;
             if (ao(mid) + bo(mid) - k0 < c_len) l = mid + 1;
@@ -762,18 +773,20 @@ __global__ __launch_bounds__(THREADS) void merge_tiles_kernel(
     auto piece_a = [&](int q) -> int {
         if (q >= pieces) return a_len;
         if (q == 0) return 0;
-        if (!overflow) return pla[q];
+        if (!overflow) return pl[q] & 0xFFFF;
         return static_cast<int>(clamp_to<int64_t>(ao(p0 + q) - a0, 0, a_len));
     };
     auto piece_b = [&](int q) -> int {
         if (q >= pieces) return b_len;
         if (q == 0) return 0;
-        if (!overflow) return plb[q];
+        if (!overflow) return static_cast<int>(static_cast<unsigned>(pl[q]) >> 16);
         return static_cast<int>(clamp_to<int64_t>(bo(p0 + q) - b0, 0, b_len));
     };
 
-    const int o0 = tid * ITEMS;
-    Key x[ITEMS];        // this lane's outputs (order images)
+    // The lane's slice: its first output (slice order of store_direct16
+    // with register stores).
+    const int o0 = (REG ? direct_slice_wide(tid) : tid) * ITEMS;
+    Key x[ITEMS] = {};   // this lane's outputs (order images)
     int vx[ITEMS * (KV ? VW : 1)];  // their payload words
     if (o0 < c_len) {
         // The piece holding output o0: the last piece starting at or before it.
@@ -836,6 +849,23 @@ __global__ __launch_bounds__(THREADS) void merge_tiles_kernel(
                 }
             }
         }
+    }
+    if constexpr (REG) {
+        // From registers: the wavefront's 64 slices as four 1 KB runs.
+        int w[16];
+#pragma unroll
+        for (int t = 0; t < ITEMS; ++t) {
+            if constexpr (KW == 1) {
+                w[t] = static_cast<int>(x[t]);
+            } else {
+                w[2 * t] = low_word(x[t]);
+                w[2 * t + 1] = high_word(x[t]);
+            }
+        }
+        const bool aligned = (word_phase(C + k0) & 3) == 0;
+        store_direct16<ORDER>(reinterpret_cast<int32_t*>(C + k0), (tid >> 6) * 64 * ITEMS * KW,
+                              KW * c_len, aligned, w, tid);
+        return;
     }
     __syncthreads();  // the window is read; its words now hold the stages
     if (o0 < c_len) {

@@ -303,6 +303,7 @@ struct Path {
                              : kMergeWindow;
     static constexpr int kTileItems = tile_items_for(KW, VW);  // tile path
     static constexpr int kBatchTile = kThreads * kTileItems;
+    static constexpr bool kTileReg = VW == 0 && KW * kTileItems == 16;
     static constexpr int kSortItems = sort_items_for(KW, VW);
     static constexpr int kShape = shape_index(KW, VW);
     // Block sort shape: the first sorted runs are kSortTile elements long.
@@ -419,11 +420,21 @@ struct Path {
         e = hipGetLastError();
         int rc = e == hipSuccess ? OMERGE_OK : hip_fail(e);
         if (rc == OMERGE_OK) {
-            hipLaunchKernelGGL((merge_tiles_kernel<kThreads, kTileItems, VW, ORDER>),
-                               dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, stream, a,
-                               static_cast<const uint32_t*>(Av), a_off, m, b,
-                               static_cast<const uint32_t*>(Bv), b_off, n, pairs, tb,
-                               static_cast<Key*>(C), static_cast<uint32_t*>(Cv));
+            // Keys alone with 16 words of output per lane store each tile
+            // from registers when C is 16-byte aligned (every tile's output
+            // then is); the other shapes and outputs go through the stage.
+            if (kTileReg && aligned16(C))
+                hipLaunchKernelGGL((merge_tiles_kernel<kThreads, kTileItems, VW, ORDER, kTileReg>),
+                                   dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, stream,
+                                   a, static_cast<const uint32_t*>(Av), a_off, m, b,
+                                   static_cast<const uint32_t*>(Bv), b_off, n, pairs, tb,
+                                   static_cast<Key*>(C), static_cast<uint32_t*>(Cv));
+            else
+                hipLaunchKernelGGL((merge_tiles_kernel<kThreads, kTileItems, VW, ORDER>),
+                                   dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, stream,
+                                   a, static_cast<const uint32_t*>(Av), a_off, m, b,
+                                   static_cast<const uint32_t*>(Bv), b_off, n, pairs, tb,
+                                   static_cast<Key*>(C), static_cast<uint32_t*>(Cv));
             e = hipGetLastError();
             rc = e == hipSuccess ? OMERGE_OK : hip_fail(e);
         }

@@ -313,6 +313,17 @@ static void tiles_cfg(const void* A, const void* Av, const int64_t* a_off, int64
         omerge::plan_tiles_kernel<4, ORDER>(a, a_off, m, b, b_off, n, pairs, kTile, tiles,
                                             tb.data());
     });
+    // the library's choice: register stores for keys alone with 16 words
+    // per lane into a 16-byte-aligned output
+    constexpr bool kReg = VW == 0 && omerge::KeyOrder<ORDER>::kWords * I == 16;
+    if (kReg && aligned16(C)) {
+        run_grid(tiles, T, [&] {
+            omerge::merge_tiles_kernel<T, I, VW, ORDER, kReg>(
+                a, static_cast<const uint32_t*>(Av), a_off, m, b, static_cast<const uint32_t*>(Bv),
+                b_off, n, pairs, tb.data(), static_cast<Key*>(C), static_cast<uint32_t*>(Cv));
+        });
+        return;
+    }
     run_grid(tiles, T, [&] {
         omerge::merge_tiles_kernel<T, I, VW, ORDER>(
             a, static_cast<const uint32_t*>(Av), a_off, m, b, static_cast<const uint32_t*>(Bv),

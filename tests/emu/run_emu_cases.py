@@ -471,8 +471,11 @@ def group_batched(r, g):
             seg_lens = [int(g.choice([tile, 3 * tile, 100, 4 * int(g.integers(1, 300))])), 0]
             if pairs >= 2000:
                 seg_lens = [0]  # thousands of one-workgroup merges: the tile path only
-            for seg_len in seg_lens:
-                Ck = np.zeros(m + n, dtype=dtype)
+            # the tile path also into an output one element off 16-byte
+            # alignment (the staged store instead of the register store)
+            runs = [(sl, 0) for sl in seg_lens] + ([(0, 1)] if 0 in seg_lens else [])
+            for seg_len, skew in runs:
+                Ck = np.zeros(m + n + skew, dtype=dtype)[skew:]
                 Cv = np.zeros(m + n, dtype=vdt)
                 held = r.lib.emu_batched(variant, order, vw, ptr(A), ptr(Av) if vw else None,
                                          ptr(a_off), m, ptr(B), ptr(Bv) if vw else None,
@@ -482,7 +485,7 @@ def group_batched(r, g):
                 ok = np.array_equal(Ck.view(np.uint8), wk.view(np.uint8))
                 if vw:
                     ok = ok and np.array_equal(Cv, wv)
-                r.check(ok, ("batched", variant, order, vw, pairs, m, n, seg_len))
+                r.check(ok, ("batched", variant, order, vw, pairs, m, n, seg_len, skew))
 
 
 def group_batched_garbage(r, g):
