@@ -488,6 +488,36 @@ def group_batched(r, g):
                 r.check(ok, ("batched", variant, order, vw, pairs, m, n, seg_len, skew))
 
 
+def group_batched_aligned(r, g):
+    """Batches whose merge starts fall on multiples of the segment length
+    (merges of seg_len/2, seg_len and 2*seg_len outputs, some empty): the plan
+    moves those multiples off the starts instead of leaving empty segments."""
+    for variant in (1, 0):
+        tile = r.lib.emu_typed_tile(variant, 0, 0)
+        for seg_len in (tile, 2 * tile):
+            for per in (seg_len // 2, seg_len, 2 * seg_len):
+                pairs = 12
+                la = np.full(pairs, per // 2, dtype=np.int64)
+                lb = np.full(pairs, per - per // 2, dtype=np.int64)
+                la[3] = lb[3] = 0            # an empty merge
+                la[5], lb[5] = per, 0        # a merge with no B
+                a_off = np.concatenate([[0], np.cumsum(la)]).astype(np.int64)
+                b_off = np.concatenate([[0], np.cumsum(lb)]).astype(np.int64)
+                m, n = int(a_off[-1]), int(b_off[-1])
+                A = np.empty(m, dtype=np.int32)
+                B = np.empty(n, dtype=np.int32)
+                for q in range(pairs):
+                    a, b = sorted_pair(g, int(la[q]), int(lb[q]), int(g.choice([3, 1 << 32])))
+                    A[a_off[q]:a_off[q + 1]] = a
+                    B[b_off[q]:b_off[q + 1]] = b
+                wk = oracle.merge_batched(A, a_off, B, b_off)
+                Ck = np.zeros(m + n, dtype=np.int32)
+                held = r.lib.emu_batched(variant, 0, 0, ptr(A), None, ptr(a_off), m, ptr(B), None,
+                                         ptr(b_off), n, pairs, seg_len, ptr(Ck), None)
+                r.check(held == 1, ("batched combo held", variant))
+                r.check(np.array_equal(Ck, wk), ("batched aligned", variant, seg_len, per))
+
+
 def group_batched_garbage(r, g):
     """Offsets that break the contract (negative, past the ends, decreasing,
     huge) and unsorted keys: the plan and merge kernels must still stay inside
@@ -515,7 +545,7 @@ def group_batched_garbage(r, g):
             r.cases += 1
 
 
-GROUPS = {"search": group_search, "batched_garbage": group_batched_garbage, "sort": group_sort, "batched": group_batched, "orders": group_orders, "small": group_small, "direct": group_direct, "skew": group_skew, "blocks": group_blocks,
+GROUPS = {"batched_aligned": group_batched_aligned, "search": group_search, "batched_garbage": group_batched_garbage, "sort": group_sort, "batched": group_batched, "orders": group_orders, "small": group_small, "direct": group_direct, "skew": group_skew, "blocks": group_blocks,
           "production": group_production, "unsorted": group_unsorted}
 
 if __name__ == "__main__":

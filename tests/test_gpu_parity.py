@@ -625,6 +625,30 @@ def test_batched_merges(dtype, desc):
         assert_same(host_bits(gv), as_bits(wv), "batched pair payloads")
 
 
+@pytest.mark.parametrize("per_side", [4096, 8192, 16384])
+def test_batched_merges_on_segment_multiples(per_side):
+    """Batches of equal merges whose starts fall on multiples of the batch
+    segment length (16,384 outputs for int32 keys): the plan moves those
+    multiples off the merge starts instead of leaving empty segments.  Every
+    output, with payloads, against the oracle."""
+    g = np.random.Generator(np.random.PCG64(790 + per_side // 4096))
+    pairs = (1 << 24) // per_side  # 2^25 outputs: large enough for 16,384-output segments
+    a_off = np.arange(pairs + 1, dtype=np.int64) * per_side
+    b_off = a_off.copy()
+    A = np.sort(g.integers(-(1 << 31), 1 << 31, size=(pairs, per_side)), axis=1)
+    B = np.sort(g.integers(-1000, 1000, size=(pairs, per_side)), axis=1)
+    A, B = A.astype(np.int32).reshape(-1), B.astype(np.int32).reshape(-1)
+    say("batched on segment multiples", per_side, pairs)
+    Av, Bv = tags(A.size, B.size)
+    gk, gv = om.merge_batched(dev(A), dev(a_off), dev(B), dev(b_off), dev(Av.view(np.int32)),
+                              dev(Bv.view(np.int32)))
+    wk, wv = oracle.merge_batched(A, a_off, B, b_off, Av, Bv)
+    assert_same(host(gk), wk, "keys")
+    assert_same(host(gv).view(np.uint32), wv, "payloads")
+    got = om.merge_batched(dev(A), dev(a_off), dev(B), dev(b_off))
+    assert_same(host(got), wk, "keys only")
+
+
 def test_batched_invalid_offsets_return():
     """Offsets are device data and are not checked; offsets that break the
     contract (negative, past the ends, decreasing) give an unspecified output
