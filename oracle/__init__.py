@@ -110,6 +110,9 @@ class Oracle:
         lib.oracle_merge_batched.restype = None
         lib.oracle_sort.argtypes = [ctypes.c_int, ctypes.c_int, p, p, i64, p, p, p, p]
         lib.oracle_sort.restype = None
+        lib.oracle_merge_runs.argtypes = [ctypes.c_int, ctypes.c_int, p, p, i64, i64,
+                                          ctypes.c_int, p, p]
+        lib.oracle_merge_runs.restype = None
         self._lib = lib
         self.path = lib_path
 
@@ -204,6 +207,27 @@ class Oracle:
                               _ptr(out_v), _ptr(tmp), _ptr(tmp_v))
         return out.view(_KIND_DTYPE[kind]), out_v.view(vdt)
 
+    def merge_runs(self, keys, run, ways, vals=None, descending: bool = False):
+        """One k-way merge-sort pass: every group of ``ways`` consecutive
+        sorted runs of ``run`` elements becomes one sorted run (ties keep the
+        input order).  Returns the keys, and the payloads moved with them."""
+        kind, K, _ = _typed_pair(keys, keys)
+        if not (1 <= ways <= 64) or run < 1:
+            raise ValueError("ways must be 1..64 and run >= 1")
+        order = kind | (ORDER_DESCENDING if descending else 0)
+        out = np.empty_like(K)
+        if vals is None:
+            self._lib.oracle_merge_runs(order, 0, _ptr(K), None, K.size, int(run), int(ways),
+                                        _ptr(out), None)
+            return out.view(_KIND_DTYPE[kind])
+        vdt, V, _ = _payloads(vals, vals)
+        if V.size != K.size:
+            raise ValueError("key and payload lengths differ")
+        out_v = np.empty_like(V)
+        self._lib.oracle_merge_runs(order, V.dtype.itemsize, _ptr(K), _ptr(V), K.size, int(run),
+                                    int(ways), _ptr(out), _ptr(out_v))
+        return out.view(_KIND_DTYPE[kind]), out_v.view(vdt)
+
     def key_le(self, dtype, x, y, descending: bool = False) -> bool:
         """The order relation itself: does key x come before key y, or tie?"""
         dt = np.dtype(dtype)
@@ -265,6 +289,10 @@ def key_le(dtype, x, y, descending=False):
 
 def merge_batched(A, a_off, B, b_off, A_vals=None, B_vals=None, descending=False):
     return default().merge_batched(A, a_off, B, b_off, A_vals, B_vals, descending)
+
+
+def merge_runs(keys, run, ways, vals=None, descending=False):
+    return default().merge_runs(keys, run, ways, vals, descending)
 
 
 def sort(keys, vals=None, descending=False):

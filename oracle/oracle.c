@@ -54,6 +54,15 @@
  *   oracle_sort        Stable sort by key: bottom-up merge sort with the
  *                      walk above (left run as A).  Its result is the unique
  *                      stable order, which is what it is pinned against.
+ *   oracle_merge_runs  One pass of a k-way merge sort: every group of `ways`
+ *                      consecutive sorted runs of `run` elements (the last
+ *                      group, and its last run, may be short) becomes one
+ *                      sorted run.  At each output the smallest head of the
+ *                      group's runs is taken; among equal heads, the run that
+ *                      comes first in the input.  That is the stable merge of
+ *                      the group (its equal keys keep their input order), the
+ *                      merge-sort stage of the 13-sorting practice page with
+ *                      `ways` runs merged at once instead of two.
  *
  * int32 keys are compared signed.  Lengths are int64, matching the size_t
  * lengths of merge_path.cu.
@@ -373,5 +382,48 @@ void oracle_sort(int order, int val_bytes, const void *in_keys,
         memcpy(out_keys, src_k, (size_t)(n * ks));
         if (vs > 0)
             memcpy(out_vals, src_v, (size_t)(n * vs));
+    }
+}
+
+/* One pass of a k-way merge sort (see the header): each group of `ways`
+ * runs of `run` elements of keys[0, n) (and vals) is merged into the same
+ * positions of out_keys (out_vals) by repeatedly taking the smallest head,
+ * ties to the run that comes first.  out must not overlap the input. */
+void oracle_merge_runs(int order, int val_bytes, const void *keys,
+                       const void *vals, int64_t n, int64_t run, int ways,
+                       void *out_keys, void *out_vals)
+{
+    int ks = key_size(order & 7), vs = val_bytes;
+    const unsigned char *k8 = keys, *v8 = vals;
+    unsigned char *ok = out_keys, *ov = out_vals;
+    int64_t g0, pos[64], end[64];
+    int r;
+    if (ways < 1 || ways > 64 || run < 1)
+        return;
+    for (g0 = 0; g0 < n; g0 += run * ways) {
+        int64_t out = g0;
+        for (r = 0; r < ways; ++r) {
+            int64_t s = g0 + run * r;
+            pos[r] = s < n ? s : n;
+            end[r] = s + run < n ? s + run : n;
+        }
+        for (;;) {
+            int best = -1;
+            for (r = 0; r < ways; ++r) {
+                if (pos[r] >= end[r])
+                    continue;
+                /* a later run takes over only with a strictly smaller key */
+                if (best < 0 || !oracle_key_le(order, key_at(k8, ks, pos[best]),
+                                               key_at(k8, ks, pos[r])))
+                    best = r;
+            }
+            if (best < 0)
+                break;
+            memcpy(ok + ks * out, k8 + ks * pos[best], ks);
+            if (vs > 0)
+                memcpy(ov + vs * out, v8 + vs * pos[best], vs);
+            ++pos[best];
+            ++out;
+        }
     }
 }

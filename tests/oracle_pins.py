@@ -718,6 +718,135 @@ def pin_batched_against_pairs(orc, seed: int = 79, cases: int = 60) -> None:
         assert np.array_equal(orc.merge_batched(A, a_off, B, b_off, descending=desc), Ck)
 
 
+def _sorted_runs(g, dtype, n, run, desc):
+    """Keys of dtype whose consecutive runs of ``run`` are each sorted in the
+    key order (rank), with many ties across runs."""
+    rank = _rank_of(dtype, desc)
+    K = _draw_keys(g, dtype, n)
+    if n and g.random() < 0.5:
+        K = K[g.integers(0, max(1, min(n, 4)), size=n)]  # few distinct keys
+    for s in range(0, n, run):
+        part = K[s:s + run]
+        K[s:s + run] = part[sorted(range(part.size), key=lambda t: rank(part[t]))]
+    return K
+
+
+def pin_merge_runs_brute(orc, seed: int = 83, cases: int = 240) -> None:
+    """A k-way pass equals, group by group, Python's stable sorted() of
+    (rank, input index) over that group of runs: the stable merge, ties to
+    the earlier run and within a run to the earlier element.  Every key type,
+    both orders, 4- and 8-byte payload tags, ragged last group and run."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    dtypes = [np.int32, np.uint32, np.float32, np.int64, np.uint64, np.float64]
+    for c in range(cases):
+        dtype = dtypes[c % len(dtypes)]
+        desc = bool((c // len(dtypes)) & 1)
+        n = int(g.integers(0, 60))
+        run = int(g.integers(1, 9))
+        ways = int(g.integers(1, 9)) if c % 5 else int(g.integers(9, 65))
+        K = _sorted_runs(g, dtype, n, run, desc)
+        rank = _rank_of(dtype, desc)
+        order = []
+        for g0 in range(0, n, run * ways):
+            grp = range(g0, min(n, g0 + run * ways))
+            order += sorted(grp, key=lambda t: rank(K[t]))
+        got = orc.merge_runs(K, run, ways, descending=desc)
+        assert np.array_equal(got.view(np.uint8), K[order].view(np.uint8))
+        for vdt in (np.uint32, np.uint64):
+            V = np.arange(n, dtype=vdt) + vdt(5)
+            gk, gv = orc.merge_runs(K, run, ways, V, descending=desc)
+            assert np.array_equal(gv, V[order])
+            assert np.array_equal(gk.view(np.uint8), K[order].view(np.uint8))
+
+
+def pin_merge_runs_two_way_is_batched(orc, seed: int = 89, cases: int = 40) -> None:
+    """With two ways, a pass is the batch of 2-way merges of adjacent runs
+    (left run as A): the co-rank merge the pages define, merge by merge."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    for c in range(cases):
+        desc = bool(c & 1)
+        n = int(g.integers(1, 400))
+        run = int(g.integers(1, 40))
+        K = _sorted_runs(g, np.int32, n, run, desc)
+        V = np.arange(n, dtype=np.uint32)
+        starts = np.arange(0, n, 2 * run, dtype=np.int64)
+        a_end = np.minimum(starts + run, n)
+        b_end = np.minimum(starts + 2 * run, n)
+        a_idx = np.concatenate([np.arange(s, e) for s, e in zip(starts, a_end)])
+        b_idx = np.concatenate([np.arange(s, e) for s, e in zip(a_end, b_end)] +
+                               [np.zeros(0, dtype=np.int64)])
+        a_off = np.concatenate([[0], np.cumsum(a_end - starts)]).astype(np.int64)
+        b_off = np.concatenate([[0], np.cumsum(b_end - a_end)]).astype(np.int64)
+        wk, wv = orc.merge_batched(K[a_idx], a_off, K[b_idx], b_off, V[a_idx],
+                                   V[b_idx].astype(np.uint32), descending=desc)
+        gk, gv = orc.merge_runs(K, run, 2, V, descending=desc)
+        assert np.array_equal(gk, wk) and np.array_equal(gv, wv)
+
+
+def pin_merge_runs_composes(orc, seed: int = 97, cases: int = 40) -> None:
+    """Stable merges compose: one 4-way pass over runs of r equals a 2-way
+    pass over runs of r and then one over runs of 2r; 8 ways equal 2 x 4 and
+    4 x 2.  Repeated passes from runs of one element give the stable sort."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    for c in range(cases):
+        dtype = [np.int32, np.float64][c & 1]
+        desc = bool(c & 2)
+        n = int(g.integers(1, 500))
+        run = int(g.integers(1, 20))
+        K = _sorted_runs(g, dtype, n, run, desc)
+        V = np.arange(n, dtype=np.uint32)
+        k2, v2 = orc.merge_runs(K, run, 2, V, descending=desc)
+        k22, v22 = orc.merge_runs(k2, 2 * run, 2, v2, descending=desc)
+        k4, v4 = orc.merge_runs(K, run, 4, V, descending=desc)
+        assert np.array_equal(v4, v22) and np.array_equal(k4.view(np.uint8), k22.view(np.uint8))
+        k24, v24 = orc.merge_runs(k2, 2 * run, 4, v2, descending=desc)
+        k42, v42 = orc.merge_runs(k4, 4 * run, 2, v4, descending=desc)
+        k8, v8 = orc.merge_runs(K, run, 8, V, descending=desc)
+        assert np.array_equal(v8, v24) and np.array_equal(v8, v42)
+        # a full sort by passes of 3 ways from runs of one element
+        U = _draw_keys(g, dtype, n)
+        k, v, r = U, V, 1
+        while r < n:
+            k, v = orc.merge_runs(k, r, 3, v, descending=desc)
+            r *= 3
+        sk, sv = orc.sort(U, V, descending=desc)
+        assert np.array_equal(v, sv) and np.array_equal(k.view(np.uint8), sk.view(np.uint8))
+
+
+def pin_merge_runs_special(orc) -> None:
+    """Closed cases: all keys equal leave every element in place; runs that
+    are already in order across their boundaries pass through; runs whose key
+    ranges fall from run to run come out last run first; one way, or a run covering the
+    whole input, is the identity."""
+    n = 37
+    V = np.arange(n, dtype=np.uint32)
+    same = np.full(n, 4, dtype=np.int32)
+    for run, ways in ((1, 2), (3, 4), (5, 7), (1, 64), (36, 2)):
+        k, v = orc.merge_runs(same, run, ways, V)
+        assert np.array_equal(v, V)
+    inc = np.arange(n, dtype=np.int32)
+    for run, ways in ((1, 2), (4, 3), (10, 4)):
+        k, v = orc.merge_runs(inc, run, ways, V)
+        assert np.array_equal(v, V)
+    # 4 runs of 3, each run's keys above the next run's: the group comes out
+    # as run 3, run 2, run 1, run 0
+    K = np.array([9, 10, 11, 6, 7, 8, 3, 4, 5, 0, 1, 2], dtype=np.int32)
+    k, v = orc.merge_runs(K, 3, 4, np.arange(12, dtype=np.uint32))
+    assert k.tolist() == list(range(12))
+    assert v.tolist() == [9, 10, 11, 6, 7, 8, 3, 4, 5, 0, 1, 2]
+    # reversed, each run descends and the largest keys sit in the last run:
+    # in descending order the group again comes out last run first
+    kd, vd = orc.merge_runs(K[::-1].copy(), 3, 4, np.arange(12, dtype=np.uint32),
+                            descending=True)
+    assert kd.tolist() == list(range(11, -1, -1))
+    assert vd.tolist() == [9, 10, 11, 6, 7, 8, 3, 4, 5, 0, 1, 2]
+    R = np.array([5, 1, 4, 2, 3], dtype=np.int32)
+    assert orc.merge_runs(R, 1, 1).tolist() == R.tolist()
+    srt = np.array([1, 3, 5, 2, 4], dtype=np.int32)
+    assert orc.merge_runs(srt, 5, 2).tolist() == srt.tolist()
+    assert orc.merge_runs(np.zeros(0, dtype=np.int32), 4, 4).size == 0
+
+
 ALL_PINS = [
     pin_worked_example,
     pin_equal_element_case,
@@ -743,6 +872,10 @@ ALL_PINS = [
     pin_sort_numpy,
     pin_sort_permutation_of_tiny,
     pin_batched_against_pairs,
+    pin_merge_runs_brute,
+    pin_merge_runs_two_way_is_batched,
+    pin_merge_runs_composes,
+    pin_merge_runs_special,
 ]
 
 

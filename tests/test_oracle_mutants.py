@@ -65,6 +65,16 @@ MUTANTS = {
                                    "    if (i < m && oracle_key_le"),
     "typed_payload_from_b": ("memcpy(cv + vs * k, av + vs * i, vs);",
                              "memcpy(cv + vs * k, (n ? bv : av) + vs * (j < n ? j : 0), vs);"),
+    "runs_ties_to_later_run": ("if (best < 0 || !oracle_key_le(order, key_at(k8, ks, pos[best]),\n                                               key_at(k8, ks, pos[r])))",
+                               "if (best < 0 || oracle_key_le(order, key_at(k8, ks, pos[r]),\n                                              key_at(k8, ks, pos[best])))"),
+    "runs_last_way_dropped": ("        for (r = 0; r < ways; ++r) {\n                if (pos[r] >= end[r])",
+                              "        for (r = 0; r + 1 < ways; ++r) {\n                if (pos[r] >= end[r])"),
+    "runs_group_stride_one_run": ("for (g0 = 0; g0 < n; g0 += run * ways)",
+                                  "for (g0 = 0; g0 < n; g0 += run * (ways > 1 ? ways - 1 : 1))"),
+    "runs_payload_from_next": ("memcpy(ov + vs * out, v8 + vs * pos[best], vs);",
+                               "memcpy(ov + vs * out, v8 + vs * (pos[best] + 1 < n ? pos[best] + 1 : pos[best]), vs);"),
+    "runs_order_ignored": ("!oracle_key_le(order, key_at(k8, ks, pos[best]),",
+                           "!oracle_key_le(order & 7, key_at(k8, ks, pos[best]),"),
 }
 
 RUNNER = r"""
