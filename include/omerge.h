@@ -210,6 +210,28 @@ int omerge_sort(const void *keys_in, const void *vals_in, void *keys_out,
                 struct ihipStream_t *stream);
 
 /*
+ * omerge_merge_runs4 -- one 4-way pass of a merge sort (the merge-sort
+ * stages of the same page, four runs merged at once instead of two; each
+ * group split into pieces by co-rank as in page "Co-rank Function ... and
+ * Basic Parallel Merge Kernel").  keys_in holds sorted runs of `run` keys
+ * (the last run may be short); every group of four consecutive runs (the
+ * last group may hold fewer) is merged into the same positions of
+ * keys_out, stably: equal keys keep their input order, so the earlier run
+ * comes first.  Keys alone.
+ *   keys_in[n]    in:  keys of `order` (as omerge_merge_keys), each run
+ *                      sorted in that order.  NOT checked (device memory):
+ *                      unsorted runs give an unspecified output, but every
+ *                      access stays inside the arrays.
+ *   keys_out[n]   out: disjoint from keys_in.
+ *   run >= 1 (a run of n or more: one run, copied).
+ * Stream-ordered scratch of one 72-byte descriptor per 2,048 keys (1,024
+ * for 8-byte keys).  omerge_sort does not use this pass: on MI355X two 2-way
+ * passes measured faster than one 4-way pass.
+ */
+int omerge_merge_runs4(const void *keys_in, void *keys_out, int64_t n,
+                       int64_t run, int order, struct ihipStream_t *stream);
+
+/*
  * omerge_co_rank -- device co-rank at arbitrary output ranks (page
  * "Co-rank Function ...", section "Binary-Search Implementation": bounds
  * i = min(k,m), i_low = max(0,k-n), j_low = max(0,k-m), half-step rounded up,

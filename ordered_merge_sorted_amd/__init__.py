@@ -23,6 +23,7 @@ from .binding import (  # noqa: F401
     merge_i32_no_alloc,
     merge_kv,
     merge_pairs,
+    merge_runs4,
     merge_segments_i32,
     merge_segments_kv,
     partition,

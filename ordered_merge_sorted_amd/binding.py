@@ -53,6 +53,7 @@ def load_library() -> ctypes.CDLL:
         "omerge_merge_pairs": (i32, [p, p, i64, p, p, i64, p, p, i32, i32, p]),
         "omerge_merge_batched": (i32, [p, p, p, i64, p, p, p, i64, i64, p, p, i32, i32, p]),
         "omerge_sort": (i32, [p, p, p, p, i64, i32, i32, p]),
+        "omerge_merge_runs4": (i32, [p, p, i64, i64, i32, p]),
         "omerge_co_rank": (i32, [p, i64, p, i64, p, i64, p, p]),
         "omerge_segment_length": (i64, [i64, i64, i32]),
         "omerge_partition_count": (i64, [i64, i64]),
@@ -316,6 +317,27 @@ def sort(keys: torch.Tensor, vals: Optional[torch.Tensor] = None, descending: bo
                              vals.element_size() if kv else 0, _stream(dev, stream))
     _raise_on(rc, "omerge_sort")
     return (out, out_vals) if kv else out
+
+
+def merge_runs4(keys: torch.Tensor, run: int, descending: bool = False,
+                out: Optional[torch.Tensor] = None,
+                stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """One 4-way merge-sort pass: keys holds sorted runs of `run` keys; each
+    group of four consecutive runs becomes one sorted run, equal keys in
+    input order (the earlier run first).  Keys alone; out must not overlap
+    keys."""
+    _vec(keys, "keys", tuple(_KEY_KIND))
+    if run < 1:
+        raise ValueError("run must be at least 1")
+    dev = keys.device
+    order = order_code(keys.dtype, descending)
+    out = _out(out, keys.numel(), keys.dtype, dev, "out")
+    lib = load_library()
+    with torch.cuda.device(dev):
+        rc = lib.omerge_merge_runs4(_ptr(keys), _ptr(out), keys.numel(), int(run), order,
+                                    _stream(dev, stream))
+    _raise_on(rc, "omerge_merge_runs4")
+    return out
 
 
 def co_rank(a: torch.Tensor, b: torch.Tensor, k: torch.Tensor,

@@ -5,10 +5,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "omerge.h"
-#include "batch_kernel.hpp"
+#include "multiway_kernel.hpp"
 
 // Scratch of merge_i32_no_alloc: the partition array of one merge, held in a
 // file-scope device array (each GPU the library runs on has its own copy,
@@ -98,6 +99,21 @@ constexpr int kVersion = 100;  // 0.1.0
 #ifndef OMERGE_SHORT_MERGE  // batches averaging fewer outputs per merge use the tile path
 #define OMERGE_SHORT_MERGE 6144
 #endif
+// Sort passes of keys alone merge 4 runs at a time when 1.  Measured slower
+// on MI355X than two 2-way passes (2^28 int32 keys: 7.9 ms against 6.9 ms;
+// the cell kernel does about 1.8 VALU wavefront-instructions per element
+// against 1.24 for two 2-way passes, and both kinds of pass are bound by
+// VALU issue), so the sort keeps 2-way passes; omerge_merge_runs4 runs the
+// 4-way pass on its own.
+#ifndef OMERGE_SORT_MULTIWAY
+#define OMERGE_SORT_MULTIWAY 0
+#endif
+#ifndef OMERGE_MULTIWAY_LANES  // lanes per sample point in the 4-way plan
+#define OMERGE_MULTIWAY_LANES 8
+#endif
+#ifndef OMERGE_MULTIWAY_CELLS  // cells per workgroup of the 4-way cell kernel
+#define OMERGE_MULTIWAY_CELLS 4
+#endif
 #ifndef OMERGE_COPY_UNROLL
 #define OMERGE_COPY_UNROLL 4
 #endif
@@ -111,6 +127,12 @@ struct SegWindow {
 constexpr SegWindow kDescWindow{OMERGE_TILES_PER_DESC_SEG, 2};
 constexpr SegWindow kSortRegWindow{OMERGE_TILES_PER_SORT_SEG, 2};
 constexpr int kCopyUnroll = OMERGE_COPY_UNROLL;  // 16-byte vectors per lane in the copy
+constexpr bool kMultiway = OMERGE_SORT_MULTIWAY != 0;
+constexpr int kMultiwayLanes = OMERGE_MULTIWAY_LANES;
+constexpr int kMultiwayCells = OMERGE_MULTIWAY_CELLS;
+// The 4-way cell kernel: 256 lanes, 64 bytes of keys per lane (16 4-byte or
+// 8 8-byte keys), so a cell holds at most 2 x 2,048 or 2 x 1,024 elements.
+constexpr int multiway_items(int kw) { return kw == 1 ? 16 : 8; }
 
 // Outputs per lane of the segment merge for KW key words and VW payload
 // words per element: 32 bytes of element per lane for 4-byte keys alone
@@ -482,9 +504,50 @@ struct Path {
         return rc;
     }
 
+    // One 4-way pass (multiway_kernel.hpp): every group of four runs of
+    // `run` keys of src[0, N) merges into the same positions of dst.  The
+    // cell array is the caller's (`cells`, at least plan.cells entries) or,
+    // when null, stream-ordered scratch.  Keys alone.
+    static constexpr int kMwItems = multiway_items(KW);
+    static constexpr int64_t kMwQ = int64_t(kThreads) * kMwItems / 2;
+    static int runs4(const Key* src, Key* dst, int64_t N, int64_t run, Cell4* cells,
+                     hipStream_t stream) {
+        static_assert(VW == 0, "the 4-way pass moves keys alone");
+        if (N == 0) return OMERGE_OK;
+        const MultiwayPlan mp = MultiwayPlan::make(N, run, kMwQ);
+        const int64_t entries = mp.points + mp.groups + 1;
+        if (ceil_div(mp.cells, kMultiwayCells) > kMaxGridBlocks ||
+            ceil_div(entries * kMultiwayLanes, 256) > kMaxGridBlocks)
+            return OMERGE_OVERFLOW;
+        Cell4* c = cells;
+        if (c == nullptr) {
+            hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&c),
+                                          static_cast<size_t>(mp.cells) * sizeof(Cell4), stream);
+            if (e != hipSuccess) return hip_fail(e);
+        }
+        hipLaunchKernelGGL((plan_multiway_kernel<kMultiwayLanes, ORDER>),
+                           dim3(static_cast<unsigned>(ceil_div(entries * kMultiwayLanes, 256))),
+                           dim3(256), 0, stream, src, N, run, kMwQ, mp, c);
+        hipError_t e = hipGetLastError();
+        if (e == hipSuccess)
+            hipLaunchKernelGGL((merge_multiway_kernel<kThreads, kMwItems, kMultiwayCells, ORDER>),
+                               dim3(static_cast<unsigned>(ceil_div(mp.cells, kMultiwayCells))),
+                               dim3(kThreads), 0, stream, src, N, c, mp.cells, dst);
+        if (e == hipSuccess) e = hipGetLastError();
+        int rc = e == hipSuccess ? OMERGE_OK : hip_fail(e);
+        if (cells == nullptr) {
+            e = hipFreeAsync(c, stream);
+            if (rc == OMERGE_OK && e != hipSuccess) rc = hip_fail(e);
+        }
+        return rc;
+    }
+
     // Stable merge sort of N elements: block sort into runs of one tile,
     // then passes that merge adjacent runs, ping-ponging between the output
-    // and a scratch copy so that the last pass lands in the output.
+    // and a scratch copy so that the last pass lands in the output.  Keys
+    // alone merge four runs per pass (multiway_kernel.hpp), after one 2-way
+    // pass when the number of doublings is odd; with payloads every pass is
+    // 2-way.
     static int sort(const void* in_k, const void* in_v, void* out_k, void* out_v, int64_t N,
                     hipStream_t stream) {
         if (N == 0) return OMERGE_OK;
@@ -492,6 +555,9 @@ struct Path {
         if (tiles > kMaxGridBlocks) return OMERGE_OVERFLOW;
         int passes = 0;
         for (int64_t run = kSortTile; run < N; run *= 2) ++passes;
+        const bool multi = kMultiway && VW == 0 && passes >= 2;
+        const int two_way = multi ? passes % 2 : passes;
+        const int four_way = multi ? passes / 2 : 0;
         // Pass segments start at multiples of seg_len inside pairs of runs
         // (multiples of the block-sort tile, itself a multiple of 4), and the
         // scratch copy is 256-byte aligned: with 16-byte-aligned outputs
@@ -503,14 +569,23 @@ struct Path {
         int64_t sl = 0;
         int rc = seg_len(N, 0, &sl, reg, reg ? &kSortRegWindow : &kDescWindow);
         if (rc != OMERGE_OK) return rc;
-        int64_t max_segs = 0;
-        for (int64_t run = kSortTile; run < N; run *= 2) {
-            const int64_t per_pair = ceil_div(2 * run, sl);
-            const int64_t full = N / (2 * run), rem = N - full * 2 * run;
-            const int64_t segs = full * per_pair + (rem > 0 ? ceil_div(rem, sl) : 0);
-            max_segs = segs > max_segs ? segs : max_segs;
+        size_t desc_need = 0;
+        {
+            int64_t run = kSortTile;
+            for (int p = 0; p < two_way; ++p, run *= 2) {
+                const int64_t per_pair = ceil_div(2 * run, sl);
+                const int64_t full = N / (2 * run), rem = N - full * 2 * run;
+                const int64_t segs = full * per_pair + (rem > 0 ? ceil_div(rem, sl) : 0);
+                if (segs > kMaxGridBlocks) return OMERGE_OVERFLOW;
+                desc_need = std::max(desc_need, static_cast<size_t>(segs) * sizeof(SegDesc));
+            }
+            for (int p = 0; p < four_way; ++p, run *= 4) {
+                const MultiwayPlan mp = MultiwayPlan::make(N, run, kMwQ);
+                if (mp.cells > kMaxGridBlocks || mp.points + mp.groups + 1 > kMaxGridBlocks)
+                    return OMERGE_OVERFLOW;
+                desc_need = std::max(desc_need, static_cast<size_t>(mp.cells) * sizeof(Cell4));
+            }
         }
-        if (max_segs > kMaxGridBlocks) return OMERGE_OVERFLOW;
         // Scratch: keys, payloads and descriptors in one stream-ordered block,
         // each part 256-byte aligned (64-bit payloads after an odd number of
         // 32-bit keys would otherwise lose their 8-byte alignment).
@@ -520,24 +595,26 @@ struct Path {
         const size_t desc_at = (val_at + val_bytes + 255) & ~size_t(255);
         char* scratch = nullptr;
         if (passes > 0) {
-            hipError_t e = hipMallocAsync(
-                reinterpret_cast<void**>(&scratch),
-                desc_at + static_cast<size_t>(max_segs) * sizeof(SegDesc), stream);
+            hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&scratch), desc_at + desc_need,
+                                          stream);
             if (e != hipSuccess) return hip_fail(e);
         }
         Key* const sk = reinterpret_cast<Key*>(scratch);
         uint32_t* const sv = VW ? reinterpret_cast<uint32_t*>(scratch + val_at) : nullptr;
         SegDesc* const desc = reinterpret_cast<SegDesc*>(scratch + desc_at);
+        Cell4* const cells = reinterpret_cast<Cell4*>(scratch + desc_at);
         Key* bufk[2] = {static_cast<Key*>(out_k), sk};
         uint32_t* bufv[2] = {static_cast<uint32_t*>(out_v), sv};
-        int cur = passes % 2;  // block sort target: the last pass then writes out
+        // block sort target: the last pass then writes out
+        int cur = (two_way + four_way) % 2;
         hipLaunchKernelGGL((block_sort_kernel<kSortThreads, kSortItems, VW, ORDER>),
                            dim3(static_cast<unsigned>(tiles)), dim3(kSortThreads), 0, stream,
                            static_cast<const Key*>(in_k), static_cast<const uint32_t*>(in_v), N,
                            bufk[cur], bufv[cur]);
         hipError_t e = hipGetLastError();
         rc = e == hipSuccess ? OMERGE_OK : hip_fail(e);
-        for (int64_t run = kSortTile; rc == OMERGE_OK && run < N; run *= 2) {
+        int64_t run = kSortTile;
+        for (int p = 0; rc == OMERGE_OK && p < two_way; ++p, run *= 2) {
             const int64_t per_pair = ceil_div(2 * run, sl);
             const int64_t full = N / (2 * run), rem = N - full * 2 * run;
             const int64_t segs = full * per_pair + (rem > 0 ? ceil_div(rem, sl) : 0);
@@ -550,6 +627,10 @@ struct Path {
             if (rc == OMERGE_OK)
                 rc = merge_desc(bufk[cur], bufv[cur], N, bufk[cur], bufv[cur], N, desc, segs, sl,
                                 bufk[1 - cur], bufv[1 - cur], N, reg, stream);
+            cur = 1 - cur;
+        }
+        for (int p = 0; rc == OMERGE_OK && p < four_way; ++p, run *= 4) {
+            if constexpr (VW == 0) rc = runs4(bufk[cur], bufk[1 - cur], N, run, cells, stream);
             cur = 1 - cur;
         }
         if (scratch) {
@@ -797,6 +878,22 @@ int omerge_sort(const void* keys_in, const void* vals_in, void* keys_out, void* 
     return with_shape(order, vb, [&](auto path) {
         return decltype(path)::sort(keys_in, vb ? vals_in : nullptr, keys_out,
                                     vb ? vals_out : nullptr, n, stream);
+    });
+}
+
+int omerge_merge_runs4(const void* keys_in, void* keys_out, int64_t n, int64_t run, int order,
+                       hipStream_t stream) {
+    if (!valid_order(order) || n < 0 || run < 1) return OMERGE_INVALID_ARG;
+    if (n > kMaxTotal) return OMERGE_OVERFLOW;
+    const int kb = key_bytes(order);
+    if (bad_array(keys_in, n, kb) || bad_array(keys_out, n, kb)) return OMERGE_INVALID_ARG;
+    if (overlaps(keys_in, n * kb, keys_out, n * kb)) return OMERGE_INVALID_ARG;
+    if (n == 0) return OMERGE_OK;
+    return with_order<0>(order, [&](auto path) {
+        using P = decltype(path);
+        return P::runs4(static_cast<const typename P::Key*>(keys_in),
+                        static_cast<typename P::Key*>(keys_out), n, run < n ? run : n, nullptr,
+                        stream);
     });
 }
 

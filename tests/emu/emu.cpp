@@ -3,6 +3,7 @@
 // runs each workgroup as THREADS host threads that meet at a std::barrier.
 // Workgroups run one after another.  Exposes extern "C" entry points that the
 // tests call through ctypes.
+#include <algorithm>
 #include <barrier>
 #include <cstdlib>
 #include <functional>
@@ -10,7 +11,7 @@
 #include <vector>
 
 #include "hip/hip_runtime.h"
-#include "batch_kernel.hpp"
+#include "multiway_kernel.hpp"
 
 thread_local EmuDim3 threadIdx;
 thread_local EmuDim3 blockIdx;
@@ -225,17 +226,77 @@ static bool typed_go(int variant, const void* A, const void* Av, int64_t m, cons
     return false;
 }
 
+// One 4-way pass (plan + cell merges, MT lanes and MI keys per lane in the
+// cell kernel) over runs of `run`.  Before the merges it checks what the
+// cell kernel assumes of the plan: every cell written, windows inside their
+// runs and in order, at most q elements of each pair per cell, outputs
+// consecutive from 0 to N.  Returns 1 when they hold (and the merges ran),
+// 0 otherwise.
+//
+// With garbage != 0 the cell array starts as pseudo-random 64-bit words
+// (as unwritten device memory might) and the checks are skipped: for
+// unsorted runs, whose plans may collide or leave cells unwritten, the
+// sanitizers then show that the cell kernel's clamps keep every access in
+// the arrays.
+template <int MT, int MI, int ORDER>
+static int multiway_pass(const typename omerge::KeyOrder<ORDER>::T* src, int64_t N, int64_t run,
+                         typename omerge::KeyOrder<ORDER>::T* dst, uint64_t garbage = 0) {
+    constexpr int64_t q = int64_t(MT) * MI / 2;
+    const omerge::MultiwayPlan mp = omerge::MultiwayPlan::make(N, run, q);
+    std::vector<omerge::Cell4> cells(mp.cells);
+    uint64_t x = garbage;
+    for (auto& c : cells) {
+        int64_t* w = reinterpret_cast<int64_t*>(&c);
+        for (int i = 0; i < 9; ++i) {
+            x = x * 6364136223846793005ull + 1442695040888963407ull;  // LCG (Knuth's MMIX)
+            w[i] = garbage ? static_cast<int64_t>(x) >> (x & 31) : -1;
+        }
+    }
+    const int64_t entries = mp.points + mp.groups + 1;
+    run_grid((entries * 8 + 255) / 256, 256, [&] {
+        omerge::plan_multiway_kernel<8, ORDER>(src, N, run, q, mp, cells.data());
+    });
+    int64_t next = garbage ? N : 0;
+    for (int64_t i = 0; !garbage && i < mp.cells; ++i) {
+        const omerge::Cell4& c = cells[i];
+        const int64_t g = c.s[0] / (4 * run);
+        int64_t n_x = 0, n_y = 0;
+        for (int r = 0; r < 4; ++r) {
+            const int64_t lo = std::min(g * 4 * run + r * run, N);
+            const int64_t hi = std::min(lo + run, N);
+            if (c.s[r] < lo || c.e[r] < c.s[r] || c.e[r] > hi) return 0;
+            (r < 2 ? n_x : n_y) += c.e[r] - c.s[r];
+        }
+        if (c.c0 != next || n_x > q || n_y > q || n_x + n_y == 0) return 0;
+        next += n_x + n_y;
+    }
+    if (next != N) return 0;
+    // three cells per workgroup: the loads of a cell are issued while the
+    // previous one merges, and the last workgroup may hold fewer
+    constexpr int kCells = 3;
+    run_grid((mp.cells + kCells - 1) / kCells, MT, [&] {
+        omerge::merge_multiway_kernel<MT, MI, kCells, ORDER>(src, N, cells.data(), mp.cells, dst);
+    });
+    return 1;
+}
+
 // The merge-sort pipeline of the library (block sort with ST lanes, then
 // plan + merge per pass, ping-pong between out and a scratch copy), for one
 // shape.
-template <int T, int I, int VW, int ORDER, int ST = T, int SI = I>
+template <int T, int I, int VW, int ORDER, int ST = T, int SI = I, int MT = 256, int MI = 16>
 static void sort_cfg(const void* in_k, const void* in_v, int64_t N, void* out_k, void* out_v,
                      int64_t seg_len) {
     using Key = typename omerge::KeyOrder<ORDER>::T;
     constexpr int kTile = ST * SI;  // the block sort's runs
     if (N == 0) return;
-    int passes = 0;
-    for (int64_t run = kTile; run < N; run *= 2) ++passes;
+    int doublings = 0;
+    for (int64_t run = kTile; run < N; run *= 2) ++doublings;
+    // as the library: keys alone merge 4 runs per pass after one 2-way pass
+    // when the doublings are odd
+    const bool multi = VW == 0 && doublings >= 2;
+    const int two_way = multi ? doublings % 2 : doublings;
+    const int four_way = multi ? doublings / 2 : 0;
+    const int passes = two_way + four_way;
     // One scratch block laid out as the library lays out its own: keys, then
     // payloads at the next 256-byte boundary.
     const size_t key_bytes = static_cast<size_t>(N) * sizeof(Key);
@@ -252,7 +313,8 @@ static void sort_cfg(const void* in_k, const void* in_v, int64_t N, void* out_k,
                                                    static_cast<const uint32_t*>(in_v), N,
                                                    bufk[cur], bufv[cur]);
     });
-    for (int64_t run = kTile; run < N; run *= 2) {
+    int64_t run = kTile;
+    for (int pass = 0; pass < two_way; ++pass, run *= 2) {
         const int64_t per_pair = (2 * run + seg_len - 1) / seg_len;
         const int64_t full = N / (2 * run), rem = N - full * 2 * run;
         const int64_t segs = full * per_pair + (rem > 0 ? (rem + seg_len - 1) / seg_len : 0);
@@ -266,6 +328,12 @@ static void sort_cfg(const void* in_k, const void* in_v, int64_t N, void* out_k,
         run_merge<T, I, VW, ORDER, true>(reg, segs, bufk[cur], bufv[cur], N, bufk[cur], bufv[cur],
                                          N, nullptr, seg_len, bufk[1 - cur], bufv[1 - cur],
                                          desc.data(), N);
+        cur = 1 - cur;
+    }
+    for (int pass = 0; pass < four_way; ++pass, run *= 4) {
+        if constexpr (VW == 0) {
+            if (!multiway_pass<MT, MI, ORDER>(bufk[cur], N, run, bufk[1 - cur])) abort();
+        }
         cur = 1 - cur;
     }
 }
@@ -349,7 +417,7 @@ static int sort_go(int variant, const void* in_k, const void* in_v, int64_t N, v
                    void* out_v, int64_t seg_len) {
     if constexpr (emu_sort_has(1, ORDER, VW)) {
         if (variant == 1) {
-            sort_cfg<128, 4, VW, ORDER>(in_k, in_v, N, out_k, out_v, seg_len);
+            sort_cfg<128, 4, VW, ORDER, 128, 4, 64, 4>(in_k, in_v, N, out_k, out_v, seg_len);
             return 1;
         }
     }
@@ -357,8 +425,8 @@ static int sort_go(int variant, const void* in_k, const void* in_v, int64_t N, v
         if (variant == 0) {
             constexpr int kw = omerge::KeyOrder<ORDER>::kWords;
             constexpr int st = production_sort_threads(kw, VW);
-            sort_cfg<256, production_items(kw, VW), VW, ORDER, st,
-                     production_sort_items(kw, VW)>(in_k, in_v, N, out_k, out_v, seg_len);
+            sort_cfg<256, production_items(kw, VW), VW, ORDER, st, production_sort_items(kw, VW),
+                     256, kw == 1 ? 16 : 8>(in_k, in_v, N, out_k, out_v, seg_len);
             return 1;
         }
     }
@@ -547,6 +615,33 @@ int emu_batched(int variant, int order, int vw, const void* A, const void* Av,
     EMU_BATCH(11, 0)
 #undef EMU_BATCH
     return 0;
+}
+
+// One 4-way pass over runs of `run` for a key order (keys alone): variant 0
+// = the library's cell kernel (256 lanes, 64 bytes of keys each), 1 = 64
+// lanes x 4 keys (cells of at most 2 x 128 elements).  Returns 1 when the
+// plan held every invariant the cell kernel assumes and the merges ran, 0
+// when it did not, -1 for an order this library does not hold.
+// garbage != 0: unsorted input allowed, cells start as garbage (see
+// multiway_pass), no plan checks.
+int emu_merge_runs4(int variant, int order, const void* src, int64_t n, int64_t run, void* dst,
+                    uint64_t garbage) {
+#define EMU_RUNS4(o)                                                                           \
+    if (order == o) {                                                                          \
+        using Key = typename omerge::KeyOrder<o>::T;                                           \
+        const Key* s = static_cast<const Key*>(src);                                           \
+        Key* d = static_cast<Key*>(dst);                                                       \
+        if (variant == 1) return multiway_pass<64, 4, o>(s, n, run, d, garbage);               \
+        return multiway_pass<256, omerge::KeyOrder<o>::kWords == 1 ? 16 : 8, o>(s, n, run, d,  \
+                                                                               garbage);       \
+    }
+    EMU_RUNS4(0)
+    EMU_RUNS4(1)
+    EMU_RUNS4(10)
+    EMU_RUNS4(11)
+    EMU_RUNS4(13)
+#undef EMU_RUNS4
+    return -1;
 }
 
 // Tile size (outputs) of a typed shape.

@@ -40,6 +40,8 @@ def load(path):
     lib.emu_typed_tile.restype = i32
     lib.emu_sort_tile.argtypes = [i32, i32, i32]
     lib.emu_sort_tile.restype = i32
+    lib.emu_merge_runs4.argtypes = [i32, i32, p, i64, i64, p, ctypes.c_uint64]
+    lib.emu_merge_runs4.restype = i32
     return lib
 
 
@@ -49,6 +51,16 @@ def placed(x, off):
     buf = np.empty(x.size + 32, dtype=x.dtype)
     base = (-(buf.ctypes.data // 4)) % 16
     v = buf[base + off: base + off + x.size]
+    v[...] = x
+    return v
+
+
+def placed_bytes(x, off):
+    """Copy of x (any element size) whose data starts `off` bytes past a
+    64-byte boundary (off a multiple of the element size)."""
+    raw = np.empty(x.nbytes + 128, dtype=np.uint8)
+    start = (-raw.ctypes.data) % 64 + off
+    v = raw[start:start + x.nbytes].view(x.dtype)
     v[...] = x
     return v
 
@@ -401,6 +413,9 @@ def unsorted_keys(g, dtype, n, pools):
     return g.integers(info.min, info.max, size=n, dtype=dtype, endpoint=True)
 
 
+MULTIWAY_COMBOS = [(1, 0), (1, 1), (1, 10), (1, 11), (1, 13), (0, 0), (0, 13)]
+
+
 def group_sort(r, g):
     """The merge sort (block sort, then plan + descriptor merges per pass)
     against the oracle's stable sort: sizes around tile multiples, several
@@ -545,7 +560,72 @@ def group_batched_garbage(r, g):
             r.cases += 1
 
 
-GROUPS = {"batched_aligned": group_batched_aligned, "search": group_search, "batched_garbage": group_batched_garbage, "sort": group_sort, "batched": group_batched, "orders": group_orders, "small": group_small, "direct": group_direct, "skew": group_skew, "blocks": group_blocks,
+def sorted_runs(g, dtype, n, run, desc, pools):
+    """n keys of dtype whose consecutive runs of `run` are each sorted in the
+    key order (the oracle's stable sort of each run)."""
+    K = np.ascontiguousarray(unsorted_keys(g, dtype, n, pools))
+    for s0 in range(0, n, run):
+        K[s0:s0 + run] = oracle.sort(K[s0:s0 + run], descending=desc)
+    return K
+
+
+def group_multiway(r, g):
+    """One 4-way pass (plan + cell merges) against the oracle's k-way pass:
+    run lengths below, at and around the cell bound q, several groups and a
+    ragged last group (one to four runs, a short last run), keys with many
+    ties or spread over the type's range, every address phase of the source
+    and the output.  The plan's invariants (windows inside runs, at most q
+    elements of each pair per cell, outputs consecutive) are checked before
+    the merges run."""
+    pools = {np.float32: float_pool(g, np.float32), np.float64: float_pool(g, np.float64)}
+    for variant, order in MULTIWAY_COMBOS:
+        dtype = KIND_DTYPE[order & 7]
+        desc = bool(order & 8)
+        q = 128 if variant else (2048 if np.dtype(dtype).itemsize == 4 else 1024)
+        # long runs put tens of sample points on each side of a group, so
+        # the plan's second phase (searches between searched neighbours)
+        # runs, across side and group boundaries too
+        runs = [1, 3, q // 2, q - 1, q, q + 1, 2 * q, 3 * q + 5, 12 * q + 7, 20 * q] if variant \
+            else [q // 2 + 3, 2 * q, 3 * q - 1, 9 * q + 1]
+        for c, run in enumerate(runs):
+            groups = int(g.integers(1, 4 if variant else 2))
+            extra = int(g.integers(0, 4 * run))  # a ragged last group
+            n = groups * 4 * run + (extra if c % 2 else 0)
+            K = sorted_runs(g, dtype, n, run, desc, pools)
+            size = np.dtype(dtype).itemsize
+            src = placed_bytes(K, 4 * int(g.integers(0, 4)) // size * size)
+            out = placed_bytes(np.zeros_like(K), 4 * int(g.integers(0, 4)) // size * size)
+            held = r.lib.emu_merge_runs4(variant, order, ptr(src), n, run, ptr(out), 0)
+            r.check(held == 1, ("multiway plan invariants", variant, order, n, run))
+            if held == 1:
+                want = oracle.merge_runs(K, run, 4, descending=desc)
+                r.check(np.array_equal(out.view(np.uint8), want.view(np.uint8)),
+                        ("multiway", variant, order, n, run))
+
+
+def group_multiway_garbage(r, g):
+    """The 4-way pass on unsorted runs, with the cell array starting as
+    pseudo-random words: the output is unspecified, but the sanitizers see
+    no access outside the arrays, and the words around the output stay
+    untouched."""
+    for variant, order in MULTIWAY_COMBOS:
+        dtype = KIND_DTYPE[order & 7]
+        size = np.dtype(dtype).itemsize
+        q = 128 if variant else (2048 if size == 4 else 1024)
+        for run in ([1, 5, q - 1, 3 * q + 1, 20 * q] if variant else [q + 1, 9 * q]):
+            n = int(g.integers(1, 4 * run + 1)) + 4 * run * int(g.integers(0, 3))
+            K = np.ascontiguousarray(g.integers(-50, 50, size=n).astype(dtype))
+            pad = 8
+            buf = np.full(n + 2 * pad, 99, dtype=dtype)
+            out = buf[pad:pad + n]
+            held = r.lib.emu_merge_runs4(variant, order, ptr(K), n, run, ptr(out),
+                                         int(g.integers(1, 1 << 62)))
+            r.check(held == 1, ("multiway garbage held", variant, order, n, run))
+            r.check(np.all(buf[:pad] == 99) and np.all(buf[pad + n:] == 99),
+                    ("multiway garbage writes outside", variant, order, n, run))
+
+
+GROUPS = {"multiway_garbage": group_multiway_garbage, "multiway": group_multiway, "batched_aligned": group_batched_aligned, "search": group_search, "batched_garbage": group_batched_garbage, "sort": group_sort, "batched": group_batched, "orders": group_orders, "small": group_small, "direct": group_direct, "skew": group_skew, "blocks": group_blocks,
           "production": group_production, "unsorted": group_unsorted}
 
 if __name__ == "__main__":

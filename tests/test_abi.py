@@ -183,6 +183,16 @@ def test_batched_and_sort_validation():
     assert s(P(a + 4), P(0), P(ck), P(0), 4, 3, 0, P(0)) == M.INVALID_ARG  # 64-bit misaligned
     assert s(P(a), P(0), P(ck), P(0), 0, 0, 0, P(0)) == M.OK
     assert s(P(0), P(0), P(0), P(0), 0, 13, 8, P(0)) == M.OK
+    r4 = lib.omerge_merge_runs4
+    assert r4(P(a), P(ck), -1, 4, 0, P(0)) == M.INVALID_ARG      # negative n
+    assert r4(P(a), P(ck), 4, 0, 0, P(0)) == M.INVALID_ARG       # run < 1
+    assert r4(P(a), P(ck), 4, 4, 6, P(0)) == M.INVALID_ARG       # order
+    assert r4(P(a), P(a + 4), 4, 4, 0, P(0)) == M.INVALID_ARG    # partial overlap
+    assert r4(P(a), P(a), 4, 4, 0, P(0)) == M.INVALID_ARG        # in place
+    assert r4(P(a + 4), P(ck), 4, 4, 3, P(0)) == M.INVALID_ARG   # 64-bit misaligned
+    assert r4(P(0), P(ck), 4, 4, 0, P(0)) == M.INVALID_ARG       # NULL keys
+    assert r4(P(a), P(ck), 0, 4, 0, P(0)) == M.OK
+    assert r4(P(0), P(0), 0, 1, 13, P(0)) == M.OK
 
 
 def test_order_code_of_dtypes():
@@ -250,6 +260,7 @@ def test_sizes_beyond_2p59_overflow():
     assert lib.merge_i32(P(FAKE), 1 << 58, P(FAKE), (1 << 58) + 1, P(FAKE), P(0)) == M.OVERFLOW
     assert lib.omerge_merge_keys(P(FAKE), big, P(FAKE), 0, P(FAKE), 3, P(0)) == M.OVERFLOW
     assert lib.omerge_sort(P(FAKE), P(0), P(FAKE), P(0), big, 3, 0, P(0)) == M.OVERFLOW
+    assert lib.omerge_merge_runs4(P(FAKE), P(FAKE + 16), big, 4, 3, P(0)) == M.OVERFLOW
     assert lib.omerge_co_rank(P(FAKE), 4, P(FAKE), 4, P(FAKE), big, P(FAKE), P(0)) == M.OVERFLOW
     assert lib.omerge_stream_copy(P(FAKE), big, P(FAKE), P(0)) == M.OVERFLOW
     assert lib.omerge_partition_count(big, 4096) == -1

@@ -586,6 +586,116 @@ def test_sort_in_place_and_large():
     assert_same(host(gv).view(np.uint32), wv, "large sort payloads")
 
 
+@pytest.mark.parametrize("dtype,desc", [(np.int32, False), (np.float32, True), (np.int64, True),
+                                        (np.float64, False)],
+                         ids=["int32", "float32-desc", "int64-desc", "float64"])
+def test_sort_keys_many_passes(dtype, desc):
+    """Key-only sorts past the block sort's runs: sizes that leave the last
+    pair of runs short or missing, an even and an odd number of passes, keys
+    over the whole range and keys with four values only.  Output bits
+    against the oracle's stable sort."""
+    needs_torch_dtype(dtype)
+    g = np.random.Generator(np.random.PCG64(780 + np.dtype(dtype).itemsize + 2 * desc))
+    tile = 16384  # the block sort's runs of 4- and 8-byte keys alone
+    for n in (4 * tile, 4 * tile + 1, 5 * tile - 3, 7 * tile + 11, 16 * tile,
+              16 * tile + 3 * tile + 5, 64 * tile + 2 * 16 * tile + 999, (1 << 22) + 77777):
+        for few in (False, True):
+            if few:
+                K = np.array([-7, 0, 3, 12], dtype=dtype)[g.integers(0, 4, size=n)]
+            else:
+                K = np.ascontiguousarray(unsorted_typed(g, dtype, n))
+            say("sort many passes", np.dtype(dtype).name, desc, n, few)
+            got = om.sort(dev_typed(K), descending=desc)
+            assert_same(host_bits(got), as_bits(oracle.sort(K, descending=desc)),
+                        "sorted keys (n=%d, few=%s)" % (n, few))
+
+
+def test_sort_headline_size():
+    """2^28 int32 keys iid uniform over the int32 range (the size the sort
+    is timed at).  Keys alone have one sorted order, so the output is
+    compared bit for bit with numpy's sort of the input (the oracle's merge
+    sort takes minutes at this size)."""
+    n = 1 << 28
+    g = np.random.Generator(np.random.PCG64(791))
+    K = g.integers(-(1 << 31), 1 << 31, size=n, dtype=np.int64).astype(np.int32)
+    say("sort headline size", n)
+    got = om.sort(dev(K))
+    want = np.sort(K)
+    h = host(got)
+    assert np.array_equal(h, want), "2^28 sort differs from the sorted input"
+    del got
+    torch.cuda.empty_cache()
+
+
+def sorted_runs(g, dtype, desc, n, run, few):
+    """n keys whose runs of `run` are each sorted in the key order (the
+    oracle's stable sort per run)."""
+    if few:
+        K = np.array([0, 3, 12, 40], dtype=dtype)[g.integers(0, 4, size=n)]
+    else:
+        K = np.ascontiguousarray(unsorted_typed(g, dtype, n))
+    for s0 in range(0, n, run):
+        K[s0:s0 + run] = oracle.sort(K[s0:s0 + run], descending=desc)
+    return K
+
+
+@pytest.mark.parametrize("dtype,desc", TYPED, ids=TYPED_IDS)
+def test_merge_runs4_against_oracle(dtype, desc):
+    """One 4-way merge pass (omerge_merge_runs4) of every key type and order
+    against the oracle's k-way pass: runs shorter than, equal to and longer
+    than a cell's bound (2,048 keys per pair for 4-byte keys, 1,024 for
+    8-byte), groups of one to four runs at the end, a short last run, keys
+    over the whole range and keys with four values (ties across all four
+    runs and across sample points), and a run of the whole input (a copy)."""
+    needs_torch_dtype(dtype)
+    g = np.random.Generator(np.random.PCG64(800 + TYPED.index((dtype, desc))))
+    q = 2048 if np.dtype(dtype).itemsize == 4 else 1024
+    cases = [(1, 13), (3, 4 * 3 * 5 + 2), (100, 4 * 100 + 250), (q - 1, 4 * (q - 1) * 2 + 1),
+             (q, 4 * q * 3), (q + 1, 4 * (q + 1) + 2 * (q + 1)), (5 * q + 3, 4 * (5 * q + 3) + 7),
+             (40 * q, 4 * 40 * q * 2 + 3 * 40 * q + 1), (1000, 1000), (50, 37)]
+    for c, (run, n) in enumerate(cases):
+        for few in (False, True):
+            K = sorted_runs(g, dtype, desc, n, run, few)
+            say("merge_runs4", np.dtype(dtype).name, desc, n, run, few)
+            got = om.merge_runs4(dev_typed(K), run, descending=desc)
+            want = oracle.merge_runs(K, run, 4, descending=desc)
+            assert_same(host_bits(got), as_bits(want), "4-way pass (n=%d, run=%d)" % (n, run))
+
+
+def test_merge_runs4_headline_size():
+    """A 4-way pass over 2^28 int32 keys in sorted runs of 2^20 (uniform
+    over the int32 range), against the oracle's k-way pass; and the last
+    pass of a 2^28 sort (runs of 2^26, one group)."""
+    n = 1 << 28
+    g = np.random.Generator(np.random.PCG64(811))
+    K = g.integers(-(1 << 31), 1 << 31, size=n, dtype=np.int64).astype(np.int32)
+    for run in (1 << 20, 1 << 26):
+        R = np.sort(K.reshape(-1, run), axis=1).reshape(-1)
+        say("merge_runs4 headline size", n, run)
+        got = host(om.merge_runs4(dev(R), run))
+        assert np.array_equal(got, oracle.merge_runs(R, run, 4)), "run %d" % run
+        del got
+    torch.cuda.empty_cache()
+
+
+def test_merge_runs4_unsorted_input_returns():
+    """Unsorted runs give an unspecified output but every access stays in
+    the arrays (the plan's cells may collide; the cell kernel clamps what it
+    reads): the call returns, and the words around the output are intact."""
+    g = np.random.Generator(np.random.PCG64(812))
+    n = 300001
+    K = g.integers(-1000, 1000, size=n).astype(np.int32)
+    sentinel = -123456789
+    buf = torch.full((n + 64,), sentinel, dtype=torch.int32, device=DEV)
+    out = buf[32:32 + n]
+    for run in (1, 777, 2048, 65536):
+        say("merge_runs4 unsorted", n, run)
+        om.merge_runs4(dev(K), run, out=out)
+        torch.cuda.synchronize()
+        h = host(buf)
+        assert np.all(h[:32] == sentinel) and np.all(h[32 + n:] == sentinel), run
+
+
 def batch_case(g, dtype, desc, pairs, scale):
     la = g.integers(0, scale + 1, size=pairs) * (g.random(pairs) > 0.15)
     lb = g.integers(0, scale + 1, size=pairs) * (g.random(pairs) > 0.15)

@@ -40,7 +40,8 @@ FLAG_SETS = {
 CORE_GROUPS = ["small", "skew", "blocks", "direct", "production", "unsorted", "search"]
 # The typed, sort and batch groups exercise the same load and store helpers
 # as the core groups, so they run in the default build only.
-WIDE_GROUPS = ["orders", "sort", "batched", "batched_aligned", "batched_garbage"]
+WIDE_GROUPS = ["orders", "sort", "batched", "batched_aligned", "batched_garbage", "multiway",
+               "multiway_garbage"]
 JOBS = [(f, g) for f in sorted(FLAG_SETS) for g in CORE_GROUPS] + \
     [("default", g) for g in WIDE_GROUPS]
 POOL = 4  # concurrent children
