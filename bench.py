@@ -410,6 +410,28 @@ def sort_and_batch(om, torch, stream):
     ms_t = _time(lambda: torch.sort(keys, stable=True), stream)
     log("%-44s %10.3f %14.4g" % ("torch.sort(stable=True), same keys", ms_t, n / (ms_t * 1e-3)))
     del out, ref
+    # one 4-way pass against one 2-way pass (a batch of merges of adjacent
+    # runs) over the same keys in sorted runs of 2^20: the 4-way pass does
+    # two doublings of the run length, the 2-way pass one
+    run = 1 << 20
+    runs = torch.sort(keys.view(-1, run), dim=1).values.reshape(-1)
+    o4 = torch.empty_like(runs)
+    om.merge_runs4(runs, run, out=o4, stream=stream)
+    torch.cuda.synchronize()
+    if not torch.equal(o4.view(-1, 4 * run), torch.sort(runs.view(-1, 4 * run), dim=1).values):
+        log("FAILED: omerge 4-way pass differs from torch's per-group sort")
+        sys.exit(1)
+    ms4 = _time(lambda: om.merge_runs4(runs, run, out=o4, stream=stream), stream)
+    half = runs.view(-1, 2, run)
+    a2, b2 = half[:, 0].reshape(-1).contiguous(), half[:, 1].reshape(-1).contiguous()
+    offs = torch.arange(0, a2.numel() + 1, run, dtype=torch.int64, device=dev)
+    ms2 = _time(lambda: om.merge_batched(a2, offs, b2, offs, out=o4, stream=stream), stream)
+    for label, ms_p in (("4-way pass (merge_runs4), runs of 2^20", ms4),
+                        ("2-way pass (batched), runs of 2^20", ms2)):
+        gbs = 2 * n * 4 / (ms_p * 1e-3) / 1e9
+        log("%-44s %10.3f %14.4g  (%.0f GB/s, %.1f%% of peak)" % (
+            label, ms_p, n / (ms_p * 1e-3), gbs, 100 * gbs / HBM_PEAK_GBS))
+    del runs, o4, half, a2, b2, offs
     n2 = 1 << 27
     k2 = keys[:n2].clone()
     v2 = torch.arange(n2, dtype=torch.int32, device=dev)
