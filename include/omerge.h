@@ -224,7 +224,7 @@ int omerge_sort(const void *keys_in, const void *vals_in, void *keys_out,
  *                      access stays inside the arrays.
  *   keys_out[n]   out: disjoint from keys_in.
  *   run >= 1 (a run of n or more: one run, copied).
- * Stream-ordered scratch of one 72-byte descriptor per 2,048 keys (1,024
+ * Stream-ordered scratch of one 72-byte descriptor per 4,096 keys (2,048
  * for 8-byte keys).  omerge_sort does not use this pass: on MI355X two 2-way
  * passes measured faster than one 4-way pass.
  */

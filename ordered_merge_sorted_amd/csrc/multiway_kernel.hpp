@@ -509,6 +509,14 @@ struct MultiwayCfg {
     static constexpr int kVec = ITEMS * KW / 4;      // 16-byte loads / stores per lane
     static constexpr int kLoose = 2 * (4 / KW - 1);  // end elements per window
     static constexpr int kStep = next_pow2(kQ);
+    // Wavefronts per SIMD that the LDS allows (160 KB per CU, 4 SIMDs), at
+    // most 8: the register budget follows from it.
+    static constexpr int kWorkgroupsPerCu = (160 * 1024) / (4 * kLds);
+    static constexpr int kWavesPerSimd =
+        kWorkgroupsPerCu * THREADS / 256 < 8 ? (kWorkgroupsPerCu * THREADS / 256 > 0
+                                                    ? kWorkgroupsPerCu * THREADS / 256
+                                                    : 1)
+                                             : 8;
     static_assert((ITEMS * KW) % 4 == 0, "rows of whole 16-byte vectors");
 };
 
@@ -628,7 +636,9 @@ __device__ __forceinline__ void commit_cell(const CellWindows& g, const CellLoad
 // another; the next cell's loads are issued as soon as the current cell is
 // in LDS and stay in registers while it is merged.
 template <int THREADS, int ITEMS, int CPW, int ORDER>
-__global__ __launch_bounds__(THREADS, THREADS / 32) void merge_multiway_kernel(
+__global__ __launch_bounds__(
+    THREADS, (MultiwayCfg<THREADS, ITEMS, KeyOrder<ORDER>::kWords>::kWavesPerSimd)) void
+merge_multiway_kernel(
     const typename KeyOrder<ORDER>::T* __restrict__ src, int64_t n,
     const Cell4* __restrict__ cells, int64_t ncells,
     typename KeyOrder<ORDER>::T* __restrict__ dst) {

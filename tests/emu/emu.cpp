@@ -426,7 +426,7 @@ static int sort_go(int variant, const void* in_k, const void* in_v, int64_t N, v
             constexpr int kw = omerge::KeyOrder<ORDER>::kWords;
             constexpr int st = production_sort_threads(kw, VW);
             sort_cfg<256, production_items(kw, VW), VW, ORDER, st, production_sort_items(kw, VW),
-                     256, kw == 1 ? 16 : 8>(in_k, in_v, N, out_k, out_v, seg_len);
+                     256, kw == 1 ? 32 : 16>(in_k, in_v, N, out_k, out_v, seg_len);
             return 1;
         }
     }
@@ -618,7 +618,7 @@ int emu_batched(int variant, int order, int vw, const void* A, const void* Av,
 }
 
 // One 4-way pass over runs of `run` for a key order (keys alone): variant 0
-// = the library's cell kernel (256 lanes, 64 bytes of keys each), 1 = 64
+// = the library's cell kernel (256 lanes, 128 bytes of keys each), 1 = 64
 // lanes x 4 keys (cells of at most 2 x 128 elements).  Returns 1 when the
 // plan held every invariant the cell kernel assumes and the merges ran, 0
 // when it did not, -1 for an order this library does not hold.
@@ -632,7 +632,7 @@ int emu_merge_runs4(int variant, int order, const void* src, int64_t n, int64_t 
         const Key* s = static_cast<const Key*>(src);                                           \
         Key* d = static_cast<Key*>(dst);                                                       \
         if (variant == 1) return multiway_pass<64, 4, o>(s, n, run, d, garbage);               \
-        return multiway_pass<256, omerge::KeyOrder<o>::kWords == 1 ? 16 : 8, o>(s, n, run, d,  \
+        return multiway_pass<256, omerge::KeyOrder<o>::kWords == 1 ? 32 : 16, o>(s, n, run, d, \
                                                                                garbage);       \
     }
     EMU_RUNS4(0)

@@ -581,7 +581,7 @@ def group_multiway(r, g):
     for variant, order in MULTIWAY_COMBOS:
         dtype = KIND_DTYPE[order & 7]
         desc = bool(order & 8)
-        q = 128 if variant else (2048 if np.dtype(dtype).itemsize == 4 else 1024)
+        q = 128 if variant else (4096 if np.dtype(dtype).itemsize == 4 else 2048)
         # long runs put tens of sample points on each side of a group, so
         # the plan's second phase (searches between searched neighbours)
         # runs, across side and group boundaries too
@@ -611,7 +611,7 @@ def group_multiway_garbage(r, g):
     for variant, order in MULTIWAY_COMBOS:
         dtype = KIND_DTYPE[order & 7]
         size = np.dtype(dtype).itemsize
-        q = 128 if variant else (2048 if size == 4 else 1024)
+        q = 128 if variant else (4096 if size == 4 else 2048)
         for run in ([1, 5, q - 1, 3 * q + 1, 20 * q] if variant else [q + 1, 9 * q]):
             n = int(g.integers(1, 4 * run + 1)) + 4 * run * int(g.integers(0, 3))
             K = np.ascontiguousarray(g.integers(-50, 50, size=n).astype(dtype))

@@ -643,13 +643,13 @@ def sorted_runs(g, dtype, desc, n, run, few):
 def test_merge_runs4_against_oracle(dtype, desc):
     """One 4-way merge pass (omerge_merge_runs4) of every key type and order
     against the oracle's k-way pass: runs shorter than, equal to and longer
-    than a cell's bound (2,048 keys per pair for 4-byte keys, 1,024 for
+    than a cell's bound (4,096 keys per pair for 4-byte keys, 2,048 for
     8-byte), groups of one to four runs at the end, a short last run, keys
     over the whole range and keys with four values (ties across all four
     runs and across sample points), and a run of the whole input (a copy)."""
     needs_torch_dtype(dtype)
     g = np.random.Generator(np.random.PCG64(800 + TYPED.index((dtype, desc))))
-    q = 2048 if np.dtype(dtype).itemsize == 4 else 1024
+    q = 4096 if np.dtype(dtype).itemsize == 4 else 2048
     cases = [(1, 13), (3, 4 * 3 * 5 + 2), (100, 4 * 100 + 250), (q - 1, 4 * (q - 1) * 2 + 1),
              (q, 4 * q * 3), (q + 1, 4 * (q + 1) + 2 * (q + 1)), (5 * q + 3, 4 * (5 * q + 3) + 7),
              (40 * q, 4 * 40 * q * 2 + 3 * 40 * q + 1), (1000, 1000), (50, 37)]
