@@ -283,7 +283,11 @@ static int multiway_pass(const typename omerge::KeyOrder<ORDER>::T* src, int64_t
 // The merge-sort pipeline of the library (block sort with ST lanes, then
 // plan + merge per pass, ping-pong between out and a scratch copy), for one
 // shape.
-template <int T, int I, int VW, int ORDER, int ST = T, int SI = I, int MT = 256, int MI = 16>
+// MULTI: keys alone merge 4 runs per pass (after one 2-way pass when the
+// doublings are odd), as the library does when built with
+// OMERGE_SORT_MULTIWAY=1; otherwise every pass is 2-way, as its default.
+template <int T, int I, int VW, int ORDER, int ST = T, int SI = I, bool MULTI = false,
+          int MT = 256, int MI = 32>
 static void sort_cfg(const void* in_k, const void* in_v, int64_t N, void* out_k, void* out_v,
                      int64_t seg_len) {
     using Key = typename omerge::KeyOrder<ORDER>::T;
@@ -291,9 +295,7 @@ static void sort_cfg(const void* in_k, const void* in_v, int64_t N, void* out_k,
     if (N == 0) return;
     int doublings = 0;
     for (int64_t run = kTile; run < N; run *= 2) ++doublings;
-    // as the library: keys alone merge 4 runs per pass after one 2-way pass
-    // when the doublings are odd
-    const bool multi = VW == 0 && doublings >= 2;
+    const bool multi = MULTI && VW == 0 && doublings >= 2;
     const int two_way = multi ? doublings % 2 : doublings;
     const int four_way = multi ? doublings / 2 : 0;
     const int passes = two_way + four_way;
@@ -417,7 +419,8 @@ static int sort_go(int variant, const void* in_k, const void* in_v, int64_t N, v
                    void* out_v, int64_t seg_len) {
     if constexpr (emu_sort_has(1, ORDER, VW)) {
         if (variant == 1) {
-            sort_cfg<128, 4, VW, ORDER, 128, 4, 64, 4>(in_k, in_v, N, out_k, out_v, seg_len);
+            // small shapes run the 4-way passes (the library's build option)
+            sort_cfg<128, 4, VW, ORDER, 128, 4, true, 64, 4>(in_k, in_v, N, out_k, out_v, seg_len);
             return 1;
         }
     }
@@ -425,8 +428,9 @@ static int sort_go(int variant, const void* in_k, const void* in_v, int64_t N, v
         if (variant == 0) {
             constexpr int kw = omerge::KeyOrder<ORDER>::kWords;
             constexpr int st = production_sort_threads(kw, VW);
+            // the library's shapes and passes (2-way)
             sort_cfg<256, production_items(kw, VW), VW, ORDER, st, production_sort_items(kw, VW),
-                     256, kw == 1 ? 32 : 16>(in_k, in_v, N, out_k, out_v, seg_len);
+                     false>(in_k, in_v, N, out_k, out_v, seg_len);
             return 1;
         }
     }

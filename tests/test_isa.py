@@ -71,6 +71,21 @@ def test_no_merge_kernel_spills(asm):
     assert not spilled, spilled
 
 
+def test_multiway_kernels_without_scratch(asm):
+    """The 4-way pass's plan and cell kernels, every key order, run without
+    scratch.  Selects over a small array of words once compiled to a
+    dynamically indexed private load (scratch memory) in every candidate
+    read; the cell kernel's candidates are 16-byte LDS reads."""
+    names = sorted(set(re.findall(r"^(_ZN6omerge2\d(?:plan|merge)_multiway_kernel\w*):", asm,
+                                  re.M)))
+    assert len(names) >= 24, len(names)
+    scratch = [n for n in names if body(asm, n)[1] != 0]
+    assert not scratch, scratch
+    code, _ = body(asm, "_ZN6omerge21merge_multiway_kernelILi256ELi32ELi4ELi0EE")
+    for ins in ("global_load_dwordx4", "global_store_dwordx4", "ds_read_b128", "ds_write_b128"):
+        assert ins in code, ins
+
+
 def test_block_sort_lane_exchanges(asm):
     code, scratch = body(asm, BLOCK_SORT)
     assert "v_mov_b32_dpp" in code
