@@ -500,6 +500,10 @@ def main():
     ap.add_argument("--ablation-direct", action="store_true",
                     help="only the global-memory kernels' tables of --ablation (headline and "
                          "even/odd workloads), e.g. under a profiler")
+    ap.add_argument("--ablation-sort", action="store_true",
+                    help="only the merge sort, 4-way pass and batched merge rows of --ablation, "
+                         "each checked first (tables on stderr, no JSON line), e.g. under a "
+                         "profiler")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -522,6 +526,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
+    if args.ablation_sort:
+        sort_and_batch(om, torch, stream)
+        return
 
     # 1. Inputs and the oracle's reference, before anything runs on the device.
     t0 = time.perf_counter()

@@ -100,11 +100,11 @@ constexpr int kVersion = 100;  // 0.1.0
 #define OMERGE_SHORT_MERGE 6144
 #endif
 // Sort passes of keys alone merge 4 runs at a time when 1.  Measured slower
-// on MI355X than two 2-way passes (2^28 int32 keys: 7.9 ms against 6.9 ms;
-// the cell kernel does about 1.8 VALU wavefront-instructions per element
-// against 1.24 for two 2-way passes, and both kinds of pass are bound by
-// VALU issue), so the sort keeps 2-way passes; omerge_merge_runs4 runs the
-// 4-way pass on its own.
+// on MI355X than two 2-way passes (a 4-way pass over 2^28 int32 keys takes
+// about 0.99 ms, two 2-way passes 0.74 ms): the cell kernel issues 1.54 VALU
+// wavefront-instructions per element, against 0.56 per 2-way pass, which
+// hides its VALU work under its HBM time.  So the sort keeps 2-way passes;
+// omerge_merge_runs4 runs the 4-way pass on its own.
 #ifndef OMERGE_SORT_MULTIWAY
 #define OMERGE_SORT_MULTIWAY 0
 #endif
