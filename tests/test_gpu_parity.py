@@ -627,6 +627,28 @@ def test_sort_headline_size():
     torch.cuda.empty_cache()
 
 
+def test_stream_copy_reference():
+    """The bandwidth reference copy (omerge_stream_copy): every size class
+    (empty, a few words, one 64-lane workgroup and its neighbours, a ragged
+    large size) and every source and destination word phase, so both the
+    16-byte path (same phase) and the word path (different phases) run;
+    the copy must equal the source and leave the words around it alone."""
+    g = np.random.Generator(np.random.PCG64(830))
+    sentinel = -55555
+    for n in (0, 1, 3, 5, 255, 256, 257, 1000003, (1 << 20) + 7):
+        src_h = g.integers(-(1 << 31), 1 << 31, size=n + 8, dtype=np.int64).astype(np.int32)
+        src_d = dev(src_h)
+        for so in range(4):
+            for do in range(4):
+                buf = torch.full((n + 16,), sentinel, dtype=torch.int32, device=DEV)
+                out = buf[4 + do:4 + do + n]
+                om.stream_copy(src_d[so:so + n], out=out)
+                h = host(buf)
+                assert np.array_equal(h[4 + do:4 + do + n], src_h[so:so + n]), (n, so, do)
+                assert np.all(h[:4 + do] == sentinel) and np.all(h[4 + do + n:] == sentinel), \
+                    (n, so, do)
+
+
 def sorted_runs(g, dtype, desc, n, run, few):
     """n keys whose runs of `run` are each sorted in the key order (the
     oracle's stable sort per run)."""
