@@ -189,7 +189,14 @@ __device__ __forceinline__ void bitonic_sort(T (&x)[N], int (&pos)[N]) {
 #pragma unroll
             for (int i = 0; i < N; ++i) {
                 const int l = i ^ j;
-                if (l > i) {
+                if (l > i && !POS) {
+                    // Keys alone: the compare-exchange as min and max (the
+                    // swap form below compiles to a compare and two selects).
+                    const T lo = min(x[i], x[l]), hi = max(x[i], x[l]);
+                    const bool up = (i & kk) == 0;
+                    x[i] = up ? lo : hi;
+                    x[l] = up ? hi : lo;
+                } else if (l > i) {
                     const bool up = (i & kk) == 0;
                     const bool gt = POS ? (x[i] > x[l] || (x[i] == x[l] && pos[i] > pos[l]))
                                         : x[i] > x[l];
@@ -254,7 +261,9 @@ __device__ __forceinline__ void get_row(const int* buf, int tid, T (&x)[ITEMS]) 
 }
 
 // A 32-bit word as held by lane (lane ^ MASK) of the wavefront; every lane
-// takes part.  The route depends on the mask: DPP inside each row of 16
+// takes part (every DPP pattern below reads a lane of the same row, so all
+// lanes are written and the old value of the destination never shows; the
+// mov form leaves it undefined, which spares a copy of x per exchange).  The route depends on the mask: DPP inside each row of 16
 // lanes where a row pattern is the xor (quad_perm for 1, 2 and 3; half-row
 // mirror for 7; rotate by 8 for 8; row mirror for 15), ds_swizzle in bit
 // mode (and 0x1f, xor MASK) inside each half of the wavefront for the other
@@ -263,17 +272,17 @@ template <int MASK>
 __device__ __forceinline__ int lane_xor_word(int x) {
     static_assert(MASK > 0 && MASK < 64, "a lane mask of the wavefront");
     if constexpr (MASK == 1) {
-        return __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+        return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
     } else if constexpr (MASK == 2) {
-        return __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+        return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
     } else if constexpr (MASK == 3) {
-        return __builtin_amdgcn_update_dpp(x, x, 0x1B, 0xF, 0xF, false);  // quad_perm 3,2,1,0
+        return __builtin_amdgcn_mov_dpp(x, 0x1B, 0xF, 0xF, false);  // quad_perm 3,2,1,0
     } else if constexpr (MASK == 7) {
-        return __builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+        return __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false);  // row_half_mirror
     } else if constexpr (MASK == 8) {
-        return __builtin_amdgcn_update_dpp(x, x, 0x128, 0xF, 0xF, false);  // row_ror:8
+        return __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);  // row_ror:8
     } else if constexpr (MASK == 15) {
-        return __builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false);  // row_mirror
+        return __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false);  // row_mirror
     } else if constexpr (MASK < 32) {
         return __builtin_amdgcn_ds_swizzle(x, 0x1F | (MASK << 10));
     } else {
@@ -298,12 +307,45 @@ __device__ __forceinline__ bool other_first(T k, int p, T yk, int yp) {
     return POS ? (yk < k || (yk == k && yp < p)) : yk < k;
 }
 
+// The median of three: one v_med3_i32 (the compiler matches this min/max
+// form).  med3(x, y, INT_MIN) is the smaller of x and y, med3(x, y, INT_MAX)
+// the larger, so one instruction keeps either side of a compare-exchange
+// with the side chosen by a per-lane bound instead of a compare and select.
+__device__ __forceinline__ int med3(int a, int b, int c) {
+    return max(min(a, b), min(max(a, b), c));
+}
+
+// The bound that makes med3 keep the smaller value where bit BIT of the
+// lane index is clear and the larger where it is set: INT_MIN or INT_MAX.
+// The compiler sees that the bound takes one of two constants and would
+// split every med3 into min, max and a select again, so the bound passes
+// through an identity DPP move (quad_perm 0,1,2,3), which it cannot see
+// through: one move per stage.
+template <int BIT>
+__device__ __forceinline__ int keep_bound(int lane) {
+    const int b = (lane >> BIT) & 1 ? std::numeric_limits<int>::max()
+                                    : std::numeric_limits<int>::min();
+    return __builtin_amdgcn_mov_dpp(b, 0xE4, 0xF, 0xF, false);
+}
+
+// Keys alone of 32 bits take the med3 form; wider keys and (key, position)
+// pairs compare and select.
+template <bool POS, typename T>
+constexpr bool kMed3Exchange = !POS && sizeof(T) == 4;
+
 // One compare-exchange stage between each lane and lane ^ MASK, element by
 // element: the lower lane keeps the smaller, the upper the larger.  With
 // POS, positions travel with their keys and break ties.
 template <int MASK, bool POS, int ITEMS, typename T>
 __device__ __forceinline__ void lane_stage(T (&x)[ITEMS], int (&pos)[ITEMS], int lane) {
     const bool low = (lane & MASK) == 0;
+    if constexpr (kMed3Exchange<POS, T>) {
+        static_assert((MASK & (MASK - 1)) == 0, "half-cleaners pair lanes one bit apart");
+        const int bound = keep_bound<__builtin_ctz(MASK)>(lane);
+#pragma unroll
+        for (int t = 0; t < ITEMS; ++t) x[t] = med3(x[t], lane_xor<MASK>(x[t]), bound);
+        return;
+    }
 #pragma unroll
     for (int t = 0; t < ITEMS; ++t) {
         const T yk = lane_xor<MASK>(x[t]);
@@ -361,11 +403,17 @@ __device__ __forceinline__ void wave_round(T (&x)[ITEMS], int (&pos)[ITEMS], int
         yk[t] = lane_xor<kMirror>(x[ITEMS - 1 - t]);
         yp[t] = POS ? lane_xor<kMirror>(pos[ITEMS - 1 - t]) : 0;
     }
+    if constexpr (kMed3Exchange<POS, T>) {
+        const int bound = keep_bound<R>(lane);
 #pragma unroll
-    for (int t = 0; t < ITEMS; ++t) {
-        const bool take = first == other_first<POS>(x[t], pos[t], yk[t], yp[t]);
-        x[t] = take ? yk[t] : x[t];
-        if (POS) pos[t] = take ? yp[t] : pos[t];
+        for (int t = 0; t < ITEMS; ++t) x[t] = med3(x[t], yk[t], bound);
+    } else {
+#pragma unroll
+        for (int t = 0; t < ITEMS; ++t) {
+            const bool take = first == other_first<POS>(x[t], pos[t], yk[t], yp[t]);
+            x[t] = take ? yk[t] : x[t];
+            if (POS) pos[t] = take ? yp[t] : pos[t];
+        }
     }
     lane_half_cleaners<(1 << R) / 2, POS>(x, pos, lane);
     bitonic_clean_pos<POS>(x, pos);
@@ -397,6 +445,9 @@ __global__ __launch_bounds__(THREADS) void block_sort_kernel(
     constexpr bool KV = VW > 0;
     constexpr int kTile = THREADS * ITEMS;
     static_assert(ITEMS >= 4 && (ITEMS & (ITEMS - 1)) == 0, "ITEMS: a power of two");
+    // The in-LDS rounds read a lane's ITEMS candidates as consecutive padded
+    // words that cross at most one pad (4 words after every 32).
+    static_assert(KW * ITEMS <= 32, "a lane's row fits in 32 words");
     // LDS: keys and positions, padded as the merge stage (the padding also
     // spreads the runs' starts over the banks; unpadded, the lanes' run
     // reads conflict badly), keys with ITEMS elements of slack for candidate

@@ -40,7 +40,7 @@ constexpr int kVersion = 100;  // 0.1.0
 #define OMERGE_ITEMS_I32 8
 #endif
 #ifndef OMERGE_SORT_ITEMS_I32  // block sort, 4-byte keys alone
-#define OMERGE_SORT_ITEMS_I32 16
+#define OMERGE_SORT_ITEMS_I32 32
 #endif
 #ifndef OMERGE_TILE_ITEMS_I32  // tile path for short merges, 4-byte keys alone
 #define OMERGE_TILE_ITEMS_I32 16
@@ -85,7 +85,7 @@ constexpr int kVersion = 100;  // 0.1.0
 #define OMERGE_ITEMS_MIXED 4
 #endif
 #ifndef OMERGE_SORT_THREADS  // lanes of the block sort for 4-byte keys without payloads
-#define OMERGE_SORT_THREADS 1024
+#define OMERGE_SORT_THREADS 512
 #endif
 #ifndef OMERGE_SORT_THREADS_KV  // lanes of the block sort for 4-byte keys with 4-byte payloads
 #define OMERGE_SORT_THREADS_KV 256
@@ -345,10 +345,12 @@ struct Path {
     // Longer runs save whole merge passes (each one read and one write of
     // the array) at the price of more rounds inside the block sort, and the
     // lane count is capped by what LDS fits.  Measured on MI355X (2^27 keys,
-    // or 2^26 for 12- and 16-byte elements): 1024 lanes for 4-byte keys alone
-    // (2% faster than 256) and 8-byte keys alone (4%); 512 for the 12- and
-    // 16-byte shapes (3-4%); 256 for 4-byte keys with 4-byte payloads, where
-    // 512 and 1024 were slower.
+    // or 2^26 for 12- and 16-byte elements): 512 lanes x 32 keys for 4-byte
+    // keys alone (16,384-key runs like 1024 x 16, but one in-LDS round fewer
+    // and 43% fewer VALU instructions per key; the 2^28 int32 sort took
+    // 6.63-6.64 ms against 6.83-6.85); 1024 lanes for 8-byte keys alone (4%
+    // faster than 256); 512 for the 12- and 16-byte shapes (3-4%); 256 for
+    // 4-byte keys with 4-byte payloads, where 512 and 1024 were slower.
     static constexpr int kSortThreads = (KW == 1 && VW == 0)   ? OMERGE_SORT_THREADS
                                         : (KW == 1 && VW == 1) ? OMERGE_SORT_THREADS_KV
                                         : (KW == 2 && VW == 0) ? OMERGE_SORT_THREADS_WIDE

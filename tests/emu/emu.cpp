@@ -94,6 +94,10 @@ int __builtin_amdgcn_update_dpp(int old, int src, int ctrl, int row_mask, int ba
     return wave_read(src, from);
 }
 
+int __builtin_amdgcn_mov_dpp(int src, int ctrl, int row_mask, int bank_mask, bool bound_ctrl) {
+    return __builtin_amdgcn_update_dpp(0, src, ctrl, row_mask, bank_mask, bound_ctrl);
+}
+
 int __builtin_amdgcn_ds_swizzle(int src, int pattern) {
     if (pattern & 0x8000) abort();  // only bit mode
     const int and_mask = pattern & 31, or_mask = (pattern >> 5) & 31, xor_mask = (pattern >> 10) & 31;
@@ -181,17 +185,18 @@ static void typed_cfg(const void* A, const void* Av, int64_t m, const void* B, c
 constexpr int production_items(int kw, int vw) {
     return kw == 1 && vw == 0 ? 8 : (kw + vw == 2 ? 8 : 4);
 }
-// Outputs per lane of the library's block sort and of its tile path for
-// short merges (16 for 4-byte keys alone, else the segment merge's count).
+// Outputs per lane of the library's block sort (32 for 4-byte keys alone)
+// and of its tile path for short merges (16 for 4-byte keys alone), else the
+// segment merge's count.
 constexpr int production_sort_items(int kw, int vw) {
-    return kw == 1 && vw == 0 ? 16 : production_items(kw, vw);
+    return kw == 1 && vw == 0 ? 32 : production_items(kw, vw);
 }
 constexpr int production_tile_items(int kw, int vw) {
     return kw == 1 && vw == 0 ? 16 : production_items(kw, vw);
 }
 // Lanes of the library's block sort for each shape.
 constexpr int production_sort_threads(int kw, int vw) {
-    return kw == 1 && vw == 0 ? 1024 : kw == 1 && vw == 1 ? 256 : kw == 2 && vw == 0 ? 1024 : 512;
+    return kw == 1 && vw == 0 ? 512 : kw == 1 && vw == 1 ? 256 : kw == 2 && vw == 0 ? 1024 : 512;
 }
 
 // Which (order, payload words, shape) combinations this library holds:

@@ -43,6 +43,7 @@ int __shfl_xor(int var, int mask);
 // mode, as the GCN/CDNA ISA defines them, over the caller's wavefront.
 int __builtin_amdgcn_update_dpp(int old, int src, int ctrl, int row_mask, int bank_mask,
                                 bool bound_ctrl);
+int __builtin_amdgcn_mov_dpp(int src, int ctrl, int row_mask, int bank_mask, bool bound_ctrl);
 int __builtin_amdgcn_ds_swizzle(int src, int pattern);
 inline int __popcll(unsigned long long x) { return __builtin_popcountll(x); }
 template <typename T>

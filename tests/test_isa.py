@@ -9,7 +9,9 @@ on (CPU only: hipcc compiles the library's device code to assembly).
   128-bit rows (ds_read_b128).
 - No instantiation of the segment merge uses scratch memory.
 - The block sort's in-wavefront rounds move lanes' keys with DPP row moves
-  and ds_swizzle, and use no scratch memory.
+  and ds_swizzle, keep one side of each exchange by v_med3_i32 (one per key
+  per cross-lane stage), copy no key before a DPP move, and use no scratch
+  memory.
 """
 import os
 import re
@@ -25,7 +27,7 @@ from ordered_merge_sorted_amd import build  # noqa: E402
 
 MERGE = "_ZN6omerge21merge_segments_kernelILi256ELi8ELi0ELi0ELb0ELb1EE"
 MERGE_STAGED = "_ZN6omerge21merge_segments_kernelILi256ELi8ELi0ELi0ELb0ELb0EE"
-BLOCK_SORT = "_ZN6omerge17block_sort_kernelILi1024ELi16ELi0ELi0EE"
+BLOCK_SORT = "_ZN6omerge17block_sort_kernelILi512ELi32ELi0ELi0EE"
 
 
 @pytest.fixture(scope="module")
@@ -93,3 +95,11 @@ def test_block_sort_lane_exchanges(asm):
         assert pattern in code, pattern
     assert "ds_swizzle_b32" in code
     assert scratch == 0
+    # six rounds of in-wavefront merges hold 1 + 2 + ... + 6 = 21 cross-lane
+    # stages, each one med3 per key (32 per lane)
+    assert len(re.findall(r"\bv_med3_i32\b", code)) == 21 * 32
+    # DPP moves write a fresh register: no v_mov_b32 copy of a key before one
+    lines = [ln.split() for ln in code.splitlines() if ln.strip()]
+    for prev, cur in zip(lines, lines[1:]):
+        if cur[0] == "v_mov_b32_dpp" and prev[0] == "v_mov_b32_e32":
+            assert prev[1].rstrip(",") != cur[1].rstrip(","), (prev, cur)
