@@ -32,12 +32,15 @@
 // cell's index without sorting the points (and the same the other way).
 //
 // One workgroup merges one cell.  It loads the four windows into LDS
-// (16-byte loads of the aligned body of each window), merges R0|R1 and R2|R3
-// there (each lane finds its slice by co-rank and orders its candidates with
-// the min/max network of the block sort), writes X and Y back over the
-// inputs, merges X|Y the same way, and stores the cell through the padded
-// stage with 16-byte stores.  Keys only: equal keys are indistinguishable in
-// a key-only output, so the splits fix every output bit.
+// (16-byte loads of the aligned body of each window, each followed by a
+// block of sentinels: the largest key image), merges R0|R1 and R2|R3 there
+// (each lane finds its slice by co-rank and orders its candidates with the
+// min/max network of the block sort; the sentinels stand in for candidates
+// past a window's end), writes X and Y back as padded rows, each side
+// followed by a sentinel row, merges X|Y the same way, and stores the cell
+// through the padded stage with 16-byte stores.  Keys only: equal keys are
+// indistinguishable in a key-only output, so the splits fix every output
+// bit, and a sentinel equal to a real key changes no output.
 #pragma once
 
 #include "batch_kernel.hpp"
@@ -405,13 +408,15 @@ __global__ __launch_bounds__(256) void plan_multiway_kernel(
     plan_multiway_body<G, ORDER>(src, total, run, q, plan, cells);
 }
 
-// Co-rank of output rank k of the merge of A (la elements at LDS word aw)
-// and B (lb at bw), by binary lifting: the largest x in [max(0, k-lb),
+// Co-rank of output rank k of the merge of A (la elements from LDS word aw)
+// and B (lb from bw), by binary lifting: the largest x in [max(0, k-lb),
 // min(k, la)] with A[x-1] <= B[k-x] (true at the low end; the passing points
-// form a prefix).  STEP is a power of two at least the interval's width.
-// Every read stays inside the LDS array: the A index is clamped at 0, and B
-// is read at most one element past its end.
-template <int STEP, int KW, typename Key>
+// form a prefix).  The steps STEP, STEP/2, ..., 1 reach 2*STEP-1 past the
+// low end, so STEP is at least half the interval's width.  Every read stays
+// inside the arrays: the A index is clamped at 0, and B is read at most one
+// element past its end (a sentinel).  Words are plain LDS words, or pass
+// through the stage padding when PADDED.
+template <int STEP, int KW, bool PADDED, typename Key>
 __device__ __forceinline__ int co_rank_lds(const int* lds, int aw, int la, int bw, int lb, int k) {
     const int lo = k > lb ? k - lb : 0, hi = k < la ? k : la;
     int x = lo;
@@ -419,96 +424,84 @@ __device__ __forceinline__ int co_rank_lds(const int* lds, int aw, int la, int b
     for (int step = STEP; step > 0; step >>= 1) {
         const int p = x + step;
         const int c = p < hi ? p : hi;
-        const Key a = ld_elem<Key>(lds, stage_word(aw + KW * (c > 0 ? c - 1 : 0)));
-        const Key b = ld_elem<Key>(lds, stage_word(bw + KW * (k - c)));
+        const int wa = aw + KW * (c > 0 ? c - 1 : 0), wb = bw + KW * (k - c);
+        const Key a = ld_elem<Key>(lds, PADDED ? stage_word(wa) : wa);
+        const Key b = ld_elem<Key>(lds, PADDED ? stage_word(wb) : wb);
         x = (p <= hi && a <= b) ? p : x;
     }
     return x;
 }
 
-// Word k (0..7, a constant after unrolling) of the 8 words lo|hi.  The
-// shifts below select between such words by value: written over a small
-// array, the compiler turns the select into a dynamically indexed load from
-// private (scratch) memory.
-__device__ __forceinline__ int word8(const int4v& lo, const int4v& hi, int k) {
-    switch (k) {
-        case 0: return lo.x;
-        case 1: return lo.y;
-        case 2: return lo.z;
-        case 3: return lo.w;
-        case 4: return hi.x;
-        case 5: return hi.y;
-        case 6: return hi.z;
-        default: return hi.w;
-    }
-}
-
 // Calls f(t, element t) for the ITEMS elements of KW words that start at
-// LDS word p (before the stage padding).  The words arrive as aligned
-// 16-byte reads (a quad never straddles the padding), two quads at a time,
-// shifted by p's phase mod 4 with selects; at most 4 words past the last
-// element are read.
-template <int ITEMS, int KW, typename Key, typename F>
-__device__ __forceinline__ void for_elems(const int* lds, int p, F f) {
-    constexpr int kChunks = ITEMS * KW / 4;  // 4 words each
-    const int q0 = p & ~3, off = p & 3;
-    const bool by2 = (off & 2) != 0, by1 = (off & 1) != 0;
-    int4v lo = *reinterpret_cast<const int4v*>(lds + stage_word(q0));
+// LDS word w.  In the padded layout (4 spare words after every 32) a window
+// of at most 32 words crosses at most one pad: word j of it sits j words
+// after the window's first, or 4 more once j reaches the pad, so each
+// element is one of two reads (both made, both inside the array), chosen by
+// one compare and one select.  Elements of 8 bytes start on even words and
+// never straddle a pad.
+template <int ITEMS, int KW, bool PADDED, typename Key, typename F>
+__device__ __forceinline__ void for_window(const int* lds, int w, F f) {
+    if constexpr (!PADDED) {
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i) {
-        const int4v hi = *reinterpret_cast<const int4v*>(lds + stage_word(q0 + 4 * (i + 1)));
-        if constexpr (KW == 1) {
-            const int h0 = by2 ? word8(lo, hi, 2) : word8(lo, hi, 0);
-            const int h1 = by2 ? word8(lo, hi, 3) : word8(lo, hi, 1);
-            const int h2 = by2 ? word8(lo, hi, 4) : word8(lo, hi, 2);
-            const int h3 = by2 ? word8(lo, hi, 5) : word8(lo, hi, 3);
-            const int h4 = by2 ? word8(lo, hi, 6) : word8(lo, hi, 4);
-            f(4 * i, static_cast<Key>(by1 ? h1 : h0));
-            f(4 * i + 1, static_cast<Key>(by1 ? h2 : h1));
-            f(4 * i + 2, static_cast<Key>(by1 ? h3 : h2));
-            f(4 * i + 3, static_cast<Key>(by1 ? h4 : h3));
-        } else {  // 8-byte elements start on even words
-            f(2 * i, static_cast<Key>(by2 ? join_words(word8(lo, hi, 2), word8(lo, hi, 3))
-                                          : join_words(word8(lo, hi, 0), word8(lo, hi, 1))));
-            f(2 * i + 1, static_cast<Key>(by2 ? join_words(word8(lo, hi, 4), word8(lo, hi, 5))
-                                              : join_words(word8(lo, hi, 2), word8(lo, hi, 3))));
+        for (int t = 0; t < ITEMS; ++t) f(t, ld_elem<Key>(lds, w + KW * t));
+    } else {
+        static_assert(ITEMS * KW <= 32, "a window crosses at most one pad");
+        const int* const base = lds + stage_word(w);
+        const int ca = 32 - (w & 31);  // words before the next pad
+#pragma unroll
+        for (int t = 0; t < ITEMS; ++t) {
+            const Key before = ld_elem<Key>(base, KW * t);
+            const Key after = ld_elem<Key>(base, KW * t + 4);
+            f(t, KW * t < ca ? before : after);
         }
-        lo = hi;
     }
 }
 
-// The lane's outputs [k0, k1) (k1 - k0 <= ITEMS) of the merge of A and B in
-// LDS, ascending, in x[0, k1-k0): from the co-rank of k0, the ITEMS smallest
-// of the next ITEMS candidates of each side (past a side's end: the largest
-// image) by the min/max network.  Those are the merge's next outputs.
-template <int ITEMS, int STEP, int KW, typename Key>
+// The lane's outputs [k0, k0 + ITEMS) of the merge of A and B in LDS,
+// ascending, in x: from the co-rank of k0, the ITEMS smallest of the next
+// ITEMS candidates of each side, by the min/max network.  Every side is
+// followed by ITEMS sentinels (the largest image), so candidates past a
+// side's end need no masking, and outputs past the merge's end are the
+// largest image.  B's candidates fold into the network's first stage as
+// they arrive, which keeps half the candidates out of registers.
+template <int ITEMS, int STEP, int KW, bool PADDED, typename Key>
 __device__ __forceinline__ void merge_slice_lds(const int* lds, int aw, int la, int bw, int lb,
-                                                int k0, Key kmax, Key (&x)[ITEMS]) {
-    const int sa = co_rank_lds<STEP, KW, Key>(lds, aw, la, bw, lb, k0);
-    const int sb = k0 - sa;
-    const int na = la - sa, nb = lb - sb;  // candidates left on each side
-    for_elems<ITEMS, KW, Key>(lds, aw + KW * sa,
-                              [&](int t, Key e) { x[t] = t < na ? e : kmax; });
-    for_elems<ITEMS, KW, Key>(lds, bw + KW * sb, [&](int t, Key e) {
-        const Key c = t < nb ? e : kmax;
-        x[ITEMS - 1 - t] = min(x[ITEMS - 1 - t], c);
+                                                int k0, Key (&x)[ITEMS]) {
+    const int sa = co_rank_lds<STEP, KW, PADDED, Key>(lds, aw, la, bw, lb, k0);
+    for_window<ITEMS, KW, PADDED, Key>(lds, aw + KW * sa, [&](int t, Key e) { x[t] = e; });
+    for_window<ITEMS, KW, PADDED, Key>(lds, bw + KW * (k0 - sa), [&](int t, Key e) {
+        x[ITEMS - 1 - t] = min(x[ITEMS - 1 - t], e);
     });
     bitonic_clean<ITEMS>(x);
 }
 
-// LDS words of the cell kernel (before the stage padding): the X side
-// (R0, R1 windows, each placed at its global address's word phase mod 4) in
-// [0, Q*KW + 8), the Y side from Q*KW + 8, and slack for candidate reads
-// past the last window (ITEMS elements and one quad).
+// Word j of a row of sentinels: the largest order image, KW words per key.
+template <int KW>
+__device__ __forceinline__ int sentinel_word(int j) {
+    return KW == 1 || (j & 1) ? 0x7FFFFFFF : -1;
+}
+
+// LDS of the cell kernel.  Level 1 reads plain words: R0's window at its
+// global word phase mod 4, a block of kRow sentinel words, R1 the same way,
+// then from kYIn R2 and R3 likewise.  A pair's windows hold at most kQ
+// elements and each window start moves up by at most 3 words to its phase.
+// Level 2 reads padded rows of kRow words (the stage layout, which keeps the
+// lanes' row writes free of bank conflicts): X's rows, a sentinel row, Y's
+// rows, a sentinel row, at most THREADS + 2 rows, and 4 words past them that
+// candidate reads may touch.  Level 2 then overwrites the rows with the
+// cell's outputs, which leave through the stage.
 template <int THREADS, int ITEMS, int KW>
 struct MultiwayCfg {
     static constexpr int kQ = THREADS * ITEMS / 2;  // at most kQ elements of X and of Y per cell
-    static constexpr int kYIn = kQ * KW + 8;        // Y side inputs
-    static constexpr int kWords = 2 * kQ * KW + 16 + ITEMS * KW + 8;
-    static constexpr int kLds = stage_word(kWords) + 4;
+    static constexpr int kRow = ITEMS * KW;         // words of a lane's slice and of a sentinel block
+    static constexpr int kYIn = kQ * KW + 2 * kRow + 8;
+    static constexpr int kIn = 2 * kYIn;
+    static constexpr int kOut = stage_word((THREADS + 2) * kRow + 4) + 4;
+    static constexpr int kLds = kIn > kOut ? kIn : kOut;
     static constexpr int kVec = ITEMS * KW / 4;      // 16-byte loads / stores per lane
     static constexpr int kLoose = 2 * (4 / KW - 1);  // end elements per window
-    static constexpr int kStep = next_pow2(kQ);
+    static constexpr int kStep1 = kQ / 2;  // level 1: widths at most kQ/2 (a pair holds kQ)
+    static constexpr int kStep2 = kQ;      // level 2: widths at most kQ
     // Wavefronts per SIMD that the LDS allows (160 KB per CU, 4 SIMDs), at
     // most 8: the register budget follows from it.
     static constexpr int kWorkgroupsPerCu = (160 * 1024) / (4 * kLds);
@@ -518,6 +511,8 @@ struct MultiwayCfg {
                                                     : 1)
                                              : 8;
     static_assert((ITEMS * KW) % 4 == 0, "rows of whole 16-byte vectors");
+    static_assert((kQ & (kQ - 1)) == 0, "kQ: a power of two");
+    static_assert(4 * kRow <= THREADS, "one lane per sentinel word");
 };
 
 // A cell's windows in words: global start, length, LDS start (the same
@@ -533,8 +528,8 @@ struct CellWindows {
 // access stays inside the n-element source and output: windows inside
 // [0, n), each pair's windows at most Q elements together (the LDS bound),
 // and the cell's outputs inside [0, n).  On a plan of sorted runs the
-// clamps change nothing.
-template <int KW, int Y_IN, int Q>
+// clamps change nothing.  GAP sentinel words follow each window.
+template <int KW, int Y_IN, int Q, int GAP>
 __device__ __forceinline__ CellWindows cell_windows(const Cell4& d, const int32_t* src32,
                                                     int64_t n) {
     CellWindows g;
@@ -560,8 +555,10 @@ __device__ __forceinline__ CellWindows cell_windows(const Cell4& d, const int32_
         g.head[r] = h0 < nw ? h0 : nw;
         g.nvec[r] = (nw - g.head[r]) >> 2;
         g.tail[r] = (nw - g.head[r]) & 3;
-        const int base = r == 0 ? 0 : r == 1 ? g.ow[0] + KW * g.len[0] : r == 2 ? Y_IN
-                                                                                 : g.ow[2] + KW * g.len[2];
+        const int base = r == 0   ? 0
+                         : r == 1 ? g.ow[0] + KW * g.len[0] + GAP
+                         : r == 2 ? Y_IN
+                                  : g.ow[2] + KW * g.len[2] + GAP;
         g.ow[r] = base + ((ph - base) & 3);
     }
     return g;
@@ -613,7 +610,7 @@ __device__ __forceinline__ void issue_cell(const CellWindows& g, const Key* __re
     }
 }
 
-template <int THREADS, int V, int ORDER, typename Key>
+template <int THREADS, int V, int KW, int ORDER, typename Key>
 __device__ __forceinline__ void commit_cell(const CellWindows& g, const CellLoads<V, Key>& ld,
                                             int tid, int* lds) {
     const int q1 = g.nvec[0], q2 = q1 + g.nvec[1], q3 = q2 + g.nvec[2], q4 = q3 + g.nvec[3];
@@ -625,11 +622,68 @@ __device__ __forceinline__ void commit_cell(const CellWindows& g, const CellLoad
         const int l0 = sel4(r, g.ow[0] + g.head[0], g.ow[1] + g.head[1], g.ow[2] + g.head[2],
                             g.ow[3] + g.head[3]);
         if (qq < q4)
-            *reinterpret_cast<int4v*>(lds + stage_word(l0 + 4 * qi)) =
-                map_vec<ORDER, true>(ld.body[v]);
+            *reinterpret_cast<int4v*>(lds + l0 + 4 * qi) = map_vec<ORDER, true>(ld.body[v]);
     }
-    if (ld.loose_w >= 0)
-        st_elem<Key>(lds, stage_word(ld.loose_w), KeyOrder<ORDER>::to_ord(ld.loose));
+    if (ld.loose_w >= 0) st_elem<Key>(lds, ld.loose_w, KeyOrder<ORDER>::to_ord(ld.loose));
+    // the sentinel block after each window
+    constexpr int kRow = V * 4;
+    if (tid < 4 * kRow) {
+        const int r = tid / kRow, j = tid % kRow;
+        const int end = sel4(r, g.ow[0] + KW * g.len[0], g.ow[1] + KW * g.len[1],
+                             g.ow[2] + KW * g.len[2], g.ow[3] + KW * g.len[3]);
+        lds[end + j] = sentinel_word<KW>(j);
+    }
+}
+
+// Body vectors of a cell's output from the padded stage, whose word j is
+// output word j: vector i covers words [HEAD + 4i, HEAD + 4i + 4), which
+// take the last 4 - HEAD words of stage quad i and the first HEAD of quad
+// i + 1 (quads never straddle the padding).  HEAD is the output's phase,
+// uniform, so the shift costs no instruction.
+template <int THREADS, int V, int ORDER, int HEAD>
+__device__ __forceinline__ void store_cell_body(int32_t* __restrict__ dst, int nvec,
+                                                const int* stage, int tid) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        const int i = tid + v * THREADS;
+        if (i < nvec) {
+            const int4v a = *reinterpret_cast<const int4v*>(stage + stage_word(4 * i));
+            int4v x = a;
+            if constexpr (HEAD > 0) {
+                const int4v b = *reinterpret_cast<const int4v*>(stage + stage_word(4 * i + 4));
+                if constexpr (HEAD == 1) x = int4v{a.y, a.z, a.w, b.x};
+                if constexpr (HEAD == 2) x = int4v{a.z, a.w, b.x, b.y};
+                if constexpr (HEAD == 3) x = int4v{a.w, b.x, b.y, b.z};
+            }
+            store_stream4(dst + HEAD + 4 * i, map_vec<ORDER, false>(x));
+        }
+    }
+}
+
+// Stores a cell's len output words from the padded stage to dst: 16-byte
+// stores on the aligned body, single elements before and after it.
+template <int THREADS, int V, int ORDER>
+__device__ __forceinline__ void store_cell(int32_t* __restrict__ dst, int len, const int* stage,
+                                           int tid) {
+    using T = typename KeyOrder<ORDER>::T;
+    constexpr int W = KeyOrder<ORDER>::kWords;
+    const int head0 = (4 - (word_phase(dst) & 3)) & 3;
+    const int head = head0 < len ? head0 : len;
+    const int nvec = (len - head) >> 2;
+    const int tail = (len - head) & 3;
+    switch (head) {
+        case 0: store_cell_body<THREADS, V, ORDER, 0>(dst, nvec, stage, tid); break;
+        case 1: store_cell_body<THREADS, V, ORDER, 1>(dst, nvec, stage, tid); break;
+        case 2: store_cell_body<THREADS, V, ORDER, 2>(dst, nvec, stage, tid); break;
+        default: store_cell_body<THREADS, V, ORDER, 3>(dst, nvec, stage, tid); break;
+    }
+    int* const d = reinterpret_cast<int*>(dst);
+    if (W * tid < head)
+        st_elem<T>(d, W * tid, map_elem<ORDER, false>(ld_elem<T>(stage, stage_word(W * tid))));
+    if (tid >= 4 && W * (tid - 3) <= tail) {
+        const int p = head + 4 * nvec + W * (tid - 4);
+        st_elem<T>(d, p, map_elem<ORDER, false>(ld_elem<T>(stage, stage_word(p))));
+    }
 }
 
 // One workgroup merges cells [blockIdx.x*CPW, +CPW) of the pass, one after
@@ -654,28 +708,27 @@ merge_multiway_kernel(
 
     Cell4 dc = cells[c_first];
     CellLoads<Cfg::kVec, Key> ld;
-    issue_cell<THREADS, Cfg::kVec, KW, Cfg::kLoose>(cell_windows<KW, Cfg::kYIn, Cfg::kQ>(dc, src32, n), src,
-                                                    tid, ld);
+    issue_cell<THREADS, Cfg::kVec, KW, Cfg::kLoose>(
+        cell_windows<KW, Cfg::kYIn, Cfg::kQ, Cfg::kRow>(dc, src32, n), src, tid, ld);
     for (int64_t c = c_first; c < c_end; ++c) {
         if (c > c_first) __syncthreads();  // the previous cell's stores have read the stage
-        const CellWindows cur = cell_windows<KW, Cfg::kYIn, Cfg::kQ>(dc, src32, n);
-        commit_cell<THREADS, Cfg::kVec, ORDER>(cur, ld, tid, lds);
+        const CellWindows cur = cell_windows<KW, Cfg::kYIn, Cfg::kQ, Cfg::kRow>(dc, src32, n);
+        commit_cell<THREADS, Cfg::kVec, KW, ORDER>(cur, ld, tid, lds);
         __syncthreads();
         if (c + 1 < c_end) {
             dc = cells[c + 1];
-            issue_cell<THREADS, Cfg::kVec, KW, Cfg::kLoose>(cell_windows<KW, Cfg::kYIn, Cfg::kQ>(dc, src32, n),
-                                                            src, tid, ld);
+            issue_cell<THREADS, Cfg::kVec, KW, Cfg::kLoose>(
+                cell_windows<KW, Cfg::kYIn, Cfg::kQ, Cfg::kRow>(dc, src32, n), src, tid, ld);
         }
 
         // Level 1: R0|R1 into X and R2|R3 into Y, ITEMS outputs per lane:
-        // lanes [0, nx) take X's slices and lanes [nx, nx+ny) Y's, and Y is
-        // written from element nx*ITEMS on.  A cell averages half its
-        // bound, so about half the wavefronts have no slice; their branch
-        // is skipped whole (the merges dominate the kernel's VALU work).
+        // lanes [0, nx) take X's slices and lanes [nx, nx+ny) Y's.  A cell
+        // averages half its bound, so about half the wavefronts have no
+        // slice; their branch is skipped whole (the merges dominate the
+        // kernel's VALU work).
         const int lx = cur.len[0] + cur.len[1], ly = cur.len[2] + cur.len[3];
         const int total = lx + ly;
         const int nx = (lx + ITEMS - 1) / ITEMS, ny = (ly + ITEMS - 1) / ITEMS;
-        const int yw = KW * ITEMS * nx;  // LDS word of Y
         Key x[ITEMS];
         if (tid < nx + ny) {
             const bool side_y = tid >= nx;
@@ -683,22 +736,27 @@ merge_multiway_kernel(
             const int la = side_y ? cur.len[2] : cur.len[0];
             const int lb = side_y ? cur.len[3] : cur.len[1];
             const int k0 = u * ITEMS < la + lb ? u * ITEMS : la + lb;
-            merge_slice_lds<ITEMS, Cfg::kStep, KW, Key>(lds, side_y ? cur.ow[2] : cur.ow[0], la,
-                                                       side_y ? cur.ow[3] : cur.ow[1], lb, k0,
-                                                       K::kMax, x);
+            merge_slice_lds<ITEMS, Cfg::kStep1, KW, false>(lds, side_y ? cur.ow[2] : cur.ow[0], la,
+                                                          side_y ? cur.ow[3] : cur.ow[1], lb, k0, x);
         }
         __syncthreads();  // every read of the inputs is done
-        if (tid < nx + ny) put_row<ITEMS>(lds, tid, x);
+        // X's rows, a sentinel row, Y's rows, a sentinel row
+        if (tid < nx + ny) put_row<ITEMS>(lds, tid < nx ? tid : tid + 1, x);
+        if (tid < 2 * Cfg::kRow) {
+            const int row = tid < Cfg::kRow ? nx : nx + 1 + ny;
+            const int j = tid % Cfg::kRow;
+            lds[stage_word(row * Cfg::kRow + j)] = sentinel_word<KW>(j);
+        }
         __syncthreads();
 
         // Level 2: X|Y into the cell's outputs, lanes [0, ceil(total/ITEMS)).
         if (tid * ITEMS < total)
-            merge_slice_lds<ITEMS, Cfg::kStep, KW, Key>(lds, 0, lx, yw, ly, tid * ITEMS, K::kMax,
-                                                       x);
+            merge_slice_lds<ITEMS, Cfg::kStep2, KW, true>(lds, 0, lx, (nx + 1) * Cfg::kRow, ly,
+                                                         tid * ITEMS, x);
         __syncthreads();
         if (tid * ITEMS < total) put_row<ITEMS>(lds, tid, x);
         __syncthreads();
-        store_tile<THREADS, Cfg::kVec, ORDER>(reinterpret_cast<int32_t*>(dst) + KW * cur.c0,
+        store_cell<THREADS, Cfg::kVec, ORDER>(reinterpret_cast<int32_t*>(dst) + KW * cur.c0,
                                               KW * total, lds, tid);
     }
 }

@@ -338,7 +338,7 @@ static void sort_cfg(const void* in_k, const void* in_v, int64_t N, void* out_k,
         cur = 1 - cur;
     }
     for (int pass = 0; pass < four_way; ++pass, run *= 4) {
-        if constexpr (VW == 0) {
+        if constexpr (VW == 0 && MULTI) {
             if (!multiway_pass<MT, MI, ORDER>(bufk[cur], N, run, bufk[1 - cur])) abort();
         }
         cur = 1 - cur;
