@@ -83,6 +83,51 @@ __global__ __launch_bounds__(256) void plan_runs_kernel(
     }
 }
 
+// The first x in [0, pairs] whose merge start start(x) lies past c, or
+// pairs + 1 if none does: the points with start(x) <= c form a prefix, as
+// merge starts never fall.  G lanes per search (G < 64), all lanes of the
+// wavefront together.  Each round tests G points of [lo, hi); the answer
+// lies after the last passing point and at or before the first failing one.
+// The first round tests G consecutive points around `guess`, where the
+// answer sits when the merges have equal lengths (then one round finds it);
+// later rounds split the interval evenly.  Every round shrinks the interval,
+// whatever the starts hold, so the search ends.
+template <int G, typename Start>
+__device__ __forceinline__ int64_t first_start_after(int64_t c, int64_t pairs, double guess,
+                                                     bool live, Start start, int g_lane,
+                                                     int g_shift) {
+    static_assert(G >= 2 && G < 64 && (64 % G) == 0, "group size");
+    constexpr int kLog = bit_length(G) - 1;
+    int64_t lo = 0, hi = live ? pairs + 1 : 0;
+    for (int round = 0; round < 64; ++round) {
+        if (__ballot(lo < hi) == 0) break;  // every group of the wavefront is done
+        const int64_t span = hi - lo;
+        const bool near = round == 0 && span > G;
+        int64_t first = 0;
+        if (near) {
+            const double f = floor(guess) - (G / 2 - 1);
+            const double top = static_cast<double>(hi - G);
+            first = static_cast<int64_t>(fmin(fmax(f, static_cast<double>(lo)), top));
+        }
+        const int64_t q = span >> kLog, r = span & (G - 1);
+        const int npts = near || span >= G ? G : static_cast<int>(span);
+        auto point = [=](int l) -> int64_t {
+            if (near) return first + l;
+            return span < G ? lo + l : lo + q * l + ((r * l) >> kLog);
+        };
+        const bool pass = lo < hi && g_lane < npts && start(point(g_lane)) <= c;
+        const unsigned long long mine = (__ballot(pass) >> g_shift) & ((1ull << G) - 1);
+        const int cnt = __popcll(mine);
+        if (lo < hi) {
+            const int64_t new_lo = cnt > 0 ? point(cnt - 1) + 1 : lo;
+            const int64_t new_hi = cnt < npts ? point(cnt) : hi;
+            lo = new_lo;
+            hi = new_hi;
+        }
+    }
+    return lo;
+}
+
 // Batch of merges: merge p takes A[a_off[p], a_off[p+1]) and B[b_off[p],
 // b_off[p+1]) to C[a_off[p]+b_off[p], a_off[p+1]+b_off[p+1]), p = 0..pairs-1
 // (a_off[0] = b_off[0] = 0, a_off[pairs] = m, b_off[pairs] = n).  The
@@ -112,20 +157,23 @@ __global__ __launch_bounds__(256) void plan_batched_kernel(
 
     int64_t p = 0, k = 0, idx = 0, c = 0;
     bool search = false;
+    // Multiples g*seg_len look up the number of merge starts <= c (guessed
+    // from an even share of the outputs per merge); merge starts need none.
+    const bool multiple = live && w > pairs;
+    const int64_t total = m + n;
+    const int64_t cm = multiple ? (w - pairs) * seg_len : 0;
+    const double guess =
+        total > 0 ? static_cast<double>(cm) * static_cast<double>(pairs) / static_cast<double>(total)
+                  : 0.0;
+    const int64_t lo = first_start_after<G>(
+        cm, pairs, guess, multiple, [&](int64_t x) { return ao(x) + bo(x); }, g_lane, g_shift);
     if (live && w <= pairs) {  // start of merge w
         p = w;
         c = ao(p) + bo(p);
         idx = p + (c > 0 ? (c - 1) / seg_len : 0);
     } else if (live) {         // multiple g*seg_len inside some merge
         const int64_t g = w - pairs;
-        c = g * seg_len;
-        // number of merge starts <= c: upper bound over the nondecreasing starts
-        int64_t lo = 0, hi = pairs + 1;
-        while (lo < hi) {
-            const int64_t mid = (lo + hi) >> 1;
-            if (ao(mid) + bo(mid) <= c) lo = mid + 1;
-            else hi = mid;
-        }
+        c = cm;
         idx = (g - 1) + lo;
         p = lo > 0 ? (lo - 1 < pairs ? lo - 1 : pairs - 1) : 0;
         k = c - (ao(p) + bo(p));
@@ -664,7 +712,9 @@ struct TileBound {
     int64_t p;     // merge holding the boundary
 };
 
-// Boundary w = 0..tiles of the tile grid: k = min(w*tile, m+n).
+// Boundary w = 0..tiles of the tile grid: k = min(w*tile, m+n).  The merge
+// holding it is found by first_start_after, guessed from an even share of
+// the outputs per merge; then its co-rank inside that merge.
 template <int G, int ORDER>
 __global__ __launch_bounds__(256) void plan_tiles_kernel(
     const typename KeyOrder<ORDER>::T* __restrict__ A, const int64_t* __restrict__ a_off,
@@ -681,16 +731,15 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(
     auto ao = [&](int64_t p) { return clamp_to<int64_t>(a_off[p], 0, m); };
     auto bo = [&](int64_t p) { return clamp_to<int64_t>(b_off[p], 0, n); };
     int64_t p = 0, k = 0, la = 0, lb = 0;
+    const int64_t total = m + n;
+    const int64_t c = live ? (w * tile < total ? w * tile : total) : 0;
+    const double guess =
+        total > 0 ? static_cast<double>(c) * static_cast<double>(pairs) / static_cast<double>(total)
+                  : 0.0;
+    const int64_t f = first_start_after<G>(
+        c, pairs, guess, live, [&](int64_t x) { return ao(x) + bo(x); }, g_lane, g_shift);
     if (live) {
-        const int64_t total = m + n;
-        const int64_t c = w * tile < total ? w * tile : total;
-        int64_t lo = 0, hi = pairs + 1;  // merge starts <= c
-        while (lo < hi) {
-            const int64_t mid = (lo + hi) >> 1;
-            if (ao(mid) + bo(mid) <= c) lo = mid + 1;
-            else hi = mid;
-        }
-        p = lo > 0 ? (lo - 1 < pairs ? lo - 1 : pairs - 1) : 0;
+        p = f > 0 ? (f - 1 < pairs ? f - 1 : pairs - 1) : 0;
         const int64_t a1 = ao(p + 1), b1 = bo(p + 1);
         la = a1 > ao(p) ? a1 - ao(p) : 0;
         lb = b1 > bo(p) ? b1 - bo(p) : 0;
