@@ -42,6 +42,9 @@ constexpr int kVersion = 100;  // 0.1.0
 #ifndef OMERGE_SORT_ITEMS_I32  // block sort, 4-byte keys alone
 #define OMERGE_SORT_ITEMS_I32 32
 #endif
+#ifndef OMERGE_SORT_ITEMS_I64  // block sort, 8-byte keys alone
+#define OMERGE_SORT_ITEMS_I64 8
+#endif
 #ifndef OMERGE_TILE_ITEMS_I32  // tile path for short merges, 4-byte keys alone
 #define OMERGE_TILE_ITEMS_I32 16
 #endif
@@ -159,7 +162,9 @@ constexpr int items_for(int kw, int vw) {
                                 : OMERGE_ITEMS_MIXED;
 }
 constexpr int sort_items_for(int kw, int vw) {
-    return kw == 1 && vw == 0 ? OMERGE_SORT_ITEMS_I32 : items_for(kw, vw);
+    return kw == 1 && vw == 0   ? OMERGE_SORT_ITEMS_I32
+           : kw == 2 && vw == 0 ? OMERGE_SORT_ITEMS_I64
+                                : items_for(kw, vw);
 }
 constexpr int tile_items_for(int kw, int vw) {
     return kw == 1 && vw == 0 ? OMERGE_TILE_ITEMS_I32 : items_for(kw, vw);
@@ -348,9 +353,10 @@ struct Path {
     // or 2^26 for 12- and 16-byte elements): 512 lanes x 32 keys for 4-byte
     // keys alone (16,384-key runs like 1024 x 16, but one in-LDS round fewer
     // and 43% fewer VALU instructions per key; the 2^28 int32 sort took
-    // 6.63-6.64 ms against 6.83-6.85); 1024 lanes for 8-byte keys alone (4%
-    // faster than 256); 512 for the 12- and 16-byte shapes (3-4%); 256 for
-    // 4-byte keys with 4-byte payloads, where 512 and 1024 were slower.
+    // 6.63-6.64 ms against 6.83-6.85); 1024 lanes x 8 keys for 8-byte keys
+    // alone (4% faster than 256; 512 x 16 took the same time, 6.63-6.65 ms
+    // for 2^27 int64 keys); 512 for the 12- and 16-byte shapes (3-4%); 256
+    // for 4-byte keys with 4-byte payloads, where 512 and 1024 were slower.
     static constexpr int kSortThreads = (KW == 1 && VW == 0)   ? OMERGE_SORT_THREADS
                                         : (KW == 1 && VW == 1) ? OMERGE_SORT_THREADS_KV
                                         : (KW == 2 && VW == 0) ? OMERGE_SORT_THREADS_WIDE
