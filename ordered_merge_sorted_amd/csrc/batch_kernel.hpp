@@ -483,6 +483,110 @@ __device__ __forceinline__ void wave_merge_rounds(T (&x)[ITEMS], int (&pos)[ITEM
     wave_round<5, POS>(x, pos, lane);
 }
 
+// Sorts a tile held in LDS: the keys' order images in kbuf (padded rows,
+// KW = sizeof(Key)/4 words each, ITEMS elements of slack after the tile),
+// with POS their positions in pbuf.  Each lane sorts its row, six rounds
+// merge inside each wavefront, and in-LDS rounds merge the wavefronts'
+// runs, until x (and pos) hold lane tid's ITEMS elements of the sorted tile.
+// kbuf, pbuf and split (THREADS words) are scratch afterwards.
+template <int THREADS, int ITEMS, bool POS, typename Key>
+__device__ __forceinline__ void sort_tile(int* kbuf, int* pbuf, int* split, Key (&x)[ITEMS],
+                                          int (&pos)[ITEMS], int tid, Key kmax) {
+    constexpr int KW = sizeof(Key) / 4;
+    constexpr int kTile = THREADS * ITEMS;
+    // Each lane sorts its row of ITEMS elements.
+    get_row<ITEMS>(kbuf, tid, x);
+#pragma unroll
+    for (int t = 0; t < ITEMS; ++t) pos[t] = tid * ITEMS + t;
+    bitonic_sort<ITEMS, POS>(x, pos);
+
+    // The first six rounds run inside each wavefront, across lanes: keys
+    // alone (equal keys are indistinguishable, so any exact order of them is
+    // the stable one), or (key, position) pairs with payloads.  Each
+    // wavefront's run then holds one contiguous block of tile positions, so
+    // the A-first merges of the LDS rounds below stay stable.
+    constexpr int kWaveRun = ITEMS * 64;
+    wave_merge_rounds<POS>(x, pos, tid & 63);
+
+    // Merge rounds: runs of `run` elements merge pairwise into runs of 2*run.
+    // The A run of a pair holds earlier positions than its B run, so taking
+    // A on equal keys is the stable order.
+    for (int run = kWaveRun; run < kTile; run *= 2) {
+        __syncthreads();  // every read of the previous round is done
+        put_row<ITEMS>(kbuf, tid, x);
+        if constexpr (POS) put_row<ITEMS>(pbuf, tid, pos);
+        __syncthreads();
+        const int lanes = 2 * run / ITEMS;   // lanes per merged pair
+        const int u = tid % lanes;           // this lane's place in it
+        const int a0 = (tid - u) * ITEMS;    // the pair's A run; B run at a0 + run
+        const int b0 = a0 + run;
+        const int o_end = (u + 1) * ITEMS;
+        // Co-rank of o_end: the largest x in [x_lo, x_hi] such that A[x-1]
+        // comes before B[o_end-x] (A[x-1] <= B[o_end-x]; true at x_lo; the
+        // passing points form a prefix), found by binary lifting: steps of
+        // run, run/2, ..., 1 (they sum past the range, which is at most run
+        // wide), each kept when its point passes.  Every tested point x in
+        // (x_lo, x_hi] reads A[x-1] and B[o_end-x], both inside the pair's
+        // runs.
+        const int x_lo = o_end > run ? o_end - run : 0;
+        const int x_hi = o_end < run ? o_end : run;
+        int lo = x_lo;
+        for (int step = run; step > 0; step >>= 1) {
+            const int p = lo + step;
+            const int pc = p < x_hi ? p : x_hi;
+            const Key av = ld_elem<Key>(kbuf, stage_word(KW * (a0 + pc - 1)));
+            const Key bv = ld_elem<Key>(kbuf, stage_word(KW * (b0 + o_end - pc)));
+            lo = (p <= x_hi && av <= bv) ? p : lo;
+        }
+        split[tid] = lo;
+        __syncthreads();
+        const int s = u > 0 ? split[tid - 1] : 0;  // A elements before this lane's outputs
+        const int bs = u * ITEMS - s;
+        if constexpr (!POS) {
+            // Candidates past a run's end read the next run (or the slack)
+            // and are replaced by the largest image.  ITEMS consecutive
+            // elements cross at most one 32-word pad: element t of a read
+            // starting at word w sits at stage_word(w) + KW*t, plus 4 once
+            // KW*t reaches the pad at 32 - (w & 31).
+            Key a[ITEMS], b[ITEMS];
+            const int wa = KW * (a0 + s), wb = KW * (b0 + bs);
+            const int* const pa = kbuf + stage_word(wa);
+            const int* const pb = kbuf + stage_word(wb);
+            const int ca = 32 - (wa & 31), cb = 32 - (wb & 31);
+#pragma unroll
+            for (int t = 0; t < ITEMS; ++t) {
+                a[t] = ld_elem<Key>(pa, KW * t + (KW * t >= ca ? 4 : 0));
+                b[t] = ld_elem<Key>(pb, KW * t + (KW * t >= cb ? 4 : 0));
+            }
+            if (s + ITEMS > run || bs + ITEMS > run) {  // rare past the first rounds
+#pragma unroll
+                for (int t = 0; t < ITEMS; ++t) {
+                    a[t] = t < run - s ? a[t] : kmax;
+                    b[t] = t < run - bs ? b[t] : kmax;
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < ITEMS; ++t) x[t] = min(a[t], b[ITEMS - 1 - t]);
+            bitonic_clean<ITEMS>(x);
+        } else {
+            int ai = s, bi = bs;
+            const int a_end = lo, b_end = o_end - lo;
+#pragma unroll
+            for (int t = 0; t < ITEMS; ++t) {
+                const int ca = ai < run ? ai : run - 1;
+                const int cb = bi < run ? bi : run - 1;
+                const Key ka = ld_elem<Key>(kbuf, stage_word(KW * (a0 + ca)));
+                const Key kb = ld_elem<Key>(kbuf, stage_word(KW * (b0 + cb)));
+                const bool take_a = ai < a_end && (bi >= b_end || ka <= kb);
+                x[t] = take_a ? ka : kb;
+                pos[t] = pbuf[stage_word(take_a ? a0 + ca : b0 + cb)];
+                ai += take_a ? 1 : 0;
+                bi += take_a ? 0 : 1;
+            }
+        }
+    }
+}
+
 template <int THREADS, int ITEMS, int VW, int ORDER>
 __global__ __launch_bounds__(THREADS) void block_sort_kernel(
     const typename KeyOrder<ORDER>::T* __restrict__ src, const uint32_t* __restrict__ src_v,
@@ -544,99 +648,9 @@ __global__ __launch_bounds__(THREADS) void block_sort_kernel(
     }
     __syncthreads();
 
-    // Each lane sorts its row of ITEMS elements.
     Key x[ITEMS];
     int pos[ITEMS];
-    get_row<ITEMS>(kbuf, tid, x);
-#pragma unroll
-    for (int t = 0; t < ITEMS; ++t) pos[t] = tid * ITEMS + t;
-    bitonic_sort<ITEMS, KV>(x, pos);
-
-    // The first six rounds run inside each wavefront, across lanes: keys
-    // alone (equal keys are indistinguishable, so any exact order of them is
-    // the stable one), or (key, position) pairs with payloads.  Each
-    // wavefront's run then holds one contiguous block of tile positions, so
-    // the A-first merges of the LDS rounds below stay stable.
-    constexpr int kWaveRun = ITEMS * 64;
-    wave_merge_rounds<KV>(x, pos, tid & 63);
-
-    // Merge rounds: runs of `run` elements merge pairwise into runs of 2*run.
-    // The A run of a pair holds earlier positions than its B run, so taking
-    // A on equal keys is the stable order.
-    for (int run = kWaveRun; run < kTile; run *= 2) {
-        __syncthreads();  // every read of the previous round is done
-        put_row<ITEMS>(kbuf, tid, x);
-        if constexpr (KV) put_row<ITEMS>(pbuf, tid, pos);
-        __syncthreads();
-        const int lanes = 2 * run / ITEMS;   // lanes per merged pair
-        const int u = tid % lanes;           // this lane's place in it
-        const int a0 = (tid - u) * ITEMS;    // the pair's A run; B run at a0 + run
-        const int b0 = a0 + run;
-        const int o_end = (u + 1) * ITEMS;
-        // Co-rank of o_end: the largest x in [x_lo, x_hi] such that A[x-1]
-        // comes before B[o_end-x] (A[x-1] <= B[o_end-x]; true at x_lo; the
-        // passing points form a prefix), found by binary lifting: steps of
-        // run, run/2, ..., 1 (they sum past the range, which is at most run
-        // wide), each kept when its point passes.  Every tested point x in
-        // (x_lo, x_hi] reads A[x-1] and B[o_end-x], both inside the pair's
-        // runs.
-        const int x_lo = o_end > run ? o_end - run : 0;
-        const int x_hi = o_end < run ? o_end : run;
-        int lo = x_lo;
-        for (int step = run; step > 0; step >>= 1) {
-            const int p = lo + step;
-            const int pc = p < x_hi ? p : x_hi;
-            const Key av = ld_elem<Key>(kbuf, stage_word(KW * (a0 + pc - 1)));
-            const Key bv = ld_elem<Key>(kbuf, stage_word(KW * (b0 + o_end - pc)));
-            lo = (p <= x_hi && av <= bv) ? p : lo;
-        }
-        split[tid] = lo;
-        __syncthreads();
-        const int s = u > 0 ? split[tid - 1] : 0;  // A elements before this lane's outputs
-        const int bs = u * ITEMS - s;
-        if constexpr (!KV) {
-            // Candidates past a run's end read the next run (or the slack)
-            // and are replaced by the largest image.  ITEMS consecutive
-            // elements cross at most one 32-word pad: element t of a read
-            // starting at word w sits at stage_word(w) + KW*t, plus 4 once
-            // KW*t reaches the pad at 32 - (w & 31).
-            Key a[ITEMS], b[ITEMS];
-            const int wa = KW * (a0 + s), wb = KW * (b0 + bs);
-            const int* const pa = kbuf + stage_word(wa);
-            const int* const pb = kbuf + stage_word(wb);
-            const int ca = 32 - (wa & 31), cb = 32 - (wb & 31);
-#pragma unroll
-            for (int t = 0; t < ITEMS; ++t) {
-                a[t] = ld_elem<Key>(pa, KW * t + (KW * t >= ca ? 4 : 0));
-                b[t] = ld_elem<Key>(pb, KW * t + (KW * t >= cb ? 4 : 0));
-            }
-            if (s + ITEMS > run || bs + ITEMS > run) {  // rare past the first rounds
-#pragma unroll
-                for (int t = 0; t < ITEMS; ++t) {
-                    a[t] = t < run - s ? a[t] : K::kMax;
-                    b[t] = t < run - bs ? b[t] : K::kMax;
-                }
-            }
-#pragma unroll
-            for (int t = 0; t < ITEMS; ++t) x[t] = min(a[t], b[ITEMS - 1 - t]);
-            bitonic_clean<ITEMS>(x);
-        } else {
-            int ai = s, bi = bs;
-            const int a_end = lo, b_end = o_end - lo;
-#pragma unroll
-            for (int t = 0; t < ITEMS; ++t) {
-                const int ca = ai < run ? ai : run - 1;
-                const int cb = bi < run ? bi : run - 1;
-                const Key ka = ld_elem<Key>(kbuf, stage_word(KW * (a0 + ca)));
-                const Key kb = ld_elem<Key>(kbuf, stage_word(KW * (b0 + cb)));
-                const bool take_a = ai < a_end && (bi >= b_end || ka <= kb);
-                x[t] = take_a ? ka : kb;
-                pos[t] = pbuf[stage_word(take_a ? a0 + ca : b0 + cb)];
-                ai += take_a ? 1 : 0;
-                bi += take_a ? 0 : 1;
-            }
-        }
-    }
+    sort_tile<THREADS, ITEMS, KV>(kbuf, pbuf, split, x, pos, tid, K::kMax);
     __syncthreads();
     put_row<ITEMS>(kbuf, tid, x);
     if constexpr (KV) put_row<ITEMS>(pbuf, tid, pos);
@@ -667,6 +681,81 @@ __global__ __launch_bounds__(THREADS) void block_sort_kernel(
 #pragma unroll
                 for (int v = 0; v < VW; ++v) dst_v[VW * (t0 + e) + v] = vbuf[VW * q + v];
             }
+        }
+    }
+}
+
+// Block sort of 4-byte keys with payloads (VW words each) as 8-byte keys
+// alone: element e of the tile sorts as the signed 64-bit value whose high
+// word is its key's order image and whose low word is e.  These values are
+// all distinct and order as (key, position), so sorting them is the stable
+// order of the tile, with one 64-bit compare per exchange where the
+// (key, position) pairs of block_sort_kernel take several.  Payloads stay
+// in global memory: each lane gathers its outputs' payloads by position
+// into registers, and a barrier separates every read of the tile from its
+// writes (dst and dst_v may be src and src_v).  The tile's missing tail
+// takes the largest image and positions past the end, which sort last and
+// are never stored.
+template <int THREADS, int ITEMS, int VW, int ORDER>
+__global__ __launch_bounds__(THREADS) void block_sort_packed_kernel(
+    const typename KeyOrder<ORDER>::T* src, const uint32_t* src_v, int64_t total,
+    typename KeyOrder<ORDER>::T* dst, uint32_t* dst_v) {
+    using K = KeyOrder<ORDER>;
+    using P = long long;
+    static_assert(K::kWords == 1 && VW > 0, "4-byte keys with payloads");
+    static_assert(ITEMS >= 4 && (ITEMS & (ITEMS - 1)) == 0, "ITEMS: a power of two");
+    static_assert(2 * ITEMS <= 32, "a lane's row fits in 32 words");
+    constexpr int kTile = THREADS * ITEMS;
+    constexpr int kKeyWords = stage_word((kTile + ITEMS) * 2);
+    __shared__ __attribute__((aligned(16))) int lds[kKeyWords + THREADS];
+    int* const kbuf = lds;
+    int* const split = lds + kKeyWords;
+
+    const int tid = threadIdx.x;
+    const int64_t t0 = blockIdx.x * static_cast<int64_t>(kTile);
+    const int len = static_cast<int>(total - t0 < kTile ? total - t0 : kTile);
+#pragma unroll
+    for (int r = 0; r < ITEMS; ++r) {
+        const int e = tid + r * THREADS;
+        const int img = e < len ? K::to_ord(src[t0 + e]) : K::kMax;
+        const uint64_t bits = (static_cast<uint64_t>(static_cast<uint32_t>(img)) << 32) |
+                              static_cast<uint32_t>(e);
+        st_elem<P>(kbuf, stage_word(2 * e), static_cast<P>(bits));
+    }
+    __syncthreads();
+
+    P x[ITEMS];
+    int pos[ITEMS];
+    sort_tile<THREADS, ITEMS, false>(kbuf, kbuf, split, x, pos, tid,
+                                     std::numeric_limits<P>::max());
+    __syncthreads();
+    put_row<ITEMS>(kbuf, tid, x);
+    __syncthreads();
+
+    // Output e = tid + r*THREADS (coalesced): its key, and its payload read
+    // from the element's position before anything of the tile is written.
+    int key[ITEMS];
+    uint32_t pay[ITEMS][VW];
+#pragma unroll
+    for (int r = 0; r < ITEMS; ++r) {
+        const int e = tid + r * THREADS;
+        key[r] = 0;
+        if (e < len) {
+            const P v = ld_elem<P>(kbuf, stage_word(2 * e));
+            key[r] = K::from_ord(static_cast<int>(v >> 32));
+            const int64_t q = t0 + static_cast<int>(static_cast<uint32_t>(v));
+#pragma unroll
+            for (int w = 0; w < VW; ++w) pay[r][w] = src_v[VW * q + w];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < ITEMS; ++r) {
+        const int e = tid + r * THREADS;
+        if (e < len) {
+            dst[t0 + e] = key[r];
+#pragma unroll
+            for (int w = 0; w < VW; ++w) dst_v[VW * (t0 + e) + w] = pay[r][w];
         }
     }
 }

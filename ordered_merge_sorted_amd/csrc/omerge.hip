@@ -96,6 +96,15 @@ constexpr int kVersion = 100;  // 0.1.0
 #ifndef OMERGE_SORT_THREADS_WIDE  // lanes of the block sort for 8-byte keys without payloads
 #define OMERGE_SORT_THREADS_WIDE 1024
 #endif
+#ifndef OMERGE_SORT_PACKED  // 4-byte keys with payloads block-sort as packed 8-byte keys
+#define OMERGE_SORT_PACKED 1
+#endif
+#ifndef OMERGE_SORT_THREADS_PACKED  // lanes and keys per lane of that block sort
+#define OMERGE_SORT_THREADS_PACKED 1024
+#endif
+#ifndef OMERGE_SORT_ITEMS_PACKED
+#define OMERGE_SORT_ITEMS_PACKED 8
+#endif
 #ifndef OMERGE_SORT_THREADS_MIXED  // lanes of the block sort for the other shapes
 #define OMERGE_SORT_THREADS_MIXED 512
 #endif
@@ -344,7 +353,11 @@ struct Path {
     static constexpr int kTileItems = tile_items_for(KW, VW);  // tile path
     static constexpr int kBatchTile = kThreads * kTileItems;
     static constexpr bool kTileReg = VW == 0 && KW * kTileItems == 16;
-    static constexpr int kSortItems = sort_items_for(KW, VW);
+    // 4-byte keys with payloads sort their tiles as packed 8-byte keys
+    // (block_sort_packed_kernel) unless built with OMERGE_SORT_PACKED=0.
+    static constexpr bool kSortPacked = OMERGE_SORT_PACKED && KW == 1 && VW > 0;
+    static constexpr int kSortItems =
+        kSortPacked ? OMERGE_SORT_ITEMS_PACKED : sort_items_for(KW, VW);
     static constexpr int kShape = shape_index(KW, VW);
     // Block sort shape: the first sorted runs are kSortTile elements long.
     // Longer runs save whole merge passes (each one read and one write of
@@ -356,8 +369,11 @@ struct Path {
     // 6.63-6.64 ms against 6.83-6.85); 1024 lanes x 8 keys for 8-byte keys
     // alone (4% faster than 256; 512 x 16 took the same time, 6.63-6.65 ms
     // for 2^27 int64 keys); 512 for the 12- and 16-byte shapes (3-4%); 256
-    // for 4-byte keys with 4-byte payloads, where 512 and 1024 were slower.
-    static constexpr int kSortThreads = (KW == 1 && VW == 0)   ? OMERGE_SORT_THREADS
+    // for 4-byte keys with 4-byte payloads as (key, position) pairs, where
+    // 512 and 1024 were slower; packed, those take 1024 lanes x 8 keys
+    // (8,192-key runs, the 8-byte keys' shape).
+    static constexpr int kSortThreads = kSortPacked                ? OMERGE_SORT_THREADS_PACKED
+                                        : (KW == 1 && VW == 0)   ? OMERGE_SORT_THREADS
                                         : (KW == 1 && VW == 1) ? OMERGE_SORT_THREADS_KV
                                         : (KW == 2 && VW == 0) ? OMERGE_SORT_THREADS_WIDE
                                                                : OMERGE_SORT_THREADS_MIXED;
@@ -628,10 +644,16 @@ struct Path {
         uint32_t* bufv[2] = {static_cast<uint32_t*>(out_v), sv};
         // block sort target: the last pass then writes out
         int cur = (two_way + four_way) % 2;
-        hipLaunchKernelGGL((block_sort_kernel<kSortThreads, kSortItems, VW, ORDER>),
-                           dim3(static_cast<unsigned>(tiles)), dim3(kSortThreads), 0, stream,
-                           static_cast<const Key*>(in_k), static_cast<const uint32_t*>(in_v), N,
-                           bufk[cur], bufv[cur]);
+        if constexpr (kSortPacked)
+            hipLaunchKernelGGL((block_sort_packed_kernel<kSortThreads, kSortItems, VW, ORDER>),
+                               dim3(static_cast<unsigned>(tiles)), dim3(kSortThreads), 0, stream,
+                               static_cast<const Key*>(in_k), static_cast<const uint32_t*>(in_v),
+                               N, bufk[cur], bufv[cur]);
+        else
+            hipLaunchKernelGGL((block_sort_kernel<kSortThreads, kSortItems, VW, ORDER>),
+                               dim3(static_cast<unsigned>(tiles)), dim3(kSortThreads), 0, stream,
+                               static_cast<const Key*>(in_k), static_cast<const uint32_t*>(in_v),
+                               N, bufk[cur], bufv[cur]);
         hipError_t e = hipGetLastError();
         rc = e == hipSuccess ? OMERGE_OK : hip_fail(e);
         int64_t run = kSortTile;

@@ -185,18 +185,18 @@ static void typed_cfg(const void* A, const void* Av, int64_t m, const void* B, c
 constexpr int production_items(int kw, int vw) {
     return kw == 1 && vw == 0 ? 8 : (kw + vw == 2 ? 8 : 4);
 }
-// Outputs per lane of the library's block sort (32 for 4-byte keys alone)
-// and of its tile path for short merges (16 for 4-byte keys alone), else the
-// segment merge's count.
+// Outputs per lane of the library's block sort (32 for 4-byte keys alone,
+// 8 for 4-byte keys with payloads, packed) and of its tile path for short
+// merges (16 for 4-byte keys alone), else the segment merge's count.
 constexpr int production_sort_items(int kw, int vw) {
-    return kw == 1 && vw == 0 ? 32 : production_items(kw, vw);
+    return kw == 1 && vw == 0 ? 32 : kw == 1 ? 8 : production_items(kw, vw);
 }
 constexpr int production_tile_items(int kw, int vw) {
     return kw == 1 && vw == 0 ? 16 : production_items(kw, vw);
 }
 // Lanes of the library's block sort for each shape.
 constexpr int production_sort_threads(int kw, int vw) {
-    return kw == 1 && vw == 0 ? 512 : kw == 1 && vw == 1 ? 256 : kw == 2 && vw == 0 ? 1024 : 512;
+    return kw == 1 && vw == 0 ? 512 : kw == 1 ? 1024 : kw == 2 && vw == 0 ? 1024 : 512;
 }
 
 // Which (order, payload words, shape) combinations this library holds:
@@ -315,10 +315,17 @@ static void sort_cfg(const void* in_k, const void* in_v, int64_t N, void* out_k,
                          VW ? reinterpret_cast<uint32_t*>(scratch + val_at) : nullptr};
     int cur = passes % 2;
     const int64_t tiles = (N + kTile - 1) / kTile;
+    // 4-byte keys with payloads block-sort as packed 8-byte keys, as the
+    // library does.
     run_grid(tiles, ST, [&] {
-        omerge::block_sort_kernel<ST, SI, VW, ORDER>(static_cast<const Key*>(in_k),
-                                                   static_cast<const uint32_t*>(in_v), N,
-                                                   bufk[cur], bufv[cur]);
+        if constexpr (omerge::KeyOrder<ORDER>::kWords == 1 && VW > 0)
+            omerge::block_sort_packed_kernel<ST, SI, VW, ORDER>(
+                static_cast<const Key*>(in_k), static_cast<const uint32_t*>(in_v), N, bufk[cur],
+                bufv[cur]);
+        else
+            omerge::block_sort_kernel<ST, SI, VW, ORDER>(static_cast<const Key*>(in_k),
+                                                       static_cast<const uint32_t*>(in_v), N,
+                                                       bufk[cur], bufv[cur]);
     });
     int64_t run = kTile;
     for (int pass = 0; pass < two_way; ++pass, run *= 2) {
