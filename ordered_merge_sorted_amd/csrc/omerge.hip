@@ -123,6 +123,12 @@ constexpr int kVersion = 100;  // 0.1.0
 #ifndef OMERGE_MULTIWAY_LANES  // lanes per sample point in the 4-way plan
 #define OMERGE_MULTIWAY_LANES 8
 #endif
+#ifndef OMERGE_MULTIWAY_THREADS  // lanes of the 4-way cell kernel
+#define OMERGE_MULTIWAY_THREADS 256
+#endif
+#ifndef OMERGE_MULTIWAY_ITEMS  // 4-byte keys per lane of the 4-way cell kernel (8-byte: half)
+#define OMERGE_MULTIWAY_ITEMS 32
+#endif
 #ifndef OMERGE_MULTIWAY_CELLS  // cells per workgroup of the 4-way cell kernel
 #define OMERGE_MULTIWAY_CELLS 4
 #endif
@@ -157,7 +163,10 @@ constexpr int kMultiwayCells = OMERGE_MULTIWAY_CELLS;
 // (37 KB of LDS, four workgroups per CU).  Against 16 keys per lane (cells of
 // half the size) the plan has half the points: on 2^28 int32 keys in runs of
 // 2^14 to 2^26 the pass took 0.92-0.99 ms against 1.05-1.09 ms.
-constexpr int multiway_items(int kw) { return kw == 1 ? 32 : 16; }
+constexpr int kMultiwayThreads = OMERGE_MULTIWAY_THREADS;
+constexpr int multiway_items(int kw) {
+    return kw == 1 ? OMERGE_MULTIWAY_ITEMS : OMERGE_MULTIWAY_ITEMS / 2;
+}
 
 // Outputs per lane of the segment merge for KW key words and VW payload
 // words per element: 32 bytes of element per lane for 4-byte keys alone
@@ -546,7 +555,7 @@ struct Path {
     // cell array is the caller's (`cells`, at least plan.cells entries) or,
     // when null, stream-ordered scratch.  Keys alone.
     static constexpr int kMwItems = multiway_items(KW);
-    static constexpr int64_t kMwQ = int64_t(kThreads) * kMwItems / 2;
+    static constexpr int64_t kMwQ = int64_t(kMultiwayThreads) * kMwItems / 2;
     static int runs4(const Key* src, Key* dst, int64_t N, int64_t run, Cell4* cells,
                      hipStream_t stream) {
         static_assert(VW == 0, "the 4-way pass moves keys alone");
@@ -567,9 +576,10 @@ struct Path {
                            dim3(256), 0, stream, src, N, run, kMwQ, mp, c);
         hipError_t e = hipGetLastError();
         if (e == hipSuccess)
-            hipLaunchKernelGGL((merge_multiway_kernel<kThreads, kMwItems, kMultiwayCells, ORDER>),
-                               dim3(static_cast<unsigned>(ceil_div(mp.cells, kMultiwayCells))),
-                               dim3(kThreads), 0, stream, src, N, c, mp.cells, dst);
+            hipLaunchKernelGGL(
+                (merge_multiway_kernel<kMultiwayThreads, kMwItems, kMultiwayCells, ORDER>),
+                dim3(static_cast<unsigned>(ceil_div(mp.cells, kMultiwayCells))),
+                dim3(kMultiwayThreads), 0, stream, src, N, c, mp.cells, dst);
         if (e == hipSuccess) e = hipGetLastError();
         int rc = e == hipSuccess ? OMERGE_OK : hip_fail(e);
         if (cells == nullptr) {
