@@ -569,8 +569,8 @@ def test_sort_unaligned_outputs(off):
 
 
 def test_sort_in_place_and_large():
-    """In-place sort (out = input), and 2^24 int32 keys with payloads (16
-    merge passes after the block sort)."""
+    """In-place sort (out = input), and 2^24 int32 keys with payloads (11
+    merge passes after the block sort's 8,192-pair runs)."""
     g = np.random.Generator(np.random.PCG64(733))
     K = g.integers(-(1 << 31), 1 << 31, size=300000, dtype=np.int64).astype(np.int32)
     t = dev(K)
