@@ -60,6 +60,15 @@ constexpr int kVersion = 100;  // 0.1.0
 #ifndef OMERGE_PART_STRIDE  // the partition's first phase searches every STRIDE-th boundary
 #define OMERGE_PART_STRIDE 16
 #endif
+#ifndef OMERGE_PART_SMALL  // partitions of at most this many boundaries take the shape below
+#define OMERGE_PART_SMALL 32768
+#endif
+#ifndef OMERGE_PART_LANES_SMALL  // lanes per boundary (both phases) of those partitions
+#define OMERGE_PART_LANES_SMALL 8
+#endif
+#ifndef OMERGE_PART_STRIDE_SMALL
+#define OMERGE_PART_STRIDE_SMALL 8
+#endif
 #ifndef OMERGE_TILES_PER_SEG  // tiles per workgroup segment of one merge, 4-byte keys alone
 #define OMERGE_TILES_PER_SEG 2
 #endif
@@ -432,14 +441,32 @@ struct Path {
         return OMERGE_OK;
     }
 
+    // Partition shape, by the number of boundaries.  The headline's 131,072
+    // boundaries are bound by the random lines their probes fetch: 4 lanes
+    // per boundary with every 16th boundary searched first measured fastest
+    // there (8 lanes: 69 us against 42).  A few tens of thousands of
+    // boundaries are bound by their dependent rounds instead: 8 lanes per
+    // boundary (9-way splits where keys tie and interpolation cannot help)
+    // and every 8th boundary first took the 21,846 boundaries of the
+    // 2^26+2^26 key+payload step with 256 distinct keys from 23.5 to 22.5 us
+    // and the step from 0.3873-0.3876 to 0.3825 ms, and left a key+payload
+    // merge of distinct keys as fast (0.397-0.400 ms).
     static int partition(const Key* A, int64_t m, const Key* B, int64_t n, int64_t seg_len,
                          int64_t* part, hipStream_t stream) {
         const int64_t count = ceil_div(m + n, seg_len) + 1;
-        const int64_t blocks = ceil_div(count * kPartLanes, 256);
+        const bool small = count <= OMERGE_PART_SMALL;
+        const int64_t blocks =
+            ceil_div(count * (small ? OMERGE_PART_LANES_SMALL : kPartLanes), 256);
         if (blocks > kMaxGridBlocks) return OMERGE_OVERFLOW;
-        hipLaunchKernelGGL((partition_kernel<kPartLanes, ORDER, kPartLanes2, OMERGE_PART_STRIDE>),
-                           dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, A, m, B, n,
-                           seg_len, count, part);
+        if (small)
+            hipLaunchKernelGGL((partition_kernel<OMERGE_PART_LANES_SMALL, ORDER,
+                                                 OMERGE_PART_LANES_SMALL, OMERGE_PART_STRIDE_SMALL>),
+                               dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, A, m, B,
+                               n, seg_len, count, part);
+        else
+            hipLaunchKernelGGL((partition_kernel<kPartLanes, ORDER, kPartLanes2, OMERGE_PART_STRIDE>),
+                               dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, A, m, B,
+                               n, seg_len, count, part);
         hipError_t e = hipGetLastError();
         return e == hipSuccess ? OMERGE_OK : hip_fail(e);
     }

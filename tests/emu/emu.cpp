@@ -170,9 +170,16 @@ static void typed_cfg(const void* A, const void* Av, int64_t m, const void* B, c
     const Key* a = static_cast<const Key*>(A);
     const Key* b = static_cast<const Key*>(B);
     const int64_t count = (m + n + seg_len - 1) / seg_len + 1;
-    run_grid((count * 4 + 255) / 256, 256, [&] {
-        omerge::partition_kernel<4, ORDER, 4, 16>(a, m, b, n, seg_len, count, part);
-    });
+    // the library's partition shapes: 8 lanes per boundary and every 8th
+    // boundary first for at most 32,768 boundaries, else 4 and 16
+    if (count <= 32768)
+        run_grid((count * 8 + 255) / 256, 256, [&] {
+            omerge::partition_kernel<8, ORDER, 8, 8>(a, m, b, n, seg_len, count, part);
+        });
+    else
+        run_grid((count * 4 + 255) / 256, 256, [&] {
+            omerge::partition_kernel<4, ORDER, 4, 16>(a, m, b, n, seg_len, count, part);
+        });
     if (m + n == 0) return;
     const bool reg = aligned16(C) && (VW == 0 || aligned16(Cv));
     run_merge<T, I, VW, ORDER, false>(reg, count - 1, a, static_cast<const uint32_t*>(Av), m, b,
