@@ -60,6 +60,9 @@ constexpr int kVersion = 100;  // 0.1.0
 #ifndef OMERGE_PART_STRIDE  // the partition's first phase searches every STRIDE-th boundary
 #define OMERGE_PART_STRIDE 16
 #endif
+#ifndef OMERGE_PLAN_LANES  // lanes per boundary in the batch and sort-pass plans
+#define OMERGE_PLAN_LANES OMERGE_PART_LANES
+#endif
 #ifndef OMERGE_PART_SMALL  // partitions of at most this many boundaries take the shape below
 #define OMERGE_PART_SMALL 32768
 #endif
@@ -156,6 +159,7 @@ constexpr int kVersion = 100;  // 0.1.0
 constexpr int kThreads = OMERGE_THREADS;
 constexpr int kPartLanes = OMERGE_PART_LANES;
 constexpr int kPartLanes2 = OMERGE_PART_LANES2;
+constexpr int kPlanLanes = OMERGE_PLAN_LANES;
 // Segment-length windows: target R and the half-width searched around it.
 struct SegWindow {
     int target, slack;
@@ -503,13 +507,13 @@ struct Path {
                              const Key* b, const void* Bv, const int64_t* b_off, int64_t n,
                              int64_t pairs, void* C, void* Cv, hipStream_t stream) {
         const int64_t tiles = ceil_div(m + n, kBatchTile);
-        const int64_t blocks = ceil_div((tiles + 1) * kPartLanes, 256);
+        const int64_t blocks = ceil_div((tiles + 1) * kPlanLanes, 256);
         if (tiles > kMaxGridBlocks || blocks > kMaxGridBlocks) return OMERGE_OVERFLOW;
         TileBound* tb = nullptr;
         hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&tb),
                                       static_cast<size_t>(tiles + 1) * sizeof(TileBound), stream);
         if (e != hipSuccess) return hip_fail(e);
-        hipLaunchKernelGGL((plan_tiles_kernel<kPartLanes, ORDER>),
+        hipLaunchKernelGGL((plan_tiles_kernel<kPlanLanes, ORDER>),
                            dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, a, a_off, m,
                            b, b_off, n, pairs, static_cast<int64_t>(kBatchTile), tiles, tb);
         e = hipGetLastError();
@@ -554,7 +558,7 @@ struct Path {
         int rc = seg_len(m, n, &sl, false, &kDescWindow);
         if (rc != OMERGE_OK) return rc;
         const int64_t segs = pairs + ceil_div(total, sl) - 1;
-        const int64_t blocks = ceil_div((segs + 1) * kPartLanes, 256);
+        const int64_t blocks = ceil_div((segs + 1) * kPlanLanes, 256);
         if (segs > kMaxGridBlocks || blocks > kMaxGridBlocks) return OMERGE_OVERFLOW;
         SegDesc* desc = nullptr;
         hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&desc),
@@ -562,7 +566,7 @@ struct Path {
         if (e != hipSuccess) return hip_fail(e);
         const Key* a = static_cast<const Key*>(A);
         const Key* b = static_cast<const Key*>(B);
-        hipLaunchKernelGGL((plan_batched_kernel<kPartLanes, ORDER>),
+        hipLaunchKernelGGL((plan_batched_kernel<kPlanLanes, ORDER>),
                            dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, a, a_off, m,
                            b, b_off, n, pairs, sl, segs, desc);
         e = hipGetLastError();
@@ -698,8 +702,8 @@ struct Path {
             const int64_t per_pair = ceil_div(2 * run, sl);
             const int64_t full = N / (2 * run), rem = N - full * 2 * run;
             const int64_t segs = full * per_pair + (rem > 0 ? ceil_div(rem, sl) : 0);
-            const int64_t blocks = ceil_div((segs + 1) * kPartLanes, 256);
-            hipLaunchKernelGGL((plan_runs_kernel<kPartLanes, ORDER>),
+            const int64_t blocks = ceil_div((segs + 1) * kPlanLanes, 256);
+            hipLaunchKernelGGL((plan_runs_kernel<kPlanLanes, ORDER>),
                                dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
                                bufk[cur], N, run, sl, per_pair, segs, desc);
             e = hipGetLastError();
