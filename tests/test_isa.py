@@ -77,7 +77,8 @@ def test_multiway_kernels_without_scratch(asm):
     """The 4-way pass's plan and cell kernels, every key order, run without
     scratch.  Selects over a small array of words once compiled to a
     dynamically indexed private load (scratch memory) in every candidate
-    read; the cell kernel's candidates are 16-byte LDS reads."""
+    read, and a select chain over an array of per-run offsets did the same;
+    the cell kernel moves its windows and its output by 16-byte accesses."""
     names = sorted(set(re.findall(r"^(_ZN6omerge2\d(?:plan|merge)_multiway_kernel\w*):", asm,
                                   re.M)))
     assert len(names) >= 24, len(names)
@@ -103,3 +104,14 @@ def test_block_sort_lane_exchanges(asm):
     for prev, cur in zip(lines, lines[1:]):
         if cur[0] == "v_mov_b32_dpp" and prev[0] == "v_mov_b32_e32":
             assert prev[1].rstrip(",") != cur[1].rstrip(","), (prev, cur)
+
+
+def test_block_sorts_without_scratch(asm):
+    """Every block sort instantiation, (key, position) pairs and packed
+    (image, position) keys included, runs without scratch."""
+    names = sorted(set(re.findall(r"^(_ZN6omerge\d+block_sort(?:_packed)?_kernel\w*):", asm,
+                                  re.M)))
+    assert any("block_sort_packed_kernel" in n for n in names), names
+    assert len(names) >= 12, len(names)
+    scratch = [n for n in names if body(asm, n)[1] != 0]
+    assert not scratch, scratch
