@@ -264,6 +264,34 @@ __device__ __forceinline__ void bitonic_sort(T (&x)[N], int (&pos)[N]) {
     }
 }
 
+// Sorts x[0..N) ascending by Batcher's odd-even merge sort (N a power of
+// two): merges of sorted halves at distances p = 1, 2, 4, ..., each a
+// cascade of compare-exchanges at strides k = p, p/2, ..., 1 between
+// elements of the same 2p block.  Every exchange keeps the smaller first,
+// so keys alone take one min and one max each; for N = 32 the network has
+// 191 exchanges against the bitonic network's 240.
+template <int N, typename T>
+__device__ __forceinline__ void odd_even_sort(T (&x)[N]) {
+#pragma unroll
+    for (int p = 1; p < N; p <<= 1) {
+#pragma unroll
+        for (int k = p; k >= 1; k >>= 1) {
+#pragma unroll
+            for (int j = k % p; j + k < N; j += 2 * k) {
+#pragma unroll
+                for (int i = 0; i < k; ++i) {
+                    const int a = i + j, b = i + j + k;
+                    if (b < N && a / (2 * p) == b / (2 * p)) {
+                        const T lo = min(x[a], x[b]), hi = max(x[a], x[b]);
+                        x[a] = lo;
+                        x[b] = hi;
+                    }
+                }
+            }
+        }
+    }
+}
+
 // A lane's row of ITEMS elements (keys or int positions) to / from the
 // padded LDS layout of the merge stage (4 spare words after every 32), as
 // 16-byte accesses, which that padding keeps free of bank conflicts.
@@ -498,7 +526,10 @@ __device__ __forceinline__ void sort_tile(int* kbuf, int* pbuf, int* split, Key 
     get_row<ITEMS>(kbuf, tid, x);
 #pragma unroll
     for (int t = 0; t < ITEMS; ++t) pos[t] = tid * ITEMS + t;
-    bitonic_sort<ITEMS, POS>(x, pos);
+    if constexpr (POS)
+        bitonic_sort<ITEMS, true>(x, pos);
+    else
+        odd_even_sort<ITEMS>(x);
 
     // The first six rounds run inside each wavefront, across lanes: keys
     // alone (equal keys are indistinguishable, so any exact order of them is
