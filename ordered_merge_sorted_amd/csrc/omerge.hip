@@ -64,7 +64,7 @@ constexpr int kVersion = 100;  // 0.1.0
 #define OMERGE_PLAN_LANES OMERGE_PART_LANES
 #endif
 #ifndef OMERGE_PART_SMALL  // partitions of at most this many boundaries take the shape below
-#define OMERGE_PART_SMALL 32768
+#define OMERGE_PART_SMALL 49152
 #endif
 #ifndef OMERGE_PART_LANES_SMALL  // lanes per boundary (both phases) of those partitions
 #define OMERGE_PART_LANES_SMALL 8
@@ -453,8 +453,10 @@ struct Path {
     // boundary (9-way splits where keys tie and interpolation cannot help)
     // and every 8th boundary first took the 21,846 boundaries of the
     // 2^26+2^26 key+payload step with 256 distinct keys from 23.5 to 22.5 us
-    // and the step from 0.3873-0.3876 to 0.3825 ms, and left a key+payload
-    // merge of distinct keys as fast (0.397-0.400 ms).
+    // and the step from 0.3873-0.3876 to 0.3825 ms, left a key+payload merge
+    // of distinct keys as fast (0.397-0.400 ms), and took the 36,865
+    // boundaries of the skewed 2^27+2^24 step from 0.2117-0.2123 to
+    // 0.2096-0.2097 ms.
     static int partition(const Key* A, int64_t m, const Key* B, int64_t n, int64_t seg_len,
                          int64_t* part, hipStream_t stream) {
         const int64_t count = ceil_div(m + n, seg_len) + 1;

@@ -171,8 +171,8 @@ static void typed_cfg(const void* A, const void* Av, int64_t m, const void* B, c
     const Key* b = static_cast<const Key*>(B);
     const int64_t count = (m + n + seg_len - 1) / seg_len + 1;
     // the library's partition shapes: 8 lanes per boundary and every 8th
-    // boundary first for at most 32,768 boundaries, else 4 and 16
-    if (count <= 32768)
+    // boundary first for at most 49,152 boundaries, else 4 and 16
+    if (count <= 49152)
         run_grid((count * 8 + 255) / 256, 256, [&] {
             omerge::partition_kernel<8, ORDER, 8, 8>(a, m, b, n, seg_len, count, part);
         });
