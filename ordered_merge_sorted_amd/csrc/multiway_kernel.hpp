@@ -706,19 +706,17 @@ merge_multiway_kernel(
     const int64_t c_first = static_cast<int64_t>(blockIdx.x) * CPW;
     const int64_t c_end = c_first + CPW < ncells ? c_first + CPW : ncells;
 
-    Cell4 dc = cells[c_first];
+    CellWindows nxt = cell_windows<KW, Cfg::kYIn, Cfg::kQ, Cfg::kRow>(cells[c_first], src32, n);
     CellLoads<Cfg::kVec, Key> ld;
-    issue_cell<THREADS, Cfg::kVec, KW, Cfg::kLoose>(
-        cell_windows<KW, Cfg::kYIn, Cfg::kQ, Cfg::kRow>(dc, src32, n), src, tid, ld);
+    issue_cell<THREADS, Cfg::kVec, KW, Cfg::kLoose>(nxt, src, tid, ld);
     for (int64_t c = c_first; c < c_end; ++c) {
         if (c > c_first) __syncthreads();  // the previous cell's stores have read the stage
-        const CellWindows cur = cell_windows<KW, Cfg::kYIn, Cfg::kQ, Cfg::kRow>(dc, src32, n);
+        const CellWindows cur = nxt;
         commit_cell<THREADS, Cfg::kVec, KW, ORDER>(cur, ld, tid, lds);
         __syncthreads();
         if (c + 1 < c_end) {
-            dc = cells[c + 1];
-            issue_cell<THREADS, Cfg::kVec, KW, Cfg::kLoose>(
-                cell_windows<KW, Cfg::kYIn, Cfg::kQ, Cfg::kRow>(dc, src32, n), src, tid, ld);
+            nxt = cell_windows<KW, Cfg::kYIn, Cfg::kQ, Cfg::kRow>(cells[c + 1], src32, n);
+            issue_cell<THREADS, Cfg::kVec, KW, Cfg::kLoose>(nxt, src, tid, ld);
         }
 
         // Level 1: R0|R1 into X and R2|R3 into Y, ITEMS outputs per lane:
