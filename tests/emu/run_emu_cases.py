@@ -213,7 +213,8 @@ def group_blocks(r, g):
 
 def group_production(r, g):
     """The shapes the library launches (256 lanes; 2048-output tiles for
-    keys alone and for key+payload), over several tiles and segments."""
+    keys alone and for key+payload), over several tiles and segments, and
+    over segments shorter than one tile."""
     for kv in (False, True):
         tile = r.lib.emu_tile(0, int(kv))
         for c in range(4):
@@ -226,6 +227,15 @@ def group_production(r, g):
                 r.case_kv(0, A, B, seg_len, tuple(int(x) for x in g.integers(0, 4, size=6)), "prod")
             else:
                 r.case_i32(0, A, B, seg_len, tuple(int(x) for x in g.integers(0, 4, size=3)), "prod")
+        # segments shorter than one tile: each workgroup's only tile is short
+        for seg_len in (4, 12):
+            m, n = int(g.integers(0, 300)), int(g.integers(1, 300))
+            A, B = sorted_pair(g, m, n, 300)
+            for c_off in (0, 3):  # aligned outputs (register stores) and staged ones
+                if kv:
+                    r.case_kv(0, A, B, seg_len, (0, 1, 2, 3, c_off, c_off), "prod-short")
+                else:
+                    r.case_i32(0, A, B, seg_len, (1, 2, c_off), "prod-short")
 
 
 def group_search(r, g):

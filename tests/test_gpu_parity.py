@@ -111,6 +111,26 @@ def test_explicit_segments(seg_tiles):
             assert_same(host(got), oracle.merge_i32(A, B), "merge_segments_i32")
 
 
+@pytest.mark.parametrize("seg_len,extra", [(4, 0), (4, 1), (12, 0), (12, 1)])
+def test_partition_shape_switch(seg_len, extra):
+    """The partition takes its 8-lane shape up to 49152 boundaries and its
+    4-lane shape above; at exactly 49152 and 49153 boundaries (ragged last
+    segment included) every co-rank and the segment merge stay exact."""
+    total = seg_len * 49151 - (0 if extra == 0 else -1)
+    g = np.random.Generator(np.random.PCG64(910 + seg_len + extra))
+    m = total // 2 + 17
+    A, B = pair(g, m, total - m, 300)
+    a, b = dev(A), dev(B)
+    say("partition switch", seg_len, total)
+    part = om.partition(a, b, seg_len)
+    assert part.numel() == 49152 + extra
+    I = oracle.co_rank_all(A, B)
+    ks = np.minimum(np.arange(part.numel()) * seg_len, total)
+    assert_same(host(part), I[ks], "partition")
+    got = om.merge_segments_i32(a, b, part, seg_len)
+    assert_same(host(got), oracle.merge_i32(A, B), "merge_segments_i32")
+
+
 def test_co_rank_every_k_with_ties():
     """Device co-rank at every output rank: here the A-first tie rule is
     visible even though the merged keys alone would not show it."""
