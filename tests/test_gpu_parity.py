@@ -116,7 +116,7 @@ def test_partition_shape_switch(seg_len, extra):
     """The partition takes its 8-lane shape up to 49152 boundaries and its
     4-lane shape above; at exactly 49152 and 49153 boundaries (ragged last
     segment included) every co-rank and the segment merge stay exact."""
-    total = seg_len * 49151 - (0 if extra == 0 else -1)
+    total = seg_len * 49151 + extra  # 49152 boundaries, or one more for a 1-element tail
     g = np.random.Generator(np.random.PCG64(910 + seg_len + extra))
     m = total // 2 + 17
     A, B = pair(g, m, total - m, 300)
