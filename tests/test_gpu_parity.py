@@ -266,6 +266,40 @@ def test_non_default_stream():
     assert_same(host(out), oracle.merge_i32(A, B), "stream")
 
 
+def test_calls_on_two_streams_at_once():
+    """Sorts, a key+payload merge and a batched merge in flight together on
+    two streams: each call takes its temporaries on its own stream and the
+    library keeps no state between calls, so every result matches the
+    oracle as it does alone."""
+    g = np.random.Generator(np.random.PCG64(12))
+    K1 = g.integers(-(1 << 31), 1 << 31, size=3_000_017, dtype=np.int64).astype(np.int32)
+    K2 = g.integers(-50, 50, size=2_100_001, dtype=np.int64).astype(np.int32)
+    A, B = pair(g, 1_500_000, 1_200_001, 5000)
+    Av, Bv = tags(A.size, B.size)
+    P, L = 700, 1000
+    X = np.sort(g.integers(0, 1 << 20, size=(P, L)), axis=1).astype(np.int32).reshape(-1)
+    Y = np.sort(g.integers(0, 1 << 20, size=(P, L)), axis=1).astype(np.int32).reshape(-1)
+    offs = np.arange(0, P * L + 1, L, dtype=np.int64)
+    k1, k2, a, av, b, bv = dev(K1), dev(K2), dev(A), dev(Av), dev(B), dev(Bv)
+    x, y, o = dev(X), dev(Y), torch.from_numpy(offs).to(DEV)
+    torch.cuda.synchronize()
+    say("two streams")
+    s1, s2 = torch.cuda.Stream(DEV), torch.cuda.Stream(DEV)
+    with torch.cuda.stream(s1):
+        got1 = om.sort(k1)
+        gotb = om.merge_batched(x, o, y, o)
+    with torch.cuda.stream(s2):
+        gk, gv = om.merge_kv(a, av, b, bv)
+        got2 = om.sort(k2)
+    torch.cuda.synchronize()
+    assert_same(host(got1), oracle.sort(K1), "sort on stream 1")
+    assert_same(host(gotb), oracle.merge_batched(X, offs, Y, offs), "batched on stream 1")
+    wk, wv = oracle.merge_kv(A, Av, B, Bv)
+    assert_same(host(gk), wk, "merge_kv keys on stream 2")
+    assert_same(host(gv).view(np.uint32), wv, "merge_kv payloads on stream 2")
+    assert_same(host(got2), oracle.sort(K2), "sort on stream 2")
+
+
 def test_repeatable_and_preallocated_out():
     g = np.random.Generator(np.random.PCG64(10))
     A, B = pair(g, 123457, 98765, 50)
