@@ -213,6 +213,35 @@ class Resident:
         t = time.perf_counter() - t
         return e0.elapsed_time(e1) / steps, t * 1e3 / steps
 
+    def graph_step_ms(self, want, per_graph=20, replays=10):
+        """ms per step with `per_graph` steps captured in one HIP graph and
+        the graph replayed `replays` times on the same stream: the device's
+        time for a step without the host's per-launch costs.  The steps'
+        launches allocate nothing; the first replay's output is checked
+        against the oracle before anything is timed (None if it differs)."""
+        import torch
+        g = torch.cuda.CUDAGraph()
+        keep, self.stream = self.stream, None  # launch on torch's capture stream
+        try:
+            with torch.cuda.graph(g):
+                for _ in range(per_graph):
+                    self.step()
+        finally:
+            self.stream = keep
+        self.out.fill_(-1)
+        with torch.cuda.stream(self.stream):
+            g.replay()
+        if not self.matches(want):
+            return None
+
+        def replay():
+            with torch.cuda.stream(self.stream):
+                g.replay()
+        _warm(replay, seconds=0.03)
+        ms = _time(replay, self.stream, reps=replays, warm=False) / per_graph
+        del g
+        return ms
+
     def kernel_times(self, steps):
         """`steps` steps with an event before the partition, between the two
         launches and after the merge: per-launch ms of each kernel."""
@@ -266,6 +295,10 @@ def workload_row(om, torch, name, dev, stream, warmup, steps):
     if not r.matches(want):
         log("FAILED: workload %s: the merged output differs from the oracle" % name)
         sys.exit(1)
+    graph_ms = r.graph_step_ms(want)
+    if graph_ms is None:
+        log("FAILED: workload %s: a graph replay's output differs from the oracle" % name)
+        sys.exit(1)
     del want
     _warm(r.step, seconds=0.05, at_least=max(warmup, 2))
     one_ms = r.timed_steps(1)[0]
@@ -281,6 +314,8 @@ def workload_row(om, torch, name, dev, stream, warmup, steps):
            "pct_copy": 100 * copy_ms / ms,
            "merge_kernel_ms": float(np.mean(merge)),
            "partition_kernel_ms": float(np.mean(part)),
+           "graph_step_ms": graph_ms,
+           "graph_pct_peak": 100 * alg / (graph_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
            "cache_resident": alg <= MALL_BYTES,
            "checked": "bit-exact vs oracle"}
     del r
@@ -569,9 +604,14 @@ def main():
     merge_ms_mean = float(np.mean(merge_ms))
     part_ms_mean = float(np.mean(part_ms))
 
-    # 6. The last timed step's output against the oracle.
+    # 6. The last timed step's output against the oracle; then the same step
+    # replayed from a HIP graph (after the timed region, reported on stderr).
     if not r.matches(want):
         log("FAILED: the output of the timed steps differs from the oracle; no number is reported")
+        sys.exit(1)
+    graph_ms = r.graph_step_ms(want)
+    if graph_ms is None:
+        log("FAILED: a graph replay's output differs from the oracle; no number is reported")
         sys.exit(1)
     del want
 
@@ -586,6 +626,7 @@ def main():
         merge_ms_mean, min(merge_ms), max(merge_ms), kern_gbs, 100 * kern_gbs / HBM_PEAK_GBS))
     log("partition kernel: %.4f ms mean (min %.4f, max %.4f); step - merge kernel: %.4f ms" % (
         part_ms_mean, min(part_ms), max(part_ms), ms_step - merge_ms_mean))
+    log("the step replayed from a HIP graph (20 steps per graph): %.4f ms" % graph_ms)
     log("streaming copy kernel, same bytes: %.4f ms -> %.1f GB/s; step at %.1f%% of it" % (
         copy_ms, copy_gbs, 100 * copy_ms / ms_step))
     log("hipMemcpyAsync device to device, same bytes: %.4f ms -> %.1f GB/s" % (memcpy_ms, memcpy_gbs))
@@ -598,17 +639,18 @@ def main():
     # 7. The other workloads, one row each.
     rows = {}
     if not args.headline_only:
-        log("%-24s %9s %11s %9s %7s %7s %9s %9s  %s" % (
+        log("%-24s %9s %11s %9s %7s %7s %9s %9s %9s  %s" % (
             "workload", "step ms", "elements/s", "GB/s", "% peak", "% copy", "merge ms",
-            "part. ms", "note"))
+            "part. ms", "graph ms", "note"))
         for other in ORDER:
             if other == name:
                 continue
             row = workload_row(om, torch, other, dev, stream, args.warmup, args.steps)
             rows[other] = row
-            log("%-24s %9.4f %11.4g %9.1f %7.1f %7.1f %9.4f %9.4f  %s" % (
+            log("%-24s %9.4f %11.4g %9.1f %7.1f %7.1f %9.4f %9.4f %9.4f  %s" % (
                 other, row["step_ms"], row["elements_per_s"], row["gbps"], row["pct_peak"],
                 row["pct_copy"], row["merge_kernel_ms"], row["partition_kernel_ms"],
+                row["graph_step_ms"],
                 "cache resident (%.0f MB moved)" % (WORKLOADS[other].roofline_bytes / 1e6)
                 if row["cache_resident"] else "checked bit-exact"))
     if args.ablation and not w.kv:

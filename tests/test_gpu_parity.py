@@ -300,6 +300,49 @@ def test_calls_on_two_streams_at_once():
     assert_same(host(got2), oracle.sort(K2), "sort on stream 2")
 
 
+def test_graph_capture_and_replay():
+    """The merge paths that allocate nothing (merge_i32_no_alloc, and the
+    two stages with a preallocated partition and output) captured once in a
+    HIP graph, then replayed on new data written into the same inputs, with
+    eager work and synchronisations between replays: every replay matches
+    the oracle on its data."""
+    g = np.random.Generator(np.random.PCG64(13))
+    m, n = 1_000_003, 777_777
+    a = torch.empty(m, dtype=torch.int32, device=DEV)
+    b = torch.empty(n, dtype=torch.int32, device=DEV)
+    out1 = torch.empty(m + n, dtype=torch.int32, device=DEV)
+    out2 = torch.empty(m + n, dtype=torch.int32, device=DEV)
+    seg_len = om.segment_length(m, n)
+    part = torch.empty(om.partition_count(m + n, seg_len), dtype=torch.int64, device=DEV)
+
+    def load(span):
+        A, B = pair(g, m, n, span)
+        a.copy_(torch.from_numpy(A))
+        b.copy_(torch.from_numpy(B))
+        return A, B
+
+    load(1000)
+    om.merge_i32_no_alloc(a, b, out1)  # the first call on a device looks up its scratch
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        om.merge_i32_no_alloc(a, b, out1)
+        om.partition(a, b, seg_len, out=part)
+        om.merge_segments_i32(a, b, part, seg_len, out=out2)
+    for r, span in enumerate((1 << 32, 7, 100000, 1 << 32)):
+        A, B = load(span)
+        out1.fill_(-1)
+        out2.fill_(-1)
+        torch.cuda.synchronize()
+        say("graph replay", r, span)
+        graph.replay()
+        torch.cuda.synchronize()
+        want = oracle.merge_i32(A, B)
+        assert_same(host(out1), want, "replay %d, merge_i32_no_alloc" % r)
+        assert_same(host(out2), want, "replay %d, partition + merge_segments_i32" % r)
+        _check_partition(A, B, host(part), seg_len)
+
+
 def test_repeatable_and_preallocated_out():
     g = np.random.Generator(np.random.PCG64(10))
     A, B = pair(g, 123457, 98765, 50)
