@@ -9,6 +9,7 @@ OmergeError: there is no fallback.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional, Tuple
@@ -92,9 +93,9 @@ def _vec(t: torch.Tensor, name: str, dtypes, device=None) -> torch.Tensor:
         raise TypeError("%s must be a torch.Tensor" % name)
     if t.dtype not in dtypes:
         raise TypeError("%s must have dtype %s, got %s" % (name, " or ".join(map(str, dtypes)), t.dtype))
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError("%s must be on a GPU, got %s" % (name, t.device))
-    if device is not None and t.device != device:
+    if device is not None and t.get_device() != device.index:
         raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
     if t.dim() != 1:
         raise ValueError("%s must be 1-D" % name)
@@ -103,13 +104,36 @@ def _vec(t: torch.Tensor, name: str, dtypes, device=None) -> torch.Tensor:
     return t
 
 
-def _ptr(t: torch.Tensor):
-    return ctypes.c_void_p(t.data_ptr() if t.numel() else 0)
+def _ptr(t: torch.Tensor) -> int:
+    """Device address of t's data (0 when empty), for a void* argument."""
+    return t.data_ptr() if t.numel() else 0
 
 
-def _stream(device: torch.device, stream) -> ctypes.c_void_p:
-    s = torch.cuda.current_stream(device) if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+# The handle of a device's current stream and the current device's index,
+# read without building Stream or device-guard objects (a few microseconds
+# per call that small merges feel); torch's public calls where this torch
+# lacks these functions.
+_current_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(device: torch.device, stream) -> int:
+    if stream is not None:
+        return stream.cuda_stream
+    if _current_raw_stream is not None:
+        index = device.index if device.index is not None else torch.cuda.current_device()
+        return _current_raw_stream(index)
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _on(device):
+    """Makes `device` (a torch.device, an index or a name) current for a
+    library call: nothing to do when it already is, torch's device guard
+    otherwise."""
+    if not isinstance(device, torch.device):
+        device = torch.device("cuda", device) if isinstance(device, int) else torch.device(device)
+    if device.index is None or torch.cuda.current_device() == device.index:
+        return contextlib.nullcontext()
+    return torch.cuda.device(device)
 
 
 def _out(out, n: int, dtype, device, name: str) -> torch.Tensor:
@@ -128,7 +152,7 @@ def merge_i32(a: torch.Tensor, b: torch.Tensor, out: Optional[torch.Tensor] = No
     _vec(b, "b", (torch.int32,), a.device)
     out = _out(out, a.numel() + b.numel(), torch.int32, a.device, "out")
     lib = load_library()
-    with torch.cuda.device(a.device):
+    with _on(a.device):
         rc = lib.merge_i32(_ptr(a), a.numel(), _ptr(b), b.numel(), _ptr(out),
                            _stream(a.device, stream))
     _raise_on(rc, "merge_i32")
@@ -146,7 +170,7 @@ def merge_i32_no_alloc(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor,
         raise ValueError("merge_i32_no_alloc needs an output tensor")
     out = _out(out, a.numel() + b.numel(), torch.int32, a.device, "out")
     lib = load_library()
-    with torch.cuda.device(a.device):
+    with _on(a.device):
         rc = lib.merge_i32_no_alloc(_ptr(a), a.numel(), _ptr(b), b.numel(), _ptr(out),
                                     _stream(a.device, stream))
     _raise_on(rc, "merge_i32_no_alloc")
@@ -170,7 +194,7 @@ def merge_kv(a_keys: torch.Tensor, a_vals: torch.Tensor, b_keys: torch.Tensor,
     out_keys = _out(out_keys, t, torch.int32, dev, "out_keys")
     out_vals = _out(out_vals, t, a_vals.dtype, dev, "out_vals")
     lib = load_library()
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = lib.merge_kv(_ptr(a_keys), _ptr(a_vals), a_keys.numel(), _ptr(b_keys),
                           _ptr(b_vals), b_keys.numel(), _ptr(out_keys), _ptr(out_vals),
                           _stream(dev, stream))
@@ -216,7 +240,7 @@ def merge(a: torch.Tensor, b: torch.Tensor, descending: bool = False,
     order = order_code(a.dtype, descending)
     out = _out(out, a.numel() + b.numel(), a.dtype, a.device, "out")
     lib = load_library()
-    with torch.cuda.device(a.device):
+    with _on(a.device):
         rc = lib.omerge_merge_keys(_ptr(a), a.numel(), _ptr(b), b.numel(), _ptr(out), order,
                                    _stream(a.device, stream))
     _raise_on(rc, "omerge_merge_keys")
@@ -243,7 +267,7 @@ def merge_pairs(a_keys: torch.Tensor, a_vals: torch.Tensor, b_keys: torch.Tensor
     out_keys = _out(out_keys, t, a_keys.dtype, dev, "out_keys")
     out_vals = _out(out_vals, t, a_vals.dtype, dev, "out_vals")
     lib = load_library()
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = lib.omerge_merge_pairs(_ptr(a_keys), _ptr(a_vals), a_keys.numel(), _ptr(b_keys),
                                     _ptr(b_vals), b_keys.numel(), _ptr(out_keys),
                                     _ptr(out_vals), order, a_vals.element_size(),
@@ -283,7 +307,7 @@ def merge_batched(a: torch.Tensor, a_offsets: torch.Tensor, b: torch.Tensor,
     if kv:
         out_vals = _out(out_vals, t, a_vals.dtype, dev, "out_vals")
     lib = load_library()
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = lib.omerge_merge_batched(
             _ptr(a), _ptr(a_vals) if kv else None, _ptr(a_offsets), a.numel(), _ptr(b),
             _ptr(b_vals) if kv else None, _ptr(b_offsets), b.numel(), a_offsets.numel() - 1,
@@ -311,7 +335,7 @@ def sort(keys: torch.Tensor, vals: Optional[torch.Tensor] = None, descending: bo
     if kv:
         out_vals = _out(out_vals, keys.numel(), vals.dtype, dev, "out_vals")
     lib = load_library()
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = lib.omerge_sort(_ptr(keys), _ptr(vals) if kv else None, _ptr(out),
                              _ptr(out_vals) if kv else None, keys.numel(), order,
                              vals.element_size() if kv else 0, _stream(dev, stream))
@@ -333,7 +357,7 @@ def merge_runs4(keys: torch.Tensor, run: int, descending: bool = False,
     order = order_code(keys.dtype, descending)
     out = _out(out, keys.numel(), keys.dtype, dev, "out")
     lib = load_library()
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = lib.omerge_merge_runs4(_ptr(keys), _ptr(out), keys.numel(), int(run), order,
                                     _stream(dev, stream))
     _raise_on(rc, "omerge_merge_runs4")
@@ -349,7 +373,7 @@ def co_rank(a: torch.Tensor, b: torch.Tensor, k: torch.Tensor,
     _vec(k, "k", (torch.int64,), a.device)
     out = _out(out, k.numel(), torch.int64, a.device, "out")
     lib = load_library()
-    with torch.cuda.device(a.device):
+    with _on(a.device):
         rc = lib.omerge_co_rank(_ptr(a), a.numel(), _ptr(b), b.numel(), _ptr(k), k.numel(),
                                 _ptr(out), _stream(a.device, stream))
     _raise_on(rc, "omerge_co_rank")
@@ -359,7 +383,7 @@ def co_rank(a: torch.Tensor, b: torch.Tensor, k: torch.Tensor,
 def segment_length(m: int, n: int, kv: bool = False, device=None) -> int:
     """Outputs per workgroup that merge_i32 / merge_kv use for these sizes."""
     lib = load_library()
-    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+    with _on(device if device is not None else torch.cuda.current_device()):
         s = lib.omerge_segment_length(int(m), int(n), int(bool(kv)))
     if s <= 0:
         raise OmergeError("omerge_segment_length failed for m=%d n=%d" % (m, n))
@@ -382,7 +406,7 @@ def partition(a: torch.Tensor, b: torch.Tensor, seg_len: int,
     count = partition_count(a.numel() + b.numel(), seg_len)
     out = _out(out, count, torch.int64, a.device, "out")
     lib = load_library()
-    with torch.cuda.device(a.device):
+    with _on(a.device):
         rc = lib.omerge_partition(_ptr(a), a.numel(), _ptr(b), b.numel(), int(seg_len),
                                   _ptr(out), _stream(a.device, stream))
     _raise_on(rc, "omerge_partition")
@@ -400,7 +424,7 @@ def merge_segments_i32(a: torch.Tensor, b: torch.Tensor, part: torch.Tensor, seg
         raise ValueError("part has the wrong length for seg_len")
     out = _out(out, a.numel() + b.numel(), torch.int32, a.device, "out")
     lib = load_library()
-    with torch.cuda.device(a.device):
+    with _on(a.device):
         rc = lib.omerge_merge_segments_i32(_ptr(a), a.numel(), _ptr(b), b.numel(), _ptr(part),
                                            int(seg_len), _ptr(out), _stream(a.device, stream))
     _raise_on(rc, "omerge_merge_segments_i32")
@@ -424,7 +448,7 @@ def merge_segments_kv(a_keys, a_vals, b_keys, b_vals, part, seg_len, out_keys=No
     out_keys = _out(out_keys, t, torch.int32, dev, "out_keys")
     out_vals = _out(out_vals, t, a_vals.dtype, dev, "out_vals")
     lib = load_library()
-    with torch.cuda.device(dev):
+    with _on(dev):
         rc = lib.omerge_merge_segments_kv(
             _ptr(a_keys), _ptr(a_vals), a_keys.numel(), _ptr(b_keys), _ptr(b_vals),
             b_keys.numel(), _ptr(part), int(seg_len), _ptr(out_keys), _ptr(out_vals),
@@ -440,7 +464,7 @@ def stream_copy(src: torch.Tensor, out: Optional[torch.Tensor] = None,
     _vec(src, "src", (torch.int32,))
     out = _out(out, src.numel(), torch.int32, src.device, "out")
     lib = load_library()
-    with torch.cuda.device(src.device):
+    with _on(src.device):
         rc = lib.omerge_stream_copy(_ptr(src), src.numel(), _ptr(out), _stream(src.device, stream))
     _raise_on(rc, "omerge_stream_copy")
     return out
@@ -456,7 +480,7 @@ def merge_i32_direct(a: torch.Tensor, b: torch.Tensor, per_thread: int = 16,
     _vec(b, "b", (torch.int32,), a.device)
     out = _out(out, a.numel() + b.numel(), torch.int32, a.device, "out")
     lib = load_library()
-    with torch.cuda.device(a.device):
+    with _on(a.device):
         rc = lib.omerge_merge_i32_direct(_ptr(a), a.numel(), _ptr(b), b.numel(), _ptr(out),
                                          int(per_thread), int(bool(two_searches)),
                                          _stream(a.device, stream))
