@@ -278,6 +278,22 @@ def test_binding_rejects_bad_tensors():
         om.merge_i32([1, 2], cpu)
 
 
+def test_binding_stream_and_device_helpers():
+    """An explicit stream is passed as its own handle; a device with no
+    index (the current one) needs no device guard.  Neither touches a GPU."""
+    import contextlib
+    import torch
+
+    class FakeStream:
+        cuda_stream = 0x1234
+
+    assert M._stream(torch.device("cuda", 0), FakeStream()) == 0x1234
+    assert isinstance(M._on(torch.device("cuda")), contextlib.nullcontext)
+    assert isinstance(M._on("cuda"), contextlib.nullcontext)
+    cpu = torch.zeros(4, dtype=torch.int32)
+    assert M._ptr(cpu[:0]) == 0 and M._ptr(cpu) == cpu.data_ptr()
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(M, "_lib", None)
     monkeypatch.setattr(M, "LIB", str(tmp_path / "absent.so"))
