@@ -305,6 +305,7 @@ def workload_row(om, torch, name, dev, stream, warmup, steps):
     reps = max(steps, int(20.0 / max(one_ms, 1e-3)) + 1)
     ms, _ = r.timed_steps(reps)
     part, merge = r.kernel_times(reps)
+    one_call_ms = _time(r.one_call, stream, reps=reps)
     alg = w.roofline_bytes
     copy_ms, _ = copy_references(om, torch, alg // 2, dev, stream)
     gbs = alg / (ms * 1e-3) / 1e9
@@ -315,6 +316,7 @@ def workload_row(om, torch, name, dev, stream, warmup, steps):
            "merge_kernel_ms": float(np.mean(merge)),
            "partition_kernel_ms": float(np.mean(part)),
            "graph_step_ms": graph_ms,
+           "one_call_ms": one_call_ms,
            "graph_pct_peak": 100 * alg / (graph_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
            "cache_resident": alg <= MALL_BYTES,
            "checked": "bit-exact vs oracle"}
@@ -639,18 +641,18 @@ def main():
     # 7. The other workloads, one row each.
     rows = {}
     if not args.headline_only:
-        log("%-24s %9s %11s %9s %7s %7s %9s %9s %9s  %s" % (
+        log("%-24s %9s %11s %9s %7s %7s %9s %9s %9s %9s  %s" % (
             "workload", "step ms", "elements/s", "GB/s", "% peak", "% copy", "merge ms",
-            "part. ms", "graph ms", "note"))
+            "part. ms", "graph ms", "1 call ms", "note"))
         for other in ORDER:
             if other == name:
                 continue
             row = workload_row(om, torch, other, dev, stream, args.warmup, args.steps)
             rows[other] = row
-            log("%-24s %9.4f %11.4g %9.1f %7.1f %7.1f %9.4f %9.4f %9.4f  %s" % (
+            log("%-24s %9.4f %11.4g %9.1f %7.1f %7.1f %9.4f %9.4f %9.4f %9.4f  %s" % (
                 other, row["step_ms"], row["elements_per_s"], row["gbps"], row["pct_peak"],
                 row["pct_copy"], row["merge_kernel_ms"], row["partition_kernel_ms"],
-                row["graph_step_ms"],
+                row["graph_step_ms"], row["one_call_ms"],
                 "cache resident (%.0f MB moved)" % (WORKLOADS[other].roofline_bytes / 1e6)
                 if row["cache_resident"] else "checked bit-exact"))
     if args.ablation and not w.kv:

@@ -71,7 +71,11 @@ enum omerge_status {
  *   C[m+n]      out: merged keys (device).
  * Enqueues a partition kernel (one co-rank per segment boundary) and the
  * segment merge kernel on `stream`; the partition array is stream-ordered
- * scratch (hipMallocAsync/hipFreeAsync on `stream`).
+ * scratch (hipMallocAsync/hipFreeAsync on `stream`).  A merge whose
+ * segments all fit the device at once (about 8 million outputs of 4-byte
+ * keys on MI355X) is one launch instead, each workgroup finding its own two
+ * boundaries (the pages' block-level co-rank done by the block itself), with
+ * no partition array.  Either way the output is the same.
  */
 int merge_i32(const int32_t *A, int64_t m, const int32_t *B, int64_t n,
               int32_t *C, struct ihipStream_t *stream);
@@ -83,7 +87,7 @@ int merge_i32(const int32_t *A, int64_t m, const int32_t *B, int64_t n,
  * calls no hipMalloc/hipMallocAsync/hipFree and no allocating library
  * routine: the partition array lives in a file-scope device array of the
  * library (2^20 + 1 co-ranks, 8 MiB on each GPU the library runs on, held
- * until the process ends).
+ * until the process ends); the one-launch path for small merges uses none.
  *   m + n at most 2^32; larger totals return OMERGE_SCRATCH_LIMIT before
  *   anything is enqueued.
  *   Every call on one GPU uses that GPU's one array, so calls that may

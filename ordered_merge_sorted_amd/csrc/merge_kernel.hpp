@@ -885,13 +885,23 @@ struct SegDesc {
 // instead of through the LDS stage; 4-byte keys with no or 4-byte payloads,
 // or 8-byte keys alone, and 8 outputs per lane only.  Any output works, but only 16-byte-aligned segment outputs
 // get 16-byte stores, so the launcher picks it when they are.
-template <int THREADS, int ITEMS, int VW, int ORDER, bool DESC = false, bool REG = false>
+//
+// SELF = true (with DESC = false): part is not read; the workgroup finds the
+// co-ranks of its own two boundaries first (the pages' block-level co-rank
+// done by the block itself), with two 4-lane group searches in its first
+// wavefront.  The search's dependent rounds then lengthen every
+// workgroup's life, which costs more than a partition kernel once the
+// workgroups run in several waves; a grid that fits the device in one wave
+// saves the partition's launch and its array instead.
+template <int THREADS, int ITEMS, int VW, int ORDER, bool DESC = false, bool REG = false,
+          bool SELF = false>
 __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
     const typename KeyOrder<ORDER>::T* __restrict__ A, const uint32_t* __restrict__ Av, int64_t m,
     const typename KeyOrder<ORDER>::T* __restrict__ B, const uint32_t* __restrict__ Bv, int64_t n,
     const int64_t* __restrict__ part, int64_t seg_len,
     typename KeyOrder<ORDER>::T* __restrict__ C, uint32_t* __restrict__ Cv,
     const SegDesc* __restrict__ desc, int64_t c_total) {
+    static_assert(!(SELF && DESC), "a workgroup searches its boundaries only in partition mode");
     using Key = typename KeyOrder<ORDER>::T;
     constexpr int KW = KeyOrder<ORDER>::kWords;
     constexpr bool KV = VW > 0;
@@ -939,10 +949,39 @@ __global__ __launch_bounds__(THREADS) void merge_segments_kernel(
         k0 = seg * seg_len;
         const int64_t k1 = k0 + seg_len < total ? k0 + seg_len : total;
         c_len = static_cast<int>(k1 - k0);
+        int64_t p0, p1;  // co-ranks of k0 and k1
+        if constexpr (SELF) {
+            // Lanes 0-3 search k0, lanes 4-7 k1; the rest of the first
+            // wavefront votes with empty ranges.  The results pass through
+            // the split words, which the tiles use only after the barriers.
+            if (tid < 64) {
+                const int grp = tid >> 2;
+                const int g_lane = tid & 3;
+                const bool act = grp < 2;
+                const int64_t i = co_rank_group<4, ORDER>(act ? (grp == 0 ? k0 : k1) : 0, A,
+                                                          act ? m : 0, B, act ? n : 0, g_lane,
+                                                          tid - g_lane);
+                if (act && g_lane == 0) {
+                    split[2 * grp] = static_cast<int>(static_cast<uint32_t>(i));
+                    split[2 * grp + 1] = static_cast<int>(static_cast<uint64_t>(i) >> 32);
+                }
+            }
+            __syncthreads();
+            p0 = static_cast<int64_t>(
+                (static_cast<uint64_t>(static_cast<uint32_t>(split[1])) << 32) |
+                static_cast<uint32_t>(split[0]));
+            p1 = static_cast<int64_t>(
+                (static_cast<uint64_t>(static_cast<uint32_t>(split[3])) << 32) |
+                static_cast<uint32_t>(split[2]));
+            __syncthreads();  // every lane has read them before the tiles reuse the words
+        } else {
+            p0 = part[seg];
+            p1 = part[seg + 1];
+        }
         // Segment windows from the partition, clamped so that any partition
         // (even one made from unsorted input) keeps every access in range.
-        i0 = clamp_to<int64_t>(part[seg], k0 > n ? k0 - n : 0, k0 < m ? k0 : m);
-        const int64_t i1 = clamp_to<int64_t>(part[seg + 1], k1 > n ? k1 - n : 0, k1 < m ? k1 : m);
+        i0 = clamp_to<int64_t>(p0, k0 > n ? k0 - n : 0, k0 < m ? k0 : m);
+        const int64_t i1 = clamp_to<int64_t>(p1, k1 > n ? k1 - n : 0, k1 < m ? k1 : m);
         a_len = static_cast<int>(clamp_to<int64_t>(i1 - i0, 0, c_len));
         b_len = c_len - a_len;
         j0 = k0 - i0;

@@ -219,14 +219,16 @@ int hip_fail(hipError_t e) {
 // Per-device launch facts, filled once per device and element shape.
 struct DeviceInfo {
     int cus = 0;
-    int wg_per_cu[2 * kShapes] = {};  // per shape and store path; 0 = not yet queried
+    // per shape and store path, with a partition array (the first 2*kShapes)
+    // or with each workgroup finding its own boundaries; 0 = not yet queried
+    int wg_per_cu[4 * kShapes] = {};
 };
 constexpr int kMaxDevices = 64;
 DeviceInfo g_dev[kMaxDevices];
 std::mutex g_dev_mutex;
 
 // Resident workgroups per CU of `kernel` on the current device (cached per
-// `shape`, an index below 2*kShapes), and the device's CU count.
+// `shape`, an index below 4*kShapes), and the device's CU count.
 int device_slots(int shape, const void* kernel, int* cus, int* wg_per_cu) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -425,6 +427,42 @@ struct Path {
         hipLaunchKernelGGL((merge_segments_kernel<kThreads, kItems, VW, ORDER, DESC, false>), grid,
                            block, 0, stream, A, Av, m, B, Bv, n, part, seg_len, C, Cv, desc,
                            c_total);
+    }
+
+    // A merge whose segments all fit the device at once, in one launch:
+    // each workgroup finds its own two boundaries, so there is no partition
+    // kernel and no partition array.  The searches lengthen each
+    // workgroup's life, which only pays while the grid runs in one wave;
+    // *done is false (nothing launched) for a larger grid.
+    static int merge_self(const Key* A, const uint32_t* Av, int64_t m, const Key* B,
+                          const uint32_t* Bv, int64_t n, int64_t seg_len, Key* C, uint32_t* Cv,
+                          bool reg, hipStream_t stream, bool* done) {
+        *done = false;
+        reg = reg && kReg;
+        const void* kernel =
+            reg ? reinterpret_cast<const void*>(
+                      merge_segments_kernel<kThreads, kItems, VW, ORDER, false, kReg, true>)
+                : reinterpret_cast<const void*>(
+                      merge_segments_kernel<kThreads, kItems, VW, ORDER, false, false, true>);
+        int cus = 0, per_cu = 0;
+        int rc = device_slots(2 * kShapes + 2 * kShape + (reg ? 1 : 0), kernel, &cus, &per_cu);
+        if (rc != OMERGE_OK) return rc;
+        const int64_t segs = ceil_div(m + n, seg_len);
+        if (segs > static_cast<int64_t>(cus) * per_cu) return OMERGE_OK;
+        const dim3 grid(static_cast<unsigned>(segs)), block(kThreads);
+        if constexpr (kReg) {
+            if (reg)
+                hipLaunchKernelGGL(
+                    (merge_segments_kernel<kThreads, kItems, VW, ORDER, false, true, true>), grid,
+                    block, 0, stream, A, Av, m, B, Bv, n, nullptr, seg_len, C, Cv, nullptr, m + n);
+        }
+        if (!reg)
+            hipLaunchKernelGGL(
+                (merge_segments_kernel<kThreads, kItems, VW, ORDER, false, false, true>), grid,
+                block, 0, stream, A, Av, m, B, Bv, n, nullptr, seg_len, C, Cv, nullptr, m + n);
+        *done = true;
+        hipError_t e = hipGetLastError();
+        return e == hipSuccess ? OMERGE_OK : hip_fail(e);
     }
 
     // Segment length for the register-store kernel (reg, where the shape has
@@ -740,6 +778,11 @@ struct Path {
         int64_t sl = 0;
         int rc = seg_len(m, n, &sl, reg);
         if (rc != OMERGE_OK) return rc;
+        bool done = false;
+        rc = merge_self(static_cast<const Key*>(A), static_cast<const uint32_t*>(Av), m,
+                        static_cast<const Key*>(B), static_cast<const uint32_t*>(Bv), n, sl,
+                        static_cast<Key*>(C), static_cast<uint32_t*>(Cv), reg, stream, &done);
+        if (rc != OMERGE_OK || done) return rc;
         const int64_t count = ceil_div(total, sl) + 1;
         int64_t* part = fixed;
         if (fixed != nullptr) {

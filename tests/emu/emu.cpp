@@ -139,9 +139,10 @@ constexpr bool reg_shape() {
 }
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-// Runs merge_segments_kernel<T, I, VW, ORDER, DESC, reg> over `blocks`
-// workgroups (reg only where the shape allows it).
-template <int T, int I, int VW, int ORDER, bool DESC>
+// Runs merge_segments_kernel<T, I, VW, ORDER, DESC, reg, SELF> over
+// `blocks` workgroups (reg only where the shape allows it; SELF: each
+// workgroup finds its own boundaries and part is not read).
+template <int T, int I, int VW, int ORDER, bool DESC, bool SELF = false>
 static void run_merge(bool reg, int64_t blocks, const typename omerge::KeyOrder<ORDER>::T* A,
                       const uint32_t* Av, int64_t m, const typename omerge::KeyOrder<ORDER>::T* B,
                       const uint32_t* Bv, int64_t n, const int64_t* part, int64_t seg_len,
@@ -150,22 +151,25 @@ static void run_merge(bool reg, int64_t blocks, const typename omerge::KeyOrder<
     if constexpr (reg_shape<I, VW, ORDER>()) {
         if (reg) {
             run_grid(blocks, T, [&] {
-                omerge::merge_segments_kernel<T, I, VW, ORDER, DESC, true>(
+                omerge::merge_segments_kernel<T, I, VW, ORDER, DESC, true, SELF>(
                     A, Av, m, B, Bv, n, part, seg_len, C, Cv, desc, c_total);
             });
             return;
         }
     }
     run_grid(blocks, T, [&] {
-        omerge::merge_segments_kernel<T, I, VW, ORDER, DESC, false>(A, Av, m, B, Bv, n, part,
-                                                                   seg_len, C, Cv, desc, c_total);
+        omerge::merge_segments_kernel<T, I, VW, ORDER, DESC, false, SELF>(
+            A, Av, m, B, Bv, n, part, seg_len, C, Cv, desc, c_total);
     });
 }
 
 // Partition + merge for one key order, payload width VW (words) and shape.
+// self: one launch whose workgroups find their own boundaries (the
+// partition is still written, for the caller's check, but not read).
 template <int T, int I, int VW, int ORDER>
 static void typed_cfg(const void* A, const void* Av, int64_t m, const void* B, const void* Bv,
-                      int64_t n, int64_t seg_len, int64_t* part, void* C, void* Cv) {
+                      int64_t n, int64_t seg_len, int64_t* part, void* C, void* Cv,
+                      bool self = false) {
     using Key = typename omerge::KeyOrder<ORDER>::T;
     const Key* a = static_cast<const Key*>(A);
     const Key* b = static_cast<const Key*>(B);
@@ -182,10 +186,16 @@ static void typed_cfg(const void* A, const void* Av, int64_t m, const void* B, c
         });
     if (m + n == 0) return;
     const bool reg = aligned16(C) && (VW == 0 || aligned16(Cv));
-    run_merge<T, I, VW, ORDER, false>(reg, count - 1, a, static_cast<const uint32_t*>(Av), m, b,
-                                      static_cast<const uint32_t*>(Bv), n, part, seg_len,
-                                      static_cast<Key*>(C), static_cast<uint32_t*>(Cv), nullptr,
-                                      m + n);
+    if (self)
+        run_merge<T, I, VW, ORDER, false, true>(reg, count - 1, a, static_cast<const uint32_t*>(Av),
+                                                m, b, static_cast<const uint32_t*>(Bv), n, nullptr,
+                                                seg_len, static_cast<Key*>(C),
+                                                static_cast<uint32_t*>(Cv), nullptr, m + n);
+    else
+        run_merge<T, I, VW, ORDER, false>(reg, count - 1, a, static_cast<const uint32_t*>(Av), m,
+                                          b, static_cast<const uint32_t*>(Bv), n, part, seg_len,
+                                          static_cast<Key*>(C), static_cast<uint32_t*>(Cv), nullptr,
+                                          m + n);
 }
 
 // Outputs per lane of the library's shapes (its items_for).
@@ -217,13 +227,16 @@ constexpr bool emu_has(int variant, int order, int vw) {
     return order == 1 || order == (3 | 8) || order == 5;
 }
 
+// variant | 2: the same shapes with each workgroup finding its own boundaries.
 template <int ORDER, int VW>
 static bool typed_go(int variant, const void* A, const void* Av, int64_t m, const void* B,
                      const void* Bv, int64_t n, int64_t seg_len, int64_t* part, void* C,
                      void* Cv) {
+    const bool self = (variant & 2) != 0;
+    variant &= 1;
     if constexpr (emu_has(1, ORDER, VW)) {
         if (variant == 1) {
-            typed_cfg<128, 4, VW, ORDER>(A, Av, m, B, Bv, n, seg_len, part, C, Cv);
+            typed_cfg<128, 4, VW, ORDER>(A, Av, m, B, Bv, n, seg_len, part, C, Cv, self);
             return true;
         }
     }
@@ -231,7 +244,7 @@ static bool typed_go(int variant, const void* A, const void* Av, int64_t m, cons
         if (variant == 0) {
             constexpr int kw = omerge::KeyOrder<ORDER>::kWords;
             typed_cfg<256, production_items(kw, VW), VW, ORDER>(A, Av, m, B, Bv, n, seg_len,
-                                                                 part, C, Cv);
+                                                                 part, C, Cv, self);
             return true;
         }
     }
@@ -507,20 +520,22 @@ static bool typed_order(int variant, int vw, const void* A, const void* Av, int6
     }
 }
 
-template <int T, int I, int VW>
+template <int T, int I, int VW, bool SELF = false>
 static void merge_cfg(const int32_t* A, const uint32_t* Av, int64_t m, const int32_t* B,
                       const uint32_t* Bv, int64_t n, const int64_t* part, int64_t seg_len,
                       int32_t* C, uint32_t* Cv) {
     const int64_t segs = (m + n + seg_len - 1) / seg_len;
     const bool reg = aligned16(C) && (VW == 0 || aligned16(Cv));
-    run_merge<T, I, VW, 0, false>(reg, segs, A, Av, m, B, Bv, n, part, seg_len, C, Cv, nullptr,
-                                  m + n);
+    run_merge<T, I, VW, 0, false, SELF>(reg, segs, A, Av, m, B, Bv, n, SELF ? nullptr : part,
+                                        seg_len, C, Cv, nullptr, m + n);
 }
 
 extern "C" {
 
 // variant 0 = the shapes the library launches; 1 = small shapes (128 lanes,
-// 4 items) that wrap the rings many times on small inputs.
+// 4 items) that wrap the rings many times on small inputs; variant | 2 (in
+// the merges) = the same shapes with each workgroup finding its own
+// boundaries, the partition array unread.
 int emu_tile(int variant, int kv) {
     if (variant == 0) return kv ? omerge::MergeCfg<256, 8, 1, 1>::kTile
                                 : omerge::MergeCfg<256, 8, 1, 0>::kTile;
@@ -561,19 +576,23 @@ void emu_direct(const int32_t* A, int64_t m, const int32_t* B, int64_t n, int32_
 
 void emu_merge_i32(int variant, const int32_t* A, int64_t m, const int32_t* B, int64_t n,
                    const int64_t* part, int64_t seg_len, int32_t* C) {
-    if (variant == 0)
-        merge_cfg<256, 8, 0>(A, nullptr, m, B, nullptr, n, part, seg_len, C, nullptr);
-    else
-        merge_cfg<128, 4, 0>(A, nullptr, m, B, nullptr, n, part, seg_len, C, nullptr);
+    switch (variant) {
+        case 0: merge_cfg<256, 8, 0>(A, nullptr, m, B, nullptr, n, part, seg_len, C, nullptr); break;
+        case 1: merge_cfg<128, 4, 0>(A, nullptr, m, B, nullptr, n, part, seg_len, C, nullptr); break;
+        case 2: merge_cfg<256, 8, 0, true>(A, nullptr, m, B, nullptr, n, part, seg_len, C, nullptr); break;
+        default: merge_cfg<128, 4, 0, true>(A, nullptr, m, B, nullptr, n, part, seg_len, C, nullptr);
+    }
 }
 
 void emu_merge_kv(int variant, const int32_t* A, const uint32_t* Av, int64_t m, const int32_t* B,
                   const uint32_t* Bv, int64_t n, const int64_t* part, int64_t seg_len, int32_t* C,
                   uint32_t* Cv) {
-    if (variant == 0)
-        merge_cfg<256, 8, 1>(A, Av, m, B, Bv, n, part, seg_len, C, Cv);
-    else
-        merge_cfg<128, 4, 1>(A, Av, m, B, Bv, n, part, seg_len, C, Cv);
+    switch (variant) {
+        case 0: merge_cfg<256, 8, 1>(A, Av, m, B, Bv, n, part, seg_len, C, Cv); break;
+        case 1: merge_cfg<128, 4, 1>(A, Av, m, B, Bv, n, part, seg_len, C, Cv); break;
+        case 2: merge_cfg<256, 8, 1, true>(A, Av, m, B, Bv, n, part, seg_len, C, Cv); break;
+        default: merge_cfg<128, 4, 1, true>(A, Av, m, B, Bv, n, part, seg_len, C, Cv);
+    }
 }
 
 // Partition and merge for a key order (kind | 8 if descending) and payload

@@ -111,7 +111,9 @@ class Runner:
     def case_i32(self, variant, A, B, seg_len, offs=(0, 0, 0), label=""):
         m, n = A.size, B.size
         Ap, Bp = placed(A, offs[0]), placed(B, offs[1])
-        part = self.partition(Ap, Bp, seg_len)
+        # variants | 2 do not read the partition: one width checks it
+        part = self.partition(Ap, Bp, seg_len, widths=(416,) if variant & 2 else
+                              (1, 4, 8, 16, 64, 416))
         I = oracle.co_rank_all(A, B)
         ks = np.minimum(np.arange(part.size, dtype=np.int64) * seg_len, m + n)
         self.check(np.array_equal(part, I[ks]), ("partition", label, m, n, seg_len))
@@ -148,7 +150,9 @@ class Runner:
 
 
 def group_small(r, g):
-    """64-lane, 4-item shapes (tile 256): many ring wraps on small inputs."""
+    """64-lane, 4-item shapes (tile 256): many ring wraps on small inputs,
+    with a partition array and with each workgroup finding its own
+    boundaries."""
     tile = r.lib.emu_tile(1, 0)
     for c in range(36):
         m, n = (int(x) for x in g.integers(0, 2500, size=2))
@@ -162,6 +166,11 @@ def group_small(r, g):
         offs = tuple(int(x) for x in g.integers(0, 4, size=6))
         r.case_i32(1, A, B, seg_len, offs[:3], "small")
         r.case_kv(1, A, B, seg_len, offs, "small")
+        # the same shapes with each workgroup finding its own boundaries
+        # (every other case, empty sides included)
+        if c % 2 == 0:
+            r.case_i32(3, A, B, seg_len, offs[:3], "small-self")
+            r.case_kv(3, A, B, seg_len, offs, "small-self")
         if m + n <= 400:
             r.case_co_rank(A, B)
 
@@ -223,19 +232,25 @@ def group_production(r, g):
             span = int(g.choice([4, 300, 1 << 32]))
             A, B = sorted_pair(g, m, n, span)
             seg_len = [tile, 3 * tile, 2 * tile + 1364, 4 * tile][c]
-            if kv:
-                r.case_kv(0, A, B, seg_len, tuple(int(x) for x in g.integers(0, 4, size=6)), "prod")
-            else:
-                r.case_i32(0, A, B, seg_len, tuple(int(x) for x in g.integers(0, 4, size=3)), "prod")
+            # partition array, or boundaries found by each workgroup (every
+            # other segment length)
+            for variant in ((0, 2) if c % 2 == 0 else (0,)):
+                if kv:
+                    r.case_kv(variant, A, B, seg_len,
+                              tuple(int(x) for x in g.integers(0, 4, size=6)), "prod")
+                else:
+                    r.case_i32(variant, A, B, seg_len,
+                               tuple(int(x) for x in g.integers(0, 4, size=3)), "prod")
         # segments shorter than one tile: each workgroup's only tile is short
         for seg_len in (4, 12):
             m, n = int(g.integers(0, 300)), int(g.integers(1, 300))
             A, B = sorted_pair(g, m, n, 300)
             for c_off in (0, 3):  # aligned outputs (register stores) and staged ones
-                if kv:
-                    r.case_kv(0, A, B, seg_len, (0, 1, 2, 3, c_off, c_off), "prod-short")
-                else:
-                    r.case_i32(0, A, B, seg_len, (1, 2, c_off), "prod-short")
+                for variant in ((0, 2) if seg_len == 12 and c_off == 0 else (0,)):
+                    if kv:
+                        r.case_kv(variant, A, B, seg_len, (0, 1, 2, 3, c_off, c_off), "prod-short")
+                    else:
+                        r.case_i32(variant, A, B, seg_len, (1, 2, c_off), "prod-short")
 
 
 def group_search(r, g):
@@ -370,13 +385,16 @@ def group_orders(r, g):
     plan = []
     for order in (0, 1, 2, 3, 4, 5, 8, 9, 10, 11, 12, 13):
         for vw in (0, 1, 2):
-            for variant in (1, 0):
+            # 1 | 2 and 0 | 2: the same shapes, each workgroup finding its own
+            # boundaries (on a spread of 4- and 8-byte orders)
+            self_variants = (3, 2) if order in (0, 10, 11, 13) else ()
+            for variant in (1, 0) + self_variants:
                 plan.append((order, vw, variant))
     ran = 0
     for c, (order, vw, variant) in enumerate(plan):
         dtype = KIND_DTYPE[order & 7]
         desc = bool(order & 8)
-        tile = r.lib.emu_typed_tile(variant, order, vw)
+        tile = r.lib.emu_typed_tile(variant & 1, order, vw)
         for rep in range(3 if variant == 1 else 1):
             m, n = (int(x) for x in g.integers(0, 5 * tile, size=2))
             if rep == 2:

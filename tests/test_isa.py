@@ -25,8 +25,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 from ordered_merge_sorted_amd import build  # noqa: E402
 
-MERGE = "_ZN6omerge21merge_segments_kernelILi256ELi8ELi0ELi0ELb0ELb1EE"
-MERGE_STAGED = "_ZN6omerge21merge_segments_kernelILi256ELi8ELi0ELi0ELb0ELb0EE"
+MERGE = "_ZN6omerge21merge_segments_kernelILi256ELi8ELi0ELi0ELb0ELb1ELb0EE"
+MERGE_STAGED = "_ZN6omerge21merge_segments_kernelILi256ELi8ELi0ELi0ELb0ELb0ELb0EE"
 BLOCK_SORT = "_ZN6omerge17block_sort_kernelILi512ELi32ELi0ELi0EE"
 
 

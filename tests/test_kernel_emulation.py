@@ -44,7 +44,7 @@ WIDE_GROUPS = ["orders", "sort", "batched", "batched_aligned", "batched_garbage"
                "multiway_garbage"]
 JOBS = [(f, g) for f in sorted(FLAG_SETS) for g in CORE_GROUPS] + \
     [("default", g) for g in WIDE_GROUPS]
-POOL = 4  # concurrent children
+POOL = 6  # concurrent children (mostly waiting in barriers)
 
 
 def _compile(flags_name, out_dir):
