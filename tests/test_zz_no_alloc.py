@@ -1,7 +1,10 @@
 """merge_i32_no_alloc, the entry point that allocates no device memory,
 against merge_i32 (and the oracle) on two calls in a row, the second with a
 smaller input: the static scratch keeps the first call's partition, and the
-second call must not read any of it."""
+second call must not read any of it.  Merges that fit the device in one wave
+of workgroups (up to about 8 million outputs) take the one-launch path and
+use no scratch at all; the first pair keeps both calls above that, on the
+scratch."""
 import numpy as np
 import pytest
 import torch
@@ -18,6 +21,9 @@ def _dev(x):
 
 
 @pytest.mark.parametrize("first,second", [
+    # 16.8M outputs (4,097 co-ranks in the scratch), then 9M (2,199): both
+    # through the partition array
+    ((16, (1 << 23) + 5, (1 << 23) - 3, -(1 << 31), (1 << 31) - 1), (17, 5000011, 4000037, -100, 100)),
     # 16.8M outputs: full 4,096-output segments (4,097 co-ranks); then 120k
     ((11, (1 << 23) + 123, (1 << 23) - 77, -(1 << 31), (1 << 31) - 1), (12, 70001, 50003, -40, 40)),
     # many ties, then a tiny ragged case with one empty side
