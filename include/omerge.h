@@ -72,8 +72,8 @@ enum omerge_status {
  * Enqueues a partition kernel (one co-rank per segment boundary) and the
  * segment merge kernel on `stream`; the partition array is stream-ordered
  * scratch (hipMallocAsync/hipFreeAsync on `stream`).  A merge whose
- * segments all fit the device at once (about 8 million outputs of 4-byte
- * keys on MI355X) is one launch instead, each workgroup finding its own two
+ * segments all fit the device at once (about 8 million int32 keys on
+ * MI355X) is one launch instead, each workgroup finding its own two
  * boundaries (the pages' block-level co-rank done by the block itself), with
  * no partition array.  Either way the output is the same.
  */

@@ -434,35 +434,45 @@ struct Path {
     // kernel and no partition array.  The searches lengthen each
     // workgroup's life, which only pays while the grid runs in one wave;
     // *done is false (nothing launched) for a larger grid.
+    // Built for int32 keys in ascending order (merge_i32, merge_kv and the
+    // typed calls with that order); the other orders keep two launches,
+    // which keeps the library's build time down.
     static int merge_self(const Key* A, const uint32_t* Av, int64_t m, const Key* B,
                           const uint32_t* Bv, int64_t n, int64_t seg_len, Key* C, uint32_t* Cv,
                           bool reg, hipStream_t stream, bool* done) {
         *done = false;
-        reg = reg && kReg;
-        const void* kernel =
-            reg ? reinterpret_cast<const void*>(
-                      merge_segments_kernel<kThreads, kItems, VW, ORDER, false, kReg, true>)
-                : reinterpret_cast<const void*>(
-                      merge_segments_kernel<kThreads, kItems, VW, ORDER, false, false, true>);
-        int cus = 0, per_cu = 0;
-        int rc = device_slots(2 * kShapes + 2 * kShape + (reg ? 1 : 0), kernel, &cus, &per_cu);
-        if (rc != OMERGE_OK) return rc;
-        const int64_t segs = ceil_div(m + n, seg_len);
-        if (segs > static_cast<int64_t>(cus) * per_cu) return OMERGE_OK;
-        const dim3 grid(static_cast<unsigned>(segs)), block(kThreads);
-        if constexpr (kReg) {
-            if (reg)
+        if constexpr (ORDER != kKeyI32) {
+            return OMERGE_OK;
+        } else {
+            reg = reg && kReg;
+            const void* kernel =
+                reg ? reinterpret_cast<const void*>(
+                          merge_segments_kernel<kThreads, kItems, VW, ORDER, false, kReg, true>)
+                    : reinterpret_cast<const void*>(
+                          merge_segments_kernel<kThreads, kItems, VW, ORDER, false, false, true>);
+            int cus = 0, per_cu = 0;
+            int rc =
+                device_slots(2 * kShapes + 2 * kShape + (reg ? 1 : 0), kernel, &cus, &per_cu);
+            if (rc != OMERGE_OK) return rc;
+            const int64_t segs = ceil_div(m + n, seg_len);
+            if (segs > static_cast<int64_t>(cus) * per_cu) return OMERGE_OK;
+            const dim3 grid(static_cast<unsigned>(segs)), block(kThreads);
+            if constexpr (kReg) {
+                if (reg)
+                    hipLaunchKernelGGL(
+                        (merge_segments_kernel<kThreads, kItems, VW, ORDER, false, true, true>),
+                        grid, block, 0, stream, A, Av, m, B, Bv, n, nullptr, seg_len, C, Cv,
+                        nullptr, m + n);
+            }
+            if (!reg)
                 hipLaunchKernelGGL(
-                    (merge_segments_kernel<kThreads, kItems, VW, ORDER, false, true, true>), grid,
-                    block, 0, stream, A, Av, m, B, Bv, n, nullptr, seg_len, C, Cv, nullptr, m + n);
+                    (merge_segments_kernel<kThreads, kItems, VW, ORDER, false, false, true>), grid,
+                    block, 0, stream, A, Av, m, B, Bv, n, nullptr, seg_len, C, Cv, nullptr,
+                    m + n);
+            *done = true;
+            hipError_t e = hipGetLastError();
+            return e == hipSuccess ? OMERGE_OK : hip_fail(e);
         }
-        if (!reg)
-            hipLaunchKernelGGL(
-                (merge_segments_kernel<kThreads, kItems, VW, ORDER, false, false, true>), grid,
-                block, 0, stream, A, Av, m, B, Bv, n, nullptr, seg_len, C, Cv, nullptr, m + n);
-        *done = true;
-        hipError_t e = hipGetLastError();
-        return e == hipSuccess ? OMERGE_OK : hip_fail(e);
     }
 
     // Segment length for the register-store kernel (reg, where the shape has
