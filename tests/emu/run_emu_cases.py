@@ -149,10 +149,8 @@ class Runner:
         self.check(np.array_equal(out, oracle.co_rank_all(A, B)), ("co_rank", A.size, B.size))
 
 
-def group_small(r, g):
-    """64-lane, 4-item shapes (tile 256): many ring wraps on small inputs,
-    with a partition array and with each workgroup finding its own
-    boundaries."""
+def small_cases(r, g):
+    """The seeded cases of the small shapes: (case, A, B, seg_len, offsets)."""
     tile = r.lib.emu_tile(1, 0)
     for c in range(36):
         m, n = (int(x) for x in g.integers(0, 2500, size=2))
@@ -164,15 +162,25 @@ def group_small(r, g):
         A, B = sorted_pair(g, m, n, span)
         seg_len = int(g.choice([tile, 2 * tile, 3 * tile, 4 * int(g.integers(1, 300))]))
         offs = tuple(int(x) for x in g.integers(0, 4, size=6))
+        yield c, A, B, seg_len, offs
+
+
+def group_small(r, g):
+    """64-lane, 4-item shapes (tile 256): many ring wraps on small inputs."""
+    for c, A, B, seg_len, offs in small_cases(r, g):
         r.case_i32(1, A, B, seg_len, offs[:3], "small")
         r.case_kv(1, A, B, seg_len, offs, "small")
-        # the same shapes with each workgroup finding its own boundaries
-        # (every other case, empty sides included)
+        if A.size + B.size <= 400:
+            r.case_co_rank(A, B)
+
+
+def group_small_self(r, g):
+    """The same cases (every other one, empty sides included) with each
+    workgroup finding its own boundaries."""
+    for c, A, B, seg_len, offs in small_cases(r, g):
         if c % 2 == 0:
             r.case_i32(3, A, B, seg_len, offs[:3], "small-self")
             r.case_kv(3, A, B, seg_len, offs, "small-self")
-        if m + n <= 400:
-            r.case_co_rank(A, B)
 
 
 def group_skew(r, g):
@@ -653,7 +661,7 @@ def group_multiway_garbage(r, g):
                     ("multiway garbage writes outside", variant, order, n, run))
 
 
-GROUPS = {"multiway_garbage": group_multiway_garbage, "multiway": group_multiway, "batched_aligned": group_batched_aligned, "search": group_search, "batched_garbage": group_batched_garbage, "sort": group_sort, "batched": group_batched, "orders": group_orders, "small": group_small, "direct": group_direct, "skew": group_skew, "blocks": group_blocks,
+GROUPS = {"small_self": group_small_self, "multiway_garbage": group_multiway_garbage, "multiway": group_multiway, "batched_aligned": group_batched_aligned, "search": group_search, "batched_garbage": group_batched_garbage, "sort": group_sort, "batched": group_batched, "orders": group_orders, "small": group_small, "direct": group_direct, "skew": group_skew, "blocks": group_blocks,
           "production": group_production, "unsorted": group_unsorted}
 
 if __name__ == "__main__":

@@ -13,17 +13,11 @@ on (CPU only: hipcc compiles the library's device code to assembly).
   per cross-lane stage), copy no key before a DPP move, and use no scratch
   memory.
 """
-import os
 import re
-import shutil
-import subprocess
-import sys
 
 import pytest
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-sys.path.insert(0, ROOT)
-from ordered_merge_sorted_amd import build  # noqa: E402
+import isa_asm
 
 MERGE = "_ZN6omerge21merge_segments_kernelILi256ELi8ELi0ELi0ELb0ELb1ELb0EE"
 MERGE_STAGED = "_ZN6omerge21merge_segments_kernelILi256ELi8ELi0ELi0ELb0ELb0ELb0EE"
@@ -31,14 +25,10 @@ BLOCK_SORT = "_ZN6omerge17block_sort_kernelILi512ELi32ELi0ELi0EE"
 
 
 @pytest.fixture(scope="module")
-def asm(tmp_path_factory):
-    if shutil.which(build.hipcc()) is None:
+def asm():
+    if not isa_asm.available():
         pytest.skip("hipcc is not installed")
-    out = str(tmp_path_factory.mktemp("isa") / "omerge.s")
-    flags = [f for f in build.HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
-    subprocess.check_call([build.hipcc(), *flags, "--cuda-device-only", "-S", "-x", "hip",
-                           *build.SOURCES, "-o", out], stderr=subprocess.DEVNULL)
-    return open(out).read()
+    return isa_asm.assembly()
 
 
 def body(asm, prefix):

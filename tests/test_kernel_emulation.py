@@ -38,10 +38,11 @@ FLAG_SETS = {
     "plain_access": ["-DOMERGE_NT_LOADS=0", "-DOMERGE_NT_STORES=0"],
 }
 CORE_GROUPS = ["small", "skew", "blocks", "direct", "production", "unsorted", "search"]
-# The typed, sort and batch groups exercise the same load and store helpers
-# as the core groups, so they run in the default build only.
+# The typed, sort and batch groups, and the small shapes with each workgroup
+# finding its own boundaries, exercise the same load and store helpers as
+# the core groups, so they run in the default build only.
 WIDE_GROUPS = ["orders", "sort", "batched", "batched_aligned", "batched_garbage", "multiway",
-               "multiway_garbage"]
+               "multiway_garbage", "small_self"]
 JOBS = [(f, g) for f in sorted(FLAG_SETS) for g in CORE_GROUPS] + \
     [("default", g) for g in WIDE_GROUPS]
 POOL = 6  # concurrent children (mostly waiting in barriers)
@@ -79,7 +80,7 @@ def emu_results(tmp_path_factory):
     libs = {f: pool.submit(_compile, f, out_dir) for f in FLAG_SETS}
     libs = {f: fut.result() for f, fut in libs.items()}
     # the longest runs first, so the pool's tail is short
-    weight = {"batched": 6, "sort": 6, "small": 4, "direct": 3, "orders": 2}
+    weight = {"batched": 6, "sort": 6, "small": 4, "small_self": 4, "direct": 3, "orders": 2}
     futures = {}
     for f, g in sorted(JOBS, key=lambda j: -weight.get(j[1], 1)):
         futures[(f, g)] = pool.submit(_run, libs[f], rt, g)
