@@ -307,12 +307,16 @@ def workload_row(om, torch, name, dev, stream, warmup, steps):
     part, merge = r.kernel_times(reps)
     one_call_ms = _time(r.one_call, stream, reps=reps)
     alg = w.roofline_bytes
-    copy_ms, _ = copy_references(om, torch, alg // 2, dev, stream)
+    # a copy of a cache-resident row's few bytes times launches, not
+    # bandwidth: no copy reference for those rows
+    copy_ms = None
+    if alg > MALL_BYTES:
+        copy_ms = copy_references(om, torch, alg // 2, dev, stream)[0]
     gbs = alg / (ms * 1e-3) / 1e9
     row = {"step_ms": ms, "steps": reps,
            "elements_per_s": w.total / (ms * 1e-3),
            "gbps": gbs, "pct_peak": 100 * gbs / HBM_PEAK_GBS,
-           "pct_copy": 100 * copy_ms / ms,
+           "pct_copy": None if copy_ms is None else 100 * copy_ms / ms,
            "merge_kernel_ms": float(np.mean(merge)),
            "partition_kernel_ms": float(np.mean(part)),
            "graph_step_ms": graph_ms,
@@ -649,9 +653,10 @@ def main():
                 continue
             row = workload_row(om, torch, other, dev, stream, args.warmup, args.steps)
             rows[other] = row
-            log("%-24s %9.4f %11.4g %9.1f %7.1f %7.1f %9.4f %9.4f %9.4f %9.4f  %s" % (
+            log("%-24s %9.4f %11.4g %9.1f %7.1f %7s %9.4f %9.4f %9.4f %9.4f  %s" % (
                 other, row["step_ms"], row["elements_per_s"], row["gbps"], row["pct_peak"],
-                row["pct_copy"], row["merge_kernel_ms"], row["partition_kernel_ms"],
+                "n/a" if row["pct_copy"] is None else "%.1f" % row["pct_copy"],
+                row["merge_kernel_ms"], row["partition_kernel_ms"],
                 row["graph_step_ms"], row["one_call_ms"],
                 "cache resident (%.0f MB moved)" % (WORKLOADS[other].roofline_bytes / 1e6)
                 if row["cache_resident"] else "checked bit-exact"))
