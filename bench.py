@@ -587,6 +587,13 @@ def main():
         log("FAILED: the merged output differs from the oracle; no number is reported")
         sys.exit(1)
     log("checked: output bit-exact against the oracle (%d elements)" % w.total)
+    # The same step replayed from a HIP graph, checked first (reported on
+    # stderr; before the references below, which keep the device busy up to
+    # the timed steps).
+    graph_ms = r.graph_step_ms(want)
+    if graph_ms is None:
+        log("FAILED: a graph replay's output differs from the oracle; no number is reported")
+        sys.exit(1)
     if (args.ablation or args.ablation_direct) and not w.kv:
         ablation(om, torch, name, dev, stream, arrs, want)
         if name != "even_odd_2p21":
@@ -610,14 +617,9 @@ def main():
     merge_ms_mean = float(np.mean(merge_ms))
     part_ms_mean = float(np.mean(part_ms))
 
-    # 6. The last timed step's output against the oracle; then the same step
-    # replayed from a HIP graph (after the timed region, reported on stderr).
+    # 6. The last timed step's output against the oracle.
     if not r.matches(want):
         log("FAILED: the output of the timed steps differs from the oracle; no number is reported")
-        sys.exit(1)
-    graph_ms = r.graph_step_ms(want)
-    if graph_ms is None:
-        log("FAILED: a graph replay's output differs from the oracle; no number is reported")
         sys.exit(1)
     del want
 
